@@ -1,0 +1,412 @@
+"""Pins that tie the float64 oracle to facts outside itself.
+
+Each ``pin_*`` function raises AssertionError when the oracle disagrees with
+what the pages print, with a closed form, with an independent library routine
+(torch's scaled_dot_product_attention / logsumexp in float64), with a
+pure-Python brute force on tiny inputs, or with an invariant the pages state.
+``test_oracle_pins.py`` runs every pin; ``test_oracle_mutations.py`` plants
+plausible mistakes in the oracle and checks that some pin catches each one.
+"""
+
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+import torch
+
+import oracle.pa_oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+# --------------------------------------------------------------------------
+# storage and index pins
+# --------------------------------------------------------------------------
+
+def pin_bf16_decoding():
+    """IEEE encodings: bf16 is the top half of an fp32 (textbook values)."""
+    bits = np.array([0x3F80, 0xC000, 0x0000, 0x8000, 0x3E80, 0x4049, 0x7F80, 0xFF80],
+                    dtype=np.uint16)
+    want = [1.0, -2.0, 0.0, -0.0, 0.25, 3.140625, math.inf, -math.inf]
+    got = O.bf16_bits_to_f64(bits)
+    assert list(got) == want, got
+    assert np.signbit(got[3])
+
+
+def _go_program_arrays():
+    g = _golden("paged_program.json")
+    n, dim = g["seqLen"], g["dim"]
+    keys = np.array([[math.sin(i * 3 + d) for d in range(dim)] for i in range(n)])
+    vals = np.array([[math.cos(i * 5 + d * 2) for d in range(dim)] for i in range(n)])
+    return g, keys, vals, np.array(g["q"])
+
+
+def _go_cache(g, keys, vals, table):
+    """Store the sequence through the page's slot formula, as its main() does."""
+    bs, nblk, dim = g["blockSize"], g["numBlocks"], g["dim"]
+    cache = np.zeros((nblk, 2, bs, 1, dim))
+    slots = np.array([O.slot_of(table, p, bs) for p in range(len(keys))])
+    cache = O.cache_write_kv(cache, keys[:, None, :], vals[:, None, :], slots)
+    return cache, slots
+
+
+def pin_go_program_slots():
+    """The slot ranges the page's program prints for blockTable {6, 1, 4}."""
+    g, keys, vals, _ = _go_program_arrays()
+    table = np.array(g["blockTable"])
+    cache, slots = _go_cache(g, keys, vals, table)
+    rng = g["slot_ranges_printed"]
+    assert [int(slots[0]), int(slots[3])] == rng["positions 0-3"]
+    assert [int(slots[4]), int(slots[7])] == rng["positions 4-7"]
+    assert [int(slots[8]), int(slots[9])] == rng["positions 8-9"]
+    # exactly slotsUsed of slotsTotal slots hold the sequence
+    flatk = cache[:, 0, :, 0, :].reshape(-1, g["dim"])
+    used = np.flatnonzero(np.any(flatk != 0, axis=1))
+    assert len(used) == g["slots_used"] and flatk.shape[0] == g["slots_total"]
+    assert sorted(used.tolist()) == sorted(slots.tolist())
+    # the gather returns the contiguous arrays bit for bit
+    k2, v2 = O.gather_kv(cache, table, len(keys))
+    assert np.array_equal(k2[:, 0], keys) and np.array_equal(v2[:, 0], vals)
+
+
+def _go_attend(q, keys, vals):
+    """Pure-Python restatement of the page's ``attend``: scaled dot products,
+    max-shifted exponentials, normalised weighted sum (scalar loops)."""
+    dim = len(q)
+    scores = [sum(q[d] * k[d] for d in range(dim)) / math.sqrt(dim) for k in keys]
+    mx = max(scores)
+    ex = [math.exp(s - mx) for s in scores]
+    tot = sum(ex)
+    return [sum(ex[i] / tot * vals[i][d] for i in range(len(vals))) for d in range(dim)]
+
+
+def pin_go_program_identical():
+    """Paged == contiguous, bit for bit, for the page's table and its Try-it
+    tables; both match the page's scalar algorithm to 1e-14."""
+    g, keys, vals, q = _go_program_arrays()
+    scale = 1.0 / math.sqrt(g["dim"])
+    contiguous, lse_c = O.attention(q[None, None, :], keys[:, None, :], vals[:, None, :],
+                                    scale, None)
+    ref = np.array(_go_attend(q.tolist(), keys.tolist(), vals.tolist()))
+    assert np.max(np.abs(contiguous[0, 0] - ref)) < 1e-14, (contiguous, ref)
+    for table in [g["blockTable"]] + g["try_it_tables"]:
+        table = np.array(table)
+        cache, _ = _go_cache(g, keys, vals, table)
+        qsl = np.array([0, 1])
+        out, lse = O.paged_attention(q[None, None, :], cache, table[None, :], qsl,
+                                     np.array([g["seqLen"]]), scale, causal=True)
+        assert np.array_equal(out, contiguous) == g["identical"], table
+        assert np.array_equal(lse, lse_c)
+
+
+def pin_num_kv_splits():
+    """max_seq_len / 512 splits, capped at 2 x compute units (Triton/MLA page,
+    關鍵檔案); the long-context workload's 131072 keys on 256 CUs give 256."""
+    assert O.num_kv_splits(131072, 256) == 256
+    assert O.num_kv_splits(4096, 256) == 8
+    assert O.num_kv_splits(8192, 256) == 16
+    assert O.num_kv_splits(10 ** 7, 256) == 512
+    assert O.num_kv_splits(1000, 2) == 2
+    assert O.num_kv_splits(10 ** 7, 2) == 4
+    assert O.num_kv_splits(1, 256) == 1
+    assert O.num_kv_splits(0, 256) == 1
+    assert O.num_kv_splits(513, 256) == 2      # rounds up (reading)
+    assert O.num_kv_splits(512, 256) == 1
+
+
+def pin_cache_write_bytes():
+    """Written slots hold the new rows bit for bit, K in half 0 and V in half
+    1; every other byte is untouched; negative slots are skipped."""
+    rng = _rng(7)
+    nb, bs, H, D = 9, 16, 3, 8
+    cache = rng.integers(0, 65536, size=(nb, 2, bs, H, D), dtype=np.uint16)
+    T = 20
+    slots = rng.choice(nb * bs, size=T, replace=False).astype(np.int64)
+    slots[5] = -1
+    k = rng.integers(0, 65536, size=(T, H, D), dtype=np.uint16)
+    v = rng.integers(0, 65536, size=(T, H, D), dtype=np.uint16)
+    out = O.cache_write_kv(cache, k, v, slots)
+    flat_k = out[:, 0].reshape(nb * bs, H, D)
+    flat_v = out[:, 1].reshape(nb * bs, H, D)
+    touched = np.zeros(nb * bs, dtype=bool)
+    for t, s in enumerate(slots):
+        if s < 0:
+            continue
+        assert np.array_equal(flat_k[s], k[t]) and np.array_equal(flat_v[s], v[t])
+        touched[s] = True
+    ck = cache[:, 0].reshape(nb * bs, H, D)
+    cv = cache[:, 1].reshape(nb * bs, H, D)
+    assert np.array_equal(flat_k[~touched], ck[~touched])
+    assert np.array_equal(flat_v[~touched], cv[~touched])
+    # MLA row layout: kv_c then k_pe
+    mc = rng.integers(0, 65536, size=(4, 8, 12), dtype=np.uint16)
+    kvc = rng.integers(0, 65536, size=(2, 9), dtype=np.uint16)
+    kpe = rng.integers(0, 65536, size=(2, 3), dtype=np.uint16)
+    mo = O.cache_write_mla(mc, kvc, kpe, np.array([13, -1]))
+    assert np.array_equal(mo[1, 5], np.concatenate([kvc[0], kpe[0]]))
+    mo[1, 5] = mc[1, 5]
+    assert np.array_equal(mo, mc)
+
+
+# --------------------------------------------------------------------------
+# merge pins
+# --------------------------------------------------------------------------
+
+def pin_fig5c_merge():
+    """Figure 5c: 15 after block A, A's share 1/3 once B joins, merged 28.33."""
+    g = _golden("fig5c_merge.json")
+    V = np.array(g["V"], dtype=np.float64)
+    a_idx, b_idx = g["block_A_keys"], g["block_B_keys"]
+    for base in (-3.0, 0.0, 11.5):
+        scores = np.array([base, base, base + math.log(2), base + math.log(2)])
+        q = np.ones((1, 1, 1))
+        keys = scores.reshape(4, 1, 1)
+        vals = V.reshape(4, 1, 1)
+        oA, lA = O.attention(q, keys[a_idx], vals[a_idx], 1.0, None)
+        oB, lB = O.attention(q, keys[b_idx], vals[b_idx], 1.0, None)
+        assert abs(oA[0, 0, 0] - g["output_after_A"]) < 1e-12
+        out, lse = O.lse_merge(np.stack([oA[0, 0], oB[0, 0]])[None],
+                               np.array([[lA[0, 0], lB[0, 0]]]))
+        share = math.exp(lA[0, 0] - lse[0])
+        assert abs(share - g["share_of_A_after_B"]) < 1e-12
+        assert round(float(out[0, 0]), g["merged_printed_decimals"]) == g["merged_printed"]
+        assert abs(out[0, 0] - 85.0 / 3.0) < 1e-12
+        naive, nl = O.attention(q, keys, vals, 1.0, None)
+        assert abs(naive[0, 0, 0] - out[0, 0]) < 1e-12 and abs(nl[0, 0] - lse[0]) < 1e-12
+
+
+def pin_merge_edges():
+    """-inf splits weigh nothing; all -inf gives out 0, lse -inf; one finite
+    split passes through unchanged; merging is order independent."""
+    o = np.array([[[1.0, 2.0], [5.0, 7.0], [9.0, 9.0]]])
+    out, lse = O.lse_merge(o, np.array([[-math.inf, 0.25, -math.inf]]))
+    assert np.array_equal(out[0], [5.0, 7.0]) and lse[0] == 0.25
+    out, lse = O.lse_merge(o, np.full((1, 3), -math.inf))
+    assert np.array_equal(out[0], [0.0, 0.0]) and lse[0] == -math.inf
+    rng = _rng(3)
+    oo = rng.standard_normal((2, 5, 4))
+    ll = rng.standard_normal((2, 5)) * 3
+    a, la = O.lse_merge(oo, ll)
+    p = rng.permutation(5)
+    b, lb = O.lse_merge(oo[:, p], ll[:, p])
+    assert np.allclose(a, b, rtol=0, atol=1e-13) and np.allclose(la, lb, rtol=0, atol=1e-13)
+    # lse of the merge is ln(sum exp(lse_s)) computed by numpy's logaddexp
+    assert np.allclose(la, np.logaddexp.reduce(ll, axis=1), rtol=0, atol=1e-13)
+    packed = np.concatenate([oo, ll[..., None]], axis=-1)
+    c, lc = O.lse_merge_packed(packed)
+    assert np.array_equal(c, a) and np.array_equal(lc, la)
+
+
+# --------------------------------------------------------------------------
+# attention pins
+# --------------------------------------------------------------------------
+
+def pin_closed_forms():
+    """One key -> its value and its score; zero query -> mean of the visible
+    values and lse = ln(#visible); equal keys -> mean of values."""
+    rng = _rng(11)
+    Hq, Hkv, D = 4, 2, 16
+    q = rng.standard_normal((1, Hq, D))
+    K = rng.standard_normal((1, Hkv, D))
+    V = rng.standard_normal((1, Hkv, D))
+    out, lse = O.attention(q, K, V, 0.3, 0)
+    for h in range(Hq):
+        kv = h // (Hq // Hkv)
+        assert np.array_equal(out[0, h], V[0, kv])
+        assert abs(lse[0, h] - 0.3 * float(q[0, h] @ K[0, kv])) < 1e-12
+    S = 37
+    K = rng.standard_normal((S, Hkv, D))
+    V = rng.standard_normal((S, Hkv, D))
+    L = 5
+    out, lse = O.attention(np.zeros((L, Hq, D)), K, V, 0.7, S - L)
+    for i in range(L):
+        nvis = S - L + i + 1
+        for h in range(Hq):
+            kv = h // (Hq // Hkv)
+            assert np.allclose(out[i, h], V[:nvis, kv].mean(axis=0), rtol=0, atol=1e-13)
+            assert abs(lse[i, h] - math.log(nvis)) < 1e-13
+    Keq = np.repeat(rng.standard_normal((1, Hkv, D)), S, axis=0)
+    q = rng.standard_normal((1, Hq, D))
+    out, _ = O.attention(q, Keq, V, 0.2, None)
+    for h in range(Hq):
+        assert np.allclose(out[0, h], V[:, h // 2].mean(axis=0), rtol=0, atol=1e-12)
+
+
+def _sdpa(q, K, V, scale, mask):
+    """torch scaled_dot_product_attention (float64, CPU) with GQA sharing."""
+    tq = torch.from_numpy(np.ascontiguousarray(q.transpose(1, 0, 2)))[None]
+    tk = torch.from_numpy(np.ascontiguousarray(K.transpose(1, 0, 2)))[None]
+    tv = torch.from_numpy(np.ascontiguousarray(V.transpose(1, 0, 2)))[None]
+    m = None if mask is None else torch.from_numpy(mask)
+    o = torch.nn.functional.scaled_dot_product_attention(
+        tq, tk, tv, attn_mask=m, scale=scale, enable_gqa=(K.shape[1] != q.shape[1]))
+    return o[0].numpy().transpose(1, 0, 2)
+
+
+def _torch_lse(q, K, scale, mask):
+    tq = torch.from_numpy(q)          # [L, Hq, D]
+    tk = torch.from_numpy(K)          # [S, Hkv, D]
+    g = q.shape[1] // K.shape[1]
+    tk = tk.repeat_interleave(g, dim=1)
+    z = torch.einsum("lhd,shd->hls", tq, tk) * scale
+    if mask is not None:
+        z = z.masked_fill(~torch.from_numpy(mask)[None], float("-inf"))
+    return torch.logsumexp(z, dim=-1).numpy().T
+
+
+def pin_torch_sdpa_gqa():
+    """Random GQA, bottom-right causal and unmasked, against torch's float64
+    scaled_dot_product_attention (repeat-interleaved KV heads) and logsumexp."""
+    rng = _rng(5)
+    for (L, S, Hq, Hkv, D, causal) in [(1, 50, 8, 2, 32, True), (7, 23, 6, 3, 16, True),
+                                       (9, 9, 4, 4, 8, True), (5, 12, 8, 1, 24, False),
+                                       (3, 40, 4, 2, 128, True)]:
+        q = rng.standard_normal((L, Hq, D))
+        K = rng.standard_normal((S, Hkv, D))
+        V = rng.standard_normal((S, Hkv, D)) * 2 + 0.5
+        scale = 1.0 / math.sqrt(D) * 1.3
+        mask = None
+        if causal:
+            mask = np.arange(S)[None, :] <= (S - L + np.arange(L))[:, None]
+        out, lse = O.attention(q, K, V, scale, (S - L) if causal else None)
+        ref = _sdpa(q, K, V, scale, mask)
+        assert np.max(np.abs(out - ref)) < 1e-12, np.max(np.abs(out - ref))
+        assert np.max(np.abs(lse - _torch_lse(q, K, scale, mask))) < 1e-12
+
+
+def pin_torch_sdpa_mla():
+    """MLA: q = [q_nope | q_pe] over the full row, V = first R columns,
+    against torch's float64 scaled_dot_product_attention with one KV head."""
+    rng = _rng(9)
+    B, H, R, P, bs = 2, 6, 16, 4, 8
+    seq = np.array([19, 8])
+    nb = 8
+    cache = rng.standard_normal((nb, bs, R + P)).astype(np.float32)
+    table = np.array([[3, 5, 0], [6, 1, 1]], dtype=np.int32)
+    qn = rng.standard_normal((B, H, R)).astype(np.float32)
+    qp = rng.standard_normal((B, H, P)).astype(np.float32)
+    out, lse = O.mla_decode(qn, qp, cache, table, seq, 0.21)
+    for r in range(B):
+        rows = np.concatenate([cache[table[r, j]] for j in range(3)])[: seq[r]].astype(np.float64)
+        q = np.concatenate([qn[r], qp[r]], axis=-1).astype(np.float64)[None]
+        ref = _sdpa(q, rows[:, None, :], rows[:, None, :R], 0.21, None)
+        assert np.max(np.abs(out[r] - ref[0])) < 1e-12
+        assert np.max(np.abs(lse[r] - _torch_lse(q, rows[:, None, :], 0.21, None)[0])) < 1e-12
+
+
+def pin_bruteforce_varlen():
+    """Pure-Python scalar loops over a tiny paged varlen causal batch."""
+    rng = _rng(13)
+    bs, Hq, Hkv, D = 4, 4, 2, 3
+    q_lens = [2, 1, 3]
+    seq = [6, 1, 9]
+    nb = 8
+    cache = rng.standard_normal((nb, 2, bs, Hkv, D))
+    table = np.array([[5, 2, 0], [7, 0, 0], [1, 3, 6]], dtype=np.int32)
+    qsl = np.array([0, 2, 3, 6])
+    T = 6
+    q = rng.standard_normal((T, Hq, D))
+    scale = 0.77
+    out, lse = O.paged_attention(q, cache, table, qsl, np.array(seq), scale, causal=True)
+    for r in range(3):
+        L, S = q_lens[r], seq[r]
+        for i in range(L):
+            t = qsl[r] + i
+            for h in range(Hq):
+                kvh = h * Hkv // Hq
+                sc = []
+                for j in range(S - L + i + 1):
+                    b, o = table[r][j // bs], j % bs
+                    sc.append((scale * sum(q[t, h, d] * cache[b, 0, o, kvh, d] for d in range(D)),
+                               [cache[b, 1, o, kvh, d] for d in range(D)]))
+                mx = max(s for s, _ in sc)
+                den = sum(math.exp(s - mx) for s, _ in sc)
+                for d in range(D):
+                    num = sum(math.exp(s - mx) * v[d] for s, v in sc)
+                    assert abs(out[t, h, d] - num / den) < 1e-13
+                assert abs(lse[t, h] - (mx + math.log(den))) < 1e-13
+
+
+# --------------------------------------------------------------------------
+# invariants the pages state
+# --------------------------------------------------------------------------
+
+def pin_split_merge_equals_unsplit():
+    """Split-KV partials merged by LSE equal unsplit attention (第 1 章 §3.1:
+    splitting adds parallelism, every key still takes part)."""
+    rng = _rng(17)
+    S, L, Hq, Hkv, D = 45, 3, 4, 2, 16
+    q = rng.standard_normal((L, Hq, D))
+    K = rng.standard_normal((S, Hkv, D)) * 2
+    V = rng.standard_normal((S, Hkv, D))
+    full, lfull = O.attention(q, K, V, 0.4, S - L)
+    for cuts in ([0, 45], [0, 16, 45], [0, 7, 8, 30, 45], [0, 44, 45], list(range(0, 46, 5))):
+        parts = [O.partial_attention(q, K, V, 0.4, lo, hi, S - L)
+                 for lo, hi in zip(cuts[:-1], cuts[1:])]
+        outs = np.stack([p[0] for p in parts], axis=2)       # [L, Hq, nsplit, D]
+        lses = np.stack([p[1] for p in parts], axis=2)
+        out, lse = O.lse_merge(outs, lses)
+        assert np.max(np.abs(out - full)) < 1e-12 and np.max(np.abs(lse - lfull)) < 1e-12
+
+
+def pin_block_permutation():
+    """Moving physical blocks (and the tables with them) changes nothing, bit
+    for bit ("Attention Backends", Try it)."""
+    rng = _rng(19)
+    bs, Hq, Hkv, D = 16, 8, 2, 32
+    seq = np.array([70, 16, 33])
+    need = (seq + bs - 1) // bs
+    nb = int(need.sum()) + 2
+    cache = rng.standard_normal((nb, 2, bs, Hkv, D))
+    ids = rng.permutation(nb)
+    table = np.zeros((3, need.max()), dtype=np.int32)
+    c = 0
+    for r in range(3):
+        table[r, :need[r]] = ids[c:c + need[r]]
+        c += need[r]
+    q = rng.standard_normal((3, Hq, D))
+    out, lse = O.paged_decode(q, cache, table, seq, 0.2)
+    perm = rng.permutation(nb)                   # new home of block b is perm[b]
+    cache2 = np.empty_like(cache)
+    cache2[perm] = cache
+    table2 = perm[table].astype(np.int32)
+    out2, lse2 = O.paged_decode(q, cache2, table2, seq, 0.2)
+    assert np.array_equal(out, out2) and np.array_equal(lse, lse2)
+
+
+def pin_chunked_prefill():
+    """A prompt attended in two chunks gives, for the second chunk's queries,
+    the same rows as attending it in one shot; a decode step equals the last
+    row of a prefill over the same keys."""
+    rng = _rng(23)
+    S, Hq, Hkv, D = 40, 4, 2, 16
+    q = rng.standard_normal((S, Hq, D))
+    K = rng.standard_normal((S, Hkv, D))
+    V = rng.standard_normal((S, Hkv, D))
+    one, l1 = O.attention(q, K, V, 0.3, 0)
+    c = 25
+    second, l2 = O.attention(q[c:], K, V, 0.3, c)
+    assert np.max(np.abs(second - one[c:])) < 1e-13 and np.max(np.abs(l2 - l1[c:])) < 1e-13
+    dec, ld = O.attention(q[-1:], K, V, 0.3, S - 1)
+    assert np.max(np.abs(dec - one[-1:])) < 1e-13 and np.max(np.abs(ld - l1[-1:])) < 1e-13
+
+
+ALL_PINS = [
+    pin_bf16_decoding, pin_go_program_slots, pin_go_program_identical,
+    pin_num_kv_splits, pin_cache_write_bytes, pin_fig5c_merge, pin_merge_edges,
+    pin_closed_forms, pin_torch_sdpa_gqa, pin_torch_sdpa_mla,
+    pin_bruteforce_varlen, pin_split_merge_equals_unsplit, pin_block_permutation,
+    pin_chunked_prefill,
+]
