@@ -1,0 +1,255 @@
+/*
+ * pa.h -- paged KV attention for AMD Instinct MI355X (gfx950): the C ABI.
+ *
+ * The operation ("Attention Backends", infra.riteshsonawane.com, section
+ * "What paged attention requires of a kernel"): for a flat batch of T tokens
+ * from N requests,
+ *   1. store the T new keys and values in the shared block-pool cache at
+ *      slot_mapping[t]  (slot = physical_block * block_size + offset);
+ *   2. for each request, attend from its queries over its first seq_len
+ *      cached tokens, fetching them block by block through its row of
+ *      block_table (position p lives at block block_table[r][p / block_size],
+ *      offset p % block_size).
+ * The result is softmax(scale * Q K^T + M) V ("第 1 章 注意力后端", §2.1), M the
+ * causal mask, plus the natural-log log-sum-exp of each softmax row.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Memory.  Every pointer argument is DEVICE memory owned by the caller:
+ *   caches, metadata, inputs, outputs and workspaces.  The library allocates
+ *   and frees nothing and keeps no per-call state.
+ * Streams.  All work is enqueued on `stream` (0 = the null stream) in the
+ *   order described, and the call returns without synchronising.  A new-token
+ *   write that an entry point performs is ordered before the attention that
+ *   reads it.
+ * Errors.  Each call returns a pa_status_t.  Host-side argument checks run
+ *   before anything is enqueued: on any error nothing is launched.
+ *   pa_last_error() returns a description of the calling thread's last error.
+ *   Device-side metadata (block ids, slots, lengths) is not validated; values
+ *   outside the documented ranges give undefined results, but the kernels
+ *   clamp every index they derive from it so that they never read or write
+ *   outside the buffers whose sizes the call describes.
+ * Types.  q, k, v, cache and out share one storage dtype (pa_dtype_t);
+ *   accumulation is fp32; lse and workspaces are fp32.  bf16 results are
+ *   rounded to nearest-even.  block_table, seq_lens and query_start_loc are
+ *   int32; slot_mapping is int64, and a negative slot means "do not write".
+ * Alignment.  Device pointers must be 16-byte aligned.
+ * Shapes.  The GQA cache is [num_blocks, 2, block_size, num_kv_heads,
+ *   head_dim] (index 0 = K, 1 = V) and the MLA latent cache is [num_blocks,
+ *   block_size, kv_lora_rank + rope_dim] ("AttentionBackend：注意力后端抽象层",
+ *   设计动机).  block_size must be a multiple of 16 ("AttentionBackend", 边界与
+ *   失败).  All tensors are dense, row-major, in the shapes given, unless a
+ *   stride argument says otherwise.
+ * Query-to-KV head map.  Query head h reads KV head h / (num_q_heads /
+ *   num_kv_heads) ("第 1 章 注意力后端", §3.2: groups of query heads share a
+ *   KV head).
+ */
+#ifndef PA_H_
+#define PA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PA_OK = 0,
+  PA_ERR_INVALID = 1,     /* an argument is out of range or a pointer is null */
+  PA_ERR_UNSUPPORTED = 2, /* a valid configuration this build does not implement */
+  PA_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required */
+  PA_ERR_HIP = 4          /* the HIP runtime reported an error (launch, device query) */
+} pa_status_t;
+
+typedef enum { PA_F32 = 0, PA_BF16 = 1 } pa_dtype_t;
+
+typedef enum {
+  PA_LAYOUT_KV = 0,  /* [num_blocks, 2, block_size, num_kv_heads, head_dim] */
+  PA_LAYOUT_MLA = 1  /* [num_blocks, block_size, kv_lora_rank + rope_dim]   */
+} pa_layout_t;
+
+/* ---------------------------------------------------------------------------
+ * Host helpers (no device work).
+ * ------------------------------------------------------------------------- */
+
+/* Number of KV splits for split-KV decode: ceil(max_seq_len / 512), at least
+ * 1 and at most 2 * num_cus ("Triton 與 MLA", 關鍵檔案, _compute_num_kv_splits:
+ * max_seq_len / 512, capped at twice the compute-unit count; rounding up is
+ * this library's reading).  num_cus <= 0 is treated as 1. */
+int pa_num_kv_splits(int max_seq_len, int num_cus);
+
+/* Bytes of fp32 workspace pa_decode / pa_mla_decode need for num_splits
+ * splits: num_seqs * num_q_heads * num_splits * (head_dim_v + 1) * 4 (the
+ * "+1" holds each split's lse, "Triton 與 MLA", 資料流).  Returns 0 if any
+ * argument is negative or the product overflows. */
+size_t pa_decode_workspace_bytes(int num_seqs, int num_q_heads, int head_dim_v,
+                                 int num_splits);
+
+/* Split count pa_mla_decode uses when called with num_splits = 0: enough
+ * splits of whole 64-token pages that num_seqs * splits work units cover the
+ * device's compute units about twice, and never more than
+ * pa_num_kv_splits(max_seq_len, num_cus).  Size the workspace with it. */
+int pa_mla_num_kv_splits(int num_seqs, int max_seq_len, int num_cus);
+
+/* Compute units of the current HIP device, or -1 if it cannot be queried. */
+int pa_device_num_cus(void);
+
+/* Thread-local description of the last error ("" if none). */
+const char* pa_last_error(void);
+
+/* ---------------------------------------------------------------------------
+ * pa_cache_write -- step 1 of the contract: store new rows at their slots.
+ *
+ * PA_LAYOUT_KV:  k, v are [num_tokens, num_kv_heads, head_dim] with a token
+ *   stride of k_token_stride / v_token_stride ELEMENTS (heads contiguous);
+ *   row t goes to cache[slot / block_size][0 or 1][slot % block_size].
+ * PA_LAYOUT_MLA: num_kv_heads must be 1 and head_dim = kv_lora_rank +
+ *   rope_dim with rope_dim = 64; k is kv_c [num_tokens, head_dim - 64]
+ *   and v is k_pe [num_tokens, 64] (token strides as above); the stored row
+ *   is kv_c followed by k_pe ("Triton 與 MLA", 資料流).  bf16 only.
+ * slot_mapping: [num_tokens] int64 in [0, num_blocks * block_size), or
+ *   negative to skip the token.  Two tokens must not share a slot.
+ * The copy is bit-exact.  num_tokens = 0 is a no-op.
+ * ------------------------------------------------------------------------- */
+pa_status_t pa_cache_write(pa_layout_t layout, pa_dtype_t dtype,
+                           const void* k, int64_t k_token_stride,
+                           const void* v, int64_t v_token_stride,
+                           void* kv_cache, int64_t num_blocks, int block_size,
+                           int num_kv_heads, int head_dim,
+                           const int64_t* slot_mapping, int num_tokens,
+                           hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * pa_decode -- GQA decode: one query token per request, split-KV partials
+ * merged by log-sum-exp ("第 1 章 注意力后端", §3.1 split-KV; "Triton 與 MLA",
+ * 資料流: workspace (B, H, num_kv_splits, D + 1), stage 2 merges by lse).
+ *
+ * q:           [num_seqs, num_q_heads, head_dim]
+ * k, v:        [num_seqs, num_kv_heads, head_dim] new rows, or both NULL
+ * slot_mapping:[num_seqs] int64, or NULL (then k, v must be NULL too)
+ * kv_cache:    GQA layout, num_blocks blocks of block_size tokens
+ * block_table: [num_seqs, max_blocks_per_seq] int32
+ * seq_lens:    [num_seqs] int32, each in [1, max_seq_len] and at most
+ *              max_blocks_per_seq * block_size; includes the new token, which
+ *              is the request's last position.
+ * max_seq_len: host copy of max(seq_lens) (sets the split partition).
+ * scale:       multiplies Q K^T before the softmax (1/sqrt(head_dim) usually).
+ * num_splits:  0 = pa_num_kv_splits(max_seq_len, pa_device_num_cus());
+ *              1 = no split (each request reduced by one work unit, in an
+ *              order independent of the rest of the batch); n > 1 = n splits.
+ *              Split s of a request covers positions [s*P, (s+1)*P) with
+ *              P = ceil(max_seq_len / n) rounded up to a multiple of
+ *              block_size; splits past the request's end are empty.
+ * workspace:   fp32 scratch of at least pa_decode_workspace_bytes(num_seqs,
+ *              num_q_heads, head_dim, n) bytes (may be NULL when n = 1).
+ * out:         [num_seqs, num_q_heads, head_dim], storage dtype.
+ * lse:         [num_seqs, num_q_heads] fp32 natural-log LSE, or NULL.
+ * Supported: head_dim 128; num_q_heads / num_kv_heads in {1, 2, 4, 8, 16};
+ * PA_F32 and PA_BF16.
+ * Enqueues: the write (if k/v given), the split kernel, the merge kernel.
+ * ------------------------------------------------------------------------- */
+pa_status_t pa_decode(pa_dtype_t dtype,
+                      const void* q, const void* k, const void* v,
+                      void* kv_cache, int64_t num_blocks, int block_size,
+                      const int32_t* block_table, int max_blocks_per_seq,
+                      const int64_t* slot_mapping,
+                      const int32_t* seq_lens, int num_seqs, int max_seq_len,
+                      int num_q_heads, int num_kv_heads, int head_dim,
+                      float scale, int num_splits,
+                      void* workspace, size_t workspace_bytes,
+                      void* out, float* lse, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * pa_prefill_varlen -- varlen prefill / chunked-prefill extend over the paged
+ * cache ("第 1 章 注意力后端", §3.1: prefill has many query rows per request,
+ * possibly in chunks; §4.1: tiled attention with an online softmax).
+ *
+ * q:              [num_tokens, num_q_heads, head_dim]
+ * k, v:           [num_tokens, num_kv_heads, head_dim] new rows, or both NULL
+ * slot_mapping:   [num_tokens] int64, or NULL (then k, v must be NULL too)
+ * query_start_loc:[num_seqs + 1] int32; request r owns query rows
+ *                 query_start_loc[r] .. query_start_loc[r+1]-1, which are its
+ *                 LAST L_r positions (L_r = query_start_loc[r+1] -
+ *                 query_start_loc[r] <= max_query_len, L_r <= seq_lens[r]).
+ * seq_lens:       [num_seqs] int32 (<= max_seq_len and <= max_blocks_per_seq *
+ *                 block_size), including the L_r new positions.
+ * causal:         1 = query i of request r sees keys j <= seq_len - L_r + i
+ *                 (bottom-right aligned); 0 = every query sees all seq_len keys.
+ * out:            [num_tokens, num_q_heads, head_dim]; lse: [num_tokens,
+ *                 num_q_heads] fp32 or NULL.  A query that sees no key gets
+ *                 out = 0 and lse = -inf.
+ * Supported: PA_BF16, head_dim 128, num_q_heads / num_kv_heads in
+ * {1, 2, 4, 8, 16}.
+ * Enqueues: the write (if k/v given), then the attention kernel.
+ * ------------------------------------------------------------------------- */
+pa_status_t pa_prefill_varlen(pa_dtype_t dtype,
+                              const void* q, const void* k, const void* v,
+                              void* kv_cache, int64_t num_blocks, int block_size,
+                              const int32_t* block_table, int max_blocks_per_seq,
+                              const int64_t* slot_mapping,
+                              const int32_t* query_start_loc,
+                              const int32_t* seq_lens, int num_seqs,
+                              int num_tokens, int max_query_len, int max_seq_len,
+                              int num_q_heads, int num_kv_heads, int head_dim,
+                              float scale, int causal,
+                              void* out, float* lse, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * pa_mla_decode -- MLA decode: the latent cache row [kv_c | k_pe] is read as
+ * ONE key head shared by every query head; the query is [q_nope | q_pe]; V is
+ * the first kv_lora_rank columns of the same row ("Triton 與 MLA", 設計動機 and
+ * 資料流).
+ *
+ * q_nope: [num_seqs, num_heads, kv_lora_rank] with strides qn_stride_b /
+ *         qn_stride_h (elements, last dim contiguous)
+ * q_pe:   [num_seqs, num_heads, rope_dim] with strides qp_stride_b / _h
+ * kv_c, k_pe: [num_seqs, kv_lora_rank] / [num_seqs, rope_dim] new rows
+ *         (dense), or both NULL; slot_mapping [num_seqs] or NULL.
+ * kv_cache: MLA layout [num_blocks, block_size, kv_lora_rank + rope_dim].
+ * block_table, seq_lens, max_seq_len, scale: as in pa_decode.
+ * num_splits: 0 = pa_mla_num_kv_splits(num_seqs, max_seq_len, CUs); else as
+ *         in pa_decode (P rounded up to a multiple of block_size).
+ * workspace: pa_decode_workspace_bytes(num_seqs, num_heads, kv_lora_rank, n).
+ * out:    [num_seqs, num_heads, kv_lora_rank]; lse [num_seqs, num_heads] or NULL.
+ * Supported: PA_BF16 only (no dtype argument), kv_lora_rank 512, rope_dim 64,
+ * num_heads a multiple of 16 up to 128, block_size a multiple of 16.
+ * Enqueues: the write (if given), the split kernel, the merge kernel.
+ * ------------------------------------------------------------------------- */
+pa_status_t pa_mla_decode(const void* q_nope, int64_t qn_stride_b, int64_t qn_stride_h,
+                          const void* q_pe, int64_t qp_stride_b, int64_t qp_stride_h,
+                          const void* kv_c, const void* k_pe,
+                          void* kv_cache, int64_t num_blocks, int block_size,
+                          const int32_t* block_table, int max_blocks_per_seq,
+                          const int64_t* slot_mapping,
+                          const int32_t* seq_lens, int num_seqs, int max_seq_len,
+                          int num_heads, int kv_lora_rank, int rope_dim,
+                          float scale, int num_splits,
+                          void* workspace, size_t workspace_bytes,
+                          void* out, float* lse, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * pa_lse_merge -- merge split-KV partials by log-sum-exp ("第 1 章 注意力后端",
+ * §3.1 and §4.1 Figure 5c).
+ *
+ * part: [num_rows, num_heads, num_splits, head_dim_v + 1] fp32; element
+ *       head_dim_v of each split is that split's natural-log lse, the first
+ *       head_dim_v its normalised partial output.  A split with lse = -inf
+ *       weighs nothing (its output values are not read).
+ * out:  [num_rows, num_heads, head_dim_v] in out_dtype:
+ *       out = sum_s exp(lse_s - M) o_s / sum_s exp(lse_s - M), M = max lse_s.
+ * lse:  [num_rows, num_heads] fp32 = M + ln sum_s exp(lse_s - M), or NULL.
+ * All splits -inf: out = 0, lse = -inf.
+ * Supported: head_dim_v <= 1024, num_splits >= 1.
+ * ------------------------------------------------------------------------- */
+pa_status_t pa_lse_merge(const float* part, int num_rows, int num_heads,
+                         int num_splits, int head_dim_v, pa_dtype_t out_dtype,
+                         void* out, float* lse, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H_ */

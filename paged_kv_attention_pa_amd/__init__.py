@@ -1,0 +1,22 @@
+"""Paged KV attention for AMD Instinct MI355X (gfx950).
+
+A thin ctypes binding over ``libpa.so`` (the C ABI of ``include/pa.h``).
+torch supplies device memory and the current HIP stream; every step of the
+computation runs in the library's HIP kernels.  Importing the package never
+loads the library; the first call does, and raises ``PaError`` if it has not
+been built (``python -m paged_kv_attention_pa_amd.build``).
+
+Functions mirror the C entry points: ``cache_write``, ``decode``,
+``prefill_varlen``, ``mla_decode``, ``lse_merge``, plus the host helpers
+``num_kv_splits``, ``mla_num_kv_splits``, ``decode_workspace_bytes``,
+``device_num_cus``.
+"""
+
+from ._binding import (  # noqa: F401
+    PA_BF16, PA_F32, PA_LAYOUT_KV, PA_LAYOUT_MLA, PaError, EXPORTED_SYMBOLS,
+    cache_write, decode, decode_workspace_bytes, device_num_cus, last_error,
+    library, library_path, lse_merge, mla_decode, mla_num_kv_splits,
+    num_kv_splits, prefill_varlen,
+)
+
+__version__ = "0.1.0"

@@ -1,0 +1,281 @@
+"""ctypes marshalling for libpa.so: tensors -> device pointers, shapes -> ints.
+
+No computation happens here.  Output buffers and workspaces are allocated
+with torch when the caller does not pass them (that is memory plumbing; the
+C ABI itself never allocates).
+"""
+
+from __future__ import annotations
+
+import ctypes as C
+import os
+import threading
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(PKG, "libpa.so")
+
+PA_F32, PA_BF16 = 0, 1
+PA_LAYOUT_KV, PA_LAYOUT_MLA = 0, 1
+_STATUS = {0: "PA_OK", 1: "PA_ERR_INVALID", 2: "PA_ERR_UNSUPPORTED",
+           3: "PA_ERR_WORKSPACE", 4: "PA_ERR_HIP"}
+
+# every symbol include/pa.h declares, with (restype, argtypes)
+_vp, _i32, _i64, _f32, _sz = C.c_void_p, C.c_int, C.c_int64, C.c_float, C.c_size_t
+_SIGNATURES = {
+    "pa_num_kv_splits": (_i32, [_i32, _i32]),
+    "pa_decode_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32]),
+    "pa_mla_num_kv_splits": (_i32, [_i32, _i32, _i32]),
+    "pa_device_num_cus": (_i32, []),
+    "pa_last_error": (C.c_char_p, []),
+    "pa_cache_write": (_i32, [_i32, _i32, _vp, _i64, _vp, _i64, _vp, _i64, _i32, _i32, _i32,
+                              _vp, _i32, _vp]),
+    "pa_decode": (_i32, [_i32, _vp, _vp, _vp, _vp, _i64, _i32, _vp, _i32, _vp, _vp, _i32, _i32,
+                         _i32, _i32, _i32, _f32, _i32, _vp, _sz, _vp, _vp, _vp]),
+    "pa_prefill_varlen": (_i32, [_i32, _vp, _vp, _vp, _vp, _i64, _i32, _vp, _i32, _vp, _vp, _vp,
+                                 _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _vp, _vp,
+                                 _vp]),
+    "pa_mla_decode": (_i32, [_vp, _i64, _i64, _vp, _i64, _i64, _vp, _vp, _vp, _i64, _i32, _vp,
+                             _i32, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _vp, _sz,
+                             _vp, _vp, _vp]),
+    "pa_lse_merge": (_i32, [_vp, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp]),
+}
+EXPORTED_SYMBOLS = tuple(_SIGNATURES)
+
+_lock = threading.Lock()
+_lib = None
+
+
+class PaError(RuntimeError):
+    """A non-OK status from libpa.so (or the library is missing)."""
+
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{_STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def library() -> C.CDLL:
+    """Load libpa.so (once).  Raises PaError if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(_LIB_PATH):
+                raise PaError(-1, f"{_LIB_PATH} is missing; build it with "
+                                  "`python -m paged_kv_attention_pa_amd.build`")
+            lib = C.CDLL(_LIB_PATH)
+            for name, (res, args) in _SIGNATURES.items():
+                fn = getattr(lib, name)
+                fn.restype = res
+                fn.argtypes = args
+            _lib = lib
+    return _lib
+
+
+def last_error() -> str:
+    return library().pa_last_error().decode()
+
+
+def _check(status: int):
+    if status != 0:
+        raise PaError(status, last_error())
+
+
+# ------------------------------------------------------------------ helpers
+def num_kv_splits(max_seq_len: int, num_cus: int) -> int:
+    return library().pa_num_kv_splits(int(max_seq_len), int(num_cus))
+
+
+def mla_num_kv_splits(num_seqs: int, max_seq_len: int, num_cus: int) -> int:
+    return library().pa_mla_num_kv_splits(int(num_seqs), int(max_seq_len), int(num_cus))
+
+
+def decode_workspace_bytes(num_seqs: int, num_q_heads: int, head_dim_v: int, num_splits: int) -> int:
+    return library().pa_decode_workspace_bytes(int(num_seqs), int(num_q_heads), int(head_dim_v),
+                                               int(num_splits))
+
+
+def device_num_cus() -> int:
+    return library().pa_device_num_cus()
+
+
+# ------------------------------------------------------------ marshalling
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return C.c_void_p(stream.cuda_stream)
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return PA_BF16
+    if t.dtype == torch.float32:
+        return PA_F32
+    raise TypeError(f"unsupported dtype {t.dtype} (bf16 or fp32)")
+
+
+def _need(cond, msg):
+    if not cond:
+        raise ValueError(msg)
+
+
+def _dev(*ts):
+    for t in ts:
+        if t is not None:
+            _need(t.is_cuda, "every tensor must be on the GPU")
+            _need(t.is_contiguous(), "tensors must be contiguous")
+
+
+def _int_tensor(t, dtype, name):
+    torch = _torch()
+    _need(t.dtype == getattr(torch, dtype), f"{name} must be {dtype}")
+
+
+# ------------------------------------------------------------- entry points
+def cache_write(kv_cache, k, v, slot_mapping, layout: int = PA_LAYOUT_KV, stream=None):
+    """Store new rows at slot_mapping.  GQA: k, v [T, Hkv, D] into
+    kv_cache [nb, 2, bs, Hkv, D].  MLA: k = kv_c [T, R], v = k_pe [T, 64]
+    into kv_cache [nb, bs, R + 64]."""
+    _dev(kv_cache, k, v, slot_mapping)
+    _int_tensor(slot_mapping, "int64", "slot_mapping")
+    dt = _dtype_code(kv_cache)
+    _need(k.dtype == kv_cache.dtype and v.dtype == kv_cache.dtype, "k/v dtype must match the cache")
+    T = k.shape[0]
+    if layout == PA_LAYOUT_KV:
+        nb, _, bs, hkv, d = kv_cache.shape
+        _need(tuple(k.shape) == (T, hkv, d) and tuple(v.shape) == (T, hkv, d), "k/v shape mismatch")
+        ks = vs = hkv * d
+    else:
+        nb, bs, row = kv_cache.shape
+        hkv, d = 1, row
+        ks, vs = k.shape[1], v.shape[1]
+        _need(ks + vs == row, "kv_c/k_pe widths must add up to the cache row")
+    _need(slot_mapping.numel() == T, "slot_mapping must have one entry per token")
+    _check(library().pa_cache_write(layout, dt, _ptr(k), ks, _ptr(v), vs, _ptr(kv_cache), nb, bs,
+                                    hkv, d, _ptr(slot_mapping), T, _stream(stream)))
+
+
+def decode(q, kv_cache, block_table, seq_lens, max_seq_len: int, scale: float,
+           k=None, v=None, slot_mapping=None, num_splits: int = 0, workspace=None,
+           out=None, lse=None, return_lse: bool = True, stream=None):
+    """GQA decode: q [B, Hq, D]; kv_cache [nb, 2, bs, Hkv, D]; returns (out, lse)."""
+    torch = _torch()
+    _dev(q, kv_cache, block_table, seq_lens, k, v, slot_mapping, workspace, out, lse)
+    _int_tensor(block_table, "int32", "block_table")
+    _int_tensor(seq_lens, "int32", "seq_lens")
+    dt = _dtype_code(q)
+    _need(kv_cache.dtype == q.dtype, "q and cache dtypes must match")
+    B, Hq, D = q.shape
+    nb, _, bs, hkv, d2 = kv_cache.shape
+    _need(d2 == D, "head_dim mismatch")
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and return_lse:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    n = num_splits
+    if n == 0:
+        n = num_kv_splits(max_seq_len, device_num_cus())
+    need = decode_workspace_bytes(B, Hq, D, n) if n > 1 else 0
+    if workspace is None and need:
+        workspace = torch.empty(need // 4, dtype=torch.float32, device=q.device)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(library().pa_decode(dt, _ptr(q), _ptr(k), _ptr(v), _ptr(kv_cache), nb, bs,
+                               _ptr(block_table), block_table.shape[1], _ptr(slot_mapping),
+                               _ptr(seq_lens), B, int(max_seq_len), Hq, hkv, D, float(scale),
+                               int(num_splits), _ptr(workspace), wbytes, _ptr(out), _ptr(lse),
+                               _stream(stream)))
+    return out, lse
+
+
+def prefill_varlen(q, kv_cache, block_table, query_start_loc, seq_lens, max_query_len: int,
+                   max_seq_len: int, scale: float, k=None, v=None, slot_mapping=None,
+                   causal: bool = True, out=None, lse=None, return_lse: bool = True,
+                   stream=None):
+    """Varlen (chunked) prefill: q [T, Hq, D]; returns (out [T, Hq, D], lse [T, Hq])."""
+    torch = _torch()
+    _dev(q, kv_cache, block_table, query_start_loc, seq_lens, k, v, slot_mapping, out, lse)
+    _int_tensor(block_table, "int32", "block_table")
+    _int_tensor(seq_lens, "int32", "seq_lens")
+    _int_tensor(query_start_loc, "int32", "query_start_loc")
+    dt = _dtype_code(q)
+    T, Hq, D = q.shape
+    nb, _, bs, hkv, _ = kv_cache.shape
+    N = seq_lens.numel()
+    _need(query_start_loc.numel() == N + 1, "query_start_loc must have num_seqs + 1 entries")
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and return_lse:
+        lse = torch.empty((T, Hq), dtype=torch.float32, device=q.device)
+    _check(library().pa_prefill_varlen(dt, _ptr(q), _ptr(k), _ptr(v), _ptr(kv_cache), nb, bs,
+                                       _ptr(block_table), block_table.shape[1], _ptr(slot_mapping),
+                                       _ptr(query_start_loc), _ptr(seq_lens), N, T,
+                                       int(max_query_len), int(max_seq_len), Hq, hkv, D,
+                                       float(scale), 1 if causal else 0, _ptr(out), _ptr(lse),
+                                       _stream(stream)))
+    return out, lse
+
+
+def mla_decode(q_nope, q_pe, kv_cache, block_table, seq_lens, max_seq_len: int, scale: float,
+               kv_c=None, k_pe=None, slot_mapping=None, num_splits: int = 0, workspace=None,
+               out=None, lse=None, return_lse: bool = True, stream=None):
+    """MLA decode: q_nope [B, H, R], q_pe [B, H, P] (last dim contiguous; may be
+    views of one [B, H, R+P] tensor); kv_cache [nb, bs, R+P].  Returns
+    (out [B, H, R], lse [B, H])."""
+    torch = _torch()
+    _dev(kv_cache, block_table, seq_lens, kv_c, k_pe, slot_mapping, workspace, out, lse)
+    for t in (q_nope, q_pe):
+        _need(t.is_cuda and t.stride(-1) == 1, "q_nope/q_pe must be GPU tensors with a contiguous last dim")
+        _need(t.dtype == torch.bfloat16, "MLA decode is bf16 only")
+    B, H, R = q_nope.shape
+    P = q_pe.shape[2]
+    nb, bs, row = kv_cache.shape
+    _need(row == R + P, "cache row must be kv_lora_rank + rope_dim")
+    if out is None:
+        out = torch.empty((B, H, R), dtype=q_nope.dtype, device=q_nope.device)
+    if lse is None and return_lse:
+        lse = torch.empty((B, H), dtype=torch.float32, device=q_nope.device)
+    n = num_splits
+    if n == 0:
+        n = mla_num_kv_splits(B, max_seq_len, device_num_cus())
+    need = decode_workspace_bytes(B, H, R, n) if n > 1 else 0
+    if workspace is None and need:
+        workspace = torch.empty(need // 4, dtype=torch.float32, device=q_nope.device)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(library().pa_mla_decode(_ptr(q_nope), q_nope.stride(0), q_nope.stride(1),
+                                   _ptr(q_pe), q_pe.stride(0), q_pe.stride(1),
+                                   _ptr(kv_c), _ptr(k_pe), _ptr(kv_cache), nb, bs,
+                                   _ptr(block_table), block_table.shape[1], _ptr(slot_mapping),
+                                   _ptr(seq_lens), B, int(max_seq_len), H, R, P, float(scale),
+                                   int(num_splits), _ptr(workspace), wbytes, _ptr(out), _ptr(lse),
+                                   _stream(stream)))
+    return out, lse
+
+
+def lse_merge(part, out_dtype=None, out=None, lse=None, return_lse: bool = True, stream=None):
+    """Merge split partials part [R, H, S, Dv+1] (lse last) -> (out [R, H, Dv], lse [R, H])."""
+    torch = _torch()
+    _dev(part, out, lse)
+    _need(part.dtype == torch.float32 and part.dim() == 4, "part must be fp32 [R, H, S, Dv+1]")
+    R, H, S, Dv1 = part.shape
+    if out is None:
+        out = torch.empty((R, H, Dv1 - 1), dtype=out_dtype or torch.float32, device=part.device)
+    if lse is None and return_lse:
+        lse = torch.empty((R, H), dtype=torch.float32, device=part.device)
+    _check(library().pa_lse_merge(_ptr(part), R, H, S, Dv1 - 1, _dtype_code(out), _ptr(out),
+                                  _ptr(lse), _stream(stream)))
+    return out, lse

@@ -1,0 +1,384 @@
+// The C entry points of include/pa.h: argument validation, split planning,
+// workspace checks, then launches on the caller's stream.  No allocation, no
+// synchronisation.  Every check runs before the first launch, so an error
+// leaves the stream untouched.
+#include "pa.h"
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <climits>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "launch.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+pa_status_t fail(pa_status_t st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+pa_status_t ok() {
+  g_err[0] = '\0';
+  return PA_OK;
+}
+
+pa_status_t hip_fail(hipError_t e, const char* what) {
+  return fail(PA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+#define PA_REQUIRE(cond, st, ...) \
+  do {                            \
+    if (!(cond)) return fail(st, __VA_ARGS__); \
+  } while (0)
+
+bool is_pow2_group(int g) { return g == 1 || g == 2 || g == 4 || g == 8; }
+
+// Tokens per split for n splits over max_seq_len keys, rounded up to whole
+// pages; at least one page.
+int split_tokens_for(int max_seq_len, int n, int block_size) {
+  int64_t p = (int64_t(max_seq_len) + n - 1) / n;
+  p = (p + block_size - 1) / block_size * block_size;
+  if (p < block_size) p = block_size;
+  return int(p > INT_MAX ? INT_MAX : p);
+}
+
+// Number of splits that actually hold keys when every split has P tokens.
+int used_splits(int max_seq_len, int P) {
+  if (max_seq_len <= 0) return 1;
+  return (max_seq_len + P - 1) / P;
+}
+
+std::atomic<int> g_cus_cache{0};
+
+pa_status_t check_common_cache(int64_t num_blocks, int block_size,
+                               const int32_t* block_table, int max_blocks_per_seq,
+                               const int32_t* seq_lens, int num_seqs, int max_seq_len) {
+  PA_REQUIRE(num_seqs >= 0, PA_ERR_INVALID, "num_seqs must be >= 0 (got %d)", num_seqs);
+  PA_REQUIRE(num_blocks > 0, PA_ERR_INVALID, "num_blocks must be > 0");
+  PA_REQUIRE(block_size > 0 && block_size % 16 == 0, PA_ERR_INVALID,
+             "block_size must be a positive multiple of 16 (got %d)", block_size);
+  PA_REQUIRE(max_blocks_per_seq > 0, PA_ERR_INVALID, "max_blocks_per_seq must be > 0");
+  PA_REQUIRE(max_seq_len >= 0, PA_ERR_INVALID, "max_seq_len must be >= 0");
+  PA_REQUIRE(int64_t(max_seq_len) <= int64_t(max_blocks_per_seq) * block_size, PA_ERR_INVALID,
+             "max_seq_len %d exceeds max_blocks_per_seq * block_size", max_seq_len);
+  PA_REQUIRE(num_blocks <= INT64_MAX / (int64_t(block_size) * 4096), PA_ERR_INVALID,
+             "num_blocks too large");
+  if (num_seqs > 0) {
+    PA_REQUIRE(block_table && seq_lens, PA_ERR_INVALID, "block_table and seq_lens must be non-null");
+  }
+  return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pa_num_kv_splits(int max_seq_len, int num_cus) {
+  if (num_cus < 1) num_cus = 1;
+  int64_t n = (int64_t(max_seq_len) + 511) / 512;
+  if (max_seq_len <= 0) n = 1;
+  if (n < 1) n = 1;
+  const int64_t cap = 2 * int64_t(num_cus);
+  return int(n > cap ? cap : n);
+}
+
+size_t pa_decode_workspace_bytes(int num_seqs, int num_q_heads, int head_dim_v, int num_splits) {
+  if (num_seqs < 0 || num_q_heads < 0 || head_dim_v < 0 || num_splits < 0) return 0;
+  const unsigned __int128 b = (unsigned __int128)num_seqs * (unsigned)num_q_heads *
+                              (unsigned)num_splits * ((unsigned)head_dim_v + 1u) * 4u;
+  if (b > (unsigned __int128)SIZE_MAX) return 0;
+  return size_t(b);
+}
+
+int pa_mla_num_kv_splits(int num_seqs, int max_seq_len, int num_cus) {
+  if (num_cus < 1) num_cus = 1;
+  if (num_seqs < 1) num_seqs = 1;
+  const int cap = pa_num_kv_splits(max_seq_len, num_cus);
+  int64_t want = (2 * int64_t(num_cus) + num_seqs - 1) / num_seqs;
+  const int64_t pages = (int64_t(max_seq_len) + 63) / 64;
+  if (want > pages) want = pages;
+  if (want > cap) want = cap;
+  if (want < 1) want = 1;
+  return int(want);
+}
+
+int pa_device_num_cus(void) {
+  int c = g_cus_cache.load(std::memory_order_relaxed);
+  if (c > 0) return c;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return -1;
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    return -1;
+  g_cus_cache.store(n, std::memory_order_relaxed);
+  return n;
+}
+
+const char* pa_last_error(void) { return g_err; }
+
+// ---------------------------------------------------------------------------
+pa_status_t pa_cache_write(pa_layout_t layout, pa_dtype_t dtype,
+                           const void* k, int64_t k_token_stride,
+                           const void* v, int64_t v_token_stride,
+                           void* kv_cache, int64_t num_blocks, int block_size,
+                           int num_kv_heads, int head_dim,
+                           const int64_t* slot_mapping, int num_tokens,
+                           hipStream_t stream) {
+  PA_REQUIRE(num_tokens >= 0, PA_ERR_INVALID, "num_tokens must be >= 0");
+  PA_REQUIRE(dtype == PA_F32 || dtype == PA_BF16, PA_ERR_INVALID, "unknown dtype %d", int(dtype));
+  PA_REQUIRE(num_blocks > 0, PA_ERR_INVALID, "num_blocks must be > 0");
+  PA_REQUIRE(block_size > 0 && block_size % 16 == 0, PA_ERR_INVALID,
+             "block_size must be a positive multiple of 16 (got %d)", block_size);
+  PA_REQUIRE(head_dim > 0 && num_kv_heads > 0, PA_ERR_INVALID, "head_dim and num_kv_heads must be > 0");
+  if (num_tokens == 0) return ok();
+  PA_REQUIRE(k && v && kv_cache && slot_mapping, PA_ERR_INVALID, "k, v, kv_cache and slot_mapping must be non-null");
+  if (layout == PA_LAYOUT_KV) {
+    PA_REQUIRE(k_token_stride >= int64_t(num_kv_heads) * head_dim &&
+               v_token_stride >= int64_t(num_kv_heads) * head_dim, PA_ERR_INVALID,
+               "token strides must be >= num_kv_heads * head_dim");
+    pa::CacheWriteKV a{k, k_token_stride, v, v_token_stride, kv_cache, num_blocks, block_size,
+                       num_kv_heads, head_dim, slot_mapping, num_tokens, dtype == PA_BF16 ? 2 : 4};
+    hipError_t e = pa::launch_cache_write_kv(a, stream);
+    if (e != hipSuccess) return hip_fail(e, "cache_write_kv launch");
+    return ok();
+  }
+  if (layout == PA_LAYOUT_MLA) {
+    PA_REQUIRE(dtype == PA_BF16, PA_ERR_UNSUPPORTED, "the MLA layout is bf16 only");
+    PA_REQUIRE(num_kv_heads == 1, PA_ERR_INVALID, "the MLA layout has one KV head");
+    PA_REQUIRE(head_dim > 64, PA_ERR_INVALID, "MLA head_dim must be kv_lora_rank + 64");
+    const int rank = head_dim - 64;
+    PA_REQUIRE(k_token_stride >= rank && v_token_stride >= 64, PA_ERR_INVALID,
+               "token strides must cover kv_lora_rank / rope_dim");
+    pa::CacheWriteMLA a{k, k_token_stride, v, v_token_stride, kv_cache, num_blocks, block_size,
+                        rank, 64, slot_mapping, num_tokens};
+    hipError_t e = pa::launch_cache_write_mla(a, stream);
+    if (e != hipSuccess) return hip_fail(e, "cache_write_mla launch");
+    return ok();
+  }
+  return fail(PA_ERR_INVALID, "unknown layout %d", int(layout));
+}
+
+// ---------------------------------------------------------------------------
+pa_status_t pa_decode(pa_dtype_t dtype,
+                      const void* q, const void* k, const void* v,
+                      void* kv_cache, int64_t num_blocks, int block_size,
+                      const int32_t* block_table, int max_blocks_per_seq,
+                      const int64_t* slot_mapping,
+                      const int32_t* seq_lens, int num_seqs, int max_seq_len,
+                      int num_q_heads, int num_kv_heads, int head_dim,
+                      float scale, int num_splits,
+                      void* workspace, size_t workspace_bytes,
+                      void* out, float* lse, hipStream_t stream) {
+  PA_REQUIRE(dtype == PA_F32 || dtype == PA_BF16, PA_ERR_INVALID, "unknown dtype %d", int(dtype));
+  pa_status_t st = check_common_cache(num_blocks, block_size, block_table, max_blocks_per_seq,
+                                      seq_lens, num_seqs, max_seq_len);
+  if (st != PA_OK) return st;
+  PA_REQUIRE(num_q_heads > 0 && num_kv_heads > 0 && num_q_heads % num_kv_heads == 0,
+             PA_ERR_INVALID, "num_q_heads (%d) must be a positive multiple of num_kv_heads (%d)",
+             num_q_heads, num_kv_heads);
+  PA_REQUIRE(head_dim > 0 && head_dim % 8 == 0 && head_dim <= 256, PA_ERR_INVALID,
+             "head_dim must be a multiple of 8 in [8, 256] (got %d)", head_dim);
+  PA_REQUIRE(head_dim == 128, PA_ERR_UNSUPPORTED, "decode supports head_dim 128 (got %d)", head_dim);
+  PA_REQUIRE(is_pow2_group(num_q_heads / num_kv_heads), PA_ERR_UNSUPPORTED,
+             "decode supports num_q_heads / num_kv_heads in {1, 2, 4, 8} (got %d)",
+             num_q_heads / num_kv_heads);
+  PA_REQUIRE(num_splits >= 0, PA_ERR_INVALID, "num_splits must be >= 0");
+  PA_REQUIRE((k == nullptr) == (v == nullptr), PA_ERR_INVALID, "k and v must both be given or both NULL");
+  PA_REQUIRE(k == nullptr || slot_mapping != nullptr, PA_ERR_INVALID, "k/v given without slot_mapping");
+  PA_REQUIRE(slot_mapping == nullptr || k != nullptr, PA_ERR_INVALID, "slot_mapping given without k/v");
+  if (num_seqs == 0) return ok();
+  PA_REQUIRE(q && kv_cache && out, PA_ERR_INVALID, "q, kv_cache and out must be non-null");
+
+  int n = num_splits;
+  if (n == 0) {
+    const int cus = pa_device_num_cus();
+    if (cus <= 0) return fail(PA_ERR_HIP, "cannot query the device's compute units");
+    n = pa_num_kv_splits(max_seq_len, cus);
+  }
+  const int P = split_tokens_for(max_seq_len, n, block_size);
+  const int used = used_splits(max_seq_len, P);  // <= n
+  if (used > 1) {
+    const size_t need = pa_decode_workspace_bytes(num_seqs, num_q_heads, head_dim, n);
+    PA_REQUIRE(workspace != nullptr && workspace_bytes >= need, PA_ERR_WORKSPACE,
+               "workspace of %zu bytes needed for %d splits (got %zu)", need, n, workspace_bytes);
+  }
+
+  if (k) {
+    pa::CacheWriteKV w{k, int64_t(num_kv_heads) * head_dim, v, int64_t(num_kv_heads) * head_dim,
+                       kv_cache, num_blocks, block_size, num_kv_heads, head_dim, slot_mapping,
+                       num_seqs, dtype == PA_BF16 ? 2 : 4};
+    hipError_t e = pa::launch_cache_write_kv(w, stream);
+    if (e != hipSuccess) return hip_fail(e, "cache_write_kv launch");
+  }
+  pa::DecodeGQA d{};
+  d.bf16 = dtype == PA_BF16;
+  d.q = q;
+  d.cache = kv_cache;
+  d.num_blocks = num_blocks;
+  d.block_size = block_size;
+  d.block_table = block_table;
+  d.max_blocks = max_blocks_per_seq;
+  d.seq_lens = seq_lens;
+  d.num_seqs = num_seqs;
+  d.num_q_heads = num_q_heads;
+  d.num_kv_heads = num_kv_heads;
+  d.head_dim = head_dim;
+  d.scale = scale;
+  d.num_splits = used;
+  d.split_tokens = P;
+  d.part = static_cast<float*>(workspace);
+  d.out = out;
+  d.lse = lse;
+  hipError_t e = pa::launch_decode_gqa(d, stream);
+  if (e != hipSuccess) return hip_fail(e, "decode launch");
+  pa::LseMerge m{static_cast<const float*>(workspace), num_seqs, num_q_heads, used, head_dim,
+                 dtype == PA_BF16, out, lse, seq_lens, P, max_blocks_per_seq * block_size};
+  e = pa::launch_lse_merge(m, stream);
+  if (e != hipSuccess) return hip_fail(e, "merge launch");
+  return ok();
+}
+
+// ---------------------------------------------------------------------------
+pa_status_t pa_prefill_varlen(pa_dtype_t dtype,
+                              const void* q, const void* k, const void* v,
+                              void* kv_cache, int64_t num_blocks, int block_size,
+                              const int32_t* block_table, int max_blocks_per_seq,
+                              const int64_t* slot_mapping,
+                              const int32_t* query_start_loc,
+                              const int32_t* seq_lens, int num_seqs,
+                              int num_tokens, int max_query_len, int max_seq_len,
+                              int num_q_heads, int num_kv_heads, int head_dim,
+                              float scale, int causal,
+                              void* out, float* lse, hipStream_t stream) {
+  PA_REQUIRE(dtype == PA_F32 || dtype == PA_BF16, PA_ERR_INVALID, "unknown dtype %d", int(dtype));
+  pa_status_t st = check_common_cache(num_blocks, block_size, block_table, max_blocks_per_seq,
+                                      seq_lens, num_seqs, max_seq_len);
+  if (st != PA_OK) return st;
+  PA_REQUIRE(num_tokens >= 0 && max_query_len >= 0, PA_ERR_INVALID, "num_tokens and max_query_len must be >= 0");
+  PA_REQUIRE(max_query_len <= num_tokens || num_seqs == 0, PA_ERR_INVALID, "max_query_len exceeds num_tokens");
+  PA_REQUIRE(num_q_heads > 0 && num_kv_heads > 0 && num_q_heads % num_kv_heads == 0,
+             PA_ERR_INVALID, "num_q_heads (%d) must be a positive multiple of num_kv_heads (%d)",
+             num_q_heads, num_kv_heads);
+  PA_REQUIRE(head_dim > 0 && head_dim % 8 == 0 && head_dim <= 256, PA_ERR_INVALID,
+             "head_dim must be a multiple of 8 in [8, 256] (got %d)", head_dim);
+  PA_REQUIRE(causal == 0 || causal == 1, PA_ERR_INVALID, "causal must be 0 or 1");
+  PA_REQUIRE(dtype == PA_BF16, PA_ERR_UNSUPPORTED, "prefill supports bf16 only");
+  PA_REQUIRE(head_dim == 128, PA_ERR_UNSUPPORTED, "prefill supports head_dim 128 (got %d)", head_dim);
+  PA_REQUIRE(is_pow2_group(num_q_heads / num_kv_heads), PA_ERR_UNSUPPORTED,
+             "prefill supports num_q_heads / num_kv_heads in {1, 2, 4, 8}");
+  PA_REQUIRE((k == nullptr) == (v == nullptr), PA_ERR_INVALID, "k and v must both be given or both NULL");
+  PA_REQUIRE(k == nullptr || slot_mapping != nullptr, PA_ERR_INVALID, "k/v given without slot_mapping");
+  PA_REQUIRE(slot_mapping == nullptr || k != nullptr, PA_ERR_INVALID, "slot_mapping given without k/v");
+  if (num_seqs == 0 || num_tokens == 0) return ok();
+  PA_REQUIRE(q && kv_cache && out && query_start_loc, PA_ERR_INVALID,
+             "q, kv_cache, out and query_start_loc must be non-null");
+  if (k) {
+    pa::CacheWriteKV w{k, int64_t(num_kv_heads) * head_dim, v, int64_t(num_kv_heads) * head_dim,
+                       kv_cache, num_blocks, block_size, num_kv_heads, head_dim, slot_mapping,
+                       num_tokens, 2};
+    hipError_t e = pa::launch_cache_write_kv(w, stream);
+    if (e != hipSuccess) return hip_fail(e, "cache_write_kv launch");
+  }
+  pa::PrefillVarlen p{q, kv_cache, num_blocks, block_size, block_table, max_blocks_per_seq,
+                      query_start_loc, seq_lens, num_seqs, num_tokens, max_query_len, max_seq_len,
+                      num_q_heads, num_kv_heads, head_dim, scale, causal, out, lse};
+  hipError_t e = pa::launch_prefill_varlen(p, stream);
+  if (e == hipErrorNotSupported) return fail(PA_ERR_UNSUPPORTED, "prefill kernel not built");
+  if (e != hipSuccess) return hip_fail(e, "prefill launch");
+  return ok();
+}
+
+// ---------------------------------------------------------------------------
+pa_status_t pa_mla_decode(const void* q_nope, int64_t qn_stride_b, int64_t qn_stride_h,
+                          const void* q_pe, int64_t qp_stride_b, int64_t qp_stride_h,
+                          const void* kv_c, const void* k_pe,
+                          void* kv_cache, int64_t num_blocks, int block_size,
+                          const int32_t* block_table, int max_blocks_per_seq,
+                          const int64_t* slot_mapping,
+                          const int32_t* seq_lens, int num_seqs, int max_seq_len,
+                          int num_heads, int kv_lora_rank, int rope_dim,
+                          float scale, int num_splits,
+                          void* workspace, size_t workspace_bytes,
+                          void* out, float* lse, hipStream_t stream) {
+  pa_status_t st = check_common_cache(num_blocks, block_size, block_table, max_blocks_per_seq,
+                                      seq_lens, num_seqs, max_seq_len);
+  if (st != PA_OK) return st;
+  PA_REQUIRE(kv_lora_rank > 0 && rope_dim > 0, PA_ERR_INVALID, "kv_lora_rank and rope_dim must be > 0");
+  PA_REQUIRE(kv_lora_rank == 512 && rope_dim == 64, PA_ERR_UNSUPPORTED,
+             "MLA decode supports kv_lora_rank 512 + rope_dim 64 (got %d + %d)", kv_lora_rank, rope_dim);
+  PA_REQUIRE(num_heads > 0, PA_ERR_INVALID, "num_heads must be > 0");
+  PA_REQUIRE(num_heads % 16 == 0 && num_heads <= 128, PA_ERR_UNSUPPORTED,
+             "MLA decode supports num_heads a multiple of 16 up to 128 (got %d)", num_heads);
+  PA_REQUIRE(qn_stride_h >= kv_lora_rank && qp_stride_h >= rope_dim &&
+             qn_stride_b >= qn_stride_h * num_heads && qp_stride_b >= qp_stride_h * num_heads,
+             PA_ERR_INVALID, "q strides do not describe [num_seqs, num_heads, dim] rows");
+  PA_REQUIRE(qn_stride_h % 8 == 0 && qp_stride_h % 8 == 0 && qn_stride_b % 8 == 0 &&
+             qp_stride_b % 8 == 0, PA_ERR_INVALID, "q strides must be multiples of 8 elements");
+  PA_REQUIRE(num_splits >= 0, PA_ERR_INVALID, "num_splits must be >= 0");
+  PA_REQUIRE((kv_c == nullptr) == (k_pe == nullptr), PA_ERR_INVALID,
+             "kv_c and k_pe must both be given or both NULL");
+  PA_REQUIRE(kv_c == nullptr || slot_mapping != nullptr, PA_ERR_INVALID, "kv_c/k_pe given without slot_mapping");
+  PA_REQUIRE(slot_mapping == nullptr || kv_c != nullptr, PA_ERR_INVALID, "slot_mapping given without kv_c/k_pe");
+  if (num_seqs == 0) return ok();
+  PA_REQUIRE(q_nope && q_pe && kv_cache && out, PA_ERR_INVALID, "q_nope, q_pe, kv_cache and out must be non-null");
+  int n = num_splits;
+  if (n == 0) {
+    const int cus = pa_device_num_cus();
+    if (cus <= 0) return fail(PA_ERR_HIP, "cannot query the device's compute units");
+    n = pa_mla_num_kv_splits(num_seqs, max_seq_len, cus);
+  }
+  const int P = split_tokens_for(max_seq_len, n, block_size);
+  const int used = used_splits(max_seq_len, P);
+  if (used > 1) {
+    const size_t need = pa_decode_workspace_bytes(num_seqs, num_heads, kv_lora_rank, n);
+    PA_REQUIRE(workspace != nullptr && workspace_bytes >= need, PA_ERR_WORKSPACE,
+               "workspace of %zu bytes needed for %d splits (got %zu)", need, n, workspace_bytes);
+  }
+  if (kv_c) {
+    pa::CacheWriteMLA w{kv_c, kv_lora_rank, k_pe, rope_dim, kv_cache, num_blocks, block_size,
+                        kv_lora_rank, rope_dim, slot_mapping, num_seqs};
+    hipError_t e = pa::launch_cache_write_mla(w, stream);
+    if (e != hipSuccess) return hip_fail(e, "cache_write_mla launch");
+  }
+  pa::MlaDecode d{q_nope, qn_stride_b, qn_stride_h, q_pe, qp_stride_b, qp_stride_h,
+                  kv_cache, num_blocks, block_size, block_table, max_blocks_per_seq,
+                  seq_lens, num_seqs, num_heads, kv_lora_rank, rope_dim, scale,
+                  used, P, static_cast<float*>(workspace), out, lse};
+  hipError_t e = pa::launch_mla_decode(d, stream);
+  if (e == hipErrorNotSupported) return fail(PA_ERR_UNSUPPORTED, "MLA kernel not built");
+  if (e != hipSuccess) return hip_fail(e, "MLA decode launch");
+  pa::LseMerge m{static_cast<const float*>(workspace), num_seqs, num_heads, used, kv_lora_rank,
+                 1, out, lse, seq_lens, P, max_blocks_per_seq * block_size};
+  e = pa::launch_lse_merge(m, stream);
+  if (e != hipSuccess) return hip_fail(e, "merge launch");
+  return ok();
+}
+
+// ---------------------------------------------------------------------------
+pa_status_t pa_lse_merge(const float* part, int num_rows, int num_heads,
+                         int num_splits, int head_dim_v, pa_dtype_t out_dtype,
+                         void* out, float* lse, hipStream_t stream) {
+  PA_REQUIRE(num_rows >= 0 && num_heads >= 0, PA_ERR_INVALID, "num_rows and num_heads must be >= 0");
+  PA_REQUIRE(num_splits >= 1, PA_ERR_INVALID, "num_splits must be >= 1");
+  PA_REQUIRE(head_dim_v >= 1 && head_dim_v <= 1024, PA_ERR_UNSUPPORTED,
+             "head_dim_v must be in [1, 1024] (got %d)", head_dim_v);
+  PA_REQUIRE(out_dtype == PA_F32 || out_dtype == PA_BF16, PA_ERR_INVALID, "unknown dtype %d", int(out_dtype));
+  if (num_rows == 0 || num_heads == 0) return ok();
+  PA_REQUIRE(part && out, PA_ERR_INVALID, "part and out must be non-null");
+  pa::LseMerge m{part, num_rows, num_heads, num_splits, head_dim_v, out_dtype == PA_BF16,
+                 out, lse, nullptr, 0, 0};
+  hipError_t e = pa::launch_lse_merge(m, stream);
+  if (e != hipSuccess) return hip_fail(e, "merge launch");
+  return ok();
+}
+
+}  // extern "C"

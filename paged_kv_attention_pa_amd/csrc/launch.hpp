@@ -1,0 +1,88 @@
+// Host-side launchers of the gfx950 kernels.  The C entry points in api.cpp
+// validate arguments and then call these; each launcher only sizes a grid and
+// enqueues on the given stream.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pa {
+
+// ----------------------------------------------------------- cache write
+struct CacheWriteKV {
+  const void* k; int64_t k_stride;   // elements between tokens
+  const void* v; int64_t v_stride;
+  void* cache; int64_t num_blocks; int block_size; int num_kv_heads; int head_dim;
+  const int64_t* slots; int num_tokens;
+  int elem_bytes;                    // 2 (bf16) or 4 (fp32)
+};
+hipError_t launch_cache_write_kv(const CacheWriteKV& a, hipStream_t s);
+
+struct CacheWriteMLA {
+  const void* kv_c; int64_t c_stride;
+  const void* k_pe; int64_t p_stride;
+  void* cache; int64_t num_blocks; int block_size; int rank; int rope;
+  const int64_t* slots; int num_tokens;
+};
+hipError_t launch_cache_write_mla(const CacheWriteMLA& a, hipStream_t s);
+
+// ---------------------------------------------------------------- decode
+struct DecodeGQA {
+  int bf16;                      // 1: bf16 storage, 0: fp32
+  const void* q;                 // [B, Hq, D]
+  const void* cache;             // [nb, 2, bs, Hkv, D]
+  int64_t num_blocks; int block_size;
+  const int32_t* block_table; int max_blocks;
+  const int32_t* seq_lens; int num_seqs;
+  int num_q_heads; int num_kv_heads; int head_dim;
+  float scale;
+  int num_splits; int split_tokens;  // P: tokens per split (multiple of block_size)
+  float* part;                   // [B, Hq, S, D+1] (unused when num_splits == 1)
+  void* out; float* lse;         // final outputs (written directly when a
+                                 // request needs only one split)
+  // Optional fused new-token write: when non-null, the work unit that owns
+  // a request's last position stores k_new/v_new there and uses them.
+  const void* k_new; const void* v_new; const int64_t* slots;
+};
+hipError_t launch_decode_gqa(const DecodeGQA& a, hipStream_t s);
+
+// Merge of split partials.  seq_lens/split_tokens: when seq_lens is non-null,
+// request r only has ceil(seq_lens[r] / split_tokens) valid splits and rows
+// with a single valid split are skipped (already final).
+struct LseMerge {
+  const float* part; int num_rows; int num_heads; int num_splits; int head_dim_v;
+  int out_bf16; void* out; float* lse;
+  const int32_t* seq_lens; int split_tokens; int max_tokens;
+};
+hipError_t launch_lse_merge(const LseMerge& a, hipStream_t s);
+
+// ------------------------------------------------------------------- MLA
+struct MlaDecode {
+  const void* q_nope; int64_t qn_sb, qn_sh;
+  const void* q_pe; int64_t qp_sb, qp_sh;
+  const void* cache; int64_t num_blocks; int block_size;
+  const int32_t* block_table; int max_blocks;
+  const int32_t* seq_lens; int num_seqs;
+  int num_heads; int rank; int rope;
+  float scale;
+  int num_splits; int split_tokens;
+  float* part; void* out; float* lse;
+};
+hipError_t launch_mla_decode(const MlaDecode& a, hipStream_t s);
+
+// --------------------------------------------------------------- prefill
+struct PrefillVarlen {
+  const void* q;                  // [T, Hq, D]
+  const void* cache;
+  int64_t num_blocks; int block_size;
+  const int32_t* block_table; int max_blocks;
+  const int32_t* query_start_loc; const int32_t* seq_lens;
+  int num_seqs; int num_tokens; int max_query_len; int max_seq_len;
+  int num_q_heads; int num_kv_heads; int head_dim;
+  float scale; int causal;
+  void* out; float* lse;
+};
+hipError_t launch_prefill_varlen(const PrefillVarlen& a, hipStream_t s);
+
+}  // namespace pa

@@ -1,0 +1,95 @@
+// Device-side helpers shared by the gfx950 kernels: bf16 packing, base-2
+// exponentials, wave64 DPP reductions and 16-byte memory access.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+typedef __attribute__((ext_vector_type(16))) float f32x16_t;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+// Finite stand-in for "no key seen yet": exp2(x - kNoMax) never produces NaN.
+constexpr float kNoMax = -1.0e30f;
+
+// ---------------------------------------------------------------- bf16 bits
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
+
+// fp32 -> bf16, round to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return uint16_t((u >> 16) | 0x0040u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return uint16_t(u >> 16);
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return uint32_t(f32_to_bf16(lo)) | (uint32_t(f32_to_bf16(hi)) << 16);
+}
+
+// ------------------------------------------------------------- arithmetic
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// Two bf16 products accumulated in fp32: a.lo*b.lo + a.hi*b.hi + c.
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                         __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+// ----------------------------------------------------------- DPP exchange
+// dpp_ctrl encodings (GCN/CDNA): quad_perm selectors, row mirror, half mirror.
+constexpr int kDppQuadXor1 = 0xB1;   // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;   // quad_perm [2,3,0,1]
+constexpr int kDppRowMirror = 0x140; // lane i <-> 15 - i within a row of 16
+constexpr int kDppRowHalfMirror = 0x141; // lane i <-> 7 - i within each 8
+
+template <int kCtrl>
+__device__ __forceinline__ float dpp(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+      0, __builtin_bit_cast(int, x), kCtrl, 0xf, 0xf, false));
+}
+
+// Sum / max over each row of 16 lanes; every lane of the row gets the result.
+__device__ __forceinline__ float row16_sum(float x) {
+  x += dpp<kDppQuadXor1>(x);
+  x += dpp<kDppQuadXor2>(x);
+  x += dpp<kDppRowHalfMirror>(x);
+  x += dpp<kDppRowMirror>(x);
+  return x;
+}
+__device__ __forceinline__ float row16_max(float x) {
+  x = fmaxf(x, dpp<kDppQuadXor1>(x));
+  x = fmaxf(x, dpp<kDppQuadXor2>(x));
+  x = fmaxf(x, dpp<kDppRowHalfMirror>(x));
+  x = fmaxf(x, dpp<kDppRowMirror>(x));
+  return x;
+}
+
+// Exchange with lane ^ 16 / ^ 32 (crosses DPP rows; routed through the LDS
+// crossbar by ds_bpermute, no LDS allocation).
+__device__ __forceinline__ float lane_xor(float x, int m) {
+  int lane = __lane_id();
+  return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(
+      (lane ^ m) << 2, __builtin_bit_cast(int, x)));
+}
+
+// ------------------------------------------------------------ 16-B access
+__device__ __forceinline__ u32x4_t load16(const void* p) {
+  return *reinterpret_cast<const u32x4_t*>(p);
+}
+__device__ __forceinline__ u32x4_t load16_stream(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+}
+__device__ __forceinline__ void store16(void* p, u32x4_t v) {
+  *reinterpret_cast<u32x4_t*>(p) = v;
+}
+
+}  // namespace pa

@@ -1,0 +1,175 @@
+"""The C ABI on the host: the library loads, exports every symbol include/pa.h
+declares, its integer helpers match the oracle bit for bit, and argument
+validation rejects bad calls before anything reaches the GPU (no compute calls
+here; these run without a GPU)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+import oracle.pa_oracle as O
+import paged_kv_attention_pa_amd as pa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pa.h")
+
+INVALID, UNSUPPORTED, WORKSPACE = 1, 2, 3
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(pa.library_path()):
+        pytest.fail("libpa.so is not built: run `python -m paged_kv_attention_pa_amd.build`")
+    return pa.library()
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pa_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_five_operations():
+    names = _declared()
+    for op in ("pa_cache_write", "pa_decode", "pa_prefill_varlen", "pa_mla_decode", "pa_lse_merge"):
+        assert op in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    names = _declared()
+    assert set(names) == set(pa.EXPORTED_SYMBOLS), (names, pa.EXPORTED_SYMBOLS)
+    for n in names:
+        assert hasattr(lib, n), n
+    # the exports are C symbols (no C++ mangling)
+    out = os.popen(f"nm -D --defined-only {pa.library_path()}").read()
+    for n in names:
+        assert re.search(rf"\bT {n}$", out, flags=re.M), n
+
+
+@pytest.mark.parametrize("max_len", [0, 1, 16, 511, 512, 513, 4096, 8190, 8192, 131072, 10 ** 6])
+@pytest.mark.parametrize("cus", [1, 2, 80, 256, 304])
+def test_num_kv_splits_matches_oracle(lib, max_len, cus):
+    assert pa.num_kv_splits(max_len, cus) == O.num_kv_splits(max_len, cus)
+
+
+def test_long_context_split_count(lib):
+    # 131072 keys on 256 compute units: 256 splits (cap 512 not reached)
+    assert pa.num_kv_splits(131072, 256) == 256
+
+
+def test_workspace_bytes(lib):
+    assert pa.decode_workspace_bytes(64, 32, 128, 16) == 64 * 32 * 16 * 129 * 4
+    assert pa.decode_workspace_bytes(4, 64, 128, 256) == 4 * 64 * 256 * 129 * 4
+    assert pa.decode_workspace_bytes(-1, 32, 128, 16) == 0
+
+
+def test_mla_split_helper(lib):
+    for B, L, cus in [(128, 8192, 256), (1, 8192, 256), (4, 100, 256), (300, 1000, 256)]:
+        n = pa.mla_num_kv_splits(B, L, cus)
+        assert 1 <= n <= max(1, pa.num_kv_splits(L, cus))
+        assert n <= max(1, -(-L // 64))
+
+
+def _null():
+    return None
+
+
+def _decode(lib, **kw):
+    args = dict(dtype=1, q=1 << 20, k=None, v=None, cache=1 << 21, nb=100, bs=16, table=1 << 22,
+                maxb=64, slots=None, seq=1 << 23, B=4, maxlen=1000, hq=32, hkv=8, d=128,
+                scale=0.1, splits=1, ws=None, wsb=0, out=1 << 24, lse=None)
+    args.update(kw)
+    a = args
+    return lib.pa_decode(a["dtype"], a["q"], a["k"], a["v"], a["cache"], a["nb"], a["bs"],
+                         a["table"], a["maxb"], a["slots"], a["seq"], a["B"], a["maxlen"],
+                         a["hq"], a["hkv"], a["d"], a["scale"], a["splits"], a["ws"], a["wsb"],
+                         a["out"], a["lse"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(bs=8), INVALID),                  # block size not a multiple of 16
+    (dict(bs=0), INVALID),
+    (dict(hq=30, hkv=8), INVALID),          # Hq % Hkv != 0
+    (dict(d=96), UNSUPPORTED),              # head_dim outside this build
+    (dict(d=100), INVALID),                 # not a multiple of 8
+    (dict(hq=96, hkv=8), UNSUPPORTED),      # group 12
+    (dict(q=None), INVALID),
+    (dict(out=None), INVALID),
+    (dict(table=None), INVALID),
+    (dict(k=1 << 25), INVALID),             # k without v / slots
+    (dict(k=1 << 25, v=1 << 26), INVALID),  # k, v without slots
+    (dict(slots=1 << 27), INVALID),         # slots without k, v
+    (dict(maxlen=2000, maxb=64), INVALID),  # longer than the table can address
+    (dict(dtype=7), INVALID),
+    (dict(splits=-1), INVALID),
+    (dict(splits=4, ws=None), WORKSPACE),   # split path needs a workspace
+    (dict(splits=4, ws=1 << 28, wsb=100), WORKSPACE),
+])
+def test_decode_validation(lib, kw, status):
+    assert _decode(lib, **kw) == status
+    assert pa.last_error() != ""
+
+
+def test_decode_empty_batch_is_noop(lib):
+    assert _decode(lib, B=0, q=None, out=None) == 0
+    assert pa.last_error() == ""
+
+
+def test_cache_write_validation(lib):
+    f = lib.pa_cache_write
+    assert f(0, 1, 1, 1024, 2, 1024, 3, 10, 16, 8, 128, 4, 0, None) == 0     # zero tokens
+    assert f(0, 1, 1, 1024, 2, 1024, 3, 10, 12, 8, 128, 4, 5, None) == INVALID  # block 12
+    assert f(0, 1, None, 1024, 2, 1024, 3, 10, 16, 8, 128, 4, 5, None) == INVALID
+    assert f(0, 1, 1, 100, 2, 1024, 3, 10, 16, 8, 128, 4, 5, None) == INVALID  # short stride
+    assert f(1, 0, 1, 512, 2, 64, 3, 10, 64, 1, 576, 4, 5, None) == UNSUPPORTED  # MLA fp32
+    assert f(1, 1, 1, 512, 2, 64, 3, 10, 64, 2, 576, 4, 5, None) == INVALID  # MLA 2 heads
+    assert f(9, 1, 1, 512, 2, 64, 3, 10, 64, 1, 576, 4, 5, None) == INVALID  # bad layout
+
+
+def test_prefill_validation(lib):
+    f = lib.pa_prefill_varlen
+    base = [1, 1, None, None, 2, 100, 16, 3, 64, None, 4, 5, 2, 100, 50, 300,
+            32, 8, 128, 0.1, 1, 6, None, None]
+    bad = list(base); bad[0] = 0                   # fp32 prefill
+    assert f(*bad) == UNSUPPORTED
+    bad = list(base); bad[20] = 2                  # causal flag
+    assert f(*bad) == INVALID
+    bad = list(base); bad[14] = 200                # max_query_len > num_tokens
+    assert f(*bad) == INVALID
+    bad = list(base); bad[10] = None               # query_start_loc
+    assert f(*bad) == INVALID
+    bad = list(base); bad[16] = 20                 # 20 % 8
+    assert f(*bad) == INVALID
+
+
+def test_mla_validation(lib):
+    f = lib.pa_mla_decode
+    base = [1, 128 * 512, 512, 2, 128 * 64, 64, None, None, 3, 100, 64, 4, 200, None, 5, 8,
+            8192, 128, 512, 64, 0.07, 1, None, 0, 6, None, None]
+    bad = list(base); bad[18] = 320                # head 320 not built
+    assert f(*bad) == UNSUPPORTED
+    bad = list(base); bad[17] = 24                 # heads not a multiple of 16
+    assert f(*bad) == UNSUPPORTED
+    bad = list(base); bad[2] = 100                 # q_nope head stride < 512
+    assert f(*bad) == INVALID
+    bad = list(base); bad[6] = 7                   # kv_c without k_pe
+    assert f(*bad) == INVALID
+    bad = list(base); bad[21] = 4                  # split without workspace
+    assert f(*bad) == WORKSPACE
+
+
+def test_lse_merge_validation(lib):
+    f = lib.pa_lse_merge
+    assert f(1, 4, 8, 0, 128, 1, 2, None, None) == INVALID        # zero splits
+    assert f(1, 4, 8, 2, 2048, 1, 2, None, None) == UNSUPPORTED   # Dv too wide
+    assert f(None, 4, 8, 2, 128, 1, 2, None, None) == INVALID
+    assert f(None, 0, 8, 2, 128, 1, 2, None, None) == 0           # nothing to do
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    import paged_kv_attention_pa_amd._binding as b
+    monkeypatch.setattr(b, "_lib", None)
+    monkeypatch.setattr(b, "_LIB_PATH", str(tmp_path / "libpa.so"))
+    with pytest.raises(pa.PaError):
+        b.library()
