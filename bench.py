@@ -1,0 +1,370 @@
+#!/usr/bin/env python3
+"""Throughput of the paged-attention hot path on one MI355X (gfx950).
+
+A step is one pass of the whole path over one synthetic batch: the new-token
+cache write, the attention kernel(s) and, for split-KV decode, the LSE merge.
+The headline line measures the Llama-3-8B-shaped GQA decode (64 requests,
+seq_len U[512, 8192], 32 q / 8 kv heads, d=128, bf16, block 16) in HBM GB/s;
+the four other workloads are measured the same way and reported under
+"workloads".  Inputs are generated on the host by ``workloads.py`` (seeded),
+uploaded once, and resident in HBM before any timed region.
+
+Timing: W untimed warm-up steps, then K steps bracketed by
+torch.cuda.synchronize() (wall clock); the dominant kernel of each workload
+is also timed alone with HIP events on the stream it is launched on (the
+library launches on torch's current stream).  The CPU baseline is the float64
+oracle on a bounded sample of the headline workload, on one host thread.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only NAME]
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+HEADLINE = "llama3_8b_gqa_decode_bf16"
+METRIC = "paged decode HBM GB/s (% of peak); prefill & MLA TFLOP/s (% of MFMA peak)"
+CSRC = os.path.join(ROOT, "paged_kv_attention_pa_amd", "csrc")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_source_sha(fname: str) -> str:
+    h = hashlib.sha256()
+    for f in (fname, "pa_device.hpp", "launch.hpp"):
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+# --------------------------------------------------------------------------
+# one workload: inputs on the device, the step, the dominant kernel alone
+# --------------------------------------------------------------------------
+
+class Case:
+    def __init__(self, name, step, kernel, step_bytes, step_flops, kern_bytes, kern_flops,
+                 bound, kernel_name, source, info):
+        self.name, self.step, self.kernel = name, step, kernel
+        self.step_bytes, self.step_flops = step_bytes, step_flops
+        self.kern_bytes, self.kern_flops = kern_bytes, kern_flops
+        self.bound, self.kernel_name, self.source, self.info = bound, kernel_name, source, info
+
+
+def _dev(a):
+    import numpy as np
+    import torch
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
+    return torch.from_numpy(a).cuda()
+
+
+def gqa_decode_case(b, num_splits, name):
+    import torch
+    import paged_kv_attention_pa_amd as pa
+    import workloads as W
+    cache, q = _dev(b.cache), _dev(b.q)
+    bt, sl = _dev(b.block_table), _dev(b.seq_lens)
+    kn, vn, sm = _dev(b.k_new), _dev(b.v_new), _dev(b.slot_mapping)
+    n = num_splits or pa.num_kv_splits(b.max_seq_len, pa.device_num_cus())
+    ws = torch.empty(max(1, pa.decode_workspace_bytes(b.num_seqs, b.num_q_heads, b.head_dim, n) // 4),
+                     dtype=torch.float32, device="cuda")
+    out = torch.empty_like(q)
+    lse = torch.empty(b.q.shape[:2], dtype=torch.float32, device="cuda")
+
+    def step():
+        pa.decode(q, cache, bt, sl, b.max_seq_len, b.scale, k=kn, v=vn, slot_mapping=sm,
+                  num_splits=n, workspace=ws, out=out, lse=lse)
+
+    def kernel():
+        pa.decode(q, cache, bt, sl, b.max_seq_len, b.scale, num_splits=n, workspace=ws,
+                  stage1_only=True)
+
+    by = W.gqa_bytes(b)
+    kb = by["kv"] + by["q"] + by["meta"] - b.num_tokens * 8   # split kernel: KV, q, table walk
+    fl = W.gqa_flops(b)
+    kname = "decode_split_kernel<%s, %d>" % ("true" if b.dtype == W.BF16 else "false",
+                                             b.num_q_heads // b.num_kv_heads)
+    info = {"num_seqs": b.num_seqs, "num_q_heads": b.num_q_heads, "num_kv_heads": b.num_kv_heads,
+            "head_dim": b.head_dim, "block_size": b.block_size, "dtype": b.dtype,
+            "max_seq_len": b.max_seq_len, "total_keys": int(b.seq_lens.sum()),
+            "num_splits": n, "grid": f"{b.num_seqs}x{b.num_kv_heads}x{n} work-groups of 256"}
+    return Case(name, step, kernel, by["total"], fl, kb, fl, "hbm", kname, "decode.hip", info)
+
+
+def prefill_case(b, name):
+    import paged_kv_attention_pa_amd as pa
+    import workloads as W
+    cache, q = _dev(b.cache), _dev(b.q)
+    bt, sl, qsl = _dev(b.block_table), _dev(b.seq_lens), _dev(b.query_start_loc)
+    kn, vn, sm = _dev(b.k_new), _dev(b.v_new), _dev(b.slot_mapping)
+    import torch
+    out = torch.empty_like(q)
+    lse = torch.empty(b.q.shape[:2], dtype=torch.float32, device="cuda")
+
+    def step():
+        pa.prefill_varlen(q, cache, bt, qsl, sl, b.max_query_len, b.max_seq_len, b.scale,
+                          k=kn, v=vn, slot_mapping=sm, out=out, lse=lse)
+
+    def kernel():
+        pa.prefill_varlen(q, cache, bt, qsl, sl, b.max_query_len, b.max_seq_len, b.scale,
+                          out=out, lse=lse)
+
+    by = W.gqa_bytes(b)
+    kb = by["total"] - by["write"]
+    fl = W.gqa_flops(b)
+    info = {"num_seqs": b.num_seqs, "num_tokens": b.num_tokens, "num_q_heads": b.num_q_heads,
+            "num_kv_heads": b.num_kv_heads, "head_dim": b.head_dim, "block_size": b.block_size,
+            "max_query_len": b.max_query_len, "max_seq_len": b.max_seq_len, "causal": True,
+            "grid": "ceil(max_q/128) x num_seqs x Hq work-groups of 256"}
+    return Case(name, step, kernel, by["total"], fl, kb, fl, "mfma", "prefill_kernel",
+                "prefill.hip", info)
+
+
+def mla_case(b, name):
+    import torch
+    import paged_kv_attention_pa_amd as pa
+    import workloads as W
+    cache = _dev(b.cache)
+    qn, qp = _dev(b.q_nope), _dev(b.q_pe)
+    bt, sl = _dev(b.block_table), _dev(b.seq_lens)
+    kc, kp, sm = _dev(b.kv_c_new), _dev(b.k_pe_new), _dev(b.slot_mapping)
+    n = pa.mla_num_kv_splits(b.num_seqs, b.max_seq_len, pa.device_num_cus())
+    ws = torch.empty(max(1, pa.decode_workspace_bytes(b.num_seqs, b.num_heads, b.kv_lora_rank, n) // 4),
+                     dtype=torch.float32, device="cuda")
+    out = torch.empty((b.num_seqs, b.num_heads, b.kv_lora_rank), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((b.num_seqs, b.num_heads), dtype=torch.float32, device="cuda")
+
+    def step():
+        pa.mla_decode(qn, qp, cache, bt, sl, b.max_seq_len, b.scale, kv_c=kc, k_pe=kp,
+                      slot_mapping=sm, num_splits=n, workspace=ws, out=out, lse=lse)
+
+    def kernel():
+        pa.mla_decode(qn, qp, cache, bt, sl, b.max_seq_len, b.scale, num_splits=n,
+                      workspace=ws, stage1_only=True)
+
+    by = W.mla_bytes(b)
+    kb = by["kv"] + by["q"] + by["meta"] - b.num_seqs * 8
+    fl = W.mla_flops(b)
+    info = {"num_seqs": b.num_seqs, "num_heads": b.num_heads, "kv_lora_rank": b.kv_lora_rank,
+            "rope_dim": b.rope_dim, "block_size": b.block_size, "max_seq_len": b.max_seq_len,
+            "total_keys": int(b.seq_lens.sum()), "num_splits": n,
+            "grid": f"{b.num_seqs}x{n} work-groups of 512"}
+    return Case(name, step, kernel, by["total"], fl, kb, fl, "mfma", "mla_split_kernel",
+                "mla_decode.hip", info)
+
+
+def build_cases(only):
+    import workloads as W
+    makers = {
+        "tiny_gqa_decode_fp32": lambda: gqa_decode_case(W.tiny_decode(), 0, "tiny_gqa_decode_fp32"),
+        HEADLINE: lambda: gqa_decode_case(W.llama_decode(), 0, HEADLINE),
+        "chunked_prefill_varlen_bf16": lambda: prefill_case(W.chunked_prefill(),
+                                                            "chunked_prefill_varlen_bf16"),
+        "long_context_split_kv_decode_bf16": lambda: gqa_decode_case(
+            W.long_context_decode(), 0, "long_context_split_kv_decode_bf16"),
+        "mla_latent_decode_bf16": lambda: mla_case(W.mla_decode_batch(), "mla_latent_decode_bf16"),
+    }
+    names = [HEADLINE] + [n for n in makers if n != HEADLINE]
+    if only:
+        names = [n for n in names if n in only or n == HEADLINE]
+    for n in names:
+        t = time.perf_counter()
+        case = makers[n]()
+        log(f"[bench] prepared {n} in {time.perf_counter() - t:.1f}s")
+        yield case
+
+
+# --------------------------------------------------------------------------
+# timing
+# --------------------------------------------------------------------------
+
+def time_steps(fn, steps, warmup):
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        fn()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / steps
+
+
+def time_kernel_events(fn, reps, warmup):
+    """Average duration of one launch of ``fn``'s kernel, from HIP events
+    recorded on torch's current stream (the stream the library launches on)."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(reps):
+        fn()
+    end.record()
+    end.synchronize()
+    return start.elapsed_time(end) / 1000.0 / reps
+
+
+def traffic_for(case):
+    """HBM bytes per launch from the stored rocprofv3 counter runs, or None
+    if they were taken on a different version of the kernel's source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    e = rec.get(case.name)
+    if not e or e.get("source_sha") != kernel_source_sha(case.source):
+        return None
+    return e.get("hbm_bytes_per_launch")
+
+
+def roofline(case, kern_s):
+    if case.bound == "hbm":
+        achieved = case.kern_bytes / kern_s / 1e9
+        peak, unit = PEAK_HBM_GBS, "GB/s"
+    else:
+        achieved = case.kern_flops / kern_s / 1e12
+        peak, unit = PEAK_BF16_TFLOPS, "TFLOP/s"
+    return {"bound": case.bound, "kernel": case.kernel_name, "achieved": round(achieved, 2),
+            "peak": peak, "unit": unit, "frac": round(achieved / peak, 4),
+            "traffic": traffic_for(case), "kernel_ms": round(kern_s * 1e3, 4),
+            "algorithmic_bytes": int(case.kern_bytes), "algorithmic_flops": int(case.kern_flops)}
+
+
+# --------------------------------------------------------------------------
+# CPU baseline: the float64 oracle on a bounded sample of the headline batch
+# --------------------------------------------------------------------------
+
+def cpu_baseline(budget_s=12.0):
+    import numpy as np
+    import workloads as W
+    import oracle.pa_oracle as O
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:       # pragma: no cover
+        threadpool_limits = None
+    b = W.llama_decode()
+    done, nbytes, passes = 0, 0, 0
+    row = b.num_kv_heads * b.head_dim * 2 * 2
+    ctx = threadpool_limits(limits=1) if threadpool_limits else None
+    t0 = time.perf_counter()
+    try:
+        # whole passes over the batch (write + decode of every request) until
+        # the budget is spent; stop early inside a pass if it runs long
+        while time.perf_counter() - t0 < budget_s:
+            cache = O.cache_write_kv(b.cache, b.k_new, b.v_new, b.slot_mapping)
+            for r in range(b.num_seqs):
+                O.paged_decode(b.q, cache, b.block_table, b.seq_lens, b.scale, requests=[r])
+                done += 1
+                nbytes += int(b.seq_lens[r]) * row + 2 * b.num_q_heads * b.head_dim * 2
+                if time.perf_counter() - t0 > 2 * budget_s:
+                    break
+            passes += 1
+    finally:
+        if ctx is not None:
+            ctx.__exit__(None, None, None)
+    dt = time.perf_counter() - t0
+    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "seconds": round(dt, 2),
+            "sample": f"float64 numpy oracle (cache write + decode) over {passes} pass(es) of the "
+                      f"64-request batch ({done} request decodes), one BLAS thread"}
+
+
+# --------------------------------------------------------------------------
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--only", nargs="*", default=None, help="extra workloads to run")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB, --steps times "
+                         "(the reference kernel that scales rocprofv3 FETCH_SIZE/WRITE_SIZE)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: the path is single-GPU by design (no collectives); "
+              "run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    if args.copy_calibration:
+        n = args.copy_calibration * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read_per_launch": n * 4, "copy_bytes_written_per_launch": n * 4,
+                          "launches": args.steps}), flush=True)
+        return
+    import paged_kv_attention_pa_amd as pa
+    pa.library()   # fails loudly if the HIP library is missing
+
+    results = {}
+    head = None
+    for case in build_cases(args.only):
+        step_s = time_steps(case.step, args.steps, args.warmup)
+        kern_s = time_kernel_events(case.kernel, args.steps, args.warmup)
+        rl = roofline(case, kern_s)
+        res = {
+            "ms_per_step": round(step_s * 1e3, 4),
+            "step_GBps": round(case.step_bytes / step_s / 1e9, 2),
+            "step_TFLOPs": round(case.step_flops / step_s / 1e12, 3),
+            "step_bytes": int(case.step_bytes), "step_flops": int(case.step_flops),
+            "roofline": rl, "config": case.info,
+        }
+        results[case.name] = res
+        log(f"[bench] {case.name}: {res['ms_per_step']} ms/step, {res['step_GBps']} GB/s, "
+            f"{res['step_TFLOPs']} TFLOP/s; kernel {rl['kernel']} {rl['kernel_ms']} ms = "
+            f"{rl['achieved']} {rl['unit']} ({100 * rl['frac']:.1f}% of peak)")
+        if case.name == HEADLINE:
+            head = (case, step_s, rl)
+        del case
+        torch.cuda.empty_cache()
+
+    case, step_s, rl = head
+    line = {
+        "metric": METRIC,
+        "value": round(case.step_bytes / step_s / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_s * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": HEADLINE, **results[HEADLINE]["config"],
+                   "seq_len": "U[512,8192]", "parallelism": "single GPU"},
+        "roofline": {k: rl[k] for k in ("bound", "achieved", "peak", "unit", "frac", "traffic")},
+        "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline(),
+        "dominant_kernel": {k: rl[k] for k in ("kernel", "kernel_ms", "algorithmic_bytes")},
+        "workloads": results,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

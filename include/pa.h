@@ -137,19 +137,25 @@ pa_status_t pa_cache_write(pa_layout_t layout, pa_dtype_t dtype,
  *              is the request's last position.
  * max_seq_len: host copy of max(seq_lens) (sets the split partition).
  * scale:       multiplies Q K^T before the softmax (1/sqrt(head_dim) usually).
- * num_splits:  0 = pa_num_kv_splits(max_seq_len, pa_device_num_cus());
+ * num_splits:  0 = n = pa_num_kv_splits(max_seq_len, pa_device_num_cus());
  *              1 = no split (each request reduced by one work unit, in an
  *              order independent of the rest of the batch); n > 1 = n splits.
  *              Split s of a request covers positions [s*P, (s+1)*P) with
  *              P = ceil(max_seq_len / n) rounded up to a multiple of
  *              block_size; splits past the request's end are empty.
  * workspace:   fp32 scratch of at least pa_decode_workspace_bytes(num_seqs,
- *              num_q_heads, head_dim, n) bytes (may be NULL when n = 1).
- * out:         [num_seqs, num_q_heads, head_dim], storage dtype.
- * lse:         [num_seqs, num_q_heads] fp32 natural-log LSE, or NULL.
- * Supported: head_dim 128; num_q_heads / num_kv_heads in {1, 2, 4, 8, 16};
+ *              num_q_heads, head_dim, n) bytes; may be NULL when one split
+ *              covers max_seq_len (then no partials are formed).
+ * out:         [num_seqs, num_q_heads, head_dim], storage dtype; or NULL for
+ *              the two-stage form: only stage 1 runs and the workspace holds
+ *              the partials [num_seqs, num_q_heads, n, head_dim + 1] (empty
+ *              splits have lse = -inf), ready for pa_lse_merge.
+ * lse:         [num_seqs, num_q_heads] fp32 natural-log LSE, or NULL (must be
+ *              NULL when out is NULL).
+ * Supported: head_dim 128; num_q_heads / num_kv_heads in {1, 2, 4, 8};
  * PA_F32 and PA_BF16.
- * Enqueues: the write (if k/v given), the split kernel, the merge kernel.
+ * Enqueues: the write (if k/v given), the split kernel, and the merge kernel
+ * unless one split covers every request or out is NULL.
  * ------------------------------------------------------------------------- */
 pa_status_t pa_decode(pa_dtype_t dtype,
                       const void* q, const void* k, const void* v,
@@ -182,7 +188,7 @@ pa_status_t pa_decode(pa_dtype_t dtype,
  *                 num_q_heads] fp32 or NULL.  A query that sees no key gets
  *                 out = 0 and lse = -inf.
  * Supported: PA_BF16, head_dim 128, num_q_heads / num_kv_heads in
- * {1, 2, 4, 8, 16}.
+ * {1, 2, 4, 8}.
  * Enqueues: the write (if k/v given), then the attention kernel.
  * ------------------------------------------------------------------------- */
 pa_status_t pa_prefill_varlen(pa_dtype_t dtype,
@@ -210,10 +216,13 @@ pa_status_t pa_prefill_varlen(pa_dtype_t dtype,
  *         (dense), or both NULL; slot_mapping [num_seqs] or NULL.
  * kv_cache: MLA layout [num_blocks, block_size, kv_lora_rank + rope_dim].
  * block_table, seq_lens, max_seq_len, scale: as in pa_decode.
- * num_splits: 0 = pa_mla_num_kv_splits(num_seqs, max_seq_len, CUs); else as
- *         in pa_decode (P rounded up to a multiple of block_size).
- * workspace: pa_decode_workspace_bytes(num_seqs, num_heads, kv_lora_rank, n).
- * out:    [num_seqs, num_heads, kv_lora_rank]; lse [num_seqs, num_heads] or NULL.
+ * num_splits: 0 = n = pa_mla_num_kv_splits(num_seqs, max_seq_len, CUs); else
+ *         as in pa_decode (P rounded up to a multiple of block_size).
+ * workspace: pa_decode_workspace_bytes(num_seqs, num_heads, kv_lora_rank, n)
+ *         bytes, as in pa_decode.
+ * out:    [num_seqs, num_heads, kv_lora_rank], or NULL for the two-stage form
+ *         (partials [num_seqs, num_heads, n, kv_lora_rank + 1] in the
+ *         workspace); lse [num_seqs, num_heads] or NULL (NULL if out is).
  * Supported: PA_BF16 only (no dtype argument), kv_lora_rank 512, rope_dim 64,
  * num_heads a multiple of 16 up to 128, block_size a multiple of 16.
  * Enqueues: the write (if given), the split kernel, the merge kernel.

@@ -172,8 +172,12 @@ def cache_write(kv_cache, k, v, slot_mapping, layout: int = PA_LAYOUT_KV, stream
 
 def decode(q, kv_cache, block_table, seq_lens, max_seq_len: int, scale: float,
            k=None, v=None, slot_mapping=None, num_splits: int = 0, workspace=None,
-           out=None, lse=None, return_lse: bool = True, stream=None):
-    """GQA decode: q [B, Hq, D]; kv_cache [nb, 2, bs, Hkv, D]; returns (out, lse)."""
+           out=None, lse=None, return_lse: bool = True, stage1_only: bool = False,
+           stream=None):
+    """GQA decode: q [B, Hq, D]; kv_cache [nb, 2, bs, Hkv, D]; returns (out, lse).
+
+    stage1_only: run only the split kernel and return the partials
+    [B, Hq, n, D + 1] (a view of the workspace) for ``lse_merge``."""
     torch = _torch()
     _dev(q, kv_cache, block_table, seq_lens, k, v, slot_mapping, workspace, out, lse)
     _int_tensor(block_table, "int32", "block_table")
@@ -183,14 +187,17 @@ def decode(q, kv_cache, block_table, seq_lens, max_seq_len: int, scale: float,
     B, Hq, D = q.shape
     nb, _, bs, hkv, d2 = kv_cache.shape
     _need(d2 == D, "head_dim mismatch")
-    if out is None:
-        out = torch.empty_like(q)
-    if lse is None and return_lse:
-        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    if stage1_only:
+        out = lse = None
+    else:
+        if out is None:
+            out = torch.empty_like(q)
+        if lse is None and return_lse:
+            lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
     n = num_splits
     if n == 0:
         n = num_kv_splits(max_seq_len, device_num_cus())
-    need = decode_workspace_bytes(B, Hq, D, n) if n > 1 else 0
+    need = decode_workspace_bytes(B, Hq, D, n) if (n > 1 or stage1_only) else 0
     if workspace is None and need:
         workspace = torch.empty(need // 4, dtype=torch.float32, device=q.device)
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
@@ -199,6 +206,8 @@ def decode(q, kv_cache, block_table, seq_lens, max_seq_len: int, scale: float,
                                _ptr(seq_lens), B, int(max_seq_len), Hq, hkv, D, float(scale),
                                int(num_splits), _ptr(workspace), wbytes, _ptr(out), _ptr(lse),
                                _stream(stream)))
+    if stage1_only:
+        return workspace[: B * Hq * n * (D + 1)].view(B, Hq, n, D + 1)
     return out, lse
 
 
@@ -232,7 +241,8 @@ def prefill_varlen(q, kv_cache, block_table, query_start_loc, seq_lens, max_quer
 
 def mla_decode(q_nope, q_pe, kv_cache, block_table, seq_lens, max_seq_len: int, scale: float,
                kv_c=None, k_pe=None, slot_mapping=None, num_splits: int = 0, workspace=None,
-               out=None, lse=None, return_lse: bool = True, stream=None):
+               out=None, lse=None, return_lse: bool = True, stage1_only: bool = False,
+               stream=None):
     """MLA decode: q_nope [B, H, R], q_pe [B, H, P] (last dim contiguous; may be
     views of one [B, H, R+P] tensor); kv_cache [nb, bs, R+P].  Returns
     (out [B, H, R], lse [B, H])."""
@@ -245,14 +255,17 @@ def mla_decode(q_nope, q_pe, kv_cache, block_table, seq_lens, max_seq_len: int, 
     P = q_pe.shape[2]
     nb, bs, row = kv_cache.shape
     _need(row == R + P, "cache row must be kv_lora_rank + rope_dim")
-    if out is None:
-        out = torch.empty((B, H, R), dtype=q_nope.dtype, device=q_nope.device)
-    if lse is None and return_lse:
-        lse = torch.empty((B, H), dtype=torch.float32, device=q_nope.device)
+    if stage1_only:
+        out = lse = None
+    else:
+        if out is None:
+            out = torch.empty((B, H, R), dtype=q_nope.dtype, device=q_nope.device)
+        if lse is None and return_lse:
+            lse = torch.empty((B, H), dtype=torch.float32, device=q_nope.device)
     n = num_splits
     if n == 0:
         n = mla_num_kv_splits(B, max_seq_len, device_num_cus())
-    need = decode_workspace_bytes(B, H, R, n) if n > 1 else 0
+    need = decode_workspace_bytes(B, H, R, n) if (n > 1 or stage1_only) else 0
     if workspace is None and need:
         workspace = torch.empty(need // 4, dtype=torch.float32, device=q_nope.device)
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
@@ -263,6 +276,8 @@ def mla_decode(q_nope, q_pe, kv_cache, block_table, seq_lens, max_seq_len: int, 
                                    _ptr(seq_lens), B, int(max_seq_len), H, R, P, float(scale),
                                    int(num_splits), _ptr(workspace), wbytes, _ptr(out), _ptr(lse),
                                    _stream(stream)))
+    if stage1_only:
+        return workspace[: B * H * n * (R + 1)].view(B, H, n, R + 1)
     return out, lse
 
 

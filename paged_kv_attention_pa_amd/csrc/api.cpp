@@ -196,7 +196,9 @@ pa_status_t pa_decode(pa_dtype_t dtype,
   PA_REQUIRE(k == nullptr || slot_mapping != nullptr, PA_ERR_INVALID, "k/v given without slot_mapping");
   PA_REQUIRE(slot_mapping == nullptr || k != nullptr, PA_ERR_INVALID, "slot_mapping given without k/v");
   if (num_seqs == 0) return ok();
-  PA_REQUIRE(q && kv_cache && out, PA_ERR_INVALID, "q, kv_cache and out must be non-null");
+  PA_REQUIRE(q && kv_cache, PA_ERR_INVALID, "q and kv_cache must be non-null");
+  PA_REQUIRE(out != nullptr || lse == nullptr, PA_ERR_INVALID,
+             "lse without out: the partial-only mode (out = NULL) returns no lse");
 
   int n = num_splits;
   if (n == 0) {
@@ -205,8 +207,9 @@ pa_status_t pa_decode(pa_dtype_t dtype,
     n = pa_num_kv_splits(max_seq_len, cus);
   }
   const int P = split_tokens_for(max_seq_len, n, block_size);
-  const int used = used_splits(max_seq_len, P);  // <= n
-  if (used > 1) {
+  const bool stage1 = (out == nullptr);            // partials only, for pa_lse_merge
+  const bool direct = !stage1 && used_splits(max_seq_len, P) == 1;
+  if (!direct) {
     const size_t need = pa_decode_workspace_bytes(num_seqs, num_q_heads, head_dim, n);
     PA_REQUIRE(workspace != nullptr && workspace_bytes >= need, PA_ERR_WORKSPACE,
                "workspace of %zu bytes needed for %d splits (got %zu)", need, n, workspace_bytes);
@@ -233,17 +236,20 @@ pa_status_t pa_decode(pa_dtype_t dtype,
   d.num_kv_heads = num_kv_heads;
   d.head_dim = head_dim;
   d.scale = scale;
-  d.num_splits = used;
+  d.num_splits = direct ? 1 : n;
   d.split_tokens = P;
+  d.direct = direct;
   d.part = static_cast<float*>(workspace);
   d.out = out;
   d.lse = lse;
   hipError_t e = pa::launch_decode_gqa(d, stream);
   if (e != hipSuccess) return hip_fail(e, "decode launch");
-  pa::LseMerge m{static_cast<const float*>(workspace), num_seqs, num_q_heads, used, head_dim,
-                 dtype == PA_BF16, out, lse, seq_lens, P, max_blocks_per_seq * block_size};
-  e = pa::launch_lse_merge(m, stream);
-  if (e != hipSuccess) return hip_fail(e, "merge launch");
+  if (!direct && !stage1) {
+    pa::LseMerge m{static_cast<const float*>(workspace), num_seqs, num_q_heads, n, head_dim,
+                   dtype == PA_BF16, out, lse};
+    e = pa::launch_lse_merge(m, stream);
+    if (e != hipSuccess) return hip_fail(e, "merge launch");
+  }
   return ok();
 }
 
@@ -329,7 +335,9 @@ pa_status_t pa_mla_decode(const void* q_nope, int64_t qn_stride_b, int64_t qn_st
   PA_REQUIRE(kv_c == nullptr || slot_mapping != nullptr, PA_ERR_INVALID, "kv_c/k_pe given without slot_mapping");
   PA_REQUIRE(slot_mapping == nullptr || kv_c != nullptr, PA_ERR_INVALID, "slot_mapping given without kv_c/k_pe");
   if (num_seqs == 0) return ok();
-  PA_REQUIRE(q_nope && q_pe && kv_cache && out, PA_ERR_INVALID, "q_nope, q_pe, kv_cache and out must be non-null");
+  PA_REQUIRE(q_nope && q_pe && kv_cache, PA_ERR_INVALID, "q_nope, q_pe and kv_cache must be non-null");
+  PA_REQUIRE(out != nullptr || lse == nullptr, PA_ERR_INVALID,
+             "lse without out: the partial-only mode (out = NULL) returns no lse");
   int n = num_splits;
   if (n == 0) {
     const int cus = pa_device_num_cus();
@@ -337,8 +345,9 @@ pa_status_t pa_mla_decode(const void* q_nope, int64_t qn_stride_b, int64_t qn_st
     n = pa_mla_num_kv_splits(num_seqs, max_seq_len, cus);
   }
   const int P = split_tokens_for(max_seq_len, n, block_size);
-  const int used = used_splits(max_seq_len, P);
-  if (used > 1) {
+  const bool stage1 = (out == nullptr);
+  const bool direct = !stage1 && used_splits(max_seq_len, P) == 1;
+  if (!direct) {
     const size_t need = pa_decode_workspace_bytes(num_seqs, num_heads, kv_lora_rank, n);
     PA_REQUIRE(workspace != nullptr && workspace_bytes >= need, PA_ERR_WORKSPACE,
                "workspace of %zu bytes needed for %d splits (got %zu)", need, n, workspace_bytes);
@@ -352,14 +361,16 @@ pa_status_t pa_mla_decode(const void* q_nope, int64_t qn_stride_b, int64_t qn_st
   pa::MlaDecode d{q_nope, qn_stride_b, qn_stride_h, q_pe, qp_stride_b, qp_stride_h,
                   kv_cache, num_blocks, block_size, block_table, max_blocks_per_seq,
                   seq_lens, num_seqs, num_heads, kv_lora_rank, rope_dim, scale,
-                  used, P, static_cast<float*>(workspace), out, lse};
+                  direct ? 1 : n, P, direct, static_cast<float*>(workspace), out, lse};
   hipError_t e = pa::launch_mla_decode(d, stream);
   if (e == hipErrorNotSupported) return fail(PA_ERR_UNSUPPORTED, "MLA kernel not built");
   if (e != hipSuccess) return hip_fail(e, "MLA decode launch");
-  pa::LseMerge m{static_cast<const float*>(workspace), num_seqs, num_heads, used, kv_lora_rank,
-                 1, out, lse, seq_lens, P, max_blocks_per_seq * block_size};
-  e = pa::launch_lse_merge(m, stream);
-  if (e != hipSuccess) return hip_fail(e, "merge launch");
+  if (!direct && !stage1) {
+    pa::LseMerge m{static_cast<const float*>(workspace), num_seqs, num_heads, n, kv_lora_rank,
+                   1, out, lse};
+    e = pa::launch_lse_merge(m, stream);
+    if (e != hipSuccess) return hip_fail(e, "merge launch");
+  }
   return ok();
 }
 
@@ -375,7 +386,7 @@ pa_status_t pa_lse_merge(const float* part, int num_rows, int num_heads,
   if (num_rows == 0 || num_heads == 0) return ok();
   PA_REQUIRE(part && out, PA_ERR_INVALID, "part and out must be non-null");
   pa::LseMerge m{part, num_rows, num_heads, num_splits, head_dim_v, out_dtype == PA_BF16,
-                 out, lse, nullptr, 0, 0};
+                 out, lse};
   hipError_t e = pa::launch_lse_merge(m, stream);
   if (e != hipSuccess) return hip_fail(e, "merge launch");
   return ok();

@@ -90,10 +90,22 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeGQA a) {
   const int bs = a.block_size;
   const int seq = min(a.seq_lens[r], a.max_blocks * bs);
   const int t0 = s * a.split_tokens;
-  if (t0 >= seq) return;
+  const int Hq = a.num_q_heads;
+  if (t0 >= seq) {   // empty split: weight 0 in the merge
+    if (!a.direct && threadIdx.x < G)
+      a.part[((int64_t(r) * Hq + int64_t(h) * G + threadIdx.x) * S + s) * (kD + 1) + kD] = -INFINITY;
+    if (a.direct) {  // no key at all: out = 0, lse = -inf
+      for (int i = threadIdx.x; i < G * kD; i += blockDim.x) {
+        const int64_t o = (int64_t(r) * Hq + int64_t(h) * G) * kD + i;
+        if constexpr (kBF16) static_cast<uint16_t*>(a.out)[o] = 0;
+        else static_cast<float*>(a.out)[o] = 0.0f;
+      }
+      if (a.lse && threadIdx.x < G) a.lse[int64_t(r) * Hq + int64_t(h) * G + threadIdx.x] = -INFINITY;
+    }
+    return;
+  }
   const int t1 = min(seq, t0 + a.split_tokens);
   const int n_groups = (t1 - t0 + kGroupTokens - 1) / kGroupTokens;
-  const bool single = seq <= a.split_tokens;  // the whole request is this split
 
   const float scale2 = a.scale * kLog2e;
   const int64_t tok_stride = int64_t(Hkv) * kD;          // elements between slots
@@ -221,7 +233,6 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeGQA a) {
     }
   }
   __syncthreads();
-  const int Hq = a.num_q_heads;
   for (int idx = threadIdx.x; idx < G * kD; idx += blockDim.x) {
     const int j = idx / kD;
     const int d = idx - j * kD;
@@ -238,7 +249,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeGQA a) {
     const float o = num / den;
     const float lse_nat = (mm + fast_log2(den)) * kLn2;
     const int64_t row = int64_t(r) * Hq + int64_t(h) * G + j;
-    if (single) {
+    if (a.direct) {
       if constexpr (kBF16) static_cast<uint16_t*>(a.out)[row * kD + d] = f32_to_bf16(o);
       else static_cast<float*>(a.out)[row * kD + d] = o;
       if (d == 0 && a.lse) a.lse[row] = lse_nat;
@@ -250,55 +261,96 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeGQA a) {
   }
 }
 
-// One wave per (row, head): weights exp(lse_s - M) over the valid splits.
-__global__ __launch_bounds__(256) void lse_merge_kernel(LseMerge a) {
-  const int lane = threadIdx.x & 63;
-  const int64_t pair = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
-  if (pair >= int64_t(a.num_rows) * a.num_heads) return;
-  const int row = int(pair / a.num_heads);
-  int n = a.num_splits;
-  if (a.seq_lens) {
-    const int seq = min(a.seq_lens[row], a.max_tokens);
-    n = min(n, (seq + a.split_tokens - 1) / a.split_tokens);
-    if (n == 1) return;  // written directly by the split kernel
-  }
+// One work-group of 256 threads per (row, head).  Threads first reduce the
+// splits' lse to M and keep the weights exp(lse_s - M) in LDS; then lane
+// l of wave w accumulates dims l, l + 64, ... over splits w, w + 4, ...
+// (each wave-wide load reads 64 consecutive floats of one split row) and the
+// four waves' sums are added through LDS.
+constexpr int kMergeThreads = 256;
+constexpr int kMergeMaxDv = 1024;
+constexpr int kMergeWChunk = 1024;   // weights held in LDS per pass over the splits
+
+__global__ __launch_bounds__(kMergeThreads) void lse_merge_kernel(LseMerge a) {
+  __shared__ float s_w[kMergeWChunk];
+  __shared__ float s_red[kMergeThreads / 64];
+  __shared__ float s_acc[3][kMergeMaxDv];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int64_t pair = blockIdx.x;
+  const int n = a.num_splits;
   const int Dv = a.head_dim_v;
-  const float* base = a.part + pair * int64_t(a.num_splits) * (Dv + 1);
+  const int64_t stride = Dv + 1;
+  const float* base = a.part + pair * int64_t(n) * stride;
+
+  // M = max_s lse_s
   float mx = -INFINITY;
-  for (int s = lane; s < n; s += 64) mx = fmaxf(mx, base[int64_t(s) * (Dv + 1) + Dv]);
+  for (int s = tid; s < n; s += kMergeThreads) mx = fmaxf(mx, base[s * stride + Dv]);
   for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+  if (lane == 0) s_red[wave] = mx;
+  __syncthreads();
+  mx = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
   float* out_f = static_cast<float*>(a.out) + pair * Dv;
   uint16_t* out_b = static_cast<uint16_t*>(a.out) + pair * Dv;
-  if (mx == -INFINITY) {
-    for (int d = lane; d < Dv; d += 64) {
+  if (mx == -INFINITY) {   // every split empty
+    for (int d = tid; d < Dv; d += kMergeThreads) {
       if (a.out_bf16) out_b[d] = 0; else out_f[d] = 0.0f;
     }
-    if (lane == 0 && a.lse) a.lse[pair] = -INFINITY;
+    if (tid == 0 && a.lse) a.lse[pair] = -INFINITY;
     return;
   }
   const float mx2 = mx * kLog2e;
+
+  constexpr int kPer = kMergeMaxDv / 64;   // dims per lane, upper bound
+  float acc[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) acc[i] = 0.0f;
   float den = 0.0f;
-  for (int s = lane; s < n; s += 64) {
-    const float ls = base[int64_t(s) * (Dv + 1) + Dv];
-    den += (ls == -INFINITY) ? 0.0f : fast_exp2(fmaf(ls, kLog2e, -mx2));
+  for (int c0 = 0; c0 < n; c0 += kMergeWChunk) {
+    const int cn = min(kMergeWChunk, n - c0);
+    __syncthreads();   // previous chunk's weights no longer read
+    for (int s = tid; s < cn; s += kMergeThreads) {
+      const float ls = base[(c0 + s) * stride + Dv];
+      const float w = (ls == -INFINITY) ? 0.0f : fast_exp2(fmaf(ls, kLog2e, -mx2));
+      s_w[s] = w;
+      den += w;
+    }
+    __syncthreads();
+    for (int s = wave; s < cn; s += 4) {
+      const float w = s_w[s];
+      if (w == 0.0f) continue;   // empty split: its output is never read
+      const float* row = base + (c0 + s) * stride;
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) {
+        const int d = lane + 64 * i;
+        if (d < Dv) acc[i] = fmaf(w, row[d], acc[i]);
+      }
+    }
   }
   for (int o = 32; o >= 1; o >>= 1) den += __shfl_xor(den, o);
-  const float inv = 1.0f / den;
-  for (int d0 = 0; d0 < Dv; d0 += 64) {
-    const int d = d0 + lane;
-    float num = 0.0f;
-    for (int s = 0; s < n; ++s) {
-      const float ls = base[int64_t(s) * (Dv + 1) + Dv];
-      if (ls == -INFINITY) continue;
-      const float w = fast_exp2(fmaf(ls, kLog2e, -mx2));
-      if (d < Dv) num = fmaf(w, base[int64_t(s) * (Dv + 1) + d], num);
-    }
-    if (d < Dv) {
-      const float o = num * inv;
-      if (a.out_bf16) out_b[d] = f32_to_bf16(o); else out_f[d] = o;
+  __syncthreads();
+  if (lane == 0) s_red[wave] = den;
+  if (wave > 0) {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int d = lane + 64 * i;
+      if (d < Dv) s_acc[wave - 1][d] = acc[i];
     }
   }
-  if (lane == 0 && a.lse) a.lse[pair] = mx + fast_log2(den) * kLn2;
+  __syncthreads();
+  if (wave == 0) {
+    den = s_red[0] + s_red[1] + s_red[2] + s_red[3];
+    const float inv = 1.0f / den;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int d = lane + 64 * i;
+      if (d < Dv) {
+        const float o = (acc[i] + s_acc[0][d] + s_acc[1][d] + s_acc[2][d]) * inv;
+        if (a.out_bf16) out_b[d] = f32_to_bf16(o); else out_f[d] = o;
+      }
+    }
+    if (lane == 0 && a.lse) a.lse[pair] = mx + fast_log2(den) * kLn2;
+  }
 }
 
 template <bool kBF16>
@@ -325,8 +377,8 @@ hipError_t launch_decode_gqa(const DecodeGQA& a, hipStream_t s) {
 hipError_t launch_lse_merge(const LseMerge& a, hipStream_t s) {
   const int64_t pairs = int64_t(a.num_rows) * a.num_heads;
   if (pairs <= 0) return hipSuccess;
-  const dim3 grid(unsigned((pairs + 3) / 4)), block(256);
-  hipLaunchKernelGGL(lse_merge_kernel, grid, block, 0, s, a);
+  if (a.head_dim_v > kMergeMaxDv || pairs > INT32_MAX) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(lse_merge_kernel, dim3(unsigned(pairs)), dim3(kMergeThreads), 0, s, a);
   return hipGetLastError();
 }
 

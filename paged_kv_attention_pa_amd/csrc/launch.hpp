@@ -37,23 +37,17 @@ struct DecodeGQA {
   const int32_t* seq_lens; int num_seqs;
   int num_q_heads; int num_kv_heads; int head_dim;
   float scale;
-  int num_splits; int split_tokens;  // P: tokens per split (multiple of block_size)
-  float* part;                   // [B, Hq, S, D+1] (unused when num_splits == 1)
-  void* out; float* lse;         // final outputs (written directly when a
-                                 // request needs only one split)
-  // Optional fused new-token write: when non-null, the work unit that owns
-  // a request's last position stores k_new/v_new there and uses them.
-  const void* k_new; const void* v_new; const int64_t* slots;
+  int num_splits; int split_tokens;  // S and P: split s covers [s P, (s+1) P)
+  int direct;                    // 1: S == 1, write out/lse directly
+  float* part;                   // [B, Hq, S, D+1] when !direct; empty splits get lse -inf
+  void* out; float* lse;         // final outputs (direct mode)
 };
 hipError_t launch_decode_gqa(const DecodeGQA& a, hipStream_t s);
 
-// Merge of split partials.  seq_lens/split_tokens: when seq_lens is non-null,
-// request r only has ceil(seq_lens[r] / split_tokens) valid splits and rows
-// with a single valid split are skipped (already final).
+// Merge of split partials [R, H, S, Dv+1]; splits with lse -inf weigh 0.
 struct LseMerge {
   const float* part; int num_rows; int num_heads; int num_splits; int head_dim_v;
   int out_bf16; void* out; float* lse;
-  const int32_t* seq_lens; int split_tokens; int max_tokens;
 };
 hipError_t launch_lse_merge(const LseMerge& a, hipStream_t s);
 
@@ -66,7 +60,7 @@ struct MlaDecode {
   const int32_t* seq_lens; int num_seqs;
   int num_heads; int rank; int rope;
   float scale;
-  int num_splits; int split_tokens;
+  int num_splits; int split_tokens; int direct;
   float* part; void* out; float* lse;
 };
 hipError_t launch_mla_decode(const MlaDecode& a, hipStream_t s);

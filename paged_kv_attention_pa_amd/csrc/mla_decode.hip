@@ -66,10 +66,21 @@ __global__ __launch_bounds__(512) void mla_split_kernel(MlaDecode a) {
   const int bs = a.block_size;
   const int seq = min(a.seq_lens[r], a.max_blocks * bs);
   const int t0 = s * a.split_tokens;
-  if (t0 >= seq) return;
+  if (t0 >= seq) {   // empty split: weight 0 in the merge (direct: no key at all)
+    for (int hd = tid; hd < H; hd += nthreads) {
+      const int64_t row = int64_t(r) * H + hd;
+      if (!a.direct) {
+        a.part[(row * S_spl + s) * (kRank + 1) + kRank] = -INFINITY;
+      } else {
+        uint16_t* op = static_cast<uint16_t*>(a.out) + row * kRank;
+        for (int d = 0; d < kRank; ++d) op[d] = 0;
+        if (a.lse) a.lse[row] = -INFINITY;
+      }
+    }
+    return;
+  }
   const int t1 = min(seq, t0 + a.split_tokens);
   const int n_tiles = (t1 - t0 + kBN - 1) / kBN;
-  const bool single = seq <= a.split_tokens;
 
   // ---- Q^T fragments: head = 16 wave + l % 16, dims 32 kk + 8 (l / 16) .. + 8
   const bool active = wave < H / 16;
@@ -202,7 +213,7 @@ __global__ __launch_bounds__(512) void mla_split_kernel(MlaDecode a) {
   const float inv = 1.0f / l_tot;
   const float lse_nat = (m_run + fast_log2(l_tot)) * kLn2;
   const int64_t row = int64_t(r) * H + head;
-  if (single) {
+  if (a.direct) {
     uint16_t* op = static_cast<uint16_t*>(a.out) + row * kRank;
 #pragma unroll
     for (int dt = 0; dt < 32; ++dt) {

@@ -237,3 +237,34 @@ def test_long_context_decode_full_size(longctx):
     for r in (0, 3):
         check_close(out[r], oref[r], f"request {r}")
         check_lse(lse[r], lref[r], f"request {r}")
+
+
+def test_two_stage_decode_matches_one_call():
+    """out = NULL runs stage 1 only; pa_lse_merge over its partials gives the
+    one-call result (the pages' two-stage split-KV form)."""
+    say("decode two-stage")
+    b = _small(21, [700, 33, 1, 2000], 32, 8, W.BF16)
+    cache_t, out1, lse1 = _run_decode(b, num_splits=5)
+    part = pa.decode(to_dev(b.q), cache_t, to_dev(b.block_table), to_dev(b.seq_lens),
+                     b.max_seq_len, b.scale, num_splits=5, stage1_only=True)
+    out2, lse2 = pa.lse_merge(part, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert part.shape == (4, 32, 5, 129)
+    assert np.array_equal(to_f64(out2), out1)
+    assert np.array_equal(lse2.cpu().numpy().astype(np.float64), lse1)
+    # the partials themselves: each non-empty split against the oracle's split
+    cache = O.cache_write_kv(b.cache, b.k_new, b.v_new, b.slot_mapping)
+    p = part.cpu().numpy().astype(np.float64)
+    P = -(-b.max_seq_len // 5)
+    P = -(-P // b.block_size) * b.block_size
+    for r in range(4):
+        K, V = O.gather_kv(cache, b.block_table[r], int(b.seq_lens[r]))
+        q = O.to_f64(b.q[r:r + 1])
+        for s in range(5):
+            lo, hi = s * P, min(int(b.seq_lens[r]), (s + 1) * P)
+            if lo >= hi:
+                assert np.all(p[r, :, s, 128] == -np.inf)
+                continue
+            o, l = O.partial_attention(q, K, V, b.scale, lo, hi, None)
+            check_close(p[r, :, s, :128], o[0], f"partial r={r} s={s}", atol=2e-3, rtol=2e-3)
+            check_lse(p[r, :, s, 128], l[0], f"partial lse r={r} s={s}")

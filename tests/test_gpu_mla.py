@@ -93,3 +93,17 @@ def test_mla_full_size(mla_full):
         check_close(out[r], oref[r], f"request {r}")
         check_lse(lse[r], lref[r], f"request {r}")
     assert np.array_equal(bits(cache_t), cache_ref)
+
+
+def test_mla_two_stage_matches_one_call():
+    say("mla two-stage")
+    b = W.make_mla(13, [1500, 64, 700], 32, 512, 64, 64)
+    cache_t, out1, lse1 = _run(b, num_splits=4)
+    part = pa.mla_decode(to_dev(b.q_nope), to_dev(b.q_pe), cache_t, to_dev(b.block_table),
+                         to_dev(b.seq_lens), b.max_seq_len, b.scale, num_splits=4,
+                         stage1_only=True)
+    out2, lse2 = pa.lse_merge(part, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert part.shape == (3, 32, 4, 513)
+    assert np.array_equal(to_f64(out2), out1)
+    assert np.array_equal(lse2.cpu().numpy().astype(np.float64), lse1)

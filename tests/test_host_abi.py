@@ -95,7 +95,8 @@ def _decode(lib, **kw):
     (dict(d=100), INVALID),                 # not a multiple of 8
     (dict(hq=96, hkv=8), UNSUPPORTED),      # group 12
     (dict(q=None), INVALID),
-    (dict(out=None), INVALID),
+    (dict(out=None), WORKSPACE),            # partial-only mode needs a workspace
+    (dict(out=None, lse=1 << 29), INVALID), # lse requested without out
     (dict(table=None), INVALID),
     (dict(k=1 << 25), INVALID),             # k without v / slots
     (dict(k=1 << 25, v=1 << 26), INVALID),  # k, v without slots
