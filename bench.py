@@ -97,8 +97,8 @@ def gqa_decode_case(b, num_splits, name):
     by = W.gqa_bytes(b)
     kb = by["kv"] + by["q"] + by["meta"] - b.num_tokens * 8   # split kernel: KV, q, table walk
     fl = W.gqa_flops(b)
-    kname = "decode_split_kernel<%s, %d>" % ("true" if b.dtype == W.BF16 else "false",
-                                             b.num_q_heads // b.num_kv_heads)
+    g = b.num_q_heads // b.num_kv_heads
+    kname = (f"decode_mfma_kernel<{g}>" if b.dtype == W.BF16 else f"decode_split_kernel<false, {g}>")
     info = {"num_seqs": b.num_seqs, "num_q_heads": b.num_q_heads, "num_kv_heads": b.num_kv_heads,
             "head_dim": b.head_dim, "block_size": b.block_size, "dtype": b.dtype,
             "max_seq_len": b.max_seq_len, "total_keys": int(b.seq_lens.sum()),
@@ -180,7 +180,7 @@ def build_cases(only):
         "mla_latent_decode_bf16": lambda: mla_case(W.mla_decode_batch(), "mla_latent_decode_bf16"),
     }
     names = [HEADLINE] + [n for n in makers if n != HEADLINE]
-    if only:
+    if only is not None:
         names = [n for n in names if n in only or n == HEADLINE]
     for n in names:
         t = time.perf_counter()

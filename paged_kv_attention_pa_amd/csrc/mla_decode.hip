@@ -55,7 +55,7 @@ __device__ __forceinline__ float head_sum(float x) {
 __global__ __launch_bounds__(512) void mla_split_kernel(MlaDecode a) {
   __shared__ __align__(16) char smem[2 * kTileBytes];
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = wave_id();
   const int nthreads = blockDim.x;
   const int tid = threadIdx.x;
   const int H = a.num_heads;
@@ -103,21 +103,24 @@ __global__ __launch_bounds__(512) void mla_split_kernel(MlaDecode a) {
   const int32_t* table = a.block_table + int64_t(r) * a.max_blocks;
   constexpr int kPerThread = (kBN * kChunks + 64 * kMaxWaves - 1) / (64 * kMaxWaves);  // 5
   u32x4_t stg[kPerThread];
+  // A 32-key tile spans at most two pages: their ids are wave-uniform scalar
+  // loads and each row picks one.  Keys past t1 re-read key t1 - 1 (finite,
+  // masked out below), so every load is unconditional.
   auto gload = [&](int tile) {
+    const int key0 = t0 + tile * kBN;
+    const int kl0 = min(key0, t1 - 1), kl1 = min(key0 + kBN - 1, t1 - 1);
+    int64_t b0 = uniform_load(table + kl0 / bs), b1 = uniform_load(table + kl1 / bs);
+    b0 = (b0 < 0 || b0 >= a.num_blocks) ? 0 : b0;
+    b1 = (b1 < 0 || b1 >= a.num_blocks) ? 0 : b1;
+    const int pg0 = kl0 / bs;
 #pragma unroll
     for (int i = 0; i < kPerThread; ++i) {
-      const int c = tid + i * nthreads;
-      stg[i] = u32x4_t{0, 0, 0, 0};
-      if (c < kBN * kChunks) {
-        const int row = c / kChunks;
-        const int col = c - row * kChunks;
-        const int key = t0 + tile * kBN + row;
-        if (key < t1) {
-          int64_t blk = table[key / bs];
-          blk = (blk < 0 || blk >= a.num_blocks) ? 0 : blk;
-          stg[i] = load16(cache + (blk * bs + (key % bs)) * kRow + 8 * col);
-        }
-      }
+      const int c = min(tid + i * nthreads, kBN * kChunks - 1);
+      const int row = c / kChunks;
+      const int col = c - row * kChunks;
+      const int key = min(key0 + row, t1 - 1);
+      const int64_t blk = (key / bs == pg0) ? b0 : b1;
+      stg[i] = load16(cache + (blk * bs + (key % bs)) * kRow + 8 * col);
     }
   };
   auto lstore = [&](int buf) {

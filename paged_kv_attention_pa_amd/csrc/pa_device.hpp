@@ -82,6 +82,22 @@ __device__ __forceinline__ float lane_xor(float x, int m) {
       (lane ^ m) << 2, __builtin_bit_cast(int, x)));
 }
 
+// Index of the calling wave in its work-group, as a wave-uniform (scalar) value.
+__device__ __forceinline__ int wave_id() {
+  return __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+}
+
+// ------------------------------------------------------- scalar metadata
+// Wave-uniform reads of read-only metadata (block tables, lengths) through the
+// constant address space, so that they become scalar loads: those complete on
+// their own counter and never make the vector-memory waits of the K/V stream
+// conservative.
+template <typename T>
+__device__ __forceinline__ T uniform_load(const T* p) {
+  return *reinterpret_cast<const __attribute__((address_space(4))) T*>(
+      reinterpret_cast<uintptr_t>(p));
+}
+
 // ------------------------------------------------------------ 16-B access
 __device__ __forceinline__ u32x4_t load16(const void* p) {
   return *reinterpret_cast<const u32x4_t*>(p);

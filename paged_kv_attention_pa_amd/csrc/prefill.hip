@@ -49,7 +49,7 @@ __device__ __forceinline__ uint2 lds_read_tr(const char* p) {
 __global__ __launch_bounds__(256) void prefill_kernel(PrefillVarlen a) {
   __shared__ __align__(16) char smem[4 * kTileBytes];   // 2 x (K tile, V tile)
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = wave_id();
   const int tid = threadIdx.x;
   const int Hq = a.num_q_heads;
   const int G = Hq / a.num_kv_heads;
@@ -94,21 +94,21 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillVarlen a) {
   const int ld_chunk = tid & 15;
   const int ld_key = tid >> 4;           // + 16 i, i = 0..3
   u32x4_t stk[4], stv[4];
+  // Keys ld_key + 16 i of a tile share one page per i (tiles and 16-key groups
+  // are 16-aligned, pages are multiples of 16): the page ids are wave-uniform
+  // scalar loads.  Keys past kv_end re-read key kv_end - 1 (finite, masked
+  // out below), so every load is unconditional and the waits stay exact.
   auto gload = [&](int tile) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int key = tile * kBN + ld_key + 16 * i;
-      if (key < kv_end) {
-        int64_t blk = table[key / bs];
-        blk = (blk < 0 || blk >= a.num_blocks) ? 0 : blk;
-        const uint16_t* p = cache + (blk * 2 * bs + (key % bs)) * tok_stride +
-                            int64_t(kvh) * kD + 8 * ld_chunk;
-        stk[i] = load16(p);
-        stv[i] = load16(p + kv_stride);
-      } else {
-        stk[i] = u32x4_t{0, 0, 0, 0};   // keys past the end: zero, never NaN
-        stv[i] = u32x4_t{0, 0, 0, 0};
-      }
+      const int key16 = min(tile * kBN + 16 * i, ((kv_end - 1) / 16) * 16);
+      int64_t blk = uniform_load(table + key16 / bs);
+      blk = (blk < 0 || blk >= a.num_blocks) ? 0 : blk;
+      const int key = min(key16 + ld_key, kv_end - 1);
+      const uint16_t* p = cache + (blk * 2 * bs + (key - (key16 / bs) * bs)) * tok_stride +
+                          int64_t(kvh) * kD + 8 * ld_chunk;
+      stk[i] = load16(p);
+      stv[i] = load16(p + kv_stride);
     }
   };
   auto lstore = [&](int buf) {
