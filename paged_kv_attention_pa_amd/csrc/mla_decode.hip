@@ -28,9 +28,15 @@ constexpr int kRope = 64;
 constexpr int kRow = kRank + kRope;             // 576 elements
 constexpr int kChunks = kRow * 2 / 16;          // 72 x 16 B per row
 constexpr int kBN = 32;                         // keys per tile
-constexpr int kRowBytes = kRow * 2 + 16;        // padded LDS row
-constexpr int kTileBytes = kBN * kRowBytes;     // 37376 B
+constexpr int kRowBytes = kRow * 2;             // 1152 B, unpadded (swizzled)
+constexpr int kTileBytes = kBN * kRowBytes;     // 36864 B
+constexpr int kTileLoads = kBN * kChunks / 64;  // 36 wave-wide 16-byte loads per tile
 constexpr int kMaxWaves = 8;
+
+// 16-byte chunk c of latent row r sits in LDS slot c ^ (r % 8) of the row
+// (within its aligned group of eight), spreading K-row and V-column reads
+// over all banks.
+__device__ __forceinline__ int tile_off(int r, int c) { return r * kRowBytes + 16 * (c ^ (r & 7)); }
 
 typedef __attribute__((ext_vector_type(4))) short s16x4_t;
 
@@ -98,43 +104,34 @@ __global__ __launch_bounds__(512) void mla_split_kernel(MlaDecode a) {
     for (int kk = 0; kk < 2; ++kk) qf[16 + kk] = load16(qp + 32 * kk + 8 * kq);
   }
 
-  // ---- cooperative gather of a tile: 32 rows x 72 chunks of 16 B
+  // ---- gather of a tile straight into LDS: 36 wave-wide loads of 64 x 16 B
+  // (global_load_lds_dwordx4; lane i lands at byte 16 i of the load's 1 KiB),
+  // wave w issuing loads w, w + 8, ...  Position p = 64 j + i of load j is
+  // row p / 72, slot p % 72, which holds chunk slot ^ (row % 8).  A 32-key
+  // tile spans at most two pages, whose ids are wave-uniform scalar loads.
+  // Keys past t1 re-read key t1 - 1 (finite, masked out below).
   const uint16_t* cache = static_cast<const uint16_t*>(a.cache);
   const int32_t* table = a.block_table + int64_t(r) * a.max_blocks;
-  constexpr int kPerThread = (kBN * kChunks + 64 * kMaxWaves - 1) / (64 * kMaxWaves);  // 5
-  u32x4_t stg[kPerThread];
-  // A 32-key tile spans at most two pages: their ids are wave-uniform scalar
-  // loads and each row picks one.  Keys past t1 re-read key t1 - 1 (finite,
-  // masked out below), so every load is unconditional.
-  auto gload = [&](int tile) {
+  auto gload = [&](int tile, char* dst) {
     const int key0 = t0 + tile * kBN;
     const int kl0 = min(key0, t1 - 1), kl1 = min(key0 + kBN - 1, t1 - 1);
     int64_t b0 = uniform_load(table + kl0 / bs), b1 = uniform_load(table + kl1 / bs);
     b0 = (b0 < 0 || b0 >= a.num_blocks) ? 0 : b0;
     b1 = (b1 < 0 || b1 >= a.num_blocks) ? 0 : b1;
     const int pg0 = kl0 / bs;
-#pragma unroll
-    for (int i = 0; i < kPerThread; ++i) {
-      const int c = min(tid + i * nthreads, kBN * kChunks - 1);
-      const int row = c / kChunks;
-      const int col = c - row * kChunks;
+    for (int j = wave; j < kTileLoads; j += kMaxWaves) {
+      const int pos = 64 * j + lane;
+      const int row = pos / kChunks;
+      const int slot = pos - row * kChunks;
       const int key = min(key0 + row, t1 - 1);
       const int64_t blk = (key / bs == pg0) ? b0 : b1;
-      stg[i] = load16(cache + (blk * bs + (key % bs)) * kRow + 8 * col);
+      const uint16_t* src = cache + (blk * bs + (key % bs)) * kRow + 8 * (slot ^ (row & 7));
+      __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(dst + 1024 * j),
+                                       16, 0, 0);
     }
   };
-  auto lstore = [&](int buf) {
-    char* tl = smem + buf * kTileBytes;
-#pragma unroll
-    for (int i = 0; i < kPerThread; ++i) {
-      const int c = tid + i * nthreads;
-      if (c < kBN * kChunks) {
-        const int row = c / kChunks;
-        const int col = c - row * kChunks;
-        *reinterpret_cast<u32x4_t*>(tl + row * kRowBytes + 16 * col) = stg[i];
-      }
-    }
-  };
+  // all of this wave's tile loads have landed (the caller then syncs the group)
+  auto gwait = [&]() { __builtin_amdgcn_s_waitcnt(0x0F70); };   // vmcnt(0)
 
   const float scale2 = a.scale * kLog2e;
   float m_run = kNoMax;
@@ -143,13 +140,13 @@ __global__ __launch_bounds__(512) void mla_split_kernel(MlaDecode a) {
 #pragma unroll
   for (int dt = 0; dt < 32; ++dt) acc[dt] = f32x4_t{0, 0, 0, 0};
 
-  gload(0);
-  lstore(0);
+  gload(0, smem);
+  gwait();
   __syncthreads();
 
   for (int t = 0; t < n_tiles; ++t) {
     const int buf = t & 1;
-    if (t + 1 < n_tiles) gload(t + 1);
+    if (t + 1 < n_tiles) gload(t + 1, smem + (buf ^ 1) * kTileBytes);
     const char* tl = smem + buf * kTileBytes;
     const int key0 = t0 + t * kBN;
     if (active) {
@@ -158,10 +155,14 @@ __global__ __launch_bounds__(512) void mla_split_kernel(MlaDecode a) {
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
       sc[hh] = f32x4_t{0, 0, 0, 0};
-      const char* krow = tl + (16 * hh + (lane & 15)) * kRowBytes + 16 * kq;
+      // chunk 4 kk + kq of row krow: slot 8 (kk / 2) + ((4 (kk % 2) + kq) ^ (krow % 8)),
+      // i.e. two per-lane bases plus a constant offset per kk
+      const int krow = 16 * hh + (lane & 15);
+      const char* kb0 = tl + krow * kRowBytes + 16 * (kq ^ (krow & 7));
+      const char* kb1 = tl + krow * kRowBytes + 16 * ((4 + kq) ^ (krow & 7));
 #pragma unroll
       for (int kk = 0; kk < 18; ++kk) {
-        const u32x4_t kf = *reinterpret_cast<const u32x4_t*>(krow + 64 * kk);
+        const u32x4_t kf = *reinterpret_cast<const u32x4_t*>((kk & 1 ? kb1 : kb0) + 128 * (kk >> 1));
         sc[hh] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kf), as_bf16x8(qf[kk]), sc[hh], 0, 0, 0);
       }
     }
@@ -192,21 +193,30 @@ __global__ __launch_bounds__(512) void mla_split_kernel(MlaDecode a) {
     const u32x4_t pf = u32x4_t{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
                                pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])};
     // O^T += V^T P^T: keys 4 kq + (0..3) and 16 + 4 kq + (0..3)
+    // lane gi of group kq: 4 bf16 of rows 4 kq + gi/4 (+16) at dims
+    // 16 dt + 4 (gi % 4), i.e. chunk 2 dt + (gi % 4)/2, half gi % 2
+    // (slot 8 (dt / 4) + ((2 (dt % 4) + (gi % 4)/2) ^ (row % 8)): four per-lane
+    // bases plus a constant offset per dt; rows vrow and vrow + 16 share row % 8)
     const int gi = lane & 15;
-    const char* v1p = tl + (4 * kq + (gi >> 2)) * kRowBytes + 8 * (gi & 3);
-    const char* v2p = v1p + 16 * kRowBytes;
+    const int vrow = 4 * kq + (gi >> 2);
+    const int bsel = (gi & 3) >> 1;
+    const char* vb[4];
+#pragma unroll
+    for (int m4 = 0; m4 < 4; ++m4)
+      vb[m4] = tl + vrow * kRowBytes + 16 * ((2 * m4 + bsel) ^ (vrow & 7)) + 8 * (gi & 1);
 #pragma unroll
     for (int dt = 0; dt < 32; ++dt) {
-      const uint2 v1 = lds_read_tr(v1p + 32 * dt);
-      const uint2 v2 = lds_read_tr(v2p + 32 * dt);
+      const char* vp = vb[dt & 3] + 128 * (dt >> 2);
+      const uint2 v1 = lds_read_tr(vp);
+      const uint2 v2 = lds_read_tr(vp + 16 * kRowBytes);
       const u32x4_t vf = u32x4_t{v1.x, v1.y, v2.x, v2.y};
       acc[dt] *= alpha;
       acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vf), as_bf16x8(pf), acc[dt], 0, 0, 0);
     }
     }  // active
     if (t + 1 < n_tiles) {
-      lstore(buf ^ 1);
-      __syncthreads();
+      gwait();           // this wave's loads of tile t + 1 have landed
+      __syncthreads();   // everyone's have, and everyone is done with tile t
     }
   }
 
