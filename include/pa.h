@@ -40,6 +40,7 @@
  *   设计动机).  block_size must be a multiple of 16 ("AttentionBackend", 边界与
  *   失败).  All tensors are dense, row-major, in the shapes given, unless a
  *   stride argument says otherwise.
+ * Scale.  The softmax scale multiplies Q K^T; it must be finite and >= 0.
  * Query-to-KV head map.  Query head h reads KV head h / (num_q_heads /
  *   num_kv_heads) ("第 1 章 注意力后端", §3.2: groups of query heads share a
  *   KV head).

@@ -42,6 +42,8 @@ pa_status_t hip_fail(hipError_t e, const char* what) {
 
 bool is_pow2_group(int g) { return g == 1 || g == 2 || g == 4 || g == 8; }
 
+bool scale_ok(float s) { return s >= 0.0f && s <= 3.0e38f; }   // finite, not negative
+
 // Tokens per split for n splits over max_seq_len keys, rounded up to whole
 // pages; at least one page.
 int split_tokens_for(int max_seq_len, int n, int block_size) {
@@ -179,6 +181,7 @@ pa_status_t pa_decode(pa_dtype_t dtype,
                       void* workspace, size_t workspace_bytes,
                       void* out, float* lse, hipStream_t stream) {
   PA_REQUIRE(dtype == PA_F32 || dtype == PA_BF16, PA_ERR_INVALID, "unknown dtype %d", int(dtype));
+  PA_REQUIRE(scale_ok(scale), PA_ERR_INVALID, "scale must be finite and >= 0");
   pa_status_t st = check_common_cache(num_blocks, block_size, block_table, max_blocks_per_seq,
                                       seq_lens, num_seqs, max_seq_len);
   if (st != PA_OK) return st;
@@ -266,6 +269,7 @@ pa_status_t pa_prefill_varlen(pa_dtype_t dtype,
                               float scale, int causal,
                               void* out, float* lse, hipStream_t stream) {
   PA_REQUIRE(dtype == PA_F32 || dtype == PA_BF16, PA_ERR_INVALID, "unknown dtype %d", int(dtype));
+  PA_REQUIRE(scale_ok(scale), PA_ERR_INVALID, "scale must be finite and >= 0");
   pa_status_t st = check_common_cache(num_blocks, block_size, block_table, max_blocks_per_seq,
                                       seq_lens, num_seqs, max_seq_len);
   if (st != PA_OK) return st;
@@ -315,6 +319,7 @@ pa_status_t pa_mla_decode(const void* q_nope, int64_t qn_stride_b, int64_t qn_st
                           float scale, int num_splits,
                           void* workspace, size_t workspace_bytes,
                           void* out, float* lse, hipStream_t stream) {
+  PA_REQUIRE(scale_ok(scale), PA_ERR_INVALID, "scale must be finite and >= 0");
   pa_status_t st = check_common_cache(num_blocks, block_size, block_table, max_blocks_per_seq,
                                       seq_lens, num_seqs, max_seq_len);
   if (st != PA_OK) return st;

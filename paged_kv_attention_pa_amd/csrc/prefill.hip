@@ -19,7 +19,8 @@
 // With the MFMA output layout (lane l holds column l % 32) the row max,
 // running sum and rescale of a query row live in lane l and lane l ^ 32.
 // Tiles entirely above the diagonal are skipped; diagonal tiles mask per
-// element.  Work-groups are ordered longest tile first.
+// element.  Work-group ids keep each (request, KV head) on one XCD (L2 reuse
+// of its K/V), longest q tile first.
 #include "launch.hpp"
 #include "pa_device.hpp"
 
@@ -29,8 +30,13 @@ namespace {
 constexpr int kD = 128;
 constexpr int kBM = 128;           // query rows per work-group
 constexpr int kBN = 64;            // keys per tile
-constexpr int kRowBytes = kD * 2 + 16;   // padded LDS row (bank spread)
-constexpr int kTileBytes = kBN * kRowBytes;
+constexpr int kRowBytes = kD * 2;        // 256 B per key row (unpadded, swizzled)
+constexpr int kTileBytes = kBN * kRowBytes;  // 16 KiB
+constexpr int kTileLoads = kBN * kRowBytes / 1024;  // 16 wave-wide 16-byte loads per tile
+// 16-byte chunk c of key row r sits in slot c ^ (r % 8) of the row (within
+// its aligned group of eight): spreads the K-row and V-column reads over the
+// banks while keeping per-lane address bases plus constant offsets.
+constexpr int kXcds = 8;           // accelerator dies work-groups are dealt to
 
 typedef __attribute__((ext_vector_type(4))) short s16x4_t;
 
@@ -46,7 +52,7 @@ __device__ __forceinline__ uint2 lds_read_tr(const char* p) {
   return __builtin_bit_cast(uint2, v);
 }
 
-__global__ __launch_bounds__(256) void prefill_kernel(PrefillVarlen a) {
+__global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillVarlen a) {
   __shared__ __align__(16) char smem[4 * kTileBytes];   // 2 x (K tile, V tile)
   const int lane = threadIdx.x & 63;
   const int wave = wave_id();
@@ -54,12 +60,24 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillVarlen a) {
   const int Hq = a.num_q_heads;
   const int G = Hq / a.num_kv_heads;
 
-  // work-group -> (q tile, request, head); larger tile index first
+  // work-group -> (request, KV head, q tile, head of the group).  Work-groups
+  // are dealt to the 8 XCDs round-robin by id, so ids are arranged such that
+  // every q tile and query head of one (request, KV head) pair land on the
+  // same XCD, one after another: that pair's K/V (at most a few MB) is read
+  // from HBM once and then served by that XCD's L2.  Within a pair, the
+  // longest (last) q tiles go first.
   const int n_qt = (a.max_query_len + kBM - 1) / kBM;
-  int id = blockIdx.x;
-  const int h = id % Hq; id /= Hq;
-  const int r = id % a.num_seqs;
-  const int qt = n_qt - 1 - id / a.num_seqs;
+  const int per_pair = n_qt * G;
+  const int id = blockIdx.x;
+  const int xcd = id % kXcds;
+  const int slot = id / kXcds;
+  const int pair = (slot / per_pair) * kXcds + xcd;          // (request, KV head)
+  if (pair >= a.num_seqs * a.num_kv_heads) return;
+  const int local = slot % per_pair;
+  const int r = pair / a.num_kv_heads;
+  const int kvh0 = pair % a.num_kv_heads;
+  const int qt = n_qt - 1 - local / G;
+  const int h = kvh0 * G + local % G;
   const int q_start = min(max(a.query_start_loc[r], 0), a.num_tokens);
   const int L = min(min(a.query_start_loc[r + 1] - q_start, a.max_query_len), a.num_tokens - q_start);
   const int bs = a.block_size;
@@ -67,7 +85,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillVarlen a) {
   const int q0 = qt * kBM;
   if (q0 >= L || L <= 0) return;
   const int C = S - L;                    // keys before the chunk
-  const int kvh = h / G;
+  const int kvh = kvh0;
 
   // keys this work-group may see
   int kv_end = S;
@@ -86,41 +104,36 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillVarlen a) {
     for (int kk = 0; kk < 8; ++kk) qf[kk] = row_ok ? load16(qp + 16 * kk) : u32x4_t{0, 0, 0, 0};
   }
 
-  // ---- cooperative gather of one K/V tile: 64 keys x 16 chunks of 16 B each
+  // ---- gather of one K/V tile straight into LDS (global_load_lds_dwordx4):
+  // 16 wave-wide loads per half, wave w issuing loads w, w + 4, w + 8, w + 12.
+  // Load j fills rows 4 j .. 4 j + 3 (lane i: row 4 j + i / 16, slot i % 16,
+  // which holds chunk slot ^ (row % 8)).  The four rows of a load share one
+  // page (16-key groups are 16-aligned, pages are multiples of 16): the page
+  // id is a wave-uniform scalar load.  Keys past kv_end re-read key
+  // kv_end - 1 (finite, masked out below).
   const int64_t tok_stride = int64_t(a.num_kv_heads) * kD;
   const int64_t kv_stride = int64_t(bs) * tok_stride;
   const uint16_t* cache = static_cast<const uint16_t*>(a.cache);
   const int32_t* table = a.block_table + int64_t(r) * a.max_blocks;
-  const int ld_chunk = tid & 15;
-  const int ld_key = tid >> 4;           // + 16 i, i = 0..3
-  u32x4_t stk[4], stv[4];
-  // Keys ld_key + 16 i of a tile share one page per i (tiles and 16-key groups
-  // are 16-aligned, pages are multiples of 16): the page ids are wave-uniform
-  // scalar loads.  Keys past kv_end re-read key kv_end - 1 (finite, masked
-  // out below), so every load is unconditional and the waits stay exact.
-  auto gload = [&](int tile) {
+  auto gload = [&](int tile, char* kdst) {
+    char* vdst = kdst + kTileBytes;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int key16 = min(tile * kBN + 16 * i, ((kv_end - 1) / 16) * 16);
+    for (int jj = 0; jj < kTileLoads / 4; ++jj) {
+      const int j = wave + 4 * jj;
+      const int row = 4 * j + (lane >> 4);
+      const int key16 = min(tile * kBN + 16 * (j >> 2), ((kv_end - 1) / 16) * 16);
       int64_t blk = uniform_load(table + key16 / bs);
       blk = (blk < 0 || blk >= a.num_blocks) ? 0 : blk;
-      const int key = min(key16 + ld_key, kv_end - 1);
-      const uint16_t* p = cache + (blk * 2 * bs + (key - (key16 / bs) * bs)) * tok_stride +
-                          int64_t(kvh) * kD + 8 * ld_chunk;
-      stk[i] = load16(p);
-      stv[i] = load16(p + kv_stride);
+      const int key = min(key16 + (row & 15), kv_end - 1);
+      const int chunk = (lane & 15) ^ (row & 7);
+      const uint16_t* src = cache + (blk * 2 * bs + (key - (key16 / bs) * bs)) * tok_stride +
+                            int64_t(kvh) * kD + 8 * chunk;
+      typedef __attribute__((address_space(3))) void* lds_ptr;
+      __builtin_amdgcn_global_load_lds(src, (lds_ptr)(kdst + 1024 * j), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(src + kv_stride, (lds_ptr)(vdst + 1024 * j), 16, 0, 0);
     }
   };
-  auto lstore = [&](int buf) {
-    char* kt = smem + buf * 2 * kTileBytes;
-    char* vt = kt + kTileBytes;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int off = (ld_key + 16 * i) * kRowBytes + ld_chunk * 16;
-      *reinterpret_cast<u32x4_t*>(kt + off) = stk[i];
-      *reinterpret_cast<u32x4_t*>(vt + off) = stv[i];
-    }
-  };
+  auto gwait = [&]() { __builtin_amdgcn_s_waitcnt(0x0F70); };   // vmcnt(0)
 
   const float scale2 = a.scale * kLog2e;
   float m_run = kNoMax;   // running max (base-2 domain) of row my_row
@@ -132,15 +145,15 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillVarlen a) {
     for (int i = 0; i < 16; ++i) acc[dt][i] = 0.0f;
 
   if (n_tiles > 0) {
-    gload(0);
-    lstore(0);
+    gload(0, smem);
+    gwait();
   }
   __syncthreads();
 
   const int row_abs = C + my_row;         // last key this row may see (causal)
   for (int t = 0; t < n_tiles; ++t) {
     const int buf = t & 1;
-    if (t + 1 < n_tiles) gload(t + 1);    // in flight during the math below
+    if (t + 1 < n_tiles) gload(t + 1, smem + (buf ^ 1) * 2 * kTileBytes);   // in flight below
     const char* kt = smem + buf * 2 * kTileBytes;
     const char* vt = kt + kTileBytes;
     const int key0 = t * kBN;
@@ -151,32 +164,39 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillVarlen a) {
     for (int hh = 0; hh < 2; ++hh) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) s[hh][i] = 0.0f;
-      const char* krow = kt + (hh * 32 + (lane & 31)) * kRowBytes + 16 * (lane >> 5);
+      // chunk 2 kk + (l / 32) of row 32 hh + l % 32: slot 8 (kk / 4) +
+      // ((2 (kk % 4) + l / 32) ^ (l % 8)) -> four per-lane bases
+      const char* krow = kt + (hh * 32 + (lane & 31)) * kRowBytes;
+      const char* kb[4];
+#pragma unroll
+      for (int m4 = 0; m4 < 4; ++m4) kb[m4] = krow + 16 * ((2 * m4 + (lane >> 5)) ^ (lane & 7));
 #pragma unroll
       for (int kk = 0; kk < 8; ++kk) {
-        const u32x4_t kf = *reinterpret_cast<const u32x4_t*>(krow + 32 * kk);
+        const u32x4_t kf = *reinterpret_cast<const u32x4_t*>(kb[kk & 3] + 128 * (kk >> 2));
         s[hh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kf), as_bf16x8(qf[kk]), s[hh], 0, 0, 0);
       }
     }
 
-    // mask, scale, tile max (keys of this lane, then lane ^ 32)
+    // mask, tile max of the raw scores (this lane's keys, then lane ^ 32);
+    // scale > 0, so the scaled max is the max of the scaled scores
     const bool need_mask = (key0 + kBN > kv_end) || (a.causal && key0 + kBN - 1 > C + q0 + wave * 32);
     float tmax = -INFINITY;
+    if (need_mask) {
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = key0 + hh * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+          const bool vis = key < kv_end && (!a.causal || key <= row_abs);
+          s[hh][i] = vis ? s[hh][i] : -INFINITY;
+        }
+    }
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float v = s[hh][i] * scale2;
-        if (need_mask) {
-          const int key = key0 + hh * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-          const bool vis = key < kv_end && (!a.causal || key <= row_abs);
-          v = vis ? v : -INFINITY;
-        }
-        s[hh][i] = v;
-        tmax = fmaxf(tmax, v);
-      }
+      for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, s[hh][i]);
     tmax = fmaxf(tmax, lane_xor(tmax, 32));
-    const float m_new = fmaxf(m_run, tmax);
+    const float m_new = fmaxf(m_run, tmax == -INFINITY ? -INFINITY : tmax * scale2);
     const float alpha = fast_exp2(m_run - m_new);
     m_run = m_new;
 
@@ -190,42 +210,49 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillVarlen a) {
         float p[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          p[j] = fast_exp2(s[hh][8 * st + j] - m_new);
+          const float x = s[hh][8 * st + j];
+          p[j] = x == -INFINITY ? 0.0f : fast_exp2(fmaf(x, scale2, -m_new));
           psum += p[j];
         }
         pf[2 * hh + st] = u32x4_t{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
                                   pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])};
       }
     l_run = l_run * alpha + psum;
+    if (__any(alpha != 1.0f)) {   // the running max moved for some row of this wave
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
+      for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) acc[dt][i] *= alpha;
+        for (int i = 0; i < 16; ++i) acc[dt][i] *= alpha;
+    }
 
-    // O^T += V^T P^T: 4 key steps of 16 x 4 d tiles of 32
+    // O^T += V^T P^T: 4 key steps of 16 x 4 d tiles of 32.  Lane gi of
+    // 16-lane group grp reads 4 bf16 of key row kbase + gi/4 (+8) at dims
+    // 32 dt + 16 (grp % 2) + 4 (gi % 4): chunk 4 dt + c0, half gi % 2, with
+    // c0 = 2 (grp % 2) + (gi % 4)/2; slot 8 (dt / 2) + ((4 (dt % 2) + c0) ^ (row % 8)).
     const int grp = lane >> 4;              // 16-lane group
     const int gi = lane & 15;
     const int kg = lane >> 5;               // k group
-    const int dhalf = grp & 1;
+    const int c0 = 2 * (grp & 1) + ((gi & 3) >> 1);
+    const int vr0 = 4 * kg + (gi >> 2);     // key row within a 16-key step (row % 8 fixed)
+    const char* vb0 = vt + vr0 * kRowBytes + 16 * (c0 ^ (vr0 & 7)) + 8 * (gi & 1);
+    const char* vb1 = vt + vr0 * kRowBytes + 16 * ((4 + c0) ^ (vr0 & 7)) + 8 * (gi & 1);
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      const int kbase = 16 * ks + 4 * kg;   // keys kbase..+3 and kbase+8..+11
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) {
-        const int dcol = 32 * dt + 16 * dhalf + 4 * (gi & 3);
-        const uint32_t o1 = uint32_t((kbase + (gi >> 2)) * kRowBytes + dcol * 2);
-        const uint32_t o2 = o1 + 8 * kRowBytes;
-        const uint2 v1 = lds_read_tr(vt + o1);
-        const uint2 v2 = lds_read_tr(vt + o2);
+        const char* vp = (dt & 1 ? vb1 : vb0) + 128 * (dt >> 1) + 16 * ks * kRowBytes;
+        const uint2 v1 = lds_read_tr(vp);
+        const uint2 v2 = lds_read_tr(vp + 8 * kRowBytes);
         const u32x4_t vf = u32x4_t{v1.x, v1.y, v2.x, v2.y};
         acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vf), as_bf16x8(pf[ks]), acc[dt], 0, 0, 0);
       }
     }
 
     if (t + 1 < n_tiles) {
-      // buffer buf ^ 1 was last read in iteration t - 1, which every wave
-      // finished before the barrier that ended it
-      lstore(buf ^ 1);
+      // this wave's loads of tile t + 1 have landed; after the barrier every
+      // wave's have, and every wave is done reading buffer buf, which the
+      // loads issued at the start of iteration t + 1 refill
+      gwait();
       __syncthreads();
     }
   }
@@ -255,7 +282,9 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillVarlen a) {
 hipError_t launch_prefill_varlen(const PrefillVarlen& a, hipStream_t s) {
   if (a.num_seqs <= 0 || a.num_tokens <= 0 || a.max_query_len <= 0) return hipSuccess;
   const int n_qt = (a.max_query_len + kBM - 1) / kBM;
-  const int64_t wgs = int64_t(n_qt) * a.num_seqs * a.num_q_heads;
+  const int G = a.num_q_heads / a.num_kv_heads;
+  const int64_t pairs = int64_t(a.num_seqs) * a.num_kv_heads;
+  const int64_t wgs = (pairs + kXcds - 1) / kXcds * kXcds * n_qt * G;
   if (wgs > INT32_MAX) return hipErrorInvalidValue;
   hipLaunchKernelGGL(prefill_kernel, dim3(unsigned(wgs)), dim3(256), 0, s, a);
   return hipGetLastError();

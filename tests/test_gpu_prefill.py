@@ -128,3 +128,13 @@ def test_chunked_prefill_full_size(chunked):
         check_close(out[a0:a1], oref[a0:a1], f"request {r}")
         check_lse(lse[a0:a1], lref[a0:a1], f"request {r}")
     assert np.array_equal(bits(cache_t), cache_ref)
+
+
+def test_prefill_scale_zero_is_uniform_attention():
+    """scale = 0: every visible key weighs the same (masked keys still none)."""
+    say("prefill scale 0")
+    b = W.make_gqa(13, [100, 3], [300, 3], 8, 2, 128, 16, W.BF16, scale=0.0)
+    _, out, lse = _run(b)
+    _, oref, lref = _oracle(b)
+    check_close(out, oref, "scale 0 out")
+    check_lse(lse, lref, "scale 0 lse")

@@ -174,3 +174,9 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(b, "_LIB_PATH", str(tmp_path / "libpa.so"))
     with pytest.raises(pa.PaError):
         b.library()
+
+
+def test_scale_must_be_finite_non_negative(lib):
+    assert _decode(lib, scale=-0.5) == INVALID
+    assert _decode(lib, scale=float("inf")) == INVALID
+    assert _decode(lib, scale=float("nan")) == INVALID
