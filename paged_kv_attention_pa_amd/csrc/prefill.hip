@@ -21,6 +21,8 @@
 // Tiles entirely above the diagonal are skipped; diagonal tiles mask per
 // element.  Work-group ids keep each (request, KV head) on one XCD (L2 reuse
 // of its K/V), longest q tile first.
+#include <type_traits>
+
 #include "launch.hpp"
 #include "pa_device.hpp"
 
@@ -33,10 +35,14 @@ constexpr int kBN = 64;            // keys per tile
 constexpr int kRowBytes = kD * 2;        // 256 B per key row (unpadded, swizzled)
 constexpr int kTileBytes = kBN * kRowBytes;  // 16 KiB
 constexpr int kTileLoads = kBN * kRowBytes / 1024;  // 16 wave-wide 16-byte loads per tile
-// 16-byte chunk c of key row r sits in slot c ^ (r % 8) of the row (within
-// its aligned group of eight): spreads the K-row and V-column reads over the
-// banks while keeping per-lane address bases plus constant offsets.
-constexpr int kXcds = 8;           // accelerator dies work-groups are dealt to
+// 16-byte chunk c of key row r sits in slot c ^ swz(r) of the row, with
+// swz(r) = 2 (r % 8) + (r / 8) % 2 (a permutation of r % 16).  Rows are
+// 256 B, so every row starts on the same bank; the XOR spreads the 16 rows of
+// a K-fragment load, and rows 0..7 of a V transpose read (which move the
+// 4-slot groups), over all 16 slots, i.e. all banks.
+constexpr int kXcds = 8;
+constexpr float kSlack = 8.0f;     // lazy-rescale headroom, log2 units
+__device__ __forceinline__ int swz(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }           // accelerator dies work-groups are dealt to
 
 typedef __attribute__((ext_vector_type(4))) short s16x4_t;
 
@@ -125,7 +131,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillVarlen a) {
       int64_t blk = uniform_load(table + key16 / bs);
       blk = (blk < 0 || blk >= a.num_blocks) ? 0 : blk;
       const int key = min(key16 + (row & 15), kv_end - 1);
-      const int chunk = (lane & 15) ^ (row & 7);
+      const int chunk = (lane & 15) ^ swz(row);
       const uint16_t* src = cache + (blk * 2 * bs + (key - (key16 / bs) * bs)) * tok_stride +
                             int64_t(kvh) * kD + 8 * chunk;
       typedef __attribute__((address_space(3))) void* lds_ptr;
@@ -164,85 +170,100 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillVarlen a) {
     for (int hh = 0; hh < 2; ++hh) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) s[hh][i] = 0.0f;
-      // chunk 2 kk + (l / 32) of row 32 hh + l % 32: slot 8 (kk / 4) +
-      // ((2 (kk % 4) + l / 32) ^ (l % 8)) -> four per-lane bases
+      // chunk 2 kk + (l / 32) of row 32 hh + l % 32 sits in slot
+      // (2 kk + l / 32) ^ swz(l % 32): one per-lane address per kk (the row
+      // offset of the second half is a constant)
       const char* krow = kt + (hh * 32 + (lane & 31)) * kRowBytes;
-      const char* kb[4];
-#pragma unroll
-      for (int m4 = 0; m4 < 4; ++m4) kb[m4] = krow + 16 * ((2 * m4 + (lane >> 5)) ^ (lane & 7));
 #pragma unroll
       for (int kk = 0; kk < 8; ++kk) {
-        const u32x4_t kf = *reinterpret_cast<const u32x4_t*>(kb[kk & 3] + 128 * (kk >> 2));
+        const u32x4_t kf = *reinterpret_cast<const u32x4_t*>(
+            krow + 16 * ((2 * kk + (lane >> 5)) ^ swz(lane & 31)));
         s[hh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kf), as_bf16x8(qf[kk]), s[hh], 0, 0, 0);
       }
     }
 
-    // mask, tile max of the raw scores (this lane's keys, then lane ^ 32);
-    // scale > 0, so the scaled max is the max of the scaled scores
+    // Online softmax update for this tile.  Diagonal and tail tiles (wave-
+    // uniform `need_mask`) take the masked path; interior tiles skip every
+    // mask test.  The running max m_run is a reference that only moves when a
+    // tile's max exceeds it by more than kSlack (log2 units): until then the
+    // accumulator needs no rescale and P stays below 2^kSlack, well inside
+    // bf16/fp32 range.  scale > 0 makes the max of the raw scores, times the
+    // scale, the max of the scaled scores.
     const bool need_mask = (key0 + kBN > kv_end) || (a.causal && key0 + kBN - 1 > C + q0 + wave * 32);
-    float tmax = -INFINITY;
-    if (need_mask) {
+    u32x4_t pf[4];
+    float psum = 0.0f;
+    auto update = [&](auto masked_tag) {
+      constexpr bool kMasked = decltype(masked_tag)::value;
+      if constexpr (kMasked) {
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int key = key0 + hh * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+            const bool vis = key < kv_end && (!a.causal || key <= row_abs);
+            s[hh][i] = vis ? s[hh][i] : -INFINITY;
+          }
+      }
+      float tmax = -INFINITY;
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = key0 + hh * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-          const bool vis = key < kv_end && (!a.causal || key <= row_abs);
-          s[hh][i] = vis ? s[hh][i] : -INFINITY;
-        }
-    }
+        for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, s[hh][i]);
+      tmax = fmaxf(tmax, lane_xor(tmax, 32));
+      const float tm = tmax == -INFINITY ? -INFINITY : tmax * scale2;
+      if (__any(tm > m_run + kSlack)) {
+        const float m_new = fmaxf(m_run, tm);
+        const float alpha = fast_exp2(m_run - m_new);
+        m_run = m_new;
+        l_run *= alpha;
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh)
+        for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, s[hh][i]);
-    tmax = fmaxf(tmax, lane_xor(tmax, 32));
-    const float m_new = fmaxf(m_run, tmax == -INFINITY ? -INFINITY : tmax * scale2);
-    const float alpha = fast_exp2(m_run - m_new);
-    m_run = m_new;
-
-    // P^T in bf16, packed as the B operand: regs 8 st .. 8 st + 7 of half hh
-    u32x4_t pf[4];
-    float psum = 0.0f;
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        float p[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const float x = s[hh][8 * st + j];
-          p[j] = x == -INFINITY ? 0.0f : fast_exp2(fmaf(x, scale2, -m_new));
-          psum += p[j];
-        }
-        pf[2 * hh + st] = u32x4_t{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
-                                  pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])};
+          for (int i = 0; i < 16; ++i) acc[dt][i] *= alpha;
       }
-    l_run = l_run * alpha + psum;
-    if (__any(alpha != 1.0f)) {   // the running max moved for some row of this wave
+      // P^T in bf16, packed as the B operand: regs 8 st .. 8 st + 7 of half hh
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
+      for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) acc[dt][i] *= alpha;
-    }
+        for (int st = 0; st < 2; ++st) {
+          float p[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const float x = s[hh][8 * st + j];
+            const float e = fast_exp2(fmaf(x, scale2, -m_run));
+            p[j] = kMasked ? (x == -INFINITY ? 0.0f : e) : e;
+            psum += p[j];
+          }
+          pf[2 * hh + st] = u32x4_t{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
+                                    pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])};
+        }
+      l_run += psum;
+    };
+    if (need_mask) update(std::true_type{});
+    else update(std::false_type{});
 
     // O^T += V^T P^T: 4 key steps of 16 x 4 d tiles of 32.  Lane gi of
-    // 16-lane group grp reads 4 bf16 of key row kbase + gi/4 (+8) at dims
+    // 16-lane group grp reads 4 bf16 of key row 16 ks + vr0 (+8) at dims
     // 32 dt + 16 (grp % 2) + 4 (gi % 4): chunk 4 dt + c0, half gi % 2, with
-    // c0 = 2 (grp % 2) + (gi % 4)/2; slot 8 (dt / 2) + ((4 (dt % 2) + c0) ^ (row % 8)).
+    // c0 = 2 (grp % 2) + (gi % 4)/2, in slot (4 dt + c0) ^ swz(row): one base
+    // per (dt, row vr0 or vr0 + 8); 16 ks rows further is a constant offset.
     const int grp = lane >> 4;              // 16-lane group
     const int gi = lane & 15;
     const int kg = lane >> 5;               // k group
     const int c0 = 2 * (grp & 1) + ((gi & 3) >> 1);
-    const int vr0 = 4 * kg + (gi >> 2);     // key row within a 16-key step (row % 8 fixed)
-    const char* vb0 = vt + vr0 * kRowBytes + 16 * (c0 ^ (vr0 & 7)) + 8 * (gi & 1);
-    const char* vb1 = vt + vr0 * kRowBytes + 16 * ((4 + c0) ^ (vr0 & 7)) + 8 * (gi & 1);
+    const int vr0 = 4 * kg + (gi >> 2);     // key row within a 16-key step, < 8
+    const char* vb[2][4];
+#pragma unroll
+    for (int e = 0; e < 2; ++e)
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+        vb[e][dt] = vt + (vr0 + 8 * e) * kRowBytes + 16 * ((4 * dt + c0) ^ swz(vr0 + 8 * e)) + 8 * (gi & 1);
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) {
-        const char* vp = (dt & 1 ? vb1 : vb0) + 128 * (dt >> 1) + 16 * ks * kRowBytes;
-        const uint2 v1 = lds_read_tr(vp);
-        const uint2 v2 = lds_read_tr(vp + 8 * kRowBytes);
+        const uint2 v1 = lds_read_tr(vb[0][dt] + 16 * ks * kRowBytes);
+        const uint2 v2 = lds_read_tr(vb[1][dt] + 16 * ks * kRowBytes);
         const u32x4_t vf = u32x4_t{v1.x, v1.y, v2.x, v2.y};
         acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vf), as_bf16x8(pf[ks]), acc[dt], 0, 0, 0);
       }
