@@ -80,30 +80,50 @@ def gqa_decode_case(b, num_splits, name):
     cache, q = _dev(b.cache), _dev(b.q)
     bt, sl = _dev(b.block_table), _dev(b.seq_lens)
     kn, vn, sm = _dev(b.k_new), _dev(b.v_new), _dev(b.slot_mapping)
-    n = num_splits or pa.num_kv_splits(b.max_seq_len, pa.device_num_cus())
-    ws = torch.empty(max(1, pa.decode_workspace_bytes(b.num_seqs, b.num_q_heads, b.head_dim, n) // 4),
-                     dtype=torch.float32, device="cuda")
+    cus = pa.device_num_cus()
+    n = num_splits or pa.num_kv_splits(b.max_seq_len, cus)
+    g = b.num_q_heads // b.num_kv_heads
+    # the automatic schedule (num_splits = 0) of bf16 decode over more than one
+    # split's worth of keys is the token-balanced one
+    balanced = num_splits == 0 and n > 1 and b.dtype == W.BF16
+    if balanced:
+        nr = pa.decode_balanced_num_ranges(b.num_kv_heads, cus)
+        wsb = pa.decode_balanced_workspace_bytes(b.num_seqs, b.num_q_heads, nr)
+    else:
+        wsb = pa.decode_workspace_bytes(b.num_seqs, b.num_q_heads, b.head_dim, n)
+    ws = torch.empty(max(1, wsb // 4), dtype=torch.float32, device="cuda")
     out = torch.empty_like(q)
     lse = torch.empty(b.q.shape[:2], dtype=torch.float32, device="cuda")
 
     def step():
         pa.decode(q, cache, bt, sl, b.max_seq_len, b.scale, k=kn, v=vn, slot_mapping=sm,
-                  num_splits=n, workspace=ws, out=out, lse=lse)
+                  num_splits=num_splits, workspace=ws, out=out, lse=lse)
 
-    def kernel():
-        pa.decode(q, cache, bt, sl, b.max_seq_len, b.scale, num_splits=n, workspace=ws,
-                  stage1_only=True)
+    if balanced:
+        def kernel():
+            pa.decode_balanced(q, cache, bt, sl, b.scale, num_ranges=nr, workspace=ws, out=out,
+                               lse=lse, merge=False)
+        kname = f"decode_balanced_kernel<{g}>"
+        grid = f"{nr} token ranges x {min(b.num_kv_heads, 8)} waves (one per KV head)"
+        source = "decode_balanced.hip"
+    else:
+        def kernel():
+            pa.decode(q, cache, bt, sl, b.max_seq_len, b.scale, num_splits=n, workspace=ws,
+                      stage1_only=True)
+        kname = (f"decode_mfma_kernel<{g}>" if b.dtype == W.BF16
+                 else f"decode_split_kernel<false, {g}>")
+        grid = f"{b.num_seqs}x{b.num_kv_heads}x{n} work-groups of 256"
+        source = "decode.hip"
 
     by = W.gqa_bytes(b)
-    kb = by["kv"] + by["q"] + by["meta"] - b.num_tokens * 8   # split kernel: KV, q, table walk
+    kb = by["kv"] + by["q"] + by["meta"] - b.num_tokens * 8   # attention kernel: KV, q, table walk
     fl = W.gqa_flops(b)
-    g = b.num_q_heads // b.num_kv_heads
-    kname = (f"decode_mfma_kernel<{g}>" if b.dtype == W.BF16 else f"decode_split_kernel<false, {g}>")
     info = {"num_seqs": b.num_seqs, "num_q_heads": b.num_q_heads, "num_kv_heads": b.num_kv_heads,
             "head_dim": b.head_dim, "block_size": b.block_size, "dtype": b.dtype,
             "max_seq_len": b.max_seq_len, "total_keys": int(b.seq_lens.sum()),
-            "num_splits": n, "grid": f"{b.num_seqs}x{b.num_kv_heads}x{n} work-groups of 256"}
-    return Case(name, step, kernel, by["total"], fl, kb, fl, "hbm", kname, "decode.hip", info)
+            "schedule": "token-balanced ranges" if balanced else f"{n} splits per request",
+            "grid": grid}
+    return Case(name, step, kernel, by["total"], fl, kb, fl, "hbm", kname, source, info)
 
 
 def prefill_case(b, name):

@@ -138,15 +138,23 @@ pa_status_t pa_cache_write(pa_layout_t layout, pa_dtype_t dtype,
  *              is the request's last position.
  * max_seq_len: host copy of max(seq_lens) (sets the split partition).
  * scale:       multiplies Q K^T before the softmax (1/sqrt(head_dim) usually).
- * num_splits:  0 = n = pa_num_kv_splits(max_seq_len, pa_device_num_cus());
+ * num_splits:  0 = automatic: with n = pa_num_kv_splits(max_seq_len,
+ *              pa_device_num_cus()), n == 1 runs one unsplit pass; n > 1 with
+ *              PA_BF16 and out != NULL runs the token-balanced schedule
+ *              (pa_decode_balanced + pa_decode_balanced_merge), whose
+ *              reduction order depends on the whole batch's lengths;
+ *              otherwise n splits.
  *              1 = no split (each request reduced by one work unit, in an
  *              order independent of the rest of the batch); n > 1 = n splits.
  *              Split s of a request covers positions [s*P, (s+1)*P) with
  *              P = ceil(max_seq_len / n) rounded up to a multiple of
  *              block_size; splits past the request's end are empty.
  * workspace:   fp32 scratch of at least pa_decode_workspace_bytes(num_seqs,
- *              num_q_heads, head_dim, n) bytes; may be NULL when one split
- *              covers max_seq_len (then no partials are formed).
+ *              num_q_heads, head_dim, n) bytes for n splits, or, for the
+ *              balanced schedule, pa_decode_balanced_workspace_bytes(num_seqs,
+ *              num_q_heads, pa_decode_balanced_num_ranges(num_kv_heads,
+ *              pa_device_num_cus())) bytes, 16-byte aligned; may be NULL
+ *              when one split covers max_seq_len (then no partials are formed).
  * out:         [num_seqs, num_q_heads, head_dim], storage dtype; or NULL for
  *              the two-stage form: only stage 1 runs and the workspace holds
  *              the partials [num_seqs, num_q_heads, n, head_dim + 1] (empty
@@ -155,8 +163,8 @@ pa_status_t pa_cache_write(pa_layout_t layout, pa_dtype_t dtype,
  *              NULL when out is NULL).
  * Supported: head_dim 128; num_q_heads / num_kv_heads in {1, 2, 4, 8};
  * PA_F32 and PA_BF16.
- * Enqueues: the write (if k/v given), the split kernel, and the merge kernel
- * unless one split covers every request or out is NULL.
+ * Enqueues: the write (if k/v given), the split (or balanced) kernel, and
+ * the merge kernel unless one split covers every request or out is NULL.
  * ------------------------------------------------------------------------- */
 pa_status_t pa_decode(pa_dtype_t dtype,
                       const void* q, const void* k, const void* v,
@@ -168,6 +176,55 @@ pa_status_t pa_decode(pa_dtype_t dtype,
                       float scale, int num_splits,
                       void* workspace, size_t workspace_bytes,
                       void* out, float* lse, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Token-balanced decode: the split-KV reduction of pa_decode ("第 1 章
+ * 注意力后端", §3.1: partial softmax states over pieces of a request's keys,
+ * merged by log-sum-exp) with the pieces cut for an even load instead of at
+ * fixed positions.  The 32-token chunks of all requests (request r has
+ * ceil(seq_lens[r] / 32) of them) are concatenated into one list of T
+ * chunks; with nr = min(num_ranges, T), range j = 0..nr-1 is chunks
+ * [floor(j T / nr), floor((j+1) T / nr)).  Each range is one work-group.
+ * A request wholly inside one range is written to out / lse by
+ * pa_decode_balanced; for the others every range they touch leaves one
+ * partial (normalised output + lse) in the workspace, and
+ * pa_decode_balanced_merge combines them.  Both run on the caller's stream
+ * and use the same workspace; the merge must follow the first call.
+ *
+ * pa_decode_balanced_num_ranges: ranges that keep 8 waves on each of num_cus
+ *   compute units (num_cus * 8 / (min(num_kv_heads, 8) * ceil(num_kv_heads /
+ *   8)), at least 1); what pa_decode uses.
+ * pa_decode_balanced_workspace_bytes: bytes of workspace: 4 (num_seqs + 1)
+ *   rounded up to 256, plus (num_ranges + num_seqs) * num_q_heads * 132 * 4.
+ *   Returns 0 for negative sizes or num_ranges < 1.
+ *
+ * pa_decode_balanced arguments are those of pa_decode (no new-token write:
+ * call pa_cache_write first), with:
+ * num_ranges:  [1, 2^24]; the workspace must hold
+ *              pa_decode_balanced_workspace_bytes(num_seqs, num_q_heads,
+ *              num_ranges) bytes, 16-byte aligned (PA_ERR_WORKSPACE if not).
+ * out, lse:    as pa_decode; after this call only the requests inside one
+ *              range are final.
+ * Supported: PA_BF16 storage, head_dim 128, num_q_heads / num_kv_heads in
+ * {1, 2, 4, 8}, num_seqs * ceil(max_blocks_per_seq * block_size / 32) < 2^31.
+ * pa_decode_balanced_merge completes out / lse (a request with no keys gets
+ * out = 0, lse = -inf); its num_seqs, num_q_heads, head_dim, num_ranges and
+ * workspace must be those of the preceding pa_decode_balanced call.
+ * ------------------------------------------------------------------------- */
+int pa_decode_balanced_num_ranges(int num_kv_heads, int num_cus);
+
+size_t pa_decode_balanced_workspace_bytes(int num_seqs, int num_q_heads, int num_ranges);
+
+pa_status_t pa_decode_balanced(const void* q, const void* kv_cache, int64_t num_blocks,
+                               int block_size, const int32_t* block_table,
+                               int max_blocks_per_seq, const int32_t* seq_lens, int num_seqs,
+                               int num_q_heads, int num_kv_heads, int head_dim, float scale,
+                               int num_ranges, void* workspace, size_t workspace_bytes,
+                               void* out, float* lse, hipStream_t stream);
+
+pa_status_t pa_decode_balanced_merge(void* workspace, size_t workspace_bytes, int num_seqs,
+                                     int num_q_heads, int head_dim, int num_ranges, void* out,
+                                     float* lse, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
  * pa_prefill_varlen -- varlen prefill / chunked-prefill extend over the paged

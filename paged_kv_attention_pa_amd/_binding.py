@@ -38,6 +38,11 @@ _SIGNATURES = {
                              _i32, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _vp, _sz,
                              _vp, _vp, _vp]),
     "pa_lse_merge": (_i32, [_vp, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp]),
+    "pa_decode_balanced_num_ranges": (_i32, [_i32, _i32]),
+    "pa_decode_balanced_workspace_bytes": (_sz, [_i32, _i32, _i32]),
+    "pa_decode_balanced": (_i32, [_vp, _vp, _i64, _i32, _vp, _i32, _vp, _i32, _i32, _i32, _i32,
+                                  _f32, _i32, _vp, _sz, _vp, _vp, _vp]),
+    "pa_decode_balanced_merge": (_i32, [_vp, _sz, _i32, _i32, _i32, _i32, _vp, _vp, _vp]),
 }
 EXPORTED_SYMBOLS = tuple(_SIGNATURES)
 
@@ -97,6 +102,15 @@ def mla_num_kv_splits(num_seqs: int, max_seq_len: int, num_cus: int) -> int:
 def decode_workspace_bytes(num_seqs: int, num_q_heads: int, head_dim_v: int, num_splits: int) -> int:
     return library().pa_decode_workspace_bytes(int(num_seqs), int(num_q_heads), int(head_dim_v),
                                                int(num_splits))
+
+
+def decode_balanced_num_ranges(num_kv_heads: int, num_cus: int) -> int:
+    return library().pa_decode_balanced_num_ranges(int(num_kv_heads), int(num_cus))
+
+
+def decode_balanced_workspace_bytes(num_seqs: int, num_q_heads: int, num_ranges: int) -> int:
+    return library().pa_decode_balanced_workspace_bytes(int(num_seqs), int(num_q_heads),
+                                                        int(num_ranges))
 
 
 def device_num_cus() -> int:
@@ -198,6 +212,10 @@ def decode(q, kv_cache, block_table, seq_lens, max_seq_len: int, scale: float,
     if n == 0:
         n = num_kv_splits(max_seq_len, device_num_cus())
     need = decode_workspace_bytes(B, Hq, D, n) if (n > 1 or stage1_only) else 0
+    if num_splits == 0 and n > 1 and not stage1_only and dt == PA_BF16:
+        # the automatic schedule is the token-balanced one
+        need = decode_balanced_workspace_bytes(
+            B, Hq, decode_balanced_num_ranges(hkv, device_num_cus()))
     if workspace is None and need:
         workspace = torch.empty(need // 4, dtype=torch.float32, device=q.device)
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
@@ -209,6 +227,53 @@ def decode(q, kv_cache, block_table, seq_lens, max_seq_len: int, scale: float,
     if stage1_only:
         return workspace[: B * Hq * n * (D + 1)].view(B, Hq, n, D + 1)
     return out, lse
+
+
+def decode_balanced(q, kv_cache, block_table, seq_lens, scale: float, num_ranges: int = 0,
+                    workspace=None, out=None, lse=None, return_lse: bool = True,
+                    merge: bool = True, stream=None):
+    """Token-balanced GQA decode (bf16): q [B, Hq, D]; kv_cache [nb, 2, bs, Hkv, D].
+
+    num_ranges = 0 takes ``decode_balanced_num_ranges(Hkv, device_num_cus())``.
+    merge=False runs only the first kernel: out / lse then hold just the
+    requests that lie inside one range, and the workspace the partials that
+    ``decode_balanced_merge`` combines.  Returns (out, lse, workspace, num_ranges)."""
+    torch = _torch()
+    _dev(q, kv_cache, block_table, seq_lens, workspace, out, lse)
+    _int_tensor(block_table, "int32", "block_table")
+    _int_tensor(seq_lens, "int32", "seq_lens")
+    _need(q.dtype == torch.bfloat16 and kv_cache.dtype == torch.bfloat16, "bf16 q and cache")
+    B, Hq, D = q.shape
+    nb, _, bs, hkv, d2 = kv_cache.shape
+    _need(d2 == D, "head_dim mismatch")
+    nr = int(num_ranges) or decode_balanced_num_ranges(hkv, device_num_cus())
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and return_lse:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    need = decode_balanced_workspace_bytes(B, Hq, nr)
+    if workspace is None:
+        workspace = torch.empty(max(1, need // 4), dtype=torch.float32, device=q.device)
+    wbytes = workspace.numel() * workspace.element_size()
+    lib = library()
+    _check(lib.pa_decode_balanced(_ptr(q), _ptr(kv_cache), nb, bs, _ptr(block_table),
+                                  block_table.shape[1], _ptr(seq_lens), B, Hq, hkv, D,
+                                  float(scale), nr, _ptr(workspace), wbytes, _ptr(out),
+                                  _ptr(lse), _stream(stream)))
+    if merge:
+        decode_balanced_merge(workspace, B, Hq, D, nr, out, lse, stream=stream)
+    return out, lse, workspace, nr
+
+
+def decode_balanced_merge(workspace, num_seqs: int, num_q_heads: int, head_dim: int,
+                          num_ranges: int, out, lse=None, stream=None):
+    """Second kernel of the balanced decode: combine the partials of requests
+    that cross ranges into out / lse."""
+    _dev(workspace, out, lse)
+    wbytes = workspace.numel() * workspace.element_size()
+    _check(library().pa_decode_balanced_merge(_ptr(workspace), wbytes, int(num_seqs),
+                                              int(num_q_heads), int(head_dim), int(num_ranges),
+                                              _ptr(out), _ptr(lse), _stream(stream)))
 
 
 def prefill_varlen(q, kv_cache, block_table, query_start_loc, seq_lens, max_query_len: int,

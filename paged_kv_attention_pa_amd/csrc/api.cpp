@@ -80,6 +80,39 @@ pa_status_t check_common_cache(int64_t num_blocks, int block_size,
   return PA_OK;
 }
 
+// Token-balanced decode: workspace = cu[num_seqs + 1] (256-B aligned), then
+// (num_ranges + num_seqs) * num_q_heads segment rows of 132 fp32.
+size_t balanced_bytes(int num_seqs, int num_q_heads, int num_ranges) {
+  if (num_seqs < 0 || num_q_heads < 0 || num_ranges < 1) return 0;
+  const unsigned __int128 b = (unsigned __int128)pa::balanced_cu_bytes(num_seqs) +
+                              (unsigned __int128)((int64_t)num_ranges + num_seqs) *
+                                  (unsigned)num_q_heads * pa::balanced_part_row_floats() * 4u;
+  if (b > (unsigned __int128)SIZE_MAX) return 0;
+  return size_t(b);
+}
+
+pa_status_t check_balanced(int num_seqs, int num_q_heads, int max_blocks_per_seq, int block_size,
+                           int num_ranges, const void* workspace, size_t workspace_bytes) {
+  PA_REQUIRE(num_ranges >= 1 && num_ranges <= (1 << 24), PA_ERR_INVALID,
+             "num_ranges must be in [1, 2^24] (got %d)", num_ranges);
+  // chunk counts are summed in int32 on the device
+  const int64_t len_cap = int64_t(max_blocks_per_seq) * block_size;
+  PA_REQUIRE(int64_t(num_seqs) * ((len_cap + 31) / 32) <= INT_MAX, PA_ERR_UNSUPPORTED,
+             "num_seqs * max_blocks_per_seq * block_size / 32 exceeds 2^31 chunks");
+  const size_t need = balanced_bytes(num_seqs, num_q_heads, num_ranges);
+  PA_REQUIRE(need > 0 && workspace != nullptr && workspace_bytes >= need, PA_ERR_WORKSPACE,
+             "workspace of %zu bytes needed for %d ranges (got %zu)", need, num_ranges,
+             workspace_bytes);
+  PA_REQUIRE((reinterpret_cast<uintptr_t>(workspace) & 15) == 0, PA_ERR_INVALID,
+             "workspace must be 16-byte aligned");
+  return PA_OK;
+}
+
+int32_t* balanced_cu(void* ws) { return static_cast<int32_t*>(ws); }
+float* balanced_part(void* ws, int num_seqs) {
+  return reinterpret_cast<float*>(static_cast<char*>(ws) + pa::balanced_cu_bytes(num_seqs));
+}
+
 }  // namespace
 
 extern "C" {
@@ -204,15 +237,24 @@ pa_status_t pa_decode(pa_dtype_t dtype,
              "lse without out: the partial-only mode (out = NULL) returns no lse");
 
   int n = num_splits;
+  int cus = 0;
   if (n == 0) {
-    const int cus = pa_device_num_cus();
+    cus = pa_device_num_cus();
     if (cus <= 0) return fail(PA_ERR_HIP, "cannot query the device's compute units");
     n = pa_num_kv_splits(max_seq_len, cus);
   }
   const int P = split_tokens_for(max_seq_len, n, block_size);
   const bool stage1 = (out == nullptr);            // partials only, for pa_lse_merge
   const bool direct = !stage1 && used_splits(max_seq_len, P) == 1;
-  if (!direct) {
+  // Automatic schedule with more than one split's worth of keys: token-balanced
+  // ranges instead of per-request splits.
+  const bool balanced = num_splits == 0 && !stage1 && !direct && dtype == PA_BF16;
+  const int nr = balanced ? pa_decode_balanced_num_ranges(num_kv_heads, cus) : 0;
+  if (balanced) {
+    st = check_balanced(num_seqs, num_q_heads, max_blocks_per_seq, block_size, nr, workspace,
+                        workspace_bytes);
+    if (st != PA_OK) return st;
+  } else if (!direct) {
     const size_t need = pa_decode_workspace_bytes(num_seqs, num_q_heads, head_dim, n);
     PA_REQUIRE(workspace != nullptr && workspace_bytes >= need, PA_ERR_WORKSPACE,
                "workspace of %zu bytes needed for %d splits (got %zu)", need, n, workspace_bytes);
@@ -224,6 +266,14 @@ pa_status_t pa_decode(pa_dtype_t dtype,
                        num_seqs, dtype == PA_BF16 ? 2 : 4};
     hipError_t e = pa::launch_cache_write_kv(w, stream);
     if (e != hipSuccess) return hip_fail(e, "cache_write_kv launch");
+  }
+  if (balanced) {
+    st = pa_decode_balanced(q, kv_cache, num_blocks, block_size, block_table, max_blocks_per_seq,
+                            seq_lens, num_seqs, num_q_heads, num_kv_heads, head_dim, scale, nr,
+                            workspace, workspace_bytes, out, lse, stream);
+    if (st != PA_OK) return st;
+    return pa_decode_balanced_merge(workspace, workspace_bytes, num_seqs, num_q_heads, head_dim,
+                                    nr, out, lse, stream);
   }
   pa::DecodeGQA d{};
   d.bf16 = dtype == PA_BF16;
@@ -253,6 +303,71 @@ pa_status_t pa_decode(pa_dtype_t dtype,
     e = pa::launch_lse_merge(m, stream);
     if (e != hipSuccess) return hip_fail(e, "merge launch");
   }
+  return ok();
+}
+
+// ---------------------------------------------------------------------------
+int pa_decode_balanced_num_ranges(int num_kv_heads, int num_cus) {
+  return pa::balanced_num_ranges(num_kv_heads, num_cus);
+}
+
+size_t pa_decode_balanced_workspace_bytes(int num_seqs, int num_q_heads, int num_ranges) {
+  return balanced_bytes(num_seqs, num_q_heads, num_ranges);
+}
+
+pa_status_t pa_decode_balanced(const void* q, const void* kv_cache, int64_t num_blocks,
+                               int block_size, const int32_t* block_table,
+                               int max_blocks_per_seq, const int32_t* seq_lens, int num_seqs,
+                               int num_q_heads, int num_kv_heads, int head_dim, float scale,
+                               int num_ranges, void* workspace, size_t workspace_bytes,
+                               void* out, float* lse, hipStream_t stream) {
+  PA_REQUIRE(scale_ok(scale), PA_ERR_INVALID, "scale must be finite and >= 0");
+  PA_REQUIRE(num_seqs >= 0, PA_ERR_INVALID, "num_seqs must be >= 0 (got %d)", num_seqs);
+  pa_status_t st = check_common_cache(num_blocks, block_size, block_table, max_blocks_per_seq,
+                                      seq_lens, num_seqs, 0);
+  if (st != PA_OK) return st;
+  PA_REQUIRE(num_q_heads > 0 && num_kv_heads > 0 && num_q_heads % num_kv_heads == 0,
+             PA_ERR_INVALID, "num_q_heads (%d) must be a positive multiple of num_kv_heads (%d)",
+             num_q_heads, num_kv_heads);
+  PA_REQUIRE(head_dim == 128, PA_ERR_UNSUPPORTED, "balanced decode supports head_dim 128 (got %d)",
+             head_dim);
+  PA_REQUIRE(is_pow2_group(num_q_heads / num_kv_heads), PA_ERR_UNSUPPORTED,
+             "balanced decode supports num_q_heads / num_kv_heads in {1, 2, 4, 8} (got %d)",
+             num_q_heads / num_kv_heads);
+  st = check_balanced(num_seqs, num_q_heads, max_blocks_per_seq, block_size, num_ranges,
+                      workspace, workspace_bytes);
+  if (st != PA_OK) return st;
+  if (num_seqs == 0) return ok();
+  PA_REQUIRE(q && kv_cache && out, PA_ERR_INVALID, "q, kv_cache and out must be non-null");
+  const int64_t cap = int64_t(max_blocks_per_seq) * block_size;
+  pa::DecodeBalanced d{q, kv_cache, num_blocks, block_size, block_table, max_blocks_per_seq,
+                       seq_lens, num_seqs, int(cap > INT_MAX ? INT_MAX : cap), num_q_heads,
+                       num_kv_heads, scale, num_ranges, balanced_cu(workspace),
+                       balanced_part(workspace, num_seqs), out, lse};
+  hipError_t e = pa::launch_decode_balanced(d, stream);
+  if (e != hipSuccess) return hip_fail(e, "balanced decode launch");
+  return ok();
+}
+
+pa_status_t pa_decode_balanced_merge(void* workspace, size_t workspace_bytes, int num_seqs,
+                                     int num_q_heads, int head_dim, int num_ranges, void* out,
+                                     float* lse, hipStream_t stream) {
+  PA_REQUIRE(num_seqs >= 0, PA_ERR_INVALID, "num_seqs must be >= 0 (got %d)", num_seqs);
+  PA_REQUIRE(num_q_heads > 0, PA_ERR_INVALID, "num_q_heads must be > 0");
+  PA_REQUIRE(head_dim == 128, PA_ERR_UNSUPPORTED, "balanced decode supports head_dim 128 (got %d)",
+             head_dim);
+  PA_REQUIRE(num_ranges >= 1 && num_ranges <= (1 << 24), PA_ERR_INVALID,
+             "num_ranges must be in [1, 2^24] (got %d)", num_ranges);
+  const size_t need = balanced_bytes(num_seqs, num_q_heads, num_ranges);
+  PA_REQUIRE(need > 0 && workspace != nullptr && workspace_bytes >= need, PA_ERR_WORKSPACE,
+             "workspace of %zu bytes needed for %d ranges (got %zu)", need, num_ranges,
+             workspace_bytes);
+  if (num_seqs == 0) return ok();
+  PA_REQUIRE(out != nullptr, PA_ERR_INVALID, "out must be non-null");
+  pa::BalancedMerge m{balanced_cu(workspace), balanced_part(workspace, num_seqs), num_seqs,
+                      num_q_heads, num_ranges, out, lse};
+  hipError_t e = pa::launch_balanced_merge(m, stream);
+  if (e != hipSuccess) return hip_fail(e, "balanced merge launch");
   return ok();
 }
 

@@ -282,13 +282,6 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeGQA a) {
 constexpr int kChunk = 32;                 // tokens per MFMA chunk
 constexpr int kTileRow = kD * 2;           // LDS row of one token (256 B)
 
-typedef __attribute__((ext_vector_type(4))) short s16x4_t;
-__device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
-__device__ __forceinline__ uint2 lds_read_tr(const char* p) {
-  typedef __attribute__((address_space(3))) s16x4_t lds_s4;
-  const s16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(p));
-  return __builtin_bit_cast(uint2, v);
-}
 // Byte offset of 16-byte chunk c of token row t in a swizzled tile.
 __device__ __forceinline__ int tile_off(int t, int c) { return t * kTileRow + 16 * (c ^ (t & 15)); }
 

@@ -1,0 +1,385 @@
+// Token-balanced GQA decode over the paged KV cache, bf16, head_dim 128.
+//
+// Split-KV decode ("第 1 章 注意力后端", §3.1) cuts every request into
+// fixed-length splits; with a batch of mixed lengths the number of splits
+// rarely divides evenly over the chip, and the last wave of work-groups runs
+// a nearly empty machine.  This schedule instead concatenates the 32-token
+// chunks of all requests into one list and gives each of `nr` work-groups an
+// equal share [c0, c1) of it (range j holds chunks [j T / nr, (j+1) T / nr),
+// T = total chunks; nr <= T so no range is empty).  A range may start and end
+// inside a request and may cover several short requests; for every request it
+// touches it produces one LSE partial ("segment"), and a request that lies
+// wholly inside one range is written to the output directly.  The merge
+// kernel then combines the segments of the requests that cross ranges.
+//
+// Segment slots: the segments of range j are (j, r) for the requests r it
+// touches.  Walking the concatenated list, each new segment advances j or r
+// (or both), so j + r is a unique slot number in [0, nr + B - 1).
+//
+// Range of a chunk c: the largest j with j T / nr <= c (integer division),
+// i.e. j(c) = ((c + 1) nr - 1) / T.  (j T / nr <= c  <=>  j T < (c + 1) nr.)
+//
+// Work-group: one wave per KV head (up to 8) of one range; the waves walk the
+// same chunks, so together they read whole 2 KiB token rows of a page.
+// Per wave: Q^T stays in registers as the B operand of S^T = K Q^T
+// (mfma 16x16x32 bf16, 16 keys x 16 query-head columns, G of them used); the
+// P^T registers feed O^T = V^T P^T directly.  K and V arrive with coalesced
+// 16-byte loads (16 lanes per 256 B head row) and are transposed through a
+// padded LDS tile; the registers of chunk c+1 are refilled as soon as chunk
+// c's values are in the tile, so one chunk of loads is in flight while the
+// previous one is computed.
+#include "launch.hpp"
+#include "pa_device.hpp"
+
+namespace pa {
+namespace {
+
+constexpr int kD = 128;
+constexpr int kChunk = 32;              // tokens per chunk (one MFMA k-extent)
+constexpr int kRow = kD * 2 + 16;       // LDS row of a token: 256 B + 16 B pad
+constexpr int kTile = kChunk * kRow;    // per-wave tile (K, then V)
+constexpr int kHeads = 8;               // KV heads (waves) per work-group
+constexpr int kPartRow = 132;           // fp32 per segment row: 128 values, lse at [128]
+
+__device__ __forceinline__ int clamp_len(int s, int cap) { return s < 0 ? 0 : (s > cap ? cap : s); }
+__device__ __forceinline__ int chunks_of(int len) { return (len + kChunk - 1) / kChunk; }
+
+// A chunk of the concatenated list: request r, its chunk lc, the request's
+// (clamped) length and the list index of its first chunk.
+struct Pos {
+  int r, lc, len, base;
+};
+
+// The chunk after p.  The caller guarantees that one exists (some later
+// request has keys), so the scan over empty requests stops inside the batch.
+__device__ __forceinline__ Pos next_pos(Pos p, const int32_t* seq_lens, int cap, int B) {
+  if ((p.lc + 1) * kChunk < p.len) {
+    ++p.lc;
+    return p;
+  }
+  p.base += chunks_of(p.len);
+  int r = min(p.r + 1, B - 1);
+  int len = clamp_len(uniform_load(seq_lens + r), cap);
+  while (len == 0 && r + 1 < B) {
+    ++r;
+    len = clamp_len(uniform_load(seq_lens + r), cap);
+  }
+  p.r = r;
+  p.lc = 0;
+  p.len = len;
+  return p;
+}
+
+template <int G>
+__global__ __launch_bounds__(64 * kHeads, 1) void decode_balanced_kernel(DecodeBalanced a) {
+  static_assert(G >= 1 && G <= 16, "group must fit the 16 MFMA columns");
+  __shared__ __align__(16) char smem[kHeads * kTile];
+  __shared__ int s_wave_sum[kHeads];
+  __shared__ int s_start[2];
+  const int tid = threadIdx.x;
+  const int nthr = blockDim.x;
+  const int lane = tid & 63;
+  const int wave = wave_id();
+  const int B = a.num_seqs;
+  const int cap = a.len_cap;
+  const int Hkv = a.num_kv_heads;
+  const int n_hg = (Hkv + kHeads - 1) / kHeads;
+  const int hg = blockIdx.x % n_hg;
+  const int j = blockIdx.x / n_hg;
+
+  // Chunk counts of all requests and their exclusive prefix sums.  Every
+  // work-group computes them (B is small next to the KV stream); range 0 of
+  // head group 0 also stores them for the merge.
+  const int per = (B + nthr - 1) / nthr;
+  const int rb = min(B, tid * per);
+  const int re = min(B, rb + per);
+  int local = 0;
+  for (int r = rb; r < re; ++r) local += chunks_of(clamp_len(a.seq_lens[r], cap));
+  int incl = local;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int t = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += t;
+  }
+  if (lane == 63) s_wave_sum[wave] = incl;
+  __syncthreads();
+  int before = 0, total = 0;
+  for (int w = 0; w < nthr / 64; ++w) {
+    const int t = s_wave_sum[w];
+    before += w < wave ? t : 0;
+    total += t;
+  }
+  const int excl = before + incl - local;
+  if (j == 0 && hg == 0) {
+    int run = excl;
+    for (int r = rb; r < re; ++r) {
+      a.cu[r] = run;
+      run += chunks_of(clamp_len(a.seq_lens[r], cap));
+    }
+    if (tid == 0) a.cu[B] = total;
+  }
+
+  // This work-group's range [c0, c1) and the request holding chunk c0.
+  const int nr = min(a.num_ranges, total);
+  if (j >= nr) return;   // the same for every thread of the work-group
+  const int c0 = int(int64_t(j) * total / nr);
+  const int c1 = int(int64_t(j + 1) * total / nr);
+  if (c0 >= excl && c0 < excl + local) {
+    int run = excl;
+    for (int r = rb; r < re; ++r) {
+      const int n = chunks_of(clamp_len(a.seq_lens[r], cap));
+      if (c0 < run + n) {
+        s_start[0] = r;
+        s_start[1] = run;
+        break;
+      }
+      run += n;
+    }
+  }
+  __syncthreads();
+  const int h = hg * kHeads + wave;
+  if (h >= Hkv) return;   // no barrier below
+
+  const int li = lane & 15;   // MFMA row/column index; 16-byte chunk of a loaded row
+  const int kq = lane >> 4;   // 16-lane group; token within a 4-token load
+  const int Hq = a.num_q_heads;
+  const int bs = a.block_size;
+  const int64_t tok_stride = int64_t(Hkv) * kD;
+  const int64_t kv_stride = int64_t(bs) * tok_stride;
+  const uint16_t* cache = static_cast<const uint16_t*>(a.cache);
+  const uint16_t* qbase = static_cast<const uint16_t*>(a.q);
+  const float scale2 = a.scale * kLog2e;
+
+  char* tl = smem + wave * kTile;
+  char* const st_base = tl + kq * kRow + 16 * li;                    // row 4 i + kq, chunk li
+  const char* const a_base = tl + li * kRow + 16 * kq;               // row 16 sub + li, chunk 4 kk + kq
+  const char* const tr_base = tl + (4 * kq + (li >> 2)) * kRow + 8 * (li & 3);
+
+  // Q^T columns: lane li holds query head h G + (li mod G); the columns past G
+  // repeat real rows and their results are never stored.
+  auto load_q = [&](int r, u32x4_t (&qf)[4]) {
+    const uint16_t* qp = qbase + (int64_t(r) * Hq + int64_t(h) * G + (li & (G - 1))) * kD + 8 * kq;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) qf[kk] = load16(qp + 32 * kk);
+  };
+  // K (plane 0) or V (plane kv_stride) rows of chunk p: instruction i reads
+  // tokens 4 i + kq of each 16-token half, lane li its 16-byte chunk li.
+  // Tokens past the request's end re-read its last token (finite data,
+  // masked below); the loads are unconditional so the waits stay exact.
+  auto load_half = [&](const Pos& p, int64_t plane, u32x4_t (&dst)[8]) {
+    const int32_t* table = a.block_table + int64_t(p.r) * a.max_blocks;
+    const int len = max(p.len, 1);   // positions always hold keys; keeps every index >= 0
+    const int last16 = ((len - 1) / 16) * 16;
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+      const int tok16 = min(p.lc * kChunk + 16 * sub, last16);
+      int64_t blk = uniform_load(table + tok16 / bs);
+      blk = (blk < 0 || blk >= a.num_blocks) ? 0 : blk;
+      const int page0 = (tok16 / bs) * bs;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int tok = min(tok16 + 4 * i + kq, len - 1);
+        const int64_t off = (blk * 2 * bs + (tok - page0)) * tok_stride + int64_t(h) * kD + 8 * li;
+        dst[4 * sub + i] = load16(cache + plane + off);
+      }
+    }
+  };
+
+  Pos cur;
+  cur.r = __builtin_amdgcn_readfirstlane(s_start[0]);
+  cur.base = __builtin_amdgcn_readfirstlane(s_start[1]);
+  cur.len = clamp_len(uniform_load(a.seq_lens + cur.r), cap);
+  cur.lc = c0 - cur.base;
+  Pos nxt = c0 + 1 < c1 ? next_pos(cur, a.seq_lens, cap, B) : cur;
+
+  u32x4_t qf[4];
+  load_q(cur.r, qf);
+  u32x4_t kr[8], vr[8];
+  load_half(cur, 0, kr);
+  load_half(cur, kv_stride, vr);
+
+  f32x4_t acc[8];   // O^T: d = 16 dt + 4 kq + i, head column li
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) acc[dt] = f32x4_t{0, 0, 0, 0};
+  float m_run = kNoMax, l_run = 0.0f;
+
+  for (int c = c0; c < c1; ++c) {
+    // K rows into the tile; the registers are refilled with the next chunk
+#pragma unroll
+    for (int i = 0; i < 8; ++i) *reinterpret_cast<u32x4_t*>(st_base + 4 * i * kRow) = kr[i];
+    __builtin_amdgcn_sched_barrier(0);
+    load_half(nxt, 0, kr);
+    f32x4_t sc[2];
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+      sc[sub] = f32x4_t{0, 0, 0, 0};
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const u32x4_t kf = *reinterpret_cast<const u32x4_t*>(a_base + 16 * sub * kRow + 64 * kk);
+        sc[sub] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kf), as_bf16x8(qf[kk]), sc[sub], 0, 0, 0);
+      }
+    }
+    const bool new_request = nxt.lc == 0 && c + 1 < c1;
+    if (new_request) load_q(nxt.r, qf);
+    // V rows into the same tile (this wave's LDS operations run in order)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) *reinterpret_cast<u32x4_t*>(st_base + 4 * i * kRow) = vr[i];
+    __builtin_amdgcn_sched_barrier(0);
+    load_half(nxt, kv_stride, vr);
+
+    // online softmax over this chunk (base 2); keys past the request end masked
+    const int tok0 = cur.lc * kChunk;
+    const bool tail = tok0 + kChunk > cur.len;
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float v = sc[sub][i] * scale2;
+        if (tail && tok0 + 16 * sub + 4 * kq + i >= cur.len) v = -INFINITY;
+        sc[sub][i] = v;
+        tmax = fmaxf(tmax, v);
+      }
+    tmax = fmaxf(tmax, lane_xor(tmax, 16));
+    tmax = fmaxf(tmax, lane_xor(tmax, 32));
+    const float m_new = fmaxf(m_run, tmax);
+    const float alpha = fast_exp2(m_run - m_new);
+    m_run = m_new;
+    float p[8];
+    float psum = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      p[i] = fast_exp2(sc[0][i] - m_new);
+      p[4 + i] = fast_exp2(sc[1][i] - m_new);
+      psum += p[i] + p[4 + i];
+    }
+    l_run = fmaf(l_run, alpha, psum);
+    const u32x4_t pf = u32x4_t{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
+                               pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])};
+    // O^T += V^T P^T: lane li of group kq reads 4 bf16 of token row
+    // 4 kq + li / 4 (and +16) at dims 16 dt + 4 (li % 4).
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      const uint2 v1 = lds_read_tr(tr_base + 32 * dt);
+      const uint2 v2 = lds_read_tr(tr_base + 16 * kRow + 32 * dt);
+      acc[dt] *= alpha;
+      acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+          as_bf16x8(u32x4_t{v1.x, v1.y, v2.x, v2.y}), as_bf16x8(pf), acc[dt], 0, 0, 0);
+    }
+
+    // end of this request's keys within the range: emit its segment
+    if (tok0 + kChunk >= cur.len || c + 1 == c1) {
+      const float l_w = l_run + lane_xor(l_run, 16);
+      const float l_tot = l_w + lane_xor(l_w, 32);
+      const float inv = 1.0f / l_tot;
+      const float lse_nat = (m_run + fast_log2(l_tot)) * kLn2;
+      const bool whole = cur.base >= c0 && cur.base + chunks_of(cur.len) <= c1;
+      if (li < G) {
+        const int64_t hrow = int64_t(h) * G + li;
+        if (whole) {
+          const int64_t row = int64_t(cur.r) * Hq + hrow;
+          uint16_t* op = static_cast<uint16_t*>(a.out) + row * kD + 4 * kq;
+#pragma unroll
+          for (int dt = 0; dt < 8; ++dt) {
+            uint2 w;
+            w.x = pack_bf16x2(acc[dt][0] * inv, acc[dt][1] * inv);
+            w.y = pack_bf16x2(acc[dt][2] * inv, acc[dt][3] * inv);
+            *reinterpret_cast<uint2*>(op + 16 * dt) = w;
+          }
+          if (kq == 0 && a.lse) a.lse[row] = lse_nat;
+        } else {
+          float* pp = a.part + (int64_t(j + cur.r) * Hq + hrow) * kPartRow;
+#pragma unroll
+          for (int dt = 0; dt < 8; ++dt)
+            *reinterpret_cast<f32x4_t*>(pp + 16 * dt + 4 * kq) = acc[dt] * inv;
+          if (kq == 0) pp[kD] = lse_nat;
+        }
+      }
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) acc[dt] = f32x4_t{0, 0, 0, 0};
+      m_run = kNoMax;
+      l_run = 0.0f;
+    }
+    cur = nxt;
+    if (c + 2 < c1) nxt = next_pos(nxt, a.seq_lens, cap, B);
+  }
+}
+
+// Combine the segments of requests that cross ranges.  One work-group per
+// (request, 8 query heads): 32 threads x 4 dims per head row.
+__global__ __launch_bounds__(256) void balanced_merge_kernel(BalancedMerge a) {
+  const int Hq = a.num_q_heads;
+  const int nqb = (Hq + 7) / 8;
+  const int r = blockIdx.x / nqb;
+  const int hq = (blockIdx.x % nqb) * 8 + (threadIdx.x >> 5);
+  if (hq >= Hq) return;
+  const int d = 4 * (threadIdx.x & 31);
+  const int B = a.num_seqs;
+  const int total = a.cu[B];
+  const int cb = a.cu[r];
+  const int ce = a.cu[r + 1];
+  const int64_t row = int64_t(r) * Hq + hq;
+  uint2* op = reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + row * kD + d);
+  if (cb == ce) {   // no keys: out 0, lse -inf
+    *op = uint2{0u, 0u};
+    if (a.lse && d == 0) a.lse[row] = -INFINITY;
+    return;
+  }
+  const int nr = min(a.num_ranges, total);
+  const int j0 = int(((int64_t(cb) + 1) * nr - 1) / total);
+  const int j1 = int((int64_t(ce) * nr - 1) / total);
+  if (j0 == j1) return;   // written by its range
+  const int64_t step = int64_t(Hq) * kPartRow;
+  const float* p0 = a.part + (int64_t(j0 + r) * Hq + hq) * kPartRow;
+  float m = -INFINITY;
+  for (int jj = 0; jj <= j1 - j0; ++jj) m = fmaxf(m, p0[jj * step + kD]);
+  float den = 0.0f;
+  f32x4_t o = f32x4_t{0, 0, 0, 0};
+  for (int jj = 0; jj <= j1 - j0; ++jj) {
+    const float* pp = p0 + jj * step;
+    const float w = fast_exp2((pp[kD] - m) * kLog2e);
+    den += w;
+    o += w * *reinterpret_cast<const f32x4_t*>(pp + d);
+  }
+  const float inv = 1.0f / den;
+  *op = uint2{pack_bf16x2(o[0] * inv, o[1] * inv), pack_bf16x2(o[2] * inv, o[3] * inv)};
+  if (a.lse && d == 0) a.lse[row] = m + fast_log2(den) * kLn2;
+}
+
+}  // namespace
+
+int balanced_num_ranges(int num_kv_heads, int num_cus) {
+  if (num_kv_heads < 1) num_kv_heads = 1;
+  if (num_cus < 1) num_cus = 1;
+  const int waves = num_kv_heads < kHeads ? num_kv_heads : kHeads;
+  const int n_hg = (num_kv_heads + kHeads - 1) / kHeads;
+  const int64_t nr = int64_t(num_cus) * kHeads / (int64_t(waves) * n_hg);   // 8 waves per CU
+  return int(nr < 1 ? 1 : nr);
+}
+
+size_t balanced_cu_bytes(int num_seqs) { return (size_t(num_seqs + 1) * 4 + 255) / 256 * 256; }
+size_t balanced_part_row_floats() { return kPartRow; }
+
+hipError_t launch_decode_balanced(const DecodeBalanced& a, hipStream_t s) {
+  const int G = a.num_q_heads / a.num_kv_heads;
+  const int n_hg = (a.num_kv_heads + kHeads - 1) / kHeads;
+  const int waves = a.num_kv_heads < kHeads ? a.num_kv_heads : kHeads;
+  const dim3 grid{unsigned(int64_t(a.num_ranges) * n_hg)}, block{unsigned(64 * waves)};
+  switch (G) {
+    case 1: hipLaunchKernelGGL((decode_balanced_kernel<1>), grid, block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((decode_balanced_kernel<2>), grid, block, 0, s, a); break;
+    case 4: hipLaunchKernelGGL((decode_balanced_kernel<4>), grid, block, 0, s, a); break;
+    case 8: hipLaunchKernelGGL((decode_balanced_kernel<8>), grid, block, 0, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_balanced_merge(const BalancedMerge& a, hipStream_t s) {
+  const int nqb = (a.num_q_heads + 7) / 8;
+  const dim3 grid{unsigned(int64_t(a.num_seqs) * nqb)}, block{256};
+  hipLaunchKernelGGL(balanced_merge_kernel, grid, block, 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace pa

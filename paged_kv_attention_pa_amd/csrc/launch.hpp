@@ -51,6 +51,35 @@ struct LseMerge {
 };
 hipError_t launch_lse_merge(const LseMerge& a, hipStream_t s);
 
+// Token-balanced decode (bf16, head_dim 128): range j of num_ranges covers
+// chunks [j T / nr, (j+1) T / nr) of the concatenated 32-token chunk list,
+// nr = min(num_ranges, T).  Requests inside one range go to out/lse; the
+// others leave one segment per range in part[(j + r) * Hq + head][132]
+// (values 0..127, lse at 128).  cu[B + 1] receives the chunk prefix sums.
+struct DecodeBalanced {
+  const void* q; const void* cache;
+  int64_t num_blocks; int block_size;
+  const int32_t* block_table; int max_blocks;
+  const int32_t* seq_lens; int num_seqs; int len_cap;   // len_cap = max_blocks * block_size
+  int num_q_heads; int num_kv_heads;
+  float scale;
+  int num_ranges;
+  int32_t* cu; float* part;
+  void* out; float* lse;
+};
+hipError_t launch_decode_balanced(const DecodeBalanced& a, hipStream_t s);
+
+struct BalancedMerge {
+  const int32_t* cu; const float* part;
+  int num_seqs; int num_q_heads; int num_ranges;
+  void* out; float* lse;
+};
+hipError_t launch_balanced_merge(const BalancedMerge& a, hipStream_t s);
+
+int balanced_num_ranges(int num_kv_heads, int num_cus);   // ranges for 8 waves per CU
+size_t balanced_cu_bytes(int num_seqs);                    // cu[] size, 256-B aligned
+size_t balanced_part_row_floats();                         // 132
+
 // ------------------------------------------------------------------- MLA
 struct MlaDecode {
   const void* q_nope; int64_t qn_sb, qn_sh;

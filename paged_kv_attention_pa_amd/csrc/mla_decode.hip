@@ -38,16 +38,6 @@ constexpr int kMaxWaves = 8;
 // over all banks.
 __device__ __forceinline__ int tile_off(int r, int c) { return r * kRowBytes + 16 * (c ^ (r & 7)); }
 
-typedef __attribute__((ext_vector_type(4))) short s16x4_t;
-
-__device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
-
-__device__ __forceinline__ uint2 lds_read_tr(const char* p) {
-  typedef __attribute__((address_space(3))) s16x4_t lds_s4;
-  const s16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(p));
-  return __builtin_bit_cast(uint2, v);
-}
-
 // Max / sum over the four lanes l, l^16, l^32, l^48 (one head).
 __device__ __forceinline__ float head_max(float x) {
   x = fmaxf(x, lane_xor(x, 16));

@@ -98,6 +98,21 @@ __device__ __forceinline__ T uniform_load(const T* p) {
       reinterpret_cast<uintptr_t>(p));
 }
 
+// ------------------------------------------------------ MFMA operand views
+typedef __attribute__((ext_vector_type(4))) short s16x4_t;
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
+
+// Four b16 values from LDS, transposed within each 16-lane group: lane i of
+// the group receives element (i % 4) of the 8-byte chunks addressed by lanes
+// 4q + i/4, q = 0..3 (so a group reading a 4-row x 16-column block gets one
+// column of 4 rows per lane).  ds_read_b64_tr_b16.
+__device__ __forceinline__ uint2 lds_read_tr(const char* p) {
+  typedef __attribute__((address_space(3))) s16x4_t lds_s4;
+  const s16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(p));
+  return __builtin_bit_cast(uint2, v);
+}
+
 // ------------------------------------------------------------ 16-B access
 __device__ __forceinline__ u32x4_t load16(const void* p) {
   return *reinterpret_cast<const u32x4_t*>(p);

@@ -35,28 +35,14 @@ constexpr int kBN = 64;            // keys per tile
 constexpr int kRowBytes = kD * 2;        // 256 B per key row (unpadded, swizzled)
 constexpr int kTileBytes = kBN * kRowBytes;  // 16 KiB
 constexpr int kTileLoads = kBN * kRowBytes / 1024;  // 16 wave-wide 16-byte loads per tile
+constexpr int kXcds = 8;           // accelerator dies work-groups are dealt to
+constexpr float kSlack = 8.0f;     // lazy-rescale headroom, log2 units
 // 16-byte chunk c of key row r sits in slot c ^ swz(r) of the row, with
 // swz(r) = 2 (r % 8) + (r / 8) % 2 (a permutation of r % 16).  Rows are
 // 256 B, so every row starts on the same bank; the XOR spreads the 16 rows of
 // a K-fragment load, and rows 0..7 of a V transpose read (which move the
 // 4-slot groups), over all 16 slots, i.e. all banks.
-constexpr int kXcds = 8;
-constexpr float kSlack = 8.0f;     // lazy-rescale headroom, log2 units
-__device__ __forceinline__ int swz(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }           // accelerator dies work-groups are dealt to
-
-typedef __attribute__((ext_vector_type(4))) short s16x4_t;
-
-__device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
-
-// Four b16 values from LDS, transposed within each 16-lane group: lane i of
-// the group receives element (i % 4) of the 8-byte chunks addressed by lanes
-// 4q + i/4, q = 0..3 (so a group reading a 4-row x 16-column block gets one
-// column of 4 rows per lane).
-__device__ __forceinline__ uint2 lds_read_tr(const char* p) {
-  typedef __attribute__((address_space(3))) s16x4_t lds_s4;
-  const s16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(p));
-  return __builtin_bit_cast(uint2, v);
-}
+__device__ __forceinline__ int swz(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
 
 __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillVarlen a) {
   __shared__ __align__(16) char smem[4 * kTileBytes];   // 2 x (K tile, V tile)

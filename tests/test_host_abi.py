@@ -180,3 +180,48 @@ def test_scale_must_be_finite_non_negative(lib):
     assert _decode(lib, scale=-0.5) == INVALID
     assert _decode(lib, scale=float("inf")) == INVALID
     assert _decode(lib, scale=float("nan")) == INVALID
+
+
+def test_balanced_helpers(lib):
+    # eight waves per compute unit: one range per CU for 8 KV heads, more for fewer
+    assert pa.decode_balanced_num_ranges(8, 256) == 256
+    assert pa.decode_balanced_num_ranges(2, 256) == 1024
+    assert pa.decode_balanced_num_ranges(1, 256) == 2048
+    assert pa.decode_balanced_num_ranges(16, 256) == 128
+    assert pa.decode_balanced_num_ranges(8, 0) == 1
+    # cu[B + 1] rounded to 256 B, then (ranges + B) * Hq rows of 132 fp32
+    assert pa.decode_balanced_workspace_bytes(64, 32, 256) == 512 + (256 + 64) * 32 * 132 * 4
+    assert pa.decode_balanced_workspace_bytes(63, 32, 256) == 256 + (256 + 63) * 32 * 132 * 4
+    assert pa.decode_balanced_workspace_bytes(4, 64, 256) == 256 + 260 * 64 * 132 * 4
+    assert pa.decode_balanced_workspace_bytes(-1, 32, 256) == 0
+    assert pa.decode_balanced_workspace_bytes(4, 32, 0) == 0
+
+
+def test_balanced_validation(lib):
+    f = lib.pa_decode_balanced
+    need = pa.decode_balanced_workspace_bytes(4, 32, 16)
+    #        q  cache  nb  bs  table maxb seq B  hq  hkv d    scale nr  ws       wsb   out  lse
+    base = [1, 2, 100, 16, 3, 64, 4, 4, 32, 8, 128, 0.1, 16, 1 << 20, need, 5, None, None]
+
+    def call(**kw):
+        a = list(base)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return f(*a)
+
+    assert call(a12=0) == INVALID                    # no ranges
+    assert call(a14=need - 1) == WORKSPACE           # workspace too small
+    assert call(a13=None) == WORKSPACE
+    assert call(a13=(1 << 20) + 4) == INVALID        # misaligned workspace
+    assert call(a10=64) == UNSUPPORTED               # head_dim 64
+    assert call(a8=96) == UNSUPPORTED                # group 12
+    assert call(a11=-1.0) == INVALID                 # negative scale
+    assert call(a3=24) == INVALID                    # block size 24
+    assert call(a15=None) == INVALID                 # no output
+    assert call(a5=1 << 30, a7=1 << 20) == UNSUPPORTED   # chunk count past int32
+    m = lib.pa_decode_balanced_merge
+    assert m(1 << 20, need - 1, 4, 32, 128, 16, 5, None, None) == WORKSPACE
+    assert m(1 << 20, need, 4, 32, 128, 0, 5, None, None) == INVALID
+    assert m(1 << 20, need, 4, 32, 64, 16, 5, None, None) == UNSUPPORTED
+    assert m(1 << 20, need, 4, 32, 128, 16, None, None, None) == INVALID
+    assert m(None, 0, 0, 32, 128, 16, None, None, None) == WORKSPACE
