@@ -306,13 +306,18 @@ __global__ __launch_bounds__(64 * kHeads, 1) void decode_balanced_kernel(DecodeB
 }
 
 // Combine the segments of requests that cross ranges.  One work-group per
-// (request, 8 query heads): 32 threads x 4 dims per head row.
+// (request, query head): 8 groups of 32 threads (4 dims each) take every 8th
+// segment and keep a running (max, sum, output) each; the 8 states are then
+// merged through LDS.  A long request's segments are thus read 8 at a time.
+constexpr int kMergeGroups = 8;
+
 __global__ __launch_bounds__(256) void balanced_merge_kernel(BalancedMerge a) {
+  __shared__ float s_m[kMergeGroups], s_l[kMergeGroups];
+  __shared__ __align__(16) float s_o[kMergeGroups][kD];
   const int Hq = a.num_q_heads;
-  const int nqb = (Hq + 7) / 8;
-  const int r = blockIdx.x / nqb;
-  const int hq = (blockIdx.x % nqb) * 8 + (threadIdx.x >> 5);
-  if (hq >= Hq) return;
+  const int r = blockIdx.x / Hq;
+  const int hq = blockIdx.x % Hq;
+  const int g = threadIdx.x >> 5;
   const int d = 4 * (threadIdx.x & 31);
   const int B = a.num_seqs;
   const int total = a.cu[B];
@@ -321,8 +326,8 @@ __global__ __launch_bounds__(256) void balanced_merge_kernel(BalancedMerge a) {
   const int64_t row = int64_t(r) * Hq + hq;
   uint2* op = reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + row * kD + d);
   if (cb == ce) {   // no keys: out 0, lse -inf
-    *op = uint2{0u, 0u};
-    if (a.lse && d == 0) a.lse[row] = -INFINITY;
+    if (g == 0) *op = uint2{0u, 0u};
+    if (a.lse && threadIdx.x == 0) a.lse[row] = -INFINITY;
     return;
   }
   const int nr = min(a.num_ranges, total);
@@ -331,19 +336,41 @@ __global__ __launch_bounds__(256) void balanced_merge_kernel(BalancedMerge a) {
   if (j0 == j1) return;   // written by its range
   const int64_t step = int64_t(Hq) * kPartRow;
   const float* p0 = a.part + (int64_t(j0 + r) * Hq + hq) * kPartRow;
-  float m = -INFINITY;
-  for (int jj = 0; jj <= j1 - j0; ++jj) m = fmaxf(m, p0[jj * step + kD]);
-  float den = 0.0f;
+  float m = -INFINITY, l = 0.0f;
   f32x4_t o = f32x4_t{0, 0, 0, 0};
-  for (int jj = 0; jj <= j1 - j0; ++jj) {
+#pragma unroll 4
+  for (int jj = g; jj <= j1 - j0; jj += kMergeGroups) {
     const float* pp = p0 + jj * step;
-    const float w = fast_exp2((pp[kD] - m) * kLog2e);
-    den += w;
-    o += w * *reinterpret_cast<const f32x4_t*>(pp + d);
+    const float lj = pp[kD];
+    const f32x4_t oj = *reinterpret_cast<const f32x4_t*>(pp + d);
+    const float mn = fmaxf(m, lj);
+    const float c = fast_exp2((m - mn) * kLog2e);   // 0 while m = -inf
+    const float w = fast_exp2((lj - mn) * kLog2e);
+    l = fmaf(l, c, w);
+    o = o * c + w * oj;
+    m = mn;
+  }
+  if ((threadIdx.x & 31) == 0) {
+    s_m[g] = m;
+    s_l[g] = l;
+  }
+  *reinterpret_cast<f32x4_t*>(&s_o[g][d]) = o;
+  __syncthreads();
+  if (g != 0) return;
+  float mm = s_m[0];
+#pragma unroll
+  for (int k = 1; k < kMergeGroups; ++k) mm = fmaxf(mm, s_m[k]);
+  float den = 0.0f;
+  f32x4_t acc = f32x4_t{0, 0, 0, 0};
+#pragma unroll
+  for (int k = 0; k < kMergeGroups; ++k) {
+    const float w = fast_exp2((s_m[k] - mm) * kLog2e);   // 0 for a group without segments
+    den = fmaf(s_l[k], w, den);
+    acc += w * *reinterpret_cast<const f32x4_t*>(&s_o[k][d]);
   }
   const float inv = 1.0f / den;
-  *op = uint2{pack_bf16x2(o[0] * inv, o[1] * inv), pack_bf16x2(o[2] * inv, o[3] * inv)};
-  if (a.lse && d == 0) a.lse[row] = m + fast_log2(den) * kLn2;
+  *op = uint2{pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv)};
+  if (a.lse && threadIdx.x == 0) a.lse[row] = mm + fast_log2(den) * kLn2;
 }
 
 }  // namespace
@@ -376,8 +403,7 @@ hipError_t launch_decode_balanced(const DecodeBalanced& a, hipStream_t s) {
 }
 
 hipError_t launch_balanced_merge(const BalancedMerge& a, hipStream_t s) {
-  const int nqb = (a.num_q_heads + 7) / 8;
-  const dim3 grid{unsigned(int64_t(a.num_seqs) * nqb)}, block{256};
+  const dim3 grid{unsigned(int64_t(a.num_seqs) * a.num_q_heads)}, block{256};
   hipLaunchKernelGGL(balanced_merge_kernel, grid, block, 0, s, a);
   return hipGetLastError();
 }
