@@ -225,14 +225,41 @@ def time_steps(fn, steps, warmup):
     return (time.perf_counter() - t0) / steps
 
 
+_SPIN_RATE = None
+
+
+def _hold_gpu(seconds):
+    """Queue torch's bounded spin kernel for about ``seconds`` so that the
+    launches issued next are all enqueued before the GPU reaches them: the
+    events then time back-to-back kernels, not the host's launch gaps."""
+    import torch
+    global _SPIN_RATE
+    if _SPIN_RATE is None:   # counter ticks per second of the spin kernel
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        s.record()
+        torch.cuda._sleep(10_000_000)
+        e.record()
+        e.synchronize()
+        _SPIN_RATE = 10_000_000 / max(s.elapsed_time(e) / 1e3, 1e-6)
+    torch.cuda._sleep(int(seconds * _SPIN_RATE))
+
+
 def time_kernel_events(fn, reps, warmup):
     """Average duration of one launch of ``fn``'s kernel, from HIP events
-    recorded on torch's current stream (the stream the library launches on)."""
+    recorded on torch's current stream (the stream the library launches on),
+    with the launches queued behind a spin kernel so none waits on the host."""
     import torch
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        fn()
+    host_s = time.perf_counter() - t0
+    torch.cuda.synchronize()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    _hold_gpu(2 * host_s + 2e-3)
     start.record()
     for _ in range(reps):
         fn()
