@@ -88,7 +88,7 @@ def gqa_decode_case(b, num_splits, name):
     balanced = num_splits == 0 and n > 1 and b.dtype == W.BF16
     if balanced:
         nr = pa.decode_balanced_num_ranges(b.num_kv_heads, cus)
-        wsb = pa.decode_balanced_workspace_bytes(b.num_seqs, b.num_q_heads, nr)
+        wsb = pa.decode_balanced_workspace_bytes(b.num_seqs, b.num_q_heads, b.head_dim, nr)
     else:
         wsb = pa.decode_workspace_bytes(b.num_seqs, b.num_q_heads, b.head_dim, n)
     ws = torch.empty(max(1, wsb // 4), dtype=torch.float32, device="cuda")
@@ -163,28 +163,29 @@ def mla_case(b, name):
     qn, qp = _dev(b.q_nope), _dev(b.q_pe)
     bt, sl = _dev(b.block_table), _dev(b.seq_lens)
     kc, kp, sm = _dev(b.kv_c_new), _dev(b.k_pe_new), _dev(b.slot_mapping)
-    n = pa.mla_num_kv_splits(b.num_seqs, b.max_seq_len, pa.device_num_cus())
-    ws = torch.empty(max(1, pa.decode_workspace_bytes(b.num_seqs, b.num_heads, b.kv_lora_rank, n) // 4),
-                     dtype=torch.float32, device="cuda")
+    # automatic schedule: token-balanced ranges, one per compute unit
+    nr = pa.device_num_cus()
+    wsb = pa.decode_balanced_workspace_bytes(b.num_seqs, b.num_heads, b.kv_lora_rank, nr)
+    ws = torch.empty(max(1, wsb // 4), dtype=torch.float32, device="cuda")
     out = torch.empty((b.num_seqs, b.num_heads, b.kv_lora_rank), dtype=torch.bfloat16, device="cuda")
     lse = torch.empty((b.num_seqs, b.num_heads), dtype=torch.float32, device="cuda")
 
     def step():
         pa.mla_decode(qn, qp, cache, bt, sl, b.max_seq_len, b.scale, kv_c=kc, k_pe=kp,
-                      slot_mapping=sm, num_splits=n, workspace=ws, out=out, lse=lse)
+                      slot_mapping=sm, num_splits=0, workspace=ws, out=out, lse=lse)
 
     def kernel():
-        pa.mla_decode(qn, qp, cache, bt, sl, b.max_seq_len, b.scale, num_splits=n,
-                      workspace=ws, stage1_only=True)
+        pa.mla_decode_balanced(qn, qp, cache, bt, sl, b.scale, num_ranges=nr, workspace=ws,
+                               out=out, lse=lse, merge=False)
 
     by = W.mla_bytes(b)
     kb = by["kv"] + by["q"] + by["meta"] - b.num_seqs * 8
     fl = W.mla_flops(b)
     info = {"num_seqs": b.num_seqs, "num_heads": b.num_heads, "kv_lora_rank": b.kv_lora_rank,
             "rope_dim": b.rope_dim, "block_size": b.block_size, "max_seq_len": b.max_seq_len,
-            "total_keys": int(b.seq_lens.sum()), "num_splits": n,
-            "grid": f"{b.num_seqs}x{n} work-groups of 512"}
-    return Case(name, step, kernel, by["total"], fl, kb, fl, "mfma", "mla_split_kernel",
+            "total_keys": int(b.seq_lens.sum()), "schedule": "token-balanced ranges",
+            "grid": f"{nr} token ranges x 8 waves (16 heads each)"}
+    return Case(name, step, kernel, by["total"], fl, kb, fl, "mfma", "mla_kernel<true>",
                 "mla_decode.hip", info)
 
 

@@ -195,25 +195,28 @@ pa_status_t pa_decode(pa_dtype_t dtype,
  *   compute units (num_cus * 8 / (min(num_kv_heads, 8) * ceil(num_kv_heads /
  *   8)), at least 1); what pa_decode uses.
  * pa_decode_balanced_workspace_bytes: bytes of workspace: 4 (num_seqs + 1)
- *   rounded up to 256, plus (num_ranges + num_seqs) * num_q_heads * 132 * 4.
- *   Returns 0 for negative sizes or num_ranges < 1.
+ *   rounded up to 256, plus (num_ranges + num_seqs) * num_heads *
+ *   (head_dim_v + 4) * 4 (head_dim_v = 128 for GQA, 512 for MLA).  Returns 0
+ *   for negative sizes or num_ranges < 1.
  *
  * pa_decode_balanced arguments are those of pa_decode (no new-token write:
  * call pa_cache_write first), with:
  * num_ranges:  [1, 2^24]; the workspace must hold
- *              pa_decode_balanced_workspace_bytes(num_seqs, num_q_heads,
+ *              pa_decode_balanced_workspace_bytes(num_seqs, num_q_heads, 128,
  *              num_ranges) bytes, 16-byte aligned (PA_ERR_WORKSPACE if not).
  * out, lse:    as pa_decode; after this call only the requests inside one
  *              range are final.
  * Supported: PA_BF16 storage, head_dim 128, num_q_heads / num_kv_heads in
  * {1, 2, 4, 8}, num_seqs * ceil(max_blocks_per_seq * block_size / 32) < 2^31.
  * pa_decode_balanced_merge completes out / lse (a request with no keys gets
- * out = 0, lse = -inf); its num_seqs, num_q_heads, head_dim, num_ranges and
- * workspace must be those of the preceding pa_decode_balanced call.
+ * out = 0, lse = -inf) after pa_decode_balanced (head_dim_v 128) or
+ * pa_mla_decode_balanced (head_dim_v 512); its num_seqs, num_heads,
+ * num_ranges and workspace must be those of the preceding call.
  * ------------------------------------------------------------------------- */
 int pa_decode_balanced_num_ranges(int num_kv_heads, int num_cus);
 
-size_t pa_decode_balanced_workspace_bytes(int num_seqs, int num_q_heads, int num_ranges);
+size_t pa_decode_balanced_workspace_bytes(int num_seqs, int num_heads, int head_dim_v,
+                                          int num_ranges);
 
 pa_status_t pa_decode_balanced(const void* q, const void* kv_cache, int64_t num_blocks,
                                int block_size, const int32_t* block_table,
@@ -223,7 +226,7 @@ pa_status_t pa_decode_balanced(const void* q, const void* kv_cache, int64_t num_
                                void* out, float* lse, hipStream_t stream);
 
 pa_status_t pa_decode_balanced_merge(void* workspace, size_t workspace_bytes, int num_seqs,
-                                     int num_q_heads, int head_dim, int num_ranges, void* out,
+                                     int num_heads, int head_dim_v, int num_ranges, void* out,
                                      float* lse, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
@@ -274,16 +277,23 @@ pa_status_t pa_prefill_varlen(pa_dtype_t dtype,
  *         (dense), or both NULL; slot_mapping [num_seqs] or NULL.
  * kv_cache: MLA layout [num_blocks, block_size, kv_lora_rank + rope_dim].
  * block_table, seq_lens, max_seq_len, scale: as in pa_decode.
- * num_splits: 0 = n = pa_mla_num_kv_splits(num_seqs, max_seq_len, CUs); else
- *         as in pa_decode (P rounded up to a multiple of block_size).
+ * num_splits: 0 = automatic: with n = pa_mla_num_kv_splits(num_seqs,
+ *         max_seq_len, CUs), n == 1 runs one unsplit pass; n > 1 with out !=
+ *         NULL runs the token-balanced schedule (pa_mla_decode_balanced with
+ *         num_ranges = CUs, then pa_decode_balanced_merge), whose reduction
+ *         order depends on the whole batch's lengths; otherwise n splits as
+ *         in pa_decode (P rounded up to a multiple of block_size).
  * workspace: pa_decode_workspace_bytes(num_seqs, num_heads, kv_lora_rank, n)
- *         bytes, as in pa_decode.
+ *         bytes for n splits, or for the balanced schedule
+ *         pa_decode_balanced_workspace_bytes(num_seqs, num_heads, 512, CUs)
+ *         bytes (16-byte aligned), as in pa_decode.
  * out:    [num_seqs, num_heads, kv_lora_rank], or NULL for the two-stage form
  *         (partials [num_seqs, num_heads, n, kv_lora_rank + 1] in the
  *         workspace); lse [num_seqs, num_heads] or NULL (NULL if out is).
  * Supported: PA_BF16 only (no dtype argument), kv_lora_rank 512, rope_dim 64,
  * num_heads a multiple of 16 up to 128, block_size a multiple of 16.
- * Enqueues: the write (if given), the split kernel, the merge kernel.
+ * Enqueues: the write (if given), the split (or balanced) kernel, the merge
+ * kernel.
  * ------------------------------------------------------------------------- */
 pa_status_t pa_mla_decode(const void* q_nope, int64_t qn_stride_b, int64_t qn_stride_h,
                           const void* q_pe, int64_t qp_stride_b, int64_t qp_stride_h,
@@ -296,6 +306,23 @@ pa_status_t pa_mla_decode(const void* q_nope, int64_t qn_stride_b, int64_t qn_st
                           float scale, int num_splits,
                           void* workspace, size_t workspace_bytes,
                           void* out, float* lse, hipStream_t stream);
+
+/* pa_mla_decode_balanced -- pa_mla_decode's reduction cut into token-balanced
+ * ranges (see pa_decode_balanced: 32-key chunks of the whole batch, range j =
+ * chunks [floor(j T / nr), floor((j+1) T / nr)), one work-group each).
+ * Arguments as in pa_mla_decode (no latent write: call pa_cache_write
+ * first), with num_ranges in [1, 2^24] and a 16-byte aligned workspace of
+ * pa_decode_balanced_workspace_bytes(num_seqs, num_heads, 512, num_ranges)
+ * bytes.  Requests inside one range are final in out / lse afterwards;
+ * pa_decode_balanced_merge(..., head_dim_v = 512, ...) completes the rest. */
+pa_status_t pa_mla_decode_balanced(const void* q_nope, int64_t qn_stride_b, int64_t qn_stride_h,
+                                   const void* q_pe, int64_t qp_stride_b, int64_t qp_stride_h,
+                                   const void* kv_cache, int64_t num_blocks, int block_size,
+                                   const int32_t* block_table, int max_blocks_per_seq,
+                                   const int32_t* seq_lens, int num_seqs, int num_heads,
+                                   int kv_lora_rank, int rope_dim, float scale, int num_ranges,
+                                   void* workspace, size_t workspace_bytes, void* out,
+                                   float* lse, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
  * pa_lse_merge -- merge split-KV partials by log-sum-exp ("第 1 章 注意力后端",

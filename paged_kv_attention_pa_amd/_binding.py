@@ -39,10 +39,13 @@ _SIGNATURES = {
                              _vp, _vp, _vp]),
     "pa_lse_merge": (_i32, [_vp, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp]),
     "pa_decode_balanced_num_ranges": (_i32, [_i32, _i32]),
-    "pa_decode_balanced_workspace_bytes": (_sz, [_i32, _i32, _i32]),
+    "pa_decode_balanced_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32]),
     "pa_decode_balanced": (_i32, [_vp, _vp, _i64, _i32, _vp, _i32, _vp, _i32, _i32, _i32, _i32,
                                   _f32, _i32, _vp, _sz, _vp, _vp, _vp]),
     "pa_decode_balanced_merge": (_i32, [_vp, _sz, _i32, _i32, _i32, _i32, _vp, _vp, _vp]),
+    "pa_mla_decode_balanced": (_i32, [_vp, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _i32, _vp,
+                                      _i32, _vp, _i32, _i32, _i32, _i32, _f32, _i32, _vp, _sz,
+                                      _vp, _vp, _vp]),
 }
 EXPORTED_SYMBOLS = tuple(_SIGNATURES)
 
@@ -108,9 +111,10 @@ def decode_balanced_num_ranges(num_kv_heads: int, num_cus: int) -> int:
     return library().pa_decode_balanced_num_ranges(int(num_kv_heads), int(num_cus))
 
 
-def decode_balanced_workspace_bytes(num_seqs: int, num_q_heads: int, num_ranges: int) -> int:
-    return library().pa_decode_balanced_workspace_bytes(int(num_seqs), int(num_q_heads),
-                                                        int(num_ranges))
+def decode_balanced_workspace_bytes(num_seqs: int, num_heads: int, head_dim_v: int,
+                                    num_ranges: int) -> int:
+    return library().pa_decode_balanced_workspace_bytes(int(num_seqs), int(num_heads),
+                                                        int(head_dim_v), int(num_ranges))
 
 
 def device_num_cus() -> int:
@@ -215,7 +219,7 @@ def decode(q, kv_cache, block_table, seq_lens, max_seq_len: int, scale: float,
     if num_splits == 0 and n > 1 and not stage1_only and dt == PA_BF16:
         # the automatic schedule is the token-balanced one
         need = decode_balanced_workspace_bytes(
-            B, Hq, decode_balanced_num_ranges(hkv, device_num_cus()))
+            B, Hq, D, decode_balanced_num_ranges(hkv, device_num_cus()))
     if workspace is None and need:
         workspace = torch.empty(need // 4, dtype=torch.float32, device=q.device)
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
@@ -251,7 +255,7 @@ def decode_balanced(q, kv_cache, block_table, seq_lens, scale: float, num_ranges
         out = torch.empty_like(q)
     if lse is None and return_lse:
         lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
-    need = decode_balanced_workspace_bytes(B, Hq, nr)
+    need = decode_balanced_workspace_bytes(B, Hq, D, nr)
     if workspace is None:
         workspace = torch.empty(max(1, need // 4), dtype=torch.float32, device=q.device)
     wbytes = workspace.numel() * workspace.element_size()
@@ -265,14 +269,14 @@ def decode_balanced(q, kv_cache, block_table, seq_lens, scale: float, num_ranges
     return out, lse, workspace, nr
 
 
-def decode_balanced_merge(workspace, num_seqs: int, num_q_heads: int, head_dim: int,
+def decode_balanced_merge(workspace, num_seqs: int, num_heads: int, head_dim_v: int,
                           num_ranges: int, out, lse=None, stream=None):
-    """Second kernel of the balanced decode: combine the partials of requests
-    that cross ranges into out / lse."""
+    """Second kernel of the balanced GQA (head_dim_v 128) or MLA (512) decode:
+    combine the partials of requests that cross ranges into out / lse."""
     _dev(workspace, out, lse)
     wbytes = workspace.numel() * workspace.element_size()
     _check(library().pa_decode_balanced_merge(_ptr(workspace), wbytes, int(num_seqs),
-                                              int(num_q_heads), int(head_dim), int(num_ranges),
+                                              int(num_heads), int(head_dim_v), int(num_ranges),
                                               _ptr(out), _ptr(lse), _stream(stream)))
 
 
@@ -331,6 +335,9 @@ def mla_decode(q_nope, q_pe, kv_cache, block_table, seq_lens, max_seq_len: int, 
     if n == 0:
         n = mla_num_kv_splits(B, max_seq_len, device_num_cus())
     need = decode_workspace_bytes(B, H, R, n) if (n > 1 or stage1_only) else 0
+    if num_splits == 0 and n > 1 and not stage1_only:
+        # the automatic schedule is the token-balanced one, one range per CU
+        need = decode_balanced_workspace_bytes(B, H, R, device_num_cus())
     if workspace is None and need:
         workspace = torch.empty(need // 4, dtype=torch.float32, device=q_nope.device)
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
@@ -344,6 +351,41 @@ def mla_decode(q_nope, q_pe, kv_cache, block_table, seq_lens, max_seq_len: int, 
     if stage1_only:
         return workspace[: B * H * n * (R + 1)].view(B, H, n, R + 1)
     return out, lse
+
+
+def mla_decode_balanced(q_nope, q_pe, kv_cache, block_table, seq_lens, scale: float,
+                        num_ranges: int = 0, workspace=None, out=None, lse=None,
+                        return_lse: bool = True, merge: bool = True, stream=None):
+    """Token-balanced MLA decode (no latent write).  num_ranges = 0 takes the
+    device's CU count.  merge=False runs only the first kernel (see
+    ``decode_balanced``).  Returns (out, lse, workspace, num_ranges)."""
+    torch = _torch()
+    _dev(kv_cache, block_table, seq_lens, workspace, out, lse)
+    for t in (q_nope, q_pe):
+        _need(t.is_cuda and t.stride(-1) == 1, "q_nope/q_pe must be GPU tensors with a contiguous last dim")
+        _need(t.dtype == torch.bfloat16, "MLA decode is bf16 only")
+    B, H, R = q_nope.shape
+    P = q_pe.shape[2]
+    nb, bs, row = kv_cache.shape
+    _need(row == R + P, "cache row must be kv_lora_rank + rope_dim")
+    nr = int(num_ranges) or device_num_cus()
+    if out is None:
+        out = torch.empty((B, H, R), dtype=q_nope.dtype, device=q_nope.device)
+    if lse is None and return_lse:
+        lse = torch.empty((B, H), dtype=torch.float32, device=q_nope.device)
+    need = decode_balanced_workspace_bytes(B, H, R, nr)
+    if workspace is None:
+        workspace = torch.empty(max(1, need // 4), dtype=torch.float32, device=q_nope.device)
+    wbytes = workspace.numel() * workspace.element_size()
+    _check(library().pa_mla_decode_balanced(_ptr(q_nope), q_nope.stride(0), q_nope.stride(1),
+                                            _ptr(q_pe), q_pe.stride(0), q_pe.stride(1),
+                                            _ptr(kv_cache), nb, bs, _ptr(block_table),
+                                            block_table.shape[1], _ptr(seq_lens), B, H, R, P,
+                                            float(scale), nr, _ptr(workspace), wbytes, _ptr(out),
+                                            _ptr(lse), _stream(stream)))
+    if merge:
+        decode_balanced_merge(workspace, B, H, R, nr, out, lse, stream=stream)
+    return out, lse, workspace, nr
 
 
 def lse_merge(part, out_dtype=None, out=None, lse=None, return_lse: bool = True, stream=None):

@@ -81,25 +81,26 @@ pa_status_t check_common_cache(int64_t num_blocks, int block_size,
 }
 
 // Token-balanced decode: workspace = cu[num_seqs + 1] (256-B aligned), then
-// (num_ranges + num_seqs) * num_q_heads segment rows of 132 fp32.
-size_t balanced_bytes(int num_seqs, int num_q_heads, int num_ranges) {
-  if (num_seqs < 0 || num_q_heads < 0 || num_ranges < 1) return 0;
+// (num_ranges + num_seqs) * num_heads segment rows of head_dim_v + 4 fp32.
+size_t balanced_bytes(int num_seqs, int num_heads, int head_dim_v, int num_ranges) {
+  if (num_seqs < 0 || num_heads < 0 || head_dim_v < 0 || num_ranges < 1) return 0;
   const unsigned __int128 b = (unsigned __int128)pa::balanced_cu_bytes(num_seqs) +
                               (unsigned __int128)((int64_t)num_ranges + num_seqs) *
-                                  (unsigned)num_q_heads * pa::balanced_part_row_floats() * 4u;
+                                  (unsigned)num_heads * ((unsigned)head_dim_v + 4u) * 4u;
   if (b > (unsigned __int128)SIZE_MAX) return 0;
   return size_t(b);
 }
 
-pa_status_t check_balanced(int num_seqs, int num_q_heads, int max_blocks_per_seq, int block_size,
-                           int num_ranges, const void* workspace, size_t workspace_bytes) {
+pa_status_t check_balanced(int num_seqs, int num_heads, int head_dim_v, int max_blocks_per_seq,
+                           int block_size, int num_ranges, const void* workspace,
+                           size_t workspace_bytes) {
   PA_REQUIRE(num_ranges >= 1 && num_ranges <= (1 << 24), PA_ERR_INVALID,
              "num_ranges must be in [1, 2^24] (got %d)", num_ranges);
   // chunk counts are summed in int32 on the device
   const int64_t len_cap = int64_t(max_blocks_per_seq) * block_size;
   PA_REQUIRE(int64_t(num_seqs) * ((len_cap + 31) / 32) <= INT_MAX, PA_ERR_UNSUPPORTED,
              "num_seqs * max_blocks_per_seq * block_size / 32 exceeds 2^31 chunks");
-  const size_t need = balanced_bytes(num_seqs, num_q_heads, num_ranges);
+  const size_t need = balanced_bytes(num_seqs, num_heads, head_dim_v, num_ranges);
   PA_REQUIRE(need > 0 && workspace != nullptr && workspace_bytes >= need, PA_ERR_WORKSPACE,
              "workspace of %zu bytes needed for %d ranges (got %zu)", need, num_ranges,
              workspace_bytes);
@@ -251,8 +252,8 @@ pa_status_t pa_decode(pa_dtype_t dtype,
   const bool balanced = num_splits == 0 && !stage1 && !direct && dtype == PA_BF16;
   const int nr = balanced ? pa_decode_balanced_num_ranges(num_kv_heads, cus) : 0;
   if (balanced) {
-    st = check_balanced(num_seqs, num_q_heads, max_blocks_per_seq, block_size, nr, workspace,
-                        workspace_bytes);
+    st = check_balanced(num_seqs, num_q_heads, head_dim, max_blocks_per_seq, block_size, nr,
+                        workspace, workspace_bytes);
     if (st != PA_OK) return st;
   } else if (!direct) {
     const size_t need = pa_decode_workspace_bytes(num_seqs, num_q_heads, head_dim, n);
@@ -311,8 +312,9 @@ int pa_decode_balanced_num_ranges(int num_kv_heads, int num_cus) {
   return pa::balanced_num_ranges(num_kv_heads, num_cus);
 }
 
-size_t pa_decode_balanced_workspace_bytes(int num_seqs, int num_q_heads, int num_ranges) {
-  return balanced_bytes(num_seqs, num_q_heads, num_ranges);
+size_t pa_decode_balanced_workspace_bytes(int num_seqs, int num_heads, int head_dim_v,
+                                          int num_ranges) {
+  return balanced_bytes(num_seqs, num_heads, head_dim_v, num_ranges);
 }
 
 pa_status_t pa_decode_balanced(const void* q, const void* kv_cache, int64_t num_blocks,
@@ -334,7 +336,7 @@ pa_status_t pa_decode_balanced(const void* q, const void* kv_cache, int64_t num_
   PA_REQUIRE(is_pow2_group(num_q_heads / num_kv_heads), PA_ERR_UNSUPPORTED,
              "balanced decode supports num_q_heads / num_kv_heads in {1, 2, 4, 8} (got %d)",
              num_q_heads / num_kv_heads);
-  st = check_balanced(num_seqs, num_q_heads, max_blocks_per_seq, block_size, num_ranges,
+  st = check_balanced(num_seqs, num_q_heads, head_dim, max_blocks_per_seq, block_size, num_ranges,
                       workspace, workspace_bytes);
   if (st != PA_OK) return st;
   if (num_seqs == 0) return ok();
@@ -350,22 +352,22 @@ pa_status_t pa_decode_balanced(const void* q, const void* kv_cache, int64_t num_
 }
 
 pa_status_t pa_decode_balanced_merge(void* workspace, size_t workspace_bytes, int num_seqs,
-                                     int num_q_heads, int head_dim, int num_ranges, void* out,
+                                     int num_heads, int head_dim_v, int num_ranges, void* out,
                                      float* lse, hipStream_t stream) {
   PA_REQUIRE(num_seqs >= 0, PA_ERR_INVALID, "num_seqs must be >= 0 (got %d)", num_seqs);
-  PA_REQUIRE(num_q_heads > 0, PA_ERR_INVALID, "num_q_heads must be > 0");
-  PA_REQUIRE(head_dim == 128, PA_ERR_UNSUPPORTED, "balanced decode supports head_dim 128 (got %d)",
-             head_dim);
+  PA_REQUIRE(num_heads > 0, PA_ERR_INVALID, "num_heads must be > 0");
+  PA_REQUIRE(head_dim_v == 128 || head_dim_v == 512, PA_ERR_UNSUPPORTED,
+             "balanced merge supports head_dim_v 128 (GQA) and 512 (MLA) (got %d)", head_dim_v);
   PA_REQUIRE(num_ranges >= 1 && num_ranges <= (1 << 24), PA_ERR_INVALID,
              "num_ranges must be in [1, 2^24] (got %d)", num_ranges);
-  const size_t need = balanced_bytes(num_seqs, num_q_heads, num_ranges);
+  const size_t need = balanced_bytes(num_seqs, num_heads, head_dim_v, num_ranges);
   PA_REQUIRE(need > 0 && workspace != nullptr && workspace_bytes >= need, PA_ERR_WORKSPACE,
              "workspace of %zu bytes needed for %d ranges (got %zu)", need, num_ranges,
              workspace_bytes);
   if (num_seqs == 0) return ok();
   PA_REQUIRE(out != nullptr, PA_ERR_INVALID, "out must be non-null");
   pa::BalancedMerge m{balanced_cu(workspace), balanced_part(workspace, num_seqs), num_seqs,
-                      num_q_heads, num_ranges, out, lse};
+                      num_heads, head_dim_v, num_ranges, out, lse};
   hipError_t e = pa::launch_balanced_merge(m, stream);
   if (e != hipSuccess) return hip_fail(e, "balanced merge launch");
   return ok();
@@ -423,21 +425,12 @@ pa_status_t pa_prefill_varlen(pa_dtype_t dtype,
 }
 
 // ---------------------------------------------------------------------------
-pa_status_t pa_mla_decode(const void* q_nope, int64_t qn_stride_b, int64_t qn_stride_h,
-                          const void* q_pe, int64_t qp_stride_b, int64_t qp_stride_h,
-                          const void* kv_c, const void* k_pe,
-                          void* kv_cache, int64_t num_blocks, int block_size,
-                          const int32_t* block_table, int max_blocks_per_seq,
-                          const int64_t* slot_mapping,
-                          const int32_t* seq_lens, int num_seqs, int max_seq_len,
-                          int num_heads, int kv_lora_rank, int rope_dim,
-                          float scale, int num_splits,
-                          void* workspace, size_t workspace_bytes,
-                          void* out, float* lse, hipStream_t stream) {
+namespace {
+
+pa_status_t check_mla_q(int64_t qn_stride_b, int64_t qn_stride_h, int64_t qp_stride_b,
+                        int64_t qp_stride_h, int num_heads, int kv_lora_rank, int rope_dim,
+                        float scale) {
   PA_REQUIRE(scale_ok(scale), PA_ERR_INVALID, "scale must be finite and >= 0");
-  pa_status_t st = check_common_cache(num_blocks, block_size, block_table, max_blocks_per_seq,
-                                      seq_lens, num_seqs, max_seq_len);
-  if (st != PA_OK) return st;
   PA_REQUIRE(kv_lora_rank > 0 && rope_dim > 0, PA_ERR_INVALID, "kv_lora_rank and rope_dim must be > 0");
   PA_REQUIRE(kv_lora_rank == 512 && rope_dim == 64, PA_ERR_UNSUPPORTED,
              "MLA decode supports kv_lora_rank 512 + rope_dim 64 (got %d + %d)", kv_lora_rank, rope_dim);
@@ -449,6 +442,59 @@ pa_status_t pa_mla_decode(const void* q_nope, int64_t qn_stride_b, int64_t qn_st
              PA_ERR_INVALID, "q strides do not describe [num_seqs, num_heads, dim] rows");
   PA_REQUIRE(qn_stride_h % 8 == 0 && qp_stride_h % 8 == 0 && qn_stride_b % 8 == 0 &&
              qp_stride_b % 8 == 0, PA_ERR_INVALID, "q strides must be multiples of 8 elements");
+  return PA_OK;
+}
+
+}  // namespace
+
+pa_status_t pa_mla_decode_balanced(const void* q_nope, int64_t qn_stride_b, int64_t qn_stride_h,
+                                   const void* q_pe, int64_t qp_stride_b, int64_t qp_stride_h,
+                                   const void* kv_cache, int64_t num_blocks, int block_size,
+                                   const int32_t* block_table, int max_blocks_per_seq,
+                                   const int32_t* seq_lens, int num_seqs, int num_heads,
+                                   int kv_lora_rank, int rope_dim, float scale, int num_ranges,
+                                   void* workspace, size_t workspace_bytes, void* out,
+                                   float* lse, hipStream_t stream) {
+  pa_status_t st = check_common_cache(num_blocks, block_size, block_table, max_blocks_per_seq,
+                                      seq_lens, num_seqs, 0);
+  if (st != PA_OK) return st;
+  st = check_mla_q(qn_stride_b, qn_stride_h, qp_stride_b, qp_stride_h, num_heads, kv_lora_rank,
+                   rope_dim, scale);
+  if (st != PA_OK) return st;
+  st = check_balanced(num_seqs, num_heads, kv_lora_rank, max_blocks_per_seq, block_size,
+                      num_ranges, workspace, workspace_bytes);
+  if (st != PA_OK) return st;
+  if (num_seqs == 0) return ok();
+  PA_REQUIRE(q_nope && q_pe && kv_cache && out, PA_ERR_INVALID,
+             "q_nope, q_pe, kv_cache and out must be non-null");
+  pa::MlaDecode d{q_nope, qn_stride_b, qn_stride_h, q_pe, qp_stride_b, qp_stride_h,
+                  kv_cache, num_blocks, block_size, block_table, max_blocks_per_seq,
+                  seq_lens, num_seqs, num_heads, kv_lora_rank, rope_dim, scale,
+                  1, 0, 0, balanced_part(workspace, num_seqs), out, lse,
+                  num_ranges, balanced_cu(workspace)};
+  hipError_t e = pa::launch_mla_decode(d, stream);
+  if (e == hipErrorNotSupported) return fail(PA_ERR_UNSUPPORTED, "MLA kernel not built");
+  if (e != hipSuccess) return hip_fail(e, "balanced MLA decode launch");
+  return ok();
+}
+
+pa_status_t pa_mla_decode(const void* q_nope, int64_t qn_stride_b, int64_t qn_stride_h,
+                          const void* q_pe, int64_t qp_stride_b, int64_t qp_stride_h,
+                          const void* kv_c, const void* k_pe,
+                          void* kv_cache, int64_t num_blocks, int block_size,
+                          const int32_t* block_table, int max_blocks_per_seq,
+                          const int64_t* slot_mapping,
+                          const int32_t* seq_lens, int num_seqs, int max_seq_len,
+                          int num_heads, int kv_lora_rank, int rope_dim,
+                          float scale, int num_splits,
+                          void* workspace, size_t workspace_bytes,
+                          void* out, float* lse, hipStream_t stream) {
+  pa_status_t st = check_common_cache(num_blocks, block_size, block_table, max_blocks_per_seq,
+                                      seq_lens, num_seqs, max_seq_len);
+  if (st != PA_OK) return st;
+  st = check_mla_q(qn_stride_b, qn_stride_h, qp_stride_b, qp_stride_h, num_heads, kv_lora_rank,
+                   rope_dim, scale);
+  if (st != PA_OK) return st;
   PA_REQUIRE(num_splits >= 0, PA_ERR_INVALID, "num_splits must be >= 0");
   PA_REQUIRE((kv_c == nullptr) == (k_pe == nullptr), PA_ERR_INVALID,
              "kv_c and k_pe must both be given or both NULL");
@@ -459,15 +505,23 @@ pa_status_t pa_mla_decode(const void* q_nope, int64_t qn_stride_b, int64_t qn_st
   PA_REQUIRE(out != nullptr || lse == nullptr, PA_ERR_INVALID,
              "lse without out: the partial-only mode (out = NULL) returns no lse");
   int n = num_splits;
+  int cus = 0;
   if (n == 0) {
-    const int cus = pa_device_num_cus();
+    cus = pa_device_num_cus();
     if (cus <= 0) return fail(PA_ERR_HIP, "cannot query the device's compute units");
     n = pa_mla_num_kv_splits(num_seqs, max_seq_len, cus);
   }
   const int P = split_tokens_for(max_seq_len, n, block_size);
   const bool stage1 = (out == nullptr);
   const bool direct = !stage1 && used_splits(max_seq_len, P) == 1;
-  if (!direct) {
+  // automatic schedule with more than one split: token-balanced ranges, one
+  // work-group per compute unit
+  const bool balanced = num_splits == 0 && !stage1 && !direct;
+  if (balanced) {
+    st = check_balanced(num_seqs, num_heads, kv_lora_rank, max_blocks_per_seq, block_size, cus,
+                        workspace, workspace_bytes);
+    if (st != PA_OK) return st;
+  } else if (!direct) {
     const size_t need = pa_decode_workspace_bytes(num_seqs, num_heads, kv_lora_rank, n);
     PA_REQUIRE(workspace != nullptr && workspace_bytes >= need, PA_ERR_WORKSPACE,
                "workspace of %zu bytes needed for %d splits (got %zu)", need, n, workspace_bytes);
@@ -478,10 +532,19 @@ pa_status_t pa_mla_decode(const void* q_nope, int64_t qn_stride_b, int64_t qn_st
     hipError_t e = pa::launch_cache_write_mla(w, stream);
     if (e != hipSuccess) return hip_fail(e, "cache_write_mla launch");
   }
+  if (balanced) {
+    st = pa_mla_decode_balanced(q_nope, qn_stride_b, qn_stride_h, q_pe, qp_stride_b, qp_stride_h,
+                                kv_cache, num_blocks, block_size, block_table, max_blocks_per_seq,
+                                seq_lens, num_seqs, num_heads, kv_lora_rank, rope_dim, scale, cus,
+                                workspace, workspace_bytes, out, lse, stream);
+    if (st != PA_OK) return st;
+    return pa_decode_balanced_merge(workspace, workspace_bytes, num_seqs, num_heads, kv_lora_rank,
+                                    cus, out, lse, stream);
+  }
   pa::MlaDecode d{q_nope, qn_stride_b, qn_stride_h, q_pe, qp_stride_b, qp_stride_h,
                   kv_cache, num_blocks, block_size, block_table, max_blocks_per_seq,
                   seq_lens, num_seqs, num_heads, kv_lora_rank, rope_dim, scale,
-                  direct ? 1 : n, P, direct, static_cast<float*>(workspace), out, lse};
+                  direct ? 1 : n, P, direct, static_cast<float*>(workspace), out, lse, 0, nullptr};
   hipError_t e = pa::launch_mla_decode(d, stream);
   if (e == hipErrorNotSupported) return fail(PA_ERR_UNSUPPORTED, "MLA kernel not built");
   if (e != hipSuccess) return hip_fail(e, "MLA decode launch");

@@ -3,21 +3,10 @@
 // Split-KV decode ("第 1 章 注意力后端", §3.1) cuts every request into
 // fixed-length splits; with a batch of mixed lengths the number of splits
 // rarely divides evenly over the chip, and the last wave of work-groups runs
-// a nearly empty machine.  This schedule instead concatenates the 32-token
-// chunks of all requests into one list and gives each of `nr` work-groups an
-// equal share [c0, c1) of it (range j holds chunks [j T / nr, (j+1) T / nr),
-// T = total chunks; nr <= T so no range is empty).  A range may start and end
-// inside a request and may cover several short requests; for every request it
-// touches it produces one LSE partial ("segment"), and a request that lies
-// wholly inside one range is written to the output directly.  The merge
-// kernel then combines the segments of the requests that cross ranges.
-//
-// Segment slots: the segments of range j are (j, r) for the requests r it
-// touches.  Walking the concatenated list, each new segment advances j or r
-// (or both), so j + r is a unique slot number in [0, nr + B - 1).
-//
-// Range of a chunk c: the largest j with j T / nr <= c (integer division),
-// i.e. j(c) = ((c + 1) nr - 1) / T.  (j T / nr <= c  <=>  j T < (c + 1) nr.)
+// a nearly empty machine.  Here the 32-token chunks of all requests form one
+// list cut into equal ranges (balanced.hpp); a range finishes the requests
+// that lie wholly inside it and leaves an LSE partial for the others, which
+// the merge kernel combines.
 //
 // Work-group: one wave per KV head (up to 8) of one range; the waves walk the
 // same chunks, so together they read whole 2 KiB token rows of a page.
@@ -28,6 +17,7 @@
 // padded LDS tile; the registers of chunk c+1 are refilled as soon as chunk
 // c's values are in the tile, so one chunk of loads is in flight while the
 // previous one is computed.
+#include "balanced.hpp"
 #include "launch.hpp"
 #include "pa_device.hpp"
 
@@ -35,40 +25,10 @@ namespace pa {
 namespace {
 
 constexpr int kD = 128;
-constexpr int kChunk = 32;              // tokens per chunk (one MFMA k-extent)
+constexpr int kChunk = kChunkTokens;    // tokens per chunk (one MFMA k-extent)
 constexpr int kRow = kD * 2 + 16;       // LDS row of a token: 256 B + 16 B pad
 constexpr int kTile = kChunk * kRow;    // per-wave tile (K, then V)
 constexpr int kHeads = 8;               // KV heads (waves) per work-group
-constexpr int kPartRow = 132;           // fp32 per segment row: 128 values, lse at [128]
-
-__device__ __forceinline__ int clamp_len(int s, int cap) { return s < 0 ? 0 : (s > cap ? cap : s); }
-__device__ __forceinline__ int chunks_of(int len) { return (len + kChunk - 1) / kChunk; }
-
-// A chunk of the concatenated list: request r, its chunk lc, the request's
-// (clamped) length and the list index of its first chunk.
-struct Pos {
-  int r, lc, len, base;
-};
-
-// The chunk after p.  The caller guarantees that one exists (some later
-// request has keys), so the scan over empty requests stops inside the batch.
-__device__ __forceinline__ Pos next_pos(Pos p, const int32_t* seq_lens, int cap, int B) {
-  if ((p.lc + 1) * kChunk < p.len) {
-    ++p.lc;
-    return p;
-  }
-  p.base += chunks_of(p.len);
-  int r = min(p.r + 1, B - 1);
-  int len = clamp_len(uniform_load(seq_lens + r), cap);
-  while (len == 0 && r + 1 < B) {
-    ++r;
-    len = clamp_len(uniform_load(seq_lens + r), cap);
-  }
-  p.r = r;
-  p.lc = 0;
-  p.len = len;
-  return p;
-}
 
 template <int G>
 __global__ __launch_bounds__(64 * kHeads, 1) void decode_balanced_kernel(DecodeBalanced a) {
@@ -87,56 +47,11 @@ __global__ __launch_bounds__(64 * kHeads, 1) void decode_balanced_kernel(DecodeB
   const int hg = blockIdx.x % n_hg;
   const int j = blockIdx.x / n_hg;
 
-  // Chunk counts of all requests and their exclusive prefix sums.  Every
-  // work-group computes them (B is small next to the KV stream); range 0 of
-  // head group 0 also stores them for the merge.
-  const int per = (B + nthr - 1) / nthr;
-  const int rb = min(B, tid * per);
-  const int re = min(B, rb + per);
-  int local = 0;
-  for (int r = rb; r < re; ++r) local += chunks_of(clamp_len(a.seq_lens[r], cap));
-  int incl = local;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int t = __shfl_up(incl, o, 64);
-    if (lane >= o) incl += t;
-  }
-  if (lane == 63) s_wave_sum[wave] = incl;
-  __syncthreads();
-  int before = 0, total = 0;
-  for (int w = 0; w < nthr / 64; ++w) {
-    const int t = s_wave_sum[w];
-    before += w < wave ? t : 0;
-    total += t;
-  }
-  const int excl = before + incl - local;
-  if (j == 0 && hg == 0) {
-    int run = excl;
-    for (int r = rb; r < re; ++r) {
-      a.cu[r] = run;
-      run += chunks_of(clamp_len(a.seq_lens[r], cap));
-    }
-    if (tid == 0) a.cu[B] = total;
-  }
-
-  // This work-group's range [c0, c1) and the request holding chunk c0.
-  const int nr = min(a.num_ranges, total);
-  if (j >= nr) return;   // the same for every thread of the work-group
-  const int c0 = int(int64_t(j) * total / nr);
-  const int c1 = int(int64_t(j + 1) * total / nr);
-  if (c0 >= excl && c0 < excl + local) {
-    int run = excl;
-    for (int r = rb; r < re; ++r) {
-      const int n = chunks_of(clamp_len(a.seq_lens[r], cap));
-      if (c0 < run + n) {
-        s_start[0] = r;
-        s_start[1] = run;
-        break;
-      }
-      run += n;
-    }
-  }
-  __syncthreads();
+  int c0, c1;
+  ChunkPos cur;
+  if (!balanced_range(a.seq_lens, B, cap, a.num_ranges, j, j == 0 && hg == 0, a.cu, s_wave_sum,
+                      s_start, c0, c1, cur))
+    return;
   const int h = hg * kHeads + wave;
   if (h >= Hkv) return;   // no barrier below
 
@@ -166,7 +81,7 @@ __global__ __launch_bounds__(64 * kHeads, 1) void decode_balanced_kernel(DecodeB
   // tokens 4 i + kq of each 16-token half, lane li its 16-byte chunk li.
   // Tokens past the request's end re-read its last token (finite data,
   // masked below); the loads are unconditional so the waits stay exact.
-  auto load_half = [&](const Pos& p, int64_t plane, u32x4_t (&dst)[8]) {
+  auto load_half = [&](const ChunkPos& p, int64_t plane, u32x4_t (&dst)[8]) {
     const int32_t* table = a.block_table + int64_t(p.r) * a.max_blocks;
     const int len = max(p.len, 1);   // positions always hold keys; keeps every index >= 0
     const int last16 = ((len - 1) / 16) * 16;
@@ -185,12 +100,7 @@ __global__ __launch_bounds__(64 * kHeads, 1) void decode_balanced_kernel(DecodeB
     }
   };
 
-  Pos cur;
-  cur.r = __builtin_amdgcn_readfirstlane(s_start[0]);
-  cur.base = __builtin_amdgcn_readfirstlane(s_start[1]);
-  cur.len = clamp_len(uniform_load(a.seq_lens + cur.r), cap);
-  cur.lc = c0 - cur.base;
-  Pos nxt = c0 + 1 < c1 ? next_pos(cur, a.seq_lens, cap, B) : cur;
+  ChunkPos nxt = c0 + 1 < c1 ? next_chunk(cur, a.seq_lens, cap, B) : cur;
 
   u32x4_t qf[4];
   load_q(cur.r, qf);
@@ -288,7 +198,7 @@ __global__ __launch_bounds__(64 * kHeads, 1) void decode_balanced_kernel(DecodeB
           }
           if (kq == 0 && a.lse) a.lse[row] = lse_nat;
         } else {
-          float* pp = a.part + (int64_t(j + cur.r) * Hq + hrow) * kPartRow;
+          float* pp = a.part + (int64_t(j + cur.r) * Hq + hrow) * (kD + 4);
 #pragma unroll
           for (int dt = 0; dt < 8; ++dt)
             *reinterpret_cast<f32x4_t*>(pp + 16 * dt + 4 * kq) = acc[dt] * inv;
@@ -301,47 +211,49 @@ __global__ __launch_bounds__(64 * kHeads, 1) void decode_balanced_kernel(DecodeB
       l_run = 0.0f;
     }
     cur = nxt;
-    if (c + 2 < c1) nxt = next_pos(nxt, a.seq_lens, cap, B);
+    if (c + 2 < c1) nxt = next_chunk(nxt, a.seq_lens, cap, B);
   }
 }
 
 // Combine the segments of requests that cross ranges.  One work-group per
-// (request, query head): 8 groups of 32 threads (4 dims each) take every 8th
-// segment and keep a running (max, sum, output) each; the 8 states are then
-// merged through LDS.  A long request's segments are thus read 8 at a time.
-constexpr int kMergeGroups = 8;
-
+// (request, query head): DV / 4 threads (4 dims each) cover a row; the
+// 1024 / DV groups of them take every k-th segment and keep a running
+// (max, sum, output) each, merged through LDS at the end.
+template <int DV>
 __global__ __launch_bounds__(256) void balanced_merge_kernel(BalancedMerge a) {
-  __shared__ float s_m[kMergeGroups], s_l[kMergeGroups];
-  __shared__ __align__(16) float s_o[kMergeGroups][kD];
+  constexpr int kGroupThreads = DV / 4;
+  constexpr int kGroups = 256 / kGroupThreads;
+  constexpr int kRowF = DV + 4;               // fp32 per segment row, lse at DV
+  __shared__ float s_m[kGroups], s_l[kGroups];
+  __shared__ __align__(16) float s_o[kGroups][DV];
   const int Hq = a.num_q_heads;
   const int r = blockIdx.x / Hq;
   const int hq = blockIdx.x % Hq;
-  const int g = threadIdx.x >> 5;
-  const int d = 4 * (threadIdx.x & 31);
+  const int g = threadIdx.x / kGroupThreads;
+  const int d = 4 * (threadIdx.x % kGroupThreads);
   const int B = a.num_seqs;
   const int total = a.cu[B];
   const int cb = a.cu[r];
   const int ce = a.cu[r + 1];
   const int64_t row = int64_t(r) * Hq + hq;
-  uint2* op = reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + row * kD + d);
+  uint2* op = reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + row * DV + d);
   if (cb == ce) {   // no keys: out 0, lse -inf
     if (g == 0) *op = uint2{0u, 0u};
     if (a.lse && threadIdx.x == 0) a.lse[row] = -INFINITY;
     return;
   }
   const int nr = min(a.num_ranges, total);
-  const int j0 = int(((int64_t(cb) + 1) * nr - 1) / total);
-  const int j1 = int((int64_t(ce) * nr - 1) / total);
+  const int j0 = range_of_chunk(cb, nr, total);
+  const int j1 = range_of_chunk(ce - 1, nr, total);
   if (j0 == j1) return;   // written by its range
-  const int64_t step = int64_t(Hq) * kPartRow;
-  const float* p0 = a.part + (int64_t(j0 + r) * Hq + hq) * kPartRow;
+  const int64_t step = int64_t(Hq) * kRowF;
+  const float* p0 = a.part + (int64_t(j0 + r) * Hq + hq) * kRowF;
   float m = -INFINITY, l = 0.0f;
   f32x4_t o = f32x4_t{0, 0, 0, 0};
 #pragma unroll 4
-  for (int jj = g; jj <= j1 - j0; jj += kMergeGroups) {
+  for (int jj = g; jj <= j1 - j0; jj += kGroups) {
     const float* pp = p0 + jj * step;
-    const float lj = pp[kD];
+    const float lj = pp[DV];
     const f32x4_t oj = *reinterpret_cast<const f32x4_t*>(pp + d);
     const float mn = fmaxf(m, lj);
     const float c = fast_exp2((m - mn) * kLog2e);   // 0 while m = -inf
@@ -350,7 +262,7 @@ __global__ __launch_bounds__(256) void balanced_merge_kernel(BalancedMerge a) {
     o = o * c + w * oj;
     m = mn;
   }
-  if ((threadIdx.x & 31) == 0) {
+  if (threadIdx.x % kGroupThreads == 0) {
     s_m[g] = m;
     s_l[g] = l;
   }
@@ -359,11 +271,11 @@ __global__ __launch_bounds__(256) void balanced_merge_kernel(BalancedMerge a) {
   if (g != 0) return;
   float mm = s_m[0];
 #pragma unroll
-  for (int k = 1; k < kMergeGroups; ++k) mm = fmaxf(mm, s_m[k]);
+  for (int k = 1; k < kGroups; ++k) mm = fmaxf(mm, s_m[k]);
   float den = 0.0f;
   f32x4_t acc = f32x4_t{0, 0, 0, 0};
 #pragma unroll
-  for (int k = 0; k < kMergeGroups; ++k) {
+  for (int k = 0; k < kGroups; ++k) {
     const float w = fast_exp2((s_m[k] - mm) * kLog2e);   // 0 for a group without segments
     den = fmaf(s_l[k], w, den);
     acc += w * *reinterpret_cast<const f32x4_t*>(&s_o[k][d]);
@@ -385,7 +297,6 @@ int balanced_num_ranges(int num_kv_heads, int num_cus) {
 }
 
 size_t balanced_cu_bytes(int num_seqs) { return (size_t(num_seqs + 1) * 4 + 255) / 256 * 256; }
-size_t balanced_part_row_floats() { return kPartRow; }
 
 hipError_t launch_decode_balanced(const DecodeBalanced& a, hipStream_t s) {
   const int G = a.num_q_heads / a.num_kv_heads;
@@ -404,7 +315,12 @@ hipError_t launch_decode_balanced(const DecodeBalanced& a, hipStream_t s) {
 
 hipError_t launch_balanced_merge(const BalancedMerge& a, hipStream_t s) {
   const dim3 grid{unsigned(int64_t(a.num_seqs) * a.num_q_heads)}, block{256};
-  hipLaunchKernelGGL(balanced_merge_kernel, grid, block, 0, s, a);
+  if (a.head_dim == 128)
+    hipLaunchKernelGGL((balanced_merge_kernel<128>), grid, block, 0, s, a);
+  else if (a.head_dim == 512)
+    hipLaunchKernelGGL((balanced_merge_kernel<512>), grid, block, 0, s, a);
+  else
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

@@ -53,9 +53,10 @@ hipError_t launch_lse_merge(const LseMerge& a, hipStream_t s);
 
 // Token-balanced decode (bf16, head_dim 128): range j of num_ranges covers
 // chunks [j T / nr, (j+1) T / nr) of the concatenated 32-token chunk list,
-// nr = min(num_ranges, T).  Requests inside one range go to out/lse; the
-// others leave one segment per range in part[(j + r) * Hq + head][132]
-// (values 0..127, lse at 128).  cu[B + 1] receives the chunk prefix sums.
+// nr = min(num_ranges, T) (balanced.hpp).  Requests inside one range go to
+// out/lse; the others leave one segment per range in
+// part[(j + r) * Hq + head][Dv + 4] (values 0..Dv-1, lse at Dv).  cu[B + 1]
+// receives the chunk prefix sums.
 struct DecodeBalanced {
   const void* q; const void* cache;
   int64_t num_blocks; int block_size;
@@ -71,16 +72,18 @@ hipError_t launch_decode_balanced(const DecodeBalanced& a, hipStream_t s);
 
 struct BalancedMerge {
   const int32_t* cu; const float* part;
-  int num_seqs; int num_q_heads; int num_ranges;
+  int num_seqs; int num_q_heads; int head_dim; int num_ranges;   // head_dim 128 or 512
   void* out; float* lse;
 };
 hipError_t launch_balanced_merge(const BalancedMerge& a, hipStream_t s);
 
 int balanced_num_ranges(int num_kv_heads, int num_cus);   // ranges for 8 waves per CU
 size_t balanced_cu_bytes(int num_seqs);                    // cu[] size, 256-B aligned
-size_t balanced_part_row_floats();                         // 132
 
 // ------------------------------------------------------------------- MLA
+// MLA decode.  num_ranges = 0: per-request splits (num_splits, split_tokens,
+// direct; partials [B, H, S, 513]).  num_ranges > 0: token-balanced ranges
+// (balanced.hpp; segment rows [(nr + B) H, 516], prefix sums in cu).
 struct MlaDecode {
   const void* q_nope; int64_t qn_sb, qn_sh;
   const void* q_pe; int64_t qp_sb, qp_sh;
@@ -91,6 +94,7 @@ struct MlaDecode {
   float scale;
   int num_splits; int split_tokens; int direct;
   float* part; void* out; float* lse;
+  int num_ranges; int32_t* cu;
 };
 hipError_t launch_mla_decode(const MlaDecode& a, hipStream_t s);
 

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <utility>
+
 namespace pa {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
@@ -111,6 +113,66 @@ __device__ __forceinline__ uint2 lds_read_tr(const char* p) {
   typedef __attribute__((address_space(3))) s16x4_t lds_s4;
   const s16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(p));
   return __builtin_bit_cast(uint2, v);
+}
+
+// Transposed LDS read issued as inline assembly, for tiles that are filled by
+// global_load_lds: the compiler cannot tell that the read does not alias the
+// tile still being filled and would wait for every outstanding load before the
+// intrinsic form.  The result is NOT ready when this returns: it must pass
+// through lds_wait() (which ties the registers to an s_waitcnt) before use.
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2_t;
+template <int kOffset>
+__device__ __forceinline__ u32x2_t lds_read_tr_issue(const char* p) {
+  u32x2_t v;
+  typedef const __attribute__((address_space(3))) char lds_char;
+  const uint32_t addr = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_char*)(p)));
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "n"(kOffset));
+  return v;
+}
+// 16-byte LDS read issued as inline assembly (same contract as
+// lds_read_tr_issue: pass the result through lds_wait() before use).
+template <int kOffset>
+__device__ __forceinline__ u32x4_t lds_read16_issue(const char* p) {
+  u32x4_t v;
+  typedef const __attribute__((address_space(3))) char lds_char;
+  const uint32_t addr = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_char*)(p)));
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "n"(kOffset));
+  return v;
+}
+
+// Wait until at most kLeft LDS (and scalar-memory) operations are outstanding;
+// the listed registers are only read after the wait.  LDS operations complete
+// in order, so the reads issued before the last kLeft ones have landed.
+template <int kLeft>
+__device__ __forceinline__ void lds_wait(u32x2_t& a, u32x2_t& b, u32x2_t& c, u32x2_t& d) {
+  asm volatile("s_waitcnt lgkmcnt(%4)" : "+v"(a), "+v"(b), "+v"(c), "+v"(d) : "n"(kLeft));
+}
+template <int kLeft>
+__device__ __forceinline__ void lds_wait(u32x2_t& a, u32x2_t& b, u32x2_t& c, u32x2_t& d,
+                                         u32x2_t& e, u32x2_t& f, u32x2_t& g, u32x2_t& h) {
+  asm volatile("s_waitcnt lgkmcnt(%8)"
+               : "+v"(a), "+v"(b), "+v"(c), "+v"(d), "+v"(e), "+v"(f), "+v"(g), "+v"(h)
+               : "n"(kLeft));
+}
+
+template <int kLeft>
+__device__ __forceinline__ void lds_wait(u32x2_t& a, u32x2_t& b) {
+  asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(a), "+v"(b) : "n"(kLeft));
+}
+template <int kLeft>
+__device__ __forceinline__ void lds_wait(u32x4_t& a, u32x4_t& b) {
+  asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(a), "+v"(b) : "n"(kLeft));
+}
+
+// Calls f(std::integral_constant<int, I>) for I = 0..N-1, so that the index
+// can be a template argument (an immediate offset) in the body.
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
 // ------------------------------------------------------------ 16-B access

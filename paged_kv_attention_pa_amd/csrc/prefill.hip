@@ -150,22 +150,36 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillVarlen a) {
     const char* vt = kt + kTileBytes;
     const int key0 = t * kBN;
 
-    // S^T for two 32-key halves
+    // S^T for two 32-key halves (two independent accumulation chains).  Chunk
+    // 2 kk + (l / 32) of row 32 hh + l % 32 sits in slot (2 kk + l / 32) ^
+    // swz(l % 32); the second half is a constant 32 rows further.  The LDS
+    // reads run one k-step ahead of the MFMAs.
     f32x16_t s[2];
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
+    for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
       for (int i = 0; i < 16; ++i) s[hh][i] = 0.0f;
-      // chunk 2 kk + (l / 32) of row 32 hh + l % 32 sits in slot
-      // (2 kk + l / 32) ^ swz(l % 32): one per-lane address per kk (the row
-      // offset of the second half is a constant)
-      const char* krow = kt + (hh * 32 + (lane & 31)) * kRowBytes;
-#pragma unroll
-      for (int kk = 0; kk < 8; ++kk) {
-        const u32x4_t kf = *reinterpret_cast<const u32x4_t*>(
-            krow + 16 * ((2 * kk + (lane >> 5)) ^ swz(lane & 31)));
-        s[hh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kf), as_bf16x8(qf[kk]), s[hh], 0, 0, 0);
-      }
+    {
+      const char* krow = kt + (lane & 31) * kRowBytes;
+      u32x4_t kr[2][2];
+      auto issue = [&](auto kc) {
+        constexpr int kk = decltype(kc)::value;
+        const char* p = krow + 16 * ((2 * kk + (lane >> 5)) ^ swz(lane & 31));
+        kr[kk & 1][0] = lds_read16_issue<0>(p);
+        kr[kk & 1][1] = lds_read16_issue<32 * kRowBytes>(p);
+      };
+      issue(std::integral_constant<int, 0>{});
+      static_for<8>([&](auto kc) {
+        constexpr int kk = decltype(kc)::value;
+        if constexpr (kk + 1 < 8) {
+          issue(std::integral_constant<int, kk + 1>{});
+          lds_wait<2>(kr[kk & 1][0], kr[kk & 1][1]);
+        } else {
+          lds_wait<0>(kr[kk & 1][0], kr[kk & 1][1]);
+        }
+        s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kr[kk & 1][0]), as_bf16x8(qf[kk]), s[0], 0, 0, 0);
+        s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kr[kk & 1][1]), as_bf16x8(qf[kk]), s[1], 0, 0, 0);
+      });
     }
 
     // Online softmax update for this tile.  Diagonal and tail tiles (wave-
@@ -244,23 +258,34 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillVarlen a) {
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt)
         vb[e][dt] = vt + (vr0 + 8 * e) * kRowBytes + 16 * ((4 * dt + c0) ^ swz(vr0 + 8 * e)) + 8 * (gi & 1);
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt) {
-        const uint2 v1 = lds_read_tr(vb[0][dt] + 16 * ks * kRowBytes);
-        const uint2 v2 = lds_read_tr(vb[1][dt] + 16 * ks * kRowBytes);
-        const u32x4_t vf = u32x4_t{v1.x, v1.y, v2.x, v2.y};
-        acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vf), as_bf16x8(pf[ks]), acc[dt], 0, 0, 0);
+    // (ks, dt) steps in order, the two reads of a step issued one step ahead
+    u32x2_t vr[2][2];
+    auto vissue = [&](auto ic) {
+      constexpr int i = decltype(ic)::value, ks = i / 4, dt = i % 4;
+      vr[i & 1][0] = lds_read_tr_issue<16 * ks * kRowBytes>(vb[0][dt]);
+      vr[i & 1][1] = lds_read_tr_issue<16 * ks * kRowBytes>(vb[1][dt]);
+    };
+    vissue(std::integral_constant<int, 0>{});
+    static_for<16>([&](auto ic) {
+      constexpr int i = decltype(ic)::value, ks = i / 4, dt = i % 4;
+      if constexpr (i + 1 < 16) {
+        vissue(std::integral_constant<int, i + 1>{});
+        lds_wait<2>(vr[i & 1][0], vr[i & 1][1]);
+      } else {
+        lds_wait<0>(vr[i & 1][0], vr[i & 1][1]);
       }
-    }
+      const u32x2_t v1 = vr[i & 1][0], v2 = vr[i & 1][1];
+      const u32x4_t vf = u32x4_t{v1.x, v1.y, v2.x, v2.y};
+      acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vf), as_bf16x8(pf[ks]), acc[dt], 0, 0, 0);
+    });
 
     if (t + 1 < n_tiles) {
       // this wave's loads of tile t + 1 have landed; after the barrier every
-      // wave's have, and every wave is done reading buffer buf, which the
-      // loads issued at the start of iteration t + 1 refill
+      // wave's have, and every wave is done reading buffer buf (its LDS reads
+      // were waited for), which the loads issued at the start of iteration
+      // t + 1 refill.  A bare barrier: the tiles' only writer is the DMA.
       gwait();
-      __syncthreads();
+      __builtin_amdgcn_s_barrier();
     }
   }
 

@@ -107,3 +107,98 @@ def test_mla_two_stage_matches_one_call():
     assert part.shape == (3, 32, 4, 513)
     assert np.array_equal(to_f64(out2), out1)
     assert np.array_equal(lse2.cpu().numpy().astype(np.float64), lse1)
+
+
+# ------------------------------------------------- token-balanced schedule
+def _run_balanced(b: W.MlaBatch, num_ranges, merge=True, seq_lens=None):
+    sl = b.seq_lens if seq_lens is None else seq_lens
+    cache = O.cache_write_mla(b.cache, b.kv_c_new, b.k_pe_new, b.slot_mapping)
+    out, lse, ws, nr = pa.mla_decode_balanced(to_dev(b.q_nope), to_dev(b.q_pe), to_dev(cache),
+                                              to_dev(b.block_table),
+                                              to_dev(np.asarray(sl, dtype=np.int32)), b.scale,
+                                              num_ranges=num_ranges, merge=merge)
+    torch.cuda.synchronize()
+    return cache, out, lse, ws, nr
+
+
+@pytest.mark.parametrize("ci", range(len(CASES)), ids=[c[0] for c in CASES])
+@pytest.mark.parametrize("num_ranges", [1, 2, 5, 40, 100000])
+def test_mla_balanced_small(ci, num_ranges):
+    name, seq, H, bs = CASES[ci]
+    say(f"mla balanced {name} ranges={num_ranges}")
+    b = W.make_mla(300 + ci, seq, H, 512, 64, bs)
+    cache, out, lse, _, _ = _run_balanced(b, num_ranges)
+    oref, lref = O.mla_decode(b.q_nope, b.q_pe, cache, b.block_table, b.seq_lens, b.scale)
+    check_close(to_f64(out), oref, f"{name} out")
+    check_lse(lse.cpu().numpy().astype(np.float64), lref, f"{name} lse")
+
+
+@pytest.mark.parametrize("num_ranges", [3, 11])
+def test_mla_balanced_segments_against_oracle(num_ranges):
+    """Stage 1 alone: prefix sums exact, whole requests final, and every
+    segment partial equal to the oracle's attention over that range's keys."""
+    seq = [700, 33, 1, 2000, 64, 130]
+    say(f"mla balanced segments ranges={num_ranges}")
+    b = W.make_mla(14, seq, 32, 512, 64, 64)
+    B, H = b.num_seqs, b.num_heads
+    cache, out, lse, ws, nr_arg = _run_balanced(b, num_ranges, merge=False)
+    n = [-(-s // 32) for s in seq]
+    cu = np.concatenate([[0], np.cumsum(n)]).astype(np.int64)
+    T = int(cu[-1])
+    nr = min(num_ranges, T)
+    ranges = [(j * T // nr, (j + 1) * T // nr) for j in range(nr)]
+    wsn = ws.cpu().numpy()
+    assert np.array_equal(wsn.view(np.int32)[: B + 1], cu)
+    off = ((B + 1) * 4 + 255) // 256 * 256 // 4
+    part = wsn[off: off + (nr_arg + B) * H * 516].reshape(nr_arg + B, H, 516)
+    o1, l1 = to_f64(out), lse.cpu().numpy().astype(np.float64)
+    oref, lref = O.mla_decode(b.q_nope, b.q_pe, cache, b.block_table, b.seq_lens, b.scale)
+    n_split = 0
+    for r in range(B):
+        js = [j for j, (c0, c1) in enumerate(ranges) if c0 < cu[r + 1] and c1 > cu[r]]
+        if len(js) == 1:
+            check_close(o1[r], oref[r], f"direct request {r}")
+            check_lse(l1[r], lref[r], f"direct request {r}")
+            continue
+        n_split += 1
+        rows = O.gather_mla(cache, b.block_table[r], seq[r])
+        q = np.concatenate([O.to_f64(b.q_nope[r]), O.to_f64(b.q_pe[r])], axis=-1)[None]
+        for j in js:
+            c0, c1 = ranges[j]
+            lo = (max(c0, cu[r]) - cu[r]) * 32
+            hi = min((min(c1, cu[r + 1]) - cu[r]) * 32, seq[r])
+            po, pl = O.partial_attention(q, rows[:, None, :], rows[:, None, :512], b.scale, lo, hi,
+                                         None)
+            check_close(part[j + r, :, :512].astype(np.float64), po[0],
+                        f"request {r} range {j} partial")
+            check_lse(part[j + r, :, 512].astype(np.float64), pl[0], f"request {r} range {j} lse")
+    assert n_split > 0
+    pa.decode_balanced_merge(ws, B, H, 512, nr_arg, out, lse)
+    torch.cuda.synchronize()
+    check_close(to_f64(out), oref, "merged out")
+    check_lse(lse.cpu().numpy().astype(np.float64), lref, "merged lse")
+
+
+def test_mla_automatic_schedule_is_balanced():
+    say("mla balanced vs automatic pa_mla_decode")
+    b = W.make_mla(15, [1500, 64, 700, 3000], 64, 512, 64, 64)
+    cache_t, out1, lse1 = _run(b, num_splits=0)
+    out2, lse2, _, nr = pa.mla_decode_balanced(to_dev(b.q_nope), to_dev(b.q_pe), cache_t,
+                                               to_dev(b.block_table), to_dev(b.seq_lens), b.scale)
+    torch.cuda.synchronize()
+    assert nr == pa.device_num_cus()
+    assert np.array_equal(to_f64(out2), out1)
+    assert np.array_equal(lse2.cpu().numpy().astype(np.float64), lse1)
+
+
+def test_mla_balanced_requests_without_keys():
+    say("mla balanced empty requests")
+    b = W.make_mla(16, [300, 5, 900, 40], 16, 512, 64, 16)
+    seq = np.array([300, 0, 900, 0], dtype=np.int32)
+    for nr in (1, 4, 100):
+        cache, out, lse, _, _ = _run_balanced(b, nr, seq_lens=seq)
+        oref, lref = O.mla_decode(b.q_nope, b.q_pe, cache, b.block_table, seq, b.scale)
+        o, l = to_f64(out), lse.cpu().numpy().astype(np.float64)
+        assert np.all(o[[1, 3]] == 0) and np.all(np.isneginf(l[[1, 3]]))
+        check_close(o, oref, f"ranges={nr} out")
+        check_lse(l, lref, f"ranges={nr} lse")

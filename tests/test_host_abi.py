@@ -189,17 +189,18 @@ def test_balanced_helpers(lib):
     assert pa.decode_balanced_num_ranges(1, 256) == 2048
     assert pa.decode_balanced_num_ranges(16, 256) == 128
     assert pa.decode_balanced_num_ranges(8, 0) == 1
-    # cu[B + 1] rounded to 256 B, then (ranges + B) * Hq rows of 132 fp32
-    assert pa.decode_balanced_workspace_bytes(64, 32, 256) == 512 + (256 + 64) * 32 * 132 * 4
-    assert pa.decode_balanced_workspace_bytes(63, 32, 256) == 256 + (256 + 63) * 32 * 132 * 4
-    assert pa.decode_balanced_workspace_bytes(4, 64, 256) == 256 + 260 * 64 * 132 * 4
-    assert pa.decode_balanced_workspace_bytes(-1, 32, 256) == 0
-    assert pa.decode_balanced_workspace_bytes(4, 32, 0) == 0
+    # cu[B + 1] rounded to 256 B, then (ranges + B) * H rows of Dv + 4 fp32
+    assert pa.decode_balanced_workspace_bytes(64, 32, 128, 256) == 512 + (256 + 64) * 32 * 132 * 4
+    assert pa.decode_balanced_workspace_bytes(63, 32, 128, 256) == 256 + (256 + 63) * 32 * 132 * 4
+    assert pa.decode_balanced_workspace_bytes(4, 64, 128, 256) == 256 + 260 * 64 * 132 * 4
+    assert pa.decode_balanced_workspace_bytes(128, 128, 512, 256) == 768 + 384 * 128 * 516 * 4
+    assert pa.decode_balanced_workspace_bytes(-1, 32, 128, 256) == 0
+    assert pa.decode_balanced_workspace_bytes(4, 32, 128, 0) == 0
 
 
 def test_balanced_validation(lib):
     f = lib.pa_decode_balanced
-    need = pa.decode_balanced_workspace_bytes(4, 32, 16)
+    need = pa.decode_balanced_workspace_bytes(4, 32, 128, 16)
     #        q  cache  nb  bs  table maxb seq B  hq  hkv d    scale nr  ws       wsb   out  lse
     base = [1, 2, 100, 16, 3, 64, 4, 4, 32, 8, 128, 0.1, 16, 1 << 20, need, 5, None, None]
 
@@ -222,6 +223,26 @@ def test_balanced_validation(lib):
     m = lib.pa_decode_balanced_merge
     assert m(1 << 20, need - 1, 4, 32, 128, 16, 5, None, None) == WORKSPACE
     assert m(1 << 20, need, 4, 32, 128, 0, 5, None, None) == INVALID
-    assert m(1 << 20, need, 4, 32, 64, 16, 5, None, None) == UNSUPPORTED
+    assert m(1 << 20, need, 4, 32, 64, 16, 5, None, None) == UNSUPPORTED   # head_dim_v 64
     assert m(1 << 20, need, 4, 32, 128, 16, None, None, None) == INVALID
     assert m(None, 0, 0, 32, 128, 16, None, None, None) == WORKSPACE
+
+
+def test_mla_balanced_validation(lib):
+    f = lib.pa_mla_decode_balanced
+    need = pa.decode_balanced_workspace_bytes(4, 128, 512, 16)
+    base = [1, 128 * 512, 512, 2, 128 * 64, 64, 3, 100, 64, 4, 200, 5, 4, 128, 512, 64, 0.07, 16,
+            1 << 20, need, 6, None, None]
+
+    def call(i, v):
+        a = list(base)
+        a[i] = v
+        return f(*a)
+
+    assert call(17, 0) == INVALID                     # no ranges
+    assert call(19, need - 1) == WORKSPACE            # workspace too small
+    assert call(14, 320) == UNSUPPORTED               # kv_lora_rank 320
+    assert call(13, 24) == UNSUPPORTED                # heads not a multiple of 16
+    assert call(2, 100) == INVALID                    # q_nope head stride < 512
+    assert call(20, None) == INVALID                  # no output
+    assert call(18, (1 << 20) + 8) == INVALID         # misaligned workspace
