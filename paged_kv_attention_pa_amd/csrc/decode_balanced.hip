@@ -285,6 +285,60 @@ __global__ __launch_bounds__(256) void balanced_merge_kernel(BalancedMerge a) {
   if (a.lse && threadIdx.x == 0) a.lse[row] = mm + fast_log2(den) * kLn2;
 }
 
+// The 512-wide (MLA) merge: requests cross few ranges but rows are long.
+// One work-group per (request, 8 heads): 32 threads per head, 16 dims each,
+// one running (max, sum, output) per thread over the request's segments.
+__global__ __launch_bounds__(256) void balanced_merge512_kernel(BalancedMerge a) {
+  constexpr int DV = 512, kRowF = DV + 4, kHeadsPerGroup = 8;
+  const int Hq = a.num_q_heads;
+  const int nhb = (Hq + kHeadsPerGroup - 1) / kHeadsPerGroup;
+  const int r = blockIdx.x / nhb;
+  const int hq = (blockIdx.x % nhb) * kHeadsPerGroup + (threadIdx.x >> 5);
+  if (hq >= Hq) return;
+  const int d = 16 * (threadIdx.x & 31);
+  const int B = a.num_seqs;
+  const int total = a.cu[B];
+  const int cb = a.cu[r];
+  const int ce = a.cu[r + 1];
+  const int64_t row = int64_t(r) * Hq + hq;
+  u32x4_t* op = reinterpret_cast<u32x4_t*>(static_cast<uint16_t*>(a.out) + row * DV + d);
+  if (cb == ce) {   // no keys: out 0, lse -inf
+    op[0] = u32x4_t{0, 0, 0, 0};
+    op[1] = u32x4_t{0, 0, 0, 0};
+    if (a.lse && (threadIdx.x & 31) == 0) a.lse[row] = -INFINITY;
+    return;
+  }
+  const int nr = min(a.num_ranges, total);
+  const int j0 = range_of_chunk(cb, nr, total);
+  const int j1 = range_of_chunk(ce - 1, nr, total);
+  if (j0 == j1) return;   // written by its range
+  const int64_t step = int64_t(Hq) * kRowF;
+  const float* p0 = a.part + (int64_t(j0 + r) * Hq + hq) * kRowF;
+  float m = -INFINITY, l = 0.0f;
+  f32x4_t o[4] = {f32x4_t{0, 0, 0, 0}, f32x4_t{0, 0, 0, 0}, f32x4_t{0, 0, 0, 0}, f32x4_t{0, 0, 0, 0}};
+#pragma unroll 2
+  for (int jj = 0; jj <= j1 - j0; ++jj) {
+    const float* pp = p0 + jj * step;
+    const float lj = pp[DV];
+    f32x4_t oj[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) oj[k] = *reinterpret_cast<const f32x4_t*>(pp + d + 4 * k);
+    const float mn = fmaxf(m, lj);
+    const float c = fast_exp2((m - mn) * kLog2e);   // 0 while m = -inf
+    const float w = fast_exp2((lj - mn) * kLog2e);
+    l = fmaf(l, c, w);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) o[k] = o[k] * c + w * oj[k];
+    m = mn;
+  }
+  const float inv = 1.0f / l;
+  op[0] = u32x4_t{pack_bf16x2(o[0][0] * inv, o[0][1] * inv), pack_bf16x2(o[0][2] * inv, o[0][3] * inv),
+                  pack_bf16x2(o[1][0] * inv, o[1][1] * inv), pack_bf16x2(o[1][2] * inv, o[1][3] * inv)};
+  op[1] = u32x4_t{pack_bf16x2(o[2][0] * inv, o[2][1] * inv), pack_bf16x2(o[2][2] * inv, o[2][3] * inv),
+                  pack_bf16x2(o[3][0] * inv, o[3][1] * inv), pack_bf16x2(o[3][2] * inv, o[3][3] * inv)};
+  if (a.lse && (threadIdx.x & 31) == 0) a.lse[row] = m + fast_log2(l) * kLn2;
+}
+
 }  // namespace
 
 int balanced_num_ranges(int num_kv_heads, int num_cus) {
@@ -314,13 +368,15 @@ hipError_t launch_decode_balanced(const DecodeBalanced& a, hipStream_t s) {
 }
 
 hipError_t launch_balanced_merge(const BalancedMerge& a, hipStream_t s) {
-  const dim3 grid{unsigned(int64_t(a.num_seqs) * a.num_q_heads)}, block{256};
-  if (a.head_dim == 128)
+  if (a.head_dim == 128) {
+    const dim3 grid{unsigned(int64_t(a.num_seqs) * a.num_q_heads)}, block{256};
     hipLaunchKernelGGL((balanced_merge_kernel<128>), grid, block, 0, s, a);
-  else if (a.head_dim == 512)
-    hipLaunchKernelGGL((balanced_merge_kernel<512>), grid, block, 0, s, a);
-  else
+  } else if (a.head_dim == 512) {
+    const dim3 grid{unsigned(int64_t(a.num_seqs) * ((a.num_q_heads + 7) / 8))}, block{256};
+    hipLaunchKernelGGL(balanced_merge512_kernel, grid, block, 0, s, a);
+  } else {
     return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
