@@ -192,6 +192,8 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillVarlen a) {
     const bool need_mask = (key0 + kBN > kv_end) || (a.causal && key0 + kBN - 1 > C + q0 + wave * 32);
     u32x4_t pf[4];
     float psum = 0.0f;
+    float alpha = 1.0f;
+    bool rescale = false;   // wave-uniform; the accumulator is scaled after the branch
     auto update = [&](auto masked_tag) {
       constexpr bool kMasked = decltype(masked_tag)::value;
       if constexpr (kMasked) {
@@ -213,13 +215,10 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillVarlen a) {
       const float tm = tmax == -INFINITY ? -INFINITY : tmax * scale2;
       if (__any(tm > m_run + kSlack)) {
         const float m_new = fmaxf(m_run, tm);
-        const float alpha = fast_exp2(m_run - m_new);
+        alpha = fast_exp2(m_run - m_new);
+        rescale = true;
         m_run = m_new;
         l_run *= alpha;
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) acc[dt][i] *= alpha;
       }
       // P^T in bf16, packed as the B operand: regs 8 st .. 8 st + 7 of half hh
 #pragma unroll
@@ -241,6 +240,12 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillVarlen a) {
     };
     if (need_mask) update(std::true_type{});
     else update(std::false_type{});
+    if (rescale) {
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[dt][i] *= alpha;
+    }
 
     // O^T += V^T P^T: 4 key steps of 16 x 4 d tiles of 32.  Lane gi of
     // 16-lane group grp reads 4 bf16 of key row 16 ks + vr0 (+8) at dims
