@@ -129,6 +129,25 @@ __device__ __forceinline__ u32x2_t lds_read_tr_issue(const char* p) {
   asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "n"(kOffset));
   return v;
 }
+// LDS byte address of a pointer into a __shared__ array.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  typedef const __attribute__((address_space(3))) char lds_char;
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_char*)(p)));
+}
+// The two reads below from a precomputed LDS byte address.
+template <int kOffset>
+__device__ __forceinline__ u32x2_t lds_read_tr_at(uint32_t addr) {
+  u32x2_t v;
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "n"(kOffset));
+  return v;
+}
+template <int kOffset>
+__device__ __forceinline__ u32x4_t lds_read16_at(uint32_t addr) {
+  u32x4_t v;
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "n"(kOffset));
+  return v;
+}
+
 // 16-byte LDS read issued as inline assembly (same contract as
 // lds_read_tr_issue: pass the result through lds_wait() before use).
 template <int kOffset>

@@ -99,30 +99,41 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillVarlen a) {
   // ---- gather of one K/V tile straight into LDS (global_load_lds_dwordx4):
   // 16 wave-wide loads per half, wave w issuing loads w, w + 4, w + 8, w + 12.
   // Load j fills rows 4 j .. 4 j + 3 (lane i: row 4 j + i / 16, slot i % 16,
-  // which holds chunk slot ^ (row % 8)).  The four rows of a load share one
+  // which holds chunk slot ^ swz(row)).  The four rows of a load share one
   // page (16-key groups are 16-aligned, pages are multiples of 16): the page
-  // id is a wave-uniform scalar load.  Keys past kv_end re-read key
-  // kv_end - 1 (finite, masked out below).
-  const int64_t tok_stride = int64_t(a.num_kv_heads) * kD;
-  const int64_t kv_stride = int64_t(bs) * tok_stride;
-  const uint16_t* cache = static_cast<const uint16_t*>(a.cache);
+  // id is a wave-uniform scalar load, the page address a scalar base, and the
+  // lane's offset within the group a per-lane constant.  Keys past kv_end
+  // re-read key kv_end - 1 (finite, masked out below).
+  const int64_t tok_bytes = int64_t(a.num_kv_heads) * kD * 2;
+  const int64_t kv_bytes = int64_t(bs) * tok_bytes;
+  const char* cache_h = static_cast<const char*>(a.cache) + int64_t(kvh) * kD * 2;
   const int32_t* table = a.block_table + int64_t(r) * a.max_blocks;
+  // byte offset of this lane's 16 bytes within its 16-key group, per load jj
+  // (the same for every tile except the last group of the keys)
+  uint32_t lane_off[kTileLoads / 4];
+#pragma unroll
+  for (int jj = 0; jj < kTileLoads / 4; ++jj) {
+    const int row = 4 * (wave + 4 * jj) + (lane >> 4);
+    lane_off[jj] = uint32_t((row & 15) * tok_bytes + 16 * ((lane & 15) ^ swz(row)));
+  }
+  const int last16 = ((kv_end - 1) / 16) * 16;
   auto gload = [&](int tile, char* kdst) {
     char* vdst = kdst + kTileBytes;
 #pragma unroll
     for (int jj = 0; jj < kTileLoads / 4; ++jj) {
       const int j = wave + 4 * jj;
-      const int row = 4 * j + (lane >> 4);
-      const int key16 = min(tile * kBN + 16 * (j >> 2), ((kv_end - 1) / 16) * 16);
+      const int key16 = min(tile * kBN + 16 * (j >> 2), last16);
       int64_t blk = uniform_load(table + key16 / bs);
       blk = (blk < 0 || blk >= a.num_blocks) ? 0 : blk;
-      const int key = min(key16 + (row & 15), kv_end - 1);
-      const int chunk = (lane & 15) ^ swz(row);
-      const uint16_t* src = cache + (blk * 2 * bs + (key - (key16 / bs) * bs)) * tok_stride +
-                            int64_t(kvh) * kD + 8 * chunk;
+      const char* base = cache_h + (blk * 2 * bs + (key16 - (key16 / bs) * bs)) * tok_bytes;
+      uint32_t off = lane_off[jj];
+      if (key16 + 15 >= kv_end) {   // last group: keys past kv_end re-read key kv_end - 1
+        const int row = 4 * j + (lane >> 4);
+        off = uint32_t(min(row & 15, kv_end - 1 - key16) * tok_bytes + 16 * ((lane & 15) ^ swz(row)));
+      }
       typedef __attribute__((address_space(3))) void* lds_ptr;
-      __builtin_amdgcn_global_load_lds(src, (lds_ptr)(kdst + 1024 * j), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(src + kv_stride, (lds_ptr)(vdst + 1024 * j), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(base + off, (lds_ptr)(kdst + 1024 * j), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(base + kv_bytes + off, (lds_ptr)(vdst + 1024 * j), 16, 0, 0);
     }
   };
   auto gwait = [&]() { __builtin_amdgcn_s_waitcnt(0x0F70); };   // vmcnt(0)
