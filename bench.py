@@ -45,7 +45,7 @@ def log(msg):
 
 def kernel_source_sha(fname: str) -> str:
     h = hashlib.sha256()
-    for f in (fname, "pa_device.hpp", "launch.hpp"):
+    for f in (fname, "pa_device.hpp", "launch.hpp", "balanced.hpp"):
         with open(os.path.join(CSRC, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
