@@ -140,10 +140,10 @@ pa_status_t pa_cache_write(pa_layout_t layout, pa_dtype_t dtype,
  * scale:       multiplies Q K^T before the softmax (1/sqrt(head_dim) usually).
  * num_splits:  0 = automatic: with n = pa_num_kv_splits(max_seq_len,
  *              pa_device_num_cus()), n == 1 runs one unsplit pass; n > 1 with
- *              PA_BF16 and out != NULL runs the token-balanced schedule
- *              (pa_decode_balanced + pa_decode_balanced_merge), whose
- *              reduction order depends on the whole batch's lengths;
- *              otherwise n splits.
+ *              PA_BF16, out != NULL and num_kv_heads 1, 2, 4 or a multiple
+ *              of 8 runs the token-balanced schedule (pa_decode_balanced +
+ *              pa_decode_balanced_merge), whose reduction order depends on
+ *              the whole batch's lengths; otherwise n splits.
  *              1 = no split (each request reduced by one work unit, in an
  *              order independent of the rest of the batch); n > 1 = n splits.
  *              Split s of a request covers positions [s*P, (s+1)*P) with
@@ -207,7 +207,9 @@ pa_status_t pa_decode(pa_dtype_t dtype,
  * out, lse:    as pa_decode; after this call only the requests inside one
  *              range are final.
  * Supported: PA_BF16 storage, head_dim 128, num_q_heads / num_kv_heads in
- * {1, 2, 4, 8}, num_seqs * ceil(max_blocks_per_seq * block_size / 32) < 2^31.
+ * {1, 2, 4, 8}, num_kv_heads 1, 2, 4 or a multiple of 8 (a work-group loads
+ * whole rows of up to 8 heads), num_seqs * ceil(max_blocks_per_seq *
+ * block_size / 32) < 2^31.
  * pa_decode_balanced_merge completes out / lse (a request with no keys gets
  * out = 0, lse = -inf) after pa_decode_balanced (head_dim_v 128) or
  * pa_mla_decode_balanced (head_dim_v 512); its num_seqs, num_heads,

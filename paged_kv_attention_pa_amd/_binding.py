@@ -216,8 +216,9 @@ def decode(q, kv_cache, block_table, seq_lens, max_seq_len: int, scale: float,
     if n == 0:
         n = num_kv_splits(max_seq_len, device_num_cus())
     need = decode_workspace_bytes(B, Hq, D, n) if (n > 1 or stage1_only) else 0
-    if num_splits == 0 and n > 1 and not stage1_only and dt == PA_BF16:
-        # the automatic schedule is the token-balanced one
+    if (num_splits == 0 and n > 1 and not stage1_only and dt == PA_BF16
+            and (hkv in (1, 2, 4) or hkv % 8 == 0)):
+        # the automatic schedule is the token-balanced one (pa_decode's rule)
         need = decode_balanced_workspace_bytes(
             B, Hq, D, decode_balanced_num_ranges(hkv, device_num_cus()))
     if workspace is None and need:

@@ -44,6 +44,10 @@ bool is_pow2_group(int g) { return g == 1 || g == 2 || g == 4 || g == 8; }
 
 bool scale_ok(float s) { return s >= 0.0f && s <= 3.0e38f; }   // finite, not negative
 
+// The balanced GQA kernel's work-groups cover a power-of-two number of KV
+// heads (at most 8) of every token row.
+bool balanced_heads_ok(int hkv) { return hkv == 1 || hkv == 2 || hkv == 4 || hkv % 8 == 0; }
+
 // Tokens per split for n splits over max_seq_len keys, rounded up to whole
 // pages; at least one page.
 int split_tokens_for(int max_seq_len, int n, int block_size) {
@@ -249,7 +253,8 @@ pa_status_t pa_decode(pa_dtype_t dtype,
   const bool direct = !stage1 && used_splits(max_seq_len, P) == 1;
   // Automatic schedule with more than one split's worth of keys: token-balanced
   // ranges instead of per-request splits.
-  const bool balanced = num_splits == 0 && !stage1 && !direct && dtype == PA_BF16;
+  const bool balanced = num_splits == 0 && !stage1 && !direct && dtype == PA_BF16 &&
+                        balanced_heads_ok(num_kv_heads);
   const int nr = balanced ? pa_decode_balanced_num_ranges(num_kv_heads, cus) : 0;
   if (balanced) {
     st = check_balanced(num_seqs, num_q_heads, head_dim, max_blocks_per_seq, block_size, nr,
@@ -336,6 +341,9 @@ pa_status_t pa_decode_balanced(const void* q, const void* kv_cache, int64_t num_
   PA_REQUIRE(is_pow2_group(num_q_heads / num_kv_heads), PA_ERR_UNSUPPORTED,
              "balanced decode supports num_q_heads / num_kv_heads in {1, 2, 4, 8} (got %d)",
              num_q_heads / num_kv_heads);
+  PA_REQUIRE(balanced_heads_ok(num_kv_heads), PA_ERR_UNSUPPORTED,
+             "balanced decode supports num_kv_heads 1, 2, 4, 8 or a multiple of 8 (got %d)",
+             num_kv_heads);
   st = check_balanced(num_seqs, num_q_heads, head_dim, max_blocks_per_seq, block_size, num_ranges,
                       workspace, workspace_bytes);
   if (st != PA_OK) return st;

@@ -9,14 +9,15 @@
 // the merge kernel combines.
 //
 // Work-group: one wave per KV head (up to 8) of one range; the waves walk the
-// same chunks, so together they read whole 2 KiB token rows of a page.
-// Per wave: Q^T stays in registers as the B operand of S^T = K Q^T
-// (mfma 16x16x32 bf16, 16 keys x 16 query-head columns, G of them used); the
-// P^T registers feed O^T = V^T P^T directly.  K and V arrive with coalesced
-// 16-byte loads (16 lanes per 256 B head row) and are transposed through a
-// padded LDS tile; the registers of chunk c+1 are refilled as soon as chunk
-// c's values are in the tile, so one chunk of loads is in flight while the
-// previous one is computed.
+// same chunks.  Loads are contiguous: each instruction fetches a whole 1 KiB
+// piece of the work-group's slice of token rows (all its heads), and the
+// pieces go through LDS to per-head tiles (a measured 10% more HBM bandwidth
+// than each wave gathering its own 256-byte head rows).  Per wave: Q^T stays
+// in registers as the B operand of S^T = K Q^T (mfma 16x16x32 bf16, 16 keys
+// x 16 query-head columns, G of them used); the P^T registers feed O^T =
+// V^T P^T directly.  The registers of chunk c+1 are refilled as soon as
+// chunk c's pieces are in LDS, so one chunk of loads is in flight while the
+// previous one is computed; two barriers per chunk guard the shared tiles.
 #include "balanced.hpp"
 #include "launch.hpp"
 #include "pa_device.hpp"
@@ -33,7 +34,7 @@ constexpr int kHeads = 8;               // KV heads (waves) per work-group
 template <int G>
 __global__ __launch_bounds__(64 * kHeads, 1) void decode_balanced_kernel(DecodeBalanced a) {
   static_assert(G >= 1 && G <= 16, "group must fit the 16 MFMA columns");
-  __shared__ __align__(16) char smem[kHeads * kTile];
+  __shared__ __align__(16) char smem[2 * kHeads * kTile];   // K tiles of every head, then V tiles
   __shared__ int s_wave_sum[kHeads];
   __shared__ int s_start[2];
   const int tid = threadIdx.x;
@@ -52,8 +53,7 @@ __global__ __launch_bounds__(64 * kHeads, 1) void decode_balanced_kernel(DecodeB
   if (!balanced_range(a.seq_lens, B, cap, a.num_ranges, j, j == 0 && hg == 0, a.cu, s_wave_sum,
                       s_start, c0, c1, cur))
     return;
-  const int h = hg * kHeads + wave;
-  if (h >= Hkv) return;   // no barrier below
+  const int h = hg * kHeads + wave;   // < Hkv: the launch gives every head group whole waves
 
   const int li = lane & 15;   // MFMA row/column index; 16-byte chunk of a loaded row
   const int kq = lane >> 4;   // 16-lane group; token within a 4-token load
@@ -65,10 +65,18 @@ __global__ __launch_bounds__(64 * kHeads, 1) void decode_balanced_kernel(DecodeB
   const uint16_t* qbase = static_cast<const uint16_t*>(a.q);
   const float scale2 = a.scale * kLog2e;
 
-  char* tl = smem + wave * kTile;
-  char* const st_base = tl + kq * kRow + 16 * li;                    // row 4 i + kq, chunk li
-  const char* const a_base = tl + li * kRow + 16 * kq;               // row 16 sub + li, chunk 4 kk + kq
-  const char* const tr_base = tl + (4 * kq + (li >> 2)) * kRow + 8 * (li & 3);
+  const int waves = blockDim.x >> 6;
+  const char* const a_base = smem + wave * kTile + li * kRow + 16 * kq;             // K: row 16 sub + li
+  const char* const tr_base = smem + (kHeads + wave) * kTile + (4 * kq + (li >> 2)) * kRow + 8 * (li & 3);
+  // Loads are contiguous 1 KiB pieces of the work-group's slice of a token
+  // row (waves x 256 B): instruction i of wave w is piece I = w + waves i,
+  // lane l its bytes 16 l .. 16 l + 15.  Piece I covers tokens (1024 I) /
+  // slice .., byte (1024 I + 16 l) % slice of the slice, i.e. head
+  // byte / 256, 16-byte chunk (byte % 256) / 16.
+  const int lw = waves == 8 ? 3 : waves == 4 ? 2 : waves == 2 ? 1 : 0;
+  const int sh = 8 + lw;                       // log2 of the slice bytes
+  const char* cache_b = static_cast<const char*>(a.cache) + int64_t(hg) * kHeads * kD * 2;
+  const int64_t tok_bytes = tok_stride * 2, kv_bytes = kv_stride * 2;
 
   // Q^T columns: lane li holds query head h G + (li mod G); the columns past G
   // repeat real rows and their results are never stored.
@@ -77,27 +85,31 @@ __global__ __launch_bounds__(64 * kHeads, 1) void decode_balanced_kernel(DecodeB
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) qf[kk] = load16(qp + 32 * kk);
   };
-  // K (plane 0) or V (plane kv_stride) rows of chunk p: instruction i reads
-  // tokens 4 i + kq of each 16-token half, lane li its 16-byte chunk li.
-  // Tokens past the request's end re-read its last token (finite data,
-  // masked below); the loads are unconditional so the waits stay exact.
+  // K (plane 0) or V (plane kv_bytes) pieces of chunk p.  Tokens past the
+  // request's end re-read its last token (finite data, masked below); the
+  // loads are unconditional so the waits stay exact.
   auto load_half = [&](const ChunkPos& p, int64_t plane, u32x4_t (&dst)[8]) {
     const int32_t* table = a.block_table + int64_t(p.r) * a.max_blocks;
     const int len = max(p.len, 1);   // positions always hold keys; keeps every index >= 0
-    const int last16 = ((len - 1) / 16) * 16;
 #pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
-      const int tok16 = min(p.lc * kChunk + 16 * sub, last16);
-      int64_t blk = uniform_load(table + tok16 / bs);
+    for (int i = 0; i < 8; ++i) {
+      const int I = wave + waves * i;
+      const int lin = I * 1024 + 16 * lane;
+      const int tl_first = (I * 1024) >> sh;                       // first token of the piece
+      const int tok_first = min(p.lc * kChunk + tl_first, len - 1);
+      int64_t blk = uniform_load(table + tok_first / bs);
       blk = (blk < 0 || blk >= a.num_blocks) ? 0 : blk;
-      const int page0 = (tok16 / bs) * bs;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int tok = min(tok16 + 4 * i + kq, len - 1);
-        const int64_t off = (blk * 2 * bs + (tok - page0)) * tok_stride + int64_t(h) * kD + 8 * li;
-        dst[4 * sub + i] = load16(cache + plane + off);
-      }
+      const int page0 = (tok_first / bs) * bs;
+      const int tok = min(p.lc * kChunk + (lin >> sh), len - 1);
+      const int byte = lin & ((1 << sh) - 1);
+      dst[i] = load16(cache_b + plane + (blk * 2 * bs + (tok - page0)) * tok_bytes + byte);
     }
+  };
+  // LDS position of this lane's piece i (head tile, token row, chunk)
+  auto lds_off = [&](int i) {
+    const int lin = (wave + waves * i) * 1024 + 16 * lane;
+    const int byte = lin & ((1 << sh) - 1);
+    return (byte >> 8) * kTile + (lin >> sh) * kRow + (byte & 255);
   };
 
   ChunkPos nxt = c0 + 1 < c1 ? next_chunk(cur, a.seq_lens, cap, B) : cur;
@@ -106,7 +118,7 @@ __global__ __launch_bounds__(64 * kHeads, 1) void decode_balanced_kernel(DecodeB
   load_q(cur.r, qf);
   u32x4_t kr[8], vr[8];
   load_half(cur, 0, kr);
-  load_half(cur, kv_stride, vr);
+  load_half(cur, kv_bytes, vr);
 
   f32x4_t acc[8];   // O^T: d = 16 dt + 4 kq + i, head column li
 #pragma unroll
@@ -114,11 +126,19 @@ __global__ __launch_bounds__(64 * kHeads, 1) void decode_balanced_kernel(DecodeB
   float m_run = kNoMax, l_run = 0.0f;
 
   for (int c = c0; c < c1; ++c) {
-    // K rows into the tile; the registers are refilled with the next chunk
+    // this chunk's pieces into every head's K and V tiles; once all waves'
+    // are there, the registers are refilled with the next chunk
 #pragma unroll
-    for (int i = 0; i < 8; ++i) *reinterpret_cast<u32x4_t*>(st_base + 4 * i * kRow) = kr[i];
+    for (int i = 0; i < 8; ++i) {
+      const int o = lds_off(i);
+      *reinterpret_cast<u32x4_t*>(smem + o) = kr[i];
+      *reinterpret_cast<u32x4_t*>(smem + kHeads * kTile + o) = vr[i];
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's LDS stores are done
+    __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
     load_half(nxt, 0, kr);
+    load_half(nxt, kv_bytes, vr);
     f32x4_t sc[2];
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
@@ -131,11 +151,6 @@ __global__ __launch_bounds__(64 * kHeads, 1) void decode_balanced_kernel(DecodeB
     }
     const bool new_request = nxt.lc == 0 && c + 1 < c1;
     if (new_request) load_q(nxt.r, qf);
-    // V rows into the same tile (this wave's LDS operations run in order)
-#pragma unroll
-    for (int i = 0; i < 8; ++i) *reinterpret_cast<u32x4_t*>(st_base + 4 * i * kRow) = vr[i];
-    __builtin_amdgcn_sched_barrier(0);
-    load_half(nxt, kv_stride, vr);
 
     // online softmax over this chunk (base 2); keys past the request end masked
     const int tok0 = cur.lc * kChunk;
@@ -212,6 +227,7 @@ __global__ __launch_bounds__(64 * kHeads, 1) void decode_balanced_kernel(DecodeB
     }
     cur = nxt;
     if (c + 2 < c1) nxt = next_chunk(nxt, a.seq_lens, cap, B);
+    __builtin_amdgcn_s_barrier();   // every wave is done reading the tiles
   }
 }
 

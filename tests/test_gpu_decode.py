@@ -92,6 +92,7 @@ CASES = [
     ("g8_bf16", [5, 64, 1000, 2049], 64, 8, 16, W.BF16),
     ("g1_bf16", [3, 40, 511, 513], 8, 8, 16, W.BF16),
     ("g2_bf16_block32", [31, 32, 33, 900], 4, 2, 32, W.BF16),
+    ("g2_hkv6_bf16", [300, 1200, 7], 12, 6, 16, W.BF16),   # automatic schedule: splits
     ("g4_fp32", [2, 128, 1025], 8, 2, 16, W.F32),
     ("g8_fp32_block64", [70, 640], 16, 2, 64, W.F32),
 ]

@@ -220,6 +220,7 @@ def test_balanced_validation(lib):
     assert call(a3=24) == INVALID                    # block size 24
     assert call(a15=None) == INVALID                 # no output
     assert call(a5=1 << 30, a7=1 << 20) == UNSUPPORTED   # chunk count past int32
+    assert call(a8=12, a9=6) == UNSUPPORTED              # 6 KV heads: not whole rows of 1/2/4/8
     m = lib.pa_decode_balanced_merge
     assert m(1 << 20, need - 1, 4, 32, 128, 16, 5, None, None) == WORKSPACE
     assert m(1 << 20, need, 4, 32, 128, 0, 5, None, None) == INVALID
