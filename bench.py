@@ -290,10 +290,17 @@ def roofline(case, kern_s):
     else:
         achieved = case.kern_flops / kern_s / 1e12
         peak, unit = PEAK_BF16_TFLOPS, "TFLOP/s"
+    # both roofs, for a reader placing the kernel against the ridge point
+    # (MLA decode, about 230 flop/byte, sits on the HBM side of it)
+    gbs = case.kern_bytes / kern_s / 1e9
+    tfs = case.kern_flops / kern_s / 1e12
     return {"bound": case.bound, "kernel": case.kernel_name, "achieved": round(achieved, 2),
             "peak": peak, "unit": unit, "frac": round(achieved / peak, 4),
             "traffic": traffic_for(case), "kernel_ms": round(kern_s * 1e3, 4),
-            "algorithmic_bytes": int(case.kern_bytes), "algorithmic_flops": int(case.kern_flops)}
+            "algorithmic_bytes": int(case.kern_bytes), "algorithmic_flops": int(case.kern_flops),
+            "kernel_GBps": round(gbs, 1), "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
+            "kernel_TFLOPs": round(tfs, 2), "mfma_frac": round(tfs / PEAK_BF16_TFLOPS, 4),
+            "flop_per_byte": round(case.kern_flops / max(case.kern_bytes, 1), 1)}
 
 
 # --------------------------------------------------------------------------
