@@ -7,21 +7,24 @@
 // split carry their lse for the stage-2 merge.  Online softmax as in
 // "第 1 章 注意力后端" §4.1.
 //
-// gfx950 mapping.  One work-group of 8 waves owns a run of 32-key tiles for
-// all H <= 128 query heads; wave w owns heads 16w..16w+15 (waves past H/16
-// only help gather tiles).  Because every head reads the same latent row, the
-// work is a real dense contraction: per tile, S^T[32 keys x 16 heads] =
-// K[32 x 576] Q^T[576 x 16] (18 k-steps of v_mfma_f32_16x16x32_bf16 per 16
-// keys) and O^T[512 x 16] += V^T[512 x 32] P^T[32 x 16] (32 MFMAs, V^T read
-// with ds_read_b64_tr_b16).  Each latent row is fetched from HBM once per
-// work-group into an LDS tile (global_load_lds_dwordx4, swizzled, two
-// buffers) and feeds both products.  Lanes l, l^16, l^32, l^48 share head
-// l % 16; the per-head softmax state lives there, and the running max is
-// rescaled lazily (only when a head's max grows by more than kSlack).
-// The LDS reads of a tile are issued as inline assembly and waited for
-// explicitly: the compiler would otherwise wait for the next tile's loads,
-// still in flight, before reading the current one (it cannot tell the two
-// buffers apart), which serialises the pipeline.
+// gfx950 mapping.  One work-group of 4 waves (one per SIMD) walks a run of
+// 32-key tiles for all H <= 128 query heads; wave w owns heads 32w..32w+31
+// (heads past H are zero queries whose results are dropped).  Every head
+// reads the same latent row, so both products are dense contractions on
+// v_mfma_f32_32x32x16_bf16, computed transposed so that each lane owns one
+// head:
+//   S^T[32 keys x 32 heads] = K[32 x 576] Q^T[576 x 32]   (36 k-steps)
+//   O^T[512 x 32 heads]    += V^T[512 x 32] P^T[32 x 32]  (16 d-tiles x 2)
+// P^T is the S^T output registers (bf16), V^T comes from gfx950's
+// transposing LDS read.  With 32 heads per operand each LDS byte read feeds
+// twice the MFMA work of a 16-head split, and the 256-register O^T
+// accumulator lives in the AGPRs of a wave that has its SIMD to itself.
+// Each latent row is fetched from HBM once per work-group into an LDS tile
+// (global_load_lds_dwordx4, four buffers: three tiles in flight) and feeds
+// both products.  The LDS operand reads are issued as inline assembly and
+// waited for explicitly, three MFMAs ahead: the compiler cannot tell the
+// DMA-filled buffers apart and would otherwise wait for every load in
+// flight before reading any of them.
 #include "balanced.hpp"
 #include "launch.hpp"
 #include "pa_device.hpp"
@@ -37,23 +40,55 @@ constexpr int kBN = 32;                         // keys per tile
 constexpr int kRowBytes = kRow * 2;             // 1152 B, unpadded (swizzled)
 constexpr int kTileBytes = kBN * kRowBytes;     // 36864 B
 constexpr int kTileLoads = kBN * kChunks / 64;  // 36 wave-wide 16-byte loads per tile
-constexpr int kMaxWaves = 8;
-constexpr int kStages = 2;                      // LDS tile buffers: kStages - 1 tiles in flight
+constexpr int kWaves = 4;
+constexpr int kLoadsPerWave = kTileLoads / kWaves;   // 9
+constexpr int kHeadsPerWave = 32;
+constexpr int kStages = 4;                      // LDS tile buffers: kStages - 1 tiles in flight
+constexpr int kKSteps = kRow / 16;              // 36 k-steps of the score product
+constexpr int kDTiles = kRank / 32;             // 16 d-tiles of the value product
 constexpr float kSlack = 8.0f;                  // lazy-rescale headroom, log2 units
+constexpr int kKDepth = 3;                      // K-fragment reads in flight ahead of their MFMA
+constexpr int kVDepth = 3;                      // V^T steps (two reads each) in flight ahead
+static_assert(kTileLoads % kWaves == 0, "loads per wave");
+static_assert(kStages * kTileBytes <= 160 * 1024 - 64, "LDS budget");
 
-// 16-byte chunk c of latent row r sits in LDS slot c ^ (r % 8) of the row
-// (within its aligned group of eight), spreading K-row and V-column reads
-// over all banks.
-__device__ __forceinline__ int tile_off(int r, int c) { return r * kRowBytes + 16 * (c ^ (r & 7)); }
-
-// Max / sum over the four lanes l, l^16, l^32, l^48 (one head).
-__device__ __forceinline__ float head_max(float x) {
-  x = fmaxf(x, lane_xor(x, 16));
-  return fmaxf(x, lane_xor(x, 32));
+// 16-byte chunk c of latent row r sits in LDS slot c ^ sx(r) of the row (the
+// XOR stays inside c's aligned group of eight), with sx(r) holding bits 1, 2
+// and 3 of r in reverse order.  Rows are 1152 B = 72 slots, so the bank
+// offset of a row alternates with r % 2; sx then makes
+// * a 16-lane phase of a K-fragment read (16 consecutive rows, one chunk)
+//   hit 16 distinct 16-byte bank groups, and
+// * a 32-lane phase of a V^T transposing read (4 consecutive rows 4q..4q+3,
+//   4 consecutive chunks 4m..4m+3, both 8-byte halves) do the same,
+// so neither read has bank conflicts.
+__device__ __forceinline__ int sx(int r) {
+  return (((r >> 1) & 1) << 2) | (((r >> 2) & 1) << 1) | ((r >> 3) & 1);
 }
-__device__ __forceinline__ float head_sum(float x) {
-  x += lane_xor(x, 16);
-  return x + lane_xor(x, 32);
+__device__ __forceinline__ int slot_of(int r, int c) { return (c & ~7) | ((c & 7) ^ sx(r)); }
+
+// The two products are issued as inline assembly so that each keeps its own
+// register file: the 256-register O^T accumulator in AGPRs, the score
+// accumulator (read by the softmax) in VGPRs.  With the builtin the compiler
+// picks one form for every MFMA of the kernel.  The hazards the compiler
+// would otherwise cover are covered by explicit s_nop below (an MFMA result
+// read by the VALU, a VALU result read by an MFMA).
+__device__ __forceinline__ void mfma_s0(f32x16_t& d, const u32x4_t& a, const u32x4_t& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_s(f32x16_t& d, const u32x4_t& a, const u32x4_t& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_o(f32x16_t& d, const u32x4_t& a, const u32x4_t& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(d) : "v"(a), "v"(b));
+}
+// Orders every read and write of the accumulator tiles after (tie) or
+// before (hazard fence) this point; kNop wait states go after the last one.
+template <int kNop>
+__device__ __forceinline__ void acc_fence(f32x16_t (&acc)[16]) {
+  asm volatile("" : "+a"(acc[0]), "+a"(acc[1]), "+a"(acc[2]), "+a"(acc[3]));
+  asm volatile("" : "+a"(acc[4]), "+a"(acc[5]), "+a"(acc[6]), "+a"(acc[7]));
+  asm volatile("" : "+a"(acc[8]), "+a"(acc[9]), "+a"(acc[10]), "+a"(acc[11]));
+  asm volatile("s_nop %4" : "+a"(acc[12]), "+a"(acc[13]), "+a"(acc[14]), "+a"(acc[15]) : "n"(kNop));
 }
 
 // Two schedules share the kernel body:
@@ -65,9 +100,9 @@ __device__ __forceinline__ float head_sum(float x) {
 // A "tile" is 32 keys [kb + 32 lc, kb + 32 lc + 32) of request r, keys at or
 // past kend masked (split: kb = t0, kend = t1; balanced: kb = 0, kend = len).
 template <bool kBalanced>
-__global__ __launch_bounds__(512) void mla_kernel(MlaDecode a) {
-  __shared__ __align__(16) char smem[kStages * kTileBytes];
-  __shared__ int s_wave_sum[kMaxWaves];
+__global__ __launch_bounds__(64 * kWaves, 1) void mla_kernel(MlaDecode a) {
+  __shared__ __align__(1024) char smem[kStages * kTileBytes];
+  __shared__ int s_wave_sum[kWaves];
   __shared__ int s_start[2];
   const int lane = threadIdx.x & 63;
   const int wave = wave_id();
@@ -118,256 +153,357 @@ __global__ __launch_bounds__(512) void mla_kernel(MlaDecode a) {
     }
   };
 
-  // ---- Q^T fragments: head = 16 wave + l % 16, dims 32 kk + 8 (l / 16) .. + 8
-  const bool active = wave < H / 16;
-  const int head = active ? 16 * wave + (lane & 15) : 0;
-  const int kq = lane >> 4;
-  u32x4_t qf[18];
+  const int c32 = lane & 31;          // head column / key row / dim row of the MFMA operands
+  const int g = lane >> 5;            // k half of the MFMA operands
+  const bool active = kHeadsPerWave * wave < H;
+  const int head = kHeadsPerWave * wave + c32;
+  const bool head_ok = head < H;
+
+  // ---- Q^T fragments (B operand of S^T): head `head`, dims 16 kk + 8 g .. + 8
+  u32x4_t qf[kKSteps];
   auto load_q = [&](int r) {
+    const int hq = head_ok ? head : 0;
     const uint16_t* qn = static_cast<const uint16_t*>(a.q_nope) + int64_t(r) * a.qn_sb +
-                         int64_t(head) * a.qn_sh;
+                         int64_t(hq) * a.qn_sh + 8 * g;
     const uint16_t* qp = static_cast<const uint16_t*>(a.q_pe) + int64_t(r) * a.qp_sb +
-                         int64_t(head) * a.qp_sh;
+                         int64_t(hq) * a.qp_sh + 8 * g;
+    // heads past H read head 0 (in bounds) and are zeroed after the wait
 #pragma unroll
-    for (int kk = 0; kk < 16; ++kk) qf[kk] = load16(qn + 32 * kk + 8 * kq);
+    for (int kk = 0; kk < kRank / 16; ++kk) qf[kk] = load16(qn + 16 * kk);
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) qf[16 + kk] = load16(qp + 32 * kk + 8 * kq);
+    for (int kk = 0; kk < kRope / 16; ++kk) qf[kRank / 16 + kk] = load16(qp + 16 * kk);
   };
 
   // ---- gather of a tile straight into LDS: 36 wave-wide loads of 64 x 16 B
   // (global_load_lds_dwordx4; lane i lands at byte 16 i of the load's 1 KiB),
-  // wave w issuing loads w, w + 8, ...  Position p = 64 j + i of load j is
-  // row p / 72, slot p % 72, which holds chunk slot ^ (row % 8).  A 32-key
-  // tile spans at most two pages, whose ids are wave-uniform scalar loads.
-  // Keys at or past kend re-read key kend - 1 (finite, masked out below).
+  // wave w issuing loads w, w + 4, ...  Position p = 64 j + i of load j is
+  // row p / 72, slot p % 72, which holds chunk slot_of(row, slot) (the XOR
+  // is an involution).  The lane's byte offset within a tile of contiguous
+  // rows is fixed (goff); rows whose key lies on the next page, or at or
+  // past kend (re-read as key kend - 1: finite, masked out below), take a
+  // per-tile correction.
   const uint16_t* cache = static_cast<const uint16_t*>(a.cache);
-  auto gload = [&](const ChunkPos& p, char* dst) {
+  uint32_t goff[kLoadsPerWave];
+#pragma unroll
+  for (int jj = 0; jj < kLoadsPerWave; ++jj) {
+    const int pos = 64 * (wave + kWaves * jj) + lane;
+    const int row = pos / kChunks;
+    const int slot = pos - row * kChunks;
+    goff[jj] = uint32_t(row * kRowBytes + 16 * slot_of(row, slot));
+  }
+  // Page ids of a tile's first and last key (scalar loads).  They are read a
+  // step before the gather that uses them, at the end of the previous tile's
+  // compute: a scalar load waited for right before its use would stall the
+  // gather's issue, and one in flight during the LDS operand reads would
+  // stall those (both count on lgkmcnt).
+  struct Pages { int32_t b0, b1; };
+  auto pages = [&](const ChunkPos& p) {
     const int32_t* table = a.block_table + int64_t(p.r) * a.max_blocks;
     const int key0 = kb + p.lc * kBN;
     const int kend = p.len;
     const int kl0 = min(key0, kend - 1), kl1 = min(key0 + kBN - 1, kend - 1);
-    int64_t b0 = uniform_load(table + kl0 / bs), b1 = uniform_load(table + kl1 / bs);
+    return Pages{uniform_load(table + kl0 / bs), uniform_load(table + kl1 / bs)};
+  };
+  auto gload = [&](const ChunkPos& p, int stage, const Pages& pg) {
+    const int key0 = kb + p.lc * kBN;
+    const int kend = p.len;
+    int64_t b0 = pg.b0, b1 = pg.b1;
     b0 = (b0 < 0 || b0 >= a.num_blocks) ? 0 : b0;
     b1 = (b1 < 0 || b1 >= a.num_blocks) ? 0 : b1;
-    // key0 + row sits at offset kin = (key0 % bs) + row of page b0, or
-    // kin - bs of page b1 (key0 is a multiple of 16 below one page's end)
-    const int in0 = key0 % bs;
-    const int last = kend - 1 - key0 + in0;          // offset of key kend - 1
-    const int64_t o0 = b0 * bs * kRow, o1 = (b1 - 1) * bs * kRow;
-    for (int jl = wave; jl < kTileLoads; jl += kMaxWaves) {
-      const int pos = 64 * jl + lane;
-      const int row = pos / kChunks;
-      const int slot = pos - row * kChunks;
-      const int kin = min(in0 + row, last);
-      const uint16_t* src = cache + ((kin < bs ? o0 : o1) + kin * kRow + 8 * (slot ^ (row & 7)));
-      __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(dst + 1024 * jl),
-                                       16, 0, 0);
+    const int in0 = key0 - (key0 / bs) * bs;      // key0's row within page b0
+    // row 0 of the tile as a byte address; the rows run on contiguously
+    // while they stay on page b0 and below kend
+    const char* base0 = reinterpret_cast<const char*>(cache) + (b0 * bs + in0) * int64_t(kRowBytes);
+    const bool simple = in0 + kBN <= bs && key0 + kBN <= kend;   // wave-uniform
+    typedef __attribute__((address_space(3))) void* lds_ptr;
+    char* dst = smem + stage * kTileBytes;
+    if (simple) {
+#pragma unroll
+      for (int jj = 0; jj < kLoadsPerWave; ++jj)
+        __builtin_amdgcn_global_load_lds(base0 + goff[jj],
+                                         (lds_ptr)(dst + 1024 * (wave + kWaves * jj)), 16, 0, 0);
+    } else {
+      const int last = kend - 1 - key0;             // tile row of key kend - 1
+      const char* base1 = reinterpret_cast<const char*>(cache) +
+                          (b1 * bs - (bs - in0)) * int64_t(kRowBytes);   // row bs - in0 -> page b1 row 0
+#pragma unroll
+      for (int jj = 0; jj < kLoadsPerWave; ++jj) {
+        const int row = int(goff[jj] / uint32_t(kRowBytes));
+        const int rr = min(row, last);
+        const int64_t off = int64_t(goff[jj]) + int64_t(rr - row) * kRowBytes;
+        const char* src = (in0 + rr < bs ? base0 : base1) + off;
+        __builtin_amdgcn_global_load_lds(src, (lds_ptr)(dst + 1024 * (wave + kWaves * jj)), 16, 0, 0);
+      }
     }
   };
-  // all of this wave's loads have landed (the caller then syncs the group)
   auto gwait = [&]() { __builtin_amdgcn_s_waitcnt(0x0F70); };   // vmcnt(0)
 
-  const float scale2 = a.scale * kLog2e;
+  // ---- LDS operand addresses (per lane; the stage and the k-step / d-tile
+  // group are added as offsets)
+  // K fragment of k-step kk = 4 q + kq: key row c32, chunk 8 q + 2 kq + g.
+  const uint32_t lds0 = lds_addr(smem);
+  uint32_t kaddr[4];
+#pragma unroll
+  for (int kq = 0; kq < 4; ++kq)
+    kaddr[kq] = lds0 + c32 * kRowBytes + 16 * slot_of(c32, 2 * kq + g);
+  // V^T fragment of d-tile m = 2 mh + ml and key step st, read e (0, 1):
+  // within each 16-lane group, lane 4 q + i reads key row 16 st + 8 e + 4 g
+  // + q, dims 32 m + 16 (lane / 16 % 2) + 4 i .. + 4 (chunk 4 m + c0, half
+  // i % 2, c0 = 2 (lane / 16 % 2) + i / 2); the transposing read hands lane
+  // 4 q + i of the group dim 16 (lane / 16 % 2) + 4 q + i, keys +0..3, which
+  // is the A layout of v_mfma_f32_32x32x16_bf16 for keys in the order of the
+  // S^T output registers.
+  uint32_t vaddr[2][2];   // [e][ml]
+  {
+    const int i4 = lane & 3, q4 = (lane >> 2) & 3;
+    const int cg = 2 * ((lane >> 4) & 1) + (i4 >> 1);
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int row = 8 * e + 4 * g + q4;
+#pragma unroll
+      for (int ml = 0; ml < 2; ++ml)
+        vaddr[e][ml] = lds0 + row * kRowBytes + 16 * slot_of(row, 4 * ml + cg) + 8 * (i4 & 1);
+    }
+  }
+
+  // Masked scores are -inf and meet the scale inside the exponent; a zero
+  // scale is raised to the smallest normal float so that -inf * scale stays
+  // -inf (weight 0) while every visible score still maps to exp2(0) = 1.
+  const float scale2 = fmaxf(a.scale * kLog2e, 0x1p-126f);
   float m_run = kNoMax;
   float l_run = 0.0f;          // this lane's share of head `head`'s sum
-  f32x4_t acc[32];             // O^T: d = 16 dt + 4 (l / 16) + r
+  bool fresh = true;           // acc holds nothing yet (no rescale needed)
+  f32x16_t acc[kDTiles];       // O^T: d = 32 m + 8 (r / 4) + 4 g + r % 4
 #pragma unroll
-  for (int dt = 0; dt < 32; ++dt) acc[dt] = f32x4_t{0, 0, 0, 0};
+  for (int m = 0; m < kDTiles; ++m)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[m][i] = 0.0f;
 
-  // ---- finish a segment: per-head sum over the 4 lanes, normalise, write
+  // ---- finish a segment: per-head sum over lanes l, l ^ 32, normalise, write
   auto finish = [&](const ChunkPos& p) {
-    const float l_tot = head_sum(l_run);
-    if (!active) return;
+    acc_fence<15>(acc);   // the VALU reads the accumulator
+    const float l_tot = xor32_sum(l_run);
+    if (!active || !head_ok) return;
     const float inv = 1.0f / l_tot;
     const float lse_nat = (m_run + fast_log2(l_tot)) * kLn2;
     const int64_t row = int64_t(p.r) * H + head;
     bool direct;
     float* pp;
+    int pstride;   // floats per partial row
     if constexpr (kBalanced) {
       direct = p.base >= c0 && p.base + chunks_of(p.len) <= c1;
       pp = a.part + (int64_t(j + p.r) * H + head) * (kRank + 4);
+      pstride = kRank + 4;
     } else {
       direct = a.direct;
       pp = a.part + (row * a.num_splits + s) * (kRank + 1);
+      pstride = kRank + 1;
     }
+    // one accumulator tile at a time through the VGPRs
     if (direct) {
       uint16_t* op = static_cast<uint16_t*>(a.out) + row * kRank;
 #pragma unroll
-      for (int dt = 0; dt < 32; ++dt) {
-        uint2 w;
-        w.x = pack_bf16x2(acc[dt][0] * inv, acc[dt][1] * inv);
-        w.y = pack_bf16x2(acc[dt][2] * inv, acc[dt][3] * inv);
-        *reinterpret_cast<uint2*>(op + 16 * dt + 4 * kq) = w;
+      for (int m = 0; m < kDTiles; ++m) {
+        asm volatile("" : "+a"(acc[m]));
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          uint2 w;
+          w.x = pack_bf16x2(acc[m][4 * q4 + 0] * inv, acc[m][4 * q4 + 1] * inv);
+          w.y = pack_bf16x2(acc[m][4 * q4 + 2] * inv, acc[m][4 * q4 + 3] * inv);
+          *reinterpret_cast<uint2*>(op + 32 * m + 8 * q4 + 4 * g) = w;
+        }
       }
-      if (kq == 0 && a.lse) a.lse[row] = lse_nat;
+      if (g == 0 && a.lse) a.lse[row] = lse_nat;
     } else {
+      if (kBalanced) {   // 16-byte aligned rows
 #pragma unroll
-      for (int dt = 0; dt < 32; ++dt)
+        for (int m = 0; m < kDTiles; ++m) {
+          asm volatile("" : "+a"(acc[m]));
 #pragma unroll
-        for (int i = 0; i < 4; ++i) pp[16 * dt + 4 * kq + i] = acc[dt][i] * inv;
-      if (kq == 0) pp[kRank] = lse_nat;
+          for (int q4 = 0; q4 < 4; ++q4)
+            *reinterpret_cast<f32x4_t*>(pp + 32 * m + 8 * q4 + 4 * g) =
+                f32x4_t{acc[m][4 * q4] * inv, acc[m][4 * q4 + 1] * inv, acc[m][4 * q4 + 2] * inv,
+                        acc[m][4 * q4 + 3] * inv};
+        }
+      } else {
+#pragma unroll
+        for (int m = 0; m < kDTiles; ++m) {
+          asm volatile("" : "+a"(acc[m]));
+#pragma unroll
+          for (int i = 0; i < 16; ++i) pp[32 * m + 8 * (i >> 2) + 4 * g + (i & 3)] = acc[m][i] * inv;
+        }
+      }
+      if (g == 0) pp[kRank] = lse_nat;
     }
+    (void)pstride;
   };
 
   // Tile pipeline: kStages - 1 tiles are loading while one is computed.  Each
-  // wave issues n_w of a tile's loads (36 over 8 waves: 5 or 4), so "tile t
-  // has landed" is "at most n_w x (tiles issued after t) loads outstanding".
-  const int n_w = (kTileLoads + kMaxWaves - 1 - wave) / kMaxWaves;
-  auto wait_tiles = [&](int k) {   // k = tiles issued after the one waited for, <= kStages - 2
-    if (n_w == 5) {
-      if (k <= 0) __builtin_amdgcn_s_waitcnt(0x0F70);        // vmcnt(0)
-      else if (k == 1) __builtin_amdgcn_s_waitcnt(0x0F75);   // vmcnt(5)
-      else __builtin_amdgcn_s_waitcnt(0x0F7A);               // vmcnt(10)
-    } else {
-      if (k <= 0) __builtin_amdgcn_s_waitcnt(0x0F70);        // vmcnt(0)
-      else if (k == 1) __builtin_amdgcn_s_waitcnt(0x0F74);   // vmcnt(4)
-      else __builtin_amdgcn_s_waitcnt(0x0F78);               // vmcnt(8)
+  // wave issues 9 of a tile's 36 loads, so "tile t has landed" is "at most
+  // 9 x (tiles issued after t) loads outstanding".
+  auto wait_tiles = [&](int k) {   // k = tiles issued after the one waited for
+    if (k <= 0) __builtin_amdgcn_s_waitcnt(0x0F70);        // vmcnt(0)
+    else if (k == 1) __builtin_amdgcn_s_waitcnt(0x0F79);   // vmcnt(9)
+    else __builtin_amdgcn_s_waitcnt(0x4F72);               // vmcnt(18)
+  };
+  static_assert(kStages <= 4 && kLoadsPerWave == 9, "wait_tiles counts");
+
+  auto zero_pad_q = [&]() {
+    if (!head_ok) {
+#pragma unroll
+      for (int kk = 0; kk < kKSteps; ++kk) qf[kk] = u32x4_t{0, 0, 0, 0};
     }
   };
-  static_assert(kStages >= 2 && kStages <= 4 && kTileLoads == 36 && kMaxWaves == 8,
-                "wait_tiles counts");
-
   load_q(cur.r);
   gwait();   // q is in registers before any tile load is issued
+  zero_pad_q();
   ChunkPos ld = cur;   // next tile to load
   int n_loaded = 0;
   for (; n_loaded < kStages - 1 && n_loaded < n_tiles; ++n_loaded) {
-    gload(ld, smem + n_loaded * kTileBytes);
+    gload(ld, n_loaded, pages(ld));
     if (n_loaded + 1 < n_tiles) ld = advance(ld);
   }
+  Pages pg_next = pages(ld);   // ld stays inside the run, so this read is in bounds
 
-  for (int t = 0; t < n_tiles; ++t) {
+  // Segments: the tiles of one request within this work-group's run.  The
+  // segment boundary work (write the segment, reset, load the next q) sits
+  // outside the tile loop.
+  int t = 0;
+  for (;;) {
+  const int seg_end = min(n_tiles, t + chunks_of(cur.len) - cur.lc);
+  for (; t < seg_end; ++t) {
     wait_tiles(n_loaded - 1 - t);   // this wave's loads of tile t have landed
     // Everyone's have, and everyone is done with tile t - 1 (its LDS reads were
     // waited for).  A bare barrier: __syncthreads() would also wait for the
     // loads of the tiles still in flight.
     __builtin_amdgcn_s_barrier();
     if (n_loaded < n_tiles) {       // refill the buffer of tile t - 1
-      gload(ld, smem + (n_loaded % kStages) * kTileBytes);
+      gload(ld, n_loaded % kStages, pg_next);
       if (++n_loaded < n_tiles) ld = advance(ld);
     }
-    const char* tl = smem + (t % kStages) * kTileBytes;
+    const uint32_t st_off = uint32_t((t % kStages) * kTileBytes);
     const int key0 = kb + cur.lc * kBN;
     const int kend = cur.len;
     if (active) {
-    // S^T halves: keys 16 hh + 4 (l/16) + r, head l % 16
-    f32x4_t sc[2] = {f32x4_t{0, 0, 0, 0}, f32x4_t{0, 0, 0, 0}};
-    // chunk 4 kk + kq of row krow = 16 hh + l % 16: slot 8 (kk / 2) +
-    // ((4 (kk % 2) + kq) ^ (krow % 8)), i.e. two per-lane bases plus a constant
-    // offset per kk (rows krow and krow + 16 share krow % 8).  The two halves
-    // are independent accumulation chains; reads run one k-step ahead.
-    {
-      const int krow = lane & 15;
-      const char* kb0 = tl + krow * kRowBytes + 16 * (kq ^ (krow & 7));
-      const char* kb1 = tl + krow * kRowBytes + 16 * ((4 + kq) ^ (krow & 7));
-      u32x4_t kr[2][2];
-      auto issue = [&](auto kc) {
-        constexpr int kk = decltype(kc)::value;
-        const char* base = kk & 1 ? kb1 : kb0;
-        kr[kk & 1][0] = lds_read16_issue<128 * (kk >> 1)>(base);
-        kr[kk & 1][1] = lds_read16_issue<128 * (kk >> 1) + 16 * kRowBytes>(base);
-      };
-      issue(std::integral_constant<int, 0>{});
-      static_for<18>([&](auto kc) {
-        constexpr int kk = decltype(kc)::value;
-        if constexpr (kk + 1 < 18) {
-          issue(std::integral_constant<int, kk + 1>{});
-          lds_wait<2>(kr[kk & 1][0], kr[kk & 1][1]);
-        } else {
-          lds_wait<0>(kr[kk & 1][0], kr[kk & 1][1]);
+      // S^T: keys 8 (i / 4) + 4 g + i % 4 (register i), head c32.  K reads
+      // run kKDepth k-steps ahead.
+      f32x16_t sc;
+      {
+        uint32_t kb4[4];
+#pragma unroll
+        for (int kq = 0; kq < 4; ++kq) kb4[kq] = kaddr[kq] + st_off;
+        constexpr int kD = kKDepth;
+        u32x4_t kr[kD + 1];
+        auto issue = [&](auto kc) {
+          constexpr int kk = decltype(kc)::value;
+          kr[kk % (kD + 1)] = lds_read16_at<128 * (kk / 4)>(kb4[kk % 4]);
+        };
+        static_for<kD>([&](auto kc) { issue(kc); });
+        static_for<kKSteps>([&](auto kc) {
+          constexpr int kk = decltype(kc)::value;
+          // reads of k-steps kk + 1 .. kk + kD may stay in flight
+          constexpr int kLeft = kk + kD < kKSteps ? kD : kKSteps - 1 - kk;
+          if constexpr (kk + kD < kKSteps) issue(std::integral_constant<int, kk + kD>{});
+          lds_wait1<kLeft>(kr[kk % (kD + 1)]);
+          if constexpr (kk == 0) mfma_s0(sc, kr[0], qf[0]);
+          else mfma_s(sc, kr[kk % (kD + 1)], qf[kk]);
+        });
+        // the VALU reads the scores: 16 wait states after the last MFMA
+        asm volatile("s_nop 15" : "+v"(sc));
+      }
+      if (key0 + kBN > kend) {   // tail tile: keys at or past kend weigh 0
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (key0 + 8 * (i >> 2) + 4 * g + (i & 3) >= kend) sc[i] = -INFINITY;
+      }
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, sc[i]);
+      tmax = xor32_max(tmax);
+      const float tm = tmax == -INFINITY ? -INFINITY : tmax * scale2;
+      // lazy rescale: the reference max only moves when a head's max grows by
+      // more than kSlack (log2 units); p <= 2^kSlack in between
+      if (__any(tm > m_run + kSlack)) {
+        const float m_new = fmaxf(m_run, tm);
+        const float alpha = fast_exp2(m_run - m_new);
+        m_run = m_new;
+        l_run *= alpha;
+        if (!fresh) {   // one accumulator tile at a time through the VGPRs
+#pragma unroll
+          for (int m = 0; m < kDTiles; ++m) {
+            asm volatile("" : "+a"(acc[m]));
+            acc[m] *= alpha;
+            asm volatile("" : "+a"(acc[m]));
+          }
         }
-        sc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kr[kk & 1][0]), as_bf16x8(qf[kk]), sc[0], 0, 0, 0);
-        sc[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kr[kk & 1][1]), as_bf16x8(qf[kk]), sc[1], 0, 0, 0);
-      });
-    }
-    const bool tail = key0 + kBN > kend;
-    float tmax = -INFINITY;
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float v = sc[hh][i] * scale2;
-        if (tail && key0 + 16 * hh + 4 * kq + i >= kend) v = -INFINITY;
-        sc[hh][i] = v;
-        tmax = fmaxf(tmax, v);
       }
-    tmax = head_max(tmax);
-    // lazy rescale: the reference max only moves when a head's max grows by
-    // more than kSlack (log2 units); p <= 2^kSlack in between
-    if (__any(tmax > m_run + kSlack)) {
-      const float m_new = fmaxf(m_run, tmax);
-      const float alpha = fast_exp2(m_run - m_new);
-      m_run = m_new;
-      l_run *= alpha;
+      fresh = false;
+      u32x4_t pf[2];
+      float psum = 0.0f;
 #pragma unroll
-      for (int dt = 0; dt < 32; ++dt) acc[dt] *= alpha;
-    }
-    float p[8];
-    float psum = 0.0f;
+      for (int st = 0; st < 2; ++st) {
+        float p[8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      p[i] = fast_exp2(sc[0][i] - m_run);
-      p[4 + i] = fast_exp2(sc[1][i] - m_run);
-      psum += p[i] + p[4 + i];
-    }
-    l_run += psum;
-    const u32x4_t pf = u32x4_t{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
-                               pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])};
-    // O^T += V^T P^T: keys 4 kq + (0..3) and 16 + 4 kq + (0..3)
-    // lane gi of group kq: 4 bf16 of rows 4 kq + gi/4 (+16) at dims
-    // 16 dt + 4 (gi % 4), i.e. chunk 2 dt + (gi % 4)/2, half gi % 2
-    // (slot 8 (dt / 4) + ((2 (dt % 4) + (gi % 4)/2) ^ (row % 8)): four per-lane
-    // bases plus a constant offset per dt; rows vrow and vrow + 16 share row % 8)
-    const int gi = lane & 15;
-    const int vrow = 4 * kq + (gi >> 2);
-    const int bsel = (gi & 3) >> 1;
-    const char* vb[4];
-#pragma unroll
-    for (int m4 = 0; m4 < 4; ++m4)
-      vb[m4] = tl + vrow * kRowBytes + 16 * ((2 * m4 + bsel) ^ (vrow & 7)) + 8 * (gi & 1);
-    // V^T fragments in groups of two d-tiles (four reads), one group ahead;
-    // dt = 2 g + e reads rows vrow (+16) at slot offset 128 (dt / 4) of vb[dt % 4]
-    u32x2_t vr[2][4];
-    auto issue = [&](auto gc) {
-      constexpr int g = decltype(gc)::value;
-      constexpr int d0 = 2 * g, d1 = 2 * g + 1;
-      vr[g & 1][0] = lds_read_tr_issue<128 * (d0 >> 2)>(vb[d0 & 3]);
-      vr[g & 1][1] = lds_read_tr_issue<128 * (d0 >> 2) + 16 * kRowBytes>(vb[d0 & 3]);
-      vr[g & 1][2] = lds_read_tr_issue<128 * (d1 >> 2)>(vb[d1 & 3]);
-      vr[g & 1][3] = lds_read_tr_issue<128 * (d1 >> 2) + 16 * kRowBytes>(vb[d1 & 3]);
-    };
-    issue(std::integral_constant<int, 0>{});
-    static_for<16>([&](auto gc) {
-      constexpr int g = decltype(gc)::value;
-      if constexpr (g + 1 < 16) {
-        issue(std::integral_constant<int, g + 1>{});
-        lds_wait<4>(vr[g & 1][0], vr[g & 1][1], vr[g & 1][2], vr[g & 1][3]);
-      } else {
-        lds_wait<0>(vr[g & 1][0], vr[g & 1][1], vr[g & 1][2], vr[g & 1][3]);
+        for (int i = 0; i < 8; ++i) {
+          p[i] = fast_exp2(fmaf(sc[8 * st + i], scale2, -m_run));
+          psum += p[i];
+        }
+        pf[st] = u32x4_t{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
+                         pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])};
       }
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const int dt = 2 * g + e;
-        const u32x2_t v1 = vr[g & 1][2 * e], v2 = vr[g & 1][2 * e + 1];
-        const u32x4_t vf = u32x4_t{v1.x, v1.y, v2.x, v2.y};
-        acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vf), as_bf16x8(pf), acc[dt], 0, 0, 0);
-      }
-    });
-    }  // active
+      l_run += psum;
+      // P (and a rescaled accumulator) written by the VALU, read by the MFMA
+      asm volatile("s_nop 4" : "+v"(pf[0]), "+v"(pf[1]));
+      acc_fence<4>(acc);
 
-    if constexpr (kBalanced) {
-      // end of this request's keys in the range: emit its segment, start the next
-      if ((cur.lc + 1) * kBN >= cur.len && t + 1 < n_tiles) {
-        finish(cur);
+      // O^T += V^T P^T: step n = 16 st + m (d-tile m, key step st), two
+      // transposing reads per step, issued kVDepth steps ahead
+      {
+        uint32_t vb[2][2];
 #pragma unroll
-        for (int dt = 0; dt < 32; ++dt) acc[dt] = f32x4_t{0, 0, 0, 0};
-        m_run = kNoMax;
-        l_run = 0.0f;
-        load_q(advance(cur).r);
-        gwait();   // q (and every tile load so far) has landed
+        for (int e = 0; e < 2; ++e)
+#pragma unroll
+          for (int ml = 0; ml < 2; ++ml) vb[e][ml] = vaddr[e][ml] + st_off;
+        constexpr int kD = kVDepth;
+        u32x2_t vr[kD + 1][2];
+        auto vissue = [&](auto nc) {
+          constexpr int n = decltype(nc)::value, st = n / kDTiles, m = n % kDTiles;
+          constexpr int off = 16 * st * kRowBytes + 128 * (m / 2);
+          vr[n % (kD + 1)][0] = lds_read_tr_at<off>(vb[0][m % 2]);
+          vr[n % (kD + 1)][1] = lds_read_tr_at<off>(vb[1][m % 2]);
+        };
+        static_for<kD>([&](auto nc) { vissue(nc); });
+        static_for<2 * kDTiles>([&](auto nc) {
+          constexpr int n = decltype(nc)::value, st = n / kDTiles, m = n % kDTiles;
+          constexpr int kN = 2 * kDTiles;
+          constexpr int kLeft = 2 * (n + kD < kN ? kD : kN - 1 - n);
+          if constexpr (n + kD < kN) vissue(std::integral_constant<int, n + kD>{});
+          lds_wait<kLeft>(vr[n % (kD + 1)][0], vr[n % (kD + 1)][1]);
+          const u32x4_t vf = u32x4_t{vr[n % (kD + 1)][0].x, vr[n % (kD + 1)][0].y,
+                                     vr[n % (kD + 1)][1].x, vr[n % (kD + 1)][1].y};
+          mfma_o(acc[m], vf, pf[st]);
+        });
       }
-    }
-    if (t + 1 < n_tiles) cur = advance(cur);
+    }  // active
+    if (n_loaded < n_tiles) pg_next = pages(ld);   // lands over the loop tail and the barrier
+
+    if (t + 1 < seg_end) ++cur.lc;
+  }
+  if (t >= n_tiles) break;
+  // end of this request's keys in the run (balanced schedule only: a split
+  // covers one request): emit its segment, start the next
+  finish(cur);
+#pragma unroll
+  for (int m = 0; m < kDTiles; ++m)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[m][i] = 0.0f;
+  m_run = kNoMax;
+  l_run = 0.0f;
+  fresh = true;
+  cur = advance(cur);
+  load_q(cur.r);
+  gwait();   // q (and every tile load so far) has landed
+  zero_pad_q();
   }
   finish(cur);
 }
@@ -376,15 +512,16 @@ __global__ __launch_bounds__(512) void mla_kernel(MlaDecode a) {
 
 hipError_t launch_mla_decode(const MlaDecode& a, hipStream_t s) {
   if (a.num_seqs <= 0) return hipSuccess;
-  if (a.rank != kRank || a.rope != kRope || a.num_heads % 16 || a.num_heads > 16 * kMaxWaves)
+  if (a.rank != kRank || a.rope != kRope || a.num_heads % 16 ||
+      a.num_heads > kHeadsPerWave * kWaves)
     return hipErrorNotSupported;
   if (a.num_ranges > 0) {
-    hipLaunchKernelGGL(mla_kernel<true>, dim3(unsigned(a.num_ranges)), dim3(64 * kMaxWaves), 0, s, a);
+    hipLaunchKernelGGL(mla_kernel<true>, dim3(unsigned(a.num_ranges)), dim3(64 * kWaves), 0, s, a);
     return hipGetLastError();
   }
   const int64_t wgs = int64_t(a.num_seqs) * a.num_splits;
   if (wgs > INT32_MAX) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(mla_kernel<false>, dim3(unsigned(wgs)), dim3(64 * kMaxWaves), 0, s, a);
+  hipLaunchKernelGGL(mla_kernel<false>, dim3(unsigned(wgs)), dim3(64 * kWaves), 0, s, a);
   return hipGetLastError();
 }
 

@@ -175,12 +175,28 @@ __device__ __forceinline__ void lds_wait(u32x2_t& a, u32x2_t& b, u32x2_t& c, u32
 }
 
 template <int kLeft>
+__device__ __forceinline__ void lds_wait1(u32x4_t& a) {
+  asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(a) : "n"(kLeft));
+}
+template <int kLeft>
 __device__ __forceinline__ void lds_wait(u32x2_t& a, u32x2_t& b) {
   asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(a), "+v"(b) : "n"(kLeft));
 }
 template <int kLeft>
 __device__ __forceinline__ void lds_wait(u32x4_t& a, u32x4_t& b) {
   asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(a), "+v"(b) : "n"(kLeft));
+}
+
+// x combined with the value of lane l ^ 32, on the VALU (v_permlane32_swap):
+// returns {x[l], x[l ^ 32]} in some order, which is all a symmetric reduction
+// needs.
+__device__ __forceinline__ float xor32_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor32_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 // Calls f(std::integral_constant<int, I>) for I = 0..N-1, so that the index

@@ -38,11 +38,13 @@ constexpr int kTileLoads = kBN * kRowBytes / 1024;  // 16 wave-wide 16-byte load
 constexpr int kXcds = 8;           // accelerator dies work-groups are dealt to
 constexpr float kSlack = 8.0f;     // lazy-rescale headroom, log2 units
 // 16-byte chunk c of key row r sits in slot c ^ swz(r) of the row, with
-// swz(r) = 2 (r % 8) + (r / 8) % 2 (a permutation of r % 16).  Rows are
-// 256 B, so every row starts on the same bank; the XOR spreads the 16 rows of
-// a K-fragment load, and rows 0..7 of a V transpose read (which move the
-// 4-slot groups), over all 16 slots, i.e. all banks.
-__device__ __forceinline__ int swz(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
+// swz(r) = 4 (r % 4) + (r / 4) % 4 (a permutation of r % 16).  Rows are
+// 256 B, so every row starts on the same bank, and the 64 banks are the 16
+// slots of a row.  A 16-lane phase of a K-fragment read (16 rows, one
+// chunk) then hits 16 distinct slots; a 32-lane phase of a V^T transpose
+// read (4 consecutive rows, 4 consecutive chunks) puts each row in its own
+// 4-slot group.  Both are conflict-free.
+__device__ __forceinline__ int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
 
 __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillVarlen a) {
   __shared__ __align__(16) char smem[4 * kTileBytes];   // 2 x (K tile, V tile)
