@@ -119,23 +119,44 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillVarlen a) {
     lane_off[jj] = uint32_t((row & 15) * tok_bytes + 16 * ((lane & 15) ^ swz(row)));
   }
   const int last16 = ((kv_end - 1) / 16) * 16;
+  // Scalar address math per load, kept small: the scalar unit is shared by
+  // the compute unit's four SIMDs, and a division plus 64-bit products per
+  // load would keep it busy for most of a tile.  Page and row of a key come
+  // from shifts when the block size is a power of two; byte offsets within a
+  // page fit 32 bits (a page is 2 x bs x Hkv x 256 bytes).
+  const bool bs_pow2 = (bs & (bs - 1)) == 0;
+  const int bs_shift = __builtin_ctz(unsigned(bs));
+  const uint32_t tok32 = uint32_t(tok_bytes);
+  const uint32_t page_bytes = 2u * uint32_t(bs) * tok32;   // one page: K rows, then V rows
+  const uint32_t kv32 = uint32_t(kv_bytes);                // V rows of a page, after its K rows
+  const uint32_t nblk = uint32_t(min(a.num_blocks, int64_t(INT32_MAX)));
   auto gload = [&](int tile, char* kdst) {
     char* vdst = kdst + kTileBytes;
+    // the four 16-key groups of the tile: page ids first (one wait for all)
+    uint32_t blk[4], in_page[4];
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const int key16 = min(tile * kBN + 16 * jj, last16);
+      const int page = bs_pow2 ? key16 >> bs_shift : key16 / bs;
+      in_page[jj] = uint32_t(key16 - page * bs);
+      blk[jj] = uint32_t(uniform_load(table + page));
+    }
+    const bool tail = tile * kBN + kBN > kv_end;   // wave-uniform
 #pragma unroll
     for (int jj = 0; jj < kTileLoads / 4; ++jj) {
-      const int j = wave + 4 * jj;
-      const int key16 = min(tile * kBN + 16 * (j >> 2), last16);
-      int64_t blk = uniform_load(table + key16 / bs);
-      blk = (blk < 0 || blk >= a.num_blocks) ? 0 : blk;
-      const char* base = cache_h + (blk * 2 * bs + (key16 - (key16 / bs) * bs)) * tok_bytes;
-      uint32_t off = lane_off[jj];
-      if (key16 + 15 >= kv_end) {   // last group: keys past kv_end re-read key kv_end - 1
+      const int j = wave + 4 * jj;   // load j: rows 4 j .. 4 j + 3 of group j / 4 = jj (4 waves)
+      const uint32_t b = blk[jj] < nblk ? blk[jj] : 0u;   // negative ids wrap high
+      const char* base = cache_h + uint64_t(b) * page_bytes;
+      uint32_t off = lane_off[jj] + in_page[jj] * tok32;
+      if (tail) {   // keys past kv_end re-read key kv_end - 1
+        const int key16 = min(tile * kBN + 16 * jj, last16);
         const int row = 4 * j + (lane >> 4);
-        off = uint32_t(min(row & 15, kv_end - 1 - key16) * tok_bytes + 16 * ((lane & 15) ^ swz(row)));
+        off = in_page[jj] * tok32 +
+              uint32_t(min(row & 15, kv_end - 1 - key16) * tok_bytes + 16 * ((lane & 15) ^ swz(row)));
       }
       typedef __attribute__((address_space(3))) void* lds_ptr;
       __builtin_amdgcn_global_load_lds(base + off, (lds_ptr)(kdst + 1024 * j), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(base + kv_bytes + off, (lds_ptr)(vdst + 1024 * j), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(base + kv32 + off, (lds_ptr)(vdst + 1024 * j), 16, 0, 0);
     }
   };
   auto gwait = [&]() { __builtin_amdgcn_s_waitcnt(0x0F70); };   // vmcnt(0)
