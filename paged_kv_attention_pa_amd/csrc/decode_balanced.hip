@@ -88,21 +88,30 @@ __global__ __launch_bounds__(64 * kHeads, 1) void decode_balanced_kernel(DecodeB
   // K (plane 0) or V (plane kv_bytes) pieces of chunk p.  Tokens past the
   // request's end re-read its last token (finite data, masked below); the
   // loads are unconditional so the waits stay exact.
+  // The scalar address math stays small (the scalar unit is shared by the
+  // compute unit's four SIMDs): page of a token by a shift when the block
+  // size is a power of two, byte offsets within a page in 32 bits.
+  const bool bs_pow2 = (bs & (bs - 1)) == 0;
+  const int bs_shift = __builtin_ctz(unsigned(bs));
+  const uint64_t page_bytes = 2 * uint64_t(bs) * uint64_t(tok_bytes);
+  const uint32_t tok32 = uint32_t(tok_bytes);
+  const uint32_t nblk = uint32_t(min(a.num_blocks, int64_t(INT32_MAX)));
   auto load_half = [&](const ChunkPos& p, int64_t plane, u32x4_t (&dst)[8]) {
     const int32_t* table = a.block_table + int64_t(p.r) * a.max_blocks;
     const int len = max(p.len, 1);   // positions always hold keys; keeps every index >= 0
+    const char* base_p = cache_b + plane;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int I = wave + waves * i;
       const int lin = I * 1024 + 16 * lane;
       const int tl_first = (I * 1024) >> sh;                       // first token of the piece
       const int tok_first = min(p.lc * kChunk + tl_first, len - 1);
-      int64_t blk = uniform_load(table + tok_first / bs);
-      blk = (blk < 0 || blk >= a.num_blocks) ? 0 : blk;
-      const int page0 = (tok_first / bs) * bs;
+      const int page = bs_pow2 ? tok_first >> bs_shift : tok_first / bs;
+      uint32_t blk = uint32_t(uniform_load(table + page));
+      blk = blk < nblk ? blk : 0u;   // negative ids wrap high
       const int tok = min(p.lc * kChunk + (lin >> sh), len - 1);
       const int byte = lin & ((1 << sh) - 1);
-      dst[i] = load16(cache_b + plane + (blk * 2 * bs + (tok - page0)) * tok_bytes + byte);
+      dst[i] = load16(base_p + blk * page_bytes + (uint32_t(tok - page * bs) * tok32 + uint32_t(byte)));
     }
   };
   // LDS position of this lane's piece i (head tile, token row, chunk)
