@@ -231,13 +231,15 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillVarlen a) {
     auto update = [&](auto masked_tag) {
       constexpr bool kMasked = decltype(masked_tag)::value;
       if constexpr (kMasked) {
+        // key = key0 + 4 (l / 32) + c with a compile-time c per register:
+        // visible iff c <= lim (one compare per score)
+        const int lim = (a.causal ? min(kv_end - 1, row_abs) : kv_end - 1) - key0 - 4 * (lane >> 5);
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
-            const int key = key0 + hh * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-            const bool vis = key < kv_end && (!a.causal || key <= row_abs);
-            s[hh][i] = vis ? s[hh][i] : -INFINITY;
+            const int c = hh * 32 + 8 * (i >> 2) + (i & 3);
+            s[hh][i] = c <= lim ? s[hh][i] : -INFINITY;
           }
       }
       float tmax = -INFINITY;
