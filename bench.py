@@ -5,8 +5,9 @@ A step is one pass of the whole path over one synthetic batch: the new-token
 cache write, the attention kernel(s) and, for split-KV decode, the LSE merge.
 The headline line measures the Llama-3-8B-shaped GQA decode (64 requests,
 seq_len U[512, 8192], 32 q / 8 kv heads, d=128, bf16, block 16) in HBM GB/s;
-the four other workloads are measured the same way and reported under
-"workloads".  Inputs are generated on the host by ``workloads.py`` (seeded),
+the other workloads (tiny fp32 decode, chunked prefill, long-context decode,
+MLA decode, a mixed prefill + decode batch) are measured the same way and
+reported under "workloads".  Inputs are generated on the host by ``workloads.py`` (seeded),
 uploaded once, and resident in HBM before any timed region.
 
 Timing: W untimed warm-up steps, then K steps bracketed by
@@ -189,6 +190,54 @@ def mla_case(b, name):
                 "mla_decode.hip", info)
 
 
+def mixed_case(b, name):
+    """A planned mixed batch: decode group (token-balanced schedule) then the
+    prefill group, one plan.  Its roofline is a time: the decode group's
+    algorithmic bytes at peak HBM bandwidth plus the prefill group's flops at
+    peak MFMA rate, the two kernels running one after the other."""
+    import torch
+    import paged_kv_attention_pa_amd as pa
+    import workloads as W
+    cache, q = _dev(b.cache), _dev(b.q)
+    bt, sl, qsl = _dev(b.block_table), _dev(b.seq_lens), _dev(b.query_start_loc)
+    kn, vn, sm = _dev(b.k_new), _dev(b.v_new), _dev(b.slot_mapping)
+    plan = pa.plan_mixed(b.query_start_loc, b.seq_lens, b.num_q_heads, b.num_kv_heads,
+                         b.head_dim, b.block_size, b.block_table.shape[1])
+    ws = torch.empty(max(1, (plan.workspace_bytes + 3) // 4), dtype=torch.float32, device="cuda")
+    out = torch.empty_like(q)
+    lse = torch.empty(b.q.shape[:2], dtype=torch.float32, device="cuda")
+
+    def step():
+        pa.mixed_attention(plan, q, cache, bt, qsl, sl, b.scale, k=kn, v=vn, slot_mapping=sm,
+                           workspace=ws, out=out, lse=lse)
+
+    def kernel():
+        pa.mixed_attention(plan, q, cache, bt, qsl, sl, b.scale, workspace=ws, out=out, lse=lse)
+
+    nd = plan.num_decode
+    e, row = b.elem_bytes, b.num_kv_heads * b.head_dim * b.elem_bytes
+    dec_bytes = (int(b.seq_lens[:nd].sum()) * row * 2 + 2 * nd * b.num_q_heads * b.head_dim * e
+                 + int(((b.seq_lens[:nd].astype(int) + b.block_size - 1) // b.block_size).sum()) * 4)
+    pf_flops = 0
+    for L, S in zip(b.q_lens[nd:], b.seq_lens[nd:]):
+        L, S = int(L), int(S)
+        pf_flops += 2 * (L * (S - L) + L * (L + 1) // 2) * b.num_q_heads * 2 * b.head_dim
+    by = W.gqa_bytes(b)
+    case = Case(name, step, kernel, by["total"], W.gqa_flops(b), by["total"] - by["write"],
+                W.gqa_flops(b), "hbm+mfma", "decode_balanced_kernel + merge + prefill_kernel",
+                "api.cpp",
+                {"num_seqs": b.num_seqs, "num_decode": nd, "prefill_tokens": plan.prefill_tokens,
+                 "num_q_heads": b.num_q_heads, "num_kv_heads": b.num_kv_heads,
+                 "head_dim": b.head_dim, "block_size": b.block_size,
+                 "max_decode_seq_len": plan.max_decode_seq_len,
+                 "max_query_len": plan.max_query_len, "max_seq_len": plan.max_seq_len,
+                 "decode_schedule": f"{plan.decode_ranges} token-balanced ranges"
+                 if plan.decode_ranges else f"{plan.decode_splits} splits",
+                 "decode_bytes": dec_bytes, "prefill_flops": pf_flops})
+    case.roof_s = dec_bytes / (PEAK_HBM_GBS * 1e9) + pf_flops / (PEAK_BF16_TFLOPS * 1e12)
+    return case
+
+
 def build_cases(only):
     import workloads as W
     makers = {
@@ -199,6 +248,7 @@ def build_cases(only):
         "long_context_split_kv_decode_bf16": lambda: gqa_decode_case(
             W.long_context_decode(), 0, "long_context_split_kv_decode_bf16"),
         "mla_latent_decode_bf16": lambda: mla_case(W.mla_decode_batch(), "mla_latent_decode_bf16"),
+        W.MIXED: lambda: mixed_case(W.mixed_batch(), W.MIXED),
     }
     names = [HEADLINE] + [n for n in makers if n != HEADLINE]
     if only is not None:
@@ -284,6 +334,15 @@ def traffic_for(case):
 
 
 def roofline(case, kern_s):
+    if case.bound == "hbm+mfma":
+        # a time roofline: each group at its own roof, one after the other
+        return {"bound": case.bound, "kernel": case.kernel_name,
+                "achieved": round(kern_s * 1e3, 4), "peak": round(case.roof_s * 1e3, 4),
+                "unit": "ms (measured vs roofline time)", "frac": round(case.roof_s / kern_s, 4),
+                "traffic": None, "kernel_ms": round(kern_s * 1e3, 4),
+                "algorithmic_bytes": int(case.kern_bytes), "algorithmic_flops": int(case.kern_flops),
+                "kernel_GBps": round(case.kern_bytes / kern_s / 1e9, 1),
+                "kernel_TFLOPs": round(case.kern_flops / kern_s / 1e12, 2)}
     if case.bound == "hbm":
         achieved = case.kern_bytes / kern_s / 1e9
         peak, unit = PEAK_HBM_GBS, "GB/s"

@@ -344,6 +344,71 @@ pa_status_t pa_lse_merge(const float* part, int num_rows, int num_heads,
                          int num_splits, int head_dim_v, pa_dtype_t out_dtype,
                          void* out, float* lse, hipStream_t stream);
 
+/* ---------------------------------------------------------------------------
+ * Mixed batches: plan once, run per layer.
+ *
+ * Prefill and decode stress a kernel differently (long query chunks are a
+ * matrix product, single-token decode is a bandwidth-bound gather), so a
+ * backend splits a mixed batch into its decode requests and the rest, and
+ * the runner orders the batch decode-first so that the two groups are
+ * contiguous ("Attention Backends", section "Two kernels inside one attention
+ * call").  The split and the decode group's work partition depend only on
+ * the request lengths, so they are worked out once per batch and reused by
+ * every layer, whose run then only reads its own q / k / v and cache
+ * ("第 1 章 注意力后端", §4.2: Plan and Run, the plan reused across layers).
+ *
+ * pa_plan_mixed (host only, no device work) reads HOST copies of
+ * query_start_loc [num_seqs + 1] and seq_lens [num_seqs] and fills *plan:
+ * the decode group is the longest leading run of requests with exactly one
+ * query row (later one-row requests are computed with the prefill group,
+ * which gives the same result); the prefill group is every request after it.
+ * Checks: query_start_loc[0] = 0 and non-decreasing; L_r <= seq_lens[r] <=
+ * max_blocks_per_seq * block_size; the head configuration is one that
+ * pa_decode and pa_prefill_varlen support (head_dim 128, num_q_heads /
+ * num_kv_heads in {1, 2, 4, 8}); block_size a multiple of 16.
+ * num_cus: compute units the decode group's schedule is sized for (as
+ * pa_decode's automatic choice: one pass, n splits, or token-balanced
+ * ranges); 0 = the current device's.  The run follows the plan's schedule
+ * whatever device it is on.  plan->workspace_bytes is the device scratch
+ * pa_mixed_attention needs (16-byte aligned).  On error *plan is all zero.
+ *
+ * pa_mixed_attention enqueues, in order: the new-token write of all
+ * plan->num_tokens rows (if k, v, slot_mapping are given), the decode group
+ * (pa_decode with the plan's split count, or pa_decode_balanced + its merge
+ * with the plan's ranges), and the prefill group as pa_prefill_varlen
+ * (causal) does it.  Every argument is checked before anything is enqueued.  Arguments as in pa_prefill_varlen
+ * (q, k, v, out [num_tokens, ...], lse [num_tokens, num_q_heads] or NULL),
+ * with num_seqs, num_tokens, head counts, block_size, max_blocks_per_seq and
+ * the length maxima taken from the plan, which must have been made from the
+ * same batch.  Supported: PA_BF16.
+ * ------------------------------------------------------------------------- */
+typedef struct {
+  int num_seqs;            /* requests in the batch */
+  int num_tokens;          /* query rows: query_start_loc[num_seqs] */
+  int num_decode;          /* leading requests with one query row each */
+  int max_decode_seq_len;  /* max seq_lens over the decode group */
+  int prefill_tokens;      /* query rows of the prefill group */
+  int max_query_len;       /* max L_r over the prefill group */
+  int max_seq_len;         /* max seq_lens over the prefill group */
+  int num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq;
+  int decode_ranges;       /* token-balanced ranges of the decode group, 0 if unsplit or split */
+  int decode_splits;       /* split count of the decode group (1 = one pass) */
+  size_t workspace_bytes;  /* device scratch of pa_mixed_attention */
+} pa_mixed_plan_t;
+
+pa_status_t pa_plan_mixed(const int32_t* query_start_loc_host, const int32_t* seq_lens_host,
+                          int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                          int block_size, int max_blocks_per_seq, int num_cus,
+                          pa_mixed_plan_t* plan);
+
+pa_status_t pa_mixed_attention(const pa_mixed_plan_t* plan, pa_dtype_t dtype,
+                               const void* q, const void* k, const void* v,
+                               void* kv_cache, int64_t num_blocks,
+                               const int32_t* block_table, const int64_t* slot_mapping,
+                               const int32_t* query_start_loc, const int32_t* seq_lens,
+                               float scale, void* workspace, size_t workspace_bytes,
+                               void* out, float* lse, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -46,6 +46,9 @@ _SIGNATURES = {
     "pa_mla_decode_balanced": (_i32, [_vp, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _i32, _vp,
                                       _i32, _vp, _i32, _i32, _i32, _i32, _f32, _i32, _vp, _sz,
                                       _vp, _vp, _vp]),
+    "pa_plan_mixed": (_i32, [_vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp]),
+    "pa_mixed_attention": (_i32, [_vp, _i32, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _vp, _vp, _f32,
+                                  _vp, _sz, _vp, _vp, _vp]),
 }
 EXPORTED_SYMBOLS = tuple(_SIGNATURES)
 
@@ -119,6 +122,43 @@ def decode_balanced_workspace_bytes(num_seqs: int, num_heads: int, head_dim_v: i
 
 def device_num_cus() -> int:
     return library().pa_device_num_cus()
+
+
+class MixedPlan(C.Structure):
+    """pa_mixed_plan_t: the split of a mixed batch into its leading decode
+    requests and the prefill rest, with the decode group's schedule."""
+
+    _fields_ = [(n, C.c_int) for n in (
+        "num_seqs", "num_tokens", "num_decode", "max_decode_seq_len", "prefill_tokens",
+        "max_query_len", "max_seq_len", "num_q_heads", "num_kv_heads", "head_dim",
+        "block_size", "max_blocks_per_seq", "decode_ranges", "decode_splits")] + [
+        ("workspace_bytes", C.c_size_t)]
+
+    def __repr__(self):
+        return "MixedPlan(" + ", ".join(f"{n}={getattr(self, n)}" for n, _ in self._fields_) + ")"
+
+
+def _host_i32(x, name):
+    """A host int32 ctypes array from a list, numpy array or CPU tensor."""
+    if hasattr(x, "is_cuda"):
+        _need(not x.is_cuda, f"{name}: pa_plan_mixed reads host copies (got a GPU tensor)")
+        x = x.tolist()
+    vals = [int(t) for t in x]
+    return (C.c_int32 * max(len(vals), 1))(*vals), len(vals)
+
+
+def plan_mixed(query_start_loc, seq_lens, num_q_heads: int, num_kv_heads: int, head_dim: int,
+               block_size: int, max_blocks_per_seq: int, num_cus: int = 0) -> MixedPlan:
+    """Host-only plan of a mixed batch (pa_plan_mixed) from host copies of
+    query_start_loc [N + 1] and seq_lens [N]."""
+    qsl, nq = _host_i32(query_start_loc, "query_start_loc")
+    sl, n = _host_i32(seq_lens, "seq_lens")
+    _need(nq == n + 1, "query_start_loc must have num_seqs + 1 entries")
+    plan = MixedPlan()
+    _check(library().pa_plan_mixed(qsl, sl, n, int(num_q_heads), int(num_kv_heads),
+                                   int(head_dim), int(block_size), int(max_blocks_per_seq),
+                                   int(num_cus), C.byref(plan)))
+    return plan
 
 
 # ------------------------------------------------------------ marshalling
@@ -306,6 +346,39 @@ def prefill_varlen(q, kv_cache, block_table, query_start_loc, seq_lens, max_quer
                                        int(max_query_len), int(max_seq_len), Hq, hkv, D,
                                        float(scale), 1 if causal else 0, _ptr(out), _ptr(lse),
                                        _stream(stream)))
+    return out, lse
+
+
+def mixed_attention(plan: MixedPlan, q, kv_cache, block_table, query_start_loc, seq_lens,
+                    scale: float, k=None, v=None, slot_mapping=None, workspace=None, out=None,
+                    lse=None, return_lse: bool = True, stream=None):
+    """One layer of a planned mixed batch (pa_mixed_attention): q [T, Hq, D]
+    with the plan's decode requests first; returns (out [T, Hq, D], lse [T, Hq])."""
+    torch = _torch()
+    _dev(q, kv_cache, block_table, query_start_loc, seq_lens, k, v, slot_mapping, workspace,
+         out, lse)
+    _int_tensor(block_table, "int32", "block_table")
+    _int_tensor(seq_lens, "int32", "seq_lens")
+    _int_tensor(query_start_loc, "int32", "query_start_loc")
+    T, Hq, D = q.shape
+    nb, _, bs, hkv, _ = kv_cache.shape
+    _need(T == plan.num_tokens and seq_lens.numel() == plan.num_seqs and
+          query_start_loc.numel() == plan.num_seqs + 1, "tensors do not match the plan's batch")
+    _need(Hq == plan.num_q_heads and hkv == plan.num_kv_heads and D == plan.head_dim and
+          bs == plan.block_size and block_table.shape[1] == plan.max_blocks_per_seq,
+          "tensor shapes do not match the plan")
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and return_lse:
+        lse = torch.empty((T, Hq), dtype=torch.float32, device=q.device)
+    if workspace is None and plan.workspace_bytes:
+        workspace = torch.empty(plan.workspace_bytes, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(library().pa_mixed_attention(C.byref(plan), _dtype_code(q), _ptr(q), _ptr(k), _ptr(v),
+                                        _ptr(kv_cache), nb, _ptr(block_table), _ptr(slot_mapping),
+                                        _ptr(query_start_loc), _ptr(seq_lens), float(scale),
+                                        _ptr(workspace), ws_bytes, _ptr(out), _ptr(lse),
+                                        _stream(stream)))
     return out, lse
 
 

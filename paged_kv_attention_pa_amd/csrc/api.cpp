@@ -583,4 +583,154 @@ pa_status_t pa_lse_merge(const float* part, int num_rows, int num_heads,
   return ok();
 }
 
+// ---------------------------------------------------------------------------
+pa_status_t pa_plan_mixed(const int32_t* qsl, const int32_t* seq_lens, int num_seqs,
+                          int num_q_heads, int num_kv_heads, int head_dim, int block_size,
+                          int max_blocks_per_seq, int num_cus, pa_mixed_plan_t* plan) {
+  PA_REQUIRE(plan != nullptr, PA_ERR_INVALID, "plan must be non-null");
+  std::memset(plan, 0, sizeof(*plan));
+  PA_REQUIRE(num_seqs >= 0, PA_ERR_INVALID, "num_seqs must be >= 0 (got %d)", num_seqs);
+  PA_REQUIRE(num_seqs == 0 || (qsl && seq_lens), PA_ERR_INVALID,
+             "query_start_loc and seq_lens (host copies) must be non-null");
+  PA_REQUIRE(block_size > 0 && block_size % 16 == 0, PA_ERR_INVALID,
+             "block_size must be a positive multiple of 16 (got %d)", block_size);
+  PA_REQUIRE(max_blocks_per_seq > 0, PA_ERR_INVALID, "max_blocks_per_seq must be > 0");
+  PA_REQUIRE(num_q_heads > 0 && num_kv_heads > 0 && num_q_heads % num_kv_heads == 0,
+             PA_ERR_INVALID, "num_q_heads (%d) must be a positive multiple of num_kv_heads (%d)",
+             num_q_heads, num_kv_heads);
+  PA_REQUIRE(head_dim == 128, PA_ERR_UNSUPPORTED, "mixed batches support head_dim 128 (got %d)",
+             head_dim);
+  PA_REQUIRE(is_pow2_group(num_q_heads / num_kv_heads), PA_ERR_UNSUPPORTED,
+             "num_q_heads / num_kv_heads must be in {1, 2, 4, 8} (got %d)",
+             num_q_heads / num_kv_heads);
+  PA_REQUIRE(num_cus >= 0, PA_ERR_INVALID, "num_cus must be >= 0");
+  int cus = num_cus;
+  if (cus == 0) {
+    cus = pa_device_num_cus();
+    if (cus <= 0) return fail(PA_ERR_HIP, "cannot query the device's compute units");
+  }
+  const int64_t cap = int64_t(max_blocks_per_seq) * block_size;
+  PA_REQUIRE(num_seqs == 0 || qsl[0] == 0, PA_ERR_INVALID, "query_start_loc[0] must be 0");
+  int nd = 0;
+  bool in_decode = true;
+  pa_mixed_plan_t p{};   // copied to *plan only when every check has passed
+  for (int r = 0; r < num_seqs; ++r) {
+    const int64_t L = int64_t(qsl[r + 1]) - qsl[r];
+    const int S = seq_lens[r];
+    PA_REQUIRE(L >= 0, PA_ERR_INVALID, "query_start_loc must be non-decreasing (request %d)", r);
+    PA_REQUIRE(S >= L && S <= cap, PA_ERR_INVALID,
+               "request %d: seq_len %d must be in [query rows %lld, max_blocks_per_seq * "
+               "block_size]", r, S, (long long)L);
+    if (in_decode && L == 1) {
+      ++nd;
+      p.max_decode_seq_len = S > p.max_decode_seq_len ? S : p.max_decode_seq_len;
+      continue;
+    }
+    in_decode = false;
+    p.max_query_len = int(L) > p.max_query_len ? int(L) : p.max_query_len;
+    p.max_seq_len = S > p.max_seq_len ? S : p.max_seq_len;
+  }
+  p.num_seqs = num_seqs;
+  p.num_tokens = num_seqs ? qsl[num_seqs] : 0;
+  p.num_decode = nd;
+  p.prefill_tokens = p.num_tokens - nd;
+  p.num_q_heads = num_q_heads;
+  p.num_kv_heads = num_kv_heads;
+  p.head_dim = head_dim;
+  p.block_size = block_size;
+  p.max_blocks_per_seq = max_blocks_per_seq;
+  // the decode group's schedule: pa_decode's automatic choice (bf16)
+  p.decode_splits = 1;
+  if (nd > 0) {
+    const int n = pa_num_kv_splits(p.max_decode_seq_len, cus);
+    const int P = split_tokens_for(p.max_decode_seq_len, n, block_size);
+    if (used_splits(p.max_decode_seq_len, P) > 1) {
+      p.decode_splits = n;
+      if (balanced_heads_ok(num_kv_heads)) {
+        p.decode_ranges = pa_decode_balanced_num_ranges(num_kv_heads, cus);
+        p.workspace_bytes = balanced_bytes(nd, num_q_heads, head_dim, p.decode_ranges);
+        PA_REQUIRE(int64_t(nd) * ((cap + 31) / 32) <= INT_MAX, PA_ERR_UNSUPPORTED,
+                   "decode group too large for the balanced schedule");
+      } else {
+        p.workspace_bytes = pa_decode_workspace_bytes(nd, num_q_heads, head_dim, n);
+      }
+      PA_REQUIRE(p.workspace_bytes > 0, PA_ERR_INVALID, "decode workspace size overflows");
+    }
+  }
+  *plan = p;
+  return ok();
+}
+
+pa_status_t pa_mixed_attention(const pa_mixed_plan_t* plan, pa_dtype_t dtype,
+                               const void* q, const void* k, const void* v,
+                               void* kv_cache, int64_t num_blocks,
+                               const int32_t* block_table, const int64_t* slot_mapping,
+                               const int32_t* query_start_loc, const int32_t* seq_lens,
+                               float scale, void* workspace, size_t workspace_bytes,
+                               void* out, float* lse, hipStream_t stream) {
+  PA_REQUIRE(plan != nullptr, PA_ERR_INVALID, "plan must be non-null");
+  const pa_mixed_plan_t& p = *plan;
+  PA_REQUIRE(dtype == PA_BF16, PA_ERR_UNSUPPORTED, "mixed batches support PA_BF16");
+  PA_REQUIRE(scale_ok(scale), PA_ERR_INVALID, "scale must be finite and >= 0");
+  PA_REQUIRE(p.num_seqs >= 0 && p.num_decode >= 0 && p.num_decode <= p.num_seqs &&
+                 p.num_tokens >= p.num_decode && p.prefill_tokens == p.num_tokens - p.num_decode,
+             PA_ERR_INVALID, "plan is not one made by pa_plan_mixed");
+  pa_status_t st = check_common_cache(num_blocks, p.block_size, block_table, p.max_blocks_per_seq,
+                                      seq_lens, p.num_seqs, 0);
+  if (st != PA_OK) return st;
+  PA_REQUIRE((k == nullptr) == (v == nullptr), PA_ERR_INVALID, "k and v must both be given or both NULL");
+  PA_REQUIRE(k == nullptr || slot_mapping != nullptr, PA_ERR_INVALID, "k/v given without slot_mapping");
+  PA_REQUIRE(slot_mapping == nullptr || k != nullptr, PA_ERR_INVALID, "slot_mapping given without k/v");
+  if (p.num_seqs == 0 || p.num_tokens == 0) return ok();
+  PA_REQUIRE(q && kv_cache && out && query_start_loc, PA_ERR_INVALID,
+             "q, kv_cache, out and query_start_loc must be non-null");
+  PA_REQUIRE(p.decode_splits >= 1 && p.decode_ranges >= 0 &&
+                 (p.decode_ranges == 0 || p.decode_splits > 1),
+             PA_ERR_INVALID, "plan is not one made by pa_plan_mixed");
+  if (p.num_decode > 0 && p.decode_ranges > 0) {
+    st = check_balanced(p.num_decode, p.num_q_heads, p.head_dim, p.max_blocks_per_seq,
+                        p.block_size, p.decode_ranges, workspace, workspace_bytes);
+    if (st != PA_OK) return st;
+  } else if (p.num_decode > 0 && p.decode_splits > 1) {
+    const size_t need =
+        pa_decode_workspace_bytes(p.num_decode, p.num_q_heads, p.head_dim, p.decode_splits);
+    PA_REQUIRE(workspace != nullptr && workspace_bytes >= need, PA_ERR_WORKSPACE,
+               "workspace of %zu bytes needed (got %zu)", need, workspace_bytes);
+  }
+  if (k) {
+    st = pa_cache_write(PA_LAYOUT_KV, dtype, k, int64_t(p.num_kv_heads) * p.head_dim, v,
+                        int64_t(p.num_kv_heads) * p.head_dim, kv_cache, num_blocks, p.block_size,
+                        p.num_kv_heads, p.head_dim, slot_mapping, p.num_tokens, stream);
+    if (st != PA_OK) return st;
+  }
+  // Rows 0 .. num_decode - 1 are the decode requests' queries, run with the
+  // plan's schedule (not re-derived from the current device).
+  if (p.num_decode > 0 && p.decode_ranges > 0) {
+    st = pa_decode_balanced(q, kv_cache, num_blocks, p.block_size, block_table,
+                            p.max_blocks_per_seq, seq_lens, p.num_decode, p.num_q_heads,
+                            p.num_kv_heads, p.head_dim, scale, p.decode_ranges, workspace,
+                            workspace_bytes, out, lse, stream);
+    if (st != PA_OK) return st;
+    st = pa_decode_balanced_merge(workspace, workspace_bytes, p.num_decode, p.num_q_heads,
+                                  p.head_dim, p.decode_ranges, out, lse, stream);
+    if (st != PA_OK) return st;
+  } else if (p.num_decode > 0) {
+    st = pa_decode(dtype, q, nullptr, nullptr, kv_cache, num_blocks, p.block_size, block_table,
+                   p.max_blocks_per_seq, nullptr, seq_lens, p.num_decode, p.max_decode_seq_len,
+                   p.num_q_heads, p.num_kv_heads, p.head_dim, scale, p.decode_splits, workspace,
+                   workspace_bytes, out, lse, stream);
+    if (st != PA_OK) return st;
+  }
+  if (p.num_decode < p.num_seqs) {   // query rows stay absolute: same q, out, lse
+    const int nd = p.num_decode;
+    st = pa_prefill_varlen(dtype, q, nullptr, nullptr, kv_cache, num_blocks, p.block_size,
+                           block_table + int64_t(nd) * p.max_blocks_per_seq, p.max_blocks_per_seq,
+                           nullptr, query_start_loc + nd, seq_lens + nd, p.num_seqs - nd,
+                           p.num_tokens, p.max_query_len, p.max_seq_len, p.num_q_heads,
+                           p.num_kv_heads, p.head_dim, scale, 1, out, lse, stream);
+    if (st != PA_OK) return st;
+  }
+  return ok();
+}
+
 }  // extern "C"

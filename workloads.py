@@ -300,6 +300,7 @@ WORKLOADS = {
     3: "long_context_split_kv_decode_bf16",
     4: "mla_latent_decode_bf16",
 }
+MIXED = "mixed_prefill_decode_bf16"
 
 
 def tiny_decode() -> GqaBatch:
@@ -341,6 +342,21 @@ def mla_decode_batch(seed: int = 1005, batch: int = 128) -> MlaBatch:
     seq = rng.integers(1024, 8192, size=batch, endpoint=True)
     return make_mla(rng, seq, 128, 512, 64, 64, 1.0 / math.sqrt(192),
                     name=WORKLOADS[4])
+
+
+def mixed_batch(seed: int = 1006, decode: int = 64, prefill: int = 4) -> GqaBatch:
+    """A serving step that mixes both phases, decode requests first: 64
+    decode requests (seq_len ~ U{512..8192}) then 4 prefill chunks (chunk ~
+    U{64..2048} over context ~ U{0..4096}); 32 q / 8 kv heads, d=128, bf16,
+    block 16 -- the decode and chunked-prefill workloads' distributions in
+    one batch."""
+    rng = np.random.default_rng(seed)
+    dec = rng.integers(512, 8192, size=decode, endpoint=True)
+    L = rng.integers(64, 2048, size=prefill, endpoint=True)
+    C = rng.integers(0, 4096, size=prefill, endpoint=True)
+    q_lens = np.concatenate([np.ones(decode, dtype=np.int64), L])
+    seq = np.concatenate([dec, C + L])
+    return make_gqa(rng, q_lens, seq, 32, 8, 128, 16, BF16, name=MIXED)
 
 
 # --------------------------------------------------------------------------
