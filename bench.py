@@ -6,7 +6,7 @@ cache write, the attention kernel(s) and, for split-KV decode, the LSE merge.
 The headline line measures the Llama-3-8B-shaped GQA decode (64 requests,
 seq_len U[512, 8192], 32 q / 8 kv heads, d=128, bf16, block 16) in HBM GB/s;
 the other workloads (tiny fp32 decode, chunked prefill, long-context decode,
-MLA decode, a mixed prefill + decode batch) are measured the same way and
+MLA decode, a mixed prefill + decode batch, a batch sharing a prefix) are measured the same way and
 reported under "workloads".  Inputs are generated on the host by ``workloads.py`` (seeded),
 uploaded once, and resident in HBM before any timed region.
 
@@ -238,6 +238,63 @@ def mixed_case(b, name):
     return case
 
 
+def cascade_case(b, name):
+    """A batch whose requests share their first pages, run as a cascade (the
+    prefix once for every query row, each request's own keys, the merge).
+    Priced against HBM: the prefix's K/V counted once, each request's own
+    K/V once.  The plain decode of the same batch (the prefix read once per
+    request) is timed beside it."""
+    import numpy as np
+    import torch
+    import paged_kv_attention_pa_amd as pa
+    cache, q = _dev(b.cache), _dev(b.q)
+    bt, sl, qsl = _dev(b.block_table), _dev(b.seq_lens), _dev(b.query_start_loc)
+    kn, vn, sm = _dev(b.k_new), _dev(b.v_new), _dev(b.slot_mapping)
+    P = b.meta["prefix_blocks"]
+    plan = pa.plan_cascade(b.query_start_loc, b.seq_lens, P, b.num_q_heads, b.num_kv_heads,
+                           b.head_dim, b.block_size, b.block_table.shape[1])
+    ws = torch.empty(max(1, plan.workspace_bytes), dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(q)
+    lse = torch.empty(b.q.shape[:2], dtype=torch.float32, device="cuda")
+
+    def step():
+        pa.cascade_attention(plan, q, cache, bt, qsl, sl, b.scale, k=kn, v=vn, slot_mapping=sm,
+                             workspace=ws, out=out, lse=lse)
+
+    def kernel():
+        pa.cascade_attention(plan, q, cache, bt, qsl, sl, b.scale, workspace=ws, out=out, lse=lse)
+
+    # the plain path over the same batch, for comparison
+    cus = pa.device_num_cus()
+    nr = pa.decode_balanced_num_ranges(b.num_kv_heads, cus)
+    pws = torch.empty(max(1, pa.decode_balanced_workspace_bytes(b.num_seqs, b.num_q_heads,
+                                                                b.head_dim, nr)),
+                      dtype=torch.uint8, device="cuda")
+    plain_s = time_kernel_events(
+        lambda: pa.decode(q, cache, bt, sl, b.max_seq_len, b.scale, workspace=pws, out=out,
+                          lse=lse), 20, 5)
+
+    e = b.elem_bytes
+    row = b.num_kv_heads * b.head_dim * e
+    Lp = P * b.block_size
+    own = b.seq_lens.astype(np.int64) - Lp
+    kv = (Lp + int(own.sum())) * row * 2
+    nblk = P + int(((own + b.block_size - 1) // b.block_size).sum())
+    qo = 2 * b.q.size * e + b.q.shape[0] * b.q.shape[1] * 4
+    kb = kv + qo + nblk * 4 + b.num_seqs * 8
+    wr = (b.k_new.size + b.v_new.size) * e * 2
+    fl = 2 * b.num_q_heads * 2 * b.head_dim * int(b.seq_lens.sum())
+    return Case(name, step, kernel, kb + wr + b.num_tokens * 8, fl, kb, fl, "hbm",
+                "suffix decode + prefix pass + merges", "prefill.hip",
+                {"num_seqs": b.num_seqs, "num_q_heads": b.num_q_heads,
+                 "num_kv_heads": b.num_kv_heads, "head_dim": b.head_dim,
+                 "block_size": b.block_size, "prefix_len": Lp,
+                 "own_keys": "U[512,4096]", "prefix_splits": plan.prefix_splits,
+                 "split_keys": plan.split_keys,
+                 "plain_decode_ms": round(plain_s * 1e3, 4),
+                 "plain_decode_reads_GB": round((int(b.seq_lens.sum()) * row * 2) / 1e9, 3)})
+
+
 def build_cases(only):
     import workloads as W
     makers = {
@@ -249,6 +306,7 @@ def build_cases(only):
             W.long_context_decode(), 0, "long_context_split_kv_decode_bf16"),
         "mla_latent_decode_bf16": lambda: mla_case(W.mla_decode_batch(), "mla_latent_decode_bf16"),
         W.MIXED: lambda: mixed_case(W.mixed_batch(), W.MIXED),
+        W.CASCADE: lambda: cascade_case(W.cascade_batch(), W.CASCADE),
     }
     names = [HEADLINE] + [n for n in makers if n != HEADLINE]
     if only is not None:

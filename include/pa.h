@@ -409,6 +409,63 @@ pa_status_t pa_mixed_attention(const pa_mixed_plan_t* plan, pa_dtype_t dtype,
                                float scale, void* workspace, size_t workspace_bytes,
                                void* out, float* lse, hipStream_t stream);
 
+/* ---------------------------------------------------------------------------
+ * Cascade (shared-prefix) attention.
+ *
+ * When every request of a batch starts with the same pages (a common system
+ * prompt), attention over those pages is computed once for all query rows and
+ * combined with each request's attention over the rest of its keys
+ * ("Attention Backends", section "Cascade attention": the scheduler counts
+ * the leading blocks common to all running requests; the shared part is
+ * processed once and the per-request parts separately; it applies only when
+ * every request shares the prefix).  The combination is the exact
+ * log-sum-exp merge of two disjoint key sets ("第 1 章 注意力后端", §3.1
+ * split-KV, §4.1 Figure 5c), so the result is the ordinary attention's up to
+ * rounding.
+ *
+ * pa_plan_cascade (host only) reads HOST copies of query_start_loc and
+ * seq_lens.  num_common_prefix_blocks = P: the first P entries of every
+ * block_table row are the same pages (the caller guarantees it; the prefix is
+ * read through row 0).  Checks, besides pa_plan_mixed's: every request's
+ * queries lie after the prefix (seq_lens[r] - L_r >= P * block_size, so
+ * every query row sees all of it) and P < max_blocks_per_seq.  The plan
+ * holds the mixed-batch plan of the suffixes (seq_lens - P * block_size, same
+ * rows), the prefix's key ranges and the workspace size.  P = 0 plans a
+ * plain mixed batch.
+ *
+ * pa_cascade_attention enqueues: the new-token write of all rows (if k, v,
+ * slot_mapping are given); the suffix lengths (a small kernel into the
+ * workspace); the suffix pass (pa_mixed_attention's kernels over block_table
+ * + P, out holding its result); the prefix pass (every query row against
+ * the prefix's keys, fp32 partials into the workspace); the merge into out
+ * and lse.  Arguments as in pa_mixed_attention.  Supported: PA_BF16,
+ * head_dim 128, num_q_heads / num_kv_heads in {1, 2, 4, 8}.
+ * ------------------------------------------------------------------------- */
+typedef struct {
+  pa_mixed_plan_t suffix;      /* the batch with the prefix's keys removed */
+  int prefix_blocks;           /* P */
+  int prefix_len;              /* P * block_size */
+  int prefix_splits;           /* key ranges of the prefix pass: about one work-group
+                                  per compute unit over (KV head, 128-row tile of the
+                                  num_tokens * G (token, group head) rows, range) */
+  int split_keys;              /* keys per range: a multiple of 64, at least 256 unless
+                                  the prefix is shorter */
+  size_t workspace_bytes;      /* device scratch of pa_cascade_attention */
+} pa_cascade_plan_t;
+
+pa_status_t pa_plan_cascade(const int32_t* query_start_loc_host, const int32_t* seq_lens_host,
+                            int num_seqs, int num_common_prefix_blocks, int num_q_heads,
+                            int num_kv_heads, int head_dim, int block_size,
+                            int max_blocks_per_seq, int num_cus, pa_cascade_plan_t* plan);
+
+pa_status_t pa_cascade_attention(const pa_cascade_plan_t* plan, pa_dtype_t dtype,
+                                 const void* q, const void* k, const void* v,
+                                 void* kv_cache, int64_t num_blocks,
+                                 const int32_t* block_table, const int64_t* slot_mapping,
+                                 const int32_t* query_start_loc, const int32_t* seq_lens,
+                                 float scale, void* workspace, size_t workspace_bytes,
+                                 void* out, float* lse, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

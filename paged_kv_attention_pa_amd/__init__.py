@@ -9,6 +9,7 @@ been built (``python -m paged_kv_attention_pa_amd.build``).
 Functions mirror the C entry points: ``cache_write``, ``decode``,
 ``prefill_varlen``, ``mla_decode``, ``lse_merge``, ``decode_balanced``,
 ``plan_mixed`` + ``mixed_attention`` (a mixed prefill/decode batch),
+``plan_cascade`` + ``cascade_attention`` (a batch sharing its first pages),
 ``mla_decode_balanced``, ``decode_balanced_merge``, plus the host helpers ``num_kv_splits``,
 ``mla_num_kv_splits``, ``decode_workspace_bytes``,
 ``decode_balanced_num_ranges``, ``decode_balanced_workspace_bytes``,
@@ -20,6 +21,7 @@ from ._binding import (  # noqa: F401
     cache_write, decode, decode_balanced, decode_balanced_merge,
     decode_balanced_num_ranges, decode_balanced_workspace_bytes,
     decode_workspace_bytes, device_num_cus, last_error, MixedPlan, mixed_attention, plan_mixed,
+    CascadePlan, cascade_attention, plan_cascade,
     library, library_path, lse_merge, mla_decode, mla_decode_balanced, mla_num_kv_splits,
     num_kv_splits, prefill_varlen,
 )

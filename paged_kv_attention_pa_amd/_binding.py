@@ -49,6 +49,9 @@ _SIGNATURES = {
     "pa_plan_mixed": (_i32, [_vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp]),
     "pa_mixed_attention": (_i32, [_vp, _i32, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _vp, _vp, _f32,
                                   _vp, _sz, _vp, _vp, _vp]),
+    "pa_plan_cascade": (_i32, [_vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp]),
+    "pa_cascade_attention": (_i32, [_vp, _i32, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _vp, _vp,
+                                    _f32, _vp, _sz, _vp, _vp, _vp]),
 }
 EXPORTED_SYMBOLS = tuple(_SIGNATURES)
 
@@ -138,6 +141,20 @@ class MixedPlan(C.Structure):
         return "MixedPlan(" + ", ".join(f"{n}={getattr(self, n)}" for n, _ in self._fields_) + ")"
 
 
+class CascadePlan(C.Structure):
+    """pa_cascade_plan_t: the mixed-batch plan of the suffixes plus the shared
+    prefix's key ranges."""
+
+    _fields_ = [("suffix", MixedPlan), ("prefix_blocks", C.c_int), ("prefix_len", C.c_int),
+                ("prefix_splits", C.c_int), ("split_keys", C.c_int),
+                ("workspace_bytes", C.c_size_t)]
+
+    def __repr__(self):
+        return (f"CascadePlan(prefix_blocks={self.prefix_blocks}, prefix_len={self.prefix_len}, "
+                f"prefix_splits={self.prefix_splits}, split_keys={self.split_keys}, "
+                f"workspace_bytes={self.workspace_bytes}, suffix={self.suffix!r})")
+
+
 def _host_i32(x, name):
     """A host int32 ctypes array from a list, numpy array or CPU tensor."""
     if hasattr(x, "is_cuda"):
@@ -158,6 +175,21 @@ def plan_mixed(query_start_loc, seq_lens, num_q_heads: int, num_kv_heads: int, h
     _check(library().pa_plan_mixed(qsl, sl, n, int(num_q_heads), int(num_kv_heads),
                                    int(head_dim), int(block_size), int(max_blocks_per_seq),
                                    int(num_cus), C.byref(plan)))
+    return plan
+
+
+def plan_cascade(query_start_loc, seq_lens, num_common_prefix_blocks: int, num_q_heads: int,
+                 num_kv_heads: int, head_dim: int, block_size: int, max_blocks_per_seq: int,
+                 num_cus: int = 0) -> CascadePlan:
+    """Host-only plan of a batch whose block-table rows share their first
+    num_common_prefix_blocks pages (pa_plan_cascade)."""
+    qsl, nq = _host_i32(query_start_loc, "query_start_loc")
+    sl, n = _host_i32(seq_lens, "seq_lens")
+    _need(nq == n + 1, "query_start_loc must have num_seqs + 1 entries")
+    plan = CascadePlan()
+    _check(library().pa_plan_cascade(qsl, sl, n, int(num_common_prefix_blocks), int(num_q_heads),
+                                     int(num_kv_heads), int(head_dim), int(block_size),
+                                     int(max_blocks_per_seq), int(num_cus), C.byref(plan)))
     return plan
 
 
@@ -354,6 +386,13 @@ def mixed_attention(plan: MixedPlan, q, kv_cache, block_table, query_start_loc, 
                     lse=None, return_lse: bool = True, stream=None):
     """One layer of a planned mixed batch (pa_mixed_attention): q [T, Hq, D]
     with the plan's decode requests first; returns (out [T, Hq, D], lse [T, Hq])."""
+    return _planned_call(library().pa_mixed_attention, plan, plan, q, kv_cache, block_table,
+                         query_start_loc, seq_lens, scale, k, v, slot_mapping, workspace, out,
+                         lse, return_lse, stream)
+
+
+def _planned_call(fn, plan, mp, q, kv_cache, block_table, query_start_loc, seq_lens, scale,
+                  k, v, slot_mapping, workspace, out, lse, return_lse, stream):
     torch = _torch()
     _dev(q, kv_cache, block_table, query_start_loc, seq_lens, k, v, slot_mapping, workspace,
          out, lse)
@@ -362,10 +401,10 @@ def mixed_attention(plan: MixedPlan, q, kv_cache, block_table, query_start_loc, 
     _int_tensor(query_start_loc, "int32", "query_start_loc")
     T, Hq, D = q.shape
     nb, _, bs, hkv, _ = kv_cache.shape
-    _need(T == plan.num_tokens and seq_lens.numel() == plan.num_seqs and
-          query_start_loc.numel() == plan.num_seqs + 1, "tensors do not match the plan's batch")
-    _need(Hq == plan.num_q_heads and hkv == plan.num_kv_heads and D == plan.head_dim and
-          bs == plan.block_size and block_table.shape[1] == plan.max_blocks_per_seq,
+    _need(T == mp.num_tokens and seq_lens.numel() == mp.num_seqs and
+          query_start_loc.numel() == mp.num_seqs + 1, "tensors do not match the plan's batch")
+    _need(Hq == mp.num_q_heads and hkv == mp.num_kv_heads and D == mp.head_dim and
+          bs == mp.block_size and block_table.shape[1] == mp.max_blocks_per_seq,
           "tensor shapes do not match the plan")
     if out is None:
         out = torch.empty_like(q)
@@ -374,12 +413,20 @@ def mixed_attention(plan: MixedPlan, q, kv_cache, block_table, query_start_loc, 
     if workspace is None and plan.workspace_bytes:
         workspace = torch.empty(plan.workspace_bytes, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(library().pa_mixed_attention(C.byref(plan), _dtype_code(q), _ptr(q), _ptr(k), _ptr(v),
-                                        _ptr(kv_cache), nb, _ptr(block_table), _ptr(slot_mapping),
-                                        _ptr(query_start_loc), _ptr(seq_lens), float(scale),
-                                        _ptr(workspace), ws_bytes, _ptr(out), _ptr(lse),
-                                        _stream(stream)))
+    _check(fn(C.byref(plan), _dtype_code(q), _ptr(q), _ptr(k), _ptr(v), _ptr(kv_cache), nb,
+              _ptr(block_table), _ptr(slot_mapping), _ptr(query_start_loc), _ptr(seq_lens),
+              float(scale), _ptr(workspace), ws_bytes, _ptr(out), _ptr(lse), _stream(stream)))
     return out, lse
+
+
+def cascade_attention(plan: CascadePlan, q, kv_cache, block_table, query_start_loc, seq_lens,
+                      scale: float, k=None, v=None, slot_mapping=None, workspace=None, out=None,
+                      lse=None, return_lse: bool = True, stream=None):
+    """One layer of a planned shared-prefix batch (pa_cascade_attention);
+    returns (out [T, Hq, D], lse [T, Hq])."""
+    return _planned_call(library().pa_cascade_attention, plan, plan.suffix, q, kv_cache,
+                         block_table, query_start_loc, seq_lens, scale, k, v, slot_mapping,
+                         workspace, out, lse, return_lse, stream)
 
 
 def mla_decode(q_nope, q_pe, kv_cache, block_table, seq_lens, max_seq_len: int, scale: float,

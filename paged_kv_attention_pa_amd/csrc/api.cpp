@@ -11,6 +11,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <new>
 
 #include "launch.hpp"
 
@@ -661,19 +662,25 @@ pa_status_t pa_plan_mixed(const int32_t* qsl, const int32_t* seq_lens, int num_s
   return ok();
 }
 
-pa_status_t pa_mixed_attention(const pa_mixed_plan_t* plan, pa_dtype_t dtype,
-                               const void* q, const void* k, const void* v,
-                               void* kv_cache, int64_t num_blocks,
-                               const int32_t* block_table, const int64_t* slot_mapping,
-                               const int32_t* query_start_loc, const int32_t* seq_lens,
-                               float scale, void* workspace, size_t workspace_bytes,
-                               void* out, float* lse, hipStream_t stream) {
-  PA_REQUIRE(plan != nullptr, PA_ERR_INVALID, "plan must be non-null");
-  const pa_mixed_plan_t& p = *plan;
+// Checks of a mixed run, all made before anything is enqueued.
+static pa_status_t mixed_check(const pa_mixed_plan_t& p, pa_dtype_t dtype, float scale,
+                               const void* q, const void* k, const void* v, const void* kv_cache,
+                               int64_t num_blocks, const int32_t* block_table,
+                               const int64_t* slot_mapping, const int32_t* query_start_loc,
+                               const int32_t* seq_lens, const void* workspace,
+                               size_t workspace_bytes, const void* out) {
   PA_REQUIRE(dtype == PA_BF16, PA_ERR_UNSUPPORTED, "mixed batches support PA_BF16");
   PA_REQUIRE(scale_ok(scale), PA_ERR_INVALID, "scale must be finite and >= 0");
+  const int64_t cap = int64_t(p.max_blocks_per_seq) * p.block_size;
   PA_REQUIRE(p.num_seqs >= 0 && p.num_decode >= 0 && p.num_decode <= p.num_seqs &&
-                 p.num_tokens >= p.num_decode && p.prefill_tokens == p.num_tokens - p.num_decode,
+                 p.num_tokens >= p.num_decode && p.prefill_tokens == p.num_tokens - p.num_decode &&
+                 p.head_dim == 128 && p.num_q_heads > 0 && p.num_kv_heads > 0 &&
+                 p.num_q_heads % p.num_kv_heads == 0 &&
+                 is_pow2_group(p.num_q_heads / p.num_kv_heads) && p.decode_splits >= 1 &&
+                 p.decode_ranges >= 0 && (p.decode_ranges == 0 || p.decode_splits > 1) &&
+                 p.max_query_len >= 0 && p.max_query_len <= p.num_tokens &&
+                 p.max_seq_len >= 0 && p.max_seq_len <= cap && p.max_decode_seq_len >= 0 &&
+                 p.max_decode_seq_len <= cap,
              PA_ERR_INVALID, "plan is not one made by pa_plan_mixed");
   pa_status_t st = check_common_cache(num_blocks, p.block_size, block_table, p.max_blocks_per_seq,
                                       seq_lens, p.num_seqs, 0);
@@ -684,9 +691,6 @@ pa_status_t pa_mixed_attention(const pa_mixed_plan_t* plan, pa_dtype_t dtype,
   if (p.num_seqs == 0 || p.num_tokens == 0) return ok();
   PA_REQUIRE(q && kv_cache && out && query_start_loc, PA_ERR_INVALID,
              "q, kv_cache, out and query_start_loc must be non-null");
-  PA_REQUIRE(p.decode_splits >= 1 && p.decode_ranges >= 0 &&
-                 (p.decode_ranges == 0 || p.decode_splits > 1),
-             PA_ERR_INVALID, "plan is not one made by pa_plan_mixed");
   if (p.num_decode > 0 && p.decode_ranges > 0) {
     st = check_balanced(p.num_decode, p.num_q_heads, p.head_dim, p.max_blocks_per_seq,
                         p.block_size, p.decode_ranges, workspace, workspace_bytes);
@@ -697,14 +701,18 @@ pa_status_t pa_mixed_attention(const pa_mixed_plan_t* plan, pa_dtype_t dtype,
     PA_REQUIRE(workspace != nullptr && workspace_bytes >= need, PA_ERR_WORKSPACE,
                "workspace of %zu bytes needed (got %zu)", need, workspace_bytes);
   }
-  if (k) {
-    st = pa_cache_write(PA_LAYOUT_KV, dtype, k, int64_t(p.num_kv_heads) * p.head_dim, v,
-                        int64_t(p.num_kv_heads) * p.head_dim, kv_cache, num_blocks, p.block_size,
-                        p.num_kv_heads, p.head_dim, slot_mapping, p.num_tokens, stream);
-    if (st != PA_OK) return st;
-  }
-  // Rows 0 .. num_decode - 1 are the decode requests' queries, run with the
-  // plan's schedule (not re-derived from the current device).
+  return ok();
+}
+
+// The attention of a checked mixed run: the decode group with the plan's
+// schedule, then the prefill group (query rows stay absolute: same q, out, lse).
+static pa_status_t mixed_enqueue(const pa_mixed_plan_t& p, pa_dtype_t dtype, const void* q,
+                                 const void* kv_cache, int64_t num_blocks,
+                                 const int32_t* block_table, const int32_t* query_start_loc,
+                                 const int32_t* seq_lens, float scale, void* workspace,
+                                 size_t workspace_bytes, void* out, float* lse,
+                                 hipStream_t stream) {
+  pa_status_t st = PA_OK;
   if (p.num_decode > 0 && p.decode_ranges > 0) {
     st = pa_decode_balanced(q, kv_cache, num_blocks, p.block_size, block_table,
                             p.max_blocks_per_seq, seq_lens, p.num_decode, p.num_q_heads,
@@ -715,21 +723,210 @@ pa_status_t pa_mixed_attention(const pa_mixed_plan_t* plan, pa_dtype_t dtype,
                                   p.head_dim, p.decode_ranges, out, lse, stream);
     if (st != PA_OK) return st;
   } else if (p.num_decode > 0) {
-    st = pa_decode(dtype, q, nullptr, nullptr, kv_cache, num_blocks, p.block_size, block_table,
-                   p.max_blocks_per_seq, nullptr, seq_lens, p.num_decode, p.max_decode_seq_len,
-                   p.num_q_heads, p.num_kv_heads, p.head_dim, scale, p.decode_splits, workspace,
-                   workspace_bytes, out, lse, stream);
+    st = pa_decode(dtype, q, nullptr, nullptr, const_cast<void*>(kv_cache), num_blocks,
+                   p.block_size, block_table, p.max_blocks_per_seq, nullptr, seq_lens,
+                   p.num_decode, p.max_decode_seq_len, p.num_q_heads, p.num_kv_heads, p.head_dim,
+                   scale, p.decode_splits, workspace, workspace_bytes, out, lse, stream);
     if (st != PA_OK) return st;
   }
-  if (p.num_decode < p.num_seqs) {   // query rows stay absolute: same q, out, lse
+  if (p.num_decode < p.num_seqs) {
     const int nd = p.num_decode;
-    st = pa_prefill_varlen(dtype, q, nullptr, nullptr, kv_cache, num_blocks, p.block_size,
-                           block_table + int64_t(nd) * p.max_blocks_per_seq, p.max_blocks_per_seq,
-                           nullptr, query_start_loc + nd, seq_lens + nd, p.num_seqs - nd,
-                           p.num_tokens, p.max_query_len, p.max_seq_len, p.num_q_heads,
-                           p.num_kv_heads, p.head_dim, scale, 1, out, lse, stream);
+    st = pa_prefill_varlen(dtype, q, nullptr, nullptr, const_cast<void*>(kv_cache), num_blocks,
+                           p.block_size, block_table + int64_t(nd) * p.max_blocks_per_seq,
+                           p.max_blocks_per_seq, nullptr, query_start_loc + nd, seq_lens + nd,
+                           p.num_seqs - nd, p.num_tokens, p.max_query_len, p.max_seq_len,
+                           p.num_q_heads, p.num_kv_heads, p.head_dim, scale, 1, out, lse, stream);
     if (st != PA_OK) return st;
   }
+  return ok();
+}
+
+pa_status_t pa_mixed_attention(const pa_mixed_plan_t* plan, pa_dtype_t dtype,
+                               const void* q, const void* k, const void* v,
+                               void* kv_cache, int64_t num_blocks,
+                               const int32_t* block_table, const int64_t* slot_mapping,
+                               const int32_t* query_start_loc, const int32_t* seq_lens,
+                               float scale, void* workspace, size_t workspace_bytes,
+                               void* out, float* lse, hipStream_t stream) {
+  PA_REQUIRE(plan != nullptr, PA_ERR_INVALID, "plan must be non-null");
+  const pa_mixed_plan_t& p = *plan;
+  pa_status_t st = mixed_check(p, dtype, scale, q, k, v, kv_cache, num_blocks, block_table,
+                               slot_mapping, query_start_loc, seq_lens, workspace,
+                               workspace_bytes, out);
+  if (st != PA_OK || p.num_seqs == 0 || p.num_tokens == 0) return st;
+  if (k) {
+    st = pa_cache_write(PA_LAYOUT_KV, dtype, k, int64_t(p.num_kv_heads) * p.head_dim, v,
+                        int64_t(p.num_kv_heads) * p.head_dim, kv_cache, num_blocks, p.block_size,
+                        p.num_kv_heads, p.head_dim, slot_mapping, p.num_tokens, stream);
+    if (st != PA_OK) return st;
+  }
+  return mixed_enqueue(p, dtype, q, kv_cache, num_blocks, block_table, query_start_loc, seq_lens,
+                       scale, workspace, workspace_bytes, out, lse, stream);
+}
+
+// ---------------------------------------------------------------------------
+// Cascade workspace: suffix lengths [N] int32, suffix lse [T, Hq], prefix
+// partial lse [splits, T, Hq], prefix partial out [splits, T, Hq, 128] (fp32),
+// then the suffix pass's own workspace; each piece 256-byte aligned.
+struct CascadeLayout {
+  size_t lens, suffix_lse, part_lse, part_o, suffix_ws, total;
+};
+
+static bool cascade_layout(int num_seqs, int num_tokens, int num_q_heads, int head_dim,
+                           int splits, size_t suffix_ws, CascadeLayout* L) {
+  auto up = [](unsigned __int128 x) { return (x + 255) / 256 * 256; };
+  const unsigned __int128 rows = (unsigned __int128)num_tokens * (unsigned)num_q_heads;
+  unsigned __int128 off = 0;
+  L->lens = 0;
+  off = up(off + (unsigned __int128)num_seqs * 4);
+  L->suffix_lse = size_t(off);
+  off = up(off + rows * 4);
+  L->part_lse = size_t(off);
+  off = up(off + rows * (unsigned)splits * 4);
+  L->part_o = size_t(off);
+  off = up(off + rows * (unsigned)splits * (unsigned)head_dim * 4);
+  L->suffix_ws = size_t(off);
+  off += suffix_ws;
+  if (off > (unsigned __int128)(SIZE_MAX / 2)) return false;
+  L->total = size_t(off);
+  return true;
+}
+
+pa_status_t pa_plan_cascade(const int32_t* qsl, const int32_t* seq_lens, int num_seqs,
+                            int num_common_prefix_blocks, int num_q_heads, int num_kv_heads,
+                            int head_dim, int block_size, int max_blocks_per_seq, int num_cus,
+                            pa_cascade_plan_t* plan) {
+  PA_REQUIRE(plan != nullptr, PA_ERR_INVALID, "plan must be non-null");
+  std::memset(plan, 0, sizeof(*plan));
+  pa_cascade_plan_t c{};
+  // the whole batch first: every check of a mixed batch
+  pa_status_t st = pa_plan_mixed(qsl, seq_lens, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                 block_size, max_blocks_per_seq, num_cus, &c.suffix);
+  if (st != PA_OK) return st;
+  const int P = num_common_prefix_blocks;
+  PA_REQUIRE(P >= 0 && (P == 0 || P < max_blocks_per_seq), PA_ERR_INVALID,
+             "num_common_prefix_blocks must be in [0, max_blocks_per_seq) (got %d)", P);
+  PA_REQUIRE(int64_t(P) * block_size <= INT_MAX, PA_ERR_INVALID, "shared prefix too long");
+  const int Lp = P * block_size;
+  int cus = num_cus;
+  if (cus == 0) {
+    cus = pa_device_num_cus();
+    if (cus <= 0) return fail(PA_ERR_HIP, "cannot query the device's compute units");
+  }
+  int32_t* suffix = nullptr;
+  if (Lp > 0 && num_seqs > 0) {
+    suffix = new (std::nothrow) int32_t[num_seqs];
+    if (!suffix) return fail(PA_ERR_INVALID, "out of host memory");
+    for (int r = 0; r < num_seqs; ++r) {
+      const int L = qsl[r + 1] - qsl[r];
+      if (seq_lens[r] - L < Lp) {
+        delete[] suffix;
+        return fail(PA_ERR_INVALID,
+                    "request %d: its queries start at position %d, inside the %d-key shared "
+                    "prefix", r, seq_lens[r] - L, Lp);
+      }
+      suffix[r] = seq_lens[r] - Lp;
+    }
+    st = pa_plan_mixed(qsl, suffix, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                       max_blocks_per_seq, cus, &c.suffix);
+    delete[] suffix;
+    if (st != PA_OK) return st;
+  }
+  c.prefix_blocks = P;
+  c.prefix_len = Lp;
+  const int T = c.suffix.num_tokens;
+  if (Lp == 0 || T == 0) {
+    c.workspace_bytes = c.suffix.workspace_bytes;
+    *plan = c;
+    return ok();
+  }
+  // prefix pass: about one work-group per compute unit, at least 256 keys
+  // (four 64-key tiles) per range
+  const int G = num_q_heads / num_kv_heads;
+  const int64_t n_qt = (int64_t(T) * G + 127) / 128;
+  const int64_t want = (cus + int64_t(num_kv_heads) * n_qt - 1) / (int64_t(num_kv_heads) * n_qt);
+  const int max_splits = (Lp + 255) / 256;
+  int splits = int(want < 1 ? 1 : (want > max_splits ? max_splits : want));
+  c.split_keys = ((Lp + splits - 1) / splits + 63) / 64 * 64;
+  c.prefix_splits = (Lp + c.split_keys - 1) / c.split_keys;
+  CascadeLayout L;
+  PA_REQUIRE(cascade_layout(num_seqs, T, num_q_heads, head_dim, c.prefix_splits,
+                            c.suffix.workspace_bytes, &L),
+             PA_ERR_INVALID, "cascade workspace size overflows");
+  c.workspace_bytes = L.total;
+  *plan = c;
+  return ok();
+}
+
+pa_status_t pa_cascade_attention(const pa_cascade_plan_t* plan, pa_dtype_t dtype,
+                                 const void* q, const void* k, const void* v,
+                                 void* kv_cache, int64_t num_blocks,
+                                 const int32_t* block_table, const int64_t* slot_mapping,
+                                 const int32_t* query_start_loc, const int32_t* seq_lens,
+                                 float scale, void* workspace, size_t workspace_bytes,
+                                 void* out, float* lse, hipStream_t stream) {
+  PA_REQUIRE(plan != nullptr, PA_ERR_INVALID, "plan must be non-null");
+  const pa_cascade_plan_t& c = *plan;
+  const pa_mixed_plan_t& p = c.suffix;
+  if (c.prefix_len == 0)
+    return pa_mixed_attention(&p, dtype, q, k, v, kv_cache, num_blocks, block_table,
+                              slot_mapping, query_start_loc, seq_lens, scale, workspace,
+                              workspace_bytes, out, lse, stream);
+  PA_REQUIRE(c.prefix_blocks > 0 && c.prefix_blocks < p.max_blocks_per_seq &&
+                 c.prefix_len == c.prefix_blocks * p.block_size &&
+                 (p.num_tokens == 0 ||
+                  (c.prefix_splits >= 1 && c.split_keys > 0 && c.split_keys % 64 == 0 &&
+                   int64_t(c.prefix_splits) * c.split_keys >= c.prefix_len)),
+             PA_ERR_INVALID, "plan is not one made by pa_plan_cascade");
+  CascadeLayout L{};
+  if (p.num_tokens > 0) {
+    PA_REQUIRE(cascade_layout(p.num_seqs, p.num_tokens, p.num_q_heads, p.head_dim,
+                              c.prefix_splits, p.workspace_bytes, &L),
+               PA_ERR_INVALID, "plan is not one made by pa_plan_cascade");
+    PA_REQUIRE(workspace != nullptr && workspace_bytes >= L.total, PA_ERR_WORKSPACE,
+               "workspace of %zu bytes needed (got %zu)", L.total, workspace_bytes);
+    PA_REQUIRE((reinterpret_cast<uintptr_t>(workspace) & 255) == 0, PA_ERR_INVALID,
+               "workspace must be 256-byte aligned");
+  }
+  char* ws = static_cast<char*>(workspace);
+  const int32_t* suffix_table = block_table ? block_table + c.prefix_blocks : nullptr;
+  pa_status_t st = mixed_check(p, dtype, scale, q, k, v, kv_cache, num_blocks, suffix_table,
+                               slot_mapping, query_start_loc, seq_lens,
+                               ws ? ws + L.suffix_ws : nullptr,
+                               workspace_bytes - L.suffix_ws, out);
+  if (st != PA_OK || p.num_seqs == 0 || p.num_tokens == 0) return st;
+  if (k) {
+    st = pa_cache_write(PA_LAYOUT_KV, dtype, k, int64_t(p.num_kv_heads) * p.head_dim, v,
+                        int64_t(p.num_kv_heads) * p.head_dim, kv_cache, num_blocks, p.block_size,
+                        p.num_kv_heads, p.head_dim, slot_mapping, p.num_tokens, stream);
+    if (st != PA_OK) return st;
+  }
+  // suffix: keys [P bs, seq_len) of each request, through its table from entry P
+  int32_t* lens = reinterpret_cast<int32_t*>(ws + L.lens);
+  float* suffix_lse = reinterpret_cast<float*>(ws + L.suffix_lse);
+  pa::SuffixLens sl{seq_lens, lens, p.num_seqs, c.prefix_len,
+                    (p.max_blocks_per_seq - c.prefix_blocks) * p.block_size};
+  hipError_t e = pa::launch_suffix_lens(sl, stream);
+  if (e != hipSuccess) return hip_fail(e, "suffix length launch");
+  st = mixed_enqueue(p, dtype, q, kv_cache, num_blocks, suffix_table, query_start_loc, lens,
+                     scale, ws + L.suffix_ws, workspace_bytes - L.suffix_ws, out, suffix_lse,
+                     stream);
+  if (st != PA_OK) return st;
+  // prefix: every query row against the shared pages (row 0 of the table)
+  float* part_lse = reinterpret_cast<float*>(ws + L.part_lse);
+  float* part_o = reinterpret_cast<float*>(ws + L.part_o);
+  pa::PrefillVarlen pv{q, kv_cache, num_blocks, p.block_size, block_table, p.max_blocks_per_seq,
+                       query_start_loc, seq_lens, p.num_seqs, p.num_tokens, p.max_query_len,
+                       c.prefix_len, p.num_q_heads, p.num_kv_heads, p.head_dim, scale, 0,
+                       nullptr, nullptr, c.prefix_len, c.prefix_splits, c.split_keys, part_o,
+                       part_lse};
+  e = pa::launch_prefill_varlen(pv, stream);
+  if (e == hipErrorNotSupported) return fail(PA_ERR_UNSUPPORTED, "prefill kernel not built");
+  if (e != hipSuccess) return hip_fail(e, "cascade prefix launch");
+  pa::CascadeMerge m{part_o, part_lse, c.prefix_splits, suffix_lse, out, lse,
+                     int64_t(p.num_tokens) * p.num_q_heads};
+  e = pa::launch_cascade_merge(m, stream);
+  if (e != hipSuccess) return hip_fail(e, "cascade merge launch");
   return ok();
 }
 

@@ -109,7 +109,34 @@ struct PrefillVarlen {
   int num_q_heads; int num_kv_heads; int head_dim;
   float scale; int causal;
   void* out; float* lse;
+  // Shared-prefix mode (prefix_splits > 0): every query row of the batch
+  // (num_tokens rows, no causal mask) against keys [0, prefix_len) of
+  // block_table row 0, cut into prefix_splits ranges of split_keys keys
+  // (a multiple of 64); fp32 partials part_o [splits, T, Hq, D] (normalised
+  // by the range's own sum) and part_lse [splits, T, Hq] (natural log)
+  // replace out and lse.
+  int prefix_len; int prefix_splits; int split_keys;
+  float* part_o; float* part_lse;
 };
 hipError_t launch_prefill_varlen(const PrefillVarlen& a, hipStream_t s);
+
+// Cascade attention: per-request key counts past the shared prefix, and the
+// merge of the prefix's partials with the suffix's result.
+struct SuffixLens {
+  const int32_t* seq_lens; int32_t* out; int num_seqs;
+  int prefix_len; int max_suffix;   // out[r] = clamp(seq_lens[r] - prefix_len, 0, max_suffix)
+};
+hipError_t launch_suffix_lens(const SuffixLens& a, hipStream_t s);
+
+struct CascadeMerge {
+  const float* part_o;     // [splits, rows, 128] fp32, normalised per split
+  const float* part_lse;   // [splits, rows] natural log
+  int num_splits;
+  const float* suffix_lse; // [rows]
+  void* out;               // [rows, 128] bf16: the suffix's result in, the merged result out
+  float* lse;              // [rows] or null
+  int64_t rows;            // num_tokens * num_q_heads
+};
+hipError_t launch_cascade_merge(const CascadeMerge& a, hipStream_t s);
 
 }  // namespace pa

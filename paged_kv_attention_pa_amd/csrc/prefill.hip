@@ -46,6 +46,12 @@ constexpr float kSlack = 8.0f;     // lazy-rescale headroom, log2 units
 // 4-slot group.  Both are conflict-free.
 __device__ __forceinline__ int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
 
+// kPrefix = false: varlen prefill, one (request, query head, 128-row q tile)
+// per work-group, out / lse written directly.
+// kPrefix = true: the shared prefix of a cascade -- the batch's query rows,
+// each (token, head of the group) pair a row (row = token * G + head), against
+// one key range of the prefix, fp32 partials out.
+template <bool kPrefix>
 __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillVarlen a) {
   __shared__ __align__(16) char smem[4 * kTileBytes];   // 2 x (K tile, V tile)
   const int lane = threadIdx.x & 63;
@@ -53,47 +59,73 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillVarlen a) {
   const int tid = threadIdx.x;
   const int Hq = a.num_q_heads;
   const int G = Hq / a.num_kv_heads;
-
-  // work-group -> (request, KV head, q tile, head of the group).  Work-groups
-  // are dealt to the 8 XCDs round-robin by id, so ids are arranged such that
-  // every q tile and query head of one (request, KV head) pair land on the
-  // same XCD, one after another: that pair's K/V (at most a few MB) is read
-  // from HBM once and then served by that XCD's L2.  Within a pair, the
-  // longest (last) q tiles go first.
-  const int n_qt = (a.max_query_len + kBM - 1) / kBM;
-  const int per_pair = n_qt * G;
+  const int bs = a.block_size;
   const int id = blockIdx.x;
   const int xcd = id % kXcds;
   const int slot = id / kXcds;
-  const int pair = (slot / per_pair) * kXcds + xcd;          // (request, KV head)
-  if (pair >= a.num_seqs * a.num_kv_heads) return;
-  const int local = slot % per_pair;
-  const int r = pair / a.num_kv_heads;
-  const int kvh0 = pair % a.num_kv_heads;
-  const int qt = n_qt - 1 - local / G;
-  const int h = kvh0 * G + local % G;
-  const int q_start = min(max(a.query_start_loc[r], 0), a.num_tokens);
-  const int L = min(min(a.query_start_loc[r + 1] - q_start, a.max_query_len), a.num_tokens - q_start);
-  const int bs = a.block_size;
-  const int S = min(a.seq_lens[r], a.max_blocks * bs);
-  const int q0 = qt * kBM;
-  if (q0 >= L || L <= 0) return;
-  const int C = S - L;                    // keys before the chunk
-  const int kvh = kvh0;
 
-  // keys this work-group may see
-  int kv_end = S;
-  if (a.causal) kv_end = min(S, max(0, C + min(q0 + kBM, L)));
+  int r, h, q_start, L, q0, C, kvh, kv_end, t_begin = 0, split = 0;
+  if constexpr (!kPrefix) {
+    // work-group -> (request, KV head, q tile, head of the group).  Work-groups
+    // are dealt to the 8 XCDs round-robin by id, so ids are arranged such that
+    // every q tile and query head of one (request, KV head) pair land on the
+    // same XCD, one after another: that pair's K/V (at most a few MB) is read
+    // from HBM once and then served by that XCD's L2.  Within a pair, the
+    // longest (last) q tiles go first.
+    const int n_qt = (a.max_query_len + kBM - 1) / kBM;
+    const int per_pair = n_qt * G;
+    const int pair = (slot / per_pair) * kXcds + xcd;          // (request, KV head)
+    if (pair >= a.num_seqs * a.num_kv_heads) return;
+    const int local = slot % per_pair;
+    r = pair / a.num_kv_heads;
+    kvh = pair % a.num_kv_heads;
+    const int qt = n_qt - 1 - local / G;
+    h = kvh * G + local % G;
+    q_start = min(max(a.query_start_loc[r], 0), a.num_tokens);
+    L = min(min(a.query_start_loc[r + 1] - q_start, a.max_query_len), a.num_tokens - q_start);
+    const int S = min(a.seq_lens[r], a.max_blocks * bs);
+    q0 = qt * kBM;
+    if (q0 >= L || L <= 0) return;
+    C = S - L;                    // keys before the chunk
+    // keys this work-group may see
+    kv_end = S;
+    if (a.causal) kv_end = min(S, max(0, C + min(q0 + kBM, L)));
+  } else {
+    // work-group -> (KV head, key range, row tile): the row tiles of one
+    // (KV head, key range) pair share that range's K/V and sit on one XCD.
+    const int n_qt = (a.num_tokens * G + kBM - 1) / kBM;
+    const int pair = (slot / n_qt) * kXcds + xcd;              // (KV head, key range)
+    if (pair >= a.num_kv_heads * a.prefix_splits) return;
+    kvh = pair / a.prefix_splits;
+    split = pair % a.prefix_splits;
+    r = 0;                        // the prefix's pages: row 0 of the table
+    h = kvh * G;                  // per-lane head set below
+    q_start = 0;
+    L = a.num_tokens * G;         // rows
+    q0 = (slot % n_qt) * kBM;
+    C = 0;
+    const int key_begin = split * a.split_keys;
+    kv_end = min(min(a.prefix_len, a.max_blocks * bs), key_begin + a.split_keys);
+    if (key_begin >= kv_end) return;
+    t_begin = key_begin / kBN;
+  }
   const int n_tiles = (kv_end + kBN - 1) / kBN;
 
   // ---- Q fragments (B operand of S^T): row = l % 32, d chunk = 16 kk + 8 (l / 32)
   const int my_row = q0 + wave * 32 + (lane & 31);
   const bool row_ok = my_row < L;
+  int64_t q_off;   // element offset of this lane's query row
+  if constexpr (!kPrefix) {
+    q_off = (int64_t(q_start) + (row_ok ? my_row : 0)) * Hq * kD + int64_t(h) * kD;
+  } else {
+    const int row = row_ok ? my_row : 0;
+    const int tok = row / G;       // G is a power of two
+    h = kvh * G + (row - tok * G);
+    q_off = (int64_t(tok) * Hq + h) * kD;
+  }
   u32x4_t qf[8];
   {
-    const uint16_t* qp = static_cast<const uint16_t*>(a.q) +
-                         (int64_t(q_start) + (row_ok ? my_row : 0)) * Hq * kD + int64_t(h) * kD +
-                         8 * (lane >> 5);
+    const uint16_t* qp = static_cast<const uint16_t*>(a.q) + q_off + 8 * (lane >> 5);
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) qf[kk] = row_ok ? load16(qp + 16 * kk) : u32x4_t{0, 0, 0, 0};
   }
@@ -170,15 +202,16 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillVarlen a) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[dt][i] = 0.0f;
 
-  if (n_tiles > 0) {
-    gload(0, smem);
+  if (n_tiles > t_begin) {
+    gload(t_begin, smem);
     gwait();
   }
   __syncthreads();
 
+  const bool causal = kPrefix ? false : a.causal;
   const int row_abs = C + my_row;         // last key this row may see (causal)
-  for (int t = 0; t < n_tiles; ++t) {
-    const int buf = t & 1;
+  for (int t = t_begin; t < n_tiles; ++t) {
+    const int buf = (t - t_begin) & 1;
     if (t + 1 < n_tiles) gload(t + 1, smem + (buf ^ 1) * 2 * kTileBytes);   // in flight below
     const char* kt = smem + buf * 2 * kTileBytes;
     const char* vt = kt + kTileBytes;
@@ -223,7 +256,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillVarlen a) {
     // accumulator needs no rescale and P stays below 2^kSlack, well inside
     // bf16/fp32 range.  scale > 0 makes the max of the raw scores, times the
     // scale, the max of the scaled scores.
-    const bool need_mask = (key0 + kBN > kv_end) || (a.causal && key0 + kBN - 1 > C + q0 + wave * 32);
+    const bool need_mask = (key0 + kBN > kv_end) || (causal && key0 + kBN - 1 > C + q0 + wave * 32);
     u32x4_t pf[4];
     float psum = 0.0f;
     float alpha = 1.0f;
@@ -233,7 +266,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillVarlen a) {
       if constexpr (kMasked) {
         // key = key0 + 4 (l / 32) + c with a compile-time c per register:
         // visible iff c <= lim (one compare per score)
-        const int lim = (a.causal ? min(kv_end - 1, row_abs) : kv_end - 1) - key0 - 4 * (lane >> 5);
+        const int lim = (causal ? min(kv_end - 1, row_abs) : kv_end - 1) - key0 - 4 * (lane >> 5);
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
@@ -333,8 +366,24 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillVarlen a) {
   // ---- finish: full row sum, normalise, write
   const float l_tot = l_run + lane_xor(l_run, 32);
   if (!row_ok) return;
-  const int64_t orow = int64_t(q_start) + my_row;
   const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+  if constexpr (kPrefix) {
+    const int64_t prow = (int64_t(split) * a.num_tokens + my_row / G) * Hq + h;
+    float* po = a.part_o + prow * kD;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int d = 32 * dt + 8 * q4 + 4 * (lane >> 5);
+        *reinterpret_cast<f32x4_t*>(po + d) =
+            f32x4_t{acc[dt][4 * q4 + 0] * inv, acc[dt][4 * q4 + 1] * inv,
+                    acc[dt][4 * q4 + 2] * inv, acc[dt][4 * q4 + 3] * inv};
+      }
+    if (lane < 32)
+      a.part_lse[prow] = l_tot > 0.0f ? (m_run + fast_log2(l_tot)) * kLn2 : -INFINITY;
+    return;
+  }
+  const int64_t orow = int64_t(q_start) + my_row;
   uint16_t* op = static_cast<uint16_t*>(a.out) + orow * Hq * kD + int64_t(h) * kD;
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt)
@@ -353,13 +402,24 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillVarlen a) {
 }  // namespace
 
 hipError_t launch_prefill_varlen(const PrefillVarlen& a, hipStream_t s) {
+  if (a.prefix_splits > 0) {
+    if (a.num_tokens <= 0 || a.prefix_len <= 0) return hipSuccess;
+    if (a.split_keys <= 0 || a.split_keys % kBN != 0) return hipErrorInvalidValue;
+    const int G = a.num_q_heads / a.num_kv_heads;
+    const int64_t n_qt = (int64_t(a.num_tokens) * G + kBM - 1) / kBM;
+    const int64_t pairs = int64_t(a.num_kv_heads) * a.prefix_splits;
+    const int64_t wgs = (pairs + kXcds - 1) / kXcds * kXcds * n_qt;
+    if (wgs > INT32_MAX || int64_t(a.num_tokens) * G > INT32_MAX) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(prefill_kernel<true>, dim3(unsigned(wgs)), dim3(256), 0, s, a);
+    return hipGetLastError();
+  }
   if (a.num_seqs <= 0 || a.num_tokens <= 0 || a.max_query_len <= 0) return hipSuccess;
   const int n_qt = (a.max_query_len + kBM - 1) / kBM;
   const int G = a.num_q_heads / a.num_kv_heads;
   const int64_t pairs = int64_t(a.num_seqs) * a.num_kv_heads;
   const int64_t wgs = (pairs + kXcds - 1) / kXcds * kXcds * n_qt * G;
   if (wgs > INT32_MAX) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(prefill_kernel, dim3(unsigned(wgs)), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(prefill_kernel<false>, dim3(unsigned(wgs)), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

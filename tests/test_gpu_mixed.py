@@ -91,8 +91,8 @@ def test_mixed_equals_its_two_groups():
     torch.cuda.synchronize()
     assert np.array_equal(out[:nd], to_f64(od))
     assert np.array_equal(lse[:nd], ld.cpu().numpy().astype(np.float64))
-    assert np.array_equal(out[nd:], to_f64(op)[nd:])
-    assert np.array_equal(lse[nd:], lp.cpu().numpy().astype(np.float64)[nd:])
+    assert np.array_equal(out[nd:], to_f64(op[nd:]))
+    assert np.array_equal(lse[nd:], lp[nd:].cpu().numpy().astype(np.float64))
 
 
 def test_one_plan_serves_every_layer():

@@ -162,3 +162,107 @@ def test_run_empty_batch_is_noop(lib):
     plan = pa.plan_mixed([0], [], 32, 8, 128, 16, 64, 256)
     assert _run(lib, plan, q=None, out=None, qsl=None, seq=None) == 0
     assert pa.last_error() == ""
+
+
+# ----------------------------------------------------------------- cascade
+def _cascade_expected(T, G, hkv, Lp, cus):
+    """Key ranges of the prefix pass as pa_cascade_plan_t documents them: about one
+    work-group per compute unit over (KV head, 128-row tile, range), at least
+    256 keys per range, ranges a multiple of 64 keys."""
+    n_qt = math.ceil(T * G / 128)
+    want = math.ceil(cus / (hkv * n_qt))
+    splits = max(1, min(want, math.ceil(Lp / 256)))
+    keys = math.ceil(math.ceil(Lp / splits) / 64) * 64
+    return math.ceil(Lp / keys), keys
+
+
+def _up(x):
+    return (x + 255) // 256 * 256
+
+
+@pytest.mark.parametrize("q_lens,own,P,hq,hkv,cus", [
+    ([1] * 64, [600] * 64, 256, 32, 8, 256),
+    ([1, 1, 1, 50], [900, 200, 100, 300], 256, 32, 8, 256),
+    ([1, 1, 400], [5, 9, 500], 3, 8, 1, 80),
+    ([1] * 6 + [40], [3, 500, 80, 1, 260, 9, 100], 137, 32, 8, 4096),
+])
+def test_cascade_plan_fields(lib, q_lens, own, P, hq, hkv, cus):
+    seq = [o + P * 16 for o in own]
+    maxb = max(math.ceil(s / 16) for s in seq) + 3
+    plan = pa.plan_cascade(_qsl(q_lens), seq, P, hq, hkv, 128, 16, maxb, cus)
+    # the suffix plan is the mixed plan of the lengths past the prefix
+    ref = pa.plan_mixed(_qsl(q_lens), own, hq, hkv, 128, 16, maxb, cus)
+    for f, _ in pa.MixedPlan._fields_:
+        assert getattr(plan.suffix, f) == getattr(ref, f), f
+    assert (plan.prefix_blocks, plan.prefix_len) == (P, P * 16)
+    T, Lp = sum(q_lens), P * 16
+    splits, keys = _cascade_expected(T, hq // hkv, hkv, Lp, cus)
+    assert (plan.prefix_splits, plan.split_keys) == (splits, keys)
+    assert splits * keys >= Lp > (splits - 1) * keys
+    rows = T * hq
+    ws = _up(_up(_up(_up(len(q_lens) * 4) + rows * 4) + rows * splits * 4) +
+             rows * splits * 128 * 4) + ref.workspace_bytes
+    assert plan.workspace_bytes == ws
+
+
+def test_cascade_plan_without_prefix(lib):
+    plan = pa.plan_cascade(_qsl([1, 1, 7]), [50, 60, 70], 0, 8, 2, 128, 16, 8, 256)
+    ref = pa.plan_mixed(_qsl([1, 1, 7]), [50, 60, 70], 8, 2, 128, 16, 8, 256)
+    assert plan.prefix_len == 0 and plan.prefix_splits == 0
+    assert plan.workspace_bytes == ref.workspace_bytes
+    assert plan.suffix.num_decode == ref.num_decode
+
+
+def _raw_cascade(lib, qsl, seq, P, maxb=64):
+    plan = pa.CascadePlan()
+    plan.prefix_len = 5
+    a = (C.c_int32 * len(qsl))(*qsl)
+    s = (C.c_int32 * max(len(seq), 1))(*seq)
+    st = lib.pa_plan_cascade(a, s, len(seq), P, 32, 8, 128, 16, maxb, 256, C.byref(plan))
+    return st, plan
+
+
+@pytest.mark.parametrize("qsl,seq,P,status", [
+    ([0, 1, 2], [100, 64], 4, INVALID),      # request 1's query at position 63 < 64
+    ([0, 1, 31], [100, 90], 4, INVALID),     # a chunk reaching into the prefix
+    ([0, 1], [100], -1, INVALID),
+    ([0, 1], [100], 64, INVALID),            # the whole table
+    ([0, 2], [1], 0, INVALID),               # mixed-batch checks still apply
+])
+def test_cascade_plan_validation(lib, qsl, seq, P, status):
+    st, plan = _raw_cascade(lib, qsl, seq, P)
+    assert st == status
+    assert pa.last_error() != ""
+    assert plan.prefix_len == 0
+
+
+def _run_cascade(lib, plan, **kw):
+    a = dict(dtype=1, q=1 << 20, k=None, v=None, cache=1 << 21, nb=100, table=1 << 22,
+             slots=None, qsl=1 << 23, seq=1 << 24, scale=0.1, ws=None, wsb=0, out=1 << 25,
+             lse=None)
+    a.update(kw)
+    return lib.pa_cascade_attention(None if plan is None else C.byref(plan), a["dtype"], a["q"],
+                                    a["k"], a["v"], a["cache"], a["nb"], a["table"], a["slots"],
+                                    a["qsl"], a["seq"], a["scale"], a["ws"], a["wsb"], a["out"],
+                                    a["lse"], None)
+
+
+def test_cascade_run_validation(lib):
+    plan = pa.plan_cascade(_qsl([1, 1, 1, 50]), [4900, 4200, 4100, 4400], 256, 32, 8, 128, 16,
+                           512, 256)
+    need = plan.workspace_bytes
+    ws = 1 << 30
+    assert _run_cascade(lib, None) == INVALID
+    assert _run_cascade(lib, plan, dtype=0, ws=ws, wsb=need) == UNSUPPORTED
+    assert _run_cascade(lib, plan, ws=None) == WORKSPACE
+    assert _run_cascade(lib, plan, ws=ws, wsb=need - 1) == WORKSPACE
+    assert _run_cascade(lib, plan, ws=ws + 16, wsb=need) == INVALID   # not 256-byte aligned
+    assert _run_cascade(lib, plan, ws=ws, wsb=need, table=None) == INVALID
+    assert _run_cascade(lib, plan, ws=ws, wsb=need, k=1 << 27) == INVALID
+    assert _run_cascade(lib, plan, ws=ws, wsb=need, scale=-1.0) == INVALID
+    bad = pa.CascadePlan.from_buffer_copy(plan)
+    bad.split_keys = 100                      # not a multiple of 64
+    assert _run_cascade(lib, bad, ws=ws, wsb=need) == INVALID
+    bad = pa.CascadePlan.from_buffer_copy(plan)
+    bad.prefix_splits = 1                     # ranges no longer cover the prefix
+    assert _run_cascade(lib, bad, ws=ws, wsb=need) == INVALID

@@ -301,6 +301,7 @@ WORKLOADS = {
     4: "mla_latent_decode_bf16",
 }
 MIXED = "mixed_prefill_decode_bf16"
+CASCADE = "cascade_shared_prefix_decode_bf16"
 
 
 def tiny_decode() -> GqaBatch:
@@ -357,6 +358,37 @@ def mixed_batch(seed: int = 1006, decode: int = 64, prefill: int = 4) -> GqaBatc
     q_lens = np.concatenate([np.ones(decode, dtype=np.int64), L])
     seq = np.concatenate([dec, C + L])
     return make_gqa(rng, q_lens, seq, 32, 8, 128, 16, BF16, name=MIXED)
+
+
+def share_prefix(b: GqaBatch, prefix_blocks: int, name: str | None = None) -> GqaBatch:
+    """Make every request start with request 0's first ``prefix_blocks``
+    pages (a common prefix: the same physical pages, hence the same keys and
+    values).  Each other request's own first pages are left unused and
+    filled with NaN, so reading them shows.  Modifies ``b`` in place (its
+    tables and pool) and returns it.  Every request's new tokens must lie
+    after the prefix."""
+    P = int(prefix_blocks)
+    Lp = P * b.block_size
+    if np.any(b.seq_lens.astype(np.int64) - b.q_lens < Lp):
+        raise ValueError("every request's queries must follow the shared prefix")
+    if P > 0 and b.num_seqs > 1:
+        orphan = b.block_table[1:, :P].ravel()
+        b.cache[orphan] = _nan(b.dtype)
+        b.block_table[1:, :P] = b.block_table[0, :P]
+    b.meta["prefix_blocks"] = P
+    if name:
+        b.name = name
+    return b
+
+
+def cascade_batch(seed: int = 1007, batch: int = 64, prefix_len: int = 4096) -> GqaBatch:
+    """64 decode requests that share a 4096-token prefix (256 pages of 16,
+    a common system prompt) followed by their own U{512..4096} tokens; 32 q /
+    8 kv heads, d=128, bf16."""
+    rng = np.random.default_rng(seed)
+    own = rng.integers(512, 4096, size=batch, endpoint=True)
+    b = make_gqa(rng, np.ones(batch, dtype=np.int64), prefix_len + own, 32, 8, 128, 16, BF16)
+    return share_prefix(b, prefix_len // 16, name=CASCADE)
 
 
 # --------------------------------------------------------------------------
