@@ -40,6 +40,11 @@ What is computed, and where the pages define it
   kv_lora_rank columns of the same row; the output has kv_lora_rank columns.
 * Split count.  Same Triton/MLA page, section 關鍵檔案 (``_compute_num_kv_splits``):
   ``max_seq_len / 512`` splits, capped at twice the compute-unit count.
+* FP8 cache.  Same Triton/MLA page, 資料流 (the layer's k_scale / v_scale go
+  to the kernel; v_scale = k_scale for the latent cache) and 邊界與失敗 (the
+  query stays bf16; the kernel dequantises).  Format and rounding are a
+  reading (OCP E4M3, round to nearest even, saturating), stated at the
+  functions.
 
 Readings where the pages leave a step open (each is also listed in the design doc):
 * ``seq_len`` includes this step's new tokens (the write happens first), and
@@ -329,9 +334,93 @@ def slot_of(block_table_row, pos: int, block_size: int) -> int:
     return int(block_table_row[pos // block_size]) * block_size + pos % block_size
 
 
+# --------------------------------------------------------------------------
+# FP8 KV cache with per-tensor scales
+# --------------------------------------------------------------------------
+# The pages name an FP8 cache read with per-layer k_scale / v_scale while the
+# query stays bf16 ("Triton 與 MLA", 資料流 passes k_scale and v_scale to the
+# kernel, v_scale = k_scale for the latent cache; 邊界與失敗: with an FP8 cache
+# the kernel dequantises and the query is not quantised).  They do not fix
+# the format or the rounding.  Reading: OCP FP8 E4M3 -- 1 sign bit, 4 exponent
+# bits with bias 7, 3 mantissa bits, subnormals m * 2^-9, no infinities,
+# S.1111.111 is NaN, largest finite 448.  A stored code is E4M3(x / scale)
+# with the quotient formed in fp32 (x is a bf16 value, exact in fp32) and
+# rounded to the nearest E4M3 value, ties to the even code, saturating at
+# +-448; the value read back is E4M3(code) * scale.
+
+def fp8_e4m3_to_f64(codes) -> np.ndarray:
+    """Exact value of E4M3 codes (uint8) by the format's definition."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = c >> 7
+    e = (c >> 3) & 15
+    m = c & 7
+    normal = (1.0 + m / 8.0) * np.exp2(e.astype(np.float64) - 7.0)
+    sub = m * 2.0 ** -9
+    val = np.where(e == 0, sub, normal)
+    val = np.where(sign == 1, -val, val)
+    return np.where((e == 15) & (m == 7), np.nan, val)
+
+
+_E4M3_POS = fp8_e4m3_to_f64(np.arange(0x7F, dtype=np.uint8))   # codes 0..126, increasing
+
+
+def f32_to_fp8_e4m3(x) -> np.ndarray:
+    """E4M3 code of float32 values: nearest value, ties to the even code,
+    magnitudes above 448 saturated to 448, NaN to 0x7F; the sign bit is
+    kept (so -0 and negatives that round to zero give 0x80)."""
+    x = np.asarray(x, dtype=np.float32)
+    a = np.minimum(np.abs(x).astype(np.float64), 448.0)
+    hi = np.clip(np.searchsorted(_E4M3_POS, a, side="left"), 0, 0x7E)   # first value >= a
+    lo = np.maximum(hi - 1, 0)
+    d_lo = a - _E4M3_POS[lo]
+    d_hi = _E4M3_POS[hi] - a
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
+    code = np.where(pick_hi, hi, lo).astype(np.uint8)
+    code = np.where(np.signbit(x), code | np.uint8(0x80), code).astype(np.uint8)
+    return np.where(np.isnan(x), np.uint8(0x7F), code).astype(np.uint8)
+
+
+def quantize_fp8(x_bits_bf16, scale: float) -> np.ndarray:
+    """Codes of bf16 values divided by ``scale`` (the quotient in fp32)."""
+    q = (bf16_bits_to_f64(x_bits_bf16).astype(np.float32) / np.float32(scale)).astype(np.float32)
+    return f32_to_fp8_e4m3(q)
+
+
+def cache_write_kv_fp8(cache: np.ndarray, k: np.ndarray, v: np.ndarray,
+                       slot_mapping: np.ndarray, k_scale: float, v_scale: float) -> np.ndarray:
+    """The GQA cache write of an FP8 cache (uint8 codes, same layout): new bf16
+    keys and values quantised with k_scale / v_scale, then stored at their
+    slots as in ``cache_write_kv``."""
+    return cache_write_kv(cache, quantize_fp8(k, k_scale), quantize_fp8(v, v_scale),
+                          slot_mapping)
+
+
+def cache_write_mla_fp8(cache: np.ndarray, kv_c: np.ndarray, k_pe: np.ndarray,
+                        slot_mapping: np.ndarray, scale: float) -> np.ndarray:
+    """The MLA latent write of an FP8 cache: the whole row uses one scale
+    ("Triton 與 MLA", 資料流: v_scale = k_scale for the latent cache)."""
+    return cache_write_mla(cache, quantize_fp8(kv_c, scale), quantize_fp8(k_pe, scale),
+                           slot_mapping)
+
+
+def dequant_kv_cache(cache: np.ndarray, k_scale: float, v_scale: float) -> np.ndarray:
+    """Values an FP8 GQA cache holds: plane 0 times k_scale, plane 1 times
+    v_scale, as float64 (for ``paged_attention`` / ``paged_decode``)."""
+    out = fp8_e4m3_to_f64(cache)
+    out[:, 0] *= float(k_scale)
+    out[:, 1] *= float(v_scale)
+    return out
+
+
+def dequant_mla_cache(cache: np.ndarray, scale: float) -> np.ndarray:
+    """Values an FP8 latent cache holds, as float64 (for ``mla_decode``)."""
+    return fp8_e4m3_to_f64(cache) * float(scale)
+
+
 __all__ = [
     "bf16_bits_to_f64", "to_f64", "cache_write_kv", "cache_write_mla",
     "gather_kv", "gather_mla", "attention", "paged_attention", "paged_decode",
     "mla_decode", "partial_attention", "lse_merge", "lse_merge_packed",
-    "num_kv_splits", "slot_of",
+    "num_kv_splits", "slot_of", "fp8_e4m3_to_f64", "f32_to_fp8_e4m3", "quantize_fp8",
+    "cache_write_kv_fp8", "cache_write_mla_fp8", "dequant_kv_cache", "dequant_mla_cache",
 ]

@@ -403,10 +403,89 @@ def pin_chunked_prefill():
     assert np.max(np.abs(dec - one[-1:])) < 1e-13 and np.max(np.abs(ld - l1[-1:])) < 1e-13
 
 
+# --------------------------------------------------------------------------
+# FP8 (E4M3) cache pins
+# --------------------------------------------------------------------------
+
+def pin_fp8_e4m3_decoding():
+    """Values the OCP E4M3 definition fixes, and torch's float8_e4m3fn
+    decoding of all 256 codes (an independent library routine)."""
+    want = {0x00: 0.0, 0x01: 2.0 ** -9, 0x07: 7 * 2.0 ** -9, 0x08: 2.0 ** -6, 0x38: 1.0,
+            0x39: 1.125, 0x40: 2.0, 0x7E: 448.0, 0xFE: -448.0, 0xB8: -1.0}
+    for c, v in want.items():
+        got = O.fp8_e4m3_to_f64(np.array([c], np.uint8))[0]
+        assert got == v, (hex(c), got, v)
+    assert np.signbit(O.fp8_e4m3_to_f64(np.array([0x80], np.uint8))[0])
+    codes = np.arange(256, dtype=np.uint8)
+    got = O.fp8_e4m3_to_f64(codes)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).double().numpy()
+    assert np.array_equal(np.isnan(got), np.isnan(ref)) and np.isnan(got).sum() == 2
+    assert np.array_equal(got[~np.isnan(got)], ref[~np.isnan(ref)])
+
+
+def pin_fp8_e4m3_encoding():
+    """Round to nearest with ties to the even code, saturation at 448, the
+    exact round trip of every finite code, brute-force nearest, and torch's
+    float8_e4m3fn conversion of in-range fp32 values."""
+    f = lambda *xs: list(O.f32_to_fp8_e4m3(np.array(xs, np.float32)))
+    # 1.0625 lies halfway between 1.0 (0x38) and 1.125 (0x39): the even code;
+    # 1.1875 halfway between 1.125 and 1.25 (0x3A): the even code again
+    assert f(1.0625, 1.1875, -1.0625) == [0x38, 0x3A, 0xB8]
+    assert f(500.0, -1e9, 464.0, 447.0) == [0x7E, 0xFE, 0x7E, 0x7E]
+    assert f(2.0 ** -10, 2.0 ** -10 * 1.0001, 3 * 2.0 ** -10) == [0x00, 0x01, 0x02]
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], np.uint8)
+    vals = O.fp8_e4m3_to_f64(codes).astype(np.float32)
+    assert np.array_equal(O.f32_to_fp8_e4m3(vals), codes)
+    rng = _rng(77)
+    x = (rng.standard_normal(20000) * np.exp2(rng.integers(-11, 9, 20000))).astype(np.float32)
+    x = x[np.abs(x) < 448]
+    got = O.f32_to_fp8_e4m3(x)
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(got, ref), int((got != ref).sum())
+    table = O.fp8_e4m3_to_f64(np.arange(0x7F, dtype=np.uint8))
+    for xi, ci in zip(x[:300], got[:300]):
+        d = np.abs(table - abs(float(xi)))
+        assert d[int(ci) & 0x7F] == d.min()
+
+
+def pin_fp8_cache_write():
+    """New rows are stored as E4M3(x / scale), the quotient in fp32 (torch's
+    float8_e4m3fn conversion of the same quotient), K with k_scale and V with
+    v_scale, at the same slots as the bf16 write; the dequantised cache holds
+    code * scale per plane."""
+    rng = _rng(78)
+    nb, bs, H, D, T = 6, 16, 2, 8, 5
+    cache = np.zeros((nb, 2, bs, H, D), np.uint8)
+    k = (rng.standard_normal((T, H, D)) * 3).astype(np.float32)
+    v = (rng.standard_normal((T, H, D)) * 0.02).astype(np.float32)
+    kb = (k.view(np.uint32) >> 16).astype(np.uint16)
+    vb = (v.view(np.uint32) >> 16).astype(np.uint16)
+    ks, vs = 0.05, 0.0003
+    slots = np.array([3, 17, 40, -1, 95])
+    out = O.cache_write_kv_fp8(cache, kb, vb, slots, ks, vs)
+    for t, sl in enumerate(slots):
+        if sl < 0:
+            continue
+        blk, off = divmod(int(sl), bs)
+        for plane, bits, sc in ((0, kb, ks), (1, vb, vs)):
+            qf = torch.from_numpy((bits[t].astype(np.uint32) << 16).view(np.float32)) / torch.tensor(
+                sc, dtype=torch.float32)
+            want = qf.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+            assert np.array_equal(out[blk, plane, off], want), (t, plane)
+    written = {divmod(int(sl), bs) for sl in slots if sl >= 0}
+    for blk in range(nb):
+        for off in range(bs):
+            if (blk, off) not in written:
+                assert not out[blk, :, off].any()
+    deq = O.dequant_kv_cache(out, ks, vs)
+    ref = torch.from_numpy(out).view(torch.float8_e4m3fn).double().numpy()
+    assert np.array_equal(deq[:, 0], ref[:, 0] * ks) and np.array_equal(deq[:, 1], ref[:, 1] * vs)
+
+
 ALL_PINS = [
     pin_bf16_decoding, pin_go_program_slots, pin_go_program_identical,
     pin_num_kv_splits, pin_cache_write_bytes, pin_fig5c_merge, pin_merge_edges,
     pin_closed_forms, pin_torch_sdpa_gqa, pin_torch_sdpa_mla,
     pin_bruteforce_varlen, pin_split_merge_equals_unsplit, pin_block_permutation,
-    pin_chunked_prefill,
+    pin_chunked_prefill, pin_fp8_e4m3_decoding, pin_fp8_e4m3_encoding, pin_fp8_cache_write,
 ]

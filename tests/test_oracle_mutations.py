@@ -1,7 +1,9 @@
 """Plant plausible mistakes in the oracle (on the CPU) and check that the pins
 catch every one: a dropped scale, a wrong KV-head map, an off-by-one causal
 mask, a transposed operand, a wrong log base, a wrong block walk, swapped K/V
-halves, a linear (not exponential) merge weight, a floor in the split count."""
+halves, a linear (not exponential) merge weight, a floor in the split count,
+an FP8 decoding with the wrong exponent bias, FP8 rounding toward zero,
+swapped K/V dequantisation scales."""
 import numpy as np
 import pytest
 
@@ -59,6 +61,29 @@ def _merge_linear(outs, lses):
     return (w[..., None] * outs).sum(axis=-2) / tot[..., None], np.log(tot)
 
 
+_fp8_dec = O.fp8_e4m3_to_f64
+_f32_to_fp8 = O.f32_to_fp8_e4m3
+_dequant = O.dequant_kv_cache
+
+
+def _fp8_bias8(codes):
+    """E4M3 decoded with exponent bias 8 (another FP8 variant's)."""
+    return _fp8_dec(codes) / 2.0
+
+
+def _fp8_truncate(x):
+    """Round toward zero instead of to nearest."""
+    x = np.asarray(x, np.float32)
+    table = _fp8_dec(np.arange(0x7F, dtype=np.uint8))
+    a = np.minimum(np.abs(x).astype(np.float64), 448.0)
+    c = np.clip(np.searchsorted(table, a, side="right") - 1, 0, 0x7E).astype(np.uint8)
+    return np.where(np.signbit(x), c | np.uint8(0x80), c).astype(np.uint8)
+
+
+def _dequant_swapped(cache, k_scale, v_scale):
+    return _dequant(cache, v_scale, k_scale)
+
+
 MUTATIONS = {
     "drop_scale": ("attention", _attention_variant(drop_scale=True)),
     "kv_head_modulo": ("attention", _attention_variant(kv_map=lambda h, Hq, Hkv: h % Hkv)),
@@ -71,6 +96,9 @@ MUTATIONS = {
     "linear_merge_weight": ("lse_merge", _merge_linear),
     "split_count_floor": ("num_kv_splits", lambda m, c: int(min(max(int(m) // 512, 1), 2 * c))),
     "slot_uses_block_size_one": ("slot_of", lambda row, p, bs: int(row[p // bs]) + p % bs),
+    "fp8_exponent_bias_8": ("fp8_e4m3_to_f64", _fp8_bias8),
+    "fp8_round_toward_zero": ("f32_to_fp8_e4m3", _fp8_truncate),
+    "fp8_swapped_plane_scales": ("dequant_kv_cache", _dequant_swapped),
 }
 
 
