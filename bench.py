@@ -6,7 +6,8 @@ cache write, the attention kernel(s) and, for split-KV decode, the LSE merge.
 The headline line measures the Llama-3-8B-shaped GQA decode (64 requests,
 seq_len U[512, 8192], 32 q / 8 kv heads, d=128, bf16, block 16) in HBM GB/s;
 the other workloads (tiny fp32 decode, chunked prefill, long-context decode,
-MLA decode, a mixed prefill + decode batch, a batch sharing a prefix) are measured the same way and
+MLA decode, a mixed prefill + decode batch, a batch sharing a prefix, decode
+over an FP8 cache) are measured the same way and
 reported under "workloads".  Inputs are generated on the host by ``workloads.py`` (seeded),
 uploaded once, and resident in HBM before any timed region.
 
@@ -295,6 +296,46 @@ def cascade_case(b, name):
                  "plain_decode_reads_GB": round((int(b.seq_lens.sum()) * row * 2) / 1e9, 3)})
 
 
+def fp8_decode_case(b, name):
+    """Decode over an FP8 (E4M3) cache: write + token-balanced decode +
+    merge.  The timed kernel is the whole decode call (decode kernel and
+    segment merge), priced against HBM with one byte per cached element."""
+    import torch
+    import paged_kv_attention_pa_amd as pa
+    import workloads as W
+    cache = torch.from_numpy(b.cache).cuda()
+    q = _dev(b.q)
+    bt, sl = _dev(b.block_table), _dev(b.seq_lens)
+    kn, vn, sm = _dev(b.k_new), _dev(b.v_new), _dev(b.slot_mapping)
+    cus = pa.device_num_cus()
+    nr = pa.decode_balanced_num_ranges(b.num_kv_heads, cus)
+    ws = torch.empty(max(1, pa.decode_balanced_workspace_bytes(b.num_seqs, b.num_q_heads,
+                                                               b.head_dim, nr) // 4),
+                     dtype=torch.float32, device="cuda")
+    out = torch.empty_like(q)
+    lse = torch.empty(b.q.shape[:2], dtype=torch.float32, device="cuda")
+
+    def step():
+        pa.decode_fp8(q, cache, bt, sl, b.scale, b.k_scale, b.v_scale, k=kn, v=vn,
+                      slot_mapping=sm, num_ranges=nr, workspace=ws, out=out, lse=lse)
+
+    def kernel():
+        pa.decode_fp8(q, cache, bt, sl, b.scale, b.k_scale, b.v_scale, num_ranges=nr,
+                      workspace=ws, out=out, lse=lse)
+
+    by = W.gqa_bytes(b)
+    kb = by["kv"] + by["q"] + by["meta"] - b.num_tokens * 8
+    fl = W.gqa_flops(b)
+    g = b.num_q_heads // b.num_kv_heads
+    info = {"num_seqs": b.num_seqs, "num_q_heads": b.num_q_heads, "num_kv_heads": b.num_kv_heads,
+            "head_dim": b.head_dim, "block_size": b.block_size, "cache_dtype": "fp8_e4m3",
+            "k_scale": b.k_scale, "v_scale": b.v_scale, "max_seq_len": b.max_seq_len,
+            "total_keys": int(b.seq_lens.sum()), "schedule": "token-balanced ranges",
+            "timed": "decode kernel + segment merge"}
+    return Case(name, step, kernel, by["total"], fl, kb, fl, "hbm",
+                f"decode_balanced_kernel<{g}, true> + merge", "decode_balanced.hip", info)
+
+
 def build_cases(only):
     import workloads as W
     makers = {
@@ -307,6 +348,7 @@ def build_cases(only):
         "mla_latent_decode_bf16": lambda: mla_case(W.mla_decode_batch(), "mla_latent_decode_bf16"),
         W.MIXED: lambda: mixed_case(W.mixed_batch(), W.MIXED),
         W.CASCADE: lambda: cascade_case(W.cascade_batch(), W.CASCADE),
+        W.FP8_DECODE: lambda: fp8_decode_case(W.llama_decode_fp8(), W.FP8_DECODE),
     }
     names = [HEADLINE] + [n for n in makers if n != HEADLINE]
     if only is not None:

@@ -466,6 +466,53 @@ pa_status_t pa_cascade_attention(const pa_cascade_plan_t* plan, pa_dtype_t dtype
                                  float scale, void* workspace, size_t workspace_bytes,
                                  void* out, float* lse, hipStream_t stream);
 
+/* ---------------------------------------------------------------------------
+ * FP8 KV cache with per-tensor scales.
+ *
+ * The cache holds one E4M3 byte per element instead of a bf16 pair: a key
+ * element is stored as code = E4M3(k / k_scale) and read back as
+ * E4M3(code) * k_scale (values likewise with v_scale); the query and the
+ * output stay bf16 ("Triton 與 MLA", 資料流: the layer's k_scale / v_scale are
+ * passed to the kernel, v_scale = k_scale for the latent cache; 邊界與失敗:
+ * with an FP8 cache the kernel dequantises and the query is not quantised).
+ * Format: OCP FP8 E4M3 (bias 7, 3 mantissa bits, largest finite 448, no
+ * infinities).  Quantisation: the quotient in fp32 (correctly rounded), then
+ * the nearest E4M3 value, ties to even, magnitudes above 448 saturated.
+ * Layouts are the bf16 ones with 1-byte elements: GQA [num_blocks, 2,
+ * block_size, num_kv_heads, head_dim] uint8, MLA [num_blocks, block_size,
+ * kv_lora_rank + rope_dim] uint8.  Scales: finite and > 0.
+ *
+ * pa_cache_write_fp8: pa_cache_write with bf16 inputs quantised on the way
+ * in (layout PA_LAYOUT_KV: k with k_scale, v with v_scale; PA_LAYOUT_MLA:
+ * k = kv_c, v = k_pe, the whole row with k_scale, v_scale unused).
+ *
+ * pa_decode_fp8: GQA decode (one query row per request, as pa_decode) over
+ * an FP8 cache, on the token-balanced schedule: num_ranges = 0 picks
+ * pa_decode_balanced_num_ranges(num_kv_heads, pa_device_num_cus());
+ * workspace of pa_decode_balanced_workspace_bytes(num_seqs, num_q_heads,
+ * head_dim, num_ranges) bytes, 16-byte aligned.  Enqueues the write (if k,
+ * v, slot_mapping are given), the decode kernel and the segment merge.
+ * q [num_seqs, num_q_heads, 128] bf16, out the same, lse [num_seqs,
+ * num_q_heads] fp32 or NULL.  Supported: head_dim 128, num_q_heads /
+ * num_kv_heads in {1, 2, 4, 8}, num_kv_heads 1, 2, 4 or a multiple of 8.
+ * ------------------------------------------------------------------------- */
+pa_status_t pa_cache_write_fp8(pa_layout_t layout,
+                               const void* k, int64_t k_token_stride,
+                               const void* v, int64_t v_token_stride,
+                               void* kv_cache, int64_t num_blocks, int block_size,
+                               int num_kv_heads, int head_dim,
+                               const int64_t* slot_mapping, int num_tokens,
+                               float k_scale, float v_scale, hipStream_t stream);
+
+pa_status_t pa_decode_fp8(const void* q, const void* k, const void* v,
+                          void* kv_cache, int64_t num_blocks, int block_size,
+                          const int32_t* block_table, int max_blocks_per_seq,
+                          const int64_t* slot_mapping, const int32_t* seq_lens, int num_seqs,
+                          int num_q_heads, int num_kv_heads, int head_dim,
+                          float scale, float k_scale, float v_scale, int num_ranges,
+                          void* workspace, size_t workspace_bytes,
+                          void* out, float* lse, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

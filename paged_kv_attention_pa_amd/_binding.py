@@ -50,6 +50,10 @@ _SIGNATURES = {
     "pa_mixed_attention": (_i32, [_vp, _i32, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _vp, _vp, _f32,
                                   _vp, _sz, _vp, _vp, _vp]),
     "pa_plan_cascade": (_i32, [_vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp]),
+    "pa_cache_write_fp8": (_i32, [_i32, _vp, _i64, _vp, _i64, _vp, _i64, _i32, _i32, _i32, _vp,
+                                  _i32, _f32, _f32, _vp]),
+    "pa_decode_fp8": (_i32, [_vp, _vp, _vp, _vp, _i64, _i32, _vp, _i32, _vp, _vp, _i32, _i32,
+                             _i32, _i32, _f32, _f32, _f32, _i32, _vp, _sz, _vp, _vp, _vp]),
     "pa_cascade_attention": (_i32, [_vp, _i32, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _vp, _vp,
                                     _f32, _vp, _sz, _vp, _vp, _vp]),
 }
@@ -258,6 +262,71 @@ def cache_write(kv_cache, k, v, slot_mapping, layout: int = PA_LAYOUT_KV, stream
     _need(slot_mapping.numel() == T, "slot_mapping must have one entry per token")
     _check(library().pa_cache_write(layout, dt, _ptr(k), ks, _ptr(v), vs, _ptr(kv_cache), nb, bs,
                                     hkv, d, _ptr(slot_mapping), T, _stream(stream)))
+
+
+def _fp8_cache(kv_cache):
+    torch = _torch()
+    _need(kv_cache.dtype in (torch.uint8, getattr(torch, "float8_e4m3fn", torch.uint8)),
+          "an FP8 cache is uint8 (or float8_e4m3fn) storage")
+
+
+def cache_write_fp8(kv_cache, k, v, slot_mapping, k_scale: float, v_scale: float = 1.0,
+                    layout: int = PA_LAYOUT_KV, stream=None):
+    """Quantise bf16 rows to E4M3 (x / scale) and store them at slot_mapping.
+    GQA: k, v [T, Hkv, D] into kv_cache [nb, 2, bs, Hkv, D] uint8.  MLA: k =
+    kv_c [T, R], v = k_pe [T, 64] into kv_cache [nb, bs, R + 64] uint8, the
+    row with k_scale."""
+    torch = _torch()
+    _dev(kv_cache, k, v, slot_mapping)
+    _fp8_cache(kv_cache)
+    _int_tensor(slot_mapping, "int64", "slot_mapping")
+    _need(k.dtype == torch.bfloat16 and v.dtype == torch.bfloat16, "k/v must be bf16")
+    T = k.shape[0]
+    if layout == PA_LAYOUT_KV:
+        nb, _, bs, hkv, d = kv_cache.shape
+        _need(tuple(k.shape) == (T, hkv, d) and tuple(v.shape) == (T, hkv, d), "k/v shape mismatch")
+        ks = vs = hkv * d
+    else:
+        nb, bs, row = kv_cache.shape
+        hkv, d = 1, row
+        ks, vs = k.shape[1], v.shape[1]
+        _need(ks + vs == row, "kv_c/k_pe widths must add up to the cache row")
+    _need(slot_mapping.numel() == T, "slot_mapping must have one entry per token")
+    _check(library().pa_cache_write_fp8(layout, _ptr(k), ks, _ptr(v), vs, _ptr(kv_cache), nb, bs,
+                                        hkv, d, _ptr(slot_mapping), T, float(k_scale),
+                                        float(v_scale), _stream(stream)))
+
+
+def decode_fp8(q, kv_cache, block_table, seq_lens, scale: float, k_scale: float, v_scale: float,
+               k=None, v=None, slot_mapping=None, num_ranges: int = 0, workspace=None, out=None,
+               lse=None, return_lse: bool = True, stream=None):
+    """GQA decode over an FP8 (E4M3) cache [nb, 2, bs, Hkv, D] uint8 with
+    per-tensor k_scale / v_scale; q bf16 [B, Hq, D].  Token-balanced schedule
+    (num_ranges = 0: one range per CU for 8 KV heads).  Returns (out, lse)."""
+    torch = _torch()
+    _dev(q, kv_cache, block_table, seq_lens, k, v, slot_mapping, workspace, out, lse)
+    _fp8_cache(kv_cache)
+    _int_tensor(block_table, "int32", "block_table")
+    _int_tensor(seq_lens, "int32", "seq_lens")
+    _need(q.dtype == torch.bfloat16, "q must be bf16")
+    B, Hq, D = q.shape
+    nb, _, bs, hkv, d2 = kv_cache.shape
+    _need(d2 == D, "head_dim mismatch")
+    nr = int(num_ranges) or decode_balanced_num_ranges(hkv, device_num_cus())
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and return_lse:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        need = decode_balanced_workspace_bytes(B, Hq, D, nr)
+        workspace = torch.empty(max(1, need // 4), dtype=torch.float32, device=q.device)
+    wbytes = workspace.numel() * workspace.element_size()
+    _check(library().pa_decode_fp8(_ptr(q), _ptr(k), _ptr(v), _ptr(kv_cache), nb, bs,
+                                   _ptr(block_table), block_table.shape[1], _ptr(slot_mapping),
+                                   _ptr(seq_lens), B, Hq, hkv, D, float(scale), float(k_scale),
+                                   float(v_scale), nr, _ptr(workspace), wbytes, _ptr(out),
+                                   _ptr(lse), _stream(stream)))
+    return out, lse
 
 
 def decode(q, kv_cache, block_table, seq_lens, max_seq_len: int, scale: float,

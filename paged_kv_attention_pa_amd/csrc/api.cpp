@@ -8,6 +8,7 @@
 
 #include <atomic>
 #include <climits>
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -928,6 +929,130 @@ pa_status_t pa_cascade_attention(const pa_cascade_plan_t* plan, pa_dtype_t dtype
   e = pa::launch_cascade_merge(m, stream);
   if (e != hipSuccess) return hip_fail(e, "cascade merge launch");
   return ok();
+}
+
+// ---------------------------------------------------------------------------
+static bool fp8_scale_ok(float s) { return std::isfinite(s) && s > 0.0f; }
+
+// Checks of an FP8 write (no device work).
+static pa_status_t check_write_fp8(pa_layout_t layout, const void* k, int64_t k_token_stride,
+                                   const void* v, int64_t v_token_stride, const void* kv_cache,
+                                   int64_t num_blocks, int block_size, int num_kv_heads,
+                                   int head_dim, const int64_t* slot_mapping, int num_tokens,
+                                   float k_scale, float v_scale) {
+  PA_REQUIRE(num_tokens >= 0, PA_ERR_INVALID, "num_tokens must be >= 0");
+  PA_REQUIRE(num_blocks > 0, PA_ERR_INVALID, "num_blocks must be > 0");
+  PA_REQUIRE(block_size > 0 && block_size % 16 == 0, PA_ERR_INVALID,
+             "block_size must be a positive multiple of 16 (got %d)", block_size);
+  PA_REQUIRE(head_dim > 0 && num_kv_heads > 0, PA_ERR_INVALID, "head_dim and num_kv_heads must be > 0");
+  PA_REQUIRE(layout == PA_LAYOUT_KV || layout == PA_LAYOUT_MLA, PA_ERR_INVALID, "unknown layout %d",
+             int(layout));
+  PA_REQUIRE(fp8_scale_ok(k_scale) && (layout == PA_LAYOUT_MLA || fp8_scale_ok(v_scale)),
+             PA_ERR_INVALID, "FP8 scales must be finite and > 0");
+  if (layout == PA_LAYOUT_KV) {
+    PA_REQUIRE(k_token_stride >= int64_t(num_kv_heads) * head_dim &&
+                   v_token_stride >= int64_t(num_kv_heads) * head_dim,
+               PA_ERR_INVALID, "token strides must be >= num_kv_heads * head_dim");
+  } else {
+    PA_REQUIRE(num_kv_heads == 1, PA_ERR_INVALID, "the MLA layout has one KV head");
+    PA_REQUIRE(head_dim > 64, PA_ERR_INVALID, "MLA head_dim must be kv_lora_rank + 64");
+    PA_REQUIRE(k_token_stride >= head_dim - 64 && v_token_stride >= 64, PA_ERR_INVALID,
+               "token strides must cover kv_lora_rank / rope_dim");
+  }
+  if (num_tokens == 0) return ok();
+  PA_REQUIRE(k && v && kv_cache && slot_mapping, PA_ERR_INVALID,
+             "k, v, kv_cache and slot_mapping must be non-null");
+  return ok();
+}
+
+static pa_status_t enqueue_write_fp8(pa_layout_t layout, const void* k, int64_t k_token_stride,
+                                     const void* v, int64_t v_token_stride, void* kv_cache,
+                                     int64_t num_blocks, int block_size, int num_kv_heads,
+                                     int head_dim, const int64_t* slot_mapping, int num_tokens,
+                                     float k_scale, float v_scale, hipStream_t stream) {
+  if (num_tokens == 0) return ok();
+  const bool mla = layout == PA_LAYOUT_MLA;
+  pa::CacheWriteFp8 a{mla ? 1 : 0, k, k_token_stride, v, v_token_stride, kv_cache, num_blocks,
+                      block_size, num_kv_heads, head_dim, mla ? head_dim - 64 : 0, mla ? 64 : 0,
+                      slot_mapping, num_tokens, k_scale, mla ? k_scale : v_scale};
+  hipError_t e = pa::launch_cache_write_fp8(a, stream);
+  if (e != hipSuccess) return hip_fail(e, "fp8 cache write launch");
+  return ok();
+}
+
+pa_status_t pa_cache_write_fp8(pa_layout_t layout, const void* k, int64_t k_token_stride,
+                               const void* v, int64_t v_token_stride, void* kv_cache,
+                               int64_t num_blocks, int block_size, int num_kv_heads, int head_dim,
+                               const int64_t* slot_mapping, int num_tokens, float k_scale,
+                               float v_scale, hipStream_t stream) {
+  pa_status_t st = check_write_fp8(layout, k, k_token_stride, v, v_token_stride, kv_cache,
+                                   num_blocks, block_size, num_kv_heads, head_dim, slot_mapping,
+                                   num_tokens, k_scale, v_scale);
+  if (st != PA_OK) return st;
+  return enqueue_write_fp8(layout, k, k_token_stride, v, v_token_stride, kv_cache, num_blocks,
+                           block_size, num_kv_heads, head_dim, slot_mapping, num_tokens, k_scale,
+                           v_scale, stream);
+}
+
+pa_status_t pa_decode_fp8(const void* q, const void* k, const void* v, void* kv_cache,
+                          int64_t num_blocks, int block_size, const int32_t* block_table,
+                          int max_blocks_per_seq, const int64_t* slot_mapping,
+                          const int32_t* seq_lens, int num_seqs, int num_q_heads,
+                          int num_kv_heads, int head_dim, float scale, float k_scale,
+                          float v_scale, int num_ranges, void* workspace, size_t workspace_bytes,
+                          void* out, float* lse, hipStream_t stream) {
+  PA_REQUIRE(scale_ok(scale), PA_ERR_INVALID, "scale must be finite and >= 0");
+  PA_REQUIRE(fp8_scale_ok(k_scale) && fp8_scale_ok(v_scale), PA_ERR_INVALID,
+             "FP8 scales must be finite and > 0");
+  PA_REQUIRE(num_seqs >= 0, PA_ERR_INVALID, "num_seqs must be >= 0 (got %d)", num_seqs);
+  pa_status_t st = check_common_cache(num_blocks, block_size, block_table, max_blocks_per_seq,
+                                      seq_lens, num_seqs, 0);
+  if (st != PA_OK) return st;
+  PA_REQUIRE(num_q_heads > 0 && num_kv_heads > 0 && num_q_heads % num_kv_heads == 0,
+             PA_ERR_INVALID, "num_q_heads (%d) must be a positive multiple of num_kv_heads (%d)",
+             num_q_heads, num_kv_heads);
+  PA_REQUIRE(head_dim == 128, PA_ERR_UNSUPPORTED, "FP8 decode supports head_dim 128 (got %d)",
+             head_dim);
+  PA_REQUIRE(is_pow2_group(num_q_heads / num_kv_heads), PA_ERR_UNSUPPORTED,
+             "FP8 decode supports num_q_heads / num_kv_heads in {1, 2, 4, 8} (got %d)",
+             num_q_heads / num_kv_heads);
+  PA_REQUIRE(balanced_heads_ok(num_kv_heads), PA_ERR_UNSUPPORTED,
+             "FP8 decode supports num_kv_heads 1, 2, 4 or a multiple of 8 (got %d)", num_kv_heads);
+  PA_REQUIRE(num_ranges >= 0, PA_ERR_INVALID, "num_ranges must be >= 0");
+  PA_REQUIRE((k == nullptr) == (v == nullptr), PA_ERR_INVALID, "k and v must both be given or both NULL");
+  PA_REQUIRE(k == nullptr || slot_mapping != nullptr, PA_ERR_INVALID, "k/v given without slot_mapping");
+  PA_REQUIRE(slot_mapping == nullptr || k != nullptr, PA_ERR_INVALID, "slot_mapping given without k/v");
+  int nr = num_ranges;
+  if (nr == 0) {
+    const int cus = pa_device_num_cus();
+    if (cus <= 0) return fail(PA_ERR_HIP, "cannot query the device's compute units");
+    nr = pa_decode_balanced_num_ranges(num_kv_heads, cus);
+  }
+  st = check_balanced(num_seqs, num_q_heads, head_dim, max_blocks_per_seq, block_size, nr,
+                      workspace, workspace_bytes);
+  if (st != PA_OK) return st;
+  if (num_seqs == 0) return ok();
+  PA_REQUIRE(q && kv_cache && out, PA_ERR_INVALID, "q, kv_cache and out must be non-null");
+  if (k) {
+    st = check_write_fp8(PA_LAYOUT_KV, k, int64_t(num_kv_heads) * head_dim, v,
+                         int64_t(num_kv_heads) * head_dim, kv_cache, num_blocks, block_size,
+                         num_kv_heads, head_dim, slot_mapping, num_seqs, k_scale, v_scale);
+    if (st != PA_OK) return st;
+    st = enqueue_write_fp8(PA_LAYOUT_KV, k, int64_t(num_kv_heads) * head_dim, v,
+                           int64_t(num_kv_heads) * head_dim, kv_cache, num_blocks, block_size,
+                           num_kv_heads, head_dim, slot_mapping, num_seqs, k_scale, v_scale,
+                           stream);
+    if (st != PA_OK) return st;
+  }
+  const int64_t cap = int64_t(max_blocks_per_seq) * block_size;
+  pa::DecodeBalanced d{q, kv_cache, num_blocks, block_size, block_table, max_blocks_per_seq,
+                       seq_lens, num_seqs, int(cap > INT_MAX ? INT_MAX : cap), num_q_heads,
+                       num_kv_heads, scale, nr, balanced_cu(workspace),
+                       balanced_part(workspace, num_seqs), out, lse, 1, k_scale, v_scale};
+  hipError_t e = pa::launch_decode_balanced(d, stream);
+  if (e != hipSuccess) return hip_fail(e, "fp8 decode launch");
+  return pa_decode_balanced_merge(workspace, workspace_bytes, num_seqs, num_q_heads, head_dim, nr,
+                                  out, lse, stream);
 }
 
 }  // extern "C"

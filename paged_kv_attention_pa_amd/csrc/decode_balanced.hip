@@ -31,7 +31,12 @@ constexpr int kRow = kD * 2 + 16;       // LDS row of a token: 256 B + 16 B pad
 constexpr int kTile = kChunk * kRow;    // per-wave tile (K, then V)
 constexpr int kHeads = 8;               // KV heads (waves) per work-group
 
-template <int G>
+// kFp8: the cache holds E4M3 codes (one byte per element); the loads fetch
+// half the bytes, each 16-byte piece is widened to bf16 on its way into LDS
+// (exact), and the scales fold into the score scale (k_scale) and the final
+// normalisation (v_scale), so the tiles and everything after them are the
+// bf16 kernel's.
+template <int G, bool kFp8>
 __global__ __launch_bounds__(64 * kHeads, 1) void decode_balanced_kernel(DecodeBalanced a) {
   static_assert(G >= 1 && G <= 16, "group must fit the 16 MFMA columns");
   __shared__ __align__(16) char smem[2 * kHeads * kTile];   // K tiles of every head, then V tiles
@@ -61,9 +66,11 @@ __global__ __launch_bounds__(64 * kHeads, 1) void decode_balanced_kernel(DecodeB
   const int bs = a.block_size;
   const int64_t tok_stride = int64_t(Hkv) * kD;
   const int64_t kv_stride = int64_t(bs) * tok_stride;
-  const uint16_t* cache = static_cast<const uint16_t*>(a.cache);
   const uint16_t* qbase = static_cast<const uint16_t*>(a.q);
-  const float scale2 = a.scale * kLog2e;
+  const float scale2 = (kFp8 ? a.scale * a.k_scale : a.scale) * kLog2e;
+  constexpr int kElem = kFp8 ? 1 : 2;           // cache bytes per element
+  constexpr int kLoads = kFp8 ? 4 : 8;          // 16-byte loads per lane per plane and chunk
+  constexpr int kRowShift = kFp8 ? 7 : 8;       // log2 of a head row's cache bytes
 
   const int waves = blockDim.x >> 6;
   const char* const a_base = smem + wave * kTile + li * kRow + 16 * kq;             // K: row 16 sub + li
@@ -74,9 +81,9 @@ __global__ __launch_bounds__(64 * kHeads, 1) void decode_balanced_kernel(DecodeB
   // slice .., byte (1024 I + 16 l) % slice of the slice, i.e. head
   // byte / 256, 16-byte chunk (byte % 256) / 16.
   const int lw = waves == 8 ? 3 : waves == 4 ? 2 : waves == 2 ? 1 : 0;
-  const int sh = 8 + lw;                       // log2 of the slice bytes
-  const char* cache_b = static_cast<const char*>(a.cache) + int64_t(hg) * kHeads * kD * 2;
-  const int64_t tok_bytes = tok_stride * 2, kv_bytes = kv_stride * 2;
+  const int sh = kRowShift + lw;               // log2 of the slice bytes
+  const char* cache_b = static_cast<const char*>(a.cache) + int64_t(hg) * kHeads * kD * kElem;
+  const int64_t tok_bytes = tok_stride * kElem, kv_bytes = kv_stride * kElem;
 
   // Q^T columns: lane li holds query head h G + (li mod G); the columns past G
   // repeat real rows and their results are never stored.
@@ -96,12 +103,12 @@ __global__ __launch_bounds__(64 * kHeads, 1) void decode_balanced_kernel(DecodeB
   const uint64_t page_bytes = 2 * uint64_t(bs) * uint64_t(tok_bytes);
   const uint32_t tok32 = uint32_t(tok_bytes);
   const uint32_t nblk = uint32_t(min(a.num_blocks, int64_t(INT32_MAX)));
-  auto load_half = [&](const ChunkPos& p, int64_t plane, u32x4_t (&dst)[8]) {
+  auto load_half = [&](const ChunkPos& p, int64_t plane, u32x4_t (&dst)[kLoads]) {
     const int32_t* table = a.block_table + int64_t(p.r) * a.max_blocks;
     const int len = max(p.len, 1);   // positions always hold keys; keeps every index >= 0
     const char* base_p = cache_b + plane;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < kLoads; ++i) {
       const int I = wave + waves * i;
       const int lin = I * 1024 + 16 * lane;
       const int tl_first = (I * 1024) >> sh;                       // first token of the piece
@@ -114,18 +121,20 @@ __global__ __launch_bounds__(64 * kHeads, 1) void decode_balanced_kernel(DecodeB
       dst[i] = load16(base_p + blk * page_bytes + (uint32_t(tok - page * bs) * tok32 + uint32_t(byte)));
     }
   };
-  // LDS position of this lane's piece i (head tile, token row, chunk)
+  // LDS position of this lane's piece i (head tile, token row, byte of the
+  // bf16 row)
   auto lds_off = [&](int i) {
     const int lin = (wave + waves * i) * 1024 + 16 * lane;
     const int byte = lin & ((1 << sh) - 1);
-    return (byte >> 8) * kTile + (lin >> sh) * kRow + (byte & 255);
+    return (byte >> kRowShift) * kTile + (lin >> sh) * kRow +
+           (byte & ((1 << kRowShift) - 1)) * (2 / kElem);
   };
 
   ChunkPos nxt = c0 + 1 < c1 ? next_chunk(cur, a.seq_lens, cap, B) : cur;
 
   u32x4_t qf[4];
   load_q(cur.r, qf);
-  u32x4_t kr[8], vr[8];
+  u32x4_t kr[kLoads], vr[kLoads];
   load_half(cur, 0, kr);
   load_half(cur, kv_bytes, vr);
 
@@ -138,10 +147,20 @@ __global__ __launch_bounds__(64 * kHeads, 1) void decode_balanced_kernel(DecodeB
     // this chunk's pieces into every head's K and V tiles; once all waves'
     // are there, the registers are refilled with the next chunk
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < kLoads; ++i) {
       const int o = lds_off(i);
-      *reinterpret_cast<u32x4_t*>(smem + o) = kr[i];
-      *reinterpret_cast<u32x4_t*>(smem + kHeads * kTile + o) = vr[i];
+      if constexpr (kFp8) {
+        u32x4_t lo, hi;
+        fp8x16_to_bf16(kr[i], lo, hi);
+        *reinterpret_cast<u32x4_t*>(smem + o) = lo;
+        *reinterpret_cast<u32x4_t*>(smem + o + 16) = hi;
+        fp8x16_to_bf16(vr[i], lo, hi);
+        *reinterpret_cast<u32x4_t*>(smem + kHeads * kTile + o) = lo;
+        *reinterpret_cast<u32x4_t*>(smem + kHeads * kTile + o + 16) = hi;
+      } else {
+        *reinterpret_cast<u32x4_t*>(smem + o) = kr[i];
+        *reinterpret_cast<u32x4_t*>(smem + kHeads * kTile + o) = vr[i];
+      }
     }
     __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's LDS stores are done
     __builtin_amdgcn_s_barrier();
@@ -205,7 +224,7 @@ __global__ __launch_bounds__(64 * kHeads, 1) void decode_balanced_kernel(DecodeB
     if (tok0 + kChunk >= cur.len || c + 1 == c1) {
       const float l_w = l_run + lane_xor(l_run, 16);
       const float l_tot = l_w + lane_xor(l_w, 32);
-      const float inv = 1.0f / l_tot;
+      const float inv = (kFp8 ? a.v_scale : 1.0f) / l_tot;
       const float lse_nat = (m_run + fast_log2(l_tot)) * kLn2;
       const bool whole = cur.base >= c0 && cur.base + chunks_of(cur.len) <= c1;
       if (li < G) {
@@ -382,11 +401,21 @@ hipError_t launch_decode_balanced(const DecodeBalanced& a, hipStream_t s) {
   const int n_hg = (a.num_kv_heads + kHeads - 1) / kHeads;
   const int waves = a.num_kv_heads < kHeads ? a.num_kv_heads : kHeads;
   const dim3 grid{unsigned(int64_t(a.num_ranges) * n_hg)}, block{unsigned(64 * waves)};
+  if (a.fp8) {
+    switch (G) {
+      case 1: hipLaunchKernelGGL((decode_balanced_kernel<1, true>), grid, block, 0, s, a); break;
+      case 2: hipLaunchKernelGGL((decode_balanced_kernel<2, true>), grid, block, 0, s, a); break;
+      case 4: hipLaunchKernelGGL((decode_balanced_kernel<4, true>), grid, block, 0, s, a); break;
+      case 8: hipLaunchKernelGGL((decode_balanced_kernel<8, true>), grid, block, 0, s, a); break;
+      default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  }
   switch (G) {
-    case 1: hipLaunchKernelGGL((decode_balanced_kernel<1>), grid, block, 0, s, a); break;
-    case 2: hipLaunchKernelGGL((decode_balanced_kernel<2>), grid, block, 0, s, a); break;
-    case 4: hipLaunchKernelGGL((decode_balanced_kernel<4>), grid, block, 0, s, a); break;
-    case 8: hipLaunchKernelGGL((decode_balanced_kernel<8>), grid, block, 0, s, a); break;
+    case 1: hipLaunchKernelGGL((decode_balanced_kernel<1, false>), grid, block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((decode_balanced_kernel<2, false>), grid, block, 0, s, a); break;
+    case 4: hipLaunchKernelGGL((decode_balanced_kernel<4, false>), grid, block, 0, s, a); break;
+    case 8: hipLaunchKernelGGL((decode_balanced_kernel<8, false>), grid, block, 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

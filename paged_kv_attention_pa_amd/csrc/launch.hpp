@@ -27,6 +27,21 @@ struct CacheWriteMLA {
 };
 hipError_t launch_cache_write_mla(const CacheWriteMLA& a, hipStream_t s);
 
+// FP8 (E4M3) cache writes: bf16 rows in, code = E4M3(x / scale) stored.
+// GQA layout [nb, 2, bs, Hkv, D] (K with k_scale, V with v_scale); MLA layout
+// [nb, bs, rank + rope] with one scale for the row (k_scale).
+struct CacheWriteFp8 {
+  int mla;
+  const void* k; int64_t k_stride;   // GQA k or MLA kv_c; stride in elements
+  const void* v; int64_t v_stride;   // GQA v or MLA k_pe
+  void* cache; int64_t num_blocks; int block_size;
+  int num_kv_heads; int head_dim;    // GQA
+  int rank; int rope;                // MLA
+  const int64_t* slots; int num_tokens;
+  float k_scale; float v_scale;
+};
+hipError_t launch_cache_write_fp8(const CacheWriteFp8& a, hipStream_t s);
+
 // ---------------------------------------------------------------- decode
 struct DecodeGQA {
   int bf16;                      // 1: bf16 storage, 0: fp32
@@ -67,6 +82,8 @@ struct DecodeBalanced {
   int num_ranges;
   int32_t* cu; float* part;
   void* out; float* lse;
+  // FP8 (E4M3) cache: keys are code * k_scale, values code * v_scale
+  int fp8; float k_scale; float v_scale;
 };
 hipError_t launch_decode_balanced(const DecodeBalanced& a, hipStream_t s);
 

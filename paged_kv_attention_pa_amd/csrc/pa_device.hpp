@@ -199,6 +199,32 @@ __device__ __forceinline__ float xor32_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// ------------------------------------------------------- FP8 (E4M3) codes
+// Sixteen E4M3 codes -> sixteen bf16 values, element i to element i
+// (v_cvt_scalef32_pk_bf16_fp8 with scale 1: exact, every E4M3 value is a
+// bf16 value).  lo gets codes 0..7, hi codes 8..15.
+template <bool kUpper>
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, kUpper));
+}
+__device__ __forceinline__ void fp8x16_to_bf16(u32x4_t x, u32x4_t& lo, u32x4_t& hi) {
+  lo = u32x4_t{fp8x2_to_bf16x2<false>(x[0]), fp8x2_to_bf16x2<true>(x[0]),
+               fp8x2_to_bf16x2<false>(x[1]), fp8x2_to_bf16x2<true>(x[1])};
+  hi = u32x4_t{fp8x2_to_bf16x2<false>(x[2]), fp8x2_to_bf16x2<true>(x[2]),
+               fp8x2_to_bf16x2<false>(x[3]), fp8x2_to_bf16x2<true>(x[3])};
+}
+// Four fp32 values -> four E4M3 codes (byte i = value i): magnitudes above
+// 448, the largest finite E4M3 value, are clamped first (the conversion
+// itself would give NaN there), then v_cvt_pk_fp8_f32 rounds to nearest
+// even.  NaN stays NaN.
+__device__ __forceinline__ float fp8_clamp(float x) {
+  return fabsf(x) > 448.0f ? copysignf(448.0f, x) : x;
+}
+__device__ __forceinline__ uint32_t f32x4_to_fp8(float a, float b, float c, float d) {
+  const uint32_t lo = __builtin_amdgcn_cvt_pk_fp8_f32(fp8_clamp(a), fp8_clamp(b), 0, false);
+  return __builtin_amdgcn_cvt_pk_fp8_f32(fp8_clamp(c), fp8_clamp(d), lo, true);
+}
+
 // Calls f(std::integral_constant<int, I>) for I = 0..N-1, so that the index
 // can be a template argument (an immediate offset) in the body.
 template <typename F, int... I>

@@ -33,8 +33,11 @@ import numpy as np
 
 BF16 = "bf16"
 F32 = "f32"
+FP8 = "fp8_e4m3"   # an FP8 cache: q, new k/v and out stay bf16
 
 NAN_BF16 = np.uint16(0x7FC0)
+NAN_FP8 = np.uint8(0x7F)      # E4M3 NaN
+FP8_MAX_CODE = 0x50           # codes 0x00..0x50: magnitudes 0 .. 8 (exponent field <= 10)
 
 
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
@@ -75,14 +78,23 @@ def _normal(rng: np.random.Generator, shape, dtype: str) -> np.ndarray:
 
 
 def _nan(dtype: str):
+    if dtype == FP8:
+        return NAN_FP8
     return NAN_BF16 if dtype == BF16 else np.float32(np.nan)
+
+
+def _fp8_codes(rng, n):
+    """Uniformly drawn finite E4M3 codes of magnitude at most 8, either sign."""
+    u = rng.integers(0, 2 * (FP8_MAX_CODE + 1), size=n, dtype=np.int32)
+    mag = u % (FP8_MAX_CODE + 1)
+    return (mag | ((u > FP8_MAX_CODE).astype(np.int32) << 7)).astype(np.uint8)
 
 
 def _fill_pool(rng, pool_shape, dtype, chunk_blocks=512):
     """Pool of N(0,1) values, filled block-chunk by block-chunk so that a
     2 GiB pool never needs a multi-GiB temporary."""
     nb = pool_shape[0]
-    store = np.uint16 if dtype == BF16 else np.float32
+    store = {BF16: np.uint16, F32: np.float32, FP8: np.uint8}[dtype]
     pool = np.empty(pool_shape, dtype=store)
     per_block = int(np.prod(pool_shape[1:]))
     flat = pool.reshape(nb, per_block)
@@ -92,6 +104,8 @@ def _fill_pool(rng, pool_shape, dtype, chunk_blocks=512):
         if dtype == BF16:
             u = rng.integers(0, 65536, size=(b1 - b0) * per_block, dtype=np.uint16)
             flat[b0:b1] = table[u].reshape(b1 - b0, per_block)
+        elif dtype == FP8:
+            flat[b0:b1] = _fp8_codes(rng, (b1 - b0) * per_block).reshape(b1 - b0, per_block)
         else:
             flat[b0:b1] = rng.standard_normal(size=(b1 - b0, per_block), dtype=np.float32)
     return pool
@@ -140,7 +154,13 @@ class GqaBatch:
     @property
     def max_query_len(self): return int(self.q_lens.max()) if len(self.seq_lens) else 0
     @property
-    def elem_bytes(self): return 2 if self.dtype == BF16 else 4
+    def elem_bytes(self): return 4 if self.dtype == F32 else 2      # q / out / new rows
+    @property
+    def cache_elem_bytes(self): return {BF16: 2, F32: 4, FP8: 1}[self.dtype]
+    @property
+    def k_scale(self): return self.meta.get("k_scale", 1.0)
+    @property
+    def v_scale(self): return self.meta.get("v_scale", 1.0)
 
 
 @dataclass
@@ -213,10 +233,14 @@ def _allocate_tables(rng, seq_lens, block_size, num_blocks=None, sample_distinct
 def make_gqa(seed: int, q_lens, seq_lens, num_q_heads: int, num_kv_heads: int,
              head_dim: int = 128, block_size: int = 16, dtype: str = BF16,
              scale: float | None = None, num_blocks: int | None = None,
-             sample_distinct: bool = False, name: str = "gqa") -> GqaBatch:
+             sample_distinct: bool = False, name: str = "gqa",
+             k_scale: float = 0.25, v_scale: float = 0.5) -> GqaBatch:
     """A paged GQA batch: request r has seq_lens[r] keys, the last q_lens[r] new.
 
-    ``seed`` is an int or an already-advanced numpy Generator."""
+    ``seed`` is an int or an already-advanced numpy Generator.  With dtype
+    FP8 the cache holds E4M3 codes (uniform over the finite codes of
+    magnitude <= 8, NaN 0x7F where nothing is stored) read with k_scale /
+    v_scale; q and the new k / v rows are bf16 N(0,1)."""
     rng = seed if isinstance(seed, np.random.Generator) else np.random.default_rng(seed)
     q_lens = np.asarray(q_lens, dtype=np.int64)
     seq_lens = np.asarray(seq_lens, dtype=np.int64)
@@ -227,9 +251,10 @@ def make_gqa(seed: int, q_lens, seq_lens, num_q_heads: int, num_kv_heads: int,
     T = int(q_lens.sum())
     qsl = np.zeros(len(seq_lens) + 1, dtype=np.int32)
     qsl[1:] = np.cumsum(q_lens)
-    q = _normal(rng, (T, num_q_heads, head_dim), dtype)
-    k_new = _normal(rng, (T, num_kv_heads, head_dim), dtype)
-    v_new = _normal(rng, (T, num_kv_heads, head_dim), dtype)
+    row_dtype = BF16 if dtype == FP8 else dtype
+    q = _normal(rng, (T, num_q_heads, head_dim), row_dtype)
+    k_new = _normal(rng, (T, num_kv_heads, head_dim), row_dtype)
+    v_new = _normal(rng, (T, num_kv_heads, head_dim), row_dtype)
     slots = np.empty(T, dtype=np.int64)
     valid = np.zeros((nb, block_size), dtype=bool)
     for r in range(len(seq_lens)):
@@ -246,11 +271,12 @@ def make_gqa(seed: int, q_lens, seq_lens, num_q_heads: int, num_kv_heads: int,
     cache[:, 1][inval] = _nan(dtype)
     if scale is None:
         scale = 1.0 / math.sqrt(head_dim)
+    meta = {"k_scale": float(k_scale), "v_scale": float(v_scale)} if dtype == FP8 else {}
     return GqaBatch(name=name, dtype=dtype, q=q, k_new=k_new, v_new=v_new,
                     cache=cache, block_table=table, slot_mapping=slots,
                     query_start_loc=qsl, seq_lens=seq_lens.astype(np.int32),
                     scale=float(scale), block_size=block_size,
-                    poison_block=poison)
+                    poison_block=poison, meta=meta)
 
 
 def make_mla(seed: int, seq_lens, num_heads: int = 128, kv_lora_rank: int = 512,
@@ -318,6 +344,19 @@ def llama_decode(seed: int = 1002, batch: int = 64) -> GqaBatch:
     seq = rng.integers(512, 8192, size=batch, endpoint=True)
     return make_gqa(rng, np.ones(batch, dtype=np.int64), seq, 32, 8, 128, 16,
                     BF16, name=WORKLOADS[1])
+
+
+FP8_DECODE = "llama3_8b_gqa_decode_fp8kv"
+
+
+def llama_decode_fp8(seed: int = 1008, batch: int = 64) -> GqaBatch:
+    """The headline decode shape (64 requests, seq_len ~ U{512..8192}, 32 q /
+    8 kv heads, d=128, block 16) over an FP8 (E4M3) cache, k_scale 0.25,
+    v_scale 0.5; q and the new rows bf16."""
+    rng = np.random.default_rng(seed)
+    seq = rng.integers(512, 8192, size=batch, endpoint=True)
+    return make_gqa(rng, np.ones(batch, dtype=np.int64), seq, 32, 8, 128, 16, FP8,
+                    name=FP8_DECODE, k_scale=0.25, v_scale=0.5)
 
 
 def chunked_prefill(seed: int = 1003, batch: int = 16) -> GqaBatch:
@@ -404,12 +443,12 @@ def gqa_bytes(b: GqaBatch, write: bool = True) -> dict:
     Split-KV partials are implementation overhead and not counted.
     """
     e = b.elem_bytes
-    row = b.num_kv_heads * b.head_dim * e
+    row = b.num_kv_heads * b.head_dim * b.cache_elem_bytes
     kv = int(np.sum(b.seq_lens)) * row * 2
     q = b.q.size * e
     out = b.q.size * e
     lse = b.q.shape[0] * b.q.shape[1] * 4
-    wr = (b.k_new.size + b.v_new.size) * e * 2 if write else 0
+    wr = (b.k_new.size + b.v_new.size) * (e + b.cache_elem_bytes) if write else 0
     nblk = int(np.sum((b.seq_lens.astype(np.int64) + b.block_size - 1) // b.block_size))
     meta = nblk * 4 + b.num_seqs * 8 + (b.num_tokens * 8 if write else 0)
     return {"kv": kv, "q": q, "out": out, "lse": lse, "write": wr, "meta": meta,
