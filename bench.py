@@ -6,8 +6,8 @@ cache write, the attention kernel(s) and, for split-KV decode, the LSE merge.
 The headline line measures the Llama-3-8B-shaped GQA decode (64 requests,
 seq_len U[512, 8192], 32 q / 8 kv heads, d=128, bf16, block 16) in HBM GB/s;
 the other workloads (tiny fp32 decode, chunked prefill, long-context decode,
-MLA decode, a mixed prefill + decode batch, a batch sharing a prefix, decode
-over an FP8 cache) are measured the same way and
+MLA decode, a mixed prefill + decode batch, a batch sharing a prefix, GQA and
+MLA decode over FP8 caches) are measured the same way and
 reported under "workloads".  Inputs are generated on the host by ``workloads.py`` (seeded),
 uploaded once, and resident in HBM before any timed region.
 
@@ -336,6 +336,44 @@ def fp8_decode_case(b, name):
                 f"decode_balanced_kernel<{g}, true> + merge", "decode_balanced.hip", info)
 
 
+def mla_fp8_case(b, name):
+    """MLA decode over an FP8 latent cache: write + balanced decode + merge;
+    the timed kernel is the decode call (decode kernel and segment merge),
+    priced against the bf16 MFMA peak (the products run on bf16 MFMAs after
+    the tiles are widened)."""
+    import torch
+    import paged_kv_attention_pa_amd as pa
+    import workloads as W
+    cache = torch.from_numpy(b.cache).cuda()
+    qn, qp = _dev(b.q_nope), _dev(b.q_pe)
+    bt, sl = _dev(b.block_table), _dev(b.seq_lens)
+    kc, kp, sm = _dev(b.kv_c_new), _dev(b.k_pe_new), _dev(b.slot_mapping)
+    nr = pa.device_num_cus()
+    wsb = pa.decode_balanced_workspace_bytes(b.num_seqs, b.num_heads, b.kv_lora_rank, nr)
+    ws = torch.empty(max(1, wsb // 4), dtype=torch.float32, device="cuda")
+    out = torch.empty((b.num_seqs, b.num_heads, b.kv_lora_rank), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((b.num_seqs, b.num_heads), dtype=torch.float32, device="cuda")
+
+    def step():
+        pa.mla_decode_fp8(qn, qp, cache, bt, sl, b.scale, b.kv_scale, kv_c=kc, k_pe=kp,
+                          slot_mapping=sm, num_ranges=nr, workspace=ws, out=out, lse=lse)
+
+    def kernel():
+        pa.mla_decode_fp8(qn, qp, cache, bt, sl, b.scale, b.kv_scale, num_ranges=nr, workspace=ws,
+                          out=out, lse=lse)
+
+    by = W.mla_bytes(b)
+    kb = by["kv"] + by["q"] + by["meta"] - b.num_seqs * 8
+    fl = W.mla_flops(b)
+    info = {"num_seqs": b.num_seqs, "num_heads": b.num_heads, "kv_lora_rank": b.kv_lora_rank,
+            "rope_dim": b.rope_dim, "block_size": b.block_size, "cache_dtype": "fp8_e4m3",
+            "kv_scale": b.kv_scale, "max_seq_len": b.max_seq_len,
+            "total_keys": int(b.seq_lens.sum()), "schedule": "token-balanced ranges",
+            "timed": "decode kernel + segment merge"}
+    return Case(name, step, kernel, by["total"], fl, kb, fl, "mfma",
+                "mla_kernel<true, true> + merge", "mla_decode.hip", info)
+
+
 def build_cases(only):
     import workloads as W
     makers = {
@@ -349,6 +387,7 @@ def build_cases(only):
         W.MIXED: lambda: mixed_case(W.mixed_batch(), W.MIXED),
         W.CASCADE: lambda: cascade_case(W.cascade_batch(), W.CASCADE),
         W.FP8_DECODE: lambda: fp8_decode_case(W.llama_decode_fp8(), W.FP8_DECODE),
+        W.FP8_MLA: lambda: mla_fp8_case(W.mla_decode_fp8_batch(), W.FP8_MLA),
     }
     names = [HEADLINE] + [n for n in makers if n != HEADLINE]
     if only is not None:

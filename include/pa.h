@@ -504,6 +504,27 @@ pa_status_t pa_cache_write_fp8(pa_layout_t layout,
                                const int64_t* slot_mapping, int num_tokens,
                                float k_scale, float v_scale, hipStream_t stream);
 
+/* pa_mla_decode_fp8: MLA decode (as pa_mla_decode) over an FP8 latent cache
+ * [num_blocks, block_size, kv_lora_rank + rope_dim] uint8 with one scale for
+ * the row (kv_scale: keys and values alike), on the token-balanced schedule
+ * (num_ranges = 0: one range per compute unit of the current device),
+ * workspace of pa_decode_balanced_workspace_bytes(num_seqs, num_heads,
+ * kv_lora_rank, num_ranges) bytes.  Enqueues the write of kv_c / k_pe (if
+ * given, quantised with kv_scale), the decode kernel and the segment merge.
+ * q_nope / q_pe bf16 with the strides of pa_mla_decode; out [num_seqs,
+ * num_heads, kv_lora_rank] bf16; lse fp32 or NULL.  Supported: kv_lora_rank
+ * 512, rope_dim 64, num_heads a multiple of 16 up to 128. */
+pa_status_t pa_mla_decode_fp8(const void* q_nope, int64_t qn_stride_b, int64_t qn_stride_h,
+                              const void* q_pe, int64_t qp_stride_b, int64_t qp_stride_h,
+                              const void* kv_c, const void* k_pe,
+                              void* kv_cache, int64_t num_blocks, int block_size,
+                              const int32_t* block_table, int max_blocks_per_seq,
+                              const int64_t* slot_mapping, const int32_t* seq_lens, int num_seqs,
+                              int num_heads, int kv_lora_rank, int rope_dim,
+                              float scale, float kv_scale, int num_ranges,
+                              void* workspace, size_t workspace_bytes,
+                              void* out, float* lse, hipStream_t stream);
+
 pa_status_t pa_decode_fp8(const void* q, const void* k, const void* v,
                           void* kv_cache, int64_t num_blocks, int block_size,
                           const int32_t* block_table, int max_blocks_per_seq,

@@ -52,6 +52,9 @@ _SIGNATURES = {
     "pa_plan_cascade": (_i32, [_vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp]),
     "pa_cache_write_fp8": (_i32, [_i32, _vp, _i64, _vp, _i64, _vp, _i64, _i32, _i32, _i32, _vp,
                                   _i32, _f32, _f32, _vp]),
+    "pa_mla_decode_fp8": (_i32, [_vp, _i64, _i64, _vp, _i64, _i64, _vp, _vp, _vp, _i64, _i32, _vp,
+                                 _i32, _vp, _vp, _i32, _i32, _i32, _i32, _f32, _f32, _i32, _vp,
+                                 _sz, _vp, _vp, _vp]),
     "pa_decode_fp8": (_i32, [_vp, _vp, _vp, _vp, _i64, _i32, _vp, _i32, _vp, _vp, _i32, _i32,
                              _i32, _i32, _f32, _f32, _f32, _i32, _vp, _sz, _vp, _vp, _vp]),
     "pa_cascade_attention": (_i32, [_vp, _i32, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _vp, _vp,
@@ -576,6 +579,40 @@ def mla_decode_balanced(q_nope, q_pe, kv_cache, block_table, seq_lens, scale: fl
     if merge:
         decode_balanced_merge(workspace, B, H, R, nr, out, lse, stream=stream)
     return out, lse, workspace, nr
+
+
+def mla_decode_fp8(q_nope, q_pe, kv_cache, block_table, seq_lens, scale: float,
+                   kv_scale: float, kv_c=None, k_pe=None, slot_mapping=None, num_ranges: int = 0,
+                   workspace=None, out=None, lse=None, return_lse: bool = True, stream=None):
+    """MLA decode over an FP8 latent cache [nb, bs, R + 64] uint8 (one scale
+    for the row), token-balanced schedule + merge; q_nope [B, H, R], q_pe
+    [B, H, 64] bf16.  Returns (out [B, H, R], lse [B, H])."""
+    torch = _torch()
+    _dev(kv_cache, block_table, seq_lens, kv_c, k_pe, slot_mapping, workspace, out, lse)
+    _fp8_cache(kv_cache)
+    for t in (q_nope, q_pe):
+        _need(t.is_cuda and t.stride(-1) == 1, "q_nope/q_pe must be GPU tensors with a contiguous last dim")
+        _need(t.dtype == torch.bfloat16, "q must be bf16")
+    B, H, R = q_nope.shape
+    P = q_pe.shape[2]
+    nb, bs, row = kv_cache.shape
+    _need(row == R + P, "cache row must be kv_lora_rank + rope_dim")
+    nr = int(num_ranges) or device_num_cus()
+    if out is None:
+        out = torch.empty((B, H, R), dtype=q_nope.dtype, device=q_nope.device)
+    if lse is None and return_lse:
+        lse = torch.empty((B, H), dtype=torch.float32, device=q_nope.device)
+    if workspace is None:
+        need = decode_balanced_workspace_bytes(B, H, R, nr)
+        workspace = torch.empty(max(1, need // 4), dtype=torch.float32, device=q_nope.device)
+    wbytes = workspace.numel() * workspace.element_size()
+    _check(library().pa_mla_decode_fp8(_ptr(q_nope), q_nope.stride(0), q_nope.stride(1),
+                                       _ptr(q_pe), q_pe.stride(0), q_pe.stride(1), _ptr(kv_c),
+                                       _ptr(k_pe), _ptr(kv_cache), nb, bs, _ptr(block_table),
+                                       block_table.shape[1], _ptr(slot_mapping), _ptr(seq_lens), B,
+                                       H, R, P, float(scale), float(kv_scale), nr, _ptr(workspace),
+                                       wbytes, _ptr(out), _ptr(lse), _stream(stream)))
+    return out, lse
 
 
 def lse_merge(part, out_dtype=None, out=None, lse=None, return_lse: bool = True, stream=None):

@@ -1055,4 +1055,60 @@ pa_status_t pa_decode_fp8(const void* q, const void* k, const void* v, void* kv_
                                   out, lse, stream);
 }
 
+pa_status_t pa_mla_decode_fp8(const void* q_nope, int64_t qn_stride_b, int64_t qn_stride_h,
+                              const void* q_pe, int64_t qp_stride_b, int64_t qp_stride_h,
+                              const void* kv_c, const void* k_pe, void* kv_cache,
+                              int64_t num_blocks, int block_size, const int32_t* block_table,
+                              int max_blocks_per_seq, const int64_t* slot_mapping,
+                              const int32_t* seq_lens, int num_seqs, int num_heads,
+                              int kv_lora_rank, int rope_dim, float scale, float kv_scale,
+                              int num_ranges, void* workspace, size_t workspace_bytes, void* out,
+                              float* lse, hipStream_t stream) {
+  pa_status_t st = check_common_cache(num_blocks, block_size, block_table, max_blocks_per_seq,
+                                      seq_lens, num_seqs, 0);
+  if (st != PA_OK) return st;
+  st = check_mla_q(qn_stride_b, qn_stride_h, qp_stride_b, qp_stride_h, num_heads, kv_lora_rank,
+                   rope_dim, scale);
+  if (st != PA_OK) return st;
+  PA_REQUIRE(fp8_scale_ok(kv_scale), PA_ERR_INVALID, "the FP8 scale must be finite and > 0");
+  PA_REQUIRE(num_ranges >= 0, PA_ERR_INVALID, "num_ranges must be >= 0");
+  PA_REQUIRE((kv_c == nullptr) == (k_pe == nullptr), PA_ERR_INVALID,
+             "kv_c and k_pe must both be given or both NULL");
+  PA_REQUIRE(kv_c == nullptr || slot_mapping != nullptr, PA_ERR_INVALID,
+             "kv_c/k_pe given without slot_mapping");
+  PA_REQUIRE(slot_mapping == nullptr || kv_c != nullptr, PA_ERR_INVALID,
+             "slot_mapping given without kv_c/k_pe");
+  int nr = num_ranges;
+  if (nr == 0) {
+    nr = pa_device_num_cus();
+    if (nr <= 0) return fail(PA_ERR_HIP, "cannot query the device's compute units");
+  }
+  st = check_balanced(num_seqs, num_heads, kv_lora_rank, max_blocks_per_seq, block_size, nr,
+                      workspace, workspace_bytes);
+  if (st != PA_OK) return st;
+  if (num_seqs == 0) return ok();
+  PA_REQUIRE(q_nope && q_pe && kv_cache && out, PA_ERR_INVALID,
+             "q_nope, q_pe, kv_cache and out must be non-null");
+  const int row = kv_lora_rank + rope_dim;
+  if (kv_c) {
+    st = check_write_fp8(PA_LAYOUT_MLA, kv_c, kv_lora_rank, k_pe, rope_dim, kv_cache, num_blocks,
+                         block_size, 1, row, slot_mapping, num_seqs, kv_scale, kv_scale);
+    if (st != PA_OK) return st;
+    st = enqueue_write_fp8(PA_LAYOUT_MLA, kv_c, kv_lora_rank, k_pe, rope_dim, kv_cache,
+                           num_blocks, block_size, 1, row, slot_mapping, num_seqs, kv_scale,
+                           kv_scale, stream);
+    if (st != PA_OK) return st;
+  }
+  pa::MlaDecode d{q_nope, qn_stride_b, qn_stride_h, q_pe, qp_stride_b, qp_stride_h,
+                  kv_cache, num_blocks, block_size, block_table, max_blocks_per_seq,
+                  seq_lens, num_seqs, num_heads, kv_lora_rank, rope_dim, scale,
+                  1, 0, 0, balanced_part(workspace, num_seqs), out, lse,
+                  nr, balanced_cu(workspace), 1, kv_scale};
+  hipError_t e = pa::launch_mla_decode(d, stream);
+  if (e == hipErrorNotSupported) return fail(PA_ERR_UNSUPPORTED, "MLA kernel not built");
+  if (e != hipSuccess) return hip_fail(e, "FP8 MLA decode launch");
+  return pa_decode_balanced_merge(workspace, workspace_bytes, num_seqs, num_heads, kv_lora_rank,
+                                  nr, out, lse, stream);
+}
+
 }  // extern "C"

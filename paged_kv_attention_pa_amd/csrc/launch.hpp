@@ -112,6 +112,7 @@ struct MlaDecode {
   int num_splits; int split_tokens; int direct;
   float* part; void* out; float* lse;
   int num_ranges; int32_t* cu;
+  int fp8; float kv_scale;   // E4M3 cache, one scale for the row (balanced schedule)
 };
 hipError_t launch_mla_decode(const MlaDecode& a, hipStream_t s);
 

@@ -99,8 +99,23 @@ __device__ __forceinline__ void acc_fence(f32x16_t (&acc)[16]) {
 //   partials [(nr + B) H, 516] for the others.
 // A "tile" is 32 keys [kb + 32 lc, kb + 32 lc + 32) of request r, keys at or
 // past kend masked (split: kb = t0, kend = t1; balanced: kb = 0, kend = len).
-template <bool kBalanced>
+// kFp8 (balanced schedule only): the cache holds E4M3 codes, one scale for
+// the whole row.  A tile's 18 KiB of codes is gathered into an LDS staging
+// ring (four stages, 16-byte DMA pieces: waves 0 and 1 issue five, waves 2
+// and 3 four), then widened once per work-group to the bf16 tile layout
+// above (v_cvt_scalef32_pk_bf16_fp8, exact) in one of two bf16 buffers, so
+// both products run unchanged; the scale multiplies the score scale and the
+// final normalisation.
+constexpr int kF8TileBytes = kBN * kRow;                 // 18432 B of codes
+constexpr int kF8Pieces = kF8TileBytes / 1024;           // 18 wave-wide 16-byte loads
+constexpr int kF8Stages = 4;
+constexpr int kF8Chunks = kF8TileBytes / 8 / (64 * kWaves);   // 9 eight-code chunks per thread
+static_assert(2 * kTileBytes + kF8Stages * kF8TileBytes <= kStages * kTileBytes, "fp8 LDS budget");
+static_assert(kF8Pieces == 18 && kF8Chunks == 9, "fp8 piece counts");
+
+template <bool kBalanced, bool kFp8>
 __global__ __launch_bounds__(64 * kWaves, 1) void mla_kernel(MlaDecode a) {
+  static_assert(kBalanced || !kFp8, "the FP8 cache runs on the balanced schedule");
   __shared__ __align__(1024) char smem[kStages * kTileBytes];
   __shared__ int s_wave_sum[kWaves];
   __shared__ int s_start[2];
@@ -238,6 +253,80 @@ __global__ __launch_bounds__(64 * kWaves, 1) void mla_kernel(MlaDecode a) {
   };
   auto gwait = [&]() { __builtin_amdgcn_s_waitcnt(0x0F70); };   // vmcnt(0)
 
+  // ---- FP8: gather of a tile's codes into staging stage `stage` (the tile's
+  // rows contiguous, 576 B each), pieces I = wave + 4 jj < 18, lane l at
+  // byte 1024 I + 16 l; the same page / kend correction as the bf16 gather.
+  constexpr int kF8Row = kRow;   // bytes of codes per row
+  const int f8_n = wave < 2 ? 5 : 4;   // pieces this wave issues per tile
+  auto gload8 = [&](const ChunkPos& p, int stage, const Pages& pg) {
+    const int key0 = kb + p.lc * kBN;
+    const int kend = p.len;
+    int64_t b0 = pg.b0, b1 = pg.b1;
+    b0 = (b0 < 0 || b0 >= a.num_blocks) ? 0 : b0;
+    b1 = (b1 < 0 || b1 >= a.num_blocks) ? 0 : b1;
+    const int in0 = key0 - (key0 / bs) * bs;
+    const char* c8 = static_cast<const char*>(a.cache);
+    const char* base0 = c8 + (b0 * bs + in0) * int64_t(kF8Row);
+    const char* base1 = c8 + (b1 * bs - (bs - in0)) * int64_t(kF8Row);
+    const bool simple = in0 + kBN <= bs && key0 + kBN <= kend;   // wave-uniform
+    const int last = kend - 1 - key0;
+    typedef __attribute__((address_space(3))) void* lds_ptr;
+    char* dst = smem + 2 * kTileBytes + stage * kF8TileBytes;
+#pragma unroll
+    for (int jj = 0; jj < 5; ++jj) {
+      if (jj == 4 && wave >= 2) break;
+      const uint32_t off = uint32_t(1024 * (wave + kWaves * jj) + 16 * lane);
+      const char* src = base0 + off;
+      if (!simple) {
+        const int row = int(off / uint32_t(kF8Row));
+        const int rr = min(row, last);
+        src = (in0 + rr < bs ? base0 : base1) + int64_t(off) + int64_t(rr - row) * kF8Row;
+      }
+      __builtin_amdgcn_global_load_lds(src, (lds_ptr)(dst + 1024 * (wave + kWaves * jj)), 16, 0, 0);
+    }
+  };
+  // tile t's codes have landed for this wave when at most f8_n x (tiles
+  // issued after t) of its loads are outstanding
+  auto wait_tiles8 = [&](int k) {
+    if (k <= 0) __builtin_amdgcn_s_waitcnt(0x0F70);                  // vmcnt(0)
+    else if (k == 1) {
+      if (f8_n == 5) __builtin_amdgcn_s_waitcnt(0x0F75);             // vmcnt(5)
+      else __builtin_amdgcn_s_waitcnt(0x0F74);                       // vmcnt(4)
+    } else if (k == 2) {
+      if (f8_n == 5) __builtin_amdgcn_s_waitcnt(0x0F7A);             // vmcnt(10)
+      else __builtin_amdgcn_s_waitcnt(0x0F78);                       // vmcnt(8)
+    } else {
+      if (f8_n == 5) __builtin_amdgcn_s_waitcnt(0x0F7F);             // vmcnt(15)
+      else __builtin_amdgcn_s_waitcnt(0x4F70);                       // vmcnt(16)
+    }
+  };
+  // staging `stage` -> bf16 buffer `buf`: thread chunk pos = tid + 256 i is
+  // row pos / 72, chunk pos % 72 (codes 8 c .. 8 c + 7), written to its
+  // swizzled slot.  The LDS accesses are inline assembly so that they stay
+  // ordered against the bare barriers around them.
+  auto convert8 = [&](int stage, int buf) {
+    const uint32_t src = lds_addr(smem) + uint32_t(2 * kTileBytes + stage * kF8TileBytes + 8 * tid);
+    const uint32_t dst = lds_addr(smem) + uint32_t(buf * kTileBytes);
+    u32x2_t c[kF8Chunks];
+    static_for<kF8Chunks>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      c[i] = lds_read8_at<2048 * i>(src);
+    });
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(c[0]), "+v"(c[1]), "+v"(c[2]), "+v"(c[3]),
+                 "+v"(c[4]), "+v"(c[5]), "+v"(c[6]), "+v"(c[7]), "+v"(c[8]));
+#pragma unroll
+    for (int i = 0; i < kF8Chunks; ++i) {
+      const int pos = tid + 256 * i;
+      const int row = pos / kChunks;
+      const int ch = pos - row * kChunks;
+      const u32x4_t w = u32x4_t{fp8x2_to_bf16x2<false>(c[i].x), fp8x2_to_bf16x2<true>(c[i].x),
+                                fp8x2_to_bf16x2<false>(c[i].y), fp8x2_to_bf16x2<true>(c[i].y)};
+      const uint32_t addr = dst + uint32_t(row * kRowBytes + 16 * slot_of(row, ch));
+      lds_write16_at(addr, w);
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  };
+
   // ---- LDS operand addresses (per lane; the stage and the k-step / d-tile
   // group are added as offsets)
   // K fragment of k-step kk = 4 q + kq: key row c32, chunk 8 q + 2 kq + g.
@@ -269,7 +358,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void mla_kernel(MlaDecode a) {
   // Masked scores are -inf and meet the scale inside the exponent; a zero
   // scale is raised to the smallest normal float so that -inf * scale stays
   // -inf (weight 0) while every visible score still maps to exp2(0) = 1.
-  const float scale2 = fmaxf(a.scale * kLog2e, 0x1p-126f);
+  const float scale2 = fmaxf((kFp8 ? a.scale * a.kv_scale : a.scale) * kLog2e, 0x1p-126f);
   float m_run = kNoMax;
   float l_run = 0.0f;          // this lane's share of head `head`'s sum
   bool fresh = true;           // acc holds nothing yet (no rescale needed)
@@ -284,7 +373,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void mla_kernel(MlaDecode a) {
     acc_fence<15>(acc);   // the VALU reads the accumulator
     const float l_tot = xor32_sum(l_run);
     if (!active || !head_ok) return;
-    const float inv = 1.0f / l_tot;
+    const float inv = (kFp8 ? a.kv_scale : 1.0f) / l_tot;
     const float lse_nat = (m_run + fast_log2(l_tot)) * kLn2;
     const int64_t row = int64_t(p.r) * H + head;
     bool direct;
@@ -359,8 +448,10 @@ __global__ __launch_bounds__(64 * kWaves, 1) void mla_kernel(MlaDecode a) {
   zero_pad_q();
   ChunkPos ld = cur;   // next tile to load
   int n_loaded = 0;
-  for (; n_loaded < kStages - 1 && n_loaded < n_tiles; ++n_loaded) {
-    gload(ld, n_loaded, pages(ld));
+  constexpr int kDepth = kFp8 ? kF8Stages : kStages;   // staging buffers
+  for (; n_loaded < kDepth - 1 && n_loaded < n_tiles; ++n_loaded) {
+    if constexpr (kFp8) gload8(ld, n_loaded, pages(ld));
+    else gload(ld, n_loaded, pages(ld));
     if (n_loaded + 1 < n_tiles) ld = advance(ld);
   }
   Pages pg_next = pages(ld);   // ld stays inside the run, so this read is in bounds
@@ -372,16 +463,25 @@ __global__ __launch_bounds__(64 * kWaves, 1) void mla_kernel(MlaDecode a) {
   for (;;) {
   const int seg_end = min(n_tiles, t + chunks_of(cur.len) - cur.lc);
   for (; t < seg_end; ++t) {
-    wait_tiles(n_loaded - 1 - t);   // this wave's loads of tile t have landed
+    if constexpr (kFp8) wait_tiles8(n_loaded - 1 - t);
+    else wait_tiles(n_loaded - 1 - t);   // this wave's loads of tile t have landed
     // Everyone's have, and everyone is done with tile t - 1 (its LDS reads were
     // waited for).  A bare barrier: __syncthreads() would also wait for the
     // loads of the tiles still in flight.
     __builtin_amdgcn_s_barrier();
     if (n_loaded < n_tiles) {       // refill the buffer of tile t - 1
-      gload(ld, n_loaded % kStages, pg_next);
+      if constexpr (kFp8) gload8(ld, n_loaded % kF8Stages, pg_next);
+      else gload(ld, n_loaded % kStages, pg_next);
       if (++n_loaded < n_tiles) ld = advance(ld);
     }
-    const uint32_t st_off = uint32_t((t % kStages) * kTileBytes);
+    if constexpr (kFp8) {
+      // widen tile t into bf16 buffer t % 2 (last read by tile t - 2, which
+      // every wave finished before the previous barrier); then everyone's
+      // part is in place
+      convert8(t % kF8Stages, t & 1);
+      __builtin_amdgcn_s_barrier();
+    }
+    const uint32_t st_off = uint32_t((kFp8 ? (t & 1) : (t % kStages)) * kTileBytes);
     const int key0 = kb + cur.lc * kBN;
     const int kend = cur.len;
     if (active) {
@@ -515,13 +615,20 @@ hipError_t launch_mla_decode(const MlaDecode& a, hipStream_t s) {
   if (a.rank != kRank || a.rope != kRope || a.num_heads % 16 ||
       a.num_heads > kHeadsPerWave * kWaves)
     return hipErrorNotSupported;
+  if (a.fp8) {
+    if (a.num_ranges <= 0) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((mla_kernel<true, true>), dim3(unsigned(a.num_ranges)), dim3(64 * kWaves), 0,
+                       s, a);
+    return hipGetLastError();
+  }
   if (a.num_ranges > 0) {
-    hipLaunchKernelGGL(mla_kernel<true>, dim3(unsigned(a.num_ranges)), dim3(64 * kWaves), 0, s, a);
+    hipLaunchKernelGGL((mla_kernel<true, false>), dim3(unsigned(a.num_ranges)), dim3(64 * kWaves),
+                       0, s, a);
     return hipGetLastError();
   }
   const int64_t wgs = int64_t(a.num_seqs) * a.num_splits;
   if (wgs > INT32_MAX) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(mla_kernel<false>, dim3(unsigned(wgs)), dim3(64 * kWaves), 0, s, a);
+  hipLaunchKernelGGL((mla_kernel<false, false>), dim3(unsigned(wgs)), dim3(64 * kWaves), 0, s, a);
   return hipGetLastError();
 }
 

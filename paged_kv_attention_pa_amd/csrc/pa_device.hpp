@@ -148,6 +148,16 @@ __device__ __forceinline__ u32x4_t lds_read16_at(uint32_t addr) {
   return v;
 }
 
+template <int kOffset>
+__device__ __forceinline__ u32x2_t lds_read8_at(uint32_t addr) {
+  u32x2_t v;
+  asm volatile("ds_read_b64 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "n"(kOffset));
+  return v;
+}
+__device__ __forceinline__ void lds_write16_at(uint32_t addr, u32x4_t v) {
+  asm volatile("ds_write_b128 %0, %1" : : "v"(addr), "v"(v) : "memory");
+}
+
 // 16-byte LDS read issued as inline assembly (same contract as
 // lds_read_tr_issue: pass the result through lds_wait() before use).
 template <int kOffset>

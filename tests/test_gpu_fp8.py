@@ -3,9 +3,9 @@ bit-exact against the oracle's (GQA and MLA layouts, saturation, the
 unaligned path), and decode over an FP8 cache matches the oracle's attention
 over the dequantised cache for every supported GQA group and head count,
 ragged lengths, block sizes 16 and 32, and sampled requests of the full
-FP8 decode workload.  With power-of-two scales the dequantised values are
-bf16 values, and the FP8 decode equals the bf16 decode over them bit for
-bit."""
+FP8 decode workload; MLA decode over an FP8 latent cache likewise.  With
+power-of-two scales the dequantised values are bf16 values, and the FP8
+kernels equal the bf16 kernels over them bit for bit."""
 import math
 
 import numpy as np
@@ -170,6 +170,98 @@ def test_fp8_decode_workload_full_size(fp8_batch):
     reqs = sorted(set([int(x) for x in np.random.default_rng(9).choice(64, 14, replace=False)] +
                       [int(np.argmax(b.seq_lens)), int(np.argmin(b.seq_lens))]))
     cache_ref, oref, lref = _oracle(b, requests=reqs)
+    for r in reqs:
+        check_close(out[r], oref[r], f"request {r} out")
+        check_lse(lse[r], lref[r], f"request {r} lse")
+    assert np.array_equal(_host(cache_t), cache_ref)
+
+
+# ------------------------------------------------------------------ MLA
+def _run_mla(b, write=True, num_ranges=0):
+    cache_t = _u8(b.cache)
+    out, lse = pa.mla_decode_fp8(to_dev(b.q_nope), to_dev(b.q_pe), cache_t, to_dev(b.block_table),
+                                 to_dev(b.seq_lens), b.scale, b.kv_scale,
+                                 kv_c=to_dev(b.kv_c_new) if write else None,
+                                 k_pe=to_dev(b.k_pe_new) if write else None,
+                                 slot_mapping=to_dev(b.slot_mapping) if write else None,
+                                 num_ranges=num_ranges)
+    torch.cuda.synchronize()
+    return cache_t, to_f64(out), lse.cpu().numpy().astype(np.float64)
+
+
+def _oracle_mla(b, requests=None):
+    cache = O.cache_write_mla_fp8(b.cache, b.kv_c_new, b.k_pe_new, b.slot_mapping, b.kv_scale)
+    deq = O.dequant_mla_cache(cache, b.kv_scale)
+    out, lse = O.mla_decode(b.q_nope, b.q_pe, deq, b.block_table, b.seq_lens, b.scale,
+                            requests=requests)
+    return cache, out, lse
+
+
+MLA_CASES = [
+    # name, seq_lens, heads, block size, kv_scale
+    ("h128_bs64", [1, 31, 32, 33, 700, 2049, 64], 128, 64, 0.3),
+    ("h16_bs16", [5, 1, 129, 1000], 16, 16, 0.07),
+    ("h64_bs32_long", [3000, 2, 95], 64, 32, 1.5),
+    ("h112_bs64", [40, 513], 112, 64, 0.25),
+]
+
+
+@pytest.mark.parametrize("ci", range(len(MLA_CASES)), ids=[c[0] for c in MLA_CASES])
+def test_fp8_mla_small(ci):
+    name, sl, H, bs, sc = MLA_CASES[ci]
+    say(f"fp8 mla {name}")
+    b = W.make_mla(740 + ci, sl, H, 512, 64, bs, cache_dtype=W.FP8, kv_scale=sc)
+    cache_t, out, lse = _run_mla(b)
+    cache_ref, oref, lref = _oracle_mla(b)
+    assert np.array_equal(_host(cache_t), cache_ref)
+    check_close(out, oref, f"{name} out")
+    check_lse(lse, lref, f"{name} lse")
+
+
+def test_fp8_mla_range_counts():
+    say("fp8 mla range counts")
+    b = W.make_mla(750, [1, 900, 64, 3000, 33], 32, 512, 64, 64, cache_dtype=W.FP8, kv_scale=0.2)
+    _, oref, lref = _oracle_mla(b)
+    for nr in (1, 5, 77, 700):
+        _, out, lse = _run_mla(b, num_ranges=nr)
+        check_close(out, oref, f"{nr} ranges out")
+        check_lse(lse, lref, f"{nr} ranges lse")
+
+
+def test_fp8_mla_equals_bf16_mla_on_dequantised_cache():
+    """Power-of-two scale: the FP8 MLA kernel (tiles widened in LDS, the scale
+    folded into the softmax and the output) gives the bf16 MLA kernel's
+    result over the dequantised cache bit for bit."""
+    say("fp8 mla vs bf16 mla")
+    b = W.make_mla(760, [3, 1000, 77, 4000, 600, 64], 128, 512, 64, 64, cache_dtype=W.FP8,
+                   kv_scale=0.5)
+    cache_t, out8, lse8 = _run_mla(b)
+    deq = O.fp8_e4m3_to_f64(_host(cache_t)) * b.kv_scale
+    deq = np.where(np.isnan(deq), 0.0, deq)
+    bf = W.f32_to_bf16_bits(deq.astype(np.float32))
+    assert np.array_equal(W.bf16_bits_to_f32(bf), deq.astype(np.float32))
+    out16, lse16, _, _ = pa.mla_decode_balanced(to_dev(b.q_nope), to_dev(b.q_pe), to_dev(bf),
+                                                to_dev(b.block_table), to_dev(b.seq_lens), b.scale)
+    torch.cuda.synchronize()
+    assert np.array_equal(out8, to_f64(out16))
+    assert np.array_equal(lse8, lse16.cpu().numpy().astype(np.float64))
+
+
+@pytest.fixture(scope="module")
+def fp8_mla_batch():
+    return W.mla_decode_fp8_batch()
+
+
+def test_fp8_mla_workload_full_size(fp8_mla_batch):
+    """128 requests U{1024..8192}, 128 heads, FP8 latent cache: 12 sampled
+    requests against the oracle, the written cache bit-exact."""
+    b = fp8_mla_batch
+    say(f"fp8 mla full size, {int(b.seq_lens.sum())} keys")
+    cache_t, out, lse = _run_mla(b)
+    assert np.all(np.isfinite(out))
+    reqs = sorted(set([int(x) for x in np.random.default_rng(10).choice(128, 10, replace=False)] +
+                      [int(np.argmax(b.seq_lens)), int(np.argmin(b.seq_lens))]))
+    cache_ref, oref, lref = _oracle_mla(b, requests=reqs)
     for r in reqs:
         check_close(out[r], oref[r], f"request {r} out")
         check_lse(lse[r], lref[r], f"request {r} lse")

@@ -197,6 +197,12 @@ class MlaBatch:
     def num_blocks(self): return self.cache.shape[0]
     @property
     def max_seq_len(self): return int(self.seq_lens.max()) if len(self.seq_lens) else 0
+    @property
+    def fp8(self): return self.meta.get("cache_dtype") == FP8
+    @property
+    def cache_elem_bytes(self): return 1 if self.fp8 else 2
+    @property
+    def kv_scale(self): return self.meta.get("kv_scale", 1.0)
 
 
 def _allocate_tables(rng, seq_lens, block_size, num_blocks=None, sample_distinct=False):
@@ -281,10 +287,12 @@ def make_gqa(seed: int, q_lens, seq_lens, num_q_heads: int, num_kv_heads: int,
 
 def make_mla(seed: int, seq_lens, num_heads: int = 128, kv_lora_rank: int = 512,
              rope_dim: int = 64, block_size: int = 64, scale: float | None = None,
-             name: str = "mla") -> MlaBatch:
+             name: str = "mla", cache_dtype: str = BF16, kv_scale: float = 0.25) -> MlaBatch:
     """An MLA decode batch: one new latent row per request at its last position.
 
-    The default scale 1/sqrt(192) is that of a 128 + 64 query/key head."""
+    The default scale 1/sqrt(192) is that of a 128 + 64 query/key head.  With
+    cache_dtype FP8 the cache holds E4M3 codes (as ``make_gqa``'s FP8 pool)
+    read with one scale, kv_scale; the queries and new rows stay bf16."""
     rng = seed if isinstance(seed, np.random.Generator) else np.random.default_rng(seed)
     seq_lens = np.asarray(seq_lens, dtype=np.int64)
     if np.any(seq_lens < 1):
@@ -304,15 +312,16 @@ def make_mla(seed: int, seq_lens, num_heads: int = 128, kv_lora_rank: int = 512,
         off = pos % block_size
         valid[blk[:S - 1], off[:S - 1]] = True
         slots[r] = blk[S - 1] * block_size + off[S - 1]
-    cache = _fill_pool(rng, (nb, block_size, kv_lora_rank + rope_dim), BF16)
-    cache[~valid] = NAN_BF16
+    cache = _fill_pool(rng, (nb, block_size, kv_lora_rank + rope_dim), cache_dtype)
+    cache[~valid] = _nan(cache_dtype)
     if scale is None:
         scale = 1.0 / math.sqrt(192.0)
+    meta = {"cache_dtype": FP8, "kv_scale": float(kv_scale)} if cache_dtype == FP8 else {}
     return MlaBatch(name=name, q_nope=q_nope, q_pe=q_pe, kv_c_new=kv_c,
                     k_pe_new=k_pe, cache=cache, block_table=table,
                     slot_mapping=slots, seq_lens=seq_lens.astype(np.int32),
                     scale=float(scale), block_size=block_size,
-                    poison_block=poison)
+                    poison_block=poison, meta=meta)
 
 
 # --------------------------------------------------------------------------
@@ -347,6 +356,17 @@ def llama_decode(seed: int = 1002, batch: int = 64) -> GqaBatch:
 
 
 FP8_DECODE = "llama3_8b_gqa_decode_fp8kv"
+FP8_MLA = "mla_latent_decode_fp8kv"
+
+
+def mla_decode_fp8_batch(seed: int = 1009, batch: int = 128) -> MlaBatch:
+    """The MLA decode shape (128 requests, seq_len ~ U{1024..8192}, 128 heads,
+    512 + 64 latent row, block 64, scale 1/sqrt(192)) over an FP8 latent cache
+    with kv_scale 0.25."""
+    rng = np.random.default_rng(seed)
+    seq = rng.integers(1024, 8192, size=batch, endpoint=True)
+    return make_mla(rng, seq, 128, 512, 64, 64, 1.0 / math.sqrt(192), name=FP8_MLA,
+                    cache_dtype=FP8, kv_scale=0.25)
 
 
 def llama_decode_fp8(seed: int = 1008, batch: int = 64) -> GqaBatch:
@@ -466,12 +486,12 @@ def gqa_flops(b: GqaBatch, causal: bool = True) -> int:
 
 def mla_bytes(b: MlaBatch, write: bool = True) -> dict:
     """Algorithmic bytes of MLA write + decode: each latent row read once."""
-    rowb = (b.kv_lora_rank + b.rope_dim) * 2
+    rowb = (b.kv_lora_rank + b.rope_dim) * b.cache_elem_bytes
     kv = int(np.sum(b.seq_lens)) * rowb
     q = (b.q_nope.size + b.q_pe.size) * 2
     out = b.num_seqs * b.num_heads * b.kv_lora_rank * 2
     lse = b.num_seqs * b.num_heads * 4
-    wr = (b.kv_c_new.size + b.k_pe_new.size) * 2 * 2 if write else 0
+    wr = (b.kv_c_new.size + b.k_pe_new.size) * (2 + b.cache_elem_bytes) if write else 0
     nblk = int(np.sum((b.seq_lens.astype(np.int64) + b.block_size - 1) // b.block_size))
     meta = nblk * 4 + b.num_seqs * 4 + (b.num_seqs * 8 if write else 0)
     return {"kv": kv, "q": q, "out": out, "lse": lse, "write": wr, "meta": meta,
