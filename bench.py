@@ -17,7 +17,7 @@ is also timed alone with HIP events on the stream it is launched on (the
 library launches on torch's current stream).  The CPU baseline is the float64
 oracle on a bounded sample of the headline workload, on one host thread.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only NAME]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only NAME ...]
 """
 
 from __future__ import annotations
@@ -105,7 +105,7 @@ def gqa_decode_case(b, num_splits, name):
         def kernel():
             pa.decode_balanced(q, cache, bt, sl, b.scale, num_ranges=nr, workspace=ws, out=out,
                                lse=lse, merge=False)
-        kname = f"decode_balanced_kernel<{g}>"
+        kname = f"decode_balanced_kernel<{g}, false>"
         grid = f"{nr} token ranges x {min(b.num_kv_heads, 8)} waves (one per KV head)"
         source = "decode_balanced.hip"
     else:
@@ -153,7 +153,7 @@ def prefill_case(b, name):
             "num_kv_heads": b.num_kv_heads, "head_dim": b.head_dim, "block_size": b.block_size,
             "max_query_len": b.max_query_len, "max_seq_len": b.max_seq_len, "causal": True,
             "grid": "ceil(max_q/128) x num_seqs x Hq work-groups of 256"}
-    return Case(name, step, kernel, by["total"], fl, kb, fl, "mfma", "prefill_kernel",
+    return Case(name, step, kernel, by["total"], fl, kb, fl, "mfma", "prefill_kernel<false>",
                 "prefill.hip", info)
 
 
@@ -187,7 +187,7 @@ def mla_case(b, name):
             "rope_dim": b.rope_dim, "block_size": b.block_size, "max_seq_len": b.max_seq_len,
             "total_keys": int(b.seq_lens.sum()), "schedule": "token-balanced ranges",
             "grid": f"{nr} token ranges x 8 waves (16 heads each)"}
-    return Case(name, step, kernel, by["total"], fl, kb, fl, "mfma", "mla_kernel<true>",
+    return Case(name, step, kernel, by["total"], fl, kb, fl, "mfma", "mla_kernel<true, false>",
                 "mla_decode.hip", info)
 
 
@@ -390,8 +390,11 @@ def build_cases(only):
         W.FP8_MLA: lambda: mla_fp8_case(W.mla_decode_fp8_batch(), W.FP8_MLA),
     }
     names = [HEADLINE] + [n for n in makers if n != HEADLINE]
-    if only is not None:
-        names = [n for n in names if n in only or n == HEADLINE]
+    if only is not None:   # exactly these (the line then reports the first one run)
+        unknown = [n for n in only if n not in makers]
+        if unknown:
+            raise SystemExit(f"unknown workload(s) {unknown}; known: {names}")
+        names = [n for n in names if n in only]
     for n in names:
         t = time.perf_counter()
         case = makers[n]()
@@ -546,7 +549,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--only", nargs="*", default=None, help="extra workloads to run")
+    ap.add_argument("--only", nargs="*", default=None,
+                    help="run only these workloads (default: all, the headline first)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB, --steps times "
@@ -590,7 +594,7 @@ def main():
         log(f"[bench] {case.name}: {res['ms_per_step']} ms/step, {res['step_GBps']} GB/s, "
             f"{res['step_TFLOPs']} TFLOP/s; kernel {rl['kernel']} {rl['kernel_ms']} ms = "
             f"{rl['achieved']} {rl['unit']} ({100 * rl['frac']:.1f}% of peak)")
-        if case.name == HEADLINE:
+        if head is None or case.name == HEADLINE:
             head = (case, step_s, rl)
         del case
         torch.cuda.empty_cache()
@@ -609,8 +613,9 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": HEADLINE, **results[HEADLINE]["config"],
-                   "seq_len": "U[512,8192]", "parallelism": "single GPU"},
+        "config": {"workload": case.name, **results[case.name]["config"],
+                   **({"seq_len": "U[512,8192]"} if case.name == HEADLINE else {}),
+                   "parallelism": "single GPU"},
         "roofline": {k: rl[k] for k in ("bound", "achieved", "peak", "unit", "frac", "traffic")},
         "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline(),
         "dominant_kernel": {k: rl[k] for k in ("kernel", "kernel_ms", "algorithmic_bytes")},
