@@ -335,6 +335,63 @@ def slot_of(block_table_row, pos: int, block_size: int) -> int:
 
 
 # --------------------------------------------------------------------------
+# MLA prefill: the multi-head form over expanded keys and values
+# --------------------------------------------------------------------------
+# "Triton 與 MLA" (設計動機, 關鍵檔案): the MLA layer holds kv_b_proj,
+# qk_nope_head_dim, qk_rope_head_dim and kv_lora_rank, and its backend has two
+# entry points, forward_mqa (decode, over the latent rows) and forward_mha;
+# "Attention Backends" ("Latent attention is a different cache"): prefill and
+# decode use different formulations of the same mathematics.  Reading of the
+# multi-head form: per head h, the key of position j is
+# [kv_c_j W_k[h] | k_pe_j] (qk_nope + rope wide) and its value kv_c_j W_v[h]
+# (v_head wide), with kv_b_proj = W of shape [kv_lora_rank, H, qk_nope + v]
+# (W_k the first qk_nope columns of each head, W_v the rest); expanded keys
+# and values are the projection's output, a bf16 tensor (each element the
+# exact product rounded to nearest even); the query is [q_nope | q_pe] per
+# head; causal attention as in ``paged_attention``.
+
+def _round_bf16(x: np.ndarray) -> np.ndarray:
+    """Nearest-even bf16 value of float64 numbers (exact arithmetic on the
+    float32 rounding: a float64 -> float32 -> bf16 double rounding is avoided
+    by rounding the float64 value directly)."""
+    x = np.asarray(x, dtype=np.float64)
+    m, e = np.frexp(x)                    # x = m 2^e, 0.5 <= |m| < 1
+    q = np.round(m * 256.0) / 256.0       # 8 significant bits, ties to even
+    return np.ldexp(q, e)
+
+
+def mla_expand(latent_rows: np.ndarray, w_kv_b: np.ndarray, qk_nope: int):
+    """Keys and values of the multi-head form from latent rows [S, R + P]:
+    keys [S, H, qk_nope + P] and values [S, H, v] (bf16 values as float64)."""
+    R = w_kv_b.shape[0]
+    kv_c, k_pe = latent_rows[:, :R], latent_rows[:, R:]
+    W = to_f64(w_kv_b)                                       # [R, H, qk_nope + v]
+    kv = _round_bf16(np.einsum("sr,rhc->shc", kv_c, W))      # [S, H, qk_nope + v]
+    S, H, _ = kv.shape
+    keys = np.concatenate([kv[:, :, :qk_nope], np.broadcast_to(k_pe[:, None, :], (S, H, k_pe.shape[1]))],
+                          axis=-1)
+    return keys, kv[:, :, qk_nope:]
+
+
+def mla_prefill(q, cache, w_kv_b, block_table, query_start_loc, seq_lens, scale,
+                qk_nope: int = 128, causal: bool = True, requests=None):
+    """MLA prefill in the multi-head form over the latent cache (already
+    written).  q [T, H, qk_nope + P]; cache [nb, bs, R + P]; w_kv_b
+    [R, H, qk_nope + v].  Returns out [T, H, v] and lse [T, H] (float64)."""
+    T, H, _ = q.shape
+    v_dim = w_kv_b.shape[2] - qk_nope
+    out = np.full((T, H, v_dim), np.nan)
+    lse = np.full((T, H), np.nan)
+    for r in (range(len(seq_lens)) if requests is None else requests):
+        a, b = int(query_start_loc[r]), int(query_start_loc[r + 1])
+        S = int(seq_lens[r])
+        keys, vals = mla_expand(gather_mla(cache, block_table[r], S), w_kv_b, qk_nope)
+        o, l = attention(to_f64(q[a:b]), keys, vals, scale, (S - (b - a)) if causal else None)
+        out[a:b], lse[a:b] = o, l
+    return out, lse
+
+
+# --------------------------------------------------------------------------
 # FP8 KV cache with per-tensor scales
 # --------------------------------------------------------------------------
 # The pages name an FP8 cache read with per-layer k_scale / v_scale while the
@@ -423,4 +480,5 @@ __all__ = [
     "mla_decode", "partial_attention", "lse_merge", "lse_merge_packed",
     "num_kv_splits", "slot_of", "fp8_e4m3_to_f64", "f32_to_fp8_e4m3", "quantize_fp8",
     "cache_write_kv_fp8", "cache_write_mla_fp8", "dequant_kv_cache", "dequant_mla_cache",
+    "mla_expand", "mla_prefill",
 ]

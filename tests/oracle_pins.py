@@ -482,10 +482,77 @@ def pin_fp8_cache_write():
     assert np.array_equal(deq[:, 0], ref[:, 0] * ks) and np.array_equal(deq[:, 1], ref[:, 1] * vs)
 
 
+# --------------------------------------------------------------------------
+# MLA prefill (multi-head form) pins
+# --------------------------------------------------------------------------
+
+def _mla_small_ints(seed, S_list, H, R, P, dn, dv):
+    """Latent rows, kv_b_proj and queries of small integers, so that every
+    expanded key and value is an exact bf16 value (no rounding anywhere)."""
+    rng = _rng(seed)
+    bs = 16
+    nb = sum(-(-S // bs) for S in S_list) + 1
+    cache = np.zeros((nb, bs, R + P))
+    table = np.zeros((len(S_list), max(-(-S // bs) for S in S_list)), np.int32)
+    cur = 1
+    for r, S in enumerate(S_list):
+        n = -(-S // bs)
+        table[r, :n] = np.arange(cur, cur + n)
+        cur += n
+    cache[1:] = rng.integers(-2, 3, size=(nb - 1, bs, R + P))
+    w = rng.integers(-1, 2, size=(R, H, dn + dv)).astype(np.float64)
+    to_bits = lambda a: (np.asarray(a, np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    return to_bits(cache), table, to_bits(w), rng
+
+
+def pin_mla_prefill_equals_absorbed_decode():
+    """The two formulations of MLA ("Attention Backends": prefill and decode
+    use different formulations of the same mathematics): for one query per
+    request, attention over the expanded keys [kv_c W_k | k_pe] and values
+    kv_c W_v equals attention over the latent rows with the absorbed query
+    [W_k q_nope | q_pe], its latent output projected by W_v."""
+    H, R, P, dn, dv = 3, 16, 8, 4, 5
+    S_list = [1, 7, 40]
+    cache, table, w, rng = _mla_small_ints(81, S_list, H, R, P, dn, dv)
+    B = len(S_list)
+    q = rng.standard_normal((B, H, dn + P))
+    qsl = np.arange(B + 1)
+    sl = np.array(S_list)
+    out, lse = O.mla_prefill(q, cache, w, table, qsl, sl, 0.3, qk_nope=dn)
+    W = O.to_f64(w)
+    q_lat = np.einsum("bhd,rhd->bhr", q[:, :, :dn], W[:, :, :dn])    # W_k q_nope per head
+    lat_out, lse2 = O.mla_decode(q_lat, q[:, :, dn:], cache, table, sl, 0.3)
+    out2 = np.einsum("bhr,rhv->bhv", lat_out, W[:, :, dn:])
+    assert np.max(np.abs(out - out2)) < 1e-10 and np.max(np.abs(lse - lse2)) < 1e-10
+
+
+def pin_mla_prefill_torch_sdpa():
+    """A chunked request (context + causal chunk) against torch's
+    scaled_dot_product_attention in float64 on keys and values expanded with
+    torch.einsum, the causal mask bottom-right aligned."""
+    H, R, P, dn, dv = 2, 16, 8, 4, 6
+    S_list, L = [30], 9
+    cache, table, w, rng = _mla_small_ints(82, S_list, H, R, P, dn, dv)
+    q = rng.standard_normal((L, H, dn + P))
+    out, lse = O.mla_prefill(q, cache, w, table, np.array([0, L]), np.array(S_list), 0.4, qk_nope=dn)
+    S = S_list[0]
+    rows = torch.from_numpy(O.gather_mla(cache, table[0], S))
+    W = torch.from_numpy(O.to_f64(w))
+    kv = torch.einsum("sr,rhc->shc", rows[:, :R], W)
+    K = torch.cat([kv[:, :, :dn], rows[:, None, R:].expand(S, H, P)], dim=-1)
+    V = kv[:, :, dn:]
+    mask = torch.arange(S)[None, :] <= (S - L + torch.arange(L))[:, None]
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q).permute(1, 0, 2), K.permute(1, 0, 2), V.permute(1, 0, 2),
+        attn_mask=mask, scale=0.4).permute(1, 0, 2).numpy()
+    assert np.max(np.abs(out - ref)) < 1e-12
+
+
 ALL_PINS = [
     pin_bf16_decoding, pin_go_program_slots, pin_go_program_identical,
     pin_num_kv_splits, pin_cache_write_bytes, pin_fig5c_merge, pin_merge_edges,
     pin_closed_forms, pin_torch_sdpa_gqa, pin_torch_sdpa_mla,
     pin_bruteforce_varlen, pin_split_merge_equals_unsplit, pin_block_permutation,
     pin_chunked_prefill, pin_fp8_e4m3_decoding, pin_fp8_e4m3_encoding, pin_fp8_cache_write,
+    pin_mla_prefill_equals_absorbed_decode, pin_mla_prefill_torch_sdpa,
 ]

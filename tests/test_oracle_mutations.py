@@ -3,7 +3,8 @@ catch every one: a dropped scale, a wrong KV-head map, an off-by-one causal
 mask, a transposed operand, a wrong log base, a wrong block walk, swapped K/V
 halves, a linear (not exponential) merge weight, a floor in the split count,
 an FP8 decoding with the wrong exponent bias, FP8 rounding toward zero,
-swapped K/V dequantisation scales."""
+swapped K/V dequantisation scales, MLA keys expanded with the value columns,
+MLA keys without their rope part."""
 import numpy as np
 import pytest
 
@@ -84,6 +85,27 @@ def _dequant_swapped(cache, k_scale, v_scale):
     return _dequant(cache, v_scale, k_scale)
 
 
+_mla_expand = O.mla_expand
+
+
+def _expand_swapped_roles(rows, w, qk_nope):
+    """Keys expanded with the value columns' block and vice versa."""
+    W = np.asarray(w)
+    dv = W.shape[2] - qk_nope
+    if dv < qk_nope:
+        return _mla_expand(rows, w, qk_nope)
+    swapped = np.concatenate([W[:, :, qk_nope:qk_nope * 2], W[:, :, :qk_nope], W[:, :, 2 * qk_nope:]], axis=2) \
+        if dv >= qk_nope else W
+    return _mla_expand(rows, swapped, qk_nope)
+
+
+def _expand_no_rope(rows, w, qk_nope):
+    keys, vals = _mla_expand(rows, w, qk_nope)
+    keys = keys.copy()
+    keys[:, :, qk_nope:] = 0.0
+    return keys, vals
+
+
 MUTATIONS = {
     "drop_scale": ("attention", _attention_variant(drop_scale=True)),
     "kv_head_modulo": ("attention", _attention_variant(kv_map=lambda h, Hq, Hkv: h % Hkv)),
@@ -99,6 +121,8 @@ MUTATIONS = {
     "fp8_exponent_bias_8": ("fp8_e4m3_to_f64", _fp8_bias8),
     "fp8_round_toward_zero": ("f32_to_fp8_e4m3", _fp8_truncate),
     "fp8_swapped_plane_scales": ("dequant_kv_cache", _dequant_swapped),
+    "mla_expand_swapped_kv_columns": ("mla_expand", _expand_swapped_roles),
+    "mla_expand_drops_rope_key": ("mla_expand", _expand_no_rope),
 }
 
 
