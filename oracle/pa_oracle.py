@@ -343,9 +343,10 @@ def slot_of(block_table_row, pos: int, block_size: int) -> int:
 # "Attention Backends" ("Latent attention is a different cache"): prefill and
 # decode use different formulations of the same mathematics.  Reading of the
 # multi-head form: per head h, the key of position j is
-# [kv_c_j W_k[h] | k_pe_j] (qk_nope + rope wide) and its value kv_c_j W_v[h]
-# (v_head wide), with kv_b_proj = W of shape [kv_lora_rank, H, qk_nope + v]
-# (W_k the first qk_nope columns of each head, W_v the rest); expanded keys
+# [W_k[h] kv_c_j | k_pe_j] (qk_nope + rope wide) and its value W_v[h] kv_c_j
+# (v_head wide), with kv_b_proj's weight stored as a linear layer stores it,
+# [H * (qk_nope + v), kv_lora_rank] = [H, qk_nope + v, kv_lora_rank] (W_k the
+# first qk_nope output rows of each head, W_v the rest); expanded keys
 # and values are the projection's output, a bf16 tensor (each element the
 # exact product rounded to nearest even); the query is [q_nope | q_pe] per
 # head; causal attention as in ``paged_attention``.
@@ -362,11 +363,12 @@ def _round_bf16(x: np.ndarray) -> np.ndarray:
 
 def mla_expand(latent_rows: np.ndarray, w_kv_b: np.ndarray, qk_nope: int):
     """Keys and values of the multi-head form from latent rows [S, R + P]:
-    keys [S, H, qk_nope + P] and values [S, H, v] (bf16 values as float64)."""
-    R = w_kv_b.shape[0]
+    keys [S, H, qk_nope + P] and values [S, H, v] (bf16 values as float64).
+    w_kv_b: [H, qk_nope + v, R]."""
+    R = w_kv_b.shape[2]
     kv_c, k_pe = latent_rows[:, :R], latent_rows[:, R:]
-    W = to_f64(w_kv_b)                                       # [R, H, qk_nope + v]
-    kv = _round_bf16(np.einsum("sr,rhc->shc", kv_c, W))      # [S, H, qk_nope + v]
+    W = to_f64(w_kv_b)                                       # [H, qk_nope + v, R]
+    kv = _round_bf16(np.einsum("sr,hcr->shc", kv_c, W))      # [S, H, qk_nope + v]
     S, H, _ = kv.shape
     keys = np.concatenate([kv[:, :, :qk_nope], np.broadcast_to(k_pe[:, None, :], (S, H, k_pe.shape[1]))],
                           axis=-1)
@@ -377,9 +379,9 @@ def mla_prefill(q, cache, w_kv_b, block_table, query_start_loc, seq_lens, scale,
                 qk_nope: int = 128, causal: bool = True, requests=None):
     """MLA prefill in the multi-head form over the latent cache (already
     written).  q [T, H, qk_nope + P]; cache [nb, bs, R + P]; w_kv_b
-    [R, H, qk_nope + v].  Returns out [T, H, v] and lse [T, H] (float64)."""
+    [H, qk_nope + v, R].  Returns out [T, H, v] and lse [T, H] (float64)."""
     T, H, _ = q.shape
-    v_dim = w_kv_b.shape[2] - qk_nope
+    v_dim = w_kv_b.shape[1] - qk_nope
     out = np.full((T, H, v_dim), np.nan)
     lse = np.full((T, H), np.nan)
     for r in (range(len(seq_lens)) if requests is None else requests):

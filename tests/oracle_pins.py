@@ -500,7 +500,7 @@ def _mla_small_ints(seed, S_list, H, R, P, dn, dv):
         table[r, :n] = np.arange(cur, cur + n)
         cur += n
     cache[1:] = rng.integers(-2, 3, size=(nb - 1, bs, R + P))
-    w = rng.integers(-1, 2, size=(R, H, dn + dv)).astype(np.float64)
+    w = rng.integers(-1, 2, size=(H, dn + dv, R)).astype(np.float64)
     to_bits = lambda a: (np.asarray(a, np.float32).view(np.uint32) >> 16).astype(np.uint16)
     return to_bits(cache), table, to_bits(w), rng
 
@@ -520,9 +520,9 @@ def pin_mla_prefill_equals_absorbed_decode():
     sl = np.array(S_list)
     out, lse = O.mla_prefill(q, cache, w, table, qsl, sl, 0.3, qk_nope=dn)
     W = O.to_f64(w)
-    q_lat = np.einsum("bhd,rhd->bhr", q[:, :, :dn], W[:, :, :dn])    # W_k q_nope per head
+    q_lat = np.einsum("bhd,hdr->bhr", q[:, :, :dn], W[:, :dn, :])    # W_k^T q_nope per head
     lat_out, lse2 = O.mla_decode(q_lat, q[:, :, dn:], cache, table, sl, 0.3)
-    out2 = np.einsum("bhr,rhv->bhv", lat_out, W[:, :, dn:])
+    out2 = np.einsum("bhr,hvr->bhv", lat_out, W[:, dn:, :])
     assert np.max(np.abs(out - out2)) < 1e-10 and np.max(np.abs(lse - lse2)) < 1e-10
 
 
@@ -538,7 +538,7 @@ def pin_mla_prefill_torch_sdpa():
     S = S_list[0]
     rows = torch.from_numpy(O.gather_mla(cache, table[0], S))
     W = torch.from_numpy(O.to_f64(w))
-    kv = torch.einsum("sr,rhc->shc", rows[:, :R], W)
+    kv = torch.einsum("sr,hcr->shc", rows[:, :R], W)
     K = torch.cat([kv[:, :, :dn], rows[:, None, R:].expand(S, H, P)], dim=-1)
     V = kv[:, :, dn:]
     mask = torch.arange(S)[None, :] <= (S - L + torch.arange(L))[:, None]

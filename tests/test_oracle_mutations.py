@@ -89,13 +89,9 @@ _mla_expand = O.mla_expand
 
 
 def _expand_swapped_roles(rows, w, qk_nope):
-    """Keys expanded with the value columns' block and vice versa."""
+    """Keys expanded with the value rows' block and vice versa."""
     W = np.asarray(w)
-    dv = W.shape[2] - qk_nope
-    if dv < qk_nope:
-        return _mla_expand(rows, w, qk_nope)
-    swapped = np.concatenate([W[:, :, qk_nope:qk_nope * 2], W[:, :, :qk_nope], W[:, :, 2 * qk_nope:]], axis=2) \
-        if dv >= qk_nope else W
+    swapped = np.concatenate([W[:, qk_nope:2 * qk_nope], W[:, :qk_nope], W[:, 2 * qk_nope:]], axis=1)
     return _mla_expand(rows, swapped, qk_nope)
 
 
