@@ -7,7 +7,7 @@ The headline line measures the Llama-3-8B-shaped GQA decode (64 requests,
 seq_len U[512, 8192], 32 q / 8 kv heads, d=128, bf16, block 16) in HBM GB/s;
 the other workloads (tiny fp32 decode, chunked prefill, long-context decode,
 MLA decode, a mixed prefill + decode batch, a batch sharing a prefix, GQA and
-MLA decode over FP8 caches) are measured the same way and
+MLA decode over FP8 caches, MLA prefill) are measured the same way and
 reported under "workloads".  Inputs are generated on the host by ``workloads.py`` (seeded),
 uploaded once, and resident in HBM before any timed region.
 
@@ -374,6 +374,41 @@ def mla_fp8_case(b, name):
                 "mla_kernel<true, true> + merge", "mla_decode.hip", info)
 
 
+def mla_prefill_case(b, name):
+    """MLA prefill in the multi-head form: latent write + key offsets +
+    projection of every key + causal attention.  The timed call is the whole
+    computation without the write (three kernels), priced against the bf16
+    MFMA peak with the projection's and the attention's flops."""
+    import torch
+    import paged_kv_attention_pa_amd as pa
+    import workloads as W
+    cache, q, w = _dev(b.cache), _dev(b.q), _dev(b.w_kv_b)
+    bt, sl, qsl = _dev(b.block_table), _dev(b.seq_lens), _dev(b.query_start_loc)
+    kc, kp, sm = _dev(b.kv_c_new), _dev(b.k_pe_new), _dev(b.slot_mapping)
+    ws = torch.empty(pa.mla_prefill_workspace_bytes(b.num_seqs, b.total_keys, b.num_heads),
+                     dtype=torch.uint8, device="cuda")
+    out = torch.empty((b.num_tokens, b.num_heads, 128), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((b.num_tokens, b.num_heads), dtype=torch.float32, device="cuda")
+
+    def step():
+        pa.mla_prefill(q, cache, bt, qsl, sl, w, b.max_query_len, b.total_keys, b.scale, kv_c=kc,
+                       k_pe=kp, slot_mapping=sm, workspace=ws, out=out, lse=lse)
+
+    def kernel():
+        pa.mla_prefill(q, cache, bt, qsl, sl, w, b.max_query_len, b.total_keys, b.scale,
+                       workspace=ws, out=out, lse=lse)
+
+    fl = W.mla_prefill_flops(b)
+    kv = b.total_keys * 1152 + b.w_kv_b.size * 2 + b.q.size * 2 + b.num_tokens * b.num_heads * (256 + 4)
+    info = {"num_seqs": b.num_seqs, "num_tokens": b.num_tokens, "num_heads": b.num_heads,
+            "kv_lora_rank": 512, "rope_dim": 64, "qk_head_dim": 192, "v_head_dim": 128,
+            "block_size": b.block_size, "total_keys": b.total_keys,
+            "max_query_len": b.max_query_len, "projection_flops": fl["projection"],
+            "attention_flops": fl["attention"], "timed": "key offsets + projection + attention"}
+    return Case(name, step, kernel, kv, fl["total"], kv, fl["total"], "mfma",
+                "mla_expand_kernel + mla_attn_kernel", "mla_prefill.hip", info)
+
+
 def build_cases(only):
     import workloads as W
     makers = {
@@ -388,6 +423,7 @@ def build_cases(only):
         W.CASCADE: lambda: cascade_case(W.cascade_batch(), W.CASCADE),
         W.FP8_DECODE: lambda: fp8_decode_case(W.llama_decode_fp8(), W.FP8_DECODE),
         W.FP8_MLA: lambda: mla_fp8_case(W.mla_decode_fp8_batch(), W.FP8_MLA),
+        W.MLA_PREFILL: lambda: mla_prefill_case(W.mla_prefill_batch(), W.MLA_PREFILL),
     }
     names = [HEADLINE] + [n for n in makers if n != HEADLINE]
     if only is not None:   # exactly these (the line then reports the first one run)

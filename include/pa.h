@@ -534,6 +534,55 @@ pa_status_t pa_decode_fp8(const void* q, const void* k, const void* v,
                           void* workspace, size_t workspace_bytes,
                           void* out, float* lse, hipStream_t stream);
 
+/* ---------------------------------------------------------------------------
+ * MLA prefill: the multi-head form over the latent cache.
+ *
+ * Decode reads the latent rows directly (pa_mla_decode: one key head of
+ * kv_lora_rank + rope dims); prefill has many queries per key, and the
+ * multi-head form is cheaper there: every key's latent part is projected by
+ * kv_b_proj into per-head keys and values, and each head attends as ordinary
+ * causal attention ("Triton 與 MLA", 設計動機 and 關鍵檔案: the layer holds
+ * kv_b_proj, qk_nope_head_dim, qk_rope_head_dim, kv_lora_rank and has a
+ * separate multi-head entry point; "Attention Backends", latent attention:
+ * prefill and decode use different formulations of the same mathematics).
+ * Per head h: key_j = [W_k[h] kv_c_j | k_pe_j], value_j = W_v[h] kv_c_j, with
+ * the weight stored as a linear layer stores it.
+ *
+ * q:           [num_tokens, num_heads, qk_nope_dim + rope_dim] bf16 at element
+ *              strides (q_stride_t, q_stride_h), last dim contiguous
+ * kv_c, k_pe:  new latent rows [num_tokens, kv_lora_rank], [num_tokens,
+ *              rope_dim] bf16 written at slot_mapping first, or all NULL
+ * kv_cache:    latent cache [num_blocks, block_size, kv_lora_rank + rope_dim]
+ * query_start_loc, seq_lens, block_table: as pa_prefill_varlen (causal,
+ *              bottom-right aligned)
+ * total_keys:  host copy of the sum of seq_lens (every key is projected once)
+ * w_kv_b:      [num_heads * (qk_nope_dim + v_head_dim), kv_lora_rank] bf16:
+ *              head h's rows h * 256 .. h * 256 + 127 expand keys, the next 128
+ *              values
+ * workspace:   pa_mla_prefill_workspace_bytes(num_seqs, total_keys, num_heads)
+ *              bytes, 256-byte aligned: key offsets and the projected keys
+ *              [total_keys, num_heads, 192] and values [total_keys, num_heads,
+ *              128], bf16 (the projection's output dtype)
+ * out:         [num_tokens, num_heads, v_head_dim] bf16; lse [num_tokens,
+ *              num_heads] fp32 or NULL
+ * Supported: kv_lora_rank 512, rope_dim 64, qk_nope_dim 128, v_head_dim 128.
+ * Enqueues: the latent write (if given), the key offsets, the projection and
+ * the attention.
+ * ------------------------------------------------------------------------- */
+size_t pa_mla_prefill_workspace_bytes(int num_seqs, int total_keys, int num_heads);
+
+pa_status_t pa_mla_prefill(const void* q, int64_t q_stride_t, int64_t q_stride_h,
+                           const void* kv_c, const void* k_pe,
+                           void* kv_cache, int64_t num_blocks, int block_size,
+                           const int32_t* block_table, int max_blocks_per_seq,
+                           const int64_t* slot_mapping,
+                           const int32_t* query_start_loc, const int32_t* seq_lens, int num_seqs,
+                           int num_tokens, int max_query_len, int total_keys,
+                           const void* w_kv_b, int num_heads, int kv_lora_rank, int rope_dim,
+                           int qk_nope_dim, int v_head_dim, float scale,
+                           void* workspace, size_t workspace_bytes,
+                           void* out, float* lse, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

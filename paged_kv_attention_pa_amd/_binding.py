@@ -55,6 +55,10 @@ _SIGNATURES = {
     "pa_mla_decode_fp8": (_i32, [_vp, _i64, _i64, _vp, _i64, _i64, _vp, _vp, _vp, _i64, _i32, _vp,
                                  _i32, _vp, _vp, _i32, _i32, _i32, _i32, _f32, _f32, _i32, _vp,
                                  _sz, _vp, _vp, _vp]),
+    "pa_mla_prefill_workspace_bytes": (_sz, [_i32, _i32, _i32]),
+    "pa_mla_prefill": (_i32, [_vp, _i64, _i64, _vp, _vp, _vp, _i64, _i32, _vp, _i32, _vp, _vp, _vp,
+                              _i32, _i32, _i32, _i32, _vp, _i32, _i32, _i32, _i32, _i32, _f32, _vp,
+                              _sz, _vp, _vp, _vp]),
     "pa_decode_fp8": (_i32, [_vp, _vp, _vp, _vp, _i64, _i32, _vp, _i32, _vp, _vp, _i32, _i32,
                              _i32, _i32, _f32, _f32, _f32, _i32, _vp, _sz, _vp, _vp, _vp]),
     "pa_cascade_attention": (_i32, [_vp, _i32, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _vp, _vp,
@@ -612,6 +616,50 @@ def mla_decode_fp8(q_nope, q_pe, kv_cache, block_table, seq_lens, scale: float,
                                        block_table.shape[1], _ptr(slot_mapping), _ptr(seq_lens), B,
                                        H, R, P, float(scale), float(kv_scale), nr, _ptr(workspace),
                                        wbytes, _ptr(out), _ptr(lse), _stream(stream)))
+    return out, lse
+
+
+def mla_prefill_workspace_bytes(num_seqs: int, total_keys: int, num_heads: int) -> int:
+    return library().pa_mla_prefill_workspace_bytes(int(num_seqs), int(total_keys), int(num_heads))
+
+
+def mla_prefill(q, kv_cache, block_table, query_start_loc, seq_lens, w_kv_b, max_query_len: int,
+                total_keys: int, scale: float, kv_c=None, k_pe=None, slot_mapping=None,
+                workspace=None, out=None, lse=None, return_lse: bool = True, stream=None):
+    """MLA prefill in the multi-head form: q [T, H, 192] bf16 (last dim
+    contiguous), latent cache [nb, bs, 576], w_kv_b [H * 256, 512] (or
+    [H, 256, 512]) bf16; total_keys = sum of seq_lens (host).  Returns
+    (out [T, H, 128], lse [T, H])."""
+    torch = _torch()
+    _dev(kv_cache, block_table, query_start_loc, seq_lens, w_kv_b, kv_c, k_pe, slot_mapping,
+         workspace, out, lse)
+    _need(q.is_cuda and q.stride(-1) == 1, "q must be a GPU tensor with a contiguous last dim")
+    _need(q.dtype == torch.bfloat16 and kv_cache.dtype == torch.bfloat16 and
+          w_kv_b.dtype == torch.bfloat16, "bf16 q, cache and weight")
+    _int_tensor(block_table, "int32", "block_table")
+    _int_tensor(seq_lens, "int32", "seq_lens")
+    _int_tensor(query_start_loc, "int32", "query_start_loc")
+    T, H, dq = q.shape
+    nb, bs, row = kv_cache.shape
+    R = w_kv_b.shape[-1]
+    _need(w_kv_b.numel() == H * 256 * R, "w_kv_b must be [H * 256, kv_lora_rank]")
+    N = seq_lens.numel()
+    _need(query_start_loc.numel() == N + 1, "query_start_loc must have num_seqs + 1 entries")
+    if out is None:
+        out = torch.empty((T, H, 128), dtype=torch.bfloat16, device=q.device)
+    if lse is None and return_lse:
+        lse = torch.empty((T, H), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        need = mla_prefill_workspace_bytes(N, total_keys, H)
+        workspace = torch.empty(max(1, need), dtype=torch.uint8, device=q.device)
+    wbytes = workspace.numel() * workspace.element_size()
+    _check(library().pa_mla_prefill(_ptr(q), q.stride(0), q.stride(1), _ptr(kv_c), _ptr(k_pe),
+                                    _ptr(kv_cache), nb, bs, _ptr(block_table), block_table.shape[1],
+                                    _ptr(slot_mapping), _ptr(query_start_loc), _ptr(seq_lens), N, T,
+                                    int(max_query_len), int(total_keys), _ptr(w_kv_b), H, R,
+                                    row - R, dq - (row - R), 256 - (dq - (row - R)), float(scale),
+                                    _ptr(workspace), wbytes, _ptr(out), _ptr(lse),
+                                    _stream(stream)))
     return out, lse
 
 

@@ -1111,4 +1111,88 @@ pa_status_t pa_mla_decode_fp8(const void* q_nope, int64_t qn_stride_b, int64_t q
                                   nr, out, lse, stream);
 }
 
+// ---------------------------------------------------------------------------
+// MLA prefill workspace: key offsets [N + 1] int32, projected keys
+// [total, H, 192] and values [total, H, 128] bf16, each 256-byte aligned.
+static bool mla_prefill_layout(int num_seqs, int total_keys, int num_heads, size_t* k_off,
+                               size_t* v_off, size_t* total) {
+  if (num_seqs < 0 || total_keys < 0 || num_heads <= 0) return false;
+  auto up = [](unsigned __int128 x) { return (x + 255) / 256 * 256; };
+  unsigned __int128 off = up((unsigned __int128)(num_seqs + 1) * 4);
+  *k_off = size_t(off);
+  off = up(off + (unsigned __int128)total_keys * (unsigned)num_heads * 192 * 2);
+  *v_off = size_t(off);
+  off = up(off + (unsigned __int128)total_keys * (unsigned)num_heads * 128 * 2);
+  if (off > (unsigned __int128)(SIZE_MAX / 2)) return false;
+  *total = size_t(off);
+  return true;
+}
+
+size_t pa_mla_prefill_workspace_bytes(int num_seqs, int total_keys, int num_heads) {
+  size_t k_off, v_off, total;
+  return mla_prefill_layout(num_seqs, total_keys, num_heads, &k_off, &v_off, &total) ? total : 0;
+}
+
+pa_status_t pa_mla_prefill(const void* q, int64_t q_stride_t, int64_t q_stride_h,
+                           const void* kv_c, const void* k_pe, void* kv_cache,
+                           int64_t num_blocks, int block_size, const int32_t* block_table,
+                           int max_blocks_per_seq, const int64_t* slot_mapping,
+                           const int32_t* query_start_loc, const int32_t* seq_lens, int num_seqs,
+                           int num_tokens, int max_query_len, int total_keys,
+                           const void* w_kv_b, int num_heads, int kv_lora_rank, int rope_dim,
+                           int qk_nope_dim, int v_head_dim, float scale, void* workspace,
+                           size_t workspace_bytes, void* out, float* lse, hipStream_t stream) {
+  PA_REQUIRE(scale_ok(scale), PA_ERR_INVALID, "scale must be finite and >= 0");
+  pa_status_t st = check_common_cache(num_blocks, block_size, block_table, max_blocks_per_seq,
+                                      seq_lens, num_seqs, 0);
+  if (st != PA_OK) return st;
+  PA_REQUIRE(kv_lora_rank > 0 && rope_dim > 0 && qk_nope_dim > 0 && v_head_dim > 0,
+             PA_ERR_INVALID, "MLA dims must be > 0");
+  PA_REQUIRE(kv_lora_rank == 512 && rope_dim == 64 && qk_nope_dim == 128 && v_head_dim == 128,
+             PA_ERR_UNSUPPORTED,
+             "MLA prefill supports kv_lora_rank 512, rope 64, qk_nope 128, v 128 (got %d, %d, %d, %d)",
+             kv_lora_rank, rope_dim, qk_nope_dim, v_head_dim);
+  PA_REQUIRE(num_heads > 0, PA_ERR_INVALID, "num_heads must be > 0");
+  PA_REQUIRE(num_tokens >= 0 && max_query_len >= 0 && total_keys >= 0, PA_ERR_INVALID,
+             "num_tokens, max_query_len and total_keys must be >= 0");
+  PA_REQUIRE(max_query_len <= num_tokens || num_seqs == 0, PA_ERR_INVALID,
+             "max_query_len exceeds num_tokens");
+  PA_REQUIRE(q_stride_h >= 192 && q_stride_t >= int64_t(num_heads) * q_stride_h, PA_ERR_INVALID,
+             "q strides must cover [num_heads, 192] per token");
+  PA_REQUIRE(q_stride_t % 8 == 0 && q_stride_h % 8 == 0, PA_ERR_INVALID,
+             "q strides must be multiples of 8 elements (16-byte rows)");
+  PA_REQUIRE((kv_c == nullptr) == (k_pe == nullptr), PA_ERR_INVALID,
+             "kv_c and k_pe must both be given or both NULL");
+  PA_REQUIRE(kv_c == nullptr || slot_mapping != nullptr, PA_ERR_INVALID,
+             "kv_c/k_pe given without slot_mapping");
+  PA_REQUIRE(slot_mapping == nullptr || kv_c != nullptr, PA_ERR_INVALID,
+             "slot_mapping given without kv_c/k_pe");
+  size_t k_off, v_off, need;
+  PA_REQUIRE(mla_prefill_layout(num_seqs, total_keys, num_heads, &k_off, &v_off, &need),
+             PA_ERR_INVALID, "workspace size overflows");
+  if (num_seqs == 0 || num_tokens == 0) return ok();
+  PA_REQUIRE(q && kv_cache && out && query_start_loc && w_kv_b, PA_ERR_INVALID,
+             "q, kv_cache, out, query_start_loc and w_kv_b must be non-null");
+  PA_REQUIRE(workspace != nullptr && workspace_bytes >= need, PA_ERR_WORKSPACE,
+             "workspace of %zu bytes needed (got %zu)", need, workspace_bytes);
+  PA_REQUIRE((reinterpret_cast<uintptr_t>(workspace) & 255) == 0, PA_ERR_INVALID,
+             "workspace must be 256-byte aligned");
+  PA_REQUIRE(int64_t(total_keys) * num_heads * 192 <= INT64_MAX / 4, PA_ERR_INVALID,
+             "total_keys too large");
+  if (kv_c) {
+    pa::CacheWriteMLA w{kv_c, kv_lora_rank, k_pe, rope_dim, kv_cache, num_blocks, block_size,
+                        kv_lora_rank, rope_dim, slot_mapping, num_tokens};
+    hipError_t e = pa::launch_cache_write_mla(w, stream);
+    if (e != hipSuccess) return hip_fail(e, "MLA latent write launch");
+  }
+  char* ws = static_cast<char*>(workspace);
+  pa::MlaPrefill m{q, q_stride_t, q_stride_h, kv_cache, num_blocks, block_size, block_table,
+                   max_blocks_per_seq, query_start_loc, seq_lens, num_seqs, num_tokens,
+                   max_query_len, total_keys, w_kv_b, num_heads, scale,
+                   reinterpret_cast<int32_t*>(ws), ws + k_off, ws + v_off, out, lse};
+  hipError_t e = pa::launch_mla_prefill(m, stream);
+  if (e != hipSuccess) return hip_fail(e, "MLA prefill launch");
+  return ok();
+}
+
 }  // extern "C"

@@ -116,6 +116,22 @@ struct MlaDecode {
 };
 hipError_t launch_mla_decode(const MlaDecode& a, hipStream_t s);
 
+// ----------------------------------------------------------- MLA prefill
+// Multi-head form: kv_lora_rank 512, rope 64, qk_nope 128, v 128.
+struct MlaPrefill {
+  const void* q; int64_t q_st, q_sh;        // [T, H, 192] bf16 (element strides)
+  const void* cache; int64_t num_blocks; int block_size;   // latent [nb, bs, 576] bf16
+  const int32_t* block_table; int max_blocks;
+  const int32_t* query_start_loc; const int32_t* seq_lens; int num_seqs;
+  int num_tokens; int max_query_len; int total_keys;
+  const void* w;                            // kv_b_proj weight [H, 256, 512] bf16
+  int num_heads; float scale;
+  int32_t* key_start;                       // [N + 1] (workspace)
+  void* k_exp; void* v_exp;                 // [total_keys, H, 192], [total_keys, H, 128] (workspace)
+  void* out; float* lse;                    // [T, H, 128] bf16, [T, H] fp32 or null
+};
+hipError_t launch_mla_prefill(const MlaPrefill& a, hipStream_t s);
+
 // --------------------------------------------------------------- prefill
 struct PrefillVarlen {
   const void* q;                  // [T, Hq, D]

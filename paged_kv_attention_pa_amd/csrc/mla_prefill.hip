@@ -1,0 +1,478 @@
+// MLA prefill in the multi-head form over the latent cache.
+//
+// Method: "Triton 與 MLA：可移植注意力與潛空間注意力" (設計動機, 關鍵檔案: the MLA
+// layer holds kv_b_proj, qk_nope_head_dim, qk_rope_head_dim and kv_lora_rank;
+// its backend's prefill entry point is the multi-head form) and "Attention
+// Backends" (latent attention: prefill and decode use different formulations
+// of the same mathematics).  Per head h the key of position j is
+// [W_k[h] kv_c_j | k_pe_j] (128 + 64) and its value W_v[h] kv_c_j (128), with
+// kv_b_proj's weight W [H, 256, 512] (rows 0..127 of a head expand keys, rows
+// 128..255 values); causal attention of the chunk's queries [q_nope | q_pe]
+// ("第 1 章 注意力后端", §2.1, bottom-right aligned; §4.1 tiling with an
+// online softmax).
+//
+// Three kernels:
+// * key_start_kernel: cumulative key counts of the requests (one block scan).
+// * mla_expand_kernel: the projection of every key of the batch, a bf16 GEMM
+//   E^T[n][g] = sum_k W[n][k] L[g][k] over the gathered latent rows L (n = a
+//   projection output of one head, g = a key of the batch), 128 x 128 tiles on
+//   v_mfma_f32_32x32x16_bf16, both operands staged in LDS by
+//   global_load_lds_dwordx4 (double-buffered 64-deep k slices); the work-group
+//   holding a head's key rows also copies k_pe next to them, so the expanded
+//   key row is 192 contiguous elements.
+// * mla_attn_kernel: the prefill kernel's tiling (128 query rows of one head
+//   per work-group, 64-key tiles gathered into LDS by DMA, S^T = K Q^T and
+//   O^T += V^T P^T on 32x32x16 MFMAs, online softmax in the exp2 domain) with
+//   a 192-wide key (a 128-wide tile and a 64-wide rope tile) read from the
+//   expanded rows, which are contiguous per request.
+#include "launch.hpp"
+#include "pa_device.hpp"
+
+namespace pa {
+namespace {
+
+constexpr int kR = 512;          // kv_lora_rank
+constexpr int kP = 64;           // rope dims
+constexpr int kDn = 128;         // qk_nope dims
+constexpr int kDv = 128;         // v dims
+constexpr int kDq = kDn + kP;    // 192: query / key width
+constexpr int kOut = kDn + kDv;  // 256 projection outputs per head
+constexpr int kLatBytes = (kR + kP) * 2;   // 1152 B per latent row
+constexpr int kXcds = 8;
+
+// ---------------------------------------------------------------- key starts
+__global__ __launch_bounds__(256) void key_start_kernel(MlaPrefill a) {
+  __shared__ int s_sum[4];
+  const int cap = a.max_blocks * a.block_size;
+  int carry = 0;
+  if (threadIdx.x == 0) a.key_start[0] = 0;
+  for (int base = 0; base < a.num_seqs; base += 256) {
+    const int r = base + threadIdx.x;
+    int v = r < a.num_seqs ? min(max(a.seq_lens[r], 0), cap) : 0;
+    // inclusive scan within the wave, then across the four waves
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int t = __shfl_up(v, o);
+      if (lane >= o) v += t;
+    }
+    if (lane == 63) s_sum[w] = v;
+    __syncthreads();
+    int before = carry;
+    for (int i = 0; i < w; ++i) before += s_sum[i];
+    if (r < a.num_seqs) a.key_start[r + 1] = before + v;
+    carry += s_sum[0] + s_sum[1] + s_sum[2] + s_sum[3];
+    __syncthreads();
+  }
+}
+
+// ------------------------------------------------------------- expansion
+constexpr int kEM = 128;                     // projection outputs per work-group
+constexpr int kEN = 128;                     // keys per work-group
+constexpr int kEK = 64;                      // k per stage
+constexpr int kESlice = kEK * 2;             // 128 B of a row per stage
+constexpr int kETile = kEM * kESlice;        // 16 KiB (either operand)
+constexpr int kEStage = 2 * kETile;          // W tile, then latent tile
+// 16-byte chunk c of row r of a staged slice sits in slot c ^ ((r >> 1) & 7):
+// rows are 128 B, so a 16-lane phase reading one chunk of 16 consecutive rows
+// hits 16 distinct 16-byte bank groups.
+__device__ __forceinline__ int eslot(int r, int c) { return c ^ ((r >> 1) & 7); }
+
+__global__ __launch_bounds__(256, 2) void mla_expand_kernel(MlaPrefill a) {
+  __shared__ __align__(16) char smem[2 * kEStage];
+  __shared__ uint64_t s_row[kEN];             // byte offset of each key's latent row
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
+  const int H = a.num_heads;
+  const int n_tiles = 2 * H;                  // a tile is the key half or the value half of a head
+  // the n tiles of one key tile run on one XCD, one after another (their
+  // latent rows stay in its L2)
+  const int id = blockIdx.x;
+  const int xcd = id % kXcds, slot = id / kXcds;
+  const int g_tile = (slot / n_tiles) * kXcds + xcd;
+  const int n_tile = slot % n_tiles;
+  const int total = a.total_keys;
+  const int g0 = g_tile * kEN;
+  if (g0 >= total) return;
+  const int h = n_tile >> 1, half = n_tile & 1;
+
+  // latent row of each key of the tile (keys past the batch re-read the last)
+  if (tid < kEN) {
+    const int g = min(g0 + tid, total - 1);
+    int lo = 0, hi = a.num_seqs - 1;          // request r with key_start[r] <= g < key_start[r + 1]
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (a.key_start[mid] <= g) lo = mid; else hi = mid - 1;
+    }
+    const int r = lo;
+    const int j = g - a.key_start[r];
+    const int page = j / a.block_size;
+    int64_t blk = a.block_table[int64_t(r) * a.max_blocks + page];
+    blk = (blk < 0 || blk >= a.num_blocks) ? 0 : blk;
+    s_row[tid] = uint64_t((blk * a.block_size + (j - page * a.block_size)) * int64_t(kLatBytes));
+  }
+  __syncthreads();
+
+  const char* wbase = static_cast<const char*>(a.w) + int64_t(n_tile) * kEM * (kR * 2);
+  const char* cbase = static_cast<const char*>(a.cache);
+  // DMA: 16 wave-wide loads per operand and stage (8 rows x 128 B each); wave
+  // w issues loads w, w + 4, w + 8, w + 12 of both.  Lane i of load j: row
+  // 8 j + i / 8, slot i % 8, which holds chunk eslot(row, slot).
+  uint32_t w_off[4], l_row[4], l_chunk[4];
+#pragma unroll
+  for (int jj = 0; jj < 4; ++jj) {
+    const int j = wave + 4 * jj;
+    const int row = 8 * j + (lane >> 3);
+    const int c = eslot(row, lane & 7);
+    w_off[jj] = uint32_t(row * (kR * 2) + 16 * c);
+    l_row[jj] = uint32_t(row);
+    l_chunk[jj] = uint32_t(16 * c);
+  }
+  typedef __attribute__((address_space(3))) void* lds_ptr;
+  auto gload = [&](int stage, int buf) {
+    char* dw = smem + buf * kEStage;
+    char* dl = dw + kETile;
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const int j = wave + 4 * jj;
+      __builtin_amdgcn_global_load_lds(wbase + w_off[jj] + stage * kESlice, (lds_ptr)(dw + 1024 * j),
+                                       16, 0, 0);
+      __builtin_amdgcn_global_load_lds(cbase + s_row[l_row[jj]] + stage * kESlice + l_chunk[jj],
+                                       (lds_ptr)(dl + 1024 * j), 16, 0, 0);
+    }
+  };
+
+  // wave tile: outputs 64 wn .. + 63, keys 64 wg .. + 63 (2 x 2 MFMA tiles)
+  const int wn = wave & 1, wg = wave >> 1;
+  const int c32 = lane & 31, kh = lane >> 5;
+  f32x16_t acc[2][2];
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+    for (int gi = 0; gi < 2; ++gi)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[mi][gi][i] = 0.0f;
+
+  constexpr int kStages = kR / kEK;   // 8
+  gload(0, 0);
+  for (int st = 0; st < kStages; ++st) {
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // this wave's loads of stage st have landed
+    __syncthreads();                      // everyone's; and everyone is done with stage st - 1
+    if (st + 1 < kStages) gload(st + 1, (st + 1) & 1);
+    const char* tw = smem + (st & 1) * kEStage;
+    const char* tl = tw + kETile;
+#pragma unroll
+    for (int kk = 0; kk < kEK / 16; ++kk) {
+      const int c = 2 * kk + kh;
+      u32x4_t af[2], bf[2];
+#pragma unroll
+      for (int mi = 0; mi < 2; ++mi) {
+        const int r = 64 * wn + 32 * mi + c32;
+        af[mi] = *reinterpret_cast<const u32x4_t*>(tw + r * kESlice + 16 * eslot(r, c));
+      }
+#pragma unroll
+      for (int gi = 0; gi < 2; ++gi) {
+        const int r = 64 * wg + 32 * gi + c32;
+        bf[gi] = *reinterpret_cast<const u32x4_t*>(tl + r * kESlice + 16 * eslot(r, c));
+      }
+#pragma unroll
+      for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+        for (int gi = 0; gi < 2; ++gi)
+          acc[mi][gi] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(af[mi]), as_bf16x8(bf[gi]),
+                                                               acc[mi][gi], 0, 0, 0);
+    }
+  }
+
+  // E^T tile (mi, gi): lane l holds key g = .. + l % 32 and outputs
+  // n = .. + 8 (i / 4) + 4 (l / 32) + i % 4: four consecutive outputs per store
+  const int64_t krow = int64_t(H) * kDq, vrow = int64_t(H) * kDv;   // elements per expanded row
+#pragma unroll
+  for (int gi = 0; gi < 2; ++gi) {
+    const int g = g0 + 64 * wg + 32 * gi + c32;
+    if (g >= total) continue;
+    uint16_t* dst = half == 0
+                        ? static_cast<uint16_t*>(a.k_exp) + int64_t(g) * krow + int64_t(h) * kDq
+                        : static_cast<uint16_t*>(a.v_exp) + int64_t(g) * vrow + int64_t(h) * kDv;
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int n = 64 * wn + 32 * mi + 8 * q4 + 4 * kh;   // within the 128 outputs
+        uint2 v;
+        v.x = pack_bf16x2(acc[mi][gi][4 * q4 + 0], acc[mi][gi][4 * q4 + 1]);
+        v.y = pack_bf16x2(acc[mi][gi][4 * q4 + 2], acc[mi][gi][4 * q4 + 3]);
+        *reinterpret_cast<uint2*>(dst + n) = v;
+      }
+  }
+  // the key half also places k_pe after the head's 128 expanded dims
+  if (half == 0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int q = tid + 256 * i;          // 128 rows x 8 chunks of 16 B
+      const int row = q >> 3, part = q & 7;
+      const int g = g0 + row;
+      if (g >= total) continue;
+      const u32x4_t v = load16(cbase + s_row[row] + kR * 2 + 16 * part);
+      store16(static_cast<uint16_t*>(a.k_exp) + int64_t(g) * krow + int64_t(h) * kDq + kDn + 8 * part, v);
+    }
+  }
+}
+
+// ------------------------------------------------------------- attention
+constexpr int kBM = 128;                      // query rows per work-group
+constexpr int kBN = 64;                       // keys per tile
+constexpr int kNRow = kDn * 2;                // 256 B: key-nope and value rows
+constexpr int kPRow = kP * 2;                 // 128 B: rope rows
+constexpr int kNTile = kBN * kNRow;           // 16 KiB
+constexpr int kPTile = kBN * kPRow;           // 8 KiB
+constexpr int kAStage = 2 * kNTile + kPTile;  // K nope, V, K rope: 40 KiB
+constexpr float kSlack = 8.0f;
+// 256-byte rows: chunk c of row r in slot c ^ swz(r) (16 slots, as in the
+// varlen prefill kernel: conflict-free K-fragment and V^T reads); 128-byte
+// rope rows: slot c ^ ((r >> 1) & 7).
+__device__ __forceinline__ int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+__device__ __forceinline__ int pslot(int r, int c) { return c ^ ((r >> 1) & 7); }
+
+__global__ __launch_bounds__(256, 2) void mla_attn_kernel(MlaPrefill a) {
+  __shared__ __align__(16) char smem[2 * kAStage];
+  const int lane = threadIdx.x & 63;
+  const int wave = wave_id();
+  const int H = a.num_heads;
+  // work-group -> (request, head, q tile): the q tiles of one (request, head)
+  // pair run on one XCD, longest first
+  const int n_qt = (a.max_query_len + kBM - 1) / kBM;
+  const int id = blockIdx.x;
+  const int xcd = id % kXcds, slot = id / kXcds;
+  const int pair = (slot / n_qt) * kXcds + xcd;
+  if (pair >= a.num_seqs * H) return;
+  const int r = pair / H, h = pair % H;
+  const int qt = n_qt - 1 - slot % n_qt;
+  const int q_start = min(max(a.query_start_loc[r], 0), a.num_tokens);
+  const int L = min(min(a.query_start_loc[r + 1] - q_start, a.max_query_len), a.num_tokens - q_start);
+  // key rows of the request in the expanded buffers (clamped to the rows the
+  // expansion wrote)
+  const int ks = min(a.key_start[r], a.total_keys);
+  const int S = min(a.key_start[r + 1], a.total_keys) - ks;
+  const int q0 = qt * kBM;
+  if (q0 >= L || L <= 0) return;
+  const int C = S - L;
+  const int kv_end = min(S, max(0, C + min(q0 + kBM, L)));
+  const int n_tiles = (kv_end + kBN - 1) / kBN;
+
+  // ---- Q fragments: nope dims 16 kk + 8 (l / 32), rope dims likewise
+  const int my_row = q0 + wave * 32 + (lane & 31);
+  const bool row_ok = my_row < L;
+  u32x4_t qf[8], qr[4];
+  {
+    const uint16_t* qp = static_cast<const uint16_t*>(a.q) +
+                         int64_t(q_start + (row_ok ? my_row : 0)) * a.q_st + int64_t(h) * a.q_sh +
+                         8 * (lane >> 5);
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) qf[kk] = row_ok ? load16(qp + 16 * kk) : u32x4_t{0, 0, 0, 0};
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) qr[kk] = row_ok ? load16(qp + kDn + 16 * kk) : u32x4_t{0, 0, 0, 0};
+  }
+
+  // ---- gather of one tile (keys of the request are contiguous rows)
+  const char* kbase = static_cast<const char*>(a.k_exp) + (int64_t(ks) * H + h) * (kDq * 2);
+  const char* vbase = static_cast<const char*>(a.v_exp) + (int64_t(ks) * H + h) * (kDv * 2);
+  const int64_t kstride = int64_t(H) * kDq * 2, vstride = int64_t(H) * kDv * 2;
+  typedef __attribute__((address_space(3))) void* lds_ptr;
+  auto gload = [&](int tile, char* dst) {
+    char* dk = dst;
+    char* dv = dst + kNTile;
+    char* dp = dst + 2 * kNTile;
+    const int key0 = tile * kBN;
+    // nope and value rows: 16 loads of 4 rows x 256 B (wave w: w + 4 jj)
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const int j = wave + 4 * jj;
+      const int row = 4 * j + (lane >> 4);
+      const int key = min(key0 + row, kv_end - 1);   // past the end: re-read the last key
+      const int c = (lane & 15) ^ swz(row);
+      __builtin_amdgcn_global_load_lds(kbase + key * kstride + 16 * c, (lds_ptr)(dk + 1024 * j), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(vbase + key * vstride + 16 * c, (lds_ptr)(dv + 1024 * j), 16, 0, 0);
+    }
+    // rope rows: 8 loads of 8 rows x 128 B (wave w: w + 4 jj)
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) {
+      const int j = wave + 4 * jj;
+      const int row = 8 * j + (lane >> 3);
+      const int key = min(key0 + row, kv_end - 1);
+      const int c = pslot(row, lane & 7);
+      __builtin_amdgcn_global_load_lds(kbase + key * kstride + kNRow + 16 * c,
+                                       (lds_ptr)(dp + 1024 * j), 16, 0, 0);
+    }
+  };
+  auto gwait = [&]() { __builtin_amdgcn_s_waitcnt(0x0F70); };
+
+  const float scale2 = fmaxf(a.scale * kLog2e, 0x1p-126f);
+  float m_run = kNoMax, l_run = 0.0f;
+  f32x16_t acc[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[dt][i] = 0.0f;
+
+  if (n_tiles > 0) {
+    gload(0, smem);
+    gwait();
+  }
+  __syncthreads();
+  const int row_abs = C + my_row;
+  for (int t = 0; t < n_tiles; ++t) {
+    const int buf = t & 1;
+    if (t + 1 < n_tiles) gload(t + 1, smem + (buf ^ 1) * kAStage);
+    const char* kt = smem + buf * kAStage;
+    const char* vt = kt + kNTile;
+    const char* pt = kt + 2 * kNTile;
+    const int key0 = t * kBN;
+
+    // S^T for two 32-key halves: 8 k-steps over the nope tile, 4 over rope
+    f32x16_t s[2];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) s[hh][i] = 0.0f;
+    {
+      const int kr = lane & 31;
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk) {
+        const int c = 2 * kk + (lane >> 5);
+        const u32x4_t k0 = *reinterpret_cast<const u32x4_t*>(kt + kr * kNRow + 16 * (c ^ swz(kr)));
+        const u32x4_t k1 = *reinterpret_cast<const u32x4_t*>(kt + (kr + 32) * kNRow + 16 * (c ^ swz(kr + 32)));
+        s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(k0), as_bf16x8(qf[kk]), s[0], 0, 0, 0);
+        s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(k1), as_bf16x8(qf[kk]), s[1], 0, 0, 0);
+      }
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const int c = 2 * kk + (lane >> 5);
+        const u32x4_t k0 = *reinterpret_cast<const u32x4_t*>(pt + kr * kPRow + 16 * pslot(kr, c));
+        const u32x4_t k1 = *reinterpret_cast<const u32x4_t*>(pt + (kr + 32) * kPRow + 16 * pslot(kr + 32, c));
+        s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(k0), as_bf16x8(qr[kk]), s[0], 0, 0, 0);
+        s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(k1), as_bf16x8(qr[kk]), s[1], 0, 0, 0);
+      }
+    }
+
+    // online softmax (lazy rescale as in the varlen prefill kernel)
+    const bool need_mask = (key0 + kBN > kv_end) || (key0 + kBN - 1 > C + q0 + wave * 32);
+    u32x4_t pf[4];
+    float psum = 0.0f, alpha = 1.0f;
+    bool rescale = false;
+    auto update = [&](auto masked_tag) {
+      constexpr bool kMasked = decltype(masked_tag)::value;
+      if constexpr (kMasked) {
+        const int lim = min(kv_end - 1, row_abs) - key0 - 4 * (lane >> 5);
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int c = hh * 32 + 8 * (i >> 2) + (i & 3);
+            s[hh][i] = c <= lim ? s[hh][i] : -INFINITY;
+          }
+      }
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, s[hh][i]);
+      tmax = xor32_max(tmax);
+      const float tm = tmax == -INFINITY ? -INFINITY : tmax * scale2;
+      if (__any(tm > m_run + kSlack)) {
+        const float m_new = fmaxf(m_run, tm);
+        alpha = fast_exp2(m_run - m_new);
+        rescale = true;
+        m_run = m_new;
+        l_run *= alpha;
+      }
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+          float p[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const float x = s[hh][8 * st + j];
+            const float e = fast_exp2(fmaf(x, scale2, -m_run));
+            p[j] = kMasked ? (x == -INFINITY ? 0.0f : e) : e;
+            psum += p[j];
+          }
+          pf[2 * hh + st] = u32x4_t{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
+                                    pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])};
+        }
+      l_run += psum;
+    };
+    if (need_mask) update(std::true_type{});
+    else update(std::false_type{});
+    if (rescale) {
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[dt][i] *= alpha;
+    }
+
+    // O^T += V^T P^T (transposing LDS reads of the value tile)
+    const int grp = lane >> 4, gi = lane & 15, kg = lane >> 5;
+    const int c0 = 2 * (grp & 1) + ((gi & 3) >> 1);
+    const int vr0 = 4 * kg + (gi >> 2);
+#pragma unroll
+    for (int ks4 = 0; ks4 < 4; ++ks4)
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) {
+        const int ra = 16 * ks4 + vr0, rb = ra + 8;
+        const uint2 v1 = lds_read_tr(vt + ra * kNRow + 16 * ((4 * dt + c0) ^ swz(ra)) + 8 * (gi & 1));
+        const uint2 v2 = lds_read_tr(vt + rb * kNRow + 16 * ((4 * dt + c0) ^ swz(rb)) + 8 * (gi & 1));
+        const u32x4_t vf = u32x4_t{v1.x, v1.y, v2.x, v2.y};
+        acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vf), as_bf16x8(pf[ks4]), acc[dt], 0, 0, 0);
+      }
+
+    if (t + 1 < n_tiles) {
+      gwait();
+      __syncthreads();
+    }
+  }
+
+  const float l_tot = xor32_sum(l_run);
+  if (!row_ok) return;
+  const int64_t orow = int64_t(q_start) + my_row;
+  const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+  uint16_t* op = static_cast<uint16_t*>(a.out) + (orow * H + h) * kDv;
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int d = 32 * dt + 8 * q4 + 4 * (lane >> 5);
+      uint2 w;
+      w.x = pack_bf16x2(acc[dt][4 * q4 + 0] * inv, acc[dt][4 * q4 + 1] * inv);
+      w.y = pack_bf16x2(acc[dt][4 * q4 + 2] * inv, acc[dt][4 * q4 + 3] * inv);
+      *reinterpret_cast<uint2*>(op + d) = w;
+    }
+  if (a.lse && lane < 32)
+    a.lse[orow * H + h] = l_tot > 0.0f ? (m_run + fast_log2(l_tot)) * kLn2 : -INFINITY;
+}
+
+}  // namespace
+
+hipError_t launch_mla_prefill(const MlaPrefill& a, hipStream_t s) {
+  if (a.num_seqs <= 0 || a.num_tokens <= 0) return hipSuccess;
+  hipLaunchKernelGGL(key_start_kernel, dim3(1), dim3(256), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (a.total_keys > 0) {
+    const int64_t g_tiles = (int64_t(a.total_keys) + kEN - 1) / kEN;
+    const int64_t wgs = (g_tiles + kXcds - 1) / kXcds * kXcds * (2 * int64_t(a.num_heads));
+    if (wgs > INT32_MAX) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(mla_expand_kernel, dim3(unsigned(wgs)), dim3(256), 0, s, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (a.max_query_len <= 0) return hipSuccess;
+  const int64_t n_qt = (a.max_query_len + kBM - 1) / kBM;
+  const int64_t pairs = int64_t(a.num_seqs) * a.num_heads;
+  const int64_t wgs = (pairs + kXcds - 1) / kXcds * kXcds * n_qt;
+  if (wgs > INT32_MAX) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(mla_attn_kernel, dim3(unsigned(wgs)), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace pa

@@ -324,6 +324,109 @@ def make_mla(seed: int, seq_lens, num_heads: int = 128, kv_lora_rank: int = 512,
                     poison_block=poison, meta=meta)
 
 
+@dataclass
+class MlaPrefillBatch:
+    """Inputs of one MLA prefill call (multi-head form).
+
+    q [T, H, 192] (q_nope 128 | q_pe 64); kv_c_new [T, 512], k_pe_new [T, 64];
+    cache [nb, bs, 576] latent rows (prior context only); w_kv_b [H * 256, 512]
+    (per head: 128 key rows, 128 value rows); block_table [N, max_blocks];
+    slot_mapping [T]; query_start_loc [N + 1]; seq_lens [N].  bf16.
+    """
+    name: str
+    q: np.ndarray
+    kv_c_new: np.ndarray
+    k_pe_new: np.ndarray
+    cache: np.ndarray
+    w_kv_b: np.ndarray
+    block_table: np.ndarray
+    slot_mapping: np.ndarray
+    query_start_loc: np.ndarray
+    seq_lens: np.ndarray
+    scale: float
+    block_size: int
+    poison_block: int
+    meta: dict = field(default_factory=dict)
+
+    @property
+    def num_seqs(self): return len(self.seq_lens)
+    @property
+    def num_tokens(self): return self.q.shape[0]
+    @property
+    def num_heads(self): return self.q.shape[1]
+    @property
+    def q_lens(self): return np.diff(self.query_start_loc)
+    @property
+    def max_query_len(self): return int(self.q_lens.max()) if len(self.seq_lens) else 0
+    @property
+    def total_keys(self): return int(self.seq_lens.astype(np.int64).sum())
+
+
+def make_mla_prefill(seed, q_lens, seq_lens, num_heads: int = 16, block_size: int = 64,
+                     scale: float | None = None, name: str = "mla_prefill") -> MlaPrefillBatch:
+    """An MLA prefill batch: request r has seq_lens[r] keys, the last q_lens[r]
+    new (their latent rows written by the call).  Latent rows, queries and new
+    rows are bf16 N(0,1); kv_b_proj's weight is bf16 N(0,1) / 16 (a power of
+    two, so the scaling is exact), which gives projected keys and values of
+    variance 2.  Scale 1/sqrt(192) by default."""
+    rng = seed if isinstance(seed, np.random.Generator) else np.random.default_rng(seed)
+    q_lens = np.asarray(q_lens, dtype=np.int64)
+    seq_lens = np.asarray(seq_lens, dtype=np.int64)
+    if np.any(q_lens > seq_lens) or np.any(q_lens < 0):
+        raise ValueError("need 0 <= q_len <= seq_len")
+    table, poison, nb, owned = _allocate_tables(rng, seq_lens, block_size)
+    T = int(q_lens.sum())
+    qsl = np.zeros(len(seq_lens) + 1, dtype=np.int32)
+    qsl[1:] = np.cumsum(q_lens)
+    q = _normal(rng, (T, num_heads, 192), BF16)
+    kv_c = _normal(rng, (T, 512), BF16)
+    k_pe = _normal(rng, (T, 64), BF16)
+    w = _normal(rng, (num_heads * 256, 512), BF16)
+    w = f32_to_bf16_bits(bf16_bits_to_f32(w) / 16.0)
+    valid = np.zeros((nb, block_size), dtype=bool)
+    slots = np.empty(T, dtype=np.int64)
+    for r in range(len(seq_lens)):
+        S, L = int(seq_lens[r]), int(q_lens[r])
+        pos = np.arange(S)
+        blk = table[r, pos // block_size].astype(np.int64)
+        off = pos % block_size
+        valid[blk[:S - L], off[:S - L]] = True
+        slots[qsl[r]:qsl[r + 1]] = blk[S - L:] * block_size + off[S - L:]
+    cache = _fill_pool(rng, (nb, block_size, 576), BF16)
+    cache[~valid] = NAN_BF16
+    if scale is None:
+        scale = 1.0 / math.sqrt(192.0)
+    return MlaPrefillBatch(name=name, q=q, kv_c_new=kv_c, k_pe_new=k_pe, cache=cache, w_kv_b=w,
+                           block_table=table, slot_mapping=slots, query_start_loc=qsl,
+                           seq_lens=seq_lens.astype(np.int32), scale=float(scale),
+                           block_size=block_size, poison_block=poison)
+
+
+MLA_PREFILL = "mla_prefill_bf16"
+
+
+def mla_prefill_batch(seed: int = 1010, batch: int = 4, num_heads: int = 16) -> MlaPrefillBatch:
+    """4 requests, chunk ~ U{256..2048} new queries over context ~ U{0..4096},
+    16 heads (one GPU's share of 128 heads split over 8), kv_lora_rank 512 +
+    rope 64 latent rows, qk 192 / v 128 per head, block 64, bf16, causal."""
+    rng = np.random.default_rng(seed)
+    L = rng.integers(256, 2048, size=batch, endpoint=True)
+    C = rng.integers(0, 4096, size=batch, endpoint=True)
+    return make_mla_prefill(rng, L, C + L, num_heads, 64, name=MLA_PREFILL)
+
+
+def mla_prefill_flops(b: MlaPrefillBatch) -> dict:
+    """Projection: 2 x 512 x 256 per key and head; attention: 2 x (192 + 128)
+    per visible (query, key) pair and head."""
+    proj = 2 * 512 * 256 * b.num_heads * b.total_keys
+    pairs = 0
+    for L, S in zip(b.q_lens, b.seq_lens):
+        L, S = int(L), int(S)
+        pairs += L * (S - L) + L * (L + 1) // 2
+    attn = 2 * (192 + 128) * b.num_heads * pairs
+    return {"projection": proj, "attention": attn, "total": proj + attn}
+
+
 # --------------------------------------------------------------------------
 # the five named workloads
 # --------------------------------------------------------------------------
