@@ -117,15 +117,15 @@ __global__ __launch_bounds__(256, 2) void mla_expand_kernel(MlaPrefill a) {
   // DMA: 16 wave-wide loads per operand and stage (8 rows x 128 B each); wave
   // w issues loads w, w + 4, w + 8, w + 12 of both.  Lane i of load j: row
   // 8 j + i / 8, slot i % 8, which holds chunk eslot(row, slot).
-  uint32_t w_off[4], l_row[4], l_chunk[4];
+  uint32_t w_off[4];
+  const char* l_src[4];   // this lane's latent bytes of each of its loads (stage 0)
 #pragma unroll
   for (int jj = 0; jj < 4; ++jj) {
     const int j = wave + 4 * jj;
     const int row = 8 * j + (lane >> 3);
     const int c = eslot(row, lane & 7);
     w_off[jj] = uint32_t(row * (kR * 2) + 16 * c);
-    l_row[jj] = uint32_t(row);
-    l_chunk[jj] = uint32_t(16 * c);
+    l_src[jj] = cbase + s_row[row] + 16 * c;
   }
   typedef __attribute__((address_space(3))) void* lds_ptr;
   auto gload = [&](int stage, int buf) {
@@ -136,8 +136,7 @@ __global__ __launch_bounds__(256, 2) void mla_expand_kernel(MlaPrefill a) {
       const int j = wave + 4 * jj;
       __builtin_amdgcn_global_load_lds(wbase + w_off[jj] + stage * kESlice, (lds_ptr)(dw + 1024 * j),
                                        16, 0, 0);
-      __builtin_amdgcn_global_load_lds(cbase + s_row[l_row[jj]] + stage * kESlice + l_chunk[jj],
-                                       (lds_ptr)(dl + 1024 * j), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(l_src[jj] + stage * kESlice, (lds_ptr)(dl + 1024 * j), 16, 0, 0);
     }
   };
 
@@ -152,36 +151,57 @@ __global__ __launch_bounds__(256, 2) void mla_expand_kernel(MlaPrefill a) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[mi][gi][i] = 0.0f;
 
+  // LDS operand addresses of k-step kk (buffer 0): rows 64 wn + 32 mi + c32 of
+  // the W tile and 64 wg + 32 gi + c32 of the latent tile, chunk 2 kk + kh.
+  // The reads are inline assembly with explicit waits: the compiler cannot
+  // tell them apart from the DMA filling the other buffer and would wait for
+  // those loads first.
+  uint32_t ra[4][2], rb[4][2];
+  {
+    const uint32_t base = lds_addr(smem);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+      for (int x = 0; x < 2; ++x) {
+        const int r1 = 64 * wn + 32 * x + c32, r2 = 64 * wg + 32 * x + c32;
+        ra[kk][x] = base + uint32_t(r1 * kESlice + 16 * eslot(r1, 2 * kk + kh));
+        rb[kk][x] = base + uint32_t(kETile + r2 * kESlice + 16 * eslot(r2, 2 * kk + kh));
+      }
+  }
   constexpr int kStages = kR / kEK;   // 8
   gload(0, 0);
-  for (int st = 0; st < kStages; ++st) {
+  static_for<kStages>([&](auto sc) {
+    constexpr int st = decltype(sc)::value;
+    constexpr int kOff = (st & 1) * kEStage;
     __builtin_amdgcn_s_waitcnt(0x0F70);   // this wave's loads of stage st have landed
-    __syncthreads();                      // everyone's; and everyone is done with stage st - 1
-    if (st + 1 < kStages) gload(st + 1, (st + 1) & 1);
-    const char* tw = smem + (st & 1) * kEStage;
-    const char* tl = tw + kETile;
+    __builtin_amdgcn_s_barrier();         // everyone's; and everyone is done with stage st - 1
+    if constexpr (st + 1 < kStages) gload(st + 1, (st + 1) & 1);
+    u32x4_t af[2][2], bf[2][2];           // [k-step parity][x]
+    auto issue = [&](auto kc) {
+      constexpr int kk = decltype(kc)::value;
 #pragma unroll
-    for (int kk = 0; kk < kEK / 16; ++kk) {
-      const int c = 2 * kk + kh;
-      u32x4_t af[2], bf[2];
-#pragma unroll
-      for (int mi = 0; mi < 2; ++mi) {
-        const int r = 64 * wn + 32 * mi + c32;
-        af[mi] = *reinterpret_cast<const u32x4_t*>(tw + r * kESlice + 16 * eslot(r, c));
+      for (int x = 0; x < 2; ++x) {
+        af[kk & 1][x] = lds_read16_at<kOff>(ra[kk][x]);
+        bf[kk & 1][x] = lds_read16_at<kOff>(rb[kk][x]);
       }
-#pragma unroll
-      for (int gi = 0; gi < 2; ++gi) {
-        const int r = 64 * wg + 32 * gi + c32;
-        bf[gi] = *reinterpret_cast<const u32x4_t*>(tl + r * kESlice + 16 * eslot(r, c));
+    };
+    issue(std::integral_constant<int, 0>{});
+    static_for<4>([&](auto kc) {
+      constexpr int kk = decltype(kc)::value;
+      if constexpr (kk + 1 < 4) {
+        issue(std::integral_constant<int, kk + 1>{});
+        lds_wait<4>(af[kk & 1][0], af[kk & 1][1], bf[kk & 1][0], bf[kk & 1][1]);
+      } else {
+        lds_wait<0>(af[kk & 1][0], af[kk & 1][1], bf[kk & 1][0], bf[kk & 1][1]);
       }
 #pragma unroll
       for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
         for (int gi = 0; gi < 2; ++gi)
-          acc[mi][gi] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(af[mi]), as_bf16x8(bf[gi]),
-                                                               acc[mi][gi], 0, 0, 0);
-    }
-  }
+          acc[mi][gi] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              as_bf16x8(af[kk & 1][mi]), as_bf16x8(bf[kk & 1][gi]), acc[mi][gi], 0, 0, 0);
+    });
+  });
 
   // E^T tile (mi, gi): lane l holds key g = .. + l % 32 and outputs
   // n = .. + 8 (i / 4) + 4 (l / 32) + i % 4: four consecutive outputs per store
@@ -335,23 +355,36 @@ __global__ __launch_bounds__(256, 2) void mla_attn_kernel(MlaPrefill a) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) s[hh][i] = 0.0f;
     {
-      const int kr = lane & 31;
-#pragma unroll
-      for (int kk = 0; kk < 8; ++kk) {
-        const int c = 2 * kk + (lane >> 5);
-        const u32x4_t k0 = *reinterpret_cast<const u32x4_t*>(kt + kr * kNRow + 16 * (c ^ swz(kr)));
-        const u32x4_t k1 = *reinterpret_cast<const u32x4_t*>(kt + (kr + 32) * kNRow + 16 * (c ^ swz(kr + 32)));
-        s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(k0), as_bf16x8(qf[kk]), s[0], 0, 0, 0);
-        s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(k1), as_bf16x8(qf[kk]), s[1], 0, 0, 0);
-      }
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const int c = 2 * kk + (lane >> 5);
-        const u32x4_t k0 = *reinterpret_cast<const u32x4_t*>(pt + kr * kPRow + 16 * pslot(kr, c));
-        const u32x4_t k1 = *reinterpret_cast<const u32x4_t*>(pt + (kr + 32) * kPRow + 16 * pslot(kr + 32, c));
-        s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(k0), as_bf16x8(qr[kk]), s[0], 0, 0, 0);
-        s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(k1), as_bf16x8(qr[kk]), s[1], 0, 0, 0);
-      }
+      // 12 k-steps (8 over the nope tile, 4 over rope), the two 32-key halves
+      // a constant offset apart; reads one step ahead of the MFMAs, issued as
+      // inline assembly (see the expansion) and waited for explicitly
+      const int kr = lane & 31, hi = lane >> 5;
+      u32x4_t kf[2][2];
+      auto issue = [&](auto kc) {
+        constexpr int kk = decltype(kc)::value;
+        if constexpr (kk < 8) {
+          const char* p = kt + kr * kNRow + 16 * ((2 * kk + hi) ^ swz(kr));
+          kf[kk & 1][0] = lds_read16_issue<0>(p);
+          kf[kk & 1][1] = lds_read16_issue<32 * kNRow>(p);
+        } else {
+          const char* p = pt + kr * kPRow + 16 * pslot(kr, 2 * (kk - 8) + hi);
+          kf[kk & 1][0] = lds_read16_issue<0>(p);
+          kf[kk & 1][1] = lds_read16_issue<32 * kPRow>(p);
+        }
+      };
+      issue(std::integral_constant<int, 0>{});
+      static_for<12>([&](auto kc) {
+        constexpr int kk = decltype(kc)::value;
+        if constexpr (kk + 1 < 12) {
+          issue(std::integral_constant<int, kk + 1>{});
+          lds_wait<2>(kf[kk & 1][0], kf[kk & 1][1]);
+        } else {
+          lds_wait<0>(kf[kk & 1][0], kf[kk & 1][1]);
+        }
+        const u32x4_t& qk = kk < 8 ? qf[kk < 8 ? kk : 0] : qr[kk < 8 ? 0 : kk - 8];
+        s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kf[kk & 1][0]), as_bf16x8(qk), s[0], 0, 0, 0);
+        s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kf[kk & 1][1]), as_bf16x8(qk), s[1], 0, 0, 0);
+      });
     }
 
     // online softmax (lazy rescale as in the varlen prefill kernel)
@@ -415,20 +448,36 @@ __global__ __launch_bounds__(256, 2) void mla_attn_kernel(MlaPrefill a) {
     const int grp = lane >> 4, gi = lane & 15, kg = lane >> 5;
     const int c0 = 2 * (grp & 1) + ((gi & 3) >> 1);
     const int vr0 = 4 * kg + (gi >> 2);
+    const char* vb[2][4];   // key rows vr0 (+ 8), d-tile dt; 16 ks rows further is a constant
 #pragma unroll
-    for (int ks4 = 0; ks4 < 4; ++ks4)
+    for (int e = 0; e < 2; ++e)
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt) {
-        const int ra = 16 * ks4 + vr0, rb = ra + 8;
-        const uint2 v1 = lds_read_tr(vt + ra * kNRow + 16 * ((4 * dt + c0) ^ swz(ra)) + 8 * (gi & 1));
-        const uint2 v2 = lds_read_tr(vt + rb * kNRow + 16 * ((4 * dt + c0) ^ swz(rb)) + 8 * (gi & 1));
-        const u32x4_t vf = u32x4_t{v1.x, v1.y, v2.x, v2.y};
-        acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vf), as_bf16x8(pf[ks4]), acc[dt], 0, 0, 0);
+      for (int dt = 0; dt < 4; ++dt)
+        vb[e][dt] = vt + (vr0 + 8 * e) * kNRow + 16 * ((4 * dt + c0) ^ swz(vr0 + 8 * e)) + 8 * (gi & 1);
+    u32x2_t vr[2][2];
+    auto vissue = [&](auto ic) {
+      constexpr int i = decltype(ic)::value, ks4 = i / 4, dt = i % 4;
+      vr[i & 1][0] = lds_read_tr_issue<16 * ks4 * kNRow>(vb[0][dt]);
+      vr[i & 1][1] = lds_read_tr_issue<16 * ks4 * kNRow>(vb[1][dt]);
+    };
+    vissue(std::integral_constant<int, 0>{});
+    static_for<16>([&](auto ic) {
+      constexpr int i = decltype(ic)::value, ks4 = i / 4, dt = i % 4;
+      if constexpr (i + 1 < 16) {
+        vissue(std::integral_constant<int, i + 1>{});
+        lds_wait<2>(vr[i & 1][0], vr[i & 1][1]);
+      } else {
+        lds_wait<0>(vr[i & 1][0], vr[i & 1][1]);
       }
+      const u32x4_t vf = u32x4_t{vr[i & 1][0].x, vr[i & 1][0].y, vr[i & 1][1].x, vr[i & 1][1].y};
+      acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vf), as_bf16x8(pf[ks4]), acc[dt], 0, 0, 0);
+    });
 
     if (t + 1 < n_tiles) {
+      // this wave's loads of tile t + 1 have landed; after the barrier
+      // everyone's have, and everyone is done reading this tile's buffer
       gwait();
-      __syncthreads();
+      __builtin_amdgcn_s_barrier();
     }
   }
 

@@ -196,6 +196,10 @@ template <int kLeft>
 __device__ __forceinline__ void lds_wait(u32x4_t& a, u32x4_t& b) {
   asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(a), "+v"(b) : "n"(kLeft));
 }
+template <int kLeft>
+__device__ __forceinline__ void lds_wait(u32x4_t& a, u32x4_t& b, u32x4_t& c, u32x4_t& d) {
+  asm volatile("s_waitcnt lgkmcnt(%4)" : "+v"(a), "+v"(b), "+v"(c), "+v"(d) : "n"(kLeft));
+}
 
 // x combined with the value of lane l ^ 32, on the VALU (v_permlane32_swap):
 // returns {x[l], x[l ^ 32]} in some order, which is all a symmetric reduction
