@@ -69,17 +69,19 @@ __global__ __launch_bounds__(256) void key_start_kernel(MlaPrefill a) {
 // ------------------------------------------------------------- expansion
 constexpr int kEM = 128;                     // projection outputs per work-group
 constexpr int kEN = 128;                     // keys per work-group
-constexpr int kEK = 64;                      // k per stage
-constexpr int kESlice = kEK * 2;             // 128 B of a row per stage
-constexpr int kETile = kEM * kESlice;        // 16 KiB (either operand)
+constexpr int kEK = 32;                      // k per stage
+constexpr int kESlice = kEK * 2;             // 64 B of a row per stage
+constexpr int kETile = kEM * kESlice;        // 8 KiB (either operand)
 constexpr int kEStage = 2 * kETile;          // W tile, then latent tile
-// 16-byte chunk c of row r of a staged slice sits in slot c ^ ((r >> 1) & 7):
-// rows are 128 B, so a 16-lane phase reading one chunk of 16 consecutive rows
-// hits 16 distinct 16-byte bank groups.
-__device__ __forceinline__ int eslot(int r, int c) { return c ^ ((r >> 1) & 7); }
+constexpr int kERing = 4;                    // stages in LDS: three in flight
+constexpr int kESteps = kR / kEK;            // 16 stages over kv_lora_rank
+// 16-byte chunk c (0..3) of row r of a staged slice sits in slot
+// c ^ ((r >> 2) & 3): rows are 64 B, so a 16-lane phase reading one chunk of
+// 16 consecutive rows hits 16 distinct 16-byte bank groups.
+__device__ __forceinline__ int eslot(int r, int c) { return c ^ ((r >> 2) & 3); }
 
 __global__ __launch_bounds__(256, 2) void mla_expand_kernel(MlaPrefill a) {
-  __shared__ __align__(16) char smem[2 * kEStage];
+  __shared__ __align__(16) char smem[kERing * kEStage];
   __shared__ uint64_t s_row[kEN];             // byte offset of each key's latent row
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int H = a.num_heads;
@@ -114,25 +116,25 @@ __global__ __launch_bounds__(256, 2) void mla_expand_kernel(MlaPrefill a) {
 
   const char* wbase = static_cast<const char*>(a.w) + int64_t(n_tile) * kEM * (kR * 2);
   const char* cbase = static_cast<const char*>(a.cache);
-  // DMA: 16 wave-wide loads per operand and stage (8 rows x 128 B each); wave
-  // w issues loads w, w + 4, w + 8, w + 12 of both.  Lane i of load j: row
-  // 8 j + i / 8, slot i % 8, which holds chunk eslot(row, slot).
-  uint32_t w_off[4];
-  const char* l_src[4];   // this lane's latent bytes of each of its loads (stage 0)
+  // DMA: 8 wave-wide loads per operand and stage (16 rows x 64 B each); wave
+  // w issues loads w and w + 4 of both.  Lane i of load j: row 16 j + i / 4,
+  // slot i % 4, which holds chunk eslot(row, slot).
+  uint32_t w_off[2];
+  const char* l_src[2];   // this lane's latent bytes of each of its loads (stage 0)
 #pragma unroll
-  for (int jj = 0; jj < 4; ++jj) {
+  for (int jj = 0; jj < 2; ++jj) {
     const int j = wave + 4 * jj;
-    const int row = 8 * j + (lane >> 3);
-    const int c = eslot(row, lane & 7);
+    const int row = 16 * j + (lane >> 2);
+    const int c = eslot(row, lane & 3);
     w_off[jj] = uint32_t(row * (kR * 2) + 16 * c);
     l_src[jj] = cbase + s_row[row] + 16 * c;
   }
   typedef __attribute__((address_space(3))) void* lds_ptr;
-  auto gload = [&](int stage, int buf) {
-    char* dw = smem + buf * kEStage;
+  auto gload = [&](int stage) {
+    char* dw = smem + (stage % kERing) * kEStage;
     char* dl = dw + kETile;
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
+    for (int jj = 0; jj < 2; ++jj) {
       const int j = wave + 4 * jj;
       __builtin_amdgcn_global_load_lds(wbase + w_off[jj] + stage * kESlice, (lds_ptr)(dw + 1024 * j),
                                        16, 0, 0);
@@ -151,16 +153,16 @@ __global__ __launch_bounds__(256, 2) void mla_expand_kernel(MlaPrefill a) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[mi][gi][i] = 0.0f;
 
-  // LDS operand addresses of k-step kk (buffer 0): rows 64 wn + 32 mi + c32 of
-  // the W tile and 64 wg + 32 gi + c32 of the latent tile, chunk 2 kk + kh.
+  // LDS operand addresses of k-step kk (ring slot 0): rows 64 wn + 32 x + c32
+  // of the W tile and 64 wg + 32 x + c32 of the latent tile, chunk 2 kk + kh.
   // The reads are inline assembly with explicit waits: the compiler cannot
-  // tell them apart from the DMA filling the other buffer and would wait for
+  // tell them apart from the DMA filling the other slots and would wait for
   // those loads first.
-  uint32_t ra[4][2], rb[4][2];
+  uint32_t ra[2][2], rb[2][2];
   {
     const uint32_t base = lds_addr(smem);
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
+    for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
       for (int x = 0; x < 2; ++x) {
         const int r1 = 64 * wn + 32 * x + c32, r2 = 64 * wg + 32 * x + c32;
@@ -168,61 +170,91 @@ __global__ __launch_bounds__(256, 2) void mla_expand_kernel(MlaPrefill a) {
         rb[kk][x] = base + uint32_t(kETile + r2 * kESlice + 16 * eslot(r2, 2 * kk + kh));
       }
   }
-  constexpr int kStages = kR / kEK;   // 8
-  gload(0, 0);
-  static_for<kStages>([&](auto sc) {
+  // stage st has landed for this wave when at most 4 x (stages issued after
+  // it) of its loads are outstanding
+  auto wait_stage = [&](auto after) {
+    constexpr int k = decltype(after)::value;
+    if constexpr (k >= 2) __builtin_amdgcn_s_waitcnt(0x0F78);        // vmcnt(8)
+    else if constexpr (k == 1) __builtin_amdgcn_s_waitcnt(0x0F74);   // vmcnt(4)
+    else __builtin_amdgcn_s_waitcnt(0x0F70);                         // vmcnt(0)
+  };
+  gload(0);
+  gload(1);
+  gload(2);
+  static_for<kESteps>([&](auto sc) {
     constexpr int st = decltype(sc)::value;
-    constexpr int kOff = (st & 1) * kEStage;
-    __builtin_amdgcn_s_waitcnt(0x0F70);   // this wave's loads of stage st have landed
-    __builtin_amdgcn_s_barrier();         // everyone's; and everyone is done with stage st - 1
-    if constexpr (st + 1 < kStages) gload(st + 1, (st + 1) & 1);
-    u32x4_t af[2][2], bf[2][2];           // [k-step parity][x]
-    auto issue = [&](auto kc) {
-      constexpr int kk = decltype(kc)::value;
+    constexpr int kOff = (st % kERing) * kEStage;
+    constexpr int kAfter = (st + 2 < kESteps ? 2 : kESteps - 1 - st);   // stages issued after st
+    wait_stage(std::integral_constant<int, kAfter>{});
+    __builtin_amdgcn_s_barrier();   // everyone's loads of st; everyone done with st - 1
+    if constexpr (st + 3 < kESteps) gload(st + 3);   // refills the slot of st - 1
+    u32x4_t af[2][2], bf[2][2];           // [k-step][x]
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
       for (int x = 0; x < 2; ++x) {
-        af[kk & 1][x] = lds_read16_at<kOff>(ra[kk][x]);
-        bf[kk & 1][x] = lds_read16_at<kOff>(rb[kk][x]);
+        af[kk][x] = lds_read16_at<kOff>(ra[kk][x]);
+        bf[kk][x] = lds_read16_at<kOff>(rb[kk][x]);
       }
-    };
-    issue(std::integral_constant<int, 0>{});
-    static_for<4>([&](auto kc) {
-      constexpr int kk = decltype(kc)::value;
-      if constexpr (kk + 1 < 4) {
-        issue(std::integral_constant<int, kk + 1>{});
-        lds_wait<4>(af[kk & 1][0], af[kk & 1][1], bf[kk & 1][0], bf[kk & 1][1]);
-      } else {
-        lds_wait<0>(af[kk & 1][0], af[kk & 1][1], bf[kk & 1][0], bf[kk & 1][1]);
-      }
-#pragma unroll
-      for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-        for (int gi = 0; gi < 2; ++gi)
-          acc[mi][gi] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              as_bf16x8(af[kk & 1][mi]), as_bf16x8(bf[kk & 1][gi]), acc[mi][gi], 0, 0, 0);
-    });
-  });
-
-  // E^T tile (mi, gi): lane l holds key g = .. + l % 32 and outputs
-  // n = .. + 8 (i / 4) + 4 (l / 32) + i % 4: four consecutive outputs per store
-  const int64_t krow = int64_t(H) * kDq, vrow = int64_t(H) * kDv;   // elements per expanded row
-#pragma unroll
-  for (int gi = 0; gi < 2; ++gi) {
-    const int g = g0 + 64 * wg + 32 * gi + c32;
-    if (g >= total) continue;
-    uint16_t* dst = half == 0
-                        ? static_cast<uint16_t*>(a.k_exp) + int64_t(g) * krow + int64_t(h) * kDq
-                        : static_cast<uint16_t*>(a.v_exp) + int64_t(g) * vrow + int64_t(h) * kDv;
+    lds_wait<4>(af[0][0], af[0][1], bf[0][0], bf[0][1]);
 #pragma unroll
     for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int n = 64 * wn + 32 * mi + 8 * q4 + 4 * kh;   // within the 128 outputs
-        uint2 v;
-        v.x = pack_bf16x2(acc[mi][gi][4 * q4 + 0], acc[mi][gi][4 * q4 + 1]);
-        v.y = pack_bf16x2(acc[mi][gi][4 * q4 + 2], acc[mi][gi][4 * q4 + 3]);
-        *reinterpret_cast<uint2*>(dst + n) = v;
-      }
+      for (int gi = 0; gi < 2; ++gi)
+        acc[mi][gi] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(af[0][mi]), as_bf16x8(bf[0][gi]),
+                                                             acc[mi][gi], 0, 0, 0);
+    lds_wait<0>(af[1][0], af[1][1], bf[1][0], bf[1][1]);
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+      for (int gi = 0; gi < 2; ++gi)
+        acc[mi][gi] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(af[1][mi]), as_bf16x8(bf[1][gi]),
+                                                             acc[mi][gi], 0, 0, 0);
+  });
+
+  // Epilogue through LDS (the ring is free: every stage has been read), so
+  // that each key's 128 outputs leave as 256 contiguous bytes.  E^T tile
+  // (mi, gi): lane l holds key g = 64 wg + 32 gi + l % 32 and outputs
+  // n = 64 wn + 32 mi + 8 (i / 4) + 4 (l / 32) + i % 4, written to the staging
+  // row of key g (272-byte rows: 256 B + 16 B of padding).
+  constexpr int kORow = kEM * 2 + 16;
+  static_assert(kEN * kORow <= kERing * kEStage, "epilogue staging fits the ring");
+  __builtin_amdgcn_s_barrier();   // every wave is done reading the ring
+  {
+    const uint32_t base = lds_addr(smem);
+#pragma unroll
+    for (int gi = 0; gi < 2; ++gi)
+#pragma unroll
+      for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int g = 64 * wg + 32 * gi + c32;
+          const int n = 64 * wn + 32 * mi + 8 * q4 + 4 * kh;
+          u32x2_t v;
+          v.x = pack_bf16x2(acc[mi][gi][4 * q4 + 0], acc[mi][gi][4 * q4 + 1]);
+          v.y = pack_bf16x2(acc[mi][gi][4 * q4 + 2], acc[mi][gi][4 * q4 + 3]);
+          asm volatile("ds_write_b64 %0, %1" : : "v"(base + uint32_t(g * kORow + 2 * n)), "v"(v) : "memory");
+        }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  }
+  __builtin_amdgcn_s_barrier();
+  const int64_t krow = int64_t(H) * kDq, vrow = int64_t(H) * kDv;   // elements per expanded row
+  {
+    // 128 keys x 16 chunks of 16 B: 8 per thread, 16 lanes per key row
+    const uint32_t base = lds_addr(smem);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int q = tid + 256 * i;
+      const int row = q >> 4, part = q & 15;
+      const int g = g0 + row;
+      u32x4_t v;
+      asm volatile("ds_read_b128 %0, %1\n s_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(base + uint32_t(row * kORow + 16 * part)) : "memory");
+      if (g >= total) continue;
+      uint16_t* dst = half == 0
+                          ? static_cast<uint16_t*>(a.k_exp) + int64_t(g) * krow + int64_t(h) * kDq
+                          : static_cast<uint16_t*>(a.v_exp) + int64_t(g) * vrow + int64_t(h) * kDv;
+      store16(dst + 8 * part, v);
+    }
   }
   // the key half also places k_pe after the head's 128 expanded dims
   if (half == 0) {
