@@ -212,7 +212,7 @@ pa_status_t pa_decode(pa_dtype_t dtype,
  * block_size / 32) < 2^31.
  * pa_decode_balanced_merge completes out / lse (a request with no keys gets
  * out = 0, lse = -inf) after pa_decode_balanced (head_dim_v 128) or
- * pa_mla_decode_balanced (head_dim_v 512); its num_seqs, num_heads,
+ * pa_mla_decode_balanced (head_dim_v = kv_lora_rank, 512 or 256); its num_seqs, num_heads,
  * num_ranges and workspace must be those of the preceding call.
  * ------------------------------------------------------------------------- */
 int pa_decode_balanced_num_ranges(int num_kv_heads, int num_cus);
@@ -292,8 +292,10 @@ pa_status_t pa_prefill_varlen(pa_dtype_t dtype,
  * out:    [num_seqs, num_heads, kv_lora_rank], or NULL for the two-stage form
  *         (partials [num_seqs, num_heads, n, kv_lora_rank + 1] in the
  *         workspace); lse [num_seqs, num_heads] or NULL (NULL if out is).
- * Supported: PA_BF16 only (no dtype argument), kv_lora_rank 512, rope_dim 64,
- * num_heads a multiple of 16 up to 128, block_size a multiple of 16.
+ * Supported: PA_BF16 only (no dtype argument), kv_lora_rank 512 or 256 with
+ * rope_dim 64 (the latent head sizes 576 and 320 of "Triton 與 MLA",
+ * 邊界與失敗), num_heads a multiple of 16 up to 128, block_size a multiple of
+ * 16.
  * Enqueues: the write (if given), the split (or balanced) kernel, the merge
  * kernel.
  * ------------------------------------------------------------------------- */

@@ -420,7 +420,7 @@ def decode_balanced(q, kv_cache, block_table, seq_lens, scale: float, num_ranges
 
 def decode_balanced_merge(workspace, num_seqs: int, num_heads: int, head_dim_v: int,
                           num_ranges: int, out, lse=None, stream=None):
-    """Second kernel of the balanced GQA (head_dim_v 128) or MLA (512) decode:
+    """Second kernel of the balanced GQA (head_dim_v 128) or MLA (512 / 256) decode:
     combine the partials of requests that cross ranges into out / lse."""
     _dev(workspace, out, lse)
     wbytes = workspace.numel() * workspace.element_size()

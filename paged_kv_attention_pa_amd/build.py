@@ -65,6 +65,15 @@ def build(verbose: bool = False, jobs: int | None = None) -> str:
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed:\n{res.stdout}\n{res.stderr}")
+    # a kernel template whose host-side launch stub was not emitted links
+    # fine and only fails when the library is loaded: refuse it here
+    nm = shutil.which("nm")
+    if nm:
+        syms = subprocess.run([nm, "-D", "--undefined-only", tmp], capture_output=True, text=True).stdout
+        bad = [l.split()[-1] for l in syms.splitlines() if "__device_stub" in l]
+        if bad:
+            os.remove(tmp)
+            raise RuntimeError(f"undefined kernel launch stubs in {LIB}: {bad}")
     os.replace(tmp, LIB)
     if verbose:
         print(f"built {LIB}", flush=True)

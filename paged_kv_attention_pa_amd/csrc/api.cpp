@@ -366,8 +366,8 @@ pa_status_t pa_decode_balanced_merge(void* workspace, size_t workspace_bytes, in
                                      float* lse, hipStream_t stream) {
   PA_REQUIRE(num_seqs >= 0, PA_ERR_INVALID, "num_seqs must be >= 0 (got %d)", num_seqs);
   PA_REQUIRE(num_heads > 0, PA_ERR_INVALID, "num_heads must be > 0");
-  PA_REQUIRE(head_dim_v == 128 || head_dim_v == 512, PA_ERR_UNSUPPORTED,
-             "balanced merge supports head_dim_v 128 (GQA) and 512 (MLA) (got %d)", head_dim_v);
+  PA_REQUIRE(head_dim_v == 128 || head_dim_v == 256 || head_dim_v == 512, PA_ERR_UNSUPPORTED,
+             "balanced merge supports head_dim_v 128 (GQA), 256 and 512 (MLA) (got %d)", head_dim_v);
   PA_REQUIRE(num_ranges >= 1 && num_ranges <= (1 << 24), PA_ERR_INVALID,
              "num_ranges must be in [1, 2^24] (got %d)", num_ranges);
   const size_t need = balanced_bytes(num_seqs, num_heads, head_dim_v, num_ranges);
@@ -442,8 +442,9 @@ pa_status_t check_mla_q(int64_t qn_stride_b, int64_t qn_stride_h, int64_t qp_str
                         float scale) {
   PA_REQUIRE(scale_ok(scale), PA_ERR_INVALID, "scale must be finite and >= 0");
   PA_REQUIRE(kv_lora_rank > 0 && rope_dim > 0, PA_ERR_INVALID, "kv_lora_rank and rope_dim must be > 0");
-  PA_REQUIRE(kv_lora_rank == 512 && rope_dim == 64, PA_ERR_UNSUPPORTED,
-             "MLA decode supports kv_lora_rank 512 + rope_dim 64 (got %d + %d)", kv_lora_rank, rope_dim);
+  PA_REQUIRE((kv_lora_rank == 512 || kv_lora_rank == 256) && rope_dim == 64, PA_ERR_UNSUPPORTED,
+             "MLA decode supports kv_lora_rank 512 or 256 + rope_dim 64 (head size 576 or 320; "
+             "got %d + %d)", kv_lora_rank, rope_dim);
   PA_REQUIRE(num_heads > 0, PA_ERR_INVALID, "num_heads must be > 0");
   PA_REQUIRE(num_heads % 16 == 0 && num_heads <= 128, PA_ERR_UNSUPPORTED,
              "MLA decode supports num_heads a multiple of 16 up to 128 (got %d)", num_heads);
@@ -1070,6 +1071,8 @@ pa_status_t pa_mla_decode_fp8(const void* q_nope, int64_t qn_stride_b, int64_t q
   st = check_mla_q(qn_stride_b, qn_stride_h, qp_stride_b, qp_stride_h, num_heads, kv_lora_rank,
                    rope_dim, scale);
   if (st != PA_OK) return st;
+  PA_REQUIRE(kv_lora_rank == 512, PA_ERR_UNSUPPORTED,
+             "FP8 MLA decode supports kv_lora_rank 512 (got %d)", kv_lora_rank);
   PA_REQUIRE(fp8_scale_ok(kv_scale), PA_ERR_INVALID, "the FP8 scale must be finite and > 0");
   PA_REQUIRE(num_ranges >= 0, PA_ERR_INVALID, "num_ranges must be >= 0");
   PA_REQUIRE((kv_c == nullptr) == (k_pe == nullptr), PA_ERR_INVALID,

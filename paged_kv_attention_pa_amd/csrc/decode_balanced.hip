@@ -425,6 +425,9 @@ hipError_t launch_balanced_merge(const BalancedMerge& a, hipStream_t s) {
   if (a.head_dim == 128) {
     const dim3 grid{unsigned(int64_t(a.num_seqs) * a.num_q_heads)}, block{256};
     hipLaunchKernelGGL((balanced_merge_kernel<128>), grid, block, 0, s, a);
+  } else if (a.head_dim == 256) {
+    const dim3 grid{unsigned(int64_t(a.num_seqs) * a.num_q_heads)}, block{256};
+    hipLaunchKernelGGL((balanced_merge_kernel<256>), grid, block, 0, s, a);
   } else if (a.head_dim == 512) {
     const dim3 grid{unsigned(int64_t(a.num_seqs) * ((a.num_q_heads + 7) / 8))}, block{256};
     hipLaunchKernelGGL(balanced_merge512_kernel, grid, block, 0, s, a);

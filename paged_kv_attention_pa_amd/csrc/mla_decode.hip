@@ -32,25 +32,37 @@
 namespace pa {
 namespace {
 
-constexpr int kRank = 512;
 constexpr int kRope = 64;
-constexpr int kRow = kRank + kRope;             // 576 elements
-constexpr int kChunks = kRow * 2 / 16;          // 72 x 16 B per row
 constexpr int kBN = 32;                         // keys per tile
-constexpr int kRowBytes = kRow * 2;             // 1152 B, unpadded (swizzled)
-constexpr int kTileBytes = kBN * kRowBytes;     // 36864 B
-constexpr int kTileLoads = kBN * kChunks / 64;  // 36 wave-wide 16-byte loads per tile
 constexpr int kWaves = 4;
-constexpr int kLoadsPerWave = kTileLoads / kWaves;   // 9
 constexpr int kHeadsPerWave = 32;
 constexpr int kStages = 4;                      // LDS tile buffers: kStages - 1 tiles in flight
-constexpr int kKSteps = kRow / 16;              // 36 k-steps of the score product
-constexpr int kDTiles = kRank / 32;             // 16 d-tiles of the value product
 constexpr float kSlack = 8.0f;                  // lazy-rescale headroom, log2 units
 constexpr int kKDepth = 3;                      // K-fragment reads in flight ahead of their MFMA
 constexpr int kVDepth = 3;                      // V^T steps (two reads each) in flight ahead
-static_assert(kTileLoads % kWaves == 0, "loads per wave");
-static_assert(kStages * kTileBytes <= 160 * 1024 - 64, "LDS budget");
+
+// Sizes that follow from kv_lora_rank R (the latent row is R + 64 elements;
+// R = 512 gives the 576-element head, R = 256 the 320-element one).
+template <int R>
+struct MlaDims {
+  static constexpr int kRank = R;
+  static constexpr int kRow = R + kRope;                   // elements per latent row
+  static constexpr int kChunks = kRow * 2 / 16;            // 16-byte chunks per row
+  static constexpr int kRowBytes = kRow * 2;               // unpadded (swizzled)
+  static constexpr int kTileBytes = kBN * kRowBytes;
+  static constexpr int kTileLoads = kBN * kChunks / 64;    // wave-wide 16-byte loads per tile
+  static constexpr int kLoadsPerWave = kTileLoads / kWaves;
+  static constexpr int kKSteps = kRow / 16;                // k-steps of the score product
+  static constexpr int kDTiles = R / 32;                   // d-tiles of the value product
+  static_assert(kTileLoads % kWaves == 0 && kKSteps % 4 == 0 && kDTiles % 2 == 0, "tiling");
+  static_assert(kStages * kTileBytes <= 160 * 1024 - 64, "LDS budget");
+  static_assert(2 * kLoadsPerWave < 64, "vmcnt range");
+};
+
+// s_waitcnt immediate for "at most n vector-memory operations outstanding"
+// (expcnt and lgkmcnt not waited for)
+template <int N>
+constexpr int vmcnt_imm() { return (N & 15) | ((N >> 4) << 14) | 0x0F70; }
 
 // 16-byte chunk c of latent row r sits in LDS slot c ^ sx(r) of the row (the
 // XOR stays inside c's aligned group of eight), with sx(r) holding bits 1, 2
@@ -83,12 +95,16 @@ __device__ __forceinline__ void mfma_o(f32x16_t& d, const u32x4_t& a, const u32x
 }
 // Orders every read and write of the accumulator tiles after (tie) or
 // before (hazard fence) this point; kNop wait states go after the last one.
-template <int kNop>
-__device__ __forceinline__ void acc_fence(f32x16_t (&acc)[16]) {
-  asm volatile("" : "+a"(acc[0]), "+a"(acc[1]), "+a"(acc[2]), "+a"(acc[3]));
-  asm volatile("" : "+a"(acc[4]), "+a"(acc[5]), "+a"(acc[6]), "+a"(acc[7]));
-  asm volatile("" : "+a"(acc[8]), "+a"(acc[9]), "+a"(acc[10]), "+a"(acc[11]));
-  asm volatile("s_nop %4" : "+a"(acc[12]), "+a"(acc[13]), "+a"(acc[14]), "+a"(acc[15]) : "n"(kNop));
+__device__ __forceinline__ void acc_tie4(f32x16_t& a, f32x16_t& b, f32x16_t& c, f32x16_t& d) {
+  asm volatile("" : "+a"(a), "+a"(b), "+a"(c), "+a"(d));
+}
+template <int kNop, int N>
+__device__ __forceinline__ void acc_fence(f32x16_t (&acc)[N]) {
+  static_assert(N % 4 == 0 && N >= 4, "groups of four tiles");
+#pragma unroll
+  for (int g = 0; g + 4 < N; g += 4) acc_tie4(acc[g], acc[g + 1], acc[g + 2], acc[g + 3]);
+  asm volatile("s_nop %4" : "+a"(acc[N - 4]), "+a"(acc[N - 3]), "+a"(acc[N - 2]), "+a"(acc[N - 1])
+               : "n"(kNop));
 }
 
 // Two schedules share the kernel body:
@@ -106,16 +122,27 @@ __device__ __forceinline__ void acc_fence(f32x16_t (&acc)[16]) {
 // above (v_cvt_scalef32_pk_bf16_fp8, exact) in one of two bf16 buffers, so
 // both products run unchanged; the scale multiplies the score scale and the
 // final normalisation.
-constexpr int kF8TileBytes = kBN * kRow;                 // 18432 B of codes
+constexpr int kF8TileBytes = kBN * (512 + kRope);        // 18432 B of codes (kv_lora_rank 512)
 constexpr int kF8Pieces = kF8TileBytes / 1024;           // 18 wave-wide 16-byte loads
 constexpr int kF8Stages = 4;
 constexpr int kF8Chunks = kF8TileBytes / 8 / (64 * kWaves);   // 9 eight-code chunks per thread
-static_assert(2 * kTileBytes + kF8Stages * kF8TileBytes <= kStages * kTileBytes, "fp8 LDS budget");
+static_assert(2 * MlaDims<512>::kTileBytes + kF8Stages * kF8TileBytes <=
+                  kStages * MlaDims<512>::kTileBytes, "fp8 LDS budget");
 static_assert(kF8Pieces == 18 && kF8Chunks == 9, "fp8 piece counts");
 
-template <bool kBalanced, bool kFp8>
+// Page ids of a tile's first and last key.
+struct Pages { int32_t b0, b1; };
+
+template <bool kBalanced, bool kFp8, int kR>
 __global__ __launch_bounds__(64 * kWaves, 1) void mla_kernel(MlaDecode a) {
   static_assert(kBalanced || !kFp8, "the FP8 cache runs on the balanced schedule");
+  static_assert(!kFp8 || kR == 512, "the FP8 cache is built for kv_lora_rank 512");
+  using Dm = MlaDims<kR>;
+  constexpr int kRank = Dm::kRank, kRow = Dm::kRow, kChunks = Dm::kChunks;
+  constexpr int kRowBytes = Dm::kRowBytes, kTileBytes = Dm::kTileBytes;
+  constexpr int kTileLoads = Dm::kTileLoads, kLoadsPerWave = Dm::kLoadsPerWave;
+  constexpr int kKSteps = Dm::kKSteps, kDTiles = Dm::kDTiles;
+  (void)kTileLoads;
   __shared__ __align__(1024) char smem[kStages * kTileBytes];
   __shared__ int s_wave_sum[kWaves];
   __shared__ int s_start[2];
@@ -198,7 +225,10 @@ __global__ __launch_bounds__(64 * kWaves, 1) void mla_kernel(MlaDecode a) {
   // past kend (re-read as key kend - 1: finite, masked out below), take a
   // per-tile correction.
   const uint16_t* cache = static_cast<const uint16_t*>(a.cache);
-  uint32_t goff[kLoadsPerWave];
+  // (sized for the largest row: with a size that depends on the template
+  // arguments, the array captured by the gather lambda cost the kernel its
+  // host-side launch stub)
+  uint32_t goff[MlaDims<512>::kLoadsPerWave];
 #pragma unroll
   for (int jj = 0; jj < kLoadsPerWave; ++jj) {
     const int pos = 64 * (wave + kWaves * jj) + lane;
@@ -211,7 +241,6 @@ __global__ __launch_bounds__(64 * kWaves, 1) void mla_kernel(MlaDecode a) {
   // compute: a scalar load waited for right before its use would stall the
   // gather's issue, and one in flight during the LDS operand reads would
   // stall those (both count on lgkmcnt).
-  struct Pages { int32_t b0, b1; };
   auto pages = [&](const ChunkPos& p) {
     const int32_t* table = a.block_table + int64_t(p.r) * a.max_blocks;
     const int key0 = kb + p.lc * kBN;
@@ -431,11 +460,11 @@ __global__ __launch_bounds__(64 * kWaves, 1) void mla_kernel(MlaDecode a) {
   // wave issues 9 of a tile's 36 loads, so "tile t has landed" is "at most
   // 9 x (tiles issued after t) loads outstanding".
   auto wait_tiles = [&](int k) {   // k = tiles issued after the one waited for
-    if (k <= 0) __builtin_amdgcn_s_waitcnt(0x0F70);        // vmcnt(0)
-    else if (k == 1) __builtin_amdgcn_s_waitcnt(0x0F79);   // vmcnt(9)
-    else __builtin_amdgcn_s_waitcnt(0x4F72);               // vmcnt(18)
+    if (k <= 0) __builtin_amdgcn_s_waitcnt(0x0F70);                               // vmcnt(0)
+    else if (k == 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm<Dm::kLoadsPerWave>());
+    else __builtin_amdgcn_s_waitcnt(vmcnt_imm<2 * Dm::kLoadsPerWave>());
   };
-  static_assert(kStages <= 4 && kLoadsPerWave == 9, "wait_tiles counts");
+  static_assert(kStages <= 4, "wait_tiles counts");
 
   auto zero_pad_q = [&]() {
     if (!head_ok) {
@@ -612,23 +641,32 @@ __global__ __launch_bounds__(64 * kWaves, 1) void mla_kernel(MlaDecode a) {
 
 hipError_t launch_mla_decode(const MlaDecode& a, hipStream_t s) {
   if (a.num_seqs <= 0) return hipSuccess;
-  if (a.rank != kRank || a.rope != kRope || a.num_heads % 16 ||
+  if ((a.rank != 512 && a.rank != 256) || a.rope != kRope || a.num_heads % 16 ||
       a.num_heads > kHeadsPerWave * kWaves)
     return hipErrorNotSupported;
   if (a.fp8) {
-    if (a.num_ranges <= 0) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((mla_kernel<true, true>), dim3(unsigned(a.num_ranges)), dim3(64 * kWaves), 0,
-                       s, a);
+    if (a.num_ranges <= 0 || a.rank != 512) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((mla_kernel<true, true, 512>), dim3(unsigned(a.num_ranges)), dim3(64 * kWaves),
+                       0, s, a);
     return hipGetLastError();
   }
   if (a.num_ranges > 0) {
-    hipLaunchKernelGGL((mla_kernel<true, false>), dim3(unsigned(a.num_ranges)), dim3(64 * kWaves),
-                       0, s, a);
+    if (a.rank == 512) {
+      hipLaunchKernelGGL((mla_kernel<true, false, 512>), dim3(unsigned(a.num_ranges)),
+                         dim3(64 * kWaves), 0, s, a);
+    } else {
+      hipLaunchKernelGGL((mla_kernel<true, false, 256>), dim3(unsigned(a.num_ranges)),
+                         dim3(64 * kWaves), 0, s, a);
+    }
     return hipGetLastError();
   }
   const int64_t wgs = int64_t(a.num_seqs) * a.num_splits;
   if (wgs > INT32_MAX) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((mla_kernel<false, false>), dim3(unsigned(wgs)), dim3(64 * kWaves), 0, s, a);
+  if (a.rank == 512) {
+    hipLaunchKernelGGL((mla_kernel<false, false, 512>), dim3(unsigned(wgs)), dim3(64 * kWaves), 0, s, a);
+  } else {
+    hipLaunchKernelGGL((mla_kernel<false, false, 256>), dim3(unsigned(wgs)), dim3(64 * kWaves), 0, s, a);
+  }
   return hipGetLastError();
 }
 

@@ -202,3 +202,37 @@ def test_mla_balanced_requests_without_keys():
         assert np.all(o[[1, 3]] == 0) and np.all(np.isneginf(l[[1, 3]]))
         check_close(o, oref, f"ranges={nr} out")
         check_lse(l, lref, f"ranges={nr} lse")
+
+
+# ------------------------------------------ latent head size 320 (rank 256)
+CASES_320 = [
+    # name, seq_lens, heads, block_size
+    ("r256_ragged_h128", [1, 31, 32, 33, 64, 65, 700], 128, 64),
+    ("r256_h16_b16", [5, 100, 1000], 16, 16),
+    ("r256_h64_long", [3000, 2], 64, 64),
+]
+
+
+@pytest.mark.parametrize("ci", range(len(CASES_320)), ids=[c[0] for c in CASES_320])
+@pytest.mark.parametrize("splits", [0, 1, 5])
+def test_mla_rank256_head320(ci, splits):
+    """kv_lora_rank 256 + rope 64: the 320-element latent row, through the
+    balanced schedule (splits 0), one pass and explicit splits."""
+    name, seq, H, bs = CASES_320[ci]
+    say(f"mla 320 {name} splits={splits}")
+    b = W.make_mla(350 + ci, seq, H, 256, 64, bs, scale=1.0 / math.sqrt(192))
+    cache_t, out, lse = _run(b, num_splits=splits)
+    cache_ref, oref, lref = _oracle(b)
+    assert np.array_equal(bits(cache_t), cache_ref)
+    check_close(out, oref, f"{name} out")
+    check_lse(lse, lref, f"{name} lse")
+
+
+@pytest.mark.parametrize("num_ranges", [1, 7, 300])
+def test_mla_rank256_balanced_ranges(num_ranges):
+    say(f"mla 320 balanced ranges={num_ranges}")
+    b = W.make_mla(360, [1, 900, 64, 2000, 33], 32, 256, 64, 64)
+    cache, out, lse, _, _ = _run_balanced(b, num_ranges)
+    oref, lref = O.mla_decode(b.q_nope, b.q_pe, cache, b.block_table, b.seq_lens, b.scale)
+    check_close(to_f64(out), oref, "320 balanced out")
+    check_lse(lse.cpu().numpy().astype(np.float64), lref, "320 balanced lse")
