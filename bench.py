@@ -7,7 +7,7 @@ The headline line measures the Llama-3-8B-shaped GQA decode (64 requests,
 seq_len U[512, 8192], 32 q / 8 kv heads, d=128, bf16, block 16) in HBM GB/s;
 the other workloads (tiny fp32 decode, chunked prefill, long-context decode,
 MLA decode, a mixed prefill + decode batch, a batch sharing a prefix, GQA and
-MLA decode over FP8 caches, MLA prefill) are measured the same way and
+MLA decode and chunked prefill over FP8 caches, MLA prefill) are measured the same way and
 reported under "workloads".  Inputs are generated on the host by ``workloads.py`` (seeded),
 uploaded once, and resident in HBM before any timed region.
 
@@ -409,6 +409,37 @@ def mla_prefill_case(b, name):
                 "mla_expand_kernel + mla_attn_kernel", "mla_prefill.hip", info)
 
 
+def fp8_prefill_case(b, name):
+    """Chunked prefill over an FP8 cache (write + attention); the timed kernel
+    is the attention alone, priced against the bf16 MFMA peak."""
+    import torch
+    import paged_kv_attention_pa_amd as pa
+    import workloads as W
+    cache = torch.from_numpy(b.cache).cuda()
+    q = _dev(b.q)
+    bt, sl, qsl = _dev(b.block_table), _dev(b.seq_lens), _dev(b.query_start_loc)
+    kn, vn, sm = _dev(b.k_new), _dev(b.v_new), _dev(b.slot_mapping)
+    out = torch.empty_like(q)
+    lse = torch.empty(b.q.shape[:2], dtype=torch.float32, device="cuda")
+
+    def step():
+        pa.prefill_varlen_fp8(q, cache, bt, qsl, sl, b.max_query_len, b.max_seq_len, b.scale,
+                              b.k_scale, b.v_scale, k=kn, v=vn, slot_mapping=sm, out=out, lse=lse)
+
+    def kernel():
+        pa.prefill_varlen_fp8(q, cache, bt, qsl, sl, b.max_query_len, b.max_seq_len, b.scale,
+                              b.k_scale, b.v_scale, out=out, lse=lse)
+
+    by = W.gqa_bytes(b)
+    fl = W.gqa_flops(b)
+    info = {"num_seqs": b.num_seqs, "num_tokens": b.num_tokens, "num_q_heads": b.num_q_heads,
+            "num_kv_heads": b.num_kv_heads, "head_dim": b.head_dim, "block_size": b.block_size,
+            "cache_dtype": "fp8_e4m3", "k_scale": b.k_scale, "v_scale": b.v_scale,
+            "max_query_len": b.max_query_len, "max_seq_len": b.max_seq_len, "causal": True}
+    return Case(name, step, kernel, by["total"], fl, by["total"] - by["write"], fl, "mfma",
+                "prefill_kernel<false, true>", "prefill.hip", info)
+
+
 def build_cases(only):
     import workloads as W
     makers = {
@@ -424,6 +455,7 @@ def build_cases(only):
         W.FP8_DECODE: lambda: fp8_decode_case(W.llama_decode_fp8(), W.FP8_DECODE),
         W.FP8_MLA: lambda: mla_fp8_case(W.mla_decode_fp8_batch(), W.FP8_MLA),
         W.MLA_PREFILL: lambda: mla_prefill_case(W.mla_prefill_batch(), W.MLA_PREFILL),
+        W.FP8_PREFILL: lambda: fp8_prefill_case(W.chunked_prefill_fp8(), W.FP8_PREFILL),
     }
     names = [HEADLINE] + [n for n in makers if n != HEADLINE]
     if only is not None:   # exactly these (the line then reports the first one run)

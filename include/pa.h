@@ -527,6 +527,22 @@ pa_status_t pa_mla_decode_fp8(const void* q_nope, int64_t qn_stride_b, int64_t q
                               void* workspace, size_t workspace_bytes,
                               void* out, float* lse, hipStream_t stream);
 
+/* pa_prefill_varlen_fp8: pa_prefill_varlen over an FP8 GQA cache
+ * [num_blocks, 2, block_size, num_kv_heads, head_dim] uint8 with per-tensor
+ * k_scale / v_scale; q, new k / v rows (quantised on the write) and out are
+ * bf16.  Same arguments otherwise; head_dim 128, num_q_heads / num_kv_heads
+ * in {1, 2, 4, 8}. */
+pa_status_t pa_prefill_varlen_fp8(const void* q, const void* k, const void* v,
+                                  void* kv_cache, int64_t num_blocks, int block_size,
+                                  const int32_t* block_table, int max_blocks_per_seq,
+                                  const int64_t* slot_mapping,
+                                  const int32_t* query_start_loc,
+                                  const int32_t* seq_lens, int num_seqs,
+                                  int num_tokens, int max_query_len, int max_seq_len,
+                                  int num_q_heads, int num_kv_heads, int head_dim,
+                                  float scale, float k_scale, float v_scale, int causal,
+                                  void* out, float* lse, hipStream_t stream);
+
 pa_status_t pa_decode_fp8(const void* q, const void* k, const void* v,
                           void* kv_cache, int64_t num_blocks, int block_size,
                           const int32_t* block_table, int max_blocks_per_seq,

@@ -10,7 +10,7 @@ Functions mirror the C entry points: ``cache_write``, ``decode``,
 ``prefill_varlen``, ``mla_decode``, ``lse_merge``, ``decode_balanced``,
 ``plan_mixed`` + ``mixed_attention`` (a mixed prefill/decode batch),
 ``plan_cascade`` + ``cascade_attention`` (a batch sharing its first pages),
-``cache_write_fp8`` + ``decode_fp8`` + ``mla_decode_fp8`` (an FP8 E4M3 cache with
+``cache_write_fp8`` + ``decode_fp8`` + ``prefill_varlen_fp8`` + ``mla_decode_fp8`` (an FP8 E4M3 cache with
 per-tensor scales), ``mla_prefill`` (MLA prefill in the multi-head form),
 ``mla_decode_balanced``, ``decode_balanced_merge``, plus the host helpers ``num_kv_splits``,
 ``mla_num_kv_splits``, ``decode_workspace_bytes``,
@@ -24,7 +24,7 @@ from ._binding import (  # noqa: F401
     decode_balanced_num_ranges, decode_balanced_workspace_bytes,
     decode_workspace_bytes, device_num_cus, last_error, MixedPlan, mixed_attention, plan_mixed,
     CascadePlan, cascade_attention, plan_cascade, cache_write_fp8, decode_fp8,
-    mla_decode_fp8, mla_prefill, mla_prefill_workspace_bytes,
+    mla_decode_fp8, mla_prefill, mla_prefill_workspace_bytes, prefill_varlen_fp8,
     library, library_path, lse_merge, mla_decode, mla_decode_balanced, mla_num_kv_splits,
     num_kv_splits, prefill_varlen,
 )

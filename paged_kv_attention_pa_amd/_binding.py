@@ -59,6 +59,9 @@ _SIGNATURES = {
     "pa_mla_prefill": (_i32, [_vp, _i64, _i64, _vp, _vp, _vp, _i64, _i32, _vp, _i32, _vp, _vp, _vp,
                               _i32, _i32, _i32, _i32, _vp, _i32, _i32, _i32, _i32, _i32, _f32, _vp,
                               _sz, _vp, _vp, _vp]),
+    "pa_prefill_varlen_fp8": (_i32, [_vp, _vp, _vp, _vp, _i64, _i32, _vp, _i32, _vp, _vp, _vp,
+                                     _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _f32, _f32,
+                                     _i32, _vp, _vp, _vp]),
     "pa_decode_fp8": (_i32, [_vp, _vp, _vp, _vp, _i64, _i32, _vp, _i32, _vp, _vp, _i32, _i32,
                              _i32, _i32, _f32, _f32, _f32, _i32, _vp, _sz, _vp, _vp, _vp]),
     "pa_cascade_attention": (_i32, [_vp, _i32, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _vp, _vp,
@@ -333,6 +336,37 @@ def decode_fp8(q, kv_cache, block_table, seq_lens, scale: float, k_scale: float,
                                    _ptr(seq_lens), B, Hq, hkv, D, float(scale), float(k_scale),
                                    float(v_scale), nr, _ptr(workspace), wbytes, _ptr(out),
                                    _ptr(lse), _stream(stream)))
+    return out, lse
+
+
+def prefill_varlen_fp8(q, kv_cache, block_table, query_start_loc, seq_lens, max_query_len: int,
+                       max_seq_len: int, scale: float, k_scale: float, v_scale: float, k=None,
+                       v=None, slot_mapping=None, causal: bool = True, out=None, lse=None,
+                       return_lse: bool = True, stream=None):
+    """Varlen (chunked) prefill over an FP8 (E4M3) cache [nb, 2, bs, Hkv, D]
+    uint8; q [T, Hq, D] bf16.  Returns (out [T, Hq, D], lse [T, Hq])."""
+    torch = _torch()
+    _dev(q, kv_cache, block_table, query_start_loc, seq_lens, k, v, slot_mapping, out, lse)
+    _fp8_cache(kv_cache)
+    _int_tensor(block_table, "int32", "block_table")
+    _int_tensor(seq_lens, "int32", "seq_lens")
+    _int_tensor(query_start_loc, "int32", "query_start_loc")
+    _need(q.dtype == torch.bfloat16, "q must be bf16")
+    T, Hq, D = q.shape
+    nb, _, bs, hkv, _ = kv_cache.shape
+    N = seq_lens.numel()
+    _need(query_start_loc.numel() == N + 1, "query_start_loc must have num_seqs + 1 entries")
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and return_lse:
+        lse = torch.empty((T, Hq), dtype=torch.float32, device=q.device)
+    _check(library().pa_prefill_varlen_fp8(_ptr(q), _ptr(k), _ptr(v), _ptr(kv_cache), nb, bs,
+                                           _ptr(block_table), block_table.shape[1],
+                                           _ptr(slot_mapping), _ptr(query_start_loc),
+                                           _ptr(seq_lens), N, T, int(max_query_len),
+                                           int(max_seq_len), Hq, hkv, D, float(scale),
+                                           float(k_scale), float(v_scale), 1 if causal else 0,
+                                           _ptr(out), _ptr(lse), _stream(stream)))
     return out, lse
 
 

@@ -995,6 +995,60 @@ pa_status_t pa_cache_write_fp8(pa_layout_t layout, const void* k, int64_t k_toke
                            v_scale, stream);
 }
 
+pa_status_t pa_prefill_varlen_fp8(const void* q, const void* k, const void* v, void* kv_cache,
+                                  int64_t num_blocks, int block_size, const int32_t* block_table,
+                                  int max_blocks_per_seq, const int64_t* slot_mapping,
+                                  const int32_t* query_start_loc, const int32_t* seq_lens,
+                                  int num_seqs, int num_tokens, int max_query_len,
+                                  int max_seq_len, int num_q_heads, int num_kv_heads,
+                                  int head_dim, float scale, float k_scale, float v_scale,
+                                  int causal, void* out, float* lse, hipStream_t stream) {
+  PA_REQUIRE(scale_ok(scale), PA_ERR_INVALID, "scale must be finite and >= 0");
+  PA_REQUIRE(fp8_scale_ok(k_scale) && fp8_scale_ok(v_scale), PA_ERR_INVALID,
+             "FP8 scales must be finite and > 0");
+  pa_status_t st = check_common_cache(num_blocks, block_size, block_table, max_blocks_per_seq,
+                                      seq_lens, num_seqs, max_seq_len);
+  if (st != PA_OK) return st;
+  PA_REQUIRE(num_tokens >= 0 && max_query_len >= 0, PA_ERR_INVALID,
+             "num_tokens and max_query_len must be >= 0");
+  PA_REQUIRE(max_query_len <= num_tokens || num_seqs == 0, PA_ERR_INVALID,
+             "max_query_len exceeds num_tokens");
+  PA_REQUIRE(num_q_heads > 0 && num_kv_heads > 0 && num_q_heads % num_kv_heads == 0,
+             PA_ERR_INVALID, "num_q_heads (%d) must be a positive multiple of num_kv_heads (%d)",
+             num_q_heads, num_kv_heads);
+  PA_REQUIRE(causal == 0 || causal == 1, PA_ERR_INVALID, "causal must be 0 or 1");
+  PA_REQUIRE(head_dim == 128, PA_ERR_UNSUPPORTED, "FP8 prefill supports head_dim 128 (got %d)",
+             head_dim);
+  PA_REQUIRE(is_pow2_group(num_q_heads / num_kv_heads), PA_ERR_UNSUPPORTED,
+             "FP8 prefill supports num_q_heads / num_kv_heads in {1, 2, 4, 8}");
+  PA_REQUIRE((k == nullptr) == (v == nullptr), PA_ERR_INVALID, "k and v must both be given or both NULL");
+  PA_REQUIRE(k == nullptr || slot_mapping != nullptr, PA_ERR_INVALID, "k/v given without slot_mapping");
+  PA_REQUIRE(slot_mapping == nullptr || k != nullptr, PA_ERR_INVALID, "slot_mapping given without k/v");
+  if (num_seqs == 0 || num_tokens == 0) return ok();
+  PA_REQUIRE(q && kv_cache && out && query_start_loc, PA_ERR_INVALID,
+             "q, kv_cache, out and query_start_loc must be non-null");
+  if (k) {
+    st = check_write_fp8(PA_LAYOUT_KV, k, int64_t(num_kv_heads) * head_dim, v,
+                         int64_t(num_kv_heads) * head_dim, kv_cache, num_blocks, block_size,
+                         num_kv_heads, head_dim, slot_mapping, num_tokens, k_scale, v_scale);
+    if (st != PA_OK) return st;
+    st = enqueue_write_fp8(PA_LAYOUT_KV, k, int64_t(num_kv_heads) * head_dim, v,
+                           int64_t(num_kv_heads) * head_dim, kv_cache, num_blocks, block_size,
+                           num_kv_heads, head_dim, slot_mapping, num_tokens, k_scale, v_scale,
+                           stream);
+    if (st != PA_OK) return st;
+  }
+  pa::PrefillVarlen p{q, kv_cache, num_blocks, block_size, block_table, max_blocks_per_seq,
+                      query_start_loc, seq_lens, num_seqs, num_tokens, max_query_len, max_seq_len,
+                      num_q_heads, num_kv_heads, head_dim, scale, causal, out, lse};
+  p.fp8 = 1;
+  p.k_scale = k_scale;
+  p.v_scale = v_scale;
+  hipError_t e = pa::launch_prefill_varlen(p, stream);
+  if (e != hipSuccess) return hip_fail(e, "FP8 prefill launch");
+  return ok();
+}
+
 pa_status_t pa_decode_fp8(const void* q, const void* k, const void* v, void* kv_cache,
                           int64_t num_blocks, int block_size, const int32_t* block_table,
                           int max_blocks_per_seq, const int64_t* slot_mapping,

@@ -151,6 +151,8 @@ struct PrefillVarlen {
   // replace out and lse.
   int prefix_len; int prefix_splits; int split_keys;
   float* part_o; float* part_lse;
+  // FP8 (E4M3) cache: keys are code * k_scale, values code * v_scale
+  int fp8; float k_scale; float v_scale;
 };
 hipError_t launch_prefill_varlen(const PrefillVarlen& a, hipStream_t s);
 

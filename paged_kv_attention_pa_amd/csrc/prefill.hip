@@ -51,8 +51,14 @@ __device__ __forceinline__ int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 
 // kPrefix = true: the shared prefix of a cascade -- the batch's query rows,
 // each (token, head of the group) pair a row (row = token * G + head), against
 // one key range of the prefix, fp32 partials out.
-template <bool kPrefix>
+// kFp8 (varlen prefill only): the cache holds E4M3 codes.  Each thread loads
+// its 16-byte pieces of tile t + 1 into registers while tile t is computed,
+// and after a barrier widens them to bf16 (exact) into the single tile
+// buffer; k_scale folds into the score scale and v_scale into the final
+// normalisation.
+template <bool kPrefix, bool kFp8>
 __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillVarlen a) {
+  static_assert(!(kPrefix && kFp8), "the shared-prefix pass reads a bf16 cache");
   __shared__ __align__(16) char smem[4 * kTileBytes];   // 2 x (K tile, V tile)
   const int lane = threadIdx.x & 63;
   const int wave = wave_id();
@@ -193,7 +199,65 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillVarlen a) {
   };
   auto gwait = [&]() { __builtin_amdgcn_s_waitcnt(0x0F70); };   // vmcnt(0)
 
-  const float scale2 = a.scale * kLog2e;
+  // ---- FP8: register gather.  Thread piece p = tid + 256 i (i = 0, 1) of a
+  // plane is key p / 8, codes 16 (p % 8) .. + 15 of its head row; its key's
+  // 16-key group is (p / 8) / 16 = 2 i + tid / 128, whose page id is one of
+  // the tile's four scalar loads.
+  const int64_t f8_tok = int64_t(a.num_kv_heads) * kD;       // bytes per token (codes)
+  const uint32_t f8_tok32 = uint32_t(f8_tok);
+  const uint32_t f8_page = 2u * uint32_t(bs) * f8_tok32;
+  const uint32_t f8_kv = uint32_t(bs) * f8_tok32;
+  const char* f8_cache_h = static_cast<const char*>(a.cache) + int64_t(kvh) * kD;
+  u32x4_t f8r[4];   // K pieces i = 0, 1, then V pieces
+  auto rload = [&](int tile) {
+    uint32_t blk[4], in_page[4];
+    int key16[4];
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      key16[jj] = min(tile * kBN + 16 * jj, last16);
+      const int page = bs_pow2 ? key16[jj] >> bs_shift : key16[jj] / bs;
+      in_page[jj] = uint32_t(key16[jj] - page * bs);
+      blk[jj] = uint32_t(uniform_load(table + page));
+    }
+    const bool tail = tile * kBN + kBN > kv_end;   // wave-uniform
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int p = tid + 256 * i;
+      const int key = p >> 3, c8 = p & 7;
+      const int grp = 2 * i + (tid >> 7);
+      // the lane's group among the two this piece can fall in
+      const uint32_t bg = (tid >> 7) ? blk[2 * i + 1] : blk[2 * i];
+      const uint32_t ip = (tid >> 7) ? in_page[2 * i + 1] : in_page[2 * i];
+      const int k16 = (tid >> 7) ? key16[2 * i + 1] : key16[2 * i];
+      (void)grp;
+      int rr = key & 15;
+      if (tail) rr = min(rr, kv_end - 1 - k16);
+      const uint32_t b = bg < nblk ? bg : 0u;
+      const char* base = f8_cache_h + uint64_t(b) * f8_page;
+      const uint32_t off = (ip + uint32_t(rr)) * f8_tok32 + 16u * uint32_t(c8);
+      f8r[i] = load16(base + off);
+      f8r[2 + i] = load16(base + f8_kv + off);
+    }
+  };
+  auto rstore = [&](char* kdst) {
+    char* vdst = kdst + kTileBytes;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int p = tid + 256 * i;
+      const int key = p >> 3, c8 = p & 7;
+      const int o0 = key * kRowBytes + 16 * ((2 * c8) ^ swz(key));
+      const int o1 = key * kRowBytes + 16 * ((2 * c8 + 1) ^ swz(key));
+      u32x4_t lo, hi;
+      fp8x16_to_bf16(f8r[i], lo, hi);
+      *reinterpret_cast<u32x4_t*>(kdst + o0) = lo;
+      *reinterpret_cast<u32x4_t*>(kdst + o1) = hi;
+      fp8x16_to_bf16(f8r[2 + i], lo, hi);
+      *reinterpret_cast<u32x4_t*>(vdst + o0) = lo;
+      *reinterpret_cast<u32x4_t*>(vdst + o1) = hi;
+    }
+  };
+
+  const float scale2 = (kFp8 ? a.scale * a.k_scale : a.scale) * kLog2e;
   float m_run = kNoMax;   // running max (base-2 domain) of row my_row
   float l_run = 0.0f;     // this lane's share of the running sum
   f32x16_t acc[4];        // O^T tiles: d = 32 dt + 8 (r/4) + 4 (l/32) + r%4
@@ -202,17 +266,27 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillVarlen a) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[dt][i] = 0.0f;
 
-  if (n_tiles > t_begin) {
-    gload(t_begin, smem);
-    gwait();
+  if constexpr (kFp8) {
+    if (n_tiles > t_begin) {
+      rload(t_begin);
+      rstore(smem);
+    }
+  } else {
+    if (n_tiles > t_begin) {
+      gload(t_begin, smem);
+      gwait();
+    }
   }
   __syncthreads();
 
   const bool causal = kPrefix ? false : a.causal;
   const int row_abs = C + my_row;         // last key this row may see (causal)
   for (int t = t_begin; t < n_tiles; ++t) {
-    const int buf = (t - t_begin) & 1;
-    if (t + 1 < n_tiles) gload(t + 1, smem + (buf ^ 1) * 2 * kTileBytes);   // in flight below
+    const int buf = kFp8 ? 0 : (t - t_begin) & 1;
+    if (t + 1 < n_tiles) {   // in flight below
+      if constexpr (kFp8) rload(t + 1);
+      else gload(t + 1, smem + (buf ^ 1) * 2 * kTileBytes);
+    }
     const char* kt = smem + buf * 2 * kTileBytes;
     const char* vt = kt + kTileBytes;
     const int key0 = t * kBN;
@@ -354,19 +428,27 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillVarlen a) {
     });
 
     if (t + 1 < n_tiles) {
-      // this wave's loads of tile t + 1 have landed; after the barrier every
-      // wave's have, and every wave is done reading buffer buf (its LDS reads
-      // were waited for), which the loads issued at the start of iteration
-      // t + 1 refill.  A bare barrier: the tiles' only writer is the DMA.
-      gwait();
-      __builtin_amdgcn_s_barrier();
+      if constexpr (kFp8) {
+        // every wave is done reading the tile buffer; then tile t + 1's
+        // widened codes go in, and the second barrier publishes them
+        __syncthreads();
+        rstore(smem);
+        __syncthreads();
+      } else {
+        // this wave's loads of tile t + 1 have landed; after the barrier every
+        // wave's have, and every wave is done reading buffer buf (its LDS reads
+        // were waited for), which the loads issued at the start of iteration
+        // t + 1 refill.  A bare barrier: the tiles' only writer is the DMA.
+        gwait();
+        __builtin_amdgcn_s_barrier();
+      }
     }
   }
 
   // ---- finish: full row sum, normalise, write
   const float l_tot = l_run + lane_xor(l_run, 32);
   if (!row_ok) return;
-  const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+  const float inv = l_tot > 0.0f ? (kFp8 ? a.v_scale : 1.0f) / l_tot : 0.0f;
   if constexpr (kPrefix) {
     const int64_t prow = (int64_t(split) * a.num_tokens + my_row / G) * Hq + h;
     float* po = a.part_o + prow * kD;
@@ -410,7 +492,7 @@ hipError_t launch_prefill_varlen(const PrefillVarlen& a, hipStream_t s) {
     const int64_t pairs = int64_t(a.num_kv_heads) * a.prefix_splits;
     const int64_t wgs = (pairs + kXcds - 1) / kXcds * kXcds * n_qt;
     if (wgs > INT32_MAX || int64_t(a.num_tokens) * G > INT32_MAX) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(prefill_kernel<true>, dim3(unsigned(wgs)), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((prefill_kernel<true, false>), dim3(unsigned(wgs)), dim3(256), 0, s, a);
     return hipGetLastError();
   }
   if (a.num_seqs <= 0 || a.num_tokens <= 0 || a.max_query_len <= 0) return hipSuccess;
@@ -419,7 +501,11 @@ hipError_t launch_prefill_varlen(const PrefillVarlen& a, hipStream_t s) {
   const int64_t pairs = int64_t(a.num_seqs) * a.num_kv_heads;
   const int64_t wgs = (pairs + kXcds - 1) / kXcds * kXcds * n_qt * G;
   if (wgs > INT32_MAX) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(prefill_kernel<false>, dim3(unsigned(wgs)), dim3(256), 0, s, a);
+  if (a.fp8) {
+    hipLaunchKernelGGL((prefill_kernel<false, true>), dim3(unsigned(wgs)), dim3(256), 0, s, a);
+  } else {
+    hipLaunchKernelGGL((prefill_kernel<false, false>), dim3(unsigned(wgs)), dim3(256), 0, s, a);
+  }
   return hipGetLastError();
 }
 

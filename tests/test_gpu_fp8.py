@@ -266,3 +266,84 @@ def test_fp8_mla_workload_full_size(fp8_mla_batch):
         check_close(out[r], oref[r], f"request {r} out")
         check_lse(lse[r], lref[r], f"request {r} lse")
     assert np.array_equal(_host(cache_t), cache_ref)
+
+
+# -------------------------------------------------------------- prefill
+def _run_prefill(b, causal=True):
+    cache_t = _u8(b.cache)
+    out, lse = pa.prefill_varlen_fp8(to_dev(b.q), cache_t, to_dev(b.block_table),
+                                     to_dev(b.query_start_loc), to_dev(b.seq_lens), b.max_query_len,
+                                     b.max_seq_len, b.scale, b.k_scale, b.v_scale,
+                                     k=to_dev(b.k_new), v=to_dev(b.v_new),
+                                     slot_mapping=to_dev(b.slot_mapping), causal=causal)
+    torch.cuda.synchronize()
+    return cache_t, to_f64(out), lse.cpu().numpy().astype(np.float64)
+
+
+def _oracle_prefill(b, causal=True, requests=None):
+    cache = O.cache_write_kv_fp8(b.cache, b.k_new, b.v_new, b.slot_mapping, b.k_scale, b.v_scale)
+    deq = O.dequant_kv_cache(cache, b.k_scale, b.v_scale)
+    out, lse = O.paged_attention(b.q, deq, b.block_table, b.query_start_loc, b.seq_lens, b.scale,
+                                 causal=causal, requests=requests)
+    return cache, out, lse
+
+
+PREFILL_CASES = [
+    # name, q_lens, context lens, Hq, Hkv, block size, k_scale, v_scale
+    ("ragged_g4", [1, 7, 64, 65, 130, 257], [0, 100, 0, 33, 511, 64], 8, 2, 16, 0.3, 0.07),
+    ("long_chunk_g8", [300], [1000], 8, 1, 16, 0.25, 0.5),
+    ("g1_block32", [129, 3], [31, 700], 2, 2, 32, 1.3, 0.011),
+    ("g4_32_8", [90, 40, 260], [17, 256, 4], 32, 8, 16, 0.02, 2.0),
+]
+
+
+@pytest.mark.parametrize("ci", range(len(PREFILL_CASES)), ids=[c[0] for c in PREFILL_CASES])
+@pytest.mark.parametrize("causal", [True, False], ids=["causal", "full"])
+def test_fp8_prefill_small(ci, causal):
+    name, ql, cl, hq, hkv, bs, ks, vs = PREFILL_CASES[ci]
+    say(f"fp8 prefill {name} causal={causal}")
+    b = W.make_gqa(770 + ci, ql, np.array(ql) + np.array(cl), hq, hkv, 128, bs, W.FP8,
+                   scale=1.0 / math.sqrt(128), k_scale=ks, v_scale=vs)
+    cache_t, out, lse = _run_prefill(b, causal)
+    cache_ref, oref, lref = _oracle_prefill(b, causal)
+    assert np.array_equal(_host(cache_t), cache_ref)
+    check_close(out, oref, f"{name} out")
+    check_lse(lse, lref, f"{name} lse")
+
+
+def test_fp8_prefill_equals_bf16_prefill_on_dequantised_cache():
+    """Power-of-two scales: the FP8 prefill equals the bf16 prefill over the
+    dequantised cache bit for bit (same tiles, same arithmetic after the
+    exact widening)."""
+    say("fp8 prefill vs bf16 prefill")
+    b = W.make_gqa(780, [150, 1, 70], [400, 90, 70], 16, 4, 128, 16, W.FP8, k_scale=0.125,
+                   v_scale=4.0)
+    cache_t, out8, lse8 = _run_prefill(b)
+    deq = O.fp8_e4m3_to_f64(_host(cache_t))
+    deq[:, 0] *= b.k_scale
+    deq[:, 1] *= b.v_scale
+    deq = np.where(np.isnan(deq), 0.0, deq)
+    bf = W.f32_to_bf16_bits(deq.astype(np.float32))
+    out16, lse16 = pa.prefill_varlen(to_dev(b.q), to_dev(bf), to_dev(b.block_table),
+                                     to_dev(b.query_start_loc), to_dev(b.seq_lens), b.max_query_len,
+                                     b.max_seq_len, b.scale)
+    torch.cuda.synchronize()
+    assert np.array_equal(out8, to_f64(out16))
+    assert np.array_equal(lse8, lse16.cpu().numpy().astype(np.float64))
+
+
+def test_fp8_prefill_workload_full_size():
+    """The chunked-prefill shape over an FP8 cache: 16 requests, chunks
+    U{64..2048} over contexts U{0..4096}, 32/8 heads; the longest and the
+    shortest chunk against the oracle."""
+    b = W.chunked_prefill_fp8()
+    say(f"fp8 prefill full size T={b.num_tokens}")
+    cache_t, out, lse = _run_prefill(b)
+    assert np.all(np.isfinite(out))
+    reqs = sorted({int(np.argmax(b.q_lens)), int(np.argmin(b.q_lens))})
+    cache_ref, oref, lref = _oracle_prefill(b, requests=reqs)
+    for r in reqs:
+        a0, a1 = b.query_start_loc[r], b.query_start_loc[r + 1]
+        check_close(out[a0:a1], oref[a0:a1], f"request {r} out")
+        check_lse(lse[a0:a1], lref[a0:a1], f"request {r} lse")
+    assert np.array_equal(_host(cache_t), cache_ref)

@@ -460,6 +460,18 @@ def llama_decode(seed: int = 1002, batch: int = 64) -> GqaBatch:
 
 FP8_DECODE = "llama3_8b_gqa_decode_fp8kv"
 FP8_MLA = "mla_latent_decode_fp8kv"
+FP8_PREFILL = "chunked_prefill_varlen_fp8kv"
+
+
+def chunked_prefill_fp8(seed: int = 1011, batch: int = 16) -> GqaBatch:
+    """The chunked-prefill shape (16 requests, chunk U{64..2048} over context
+    U{0..4096}, 32 q / 8 kv heads, d=128, block 16, causal) over an FP8
+    cache, k_scale 0.25, v_scale 0.5."""
+    rng = np.random.default_rng(seed)
+    L = rng.integers(64, 2048, size=batch, endpoint=True)
+    C = rng.integers(0, 4096, size=batch, endpoint=True)
+    return make_gqa(rng, L, C + L, 32, 8, 128, 16, FP8, name=FP8_PREFILL, k_scale=0.25,
+                    v_scale=0.5)
 
 
 def mla_decode_fp8_batch(seed: int = 1009, batch: int = 128) -> MlaBatch:
