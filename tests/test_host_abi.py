@@ -247,3 +247,115 @@ def test_mla_balanced_validation(lib):
     assert call(2, 100) == INVALID                    # q_nope head stride < 512
     assert call(20, None) == INVALID                  # no output
     assert call(18, (1 << 20) + 8) == INVALID         # misaligned workspace
+
+
+def test_fp8_write_validation(lib):
+    f = lib.pa_cache_write_fp8
+    #     layout k  kst   v  vst   cache nb  bs  hkv d    slots T  ks   vs   stream
+    base = [0, 1, 1024, 2, 1024, 3, 10, 16, 8, 128, 4, 5, 0.5, 0.25, None]
+
+    def call(i, v):
+        a = list(base)
+        a[i] = v
+        return f(*a)
+
+    assert call(11, 0) == 0                            # zero tokens: nothing to do
+    assert call(12, 0.0) == INVALID                    # k_scale 0
+    assert call(13, float("inf")) == INVALID           # v_scale not finite
+    assert call(12, float("nan")) == INVALID
+    assert call(7, 12) == INVALID                      # block size 12
+    assert call(2, 100) == INVALID                     # k stride too short
+    assert call(0, 9) == INVALID                       # unknown layout
+    assert call(1, None) == INVALID                    # no k
+    # MLA layout: one KV head, a rank + 64 row; v_scale unused (zero tokens: no launch)
+    assert f(1, 1, 512, 2, 64, 3, 10, 64, 1, 576, 4, 0, 0.5, 0.0, None) == 0
+    assert f(1, 1, 512, 2, 64, 3, 10, 64, 2, 576, 4, 5, 0.5, 1.0, None) == INVALID
+
+
+def test_fp8_decode_validation(lib):
+    f = lib.pa_decode_fp8
+    need = pa.decode_balanced_workspace_bytes(4, 32, 128, 16)
+    #       q  k     v     cache nb  bs  table maxb slots seq B  hq  hkv d    sc   ks   vs  nr
+    base = [1, None, None, 2, 100, 16, 3, 64, None, 4, 4, 32, 8, 128, 0.1, 0.5, 0.5, 16,
+            1 << 20, need, 5, None, None]
+
+    def call(i, v):
+        a = list(base)
+        a[i] = v
+        return f(*a)
+
+    assert call(15, 0.0) == INVALID                    # k_scale
+    assert call(16, -1.0) == INVALID                   # v_scale
+    assert call(13, 64) == UNSUPPORTED                 # head_dim 64
+    assert call(11, 96) == UNSUPPORTED                 # group 12
+    six = list(base)
+    six[11], six[12] = 12, 6                           # 6 KV heads: not whole rows of 1/2/4/8
+    assert f(*six) == UNSUPPORTED
+    assert call(19, need - 1) == WORKSPACE
+    assert call(18, (1 << 20) + 4) == INVALID          # misaligned workspace
+    assert call(1, 7) == INVALID                       # k without v
+    assert call(17, -1) == INVALID                     # negative range count
+    assert call(10, 0) == 0                            # empty batch
+
+
+def test_fp8_prefill_validation(lib):
+    f = lib.pa_prefill_varlen_fp8
+    #       q  k     v     cache nb  bs  table maxb slots qsl seq N  T    maxq maxs hq hkv d
+    base = [1, None, None, 2, 100, 16, 3, 64, None, 4, 5, 2, 100, 50, 300, 32, 8, 128,
+            0.1, 0.5, 0.5, 1, 6, None, None]
+
+    def call(i, v):
+        a = list(base)
+        a[i] = v
+        return f(*a)
+
+    assert call(19, 0.0) == INVALID                    # k_scale
+    assert call(20, float("nan")) == INVALID           # v_scale
+    assert call(21, 2) == INVALID                      # causal flag
+    assert call(13, 200) == INVALID                    # max_query_len > num_tokens
+    assert call(17, 64) == UNSUPPORTED                 # head_dim 64
+    assert call(9, None) == INVALID                    # query_start_loc
+    assert call(11, 0) == 0                            # no requests
+
+
+def test_fp8_mla_validation(lib):
+    f = lib.pa_mla_decode_fp8
+    need = pa.decode_balanced_workspace_bytes(4, 128, 512, 16)
+    base = [1, 128 * 512, 512, 2, 128 * 64, 64, None, None, 3, 100, 64, 4, 64, None, 5, 4, 128, 512,
+            64, 0.07, 0.5, 16, 1 << 20, need, 6, None, None]
+
+    def call(i, v):
+        a = list(base)
+        a[i] = v
+        return f(*a)
+
+    assert call(20, 0.0) == INVALID                    # kv_scale
+    assert call(17, 256) == UNSUPPORTED                # rank 256 is bf16 only
+    assert call(23, need - 1) == WORKSPACE
+    assert call(6, 9) == INVALID                       # kv_c without k_pe
+    assert call(21, -2) == INVALID                     # negative range count
+
+
+def test_mla_prefill_validation(lib):
+    f = lib.pa_mla_prefill
+    need = pa.mla_prefill_workspace_bytes(2, 700, 16)
+    assert need == 256 + ((700 * 16 * 192 * 2 + 255) // 256) * 256 + ((700 * 16 * 128 * 2 + 255) // 256) * 256
+    #       q  qst       qsh  kv_c  k_pe  cache nb  bs  table maxb slots qsl seq N  T    maxq keys
+    base = [1, 16 * 192, 192, None, None, 2, 100, 64, 3, 64, None, 4, 5, 2, 300, 200, 700,
+            7, 16, 512, 64, 128, 128, 0.07, 1 << 20, need, 6, None, None]
+
+    def call(i, v):
+        a = list(base)
+        a[i] = v
+        return f(*a)
+
+    assert call(19, 256) == UNSUPPORTED                # kv_lora_rank 256
+    assert call(21, 192) == UNSUPPORTED                # qk_nope 192
+    assert call(25, need - 1) == WORKSPACE
+    assert call(24, (1 << 20) + 16) == INVALID         # misaligned workspace
+    assert call(2, 100) == INVALID                     # head stride < 192
+    assert call(15, 400) == INVALID                    # max_query_len > num_tokens
+    assert call(3, 9) == INVALID                       # kv_c without k_pe
+    assert call(17, None) == INVALID                   # no weight
+    assert call(23, -1.0) == INVALID                   # negative scale
+    assert call(13, 0) == 0                            # no requests
