@@ -153,7 +153,7 @@ def prefill_case(b, name):
             "num_kv_heads": b.num_kv_heads, "head_dim": b.head_dim, "block_size": b.block_size,
             "max_query_len": b.max_query_len, "max_seq_len": b.max_seq_len, "causal": True,
             "grid": "ceil(max_q/128) x num_seqs x Hq work-groups of 256"}
-    return Case(name, step, kernel, by["total"], fl, kb, fl, "mfma", "prefill_kernel<false>",
+    return Case(name, step, kernel, by["total"], fl, kb, fl, "mfma", "prefill_kernel<false, false>",
                 "prefill.hip", info)
 
 
@@ -187,7 +187,7 @@ def mla_case(b, name):
             "rope_dim": b.rope_dim, "block_size": b.block_size, "max_seq_len": b.max_seq_len,
             "total_keys": int(b.seq_lens.sum()), "schedule": "token-balanced ranges",
             "grid": f"{nr} token ranges x 8 waves (16 heads each)"}
-    return Case(name, step, kernel, by["total"], fl, kb, fl, "mfma", "mla_kernel<true, false>",
+    return Case(name, step, kernel, by["total"], fl, kb, fl, "mfma", "mla_kernel<true, false, 512>",
                 "mla_decode.hip", info)
 
 
@@ -371,7 +371,7 @@ def mla_fp8_case(b, name):
             "total_keys": int(b.seq_lens.sum()), "schedule": "token-balanced ranges",
             "timed": "decode kernel + segment merge"}
     return Case(name, step, kernel, by["total"], fl, kb, fl, "mfma",
-                "mla_kernel<true, true> + merge", "mla_decode.hip", info)
+                "mla_kernel<true, true, 512> + merge", "mla_decode.hip", info)
 
 
 def mla_prefill_case(b, name):
