@@ -115,7 +115,7 @@ def full():
 
 
 def test_mla_prefill_workload_full_size(full):
-    """4 requests, chunks U{256..2048} over contexts U{0..4096}, 16 heads:
+    """16 requests, chunks U{64..2048} over contexts U{0..4096}, 16 heads:
     the shortest and the longest chunk against the oracle, cache bit-exact."""
     b = full
     say(f"mla prefill full size T={b.num_tokens} keys={b.total_keys}")

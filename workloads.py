@@ -405,12 +405,13 @@ def make_mla_prefill(seed, q_lens, seq_lens, num_heads: int = 16, block_size: in
 MLA_PREFILL = "mla_prefill_bf16"
 
 
-def mla_prefill_batch(seed: int = 1010, batch: int = 4, num_heads: int = 16) -> MlaPrefillBatch:
-    """4 requests, chunk ~ U{256..2048} new queries over context ~ U{0..4096},
-    16 heads (one GPU's share of 128 heads split over 8), kv_lora_rank 512 +
-    rope 64 latent rows, qk 192 / v 128 per head, block 64, bf16, causal."""
+def mla_prefill_batch(seed: int = 1010, batch: int = 16, num_heads: int = 16) -> MlaPrefillBatch:
+    """The chunked-prefill distribution (16 requests, chunk ~ U{64..2048} new
+    queries over context ~ U{0..4096}) for MLA: 16 heads (one GPU's share of
+    128 heads split over 8), kv_lora_rank 512 + rope 64 latent rows, qk 192 /
+    v 128 per head, block 64, bf16, causal."""
     rng = np.random.default_rng(seed)
-    L = rng.integers(256, 2048, size=batch, endpoint=True)
+    L = rng.integers(64, 2048, size=batch, endpoint=True)
     C = rng.integers(0, 4096, size=batch, endpoint=True)
     return make_mla_prefill(rng, L, C + L, num_heads, 64, name=MLA_PREFILL)
 
