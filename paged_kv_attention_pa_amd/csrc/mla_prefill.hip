@@ -68,37 +68,54 @@ __global__ __launch_bounds__(256) void key_start_kernel(MlaPrefill a) {
 
 // ------------------------------------------------------------- expansion
 constexpr int kEM = 128;                     // projection outputs per work-group
-constexpr int kEN = 128;                     // keys per work-group
+constexpr int kEN = 256;                     // keys per work-group
 constexpr int kEK = 32;                      // k per stage
 constexpr int kESlice = kEK * 2;             // 64 B of a row per stage
-constexpr int kETile = kEM * kESlice;        // 8 KiB (either operand)
-constexpr int kEStage = 2 * kETile;          // W tile, then latent tile
-constexpr int kERing = 4;                    // stages in LDS: three in flight
+constexpr int kEWTile = kEM * kESlice;       // 8 KiB of W per stage
+constexpr int kELTile = kEN * kESlice;       // 16 KiB of latent rows per stage
+constexpr int kEStage = kEWTile + kELTile;   // 24 KiB
+constexpr int kERing = 3;                    // stages in LDS: two in flight
+// ring layout: the three W slices first, then the three latent slices
+constexpr int kELBase = kERing * kEWTile;
 constexpr int kESteps = kR / kEK;            // 16 stages over kv_lora_rank
+constexpr int kEWLoads = kEWTile / 1024 / 4; // wave-wide 16-byte loads per wave and stage: W
+constexpr int kELoads = kEStage / 1024 / 4;  // all (W first)
 // 16-byte chunk c (0..3) of row r of a staged slice sits in slot
 // c ^ ((r >> 2) & 3): rows are 64 B, so a 16-lane phase reading one chunk of
 // 16 consecutive rows hits 16 distinct 16-byte bank groups.
 __device__ __forceinline__ int eslot(int r, int c) { return c ^ ((r >> 2) & 3); }
 
+// Two work-groups per CU (74 KiB of LDS each): one's prologue (row lookup,
+// first loads) and epilogue (the stores of its outputs) run under the other's
+// MFMA work.
 __global__ __launch_bounds__(256, 2) void mla_expand_kernel(MlaPrefill a) {
   __shared__ __align__(16) char smem[kERing * kEStage];
   __shared__ uint64_t s_row[kEN];             // byte offset of each key's latent row
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int H = a.num_heads;
   const int n_tiles = 2 * H;                  // a tile is the key half or the value half of a head
-  // the n tiles of one key tile run on one XCD, one after another (their
-  // latent rows stay in its L2)
+  // XCD-aware order.  When the n tiles divide over the XCDs, each XCD keeps
+  // its share of W (n_tiles / 8 slices of 128 KiB) in its L2 and walks all
+  // key tiles; otherwise the n tiles of one key tile run on one XCD, one
+  // after another, and share its latent rows there.
   const int id = blockIdx.x;
   const int xcd = id % kXcds, slot = id / kXcds;
-  const int g_tile = (slot / n_tiles) * kXcds + xcd;
-  const int n_tile = slot % n_tiles;
+  int g_tile, n_tile;
+  if (n_tiles % kXcds == 0) {
+    const int n_per = n_tiles / kXcds;
+    n_tile = xcd * n_per + slot % n_per;
+    g_tile = slot / n_per;
+  } else {
+    g_tile = (slot / n_tiles) * kXcds + xcd;
+    n_tile = slot % n_tiles;
+  }
   const int total = a.total_keys;
   const int g0 = g_tile * kEN;
   if (g0 >= total) return;
   const int h = n_tile >> 1, half = n_tile & 1;
 
   // latent row of each key of the tile (keys past the batch re-read the last)
-  if (tid < kEN) {
+  {
     const int g = min(g0 + tid, total - 1);
     int lo = 0, hi = a.num_seqs - 1;          // request r with key_start[r] <= g < key_start[r + 1]
     while (lo < hi) {
@@ -116,120 +133,139 @@ __global__ __launch_bounds__(256, 2) void mla_expand_kernel(MlaPrefill a) {
 
   const char* wbase = static_cast<const char*>(a.w) + int64_t(n_tile) * kEM * (kR * 2);
   const char* cbase = static_cast<const char*>(a.cache);
-  // DMA: 8 wave-wide loads per operand and stage (16 rows x 64 B each); wave
-  // w issues loads w and w + 4 of both.  Lane i of load j: row 16 j + i / 4,
-  // slot i % 4, which holds chunk eslot(row, slot).
-  uint32_t w_off[2];
-  const char* l_src[2];   // this lane's latent bytes of each of its loads (stage 0)
+  // DMA: a stage is 24 wave-wide loads of 16 rows x 64 B: loads 0..7 the W
+  // slice, 8..23 the latent slice; wave w issues loads j = w + 4 jj (its
+  // first two are W loads).  Lane i of load j: row 16 j' + i / 4 of its
+  // operand (j' = j, or j - 8), slot i % 4, which holds chunk eslot(row, slot).
+  constexpr int kWJ = 4 * kEWLoads;   // W loads per stage
+  const char* src[kELoads];   // this lane's bytes of each of its loads (stage 0)
 #pragma unroll
-  for (int jj = 0; jj < 2; ++jj) {
+  for (int jj = 0; jj < kELoads; ++jj) {
     const int j = wave + 4 * jj;
-    const int row = 16 * j + (lane >> 2);
-    const int c = eslot(row, lane & 3);
-    w_off[jj] = uint32_t(row * (kR * 2) + 16 * c);
-    l_src[jj] = cbase + s_row[row] + 16 * c;
+    if (jj < kEWLoads) {
+      const int row = 16 * j + (lane >> 2);
+      src[jj] = wbase + row * (kR * 2) + 16 * eslot(row, lane & 3);
+    } else {
+      const int row = 16 * (j - kWJ) + (lane >> 2);
+      src[jj] = cbase + s_row[row] + 16 * eslot(row, lane & 3);
+    }
   }
   typedef __attribute__((address_space(3))) void* lds_ptr;
   auto gload = [&](int stage) {
-    char* dw = smem + (stage % kERing) * kEStage;
-    char* dl = dw + kETile;
+    const int slot = stage % kERing;
 #pragma unroll
-    for (int jj = 0; jj < 2; ++jj) {
+    for (int jj = 0; jj < kELoads; ++jj) {
       const int j = wave + 4 * jj;
-      __builtin_amdgcn_global_load_lds(wbase + w_off[jj] + stage * kESlice, (lds_ptr)(dw + 1024 * j),
-                                       16, 0, 0);
-      __builtin_amdgcn_global_load_lds(l_src[jj] + stage * kESlice, (lds_ptr)(dl + 1024 * j), 16, 0, 0);
+      char* dst = jj < kEWLoads ? smem + slot * kEWTile + 1024 * j
+                                : smem + kELBase + slot * kELTile + 1024 * (j - kWJ);
+      __builtin_amdgcn_global_load_lds(src[jj] + stage * kESlice, (lds_ptr)dst, 16, 0, 0);
     }
   };
 
-  // wave tile: outputs 64 wn .. + 63, keys 64 wg .. + 63 (2 x 2 MFMA tiles)
-  const int wn = wave & 1, wg = wave >> 1;
+  // wave tile: all 128 outputs x keys 64 w .. + 63 (4 x 2 MFMA tiles)
   const int c32 = lane & 31, kh = lane >> 5;
-  f32x16_t acc[2][2];
+  f32x16_t acc[4][2];
 #pragma unroll
-  for (int mi = 0; mi < 2; ++mi)
+  for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
     for (int gi = 0; gi < 2; ++gi)
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[mi][gi][i] = 0.0f;
 
-  // LDS operand addresses of k-step kk (ring slot 0): rows 64 wn + 32 x + c32
-  // of the W tile and 64 wg + 32 x + c32 of the latent tile, chunk 2 kk + kh.
-  // The reads are inline assembly with explicit waits: the compiler cannot
-  // tell them apart from the DMA filling the other slots and would wait for
-  // those loads first.
-  uint32_t ra[2][2], rb[2][2];
+  // LDS operand addresses of k-step kk (ring slot 0): output rows 32 mi + c32
+  // of the W slice, key rows 64 wave + 32 gi + c32 of the latent slice, chunk
+  // 2 kk + kh.  The reads are inline assembly with explicit waits: the
+  // compiler cannot tell them apart from the DMA filling the other slots and
+  // would wait for those loads first.
+  constexpr int kKSteps = kEK / 16;
+  uint32_t ra[kKSteps][4], rb[kKSteps][2];
   {
     const uint32_t base = lds_addr(smem);
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk)
+    for (int kk = 0; kk < kKSteps; ++kk) {
 #pragma unroll
-      for (int x = 0; x < 2; ++x) {
-        const int r1 = 64 * wn + 32 * x + c32, r2 = 64 * wg + 32 * x + c32;
-        ra[kk][x] = base + uint32_t(r1 * kESlice + 16 * eslot(r1, 2 * kk + kh));
-        rb[kk][x] = base + uint32_t(kETile + r2 * kESlice + 16 * eslot(r2, 2 * kk + kh));
+      for (int mi = 0; mi < 4; ++mi) {
+        const int r = 32 * mi + c32;
+        ra[kk][mi] = base + uint32_t(r * kESlice + 16 * eslot(r, 2 * kk + kh));
       }
+#pragma unroll
+      for (int gi = 0; gi < 2; ++gi) {
+        const int r = 64 * wave + 32 * gi + c32;
+        rb[kk][gi] = base + uint32_t(kELBase + r * kESlice + 16 * eslot(r, 2 * kk + kh));
+      }
+    }
   }
-  // stage st has landed for this wave when at most 4 x (stages issued after
-  // it) of its loads are outstanding
-  auto wait_stage = [&](auto after) {
-    constexpr int k = decltype(after)::value;
-    if constexpr (k >= 2) __builtin_amdgcn_s_waitcnt(0x0F78);        // vmcnt(8)
-    else if constexpr (k == 1) __builtin_amdgcn_s_waitcnt(0x0F74);   // vmcnt(4)
-    else __builtin_amdgcn_s_waitcnt(0x0F70);                         // vmcnt(0)
-  };
   gload(0);
   gload(1);
-  gload(2);
   static_for<kESteps>([&](auto sc) {
     constexpr int st = decltype(sc)::value;
-    constexpr int kOff = (st % kERing) * kEStage;
-    constexpr int kAfter = (st + 2 < kESteps ? 2 : kESteps - 1 - st);   // stages issued after st
-    wait_stage(std::integral_constant<int, kAfter>{});
+    constexpr int kSlot = st % kERing;
+    constexpr int kAOff = kSlot * kEWTile;
+    constexpr int kBOff = kSlot * kELTile;
+    static_assert(kAOff < 65536 && kBOff < 65536, "immediate LDS offsets");
+    // stage st has landed for this wave when the loads of the stages issued
+    // after it are the only ones outstanding
+    static_assert(kELoads == 6, "the wait below counts one stage's loads");
+    if constexpr (st + 1 < kESteps) __builtin_amdgcn_s_waitcnt(0x0F76);   // vmcnt(6)
+    else __builtin_amdgcn_s_waitcnt(0x0F70);                               // vmcnt(0)
     __builtin_amdgcn_s_barrier();   // everyone's loads of st; everyone done with st - 1
-    if constexpr (st + 3 < kESteps) gload(st + 3);   // refills the slot of st - 1
-    u32x4_t af[2][2], bf[2][2];           // [k-step][x]
+    if constexpr (st + 2 < kESteps) gload(st + 2);   // refills the slot of st - 1
+    u32x4_t af[2][4], bf[2][2];     // [k-step parity][tile]
+    auto issue = [&](auto kc) {
+      constexpr int kk = decltype(kc)::value;
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk)
+      for (int mi = 0; mi < 4; ++mi) af[kk & 1][mi] = lds_read16_at<kAOff>(ra[kk][mi]);
 #pragma unroll
-      for (int x = 0; x < 2; ++x) {
-        af[kk][x] = lds_read16_at<kOff>(ra[kk][x]);
-        bf[kk][x] = lds_read16_at<kOff>(rb[kk][x]);
+      for (int gi = 0; gi < 2; ++gi) bf[kk & 1][gi] = lds_read16_at<kBOff>(rb[kk][gi]);
+    };
+    issue(std::integral_constant<int, 0>{});
+    static_for<kKSteps>([&](auto kc) {
+      constexpr int kk = decltype(kc)::value;
+      if constexpr (kk + 1 < kKSteps) {
+        issue(std::integral_constant<int, kk + 1>{});
+        lds_wait<6>(af[kk & 1][0], af[kk & 1][1], af[kk & 1][2], af[kk & 1][3]);
+        lds_wait<6>(bf[kk & 1][0], bf[kk & 1][1]);
+      } else {
+        lds_wait<0>(af[kk & 1][0], af[kk & 1][1], af[kk & 1][2], af[kk & 1][3]);
+        lds_wait<0>(bf[kk & 1][0], bf[kk & 1][1]);
       }
-    lds_wait<4>(af[0][0], af[0][1], bf[0][0], bf[0][1]);
 #pragma unroll
-    for (int mi = 0; mi < 2; ++mi)
+      for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
-      for (int gi = 0; gi < 2; ++gi)
-        acc[mi][gi] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(af[0][mi]), as_bf16x8(bf[0][gi]),
-                                                             acc[mi][gi], 0, 0, 0);
-    lds_wait<0>(af[1][0], af[1][1], bf[1][0], bf[1][1]);
-#pragma unroll
-    for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-      for (int gi = 0; gi < 2; ++gi)
-        acc[mi][gi] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(af[1][mi]), as_bf16x8(bf[1][gi]),
-                                                             acc[mi][gi], 0, 0, 0);
+        for (int gi = 0; gi < 2; ++gi)
+          acc[mi][gi] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              as_bf16x8(af[kk & 1][mi]), as_bf16x8(bf[kk & 1][gi]), acc[mi][gi], 0, 0, 0);
+    });
   });
 
   // Epilogue through LDS (the ring is free: every stage has been read), so
   // that each key's 128 outputs leave as 256 contiguous bytes.  E^T tile
-  // (mi, gi): lane l holds key g = 64 wg + 32 gi + l % 32 and outputs
-  // n = 64 wn + 32 mi + 8 (i / 4) + 4 (l / 32) + i % 4, written to the staging
-  // row of key g (272-byte rows: 256 B + 16 B of padding).
+  // (mi, gi): lane l holds key g = 64 wave + 32 gi + l % 32 and outputs
+  // n = 32 mi + 8 (i / 4) + 4 (l / 32) + i % 4, written to the staging row of
+  // key g (272-byte rows: 256 B + 16 B of padding).
   constexpr int kORow = kEM * 2 + 16;
   static_assert(kEN * kORow <= kERing * kEStage, "epilogue staging fits the ring");
+  // the key half also places k_pe after the head's 128 projected dims: its
+  // loads go out first (keys past the batch read the last key's row)
+  u32x4_t pe[8] = {};
+  if (half == 0) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int q = tid + 256 * i;          // 256 rows x 8 chunks of 16 B
+      pe[i] = load16(cbase + s_row[q >> 3] + kR * 2 + 16 * (q & 7));
+    }
+  }
   __builtin_amdgcn_s_barrier();   // every wave is done reading the ring
   {
     const uint32_t base = lds_addr(smem);
 #pragma unroll
     for (int gi = 0; gi < 2; ++gi)
 #pragma unroll
-      for (int mi = 0; mi < 2; ++mi)
+      for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
-          const int g = 64 * wg + 32 * gi + c32;
-          const int n = 64 * wn + 32 * mi + 8 * q4 + 4 * kh;
+          const int g = 64 * wave + 32 * gi + c32;
+          const int n = 32 * mi + 8 * q4 + 4 * kh;
           u32x2_t v;
           v.x = pack_bf16x2(acc[mi][gi][4 * q4 + 0], acc[mi][gi][4 * q4 + 1]);
           v.y = pack_bf16x2(acc[mi][gi][4 * q4 + 2], acc[mi][gi][4 * q4 + 3]);
@@ -237,35 +273,45 @@ __global__ __launch_bounds__(256, 2) void mla_expand_kernel(MlaPrefill a) {
         }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   }
+  // the k_pe rows have arrived before any output store is issued (a wait
+  // after those stores would wait for them too); unconditional, so that no
+  // path reaches the k_pe stores with the loads still counted as pending
+  asm volatile("s_waitcnt vmcnt(0)"
+                 : "+v"(pe[0]), "+v"(pe[1]), "+v"(pe[2]), "+v"(pe[3]),
+                   "+v"(pe[4]), "+v"(pe[5]), "+v"(pe[6]), "+v"(pe[7]));
   __builtin_amdgcn_s_barrier();
   const int64_t krow = int64_t(H) * kDq, vrow = int64_t(H) * kDv;   // elements per expanded row
   {
-    // 128 keys x 16 chunks of 16 B: 8 per thread, 16 lanes per key row
+    // 256 keys x 16 chunks of 16 B: 16 per thread, 16 lanes per key row,
+    // read four at a time
     const uint32_t base = lds_addr(smem);
+    char* out = half == 0 ? static_cast<char*>(a.k_exp) + 2 * (int64_t(h) * kDq)
+                          : static_cast<char*>(a.v_exp) + 2 * (int64_t(h) * kDv);
+    const int64_t orow = 2 * (half == 0 ? krow : vrow);   // bytes per expanded row
+#pragma unroll
+    for (int i0 = 0; i0 < 16; i0 += 4) {
+      u32x4_t v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int q = tid + 256 * (i0 + u);
+        v[u] = lds_read16_at<0>(base + uint32_t((q >> 4) * kORow + 16 * (q & 15)));
+      }
+      lds_wait<0>(v[0], v[1], v[2], v[3]);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int q = tid + 256 * (i0 + u);
+        const int g = g0 + (q >> 4);
+        if (g < total) store16(out + int64_t(g) * orow + 16 * (q & 15), v[u]);
+      }
+    }
+  }
+  if (half == 0) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int q = tid + 256 * i;
-      const int row = q >> 4, part = q & 15;
-      const int g = g0 + row;
-      u32x4_t v;
-      asm volatile("ds_read_b128 %0, %1\n s_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(base + uint32_t(row * kORow + 16 * part)) : "memory");
-      if (g >= total) continue;
-      uint16_t* dst = half == 0
-                          ? static_cast<uint16_t*>(a.k_exp) + int64_t(g) * krow + int64_t(h) * kDq
-                          : static_cast<uint16_t*>(a.v_exp) + int64_t(g) * vrow + int64_t(h) * kDv;
-      store16(dst + 8 * part, v);
-    }
-  }
-  // the key half also places k_pe after the head's 128 expanded dims
-  if (half == 0) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int q = tid + 256 * i;          // 128 rows x 8 chunks of 16 B
-      const int row = q >> 3, part = q & 7;
-      const int g = g0 + row;
-      if (g >= total) continue;
-      const u32x4_t v = load16(cbase + s_row[row] + kR * 2 + 16 * part);
-      store16(static_cast<uint16_t*>(a.k_exp) + int64_t(g) * krow + int64_t(h) * kDq + kDn + 8 * part, v);
+      const int g = g0 + (q >> 3);
+      if (g < total)
+        store16(static_cast<uint16_t*>(a.k_exp) + int64_t(g) * krow + int64_t(h) * kDq + kDn + 8 * (q & 7), pe[i]);
     }
   }
 }
