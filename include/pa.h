@@ -578,14 +578,17 @@ pa_status_t pa_decode_fp8(const void* q, const void* k, const void* v,
  *              head h's rows h * 256 .. h * 256 + 127 expand keys, the next 128
  *              values
  * workspace:   pa_mla_prefill_workspace_bytes(num_seqs, total_keys, num_heads)
- *              bytes, 256-byte aligned: key offsets and the projected keys
+ *              bytes, 256-byte aligned: key offsets, the attention's work
+ *              list (one entry per 128-query tile, longest first; sized for
+ *              num_seqs + total_keys / 128 + 1 tiles, which holds whenever every
+ *              seq_lens[r] counts request r's queries), and the projected keys
  *              [total_keys, num_heads, 192] and values [total_keys, num_heads,
  *              128], bf16 (the projection's output dtype)
  * out:         [num_tokens, num_heads, v_head_dim] bf16; lse [num_tokens,
  *              num_heads] fp32 or NULL
  * Supported: kv_lora_rank 512, rope_dim 64, qk_nope_dim 128, v_head_dim 128.
- * Enqueues: the latent write (if given), the key offsets, the projection and
- * the attention.
+ * Enqueues: the latent write (if given), the key offsets and work list, the
+ * projection and the attention.
  * ------------------------------------------------------------------------- */
 size_t pa_mla_prefill_workspace_bytes(int num_seqs, int total_keys, int num_heads);
 

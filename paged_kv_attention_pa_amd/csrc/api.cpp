@@ -1171,23 +1171,34 @@ pa_status_t pa_mla_decode_fp8(const void* q_nope, int64_t qn_stride_b, int64_t q
 // ---------------------------------------------------------------------------
 // MLA prefill workspace: key offsets [N + 1] int32, projected keys
 // [total, H, 192] and values [total, H, 128] bf16, each 256-byte aligned.
-static bool mla_prefill_layout(int num_seqs, int total_keys, int num_heads, size_t* k_off,
-                               size_t* v_off, size_t* total) {
+// Workspace of pa_mla_prefill: key offsets [N + 1] and the work list's length,
+// the work list (one (request, q tile) pair per 128-query tile: at most
+// N + T / 128 of them, and T <= total_keys), then the expanded keys and values.
+struct MlaPrefillLayout {
+  size_t items_off, k_off, v_off, total;
+  int item_cap;
+};
+static bool mla_prefill_layout(int num_seqs, int total_keys, int num_heads, MlaPrefillLayout* l) {
   if (num_seqs < 0 || total_keys < 0 || num_heads <= 0) return false;
   auto up = [](unsigned __int128 x) { return (x + 255) / 256 * 256; };
-  unsigned __int128 off = up((unsigned __int128)(num_seqs + 1) * 4);
-  *k_off = size_t(off);
+  const int64_t cap = int64_t(num_seqs) + total_keys / 128 + 1;
+  if (cap > INT32_MAX) return false;
+  l->item_cap = int(cap);
+  unsigned __int128 off = up((unsigned __int128)(num_seqs + 2) * 4);
+  l->items_off = size_t(off);
+  off = up(off + (unsigned __int128)cap * 8);
+  l->k_off = size_t(off);
   off = up(off + (unsigned __int128)total_keys * (unsigned)num_heads * 192 * 2);
-  *v_off = size_t(off);
+  l->v_off = size_t(off);
   off = up(off + (unsigned __int128)total_keys * (unsigned)num_heads * 128 * 2);
   if (off > (unsigned __int128)(SIZE_MAX / 2)) return false;
-  *total = size_t(off);
+  l->total = size_t(off);
   return true;
 }
 
 size_t pa_mla_prefill_workspace_bytes(int num_seqs, int total_keys, int num_heads) {
-  size_t k_off, v_off, total;
-  return mla_prefill_layout(num_seqs, total_keys, num_heads, &k_off, &v_off, &total) ? total : 0;
+  MlaPrefillLayout l;
+  return mla_prefill_layout(num_seqs, total_keys, num_heads, &l) ? l.total : 0;
 }
 
 pa_status_t pa_mla_prefill(const void* q, int64_t q_stride_t, int64_t q_stride_h,
@@ -1224,14 +1235,14 @@ pa_status_t pa_mla_prefill(const void* q, int64_t q_stride_t, int64_t q_stride_h
              "kv_c/k_pe given without slot_mapping");
   PA_REQUIRE(slot_mapping == nullptr || kv_c != nullptr, PA_ERR_INVALID,
              "slot_mapping given without kv_c/k_pe");
-  size_t k_off, v_off, need;
-  PA_REQUIRE(mla_prefill_layout(num_seqs, total_keys, num_heads, &k_off, &v_off, &need),
+  MlaPrefillLayout lay;
+  PA_REQUIRE(mla_prefill_layout(num_seqs, total_keys, num_heads, &lay),
              PA_ERR_INVALID, "workspace size overflows");
   if (num_seqs == 0 || num_tokens == 0) return ok();
   PA_REQUIRE(q && kv_cache && out && query_start_loc && w_kv_b, PA_ERR_INVALID,
              "q, kv_cache, out, query_start_loc and w_kv_b must be non-null");
-  PA_REQUIRE(workspace != nullptr && workspace_bytes >= need, PA_ERR_WORKSPACE,
-             "workspace of %zu bytes needed (got %zu)", need, workspace_bytes);
+  PA_REQUIRE(workspace != nullptr && workspace_bytes >= lay.total, PA_ERR_WORKSPACE,
+             "workspace of %zu bytes needed (got %zu)", lay.total, workspace_bytes);
   PA_REQUIRE((reinterpret_cast<uintptr_t>(workspace) & 255) == 0, PA_ERR_INVALID,
              "workspace must be 256-byte aligned");
   PA_REQUIRE(int64_t(total_keys) * num_heads * 192 <= INT64_MAX / 4, PA_ERR_INVALID,
@@ -1246,7 +1257,9 @@ pa_status_t pa_mla_prefill(const void* q, int64_t q_stride_t, int64_t q_stride_h
   pa::MlaPrefill m{q, q_stride_t, q_stride_h, kv_cache, num_blocks, block_size, block_table,
                    max_blocks_per_seq, query_start_loc, seq_lens, num_seqs, num_tokens,
                    max_query_len, total_keys, w_kv_b, num_heads, scale,
-                   reinterpret_cast<int32_t*>(ws), ws + k_off, ws + v_off, out, lse};
+                   reinterpret_cast<int32_t*>(ws), ws + lay.k_off, ws + lay.v_off, out, lse,
+                   reinterpret_cast<int32_t*>(ws + lay.items_off),
+                   reinterpret_cast<int32_t*>(ws) + num_seqs + 1, lay.item_cap};
   hipError_t e = pa::launch_mla_prefill(m, stream);
   if (e != hipSuccess) return hip_fail(e, "MLA prefill launch");
   return ok();

@@ -129,6 +129,8 @@ struct MlaPrefill {
   int32_t* key_start;                       // [N + 1] (workspace)
   void* k_exp; void* v_exp;                 // [total_keys, H, 192], [total_keys, H, 128] (workspace)
   void* out; float* lse;                    // [T, H, 128] bf16, [T, H] fp32 or null
+  int32_t* items; int32_t* n_items;         // attention work list [item_cap][2] (request, q tile),
+  int item_cap;                             // and its length (workspace)
 };
 hipError_t launch_mla_prefill(const MlaPrefill& a, hipStream_t s);
 

@@ -12,14 +12,18 @@
 // online softmax).
 //
 // Three kernels:
-// * key_start_kernel: cumulative key counts of the requests (one block scan).
+// * mla_schedule_kernel: cumulative key counts of the requests (one block
+//   scan), then the attention's work list: every (request, 128-query tile)
+//   item, longest first (counting sort on the number of 64-key tiles the item
+//   visits), so that the long items start early and the short ones fill the
+//   tail.
 // * mla_expand_kernel: the projection of every key of the batch, a bf16 GEMM
 //   E^T[n][g] = sum_k W[n][k] L[g][k] over the gathered latent rows L (n = a
-//   projection output of one head, g = a key of the batch), 128 x 128 tiles on
+//   projection output of one head, g = a key of the batch), 128 x 256 tiles on
 //   v_mfma_f32_32x32x16_bf16, both operands staged in LDS by
-//   global_load_lds_dwordx4 (double-buffered 64-deep k slices); the work-group
-//   holding a head's key rows also copies k_pe next to them, so the expanded
-//   key row is 192 contiguous elements.
+//   global_load_lds_dwordx4 (32-deep k slices in a three-stage ring, two
+//   work-groups per CU); the work-group holding a head's key rows also copies
+//   k_pe next to them, so the expanded key row is 192 contiguous elements.
 // * mla_attn_kernel: the prefill kernel's tiling (128 query rows of one head
 //   per work-group, 64-key tiles gathered into LDS by DMA, S^T = K Q^T and
 //   O^T += V^T P^T on 32x32x16 MFMAs, online softmax in the exp2 domain) with
@@ -39,32 +43,6 @@ constexpr int kDq = kDn + kP;    // 192: query / key width
 constexpr int kOut = kDn + kDv;  // 256 projection outputs per head
 constexpr int kLatBytes = (kR + kP) * 2;   // 1152 B per latent row
 constexpr int kXcds = 8;
-
-// ---------------------------------------------------------------- key starts
-__global__ __launch_bounds__(256) void key_start_kernel(MlaPrefill a) {
-  __shared__ int s_sum[4];
-  const int cap = a.max_blocks * a.block_size;
-  int carry = 0;
-  if (threadIdx.x == 0) a.key_start[0] = 0;
-  for (int base = 0; base < a.num_seqs; base += 256) {
-    const int r = base + threadIdx.x;
-    int v = r < a.num_seqs ? min(max(a.seq_lens[r], 0), cap) : 0;
-    // inclusive scan within the wave, then across the four waves
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int t = __shfl_up(v, o);
-      if (lane >= o) v += t;
-    }
-    if (lane == 63) s_sum[w] = v;
-    __syncthreads();
-    int before = carry;
-    for (int i = 0; i < w; ++i) before += s_sum[i];
-    if (r < a.num_seqs) a.key_start[r + 1] = before + v;
-    carry += s_sum[0] + s_sum[1] + s_sum[2] + s_sum[3];
-    __syncthreads();
-  }
-}
 
 // ------------------------------------------------------------- expansion
 constexpr int kEM = 128;                     // projection outputs per work-group
@@ -331,30 +309,131 @@ constexpr float kSlack = 8.0f;
 __device__ __forceinline__ int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
 __device__ __forceinline__ int pslot(int r, int c) { return c ^ ((r >> 1) & 7); }
 
+// Request r's queries [q_start, q_start + L) and keys [ks, ks + S) of the
+// expanded buffers, clamped to the rows that exist (the schedule and the
+// attention read them through this one function).
+struct ReqGeom { int q_start, L, ks, S; };
+__device__ __forceinline__ ReqGeom request_geometry(const MlaPrefill& a, int r) {
+  ReqGeom g;
+  g.q_start = min(max(a.query_start_loc[r], 0), a.num_tokens);
+  g.L = min(min(a.query_start_loc[r + 1] - g.q_start, a.max_query_len), a.num_tokens - g.q_start);
+  g.ks = min(a.key_start[r], a.total_keys);
+  g.S = min(a.key_start[r + 1], a.total_keys) - g.ks;
+  return g;
+}
+// keys visible to some query of the tile starting at query q0 (causal,
+// bottom-right aligned: query i sees keys 0 .. S - L + i)
+__device__ __forceinline__ int visible_keys(const ReqGeom& g, int q0) {
+  return min(g.S, max(0, g.S - g.L + min(q0 + kBM, g.L)));
+}
+
+// ------------------------------------------------------------- schedule
+constexpr int kSortBuckets = 1024;
+
+__global__ __launch_bounds__(256) void mla_schedule_kernel(MlaPrefill a) {
+  __shared__ int s_sum[4];
+  __shared__ int s_hist[kSortBuckets];
+  __shared__ int s_max;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  // key offsets: inclusive block scan of the (clamped) sequence lengths
+  const int cap = a.max_blocks * a.block_size;
+  int carry = 0;
+  if (tid == 0) {
+    a.key_start[0] = 0;
+    s_max = 0;
+  }
+  for (int base = 0; base < a.num_seqs; base += 256) {
+    const int r = base + tid;
+    int v = r < a.num_seqs ? min(max(a.seq_lens[r], 0), cap) : 0;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int t = __shfl_up(v, o);
+      if (lane >= o) v += t;
+    }
+    if (lane == 63) s_sum[w] = v;
+    __syncthreads();
+    int before = carry;
+    for (int i = 0; i < w; ++i) before += s_sum[i];
+    if (r < a.num_seqs) a.key_start[r + 1] = before + v;
+    carry += s_sum[0] + s_sum[1] + s_sum[2] + s_sum[3];
+    __syncthreads();
+  }
+  for (int i = tid; i < kSortBuckets; i += 256) s_hist[i] = 0;
+  __syncthreads();   // also orders the key offsets above before the reads below
+
+  // sort key of an item: 1 + its 64-key tiles (largest at a request's last
+  // q tile), coarsened by a shift so that the largest fits the buckets;
+  // bucket 0 holds the longest items
+  for (int r = tid; r < a.num_seqs; r += 256) {
+    const ReqGeom g = request_geometry(a, r);
+    if (g.L > 0) atomicMax(&s_max, 1 + (max(g.S, 0) + kBN - 1) / kBN);
+  }
+  __syncthreads();
+  int shift = 0;
+  while ((s_max >> shift) >= kSortBuckets) ++shift;
+  auto bucket = [&](const ReqGeom& g, int qt) {
+    const int cost = 1 + (visible_keys(g, qt * kBM) + kBN - 1) / kBN;
+    return kSortBuckets - 1 - min(cost >> shift, kSortBuckets - 1);
+  };
+  for (int r = tid; r < a.num_seqs; r += 256) {
+    const ReqGeom g = request_geometry(a, r);
+    for (int qt = 0; qt * kBM < g.L; ++qt) atomicAdd(&s_hist[bucket(g, qt)], 1);
+  }
+  __syncthreads();
+  // exclusive scan of the histogram: 4 buckets per thread
+  int loc[4], sum = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    loc[i] = sum;
+    sum += s_hist[4 * tid + i];
+  }
+  int v = sum;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int t = __shfl_up(v, o);
+    if (lane >= o) v += t;
+  }
+  __syncthreads();
+  if (lane == 63) s_sum[w] = v;
+  __syncthreads();
+  int before = v - sum;
+  for (int i = 0; i < w; ++i) before += s_sum[i];
+  const int n_items = s_sum[0] + s_sum[1] + s_sum[2] + s_sum[3];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) s_hist[4 * tid + i] = before + loc[i];
+  __syncthreads();
+  // placement (the order within a bucket is arbitrary: each item's result
+  // does not depend on where it runs)
+  for (int r = tid; r < a.num_seqs; r += 256) {
+    const ReqGeom g = request_geometry(a, r);
+    for (int qt = 0; qt * kBM < g.L; ++qt) {
+      const int pos = atomicAdd(&s_hist[bucket(g, qt)], 1);
+      if (pos < a.item_cap) reinterpret_cast<int2*>(a.items)[pos] = make_int2(r, qt);
+    }
+  }
+  if (tid == 0) *a.n_items = min(n_items, a.item_cap);
+}
+
+// ------------------------------------------------------------- attention kernel
 __global__ __launch_bounds__(256, 2) void mla_attn_kernel(MlaPrefill a) {
   __shared__ __align__(16) char smem[2 * kAStage];
   const int lane = threadIdx.x & 63;
   const int wave = wave_id();
   const int H = a.num_heads;
-  // work-group -> (request, head, q tile): the q tiles of one (request, head)
-  // pair run on one XCD, longest first
-  const int n_qt = (a.max_query_len + kBM - 1) / kBM;
+  // work-group -> (item of the work list, head): items longest first, the
+  // heads of an item consecutive (with H a multiple of 8, head h of every
+  // item runs on XCD h % 8, where its expanded rows stay in L2)
   const int id = blockIdx.x;
-  const int xcd = id % kXcds, slot = id / kXcds;
-  const int pair = (slot / n_qt) * kXcds + xcd;
-  if (pair >= a.num_seqs * H) return;
-  const int r = pair / H, h = pair % H;
-  const int qt = n_qt - 1 - slot % n_qt;
-  const int q_start = min(max(a.query_start_loc[r], 0), a.num_tokens);
-  const int L = min(min(a.query_start_loc[r + 1] - q_start, a.max_query_len), a.num_tokens - q_start);
-  // key rows of the request in the expanded buffers (clamped to the rows the
-  // expansion wrote)
-  const int ks = min(a.key_start[r], a.total_keys);
-  const int S = min(a.key_start[r + 1], a.total_keys) - ks;
+  const int item = id / H, h = id % H;
+  if (item >= *a.n_items) return;
+  const int2 it = reinterpret_cast<const int2*>(a.items)[item];
+  const int r = it.x, qt = it.y;
+  const ReqGeom geom = request_geometry(a, r);
+  const int q_start = geom.q_start, L = geom.L, ks = geom.ks, S = geom.S;
   const int q0 = qt * kBM;
   if (q0 >= L || L <= 0) return;
   const int C = S - L;
-  const int kv_end = min(S, max(0, C + min(q0 + kBM, L)));
+  const int kv_end = visible_keys(geom, q0);
   const int n_tiles = (kv_end + kBN - 1) / kBN;
 
   // ---- Q fragments: nope dims 16 kk + 8 (l / 32), rope dims likewise
@@ -376,30 +455,60 @@ __global__ __launch_bounds__(256, 2) void mla_attn_kernel(MlaPrefill a) {
   const char* vbase = static_cast<const char*>(a.v_exp) + (int64_t(ks) * H + h) * (kDv * 2);
   const int64_t kstride = int64_t(H) * kDq * 2, vstride = int64_t(H) * kDv * 2;
   typedef __attribute__((address_space(3))) void* lds_ptr;
+  // Lane offsets of the DMA loads within a tile of 64 keys: nope and value
+  // rows (4 rows x 256 B per load, wave w: loads w + 4 jj), rope rows (8 rows
+  // x 128 B).  A full tile adds only a scalar base; the last tile clamps rows
+  // past its end to the last visible key.
+  uint32_t koff[4], voff[4], poff[2];
+  int krow[4], prow[2];
+#pragma unroll
+  for (int jj = 0; jj < 4; ++jj) {
+    const int row = 4 * (wave + 4 * jj) + (lane >> 4);
+    const int c = (lane & 15) ^ swz(row);
+    krow[jj] = row;
+    koff[jj] = uint32_t(row * kstride + 16 * c);
+    voff[jj] = uint32_t(row * vstride + 16 * c);
+  }
+#pragma unroll
+  for (int jj = 0; jj < 2; ++jj) {
+    const int row = 8 * (wave + 4 * jj) + (lane >> 3);
+    prow[jj] = row;
+    poff[jj] = uint32_t(row * kstride + kNRow + 16 * pslot(row, lane & 7));
+  }
   auto gload = [&](int tile, char* dst) {
     char* dk = dst;
     char* dv = dst + kNTile;
     char* dp = dst + 2 * kNTile;
     const int key0 = tile * kBN;
-    // nope and value rows: 16 loads of 4 rows x 256 B (wave w: w + 4 jj)
+    const char* kb = kbase + int64_t(key0) * kstride;
+    const char* vb = vbase + int64_t(key0) * vstride;
+    if (key0 + kBN <= kv_end) {
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      const int j = wave + 4 * jj;
-      const int row = 4 * j + (lane >> 4);
-      const int key = min(key0 + row, kv_end - 1);   // past the end: re-read the last key
-      const int c = (lane & 15) ^ swz(row);
-      __builtin_amdgcn_global_load_lds(kbase + key * kstride + 16 * c, (lds_ptr)(dk + 1024 * j), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(vbase + key * vstride + 16 * c, (lds_ptr)(dv + 1024 * j), 16, 0, 0);
-    }
-    // rope rows: 8 loads of 8 rows x 128 B (wave w: w + 4 jj)
+      for (int jj = 0; jj < 4; ++jj) {
+        const int j = wave + 4 * jj;
+        __builtin_amdgcn_global_load_lds(kb + koff[jj], (lds_ptr)(dk + 1024 * j), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(vb + voff[jj], (lds_ptr)(dv + 1024 * j), 16, 0, 0);
+      }
 #pragma unroll
-    for (int jj = 0; jj < 2; ++jj) {
-      const int j = wave + 4 * jj;
-      const int row = 8 * j + (lane >> 3);
-      const int key = min(key0 + row, kv_end - 1);
-      const int c = pslot(row, lane & 7);
-      __builtin_amdgcn_global_load_lds(kbase + key * kstride + kNRow + 16 * c,
-                                       (lds_ptr)(dp + 1024 * j), 16, 0, 0);
+      for (int jj = 0; jj < 2; ++jj)
+        __builtin_amdgcn_global_load_lds(kb + poff[jj], (lds_ptr)(dp + 1024 * (wave + 4 * jj)), 16, 0, 0);
+    } else {
+      const int last = kv_end - 1 - key0;   // rows past it re-read the last visible key
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int j = wave + 4 * jj;
+        const int back = krow[jj] - min(krow[jj], last);
+        __builtin_amdgcn_global_load_lds(kb + (koff[jj] - uint32_t(back * kstride)),
+                                         (lds_ptr)(dk + 1024 * j), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(vb + (voff[jj] - uint32_t(back * vstride)),
+                                         (lds_ptr)(dv + 1024 * j), 16, 0, 0);
+      }
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj) {
+        const int back = prow[jj] - min(prow[jj], last);
+        __builtin_amdgcn_global_load_lds(kb + (poff[jj] - uint32_t(back * kstride)),
+                                         (lds_ptr)(dp + 1024 * (wave + 4 * jj)), 16, 0, 0);
+      }
     }
   };
   auto gwait = [&]() { __builtin_amdgcn_s_waitcnt(0x0F70); };
@@ -582,7 +691,7 @@ __global__ __launch_bounds__(256, 2) void mla_attn_kernel(MlaPrefill a) {
 
 hipError_t launch_mla_prefill(const MlaPrefill& a, hipStream_t s) {
   if (a.num_seqs <= 0 || a.num_tokens <= 0) return hipSuccess;
-  hipLaunchKernelGGL(key_start_kernel, dim3(1), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(mla_schedule_kernel, dim3(1), dim3(256), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (a.total_keys > 0) {
@@ -595,8 +704,8 @@ hipError_t launch_mla_prefill(const MlaPrefill& a, hipStream_t s) {
   }
   if (a.max_query_len <= 0) return hipSuccess;
   const int64_t n_qt = (a.max_query_len + kBM - 1) / kBM;
-  const int64_t pairs = int64_t(a.num_seqs) * a.num_heads;
-  const int64_t wgs = (pairs + kXcds - 1) / kXcds * kXcds * n_qt;
+  const int64_t items = std::min<int64_t>(int64_t(a.num_seqs) * n_qt, a.item_cap);
+  const int64_t wgs = items * a.num_heads;
   if (wgs > INT32_MAX) return hipErrorInvalidValue;
   hipLaunchKernelGGL(mla_attn_kernel, dim3(unsigned(wgs)), dim3(256), 0, s, a);
   return hipGetLastError();

@@ -339,7 +339,10 @@ def test_fp8_mla_validation(lib):
 def test_mla_prefill_validation(lib):
     f = lib.pa_mla_prefill
     need = pa.mla_prefill_workspace_bytes(2, 700, 16)
-    assert need == 256 + ((700 * 16 * 192 * 2 + 255) // 256) * 256 + ((700 * 16 * 128 * 2 + 255) // 256) * 256
+    up = lambda x: (x + 255) // 256 * 256
+    # key offsets + list length, work list (2 + 700 // 128 + 1 entries of 8 B),
+    # projected keys, projected values
+    assert need == up(4 * 4) + up(8 * 8) + up(700 * 16 * 192 * 2) + up(700 * 16 * 128 * 2)
     #       q  qst       qsh  kv_c  k_pe  cache nb  bs  table maxb slots qsl seq N  T    maxq keys
     base = [1, 16 * 192, 192, None, None, 2, 100, 64, 3, 64, None, 4, 5, 2, 300, 200, 700,
             7, 16, 512, 64, 128, 128, 0.07, 1 << 20, need, 6, None, None]
