@@ -14,9 +14,10 @@
 // Three kernels:
 // * mla_schedule_kernel: cumulative key counts of the requests (one block
 //   scan), then the attention's work list: every (request, 128-query tile)
-//   item, longest first (counting sort on the number of 64-key tiles the item
-//   visits), so that the long items start early and the short ones fill the
-//   tail.
+//   item, requests longest first (counting sort on the key tiles of their last
+//   q tile), a request's q tiles together and longest first, so that the long
+//   items start early, the short ones fill the tail, and the q tiles sharing
+//   keys run close together.
 // * mla_expand_kernel: the projection of every key of the batch, a bf16 GEMM
 //   E^T[n][g] = sum_k W[n][k] L[g][k] over the gathered latent rows L (n = a
 //   projection output of one head, g = a key of the batch), 128 x 256 tiles on
@@ -361,9 +362,11 @@ __global__ __launch_bounds__(256) void mla_schedule_kernel(MlaPrefill a) {
   for (int i = tid; i < kSortBuckets; i += 256) s_hist[i] = 0;
   __syncthreads();   // also orders the key offsets above before the reads below
 
-  // sort key of an item: 1 + its 64-key tiles (largest at a request's last
-  // q tile), coarsened by a shift so that the largest fits the buckets;
-  // bucket 0 holds the longest items
+  // Requests longest first, each request's q tiles together (last, longest,
+  // first): the sort key of a request is 1 + the 64-key tiles its last q tile
+  // visits, coarsened by a shift so that the largest fits the buckets; bucket
+  // 0 holds the longest.  Keeping a request's tiles together keeps its
+  // expanded keys and values in L2 while they run.
   for (int r = tid; r < a.num_seqs; r += 256) {
     const ReqGeom g = request_geometry(a, r);
     if (g.L > 0) atomicMax(&s_max, 1 + (max(g.S, 0) + kBN - 1) / kBN);
@@ -371,16 +374,18 @@ __global__ __launch_bounds__(256) void mla_schedule_kernel(MlaPrefill a) {
   __syncthreads();
   int shift = 0;
   while ((s_max >> shift) >= kSortBuckets) ++shift;
-  auto bucket = [&](const ReqGeom& g, int qt) {
-    const int cost = 1 + (visible_keys(g, qt * kBM) + kBN - 1) / kBN;
+  auto bucket = [&](const ReqGeom& g) {
+    const int cost = 1 + (max(g.S, 0) + kBN - 1) / kBN;
     return kSortBuckets - 1 - min(cost >> shift, kSortBuckets - 1);
   };
+  auto q_tiles = [&](const ReqGeom& g) { return g.L > 0 ? (g.L + kBM - 1) / kBM : 0; };
   for (int r = tid; r < a.num_seqs; r += 256) {
     const ReqGeom g = request_geometry(a, r);
-    for (int qt = 0; qt * kBM < g.L; ++qt) atomicAdd(&s_hist[bucket(g, qt)], 1);
+    const int nq = q_tiles(g);
+    if (nq > 0) atomicAdd(&s_hist[bucket(g)], nq);
   }
   __syncthreads();
-  // exclusive scan of the histogram: 4 buckets per thread
+  // exclusive scan of the histogram (in items): 4 buckets per thread
   int loc[4], sum = 0;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -402,14 +407,15 @@ __global__ __launch_bounds__(256) void mla_schedule_kernel(MlaPrefill a) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) s_hist[4 * tid + i] = before + loc[i];
   __syncthreads();
-  // placement (the order within a bucket is arbitrary: each item's result
-  // does not depend on where it runs)
+  // placement (the order of requests within a bucket is arbitrary: each
+  // item's result does not depend on where it runs)
   for (int r = tid; r < a.num_seqs; r += 256) {
     const ReqGeom g = request_geometry(a, r);
-    for (int qt = 0; qt * kBM < g.L; ++qt) {
-      const int pos = atomicAdd(&s_hist[bucket(g, qt)], 1);
-      if (pos < a.item_cap) reinterpret_cast<int2*>(a.items)[pos] = make_int2(r, qt);
-    }
+    const int nq = q_tiles(g);
+    if (nq == 0) continue;
+    const int pos = atomicAdd(&s_hist[bucket(g)], nq);
+    for (int i = 0; i < nq && pos + i < a.item_cap; ++i)
+      reinterpret_cast<int2*>(a.items)[pos + i] = make_int2(r, nq - 1 - i);
   }
   if (tid == 0) *a.n_items = min(n_items, a.item_cap);
 }
@@ -545,32 +551,33 @@ __global__ __launch_bounds__(256, 2) void mla_attn_kernel(MlaPrefill a) {
       // 12 k-steps (8 over the nope tile, 4 over rope), the two 32-key halves
       // a constant offset apart; reads one step ahead of the MFMAs, issued as
       // inline assembly (see the expansion) and waited for explicitly
+      // kQD k-steps of reads in flight ahead of the MFMAs (LDS latency is
+      // longer than the two MFMAs of a step)
+      constexpr int kQD = 2;
       const int kr = lane & 31, hi = lane >> 5;
-      u32x4_t kf[2][2];
+      u32x4_t kf[kQD + 1][2];
       auto issue = [&](auto kc) {
-        constexpr int kk = decltype(kc)::value;
+        constexpr int kk = decltype(kc)::value, b = kk % (kQD + 1);
         if constexpr (kk < 8) {
           const char* p = kt + kr * kNRow + 16 * ((2 * kk + hi) ^ swz(kr));
-          kf[kk & 1][0] = lds_read16_issue<0>(p);
-          kf[kk & 1][1] = lds_read16_issue<32 * kNRow>(p);
+          kf[b][0] = lds_read16_issue<0>(p);
+          kf[b][1] = lds_read16_issue<32 * kNRow>(p);
         } else {
           const char* p = pt + kr * kPRow + 16 * pslot(kr, 2 * (kk - 8) + hi);
-          kf[kk & 1][0] = lds_read16_issue<0>(p);
-          kf[kk & 1][1] = lds_read16_issue<32 * kPRow>(p);
+          kf[b][0] = lds_read16_issue<0>(p);
+          kf[b][1] = lds_read16_issue<32 * kPRow>(p);
         }
       };
-      issue(std::integral_constant<int, 0>{});
+      static_for<kQD>([&](auto kc) { issue(kc); });
       static_for<12>([&](auto kc) {
-        constexpr int kk = decltype(kc)::value;
-        if constexpr (kk + 1 < 12) {
-          issue(std::integral_constant<int, kk + 1>{});
-          lds_wait<2>(kf[kk & 1][0], kf[kk & 1][1]);
-        } else {
-          lds_wait<0>(kf[kk & 1][0], kf[kk & 1][1]);
-        }
+        constexpr int kk = decltype(kc)::value, b = kk % (kQD + 1);
+        if constexpr (kk + kQD < 12) issue(std::integral_constant<int, kk + kQD>{});
+        // reads of the later steps still in flight: 2 per step
+        constexpr int kLater = 2 * (kk + kQD < 12 ? kQD : 11 - kk);
+        lds_wait<kLater>(kf[b][0], kf[b][1]);
         const u32x4_t& qk = kk < 8 ? qf[kk < 8 ? kk : 0] : qr[kk < 8 ? 0 : kk - 8];
-        s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kf[kk & 1][0]), as_bf16x8(qk), s[0], 0, 0, 0);
-        s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kf[kk & 1][1]), as_bf16x8(qk), s[1], 0, 0, 0);
+        s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kf[b][0]), as_bf16x8(qk), s[0], 0, 0, 0);
+        s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kf[b][1]), as_bf16x8(qk), s[1], 0, 0, 0);
       });
     }
 
@@ -641,22 +648,21 @@ __global__ __launch_bounds__(256, 2) void mla_attn_kernel(MlaPrefill a) {
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt)
         vb[e][dt] = vt + (vr0 + 8 * e) * kNRow + 16 * ((4 * dt + c0) ^ swz(vr0 + 8 * e)) + 8 * (gi & 1);
-    u32x2_t vr[2][2];
+    // kVD steps of transposing reads in flight ahead of the MFMAs
+    constexpr int kVD = 4;
+    u32x2_t vr[kVD + 1][2];
     auto vissue = [&](auto ic) {
-      constexpr int i = decltype(ic)::value, ks4 = i / 4, dt = i % 4;
-      vr[i & 1][0] = lds_read_tr_issue<16 * ks4 * kNRow>(vb[0][dt]);
-      vr[i & 1][1] = lds_read_tr_issue<16 * ks4 * kNRow>(vb[1][dt]);
+      constexpr int i = decltype(ic)::value, ks4 = i / 4, dt = i % 4, b = i % (kVD + 1);
+      vr[b][0] = lds_read_tr_issue<16 * ks4 * kNRow>(vb[0][dt]);
+      vr[b][1] = lds_read_tr_issue<16 * ks4 * kNRow>(vb[1][dt]);
     };
-    vissue(std::integral_constant<int, 0>{});
+    static_for<kVD>([&](auto ic) { vissue(ic); });
     static_for<16>([&](auto ic) {
-      constexpr int i = decltype(ic)::value, ks4 = i / 4, dt = i % 4;
-      if constexpr (i + 1 < 16) {
-        vissue(std::integral_constant<int, i + 1>{});
-        lds_wait<2>(vr[i & 1][0], vr[i & 1][1]);
-      } else {
-        lds_wait<0>(vr[i & 1][0], vr[i & 1][1]);
-      }
-      const u32x4_t vf = u32x4_t{vr[i & 1][0].x, vr[i & 1][0].y, vr[i & 1][1].x, vr[i & 1][1].y};
+      constexpr int i = decltype(ic)::value, ks4 = i / 4, dt = i % 4, b = i % (kVD + 1);
+      if constexpr (i + kVD < 16) vissue(std::integral_constant<int, i + kVD>{});
+      constexpr int kLater = 2 * (i + kVD < 16 ? kVD : 15 - i);
+      lds_wait<kLater>(vr[b][0], vr[b][1]);
+      const u32x4_t vf = u32x4_t{vr[b][0].x, vr[b][0].y, vr[b][1].x, vr[b][1].y};
       acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vf), as_bf16x8(pf[ks4]), acc[dt], 0, 0, 0);
     });
 
