@@ -294,32 +294,30 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillVarlen a) {
     // S^T for two 32-key halves (two independent accumulation chains).  Chunk
     // 2 kk + (l / 32) of row 32 hh + l % 32 sits in slot (2 kk + l / 32) ^
     // swz(l % 32); the second half is a constant 32 rows further.  The LDS
-    // reads run one k-step ahead of the MFMAs.
+    // reads run two k-steps ahead of the MFMAs.
     f32x16_t s[2];
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
       for (int i = 0; i < 16; ++i) s[hh][i] = 0.0f;
     {
+      constexpr int kQD = 2;   // k-steps of reads in flight ahead of the MFMAs
       const char* krow = kt + (lane & 31) * kRowBytes;
-      u32x4_t kr[2][2];
+      u32x4_t kr[kQD + 1][2];
       auto issue = [&](auto kc) {
-        constexpr int kk = decltype(kc)::value;
+        constexpr int kk = decltype(kc)::value, b = kk % (kQD + 1);
         const char* p = krow + 16 * ((2 * kk + (lane >> 5)) ^ swz(lane & 31));
-        kr[kk & 1][0] = lds_read16_issue<0>(p);
-        kr[kk & 1][1] = lds_read16_issue<32 * kRowBytes>(p);
+        kr[b][0] = lds_read16_issue<0>(p);
+        kr[b][1] = lds_read16_issue<32 * kRowBytes>(p);
       };
-      issue(std::integral_constant<int, 0>{});
+      static_for<kQD>([&](auto kc) { issue(kc); });
       static_for<8>([&](auto kc) {
-        constexpr int kk = decltype(kc)::value;
-        if constexpr (kk + 1 < 8) {
-          issue(std::integral_constant<int, kk + 1>{});
-          lds_wait<2>(kr[kk & 1][0], kr[kk & 1][1]);
-        } else {
-          lds_wait<0>(kr[kk & 1][0], kr[kk & 1][1]);
-        }
-        s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kr[kk & 1][0]), as_bf16x8(qf[kk]), s[0], 0, 0, 0);
-        s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kr[kk & 1][1]), as_bf16x8(qf[kk]), s[1], 0, 0, 0);
+        constexpr int kk = decltype(kc)::value, b = kk % (kQD + 1);
+        if constexpr (kk + kQD < 8) issue(std::integral_constant<int, kk + kQD>{});
+        constexpr int kLater = 2 * (kk + kQD < 8 ? kQD : 7 - kk);   // 2 reads per later step
+        lds_wait<kLater>(kr[b][0], kr[b][1]);
+        s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kr[b][0]), as_bf16x8(qf[kk]), s[0], 0, 0, 0);
+        s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kr[b][1]), as_bf16x8(qf[kk]), s[1], 0, 0, 0);
       });
     }
 
@@ -406,23 +404,21 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillVarlen a) {
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt)
         vb[e][dt] = vt + (vr0 + 8 * e) * kRowBytes + 16 * ((4 * dt + c0) ^ swz(vr0 + 8 * e)) + 8 * (gi & 1);
-    // (ks, dt) steps in order, the two reads of a step issued one step ahead
-    u32x2_t vr[2][2];
+    // (ks, dt) steps in order, the two reads of a step issued kVD steps ahead
+    constexpr int kVD = 4;
+    u32x2_t vr[kVD + 1][2];
     auto vissue = [&](auto ic) {
-      constexpr int i = decltype(ic)::value, ks = i / 4, dt = i % 4;
-      vr[i & 1][0] = lds_read_tr_issue<16 * ks * kRowBytes>(vb[0][dt]);
-      vr[i & 1][1] = lds_read_tr_issue<16 * ks * kRowBytes>(vb[1][dt]);
+      constexpr int i = decltype(ic)::value, ks = i / 4, dt = i % 4, b = i % (kVD + 1);
+      vr[b][0] = lds_read_tr_issue<16 * ks * kRowBytes>(vb[0][dt]);
+      vr[b][1] = lds_read_tr_issue<16 * ks * kRowBytes>(vb[1][dt]);
     };
-    vissue(std::integral_constant<int, 0>{});
+    static_for<kVD>([&](auto ic) { vissue(ic); });
     static_for<16>([&](auto ic) {
-      constexpr int i = decltype(ic)::value, ks = i / 4, dt = i % 4;
-      if constexpr (i + 1 < 16) {
-        vissue(std::integral_constant<int, i + 1>{});
-        lds_wait<2>(vr[i & 1][0], vr[i & 1][1]);
-      } else {
-        lds_wait<0>(vr[i & 1][0], vr[i & 1][1]);
-      }
-      const u32x2_t v1 = vr[i & 1][0], v2 = vr[i & 1][1];
+      constexpr int i = decltype(ic)::value, ks = i / 4, dt = i % 4, b = i % (kVD + 1);
+      if constexpr (i + kVD < 16) vissue(std::integral_constant<int, i + kVD>{});
+      constexpr int kLater = 2 * (i + kVD < 16 ? kVD : 15 - i);
+      lds_wait<kLater>(vr[b][0], vr[b][1]);
+      const u32x2_t v1 = vr[b][0], v2 = vr[b][1];
       const u32x4_t vf = u32x4_t{v1.x, v1.y, v2.x, v2.y};
       acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vf), as_bf16x8(pf[ks]), acc[dt], 0, 0, 0);
     });
