@@ -568,6 +568,10 @@ __global__ __launch_bounds__(256, 2) void mla_attn_kernel(MlaPrefill a) {
           kf[b][1] = lds_read16_issue<32 * kPRow>(p);
         }
       };
+      // the MFMA phases run at raised wave priority: of the two work-groups
+      // sharing a SIMD, the one issuing MFMAs keeps the matrix unit fed and
+      // the other's softmax takes the free issue slots
+      __builtin_amdgcn_s_setprio(1);
       static_for<kQD>([&](auto kc) { issue(kc); });
       static_for<12>([&](auto kc) {
         constexpr int kk = decltype(kc)::value, b = kk % (kQD + 1);
@@ -581,6 +585,7 @@ __global__ __launch_bounds__(256, 2) void mla_attn_kernel(MlaPrefill a) {
       });
     }
 
+    __builtin_amdgcn_s_setprio(0);
     // online softmax (lazy rescale as in the varlen prefill kernel)
     const bool need_mask = (key0 + kBN > kv_end) || (key0 + kBN - 1 > C + q0 + wave * 32);
     u32x4_t pf[4];
@@ -656,6 +661,7 @@ __global__ __launch_bounds__(256, 2) void mla_attn_kernel(MlaPrefill a) {
       vr[b][0] = lds_read_tr_issue<16 * ks4 * kNRow>(vb[0][dt]);
       vr[b][1] = lds_read_tr_issue<16 * ks4 * kNRow>(vb[1][dt]);
     };
+    __builtin_amdgcn_s_setprio(1);
     static_for<kVD>([&](auto ic) { vissue(ic); });
     static_for<16>([&](auto ic) {
       constexpr int i = decltype(ic)::value, ks4 = i / 4, dt = i % 4, b = i % (kVD + 1);
@@ -666,6 +672,7 @@ __global__ __launch_bounds__(256, 2) void mla_attn_kernel(MlaPrefill a) {
       acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vf), as_bf16x8(pf[ks4]), acc[dt], 0, 0, 0);
     });
 
+    __builtin_amdgcn_s_setprio(0);
     if (t + 1 < n_tiles) {
       // this wave's loads of tile t + 1 have landed; after the barrier
       // everyone's have, and everyone is done reading this tile's buffer
