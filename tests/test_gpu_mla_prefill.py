@@ -3,7 +3,8 @@ write, projection of every key by kv_b_proj, causal attention with 192-wide
 keys and 128-wide values) against the oracle: ragged chunks over contexts
 that span several 128-row query tiles and 64-key tiles with ragged tails,
 one-query and empty requests, head counts 1 to 16, block sizes 16 and 64,
-strided queries, and sampled requests of the full workload."""
+strided queries, a 70000-key context (the work list's coarsened sort), and
+sampled requests of the full workload."""
 import numpy as np
 import pytest
 import torch
@@ -99,6 +100,17 @@ def test_mla_prefill_one_query_matches_latent_decode():
     # query and output): compare against each other at twice the tolerance
     check_close(out, o_dec, "prefill vs decode", atol=2e-2, rtol=2e-2)
     check_lse(lse, lse_d.cpu().numpy().astype(np.float64), "prefill vs decode lse", tol=2e-2)
+
+
+def test_mla_prefill_long_context_coarse_schedule():
+    """A 70000-key context: the work list's sort key (key tiles of a request's
+    last q tile) exceeds the 1024 buckets, so the schedule coarsens it; the
+    result must not change."""
+    say("mla prefill 70000-key context")
+    b = W.make_mla_prefill(840, [64, 1], [70000, 5], 1, 64)
+    _, out, lse = _run(b)
+    _, oref, lref = _oracle(b)
+    _check(b, out, lse, oref, lref, range(b.num_seqs), "long context")
 
 
 def test_mla_prefill_deterministic():
