@@ -73,17 +73,18 @@ __global__ __launch_bounds__(256, 2) void mla_expand_kernel(MlaPrefill a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int H = a.num_heads;
   const int n_tiles = 2 * H;                  // a tile is the key half or the value half of a head
-  // XCD-aware order.  When the n tiles divide over the XCDs, each XCD keeps
-  // its share of W (n_tiles / 8 slices of 128 KiB) in its L2 and walks all
-  // key tiles; otherwise the n tiles of one key tile run on one XCD, one
-  // after another, and share its latent rows there.
+  // XCD-aware order.  When the n tiles divide over the XCDs, XCD x keeps a
+  // quarter of W (n group x % 4) in its L2 and walks half of the key tiles
+  // (x / 4): each latent row is fetched by 4 XCDs, and W plus the latent
+  // tiles in flight fit the 4 MiB L2.  Otherwise the n tiles of one key tile
+  // run on one XCD, one after another, and share its latent rows there.
   const int id = blockIdx.x;
   const int xcd = id % kXcds, slot = id / kXcds;
   int g_tile, n_tile;
   if (n_tiles % kXcds == 0) {
-    const int n_per = n_tiles / kXcds;
-    n_tile = xcd * n_per + slot % n_per;
-    g_tile = slot / n_per;
+    const int n_per = n_tiles / 4;            // 4 groups of n tiles x 2 halves of the key tiles
+    n_tile = (xcd & 3) * n_per + slot % n_per;
+    g_tile = (slot / n_per) * 2 + (xcd >> 2);
   } else {
     g_tile = (slot / n_tiles) * kXcds + xcd;
     n_tile = slot % n_tiles;
