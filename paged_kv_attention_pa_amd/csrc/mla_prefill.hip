@@ -281,7 +281,8 @@ __global__ __launch_bounds__(256, 2) void mla_expand_kernel(MlaPrefill a) {
       for (int u = 0; u < 4; ++u) {
         const int q = tid + 256 * (i0 + u);
         const int g = g0 + (q >> 4);
-        if (g < total) store16(out + int64_t(g) * orow + 16 * (q & 15), v[u]);
+        if (g < total)   // streaming stores: read back only after the whole projection
+          __builtin_nontemporal_store(v[u], reinterpret_cast<u32x4_t*>(out + int64_t(g) * orow + 16 * (q & 15)));
       }
     }
   }
@@ -291,7 +292,8 @@ __global__ __launch_bounds__(256, 2) void mla_expand_kernel(MlaPrefill a) {
       const int q = tid + 256 * i;
       const int g = g0 + (q >> 3);
       if (g < total)
-        store16(static_cast<uint16_t*>(a.k_exp) + int64_t(g) * krow + int64_t(h) * kDq + kDn + 8 * (q & 7), pe[i]);
+        __builtin_nontemporal_store(pe[i], reinterpret_cast<u32x4_t*>(static_cast<uint16_t*>(a.k_exp) + int64_t(g) * krow +
+                                                                       int64_t(h) * kDq + kDn + 8 * (q & 7)));
     }
   }
 }
