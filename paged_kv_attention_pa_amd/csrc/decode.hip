@@ -35,6 +35,8 @@ template <bool kBF16> struct Row8;
 template <> struct Row8<true> {
   u32x4_t w;
   __device__ __forceinline__ void load(const uint16_t* p) { w = load16(p); }
+  // cache rows are read once: non-temporal loads keep them out of L2 / MALL
+  __device__ __forceinline__ void stream(const uint16_t* p) { w = load16_stream(p); }
   __device__ __forceinline__ void zero() { w = u32x4_t{0, 0, 0, 0}; }
   __device__ __forceinline__ float at(int e) const {
     return (e & 1) ? bf16_hi(w[e >> 1]) : bf16_lo(w[e >> 1]);
@@ -43,6 +45,7 @@ template <> struct Row8<true> {
 template <> struct Row8<false> {
   u32x4_t w0, w1;
   __device__ __forceinline__ void load(const float* p) { w0 = load16(p); w1 = load16(p + 4); }
+  __device__ __forceinline__ void stream(const float* p) { w0 = load16_stream(p); w1 = load16_stream(p + 4); }
   __device__ __forceinline__ void zero() { w0 = u32x4_t{0, 0, 0, 0}; w1 = w0; }
   __device__ __forceinline__ float at(int e) const {
     return __uint_as_float(e < 4 ? w0[e] : w1[e - 4]);
@@ -142,8 +145,8 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeGQA a) {
     const T* p = group_ptr(g);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      kc[i].load(p + (4 * i + sub) * tok_stride);
-      vc[i].load(p + kv_stride + (4 * i + sub) * tok_stride);
+      kc[i].stream(p + (4 * i + sub) * tok_stride);
+      vc[i].stream(p + kv_stride + (4 * i + sub) * tok_stride);
     }
   }
   for (; g < n_groups; g += kWaves) {
@@ -152,8 +155,8 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeGQA a) {
       const T* p = group_ptr(gn);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        kn[i].load(p + (4 * i + sub) * tok_stride);
-        vn[i].load(p + kv_stride + (4 * i + sub) * tok_stride);
+        kn[i].stream(p + (4 * i + sub) * tok_stride);
+        vn[i].stream(p + kv_stride + (4 * i + sub) * tok_stride);
       }
     }
     const int tok0 = t0 + g * kGroupTokens;
@@ -353,8 +356,8 @@ __global__ __launch_bounds__(256, 4) void decode_mfma_kernel(DecodeGQA a) {
       for (int i = 0; i < 4; ++i) {
         const int tok = min(tok16 + 4 * i + lt, t1 - 1);
         const int64_t off = (blk * 2 * bs + (tok - page0)) * tok_stride + int64_t(h) * kD + 8 * lc;
-        kr[4 * sub + i] = load16(cache + off);
-        vr[4 * sub + i] = load16(cache + off + kv_stride);
+        kr[4 * sub + i] = load16_stream(cache + off);
+        vr[4 * sub + i] = load16_stream(cache + off + kv_stride);
       }
     }
   };

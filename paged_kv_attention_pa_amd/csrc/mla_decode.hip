@@ -261,11 +261,12 @@ __global__ __launch_bounds__(64 * kWaves, 1) void mla_kernel(MlaDecode a) {
     const bool simple = in0 + kBN <= bs && key0 + kBN <= kend;   // wave-uniform
     typedef __attribute__((address_space(3))) void* lds_ptr;
     char* dst = smem + stage * kTileBytes;
+    // cache policy 2 = non-temporal: every latent row is read once
     if (simple) {
 #pragma unroll
       for (int jj = 0; jj < kLoadsPerWave; ++jj)
         __builtin_amdgcn_global_load_lds(base0 + goff[jj],
-                                         (lds_ptr)(dst + 1024 * (wave + kWaves * jj)), 16, 0, 0);
+                                         (lds_ptr)(dst + 1024 * (wave + kWaves * jj)), 16, 0, 2);
     } else {
       const int last = kend - 1 - key0;             // tile row of key kend - 1
       const char* base1 = reinterpret_cast<const char*>(cache) +
@@ -276,7 +277,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void mla_kernel(MlaDecode a) {
         const int rr = min(row, last);
         const int64_t off = int64_t(goff[jj]) + int64_t(rr - row) * kRowBytes;
         const char* src = (in0 + rr < bs ? base0 : base1) + off;
-        __builtin_amdgcn_global_load_lds(src, (lds_ptr)(dst + 1024 * (wave + kWaves * jj)), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(src, (lds_ptr)(dst + 1024 * (wave + kWaves * jj)), 16, 0, 2);
       }
     }
   };
@@ -311,7 +312,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void mla_kernel(MlaDecode a) {
         const int rr = min(row, last);
         src = (in0 + rr < bs ? base0 : base1) + int64_t(off) + int64_t(rr - row) * kF8Row;
       }
-      __builtin_amdgcn_global_load_lds(src, (lds_ptr)(dst + 1024 * (wave + kWaves * jj)), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(src, (lds_ptr)(dst + 1024 * (wave + kWaves * jj)), 16, 0, 2);
     }
   };
   // tile t's codes have landed for this wave when at most f8_n x (tiles
