@@ -43,7 +43,6 @@ __global__ __launch_bounds__(64 * kHeads, 1) void decode_balanced_kernel(DecodeB
   __shared__ int s_wave_sum[kHeads];
   __shared__ int s_start[2];
   const int tid = threadIdx.x;
-  const int nthr = blockDim.x;
   const int lane = tid & 63;
   const int wave = wave_id();
   const int B = a.num_seqs;

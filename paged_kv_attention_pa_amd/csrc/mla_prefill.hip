@@ -41,7 +41,6 @@ constexpr int kP = 64;           // rope dims
 constexpr int kDn = 128;         // qk_nope dims
 constexpr int kDv = 128;         // v dims
 constexpr int kDq = kDn + kP;    // 192: query / key width
-constexpr int kOut = kDn + kDv;  // 256 projection outputs per head
 constexpr int kLatBytes = (kR + kP) * 2;   // 1152 B per latent row
 constexpr int kXcds = 8;
 
