@@ -56,6 +56,8 @@ CASES = [
     ("block16_h2", [129, 3, 1], [31, 200, 5], 2, 16),
     ("no_context_h16", [200, 128], [0, 0], 16, 64),
     ("odd_heads_h5", [90, 1, 45], [17, 900, 64], 5, 64),
+    # a request with no keys at all and one with keys but no queries
+    ("empty_requests_h8", [5, 0, 0, 9], [0, 0, 3, 0], 8, 16),
 ]
 
 
