@@ -98,6 +98,28 @@ int pa_mla_num_kv_splits(int num_seqs, int max_seq_len, int num_cus);
 /* Compute units of the current HIP device, or -1 if it cannot be queried. */
 int pa_device_num_cus(void);
 
+/* Workspace bytes pa_decode needs when called with these sizes: the
+ * schedule it picks ("Triton 與 MLA", 邊界與失敗: the split count used to
+ * reserve the workspace must be the one the forward pass uses) decides
+ * between no workspace (one split covers max_seq_len), the split partials
+ * (pa_decode_workspace_bytes for n splits) and the token-balanced ranges
+ * (pa_decode_balanced_workspace_bytes).  partials_only != 0 means out =
+ * NULL (the two-stage form).  num_splits = 0 queries the current device's
+ * compute units, as pa_decode does.  On success *bytes holds the size (0 =
+ * none needed).  Errors: PA_ERR_INVALID for a null bytes pointer or sizes
+ * pa_decode would reject on their face (negative counts, block_size not a
+ * positive multiple of 16); PA_ERR_HIP if the device cannot be queried. */
+pa_status_t pa_decode_workspace_size(pa_dtype_t dtype, int num_seqs, int max_seq_len,
+                                     int block_size, int num_q_heads, int num_kv_heads,
+                                     int head_dim, int num_splits, int partials_only,
+                                     size_t* bytes);
+
+/* The same query for pa_mla_decode (bf16 latent cache); head_dim_v is
+ * kv_lora_rank. */
+pa_status_t pa_mla_decode_workspace_size(int num_seqs, int max_seq_len, int block_size,
+                                         int num_heads, int kv_lora_rank, int num_splits,
+                                         int partials_only, size_t* bytes);
+
 /* Thread-local description of the last error ("" if none). */
 const char* pa_last_error(void);
 
@@ -149,12 +171,13 @@ pa_status_t pa_cache_write(pa_layout_t layout, pa_dtype_t dtype,
  *              Split s of a request covers positions [s*P, (s+1)*P) with
  *              P = ceil(max_seq_len / n) rounded up to a multiple of
  *              block_size; splits past the request's end are empty.
- * workspace:   fp32 scratch of at least pa_decode_workspace_bytes(num_seqs,
- *              num_q_heads, head_dim, n) bytes for n splits, or, for the
- *              balanced schedule, pa_decode_balanced_workspace_bytes(num_seqs,
- *              num_q_heads, pa_decode_balanced_num_ranges(num_kv_heads,
- *              pa_device_num_cus())) bytes, 16-byte aligned; may be NULL
- *              when one split covers max_seq_len (then no partials are formed).
+ * workspace:   fp32 scratch of at least pa_decode_workspace_size(...) bytes
+ *              (that is pa_decode_workspace_bytes(num_seqs, num_q_heads,
+ *              head_dim, n) for n splits, or, for the balanced schedule,
+ *              pa_decode_balanced_workspace_bytes(num_seqs, num_q_heads, 128,
+ *              pa_decode_balanced_num_ranges(num_kv_heads,
+ *              pa_device_num_cus()))), 16-byte aligned; may be NULL when one
+ *              split covers max_seq_len (then no partials are formed).
  * out:         [num_seqs, num_q_heads, head_dim], storage dtype; or NULL for
  *              the two-stage form: only stage 1 runs and the workspace holds
  *              the partials [num_seqs, num_q_heads, n, head_dim + 1] (empty

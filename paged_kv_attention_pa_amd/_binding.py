@@ -26,6 +26,10 @@ _SIGNATURES = {
     "pa_decode_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32]),
     "pa_mla_num_kv_splits": (_i32, [_i32, _i32, _i32]),
     "pa_device_num_cus": (_i32, []),
+    "pa_decode_workspace_size": (_i32, [_i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                                        C.POINTER(_sz)]),
+    "pa_mla_decode_workspace_size": (_i32, [_i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                                            C.POINTER(_sz)]),
     "pa_last_error": (C.c_char_p, []),
     "pa_cache_write": (_i32, [_i32, _i32, _vp, _i64, _vp, _i64, _vp, _i64, _i32, _i32, _i32,
                               _vp, _i32, _vp]),
@@ -125,6 +129,30 @@ def mla_num_kv_splits(num_seqs: int, max_seq_len: int, num_cus: int) -> int:
 def decode_workspace_bytes(num_seqs: int, num_q_heads: int, head_dim_v: int, num_splits: int) -> int:
     return library().pa_decode_workspace_bytes(int(num_seqs), int(num_q_heads), int(head_dim_v),
                                                int(num_splits))
+
+
+def decode_workspace_size(dtype: int, num_seqs: int, max_seq_len: int, block_size: int,
+                          num_q_heads: int, num_kv_heads: int, head_dim: int, num_splits: int,
+                          partials_only: bool = False) -> int:
+    """Bytes of workspace ``pa_decode`` needs for these sizes (0 = none)."""
+    n = C.c_size_t(0)
+    _check(library().pa_decode_workspace_size(int(dtype), int(num_seqs), int(max_seq_len),
+                                              int(block_size), int(num_q_heads),
+                                              int(num_kv_heads), int(head_dim), int(num_splits),
+                                              1 if partials_only else 0, C.byref(n)))
+    return n.value
+
+
+def mla_decode_workspace_size(num_seqs: int, max_seq_len: int, block_size: int, num_heads: int,
+                              kv_lora_rank: int, num_splits: int,
+                              partials_only: bool = False) -> int:
+    """Bytes of workspace ``pa_mla_decode`` needs for these sizes (0 = none)."""
+    n = C.c_size_t(0)
+    _check(library().pa_mla_decode_workspace_size(int(num_seqs), int(max_seq_len),
+                                                  int(block_size), int(num_heads),
+                                                  int(kv_lora_rank), int(num_splits),
+                                                  1 if partials_only else 0, C.byref(n)))
+    return n.value
 
 
 def decode_balanced_num_ranges(num_kv_heads: int, num_cus: int) -> int:
@@ -394,15 +422,7 @@ def decode(q, kv_cache, block_table, seq_lens, max_seq_len: int, scale: float,
             out = torch.empty_like(q)
         if lse is None and return_lse:
             lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
-    n = num_splits
-    if n == 0:
-        n = num_kv_splits(max_seq_len, device_num_cus())
-    need = decode_workspace_bytes(B, Hq, D, n) if (n > 1 or stage1_only) else 0
-    if (num_splits == 0 and n > 1 and not stage1_only and dt == PA_BF16
-            and (hkv in (1, 2, 4) or hkv % 8 == 0)):
-        # the automatic schedule is the token-balanced one (pa_decode's rule)
-        need = decode_balanced_workspace_bytes(
-            B, Hq, D, decode_balanced_num_ranges(hkv, device_num_cus()))
+    need = decode_workspace_size(dt, B, max_seq_len, bs, Hq, hkv, D, num_splits, stage1_only)
     if workspace is None and need:
         workspace = torch.empty(need // 4, dtype=torch.float32, device=q.device)
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
@@ -412,6 +432,9 @@ def decode(q, kv_cache, block_table, seq_lens, max_seq_len: int, scale: float,
                                int(num_splits), _ptr(workspace), wbytes, _ptr(out), _ptr(lse),
                                _stream(stream)))
     if stage1_only:
+        n = need // max(1, 4 * B * Hq * (D + 1))    # the split count the call used
+        if workspace is None:
+            return torch.empty((B, Hq, 0, D + 1), dtype=torch.float32, device=q.device)
         return workspace[: B * Hq * n * (D + 1)].view(B, Hq, n, D + 1)
     return out, lse
 
@@ -562,13 +585,7 @@ def mla_decode(q_nope, q_pe, kv_cache, block_table, seq_lens, max_seq_len: int, 
             out = torch.empty((B, H, R), dtype=q_nope.dtype, device=q_nope.device)
         if lse is None and return_lse:
             lse = torch.empty((B, H), dtype=torch.float32, device=q_nope.device)
-    n = num_splits
-    if n == 0:
-        n = mla_num_kv_splits(B, max_seq_len, device_num_cus())
-    need = decode_workspace_bytes(B, H, R, n) if (n > 1 or stage1_only) else 0
-    if num_splits == 0 and n > 1 and not stage1_only:
-        # the automatic schedule is the token-balanced one, one range per CU
-        need = decode_balanced_workspace_bytes(B, H, R, device_num_cus())
+    need = mla_decode_workspace_size(B, max_seq_len, bs, H, R, num_splits, stage1_only)
     if workspace is None and need:
         workspace = torch.empty(need // 4, dtype=torch.float32, device=q_nope.device)
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
@@ -580,6 +597,9 @@ def mla_decode(q_nope, q_pe, kv_cache, block_table, seq_lens, max_seq_len: int, 
                                    int(num_splits), _ptr(workspace), wbytes, _ptr(out), _ptr(lse),
                                    _stream(stream)))
     if stage1_only:
+        n = need // max(1, 4 * B * H * (R + 1))     # the split count the call used
+        if workspace is None:
+            return torch.empty((B, H, 0, R + 1), dtype=torch.float32, device=q_nope.device)
         return workspace[: B * H * n * (R + 1)].view(B, H, n, R + 1)
     return out, lse
 

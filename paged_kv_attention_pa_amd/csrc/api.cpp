@@ -115,6 +115,79 @@ pa_status_t check_balanced(int num_seqs, int num_heads, int head_dim_v, int max_
   return PA_OK;
 }
 
+// The schedule pa_decode / pa_mla_decode run for given sizes, and the
+// workspace it needs.  One definition serves the entry points and the
+// workspace-size queries, so a caller that sizes its workspace with the
+// query gets exactly what the call checks for.
+struct DecodeSchedule {
+  int n = 1;               // splits (fixed partition)
+  int P = 0;               // tokens per split
+  bool stage1 = false;     // partials only (out == NULL)
+  bool direct = false;     // one split covers every request: no partials
+  bool balanced = false;   // token-balanced ranges + segment merge
+  int nr = 0;              // balanced ranges
+  size_t need = 0;         // workspace bytes
+};
+
+pa_status_t device_cus(int* cus) {
+  *cus = pa_device_num_cus();
+  if (*cus <= 0) return fail(PA_ERR_HIP, "cannot query the device's compute units");
+  return PA_OK;
+}
+
+pa_status_t gqa_decode_schedule(pa_dtype_t dtype, int num_seqs, int max_seq_len, int block_size,
+                                int num_q_heads, int num_kv_heads, int head_dim, int num_splits,
+                                bool stage1, DecodeSchedule* s) {
+  s->n = num_splits;
+  int cus = 0;
+  if (s->n == 0) {
+    pa_status_t st = device_cus(&cus);
+    if (st != PA_OK) return st;
+    s->n = pa_num_kv_splits(max_seq_len, cus);
+  }
+  s->P = split_tokens_for(max_seq_len, s->n, block_size);
+  s->stage1 = stage1;
+  s->direct = !stage1 && used_splits(max_seq_len, s->P) == 1;
+  // automatic schedule with more than one split's worth of keys:
+  // token-balanced ranges instead of per-request splits
+  s->balanced = num_splits == 0 && !stage1 && !s->direct && dtype == PA_BF16 &&
+                balanced_heads_ok(num_kv_heads);
+  s->nr = s->balanced ? pa_decode_balanced_num_ranges(num_kv_heads, cus) : 0;
+  if (s->balanced)
+    s->need = balanced_bytes(num_seqs, num_q_heads, head_dim, s->nr);
+  else if (!s->direct)
+    s->need = pa_decode_workspace_bytes(num_seqs, num_q_heads, head_dim, s->n);
+  else
+    s->need = 0;
+  return PA_OK;
+}
+
+pa_status_t mla_decode_schedule(int num_seqs, int max_seq_len, int block_size, int num_heads,
+                                int kv_lora_rank, int num_splits, bool stage1,
+                                DecodeSchedule* s) {
+  s->n = num_splits;
+  int cus = 0;
+  if (s->n == 0) {
+    pa_status_t st = device_cus(&cus);
+    if (st != PA_OK) return st;
+    s->n = pa_mla_num_kv_splits(num_seqs, max_seq_len, cus);
+  }
+  s->P = split_tokens_for(max_seq_len, s->n, block_size);
+  s->stage1 = stage1;
+  s->direct = !stage1 && used_splits(max_seq_len, s->P) == 1;
+  // automatic schedule with more than one split: token-balanced ranges, one
+  // work-group per compute unit
+  s->balanced = num_splits == 0 && !stage1 && !s->direct;
+  s->nr = s->balanced ? cus : 0;
+  if (s->balanced)
+    s->need = balanced_bytes(num_seqs, num_heads, kv_lora_rank, s->nr);
+  else if (!s->direct)
+    s->need = pa_decode_workspace_bytes(num_seqs, num_heads, kv_lora_rank, s->n);
+  else
+    s->need = 0;
+  return PA_OK;
+}
+
 int32_t* balanced_cu(void* ws) { return static_cast<int32_t*>(ws); }
 float* balanced_part(void* ws, int num_seqs) {
   return reinterpret_cast<float*>(static_cast<char*>(ws) + pa::balanced_cu_bytes(num_seqs));
@@ -166,6 +239,46 @@ int pa_device_num_cus(void) {
 }
 
 const char* pa_last_error(void) { return g_err; }
+
+pa_status_t pa_decode_workspace_size(pa_dtype_t dtype, int num_seqs, int max_seq_len,
+                                     int block_size, int num_q_heads, int num_kv_heads,
+                                     int head_dim, int num_splits, int partials_only,
+                                     size_t* bytes) {
+  PA_REQUIRE(bytes != nullptr, PA_ERR_INVALID, "bytes must be non-null");
+  *bytes = 0;
+  PA_REQUIRE(num_seqs >= 0 && max_seq_len >= 0 && num_splits >= 0, PA_ERR_INVALID,
+             "num_seqs, max_seq_len and num_splits must be >= 0");
+  PA_REQUIRE(block_size > 0 && block_size % 16 == 0, PA_ERR_INVALID,
+             "block_size must be a positive multiple of 16 (got %d)", block_size);
+  PA_REQUIRE(num_q_heads > 0 && num_kv_heads > 0 && head_dim > 0, PA_ERR_INVALID,
+             "head counts and head_dim must be positive");
+  DecodeSchedule sc;
+  pa_status_t st = gqa_decode_schedule(dtype, num_seqs, max_seq_len, block_size, num_q_heads,
+                                       num_kv_heads, head_dim, num_splits, partials_only != 0,
+                                       &sc);
+  if (st != PA_OK) return st;
+  *bytes = sc.need;
+  return ok();
+}
+
+pa_status_t pa_mla_decode_workspace_size(int num_seqs, int max_seq_len, int block_size,
+                                         int num_heads, int kv_lora_rank, int num_splits,
+                                         int partials_only, size_t* bytes) {
+  PA_REQUIRE(bytes != nullptr, PA_ERR_INVALID, "bytes must be non-null");
+  *bytes = 0;
+  PA_REQUIRE(num_seqs >= 0 && max_seq_len >= 0 && num_splits >= 0, PA_ERR_INVALID,
+             "num_seqs, max_seq_len and num_splits must be >= 0");
+  PA_REQUIRE(block_size > 0 && block_size % 16 == 0, PA_ERR_INVALID,
+             "block_size must be a positive multiple of 16 (got %d)", block_size);
+  PA_REQUIRE(num_heads > 0 && kv_lora_rank > 0, PA_ERR_INVALID,
+             "num_heads and kv_lora_rank must be positive");
+  DecodeSchedule sc;
+  pa_status_t st = mla_decode_schedule(num_seqs, max_seq_len, block_size, num_heads,
+                                       kv_lora_rank, num_splits, partials_only != 0, &sc);
+  if (st != PA_OK) return st;
+  *bytes = sc.need;
+  return ok();
+}
 
 // ---------------------------------------------------------------------------
 pa_status_t pa_cache_write(pa_layout_t layout, pa_dtype_t dtype,
@@ -243,29 +356,20 @@ pa_status_t pa_decode(pa_dtype_t dtype,
   PA_REQUIRE(out != nullptr || lse == nullptr, PA_ERR_INVALID,
              "lse without out: the partial-only mode (out = NULL) returns no lse");
 
-  int n = num_splits;
-  int cus = 0;
-  if (n == 0) {
-    cus = pa_device_num_cus();
-    if (cus <= 0) return fail(PA_ERR_HIP, "cannot query the device's compute units");
-    n = pa_num_kv_splits(max_seq_len, cus);
-  }
-  const int P = split_tokens_for(max_seq_len, n, block_size);
-  const bool stage1 = (out == nullptr);            // partials only, for pa_lse_merge
-  const bool direct = !stage1 && used_splits(max_seq_len, P) == 1;
-  // Automatic schedule with more than one split's worth of keys: token-balanced
-  // ranges instead of per-request splits.
-  const bool balanced = num_splits == 0 && !stage1 && !direct && dtype == PA_BF16 &&
-                        balanced_heads_ok(num_kv_heads);
-  const int nr = balanced ? pa_decode_balanced_num_ranges(num_kv_heads, cus) : 0;
+  DecodeSchedule sc;
+  st = gqa_decode_schedule(dtype, num_seqs, max_seq_len, block_size, num_q_heads, num_kv_heads,
+                           head_dim, num_splits, out == nullptr, &sc);
+  if (st != PA_OK) return st;
+  const int n = sc.n, P = sc.P, nr = sc.nr;
+  const bool stage1 = sc.stage1, direct = sc.direct, balanced = sc.balanced;
   if (balanced) {
     st = check_balanced(num_seqs, num_q_heads, head_dim, max_blocks_per_seq, block_size, nr,
                         workspace, workspace_bytes);
     if (st != PA_OK) return st;
   } else if (!direct) {
-    const size_t need = pa_decode_workspace_bytes(num_seqs, num_q_heads, head_dim, n);
-    PA_REQUIRE(workspace != nullptr && workspace_bytes >= need, PA_ERR_WORKSPACE,
-               "workspace of %zu bytes needed for %d splits (got %zu)", need, n, workspace_bytes);
+    PA_REQUIRE(workspace != nullptr && workspace_bytes >= sc.need, PA_ERR_WORKSPACE,
+               "workspace of %zu bytes needed for %d splits (got %zu)", sc.need, n,
+               workspace_bytes);
   }
 
   if (k) {
@@ -515,27 +619,20 @@ pa_status_t pa_mla_decode(const void* q_nope, int64_t qn_stride_b, int64_t qn_st
   PA_REQUIRE(q_nope && q_pe && kv_cache, PA_ERR_INVALID, "q_nope, q_pe and kv_cache must be non-null");
   PA_REQUIRE(out != nullptr || lse == nullptr, PA_ERR_INVALID,
              "lse without out: the partial-only mode (out = NULL) returns no lse");
-  int n = num_splits;
-  int cus = 0;
-  if (n == 0) {
-    cus = pa_device_num_cus();
-    if (cus <= 0) return fail(PA_ERR_HIP, "cannot query the device's compute units");
-    n = pa_mla_num_kv_splits(num_seqs, max_seq_len, cus);
-  }
-  const int P = split_tokens_for(max_seq_len, n, block_size);
-  const bool stage1 = (out == nullptr);
-  const bool direct = !stage1 && used_splits(max_seq_len, P) == 1;
-  // automatic schedule with more than one split: token-balanced ranges, one
-  // work-group per compute unit
-  const bool balanced = num_splits == 0 && !stage1 && !direct;
+  DecodeSchedule sc;
+  st = mla_decode_schedule(num_seqs, max_seq_len, block_size, num_heads, kv_lora_rank, num_splits,
+                           out == nullptr, &sc);
+  if (st != PA_OK) return st;
+  const int n = sc.n, P = sc.P, cus = sc.nr;
+  const bool stage1 = sc.stage1, direct = sc.direct, balanced = sc.balanced;
   if (balanced) {
     st = check_balanced(num_seqs, num_heads, kv_lora_rank, max_blocks_per_seq, block_size, cus,
                         workspace, workspace_bytes);
     if (st != PA_OK) return st;
   } else if (!direct) {
-    const size_t need = pa_decode_workspace_bytes(num_seqs, num_heads, kv_lora_rank, n);
-    PA_REQUIRE(workspace != nullptr && workspace_bytes >= need, PA_ERR_WORKSPACE,
-               "workspace of %zu bytes needed for %d splits (got %zu)", need, n, workspace_bytes);
+    PA_REQUIRE(workspace != nullptr && workspace_bytes >= sc.need, PA_ERR_WORKSPACE,
+               "workspace of %zu bytes needed for %d splits (got %zu)", sc.need, n,
+               workspace_bytes);
   }
   if (kv_c) {
     pa::CacheWriteMLA w{kv_c, kv_lora_rank, k_pe, rope_dim, kv_cache, num_blocks, block_size,

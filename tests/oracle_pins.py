@@ -45,16 +45,20 @@ def pin_bf16_decoding():
     assert np.signbit(got[3])
 
 
-def _go_program_arrays():
+def _paged_program_arrays():
+    """The page's program geometry (block size, dim, pool, table, length) from
+    the golden file, with this project's own seeded keys, values and query."""
     g = _golden("paged_program.json")
+    rng = _rng(29)
     n, dim = g["seqLen"], g["dim"]
-    keys = np.array([[math.sin(i * 3 + d) for d in range(dim)] for i in range(n)])
-    vals = np.array([[math.cos(i * 5 + d * 2) for d in range(dim)] for i in range(n)])
-    return g, keys, vals, np.array(g["q"])
+    keys = rng.standard_normal((n, dim))
+    vals = rng.standard_normal((n, dim))
+    q = rng.standard_normal(dim)
+    return g, keys, vals, q
 
 
-def _go_cache(g, keys, vals, table):
-    """Store the sequence through the page's slot formula, as its main() does."""
+def _paged_program_cache(g, keys, vals, table):
+    """Store the sequence at the slots the page's formula gives."""
     bs, nblk, dim = g["blockSize"], g["numBlocks"], g["dim"]
     cache = np.zeros((nblk, 2, bs, 1, dim))
     slots = np.array([O.slot_of(table, p, bs) for p in range(len(keys))])
@@ -62,11 +66,11 @@ def _go_cache(g, keys, vals, table):
     return cache, slots
 
 
-def pin_go_program_slots():
+def pin_paged_program_slots():
     """The slot ranges the page's program prints for blockTable {6, 1, 4}."""
-    g, keys, vals, _ = _go_program_arrays()
+    g, keys, vals, _ = _paged_program_arrays()
     table = np.array(g["blockTable"])
-    cache, slots = _go_cache(g, keys, vals, table)
+    cache, slots = _paged_program_cache(g, keys, vals, table)
     rng = g["slot_ranges_printed"]
     assert [int(slots[0]), int(slots[3])] == rng["positions 0-3"]
     assert [int(slots[4]), int(slots[7])] == rng["positions 4-7"]
@@ -81,29 +85,19 @@ def pin_go_program_slots():
     assert np.array_equal(k2[:, 0], keys) and np.array_equal(v2[:, 0], vals)
 
 
-def _go_attend(q, keys, vals):
-    """Pure-Python restatement of the page's ``attend``: scaled dot products,
-    max-shifted exponentials, normalised weighted sum (scalar loops)."""
-    dim = len(q)
-    scores = [sum(q[d] * k[d] for d in range(dim)) / math.sqrt(dim) for k in keys]
-    mx = max(scores)
-    ex = [math.exp(s - mx) for s in scores]
-    tot = sum(ex)
-    return [sum(ex[i] / tot * vals[i][d] for i in range(len(vals))) for d in range(dim)]
-
-
-def pin_go_program_identical():
+def pin_paged_program_identical():
     """Paged == contiguous, bit for bit, for the page's table and its Try-it
-    tables; both match the page's scalar algorithm to 1e-14."""
-    g, keys, vals, q = _go_program_arrays()
+    tables; the contiguous result matches torch's float64 attention."""
+    g, keys, vals, q = _paged_program_arrays()
     scale = 1.0 / math.sqrt(g["dim"])
     contiguous, lse_c = O.attention(q[None, None, :], keys[:, None, :], vals[:, None, :],
                                     scale, None)
-    ref = np.array(_go_attend(q.tolist(), keys.tolist(), vals.tolist()))
-    assert np.max(np.abs(contiguous[0, 0] - ref)) < 1e-14, (contiguous, ref)
+    ref = _sdpa(q[None, None, :], keys[:, None, :], vals[:, None, :], scale, None)
+    assert np.max(np.abs(contiguous - ref)) < 1e-14, (contiguous, ref)
+    assert np.max(np.abs(lse_c - _torch_lse(q[None, None, :], keys[:, None, :], scale, None))) < 1e-14
     for table in [g["blockTable"]] + g["try_it_tables"]:
         table = np.array(table)
-        cache, _ = _go_cache(g, keys, vals, table)
+        cache, _ = _paged_program_cache(g, keys, vals, table)
         qsl = np.array([0, 1])
         out, lse = O.paged_attention(q[None, None, :], cache, table[None, :], qsl,
                                      np.array([g["seqLen"]]), scale, causal=True)
@@ -548,11 +542,115 @@ def pin_mla_prefill_torch_sdpa():
     assert np.max(np.abs(out - ref)) < 1e-12
 
 
+# --------------------------------------------------------------------------
+# bf16 rounding of the projection output, FP8 latent cache
+# --------------------------------------------------------------------------
+
+def _bf16_grid():
+    """Every finite bf16 value (positive and negative), sorted, with its bits."""
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    with np.errstate(invalid="ignore"):
+        vals = O.bf16_bits_to_f64(bits)
+    ok = np.isfinite(vals)
+    order = np.argsort(vals[ok], kind="stable")
+    return vals[ok][order], bits[ok][order]
+
+
+def _nearest_bf16_brute(x):
+    """Nearest bf16 value by search over the whole grid; a tie goes to the
+    value whose bit pattern is even (round half to even)."""
+    grid, gbits = _bf16_grid()
+    out = np.empty(len(x))
+    for i, xi in enumerate(np.asarray(x, np.float64)):
+        d = np.abs(grid - xi)
+        best = np.flatnonzero(d == d.min())
+        if len(best) > 1:
+            even = [b for b in best if gbits[b] % 2 == 0 and grid[b] != 0.0]
+            best = even if even else best
+        out[i] = grid[best[0]]
+    return out
+
+
+def pin_round_bf16():
+    """Round to nearest bf16, ties to even: brute-force search of the bf16
+    grid on random float64 values over the normal range, the halfway cases
+    1 + 2^-8 -> 1 and 1 + 3 * 2^-8 -> 1 + 2^-6 (both signs), and torch's
+    bfloat16 conversion of float32-exact values (one rounding)."""
+    f = lambda *xs: list(O._round_bf16(np.array(xs, np.float64)))
+    assert f(1 + 2.0 ** -8, 1 + 3 * 2.0 ** -8, -(1 + 2.0 ** -8), -(1 + 3 * 2.0 ** -8)) == \
+        [1.0, 1 + 2.0 ** -6, -1.0, -(1 + 2.0 ** -6)]
+    assert f(1 + 2.0 ** -8 + 2.0 ** -30, 0.0, 3.0, -0.5) == [1 + 2.0 ** -7, 0.0, 3.0, -0.5]
+    rng = _rng(91)
+    x = rng.standard_normal(3000) * np.exp2(rng.integers(-40, 40, 3000))
+    assert np.array_equal(O._round_bf16(x), _nearest_bf16_brute(x))
+    x32 = (rng.standard_normal(20000) * np.exp2(rng.integers(-60, 60, 20000))).astype(np.float32)
+    ref = torch.from_numpy(x32).to(torch.bfloat16).double().numpy()
+    assert np.array_equal(O._round_bf16(x32.astype(np.float64)), ref)
+
+
+def pin_mla_expand_rounding():
+    """The expanded keys and values are the exact products W kv_c rounded to
+    the nearest bf16 (brute-force grid search), the key's rope part is k_pe
+    unchanged, on random (not integer) inputs where rounding happens."""
+    rng = _rng(92)
+    H, R, P, dn, dv, S = 2, 16, 4, 3, 5, 6
+    to_bits = lambda a: (np.asarray(a, np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    rows = O.to_f64(to_bits(rng.standard_normal((S, R + P))))
+    w = to_bits(rng.standard_normal((H, dn + dv, R)) / 4)
+    keys, vals = O.mla_expand(rows, w, dn)
+    W = O.to_f64(w)
+    exact = np.einsum("sr,hcr->shc", rows[:, :R], W)
+    want = _nearest_bf16_brute(exact.ravel()).reshape(exact.shape)
+    assert np.array_equal(keys[:, :, :dn], want[:, :, :dn])
+    assert np.array_equal(vals, want[:, :, dn:])
+    assert np.array_equal(keys[:, :, dn:], np.broadcast_to(rows[:, None, R:], (S, H, P)))
+    assert not np.array_equal(want, exact)        # rounding did happen
+
+
+def pin_fp8_mla_cache_write():
+    """The FP8 latent write: both parts of the row (kv_c and k_pe) stored as
+    E4M3(x / scale) with one scale for the row ("Triton 與 MLA", 資料流:
+    v_scale = k_scale for the latent cache), the quotient in fp32 and
+    converted by torch's float8_e4m3fn; the dequantised cache holds
+    code * scale (torch's decoding of the codes)."""
+    rng = _rng(93)
+    nb, bs, R, P, T = 4, 16, 12, 4, 5
+    cache = np.full((nb, bs, R + P), 0x7F, np.uint8)
+    to_bits = lambda a: (np.asarray(a, np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    kvc = to_bits(rng.standard_normal((T, R)) * 3)
+    kpe = to_bits(rng.standard_normal((T, P)) * 3)
+    sc = 0.37
+    slots = np.array([2, 21, -1, 40, 63])
+    out = O.cache_write_mla_fp8(cache, kvc, kpe, slots, sc)
+
+    def ref_codes(bits):
+        f = torch.from_numpy((bits.astype(np.uint32) << 16).view(np.float32))
+        return (f / torch.tensor(sc, dtype=torch.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+    for t, sl in enumerate(slots):
+        if sl < 0:
+            continue
+        blk, off = divmod(int(sl), bs)
+        assert np.array_equal(out[blk, off, :R], ref_codes(kvc[t])), t
+        assert np.array_equal(out[blk, off, R:], ref_codes(kpe[t])), t
+    written = {divmod(int(sl), bs) for sl in slots if sl >= 0}
+    for blk in range(nb):
+        for off in range(bs):
+            if (blk, off) not in written:
+                assert np.all(out[blk, off] == 0x7F)
+    finite = out.copy()
+    finite[finite == 0x7F] = 0
+    deq = O.dequant_mla_cache(finite, sc)
+    ref = torch.from_numpy(finite).view(torch.float8_e4m3fn).double().numpy() * sc
+    assert np.array_equal(deq, ref)
+
+
 ALL_PINS = [
-    pin_bf16_decoding, pin_go_program_slots, pin_go_program_identical,
+    pin_bf16_decoding, pin_paged_program_slots, pin_paged_program_identical,
     pin_num_kv_splits, pin_cache_write_bytes, pin_fig5c_merge, pin_merge_edges,
     pin_closed_forms, pin_torch_sdpa_gqa, pin_torch_sdpa_mla,
     pin_bruteforce_varlen, pin_split_merge_equals_unsplit, pin_block_permutation,
     pin_chunked_prefill, pin_fp8_e4m3_decoding, pin_fp8_e4m3_encoding, pin_fp8_cache_write,
     pin_mla_prefill_equals_absorbed_decode, pin_mla_prefill_torch_sdpa,
+    pin_round_bf16, pin_mla_expand_rounding, pin_fp8_mla_cache_write,
 ]

@@ -64,6 +64,33 @@ def test_workspace_bytes(lib):
     assert pa.decode_workspace_bytes(-1, 32, 128, 16) == 0
 
 
+def test_decode_workspace_size_queries(lib):
+    """The size queries return what pa_decode / pa_mla_decode check for, for
+    explicit split counts (the automatic count needs a device)."""
+    sz = C.c_size_t(0)
+    # 64 requests, 32 q heads, 4 splits over 8192 keys: the split partials
+    assert lib.pa_decode_workspace_size(1, 64, 8192, 16, 32, 8, 128, 4, 0, C.byref(sz)) == 0
+    assert sz.value == 64 * 32 * 4 * 129 * 4
+    # one split covers everything: no workspace, unless only partials are wanted
+    assert lib.pa_decode_workspace_size(1, 64, 8192, 16, 32, 8, 128, 1, 0, C.byref(sz)) == 0
+    assert sz.value == 0
+    assert lib.pa_decode_workspace_size(1, 64, 8192, 16, 32, 8, 128, 1, 1, C.byref(sz)) == 0
+    assert sz.value == 64 * 32 * 1 * 129 * 4
+    # 16 splits of a 300-key batch: pages of 16 -> P = 32, ten splits hold keys
+    assert lib.pa_decode_workspace_size(0, 3, 300, 16, 8, 2, 128, 16, 0, C.byref(sz)) == 0
+    assert sz.value == 3 * 8 * 16 * 129 * 4
+    assert lib.pa_mla_decode_workspace_size(128, 8192, 64, 128, 512, 3, 0, C.byref(sz)) == 0
+    assert sz.value == 128 * 128 * 3 * 513 * 4
+    assert lib.pa_mla_decode_workspace_size(128, 64, 64, 128, 512, 2, 0, C.byref(sz)) == 0
+    assert sz.value == 0                      # 64 keys fit one page, one split
+    for args in [(1, -1, 10, 16, 8, 2, 128, 2, 0), (1, 2, 10, 24, 8, 2, 128, 2, 0),
+                 (1, 2, 10, 16, 0, 2, 128, 2, 0), (1, 2, 10, 16, 8, 2, 128, -1, 0)]:
+        assert lib.pa_decode_workspace_size(*args, C.byref(sz)) == INVALID, args
+        assert pa.last_error() != ""
+    assert lib.pa_decode_workspace_size(1, 2, 10, 16, 8, 2, 128, 2, 0, None) == INVALID
+    assert lib.pa_mla_decode_workspace_size(2, 10, 8, 16, 512, 2, 0, C.byref(sz)) == INVALID
+
+
 def test_mla_split_helper(lib):
     for B, L, cus in [(128, 8192, 256), (1, 8192, 256), (4, 100, 256), (300, 1000, 256)]:
         n = pa.mla_num_kv_splits(B, L, cus)

@@ -114,10 +114,9 @@ def test_plan_validation(lib, qsl, seq, kw, status):
     assert plan.num_seqs == 0
 
 
+@pytest.mark.gpu
 def test_plan_requires_host_copies():
     torch = pytest.importorskip("torch")
-    if not torch.cuda.is_available():
-        pytest.skip("no GPU tensors here")
     with pytest.raises(ValueError):
         pa.plan_mixed(torch.zeros(2, dtype=torch.int32, device="cuda"), [1], 8, 8, 128, 16, 4)
 

@@ -4,7 +4,9 @@ mask, a transposed operand, a wrong log base, a wrong block walk, swapped K/V
 halves, a linear (not exponential) merge weight, a floor in the split count,
 an FP8 decoding with the wrong exponent bias, FP8 rounding toward zero,
 swapped K/V dequantisation scales, MLA keys expanded with the value columns,
-MLA keys without their rope part."""
+MLA keys without their rope part, the projection's bf16 rounding left out or
+done by truncation, the FP8 latent row's rope part stored without its scale,
+and the FP8 latent dequantisation without its scale."""
 import numpy as np
 import pytest
 
@@ -102,6 +104,20 @@ def _expand_no_rope(rows, w, qk_nope):
     return keys, vals
 
 
+def _round_bf16_truncate(x):
+    """Round toward zero to 8 significant bits instead of to nearest."""
+    m, e = np.frexp(np.asarray(x, np.float64))
+    return np.ldexp(np.trunc(m * 256.0) / 256.0, e)
+
+
+_quantize_fp8 = O.quantize_fp8
+_cache_write_mla = O.cache_write_mla
+
+
+def _mla_fp8_unscaled_rope(cache, kv_c, k_pe, slots, scale):
+    return _cache_write_mla(cache, _quantize_fp8(kv_c, scale), _quantize_fp8(k_pe, 1.0), slots)
+
+
 MUTATIONS = {
     "drop_scale": ("attention", _attention_variant(drop_scale=True)),
     "kv_head_modulo": ("attention", _attention_variant(kv_map=lambda h, Hq, Hkv: h % Hkv)),
@@ -119,6 +135,10 @@ MUTATIONS = {
     "fp8_swapped_plane_scales": ("dequant_kv_cache", _dequant_swapped),
     "mla_expand_swapped_kv_columns": ("mla_expand", _expand_swapped_roles),
     "mla_expand_drops_rope_key": ("mla_expand", _expand_no_rope),
+    "bf16_rounding_identity": ("_round_bf16", lambda x: np.asarray(x, np.float64)),
+    "bf16_rounding_truncates": ("_round_bf16", _round_bf16_truncate),
+    "fp8_mla_rope_unscaled": ("cache_write_mla_fp8", _mla_fp8_unscaled_rope),
+    "fp8_mla_dequant_drops_scale": ("dequant_mla_cache", lambda c, s: _fp8_dec(c)),
 }
 
 
