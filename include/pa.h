@@ -201,6 +201,37 @@ pa_status_t pa_decode(pa_dtype_t dtype,
                       void* out, float* lse, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * pa_decode_noalloc -- pa_decode for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the arguments of pa_decode without the workspace, which
+ * is taken from a device array the library owns instead.
+ *
+ * The array holds PA_NOALLOC_SCRATCH_BYTES (64 MiB) on every device the
+ * library runs on, from the first call there until the process ends.  A call
+ * needing more (pa_decode_workspace_size with partials_only = 0 larger than
+ * that, e.g. a few hundred requests with many splits) fails with
+ * PA_ERR_WORKSPACE and launches nothing; out must be non-NULL (the
+ * partial-only form is PA_ERR_INVALID here).  Nothing in the array needs to
+ * start at any value: every partial is written before it is read.  Every
+ * call on one device shares that device's array: calls that overlap on one
+ * device (on different streams, or from different threads without ordering)
+ * race and give wrong results; calls in one stream's order are safe.  This
+ * entry point calls no allocator.  Other arguments, supported
+ * configurations, errors and what is enqueued are those of pa_decode.
+ * ------------------------------------------------------------------------- */
+#define PA_NOALLOC_SCRATCH_BYTES (64u * 1024u * 1024u)
+
+pa_status_t pa_decode_noalloc(pa_dtype_t dtype,
+                              const void* q, const void* k, const void* v,
+                              void* kv_cache, int64_t num_blocks, int block_size,
+                              const int32_t* block_table, int max_blocks_per_seq,
+                              const int64_t* slot_mapping,
+                              const int32_t* seq_lens, int num_seqs, int max_seq_len,
+                              int num_q_heads, int num_kv_heads, int head_dim,
+                              float scale, int num_splits,
+                              void* out, float* lse, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
  * Token-balanced decode: the split-KV reduction of pa_decode ("第 1 章
  * 注意力后端", §3.1: partial softmax states over pieces of a request's keys,
  * merged by log-sum-exp) with the pieces cut for an even load instead of at

@@ -22,7 +22,8 @@ from ._binding import (  # noqa: F401
     PA_BF16, PA_F32, PA_LAYOUT_KV, PA_LAYOUT_MLA, PaError, EXPORTED_SYMBOLS,
     cache_write, decode, decode_balanced, decode_balanced_merge,
     decode_balanced_num_ranges, decode_balanced_workspace_bytes,
-    decode_workspace_bytes, device_num_cus, last_error, MixedPlan, mixed_attention, plan_mixed,
+    decode_workspace_bytes, decode_workspace_size, mla_decode_workspace_size, decode_noalloc,
+    NOALLOC_SCRATCH_BYTES, device_num_cus, last_error, MixedPlan, mixed_attention, plan_mixed,
     CascadePlan, cascade_attention, plan_cascade, cache_write_fp8, decode_fp8,
     mla_decode_fp8, mla_prefill, mla_prefill_workspace_bytes, prefill_varlen_fp8,
     library, library_path, lse_merge, mla_decode, mla_decode_balanced, mla_num_kv_splits,

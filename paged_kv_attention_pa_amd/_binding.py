@@ -70,6 +70,8 @@ _SIGNATURES = {
                              _i32, _i32, _f32, _f32, _f32, _i32, _vp, _sz, _vp, _vp, _vp]),
     "pa_cascade_attention": (_i32, [_vp, _i32, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _vp, _vp,
                                     _f32, _vp, _sz, _vp, _vp, _vp]),
+    "pa_decode_noalloc": (_i32, [_i32, _vp, _vp, _vp, _vp, _i64, _i32, _vp, _i32, _vp, _vp, _i32,
+                                 _i32, _i32, _i32, _i32, _f32, _i32, _vp, _vp, _vp]),
 }
 EXPORTED_SYMBOLS = tuple(_SIGNATURES)
 
@@ -436,6 +438,33 @@ def decode(q, kv_cache, block_table, seq_lens, max_seq_len: int, scale: float,
         if workspace is None:
             return torch.empty((B, Hq, 0, D + 1), dtype=torch.float32, device=q.device)
         return workspace[: B * Hq * n * (D + 1)].view(B, Hq, n, D + 1)
+    return out, lse
+
+
+NOALLOC_SCRATCH_BYTES = 64 * 1024 * 1024   # PA_NOALLOC_SCRATCH_BYTES
+
+
+def decode_noalloc(q, kv_cache, block_table, seq_lens, max_seq_len: int, scale: float,
+                   k=None, v=None, slot_mapping=None, num_splits: int = 0, out=None, lse=None,
+                   return_lse: bool = True, stream=None):
+    """``pa_decode_noalloc``: GQA decode whose partials live in the library's
+    own device array (no workspace argument).  Returns (out, lse)."""
+    torch = _torch()
+    _dev(q, kv_cache, block_table, seq_lens, k, v, slot_mapping, out, lse)
+    _int_tensor(block_table, "int32", "block_table")
+    _int_tensor(seq_lens, "int32", "seq_lens")
+    dt = _dtype_code(q)
+    B, Hq, D = q.shape
+    nb, _, bs, hkv, _ = kv_cache.shape
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and return_lse:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    _check(library().pa_decode_noalloc(dt, _ptr(q), _ptr(k), _ptr(v), _ptr(kv_cache), nb, bs,
+                                       _ptr(block_table), block_table.shape[1], _ptr(slot_mapping),
+                                       _ptr(seq_lens), B, int(max_seq_len), Hq, hkv, D,
+                                       float(scale), int(num_splits), _ptr(out), _ptr(lse),
+                                       _stream(stream)))
     return out, lse
 
 

@@ -195,6 +195,16 @@ float* balanced_part(void* ws, int num_seqs) {
 
 }  // namespace
 
+namespace pa {
+int set_error(int st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+}  // namespace pa
+
 extern "C" {
 
 int pa_num_kv_splits(int max_seq_len, int num_cus) {

@@ -177,4 +177,8 @@ struct CascadeMerge {
 };
 hipError_t launch_cascade_merge(const CascadeMerge& a, hipStream_t s);
 
+// Record a message for pa_last_error() (printf format) and return st.
+// Defined with the entry points; for entry points in other sources.
+int set_error(int st, const char* fmt, ...);
+
 }  // namespace pa
