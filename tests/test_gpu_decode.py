@@ -95,6 +95,10 @@ CASES = [
     ("g2_hkv6_bf16", [300, 1200, 7], 12, 6, 16, W.BF16),   # automatic schedule: splits
     ("g4_fp32", [2, 128, 1025], 8, 2, 16, W.F32),
     ("g8_fp32_block64", [70, 640], 16, 2, 64, W.F32),
+    # page sizes that are multiples of 16 but not powers of two
+    ("g4_bf16_block48", [47, 48, 49, 700, 1500], 32, 8, 48, W.BF16),
+    ("g8_bf16_block80", [79, 81, 2000], 64, 8, 80, W.BF16),
+    ("g4_fp32_block48", [5, 95, 1000], 8, 2, 48, W.F32),
 ]
 
 
@@ -209,35 +213,47 @@ def llama():
 
 def test_llama_decode_full_size(llama):
     """64 requests, 32/8 heads, bf16; heuristic splits (as the bench runs it);
-    eight sampled requests against the oracle, the whole pool bit-exact."""
+    every request against the oracle, the whole pool bit-exact."""
     b = llama
     say(f"decode llama3-8b full size, max_seq_len={b.max_seq_len}")
     cache_t, out, lse = _run_decode(b, num_splits=0)
     assert np.all(np.isfinite(out))
-    reqs = [int(i) for i in np.argsort(b.seq_lens)[[0, 1, 20, 31, 40, 50, 62, 63]]]
-    cache_ref, oref, lref = _oracle_decode(b, requests=reqs)
-    for r in reqs:
-        check_close(out[r], oref[r], f"request {r}")
-        check_lse(lse[r], lref[r], f"request {r}")
+    cache_ref, oref, lref = _oracle_decode(b)
+    check_close(out, oref, "llama decode out")
+    check_lse(lse, lref, "llama decode lse")
     assert np.array_equal(bits(cache_t), cache_ref)
 
 
 @pytest.fixture(scope="module")
 def longctx():
-    return W.long_context_decode()
+    """The long-context batch and its oracle result (computed once: about a
+    minute and a half of CPU work, shared by both schedules' tests)."""
+    b = W.long_context_decode()
+    say("long-context oracle")
+    _, oref, lref = _oracle_decode(b)
+    return b, oref, lref
 
 
 def test_long_context_decode_full_size(longctx):
-    """4 x 131072 keys, 64/8 heads, 256 splits; two requests against the oracle."""
-    b = longctx
+    """4 x 131072 keys, 64/8 heads, 256 splits; every request against the oracle."""
+    b, oref, lref = longctx
     say("decode long-context full size (256 splits)")
     assert pa.num_kv_splits(b.max_seq_len, 256) == 256
     _, out, lse = _run_decode(b, num_splits=256)
     assert np.all(np.isfinite(out))
-    _, oref, lref = _oracle_decode(b, requests=[0, 3])
-    for r in (0, 3):
-        check_close(out[r], oref[r], f"request {r}")
-        check_lse(lse[r], lref[r], f"request {r}")
+    check_close(out, oref, "long-context out")
+    check_lse(lse, lref, "long-context lse")
+
+
+def test_long_context_balanced_full_size(longctx):
+    """The same batch on the automatic (token-balanced) schedule, as the bench
+    runs it; every request against the oracle."""
+    b, oref, lref = longctx
+    say("balanced long-context full size")
+    _, out, lse = _run_decode(b, num_splits=0)
+    assert np.all(np.isfinite(out))
+    check_close(out, oref, "long-context balanced out")
+    check_lse(lse, lref, "long-context balanced lse")
 
 
 def test_two_stage_decode_matches_one_call():

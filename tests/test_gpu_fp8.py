@@ -105,6 +105,9 @@ CASES = [
     ("g1_4kv", [17, 3000, 1, 250], 4, 4, 32, 1.3, 0.011),
     ("g2_2kv", [600, 5, 1111], 4, 2, 16, 0.02, 2.0),
     ("g4_16kv", [1, 100, 3333, 64, 65], 64, 16, 16, 0.125, 0.75),
+    # page sizes that are multiples of 16 but not powers of two
+    ("g4_8kv_bs48", [47, 49, 700, 2000], 32, 8, 48, 0.3, 0.07),
+    ("g8_1kv_bs80", [79, 81, 1500], 8, 1, 80, 0.25, 0.5),
 ]
 
 
@@ -203,6 +206,8 @@ MLA_CASES = [
     ("h16_bs16", [5, 1, 129, 1000], 16, 16, 0.07),
     ("h64_bs32_long", [3000, 2, 95], 64, 32, 1.5),
     ("h112_bs64", [40, 513], 112, 64, 0.25),
+    ("h128_bs48", [47, 49, 1000], 128, 48, 0.3),
+    ("h32_bs80", [79, 81, 1700], 32, 80, 0.2),
 ]
 
 
@@ -294,6 +299,8 @@ PREFILL_CASES = [
     ("long_chunk_g8", [300], [1000], 8, 1, 16, 0.25, 0.5),
     ("g1_block32", [129, 3], [31, 700], 2, 2, 32, 1.3, 0.011),
     ("g4_32_8", [90, 40, 260], [17, 256, 4], 32, 8, 16, 0.02, 2.0),
+    ("g4_bs48_empty", [0, 70, 129], [40, 50, 100], 32, 8, 48, 0.3, 0.07),
+    ("g8_bs80", [200, 33], [90, 400], 16, 2, 80, 0.25, 0.5),
 ]
 
 

@@ -41,6 +41,11 @@ CASES = [
     ("g1_block32", [129, 3], [31, 700], 2, 2, 32),
     ("g2_no_ctx", [200, 128], [0, 0], 4, 2, 16),
     ("g4_32_8", [90, 40, 260], [17, 256, 4], 32, 8, 16),
+    # requests with no query rows (L_r = 0) between others
+    ("empty_chunks_g4", [0, 70, 129, 0, 5], [40, 50, 100, 1, 300], 32, 8, 16),
+    # page sizes that are multiples of 16 but not powers of two
+    ("g4_block48_empty", [0, 70, 129, 33], [40, 50, 100, 17], 32, 8, 48),
+    ("g8_block80", [200, 33], [90, 400], 16, 2, 80),
 ]
 
 
