@@ -15,7 +15,11 @@ Timing: W untimed warm-up steps, then K steps bracketed by
 torch.cuda.synchronize() (wall clock); the dominant kernel of each workload
 is also timed alone with HIP events on the stream it is launched on (the
 library launches on torch's current stream).  The CPU baseline is the float64
-oracle on a bounded sample of the headline workload, on one host thread.
+oracle on a bounded sample of each of the five configurations (tiny decode,
+Llama-3-8B decode, chunked prefill, long-context decode, MLA decode) on the
+host's cores; the headline line carries the Llama-3-8B one.  Beside the
+automatic schedule, the decode and MLA workloads are also timed at fixed
+split counts, and the headline batch with an identity-like block table.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only NAME ...]
 """
@@ -59,11 +63,13 @@ def kernel_source_sha(fname: str) -> str:
 
 class Case:
     def __init__(self, name, step, kernel, step_bytes, step_flops, kern_bytes, kern_flops,
-                 bound, kernel_name, source, info):
+                 bound, kernel_name, source, info, sweep=None):
         self.name, self.step, self.kernel = name, step, kernel
         self.step_bytes, self.step_flops = step_bytes, step_flops
         self.kern_bytes, self.kern_flops = kern_bytes, kern_flops
         self.bound, self.kernel_name, self.source, self.info = bound, kernel_name, source, info
+        # optional: {label: (num_splits, step function)} timed beside the case
+        self.sweep = sweep
 
 
 def _dev(a):
@@ -75,7 +81,7 @@ def _dev(a):
     return torch.from_numpy(a).cuda()
 
 
-def gqa_decode_case(b, num_splits, name):
+def gqa_decode_case(b, num_splits, name, split_sweep=False):
     import torch
     import paged_kv_attention_pa_amd as pa
     import workloads as W
@@ -125,7 +131,24 @@ def gqa_decode_case(b, num_splits, name):
             "max_seq_len": b.max_seq_len, "total_keys": int(b.seq_lens.sum()),
             "schedule": "token-balanced ranges" if balanced else f"{n} splits per request",
             "grid": grid}
-    return Case(name, step, kernel, by["total"], fl, kb, fl, "hbm", kname, source, info)
+    sweep = None
+    if split_sweep:
+        # the pages' fixed partition at several split counts: unsplit, two,
+        # their heuristic (max_seq_len / 512, capped at 2 x CUs) and the cap
+        counts = {"1": 1, "2": 2, "heuristic": pa.num_kv_splits(b.max_seq_len, cus),
+                  "max (2 x CUs)": 2 * cus}
+        sweep = {}
+        for label, ns in counts.items():
+            need = pa.decode_workspace_bytes(b.num_seqs, b.num_q_heads, b.head_dim, ns)
+            wsn = torch.empty(max(1, need // 4), dtype=torch.float32, device="cuda")
+
+            def run(ns=ns, wsn=wsn):
+                pa.decode(q, cache, bt, sl, b.max_seq_len, b.scale, k=kn, v=vn, slot_mapping=sm,
+                          num_splits=ns, workspace=wsn, out=out, lse=lse)
+            sweep[label] = (ns, run)
+    c = Case(name, step, kernel, by["total"], fl, kb, fl, "hbm", kname, source, info, sweep)
+    c.batch = b
+    return c
 
 
 def prefill_case(b, name):
@@ -153,8 +176,10 @@ def prefill_case(b, name):
             "num_kv_heads": b.num_kv_heads, "head_dim": b.head_dim, "block_size": b.block_size,
             "max_query_len": b.max_query_len, "max_seq_len": b.max_seq_len, "causal": True,
             "grid": "ceil(max_q/128) x num_seqs x Hq work-groups of 256"}
-    return Case(name, step, kernel, by["total"], fl, kb, fl, "mfma", "prefill_kernel<false, false>",
-                "prefill.hip", info)
+    c = Case(name, step, kernel, by["total"], fl, kb, fl, "mfma", "prefill_kernel<false, false>",
+             "prefill.hip", info)
+    c.batch = b
+    return c
 
 
 def mla_case(b, name):
@@ -186,9 +211,25 @@ def mla_case(b, name):
     info = {"num_seqs": b.num_seqs, "num_heads": b.num_heads, "kv_lora_rank": b.kv_lora_rank,
             "rope_dim": b.rope_dim, "block_size": b.block_size, "max_seq_len": b.max_seq_len,
             "total_keys": int(b.seq_lens.sum()), "schedule": "token-balanced ranges",
-            "grid": f"{nr} token ranges x 8 waves (16 heads each)"}
-    return Case(name, step, kernel, by["total"], fl, kb, fl, "mfma", "mla_kernel<true, false, 512>",
-                "mla_decode.hip", info)
+            "grid": f"{nr} token ranges x 4 waves (32 heads each)"}
+    # fixed partitions: unsplit, 2, 4, the library's MLA rule (enough splits to
+    # cover the CUs about twice) and the pages' max_seq_len / 512
+    counts = {"1": 1, "2": 2, "4": 4,
+              "mla rule": pa.mla_num_kv_splits(b.num_seqs, b.max_seq_len, nr),
+              "heuristic (max_seq_len / 512)": pa.num_kv_splits(b.max_seq_len, nr)}
+    sweep = {}
+    for label, ns in counts.items():
+        need = pa.decode_workspace_bytes(b.num_seqs, b.num_heads, b.kv_lora_rank, ns)
+        wsn = torch.empty(max(1, need // 4), dtype=torch.float32, device="cuda")
+
+        def run(ns=ns, wsn=wsn):
+            pa.mla_decode(qn, qp, cache, bt, sl, b.max_seq_len, b.scale, kv_c=kc, k_pe=kp,
+                          slot_mapping=sm, num_splits=ns, workspace=wsn, out=out, lse=lse)
+        sweep[label] = (ns, run)
+    c = Case(name, step, kernel, by["total"], fl, kb, fl, "mfma", "mla_kernel<true, false, 512>",
+             "mla_decode.hip", info, sweep)
+    c.batch = b
+    return c
 
 
 def mixed_case(b, name):
@@ -444,11 +485,13 @@ def build_cases(only):
     import workloads as W
     makers = {
         "tiny_gqa_decode_fp32": lambda: gqa_decode_case(W.tiny_decode(), 0, "tiny_gqa_decode_fp32"),
-        HEADLINE: lambda: gqa_decode_case(W.llama_decode(), 0, HEADLINE),
+        HEADLINE: lambda: gqa_decode_case(W.llama_decode(), 0, HEADLINE, split_sweep=True),
         "chunked_prefill_varlen_bf16": lambda: prefill_case(W.chunked_prefill(),
                                                             "chunked_prefill_varlen_bf16"),
         "long_context_split_kv_decode_bf16": lambda: gqa_decode_case(
-            W.long_context_decode(), 0, "long_context_split_kv_decode_bf16"),
+            W.long_context_decode(), 0, "long_context_split_kv_decode_bf16", split_sweep=True),
+        W.IDENTITY_DECODE: lambda: gqa_decode_case(
+            W.identity_layout(W.llama_decode(), W.IDENTITY_DECODE), 0, W.IDENTITY_DECODE),
         "mla_latent_decode_bf16": lambda: mla_case(W.mla_decode_batch(), "mla_latent_decode_bf16"),
         W.MIXED: lambda: mixed_case(W.mixed_batch(), W.MIXED),
         W.CASCADE: lambda: cascade_case(W.cascade_batch(), W.CASCADE),
@@ -573,42 +616,82 @@ def roofline(case, kern_s):
 
 
 # --------------------------------------------------------------------------
-# CPU baseline: the float64 oracle on a bounded sample of the headline batch
+# CPU baseline: the float64 oracle on a bounded sample of each of the five
+# configurations, on the host's cores
 # --------------------------------------------------------------------------
 
-def cpu_baseline(budget_s=12.0):
+CPU_SAMPLES = {   # workload -> (kind, seconds of oracle work to aim for)
+    "tiny_gqa_decode_fp32": ("decode", 2.0),
+    HEADLINE: ("decode", 5.0),
+    "chunked_prefill_varlen_bf16": ("prefill", 5.0),
+    "long_context_split_kv_decode_bf16": ("decode", 5.0),
+    "mla_latent_decode_bf16": ("mla", 5.0),
+}
+
+
+def _host_threads() -> int:
+    """Threads the oracle's BLAS may use: the cores this process may run on,
+    no more than the OMP_NUM_THREADS share when one is set."""
+    n = len(os.sched_getaffinity(0))
+    try:
+        n = min(n, int(os.environ["OMP_NUM_THREADS"]))
+    except (KeyError, ValueError):
+        pass
+    return max(1, n)
+
+
+def cpu_baseline(name, case):
+    """Time the oracle on a bounded sample of workload ``name``: the whole
+    batch's cache write, then the attention of its requests in order until
+    the time budget is spent (at least one request).  Reported in the unit of
+    the workload's roofline: GB/s of the sampled requests' algorithmic bytes
+    for decode, GFLOP/s of their flops for prefill and MLA."""
     import numpy as np
     import workloads as W
     import oracle.pa_oracle as O
-    try:
-        from threadpoolctl import threadpool_limits
-    except ImportError:       # pragma: no cover
-        threadpool_limits = None
-    b = W.llama_decode()
-    done, nbytes, passes = 0, 0, 0
-    row = b.num_kv_heads * b.head_dim * 2 * 2
-    ctx = threadpool_limits(limits=1) if threadpool_limits else None
-    t0 = time.perf_counter()
-    try:
-        # whole passes over the batch (write + decode of every request) until
-        # the budget is spent; stop early inside a pass if it runs long
-        while time.perf_counter() - t0 < budget_s:
+    from threadpoolctl import threadpool_limits
+    kind, budget = CPU_SAMPLES[name]
+    make = {"tiny_gqa_decode_fp32": W.tiny_decode, HEADLINE: W.llama_decode,
+            "chunked_prefill_varlen_bf16": W.chunked_prefill,
+            "long_context_split_kv_decode_bf16": W.long_context_decode,
+            "mla_latent_decode_bf16": W.mla_decode_batch}[name]
+    b = getattr(case, "batch", None) or make()
+    threads = _host_threads()
+    done, work = 0, 0.0
+    with threadpool_limits(limits=threads):
+        tw = time.perf_counter()
+        if kind == "mla":
+            cache = O.cache_write_mla(b.cache, b.kv_c_new, b.k_pe_new, b.slot_mapping)
+        else:
             cache = O.cache_write_kv(b.cache, b.k_new, b.v_new, b.slot_mapping)
-            for r in range(b.num_seqs):
+        t0 = time.perf_counter()
+        write_s = t0 - tw
+        for r in range(b.num_seqs):
+            S = int(b.seq_lens[r])
+            if kind == "decode":
                 O.paged_decode(b.q, cache, b.block_table, b.seq_lens, b.scale, requests=[r])
-                done += 1
-                nbytes += int(b.seq_lens[r]) * row + 2 * b.num_q_heads * b.head_dim * 2
-                if time.perf_counter() - t0 > 2 * budget_s:
-                    break
-            passes += 1
-    finally:
-        if ctx is not None:
-            ctx.__exit__(None, None, None)
-    dt = time.perf_counter() - t0
-    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "seconds": round(dt, 2),
-            "sample": f"float64 numpy oracle (cache write + decode) over {passes} pass(es) of the "
-                      f"64-request batch ({done} request decodes), one BLAS thread"}
+                elem = 4 if b.dtype == W.F32 else 2
+                work += S * 2 * b.num_kv_heads * b.head_dim * elem + 2 * b.num_q_heads * b.head_dim * elem
+            elif kind == "prefill":
+                O.paged_attention(b.q, cache, b.block_table, b.query_start_loc, b.seq_lens,
+                                  b.scale, requests=[r])
+                L = int(b.query_start_loc[r + 1] - b.query_start_loc[r])
+                C = S - L
+                work += 4.0 * b.head_dim * b.num_q_heads * (L * C + L * (L + 1) / 2)
+            else:
+                O.mla_decode(b.q_nope, b.q_pe, cache, b.block_table, b.seq_lens, b.scale,
+                             requests=[r])
+                work += 2.0 * b.num_heads * S * ((b.kv_lora_rank + b.rope_dim) + b.kv_lora_rank)
+            done += 1
+            if time.perf_counter() - t0 >= budget:
+                break
+        dt = time.perf_counter() - t0
+    unit, value = ("GB/s", work / dt / 1e9) if kind == "decode" else ("GFLOP/s", work / dt / 1e9)
+    return {"value": round(value, 4), "unit": unit, "cores": threads, "kind": "oracle",
+            "seconds": round(dt, 2), "write_seconds": round(write_s, 2),
+            "sample": f"float64 numpy oracle, {threads} BLAS threads: the attention of {done} of "
+                      f"{b.num_seqs} requests (in order) over the cache after the batch's write "
+                      f"(the write, {write_s:.2f} s, is timed apart and not in the rate)"}
 
 
 # --------------------------------------------------------------------------
@@ -658,6 +741,22 @@ def main():
             "step_bytes": int(case.step_bytes), "step_flops": int(case.step_flops),
             "roofline": rl, "config": case.info,
         }
+        if case.sweep:
+            sw = {}
+            for label, (ns, fn) in case.sweep.items():
+                t = time_steps(fn, args.steps, args.warmup)
+                sw[label] = {"num_splits": ns, "ms_per_step": round(t * 1e3, 4),
+                             "step_GBps": round(case.step_bytes / t / 1e9, 2),
+                             "step_TFLOPs": round(case.step_flops / t / 1e12, 3)}
+                log(f"[bench]   {case.name} num_splits={ns} ({label}): {sw[label]['ms_per_step']} ms/step")
+            sw["automatic (this line)"] = {"num_splits": 0, "ms_per_step": res["ms_per_step"],
+                                           "step_GBps": res["step_GBps"],
+                                           "step_TFLOPs": res["step_TFLOPs"]}
+            res["num_splits_sweep"] = sw
+        if not args.no_cpu_baseline and case.name in CPU_SAMPLES:
+            res["cpu_baseline"] = cpu_baseline(case.name, case)
+            log(f"[bench]   {case.name} cpu baseline: {res['cpu_baseline']['value']} "
+                f"{res['cpu_baseline']['unit']} on {res['cpu_baseline']['cores']} threads")
         results[case.name] = res
         log(f"[bench] {case.name}: {res['ms_per_step']} ms/step, {res['step_GBps']} GB/s, "
             f"{res['step_TFLOPs']} TFLOP/s; kernel {rl['kernel']} {rl['kernel_ms']} ms = "
@@ -685,7 +784,7 @@ def main():
                    **({"seq_len": "U[512,8192]"} if case.name == HEADLINE else {}),
                    "parallelism": "single GPU"},
         "roofline": {k: rl[k] for k in ("bound", "achieved", "peak", "unit", "frac", "traffic")},
-        "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline(),
+        "cpu_baseline": results[case.name].get("cpu_baseline"),
         "dominant_kernel": {k: rl[k] for k in ("kernel", "kernel_ms", "algorithmic_bytes")},
         "workloads": results,
     }

@@ -69,3 +69,25 @@ def test_byte_and_flop_counts():
     by = W.gqa_bytes(b)
     assert by["kv"] == 400 * 8 * 128 * 2 * 2
     assert W.gqa_flops(b) == 2 * 400 * 32 * 256
+
+
+def test_identity_layout_same_bytes_consecutive_pages():
+    """The identity-like layout moves pages, not values: every request's pages
+    are consecutive in logical order, and the oracle's result is unchanged
+    bit for bit."""
+    import oracle.pa_oracle as O
+    b = W.make_gqa(3, [1, 1, 1], [40, 300, 17], 8, 2, 128, 16, W.BF16)
+    c = W.identity_layout(b, "identity")
+    bs = b.block_size
+    cur = 0
+    for r, S in enumerate(b.seq_lens):
+        n = -(-int(S) // bs)
+        assert list(c.block_table[r, :n]) == list(range(cur, cur + n))
+        cur += n
+    o1, l1 = O.paged_decode(b.q, O.cache_write_kv(b.cache, b.k_new, b.v_new, b.slot_mapping),
+                            b.block_table, b.seq_lens, b.scale)
+    o2, l2 = O.paged_decode(c.q, O.cache_write_kv(c.cache, c.k_new, c.v_new, c.slot_mapping),
+                            c.block_table, c.seq_lens, c.scale)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+    assert sorted(c.cache.reshape(c.cache.shape[0], -1).view(np.uint16)[:, 0].tolist()) == \
+        sorted(b.cache.reshape(b.cache.shape[0], -1).view(np.uint16)[:, 0].tolist())

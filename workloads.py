@@ -459,6 +459,36 @@ def llama_decode(seed: int = 1002, batch: int = 64) -> GqaBatch:
                     BF16, name=WORKLOADS[1])
 
 
+IDENTITY_DECODE = "llama3_8b_gqa_decode_bf16_identity_table"
+
+
+def identity_layout(b: GqaBatch, name: str | None = None) -> GqaBatch:
+    """The same batch with the pool's blocks renumbered so that request r's
+    pages are consecutive physical blocks in logical order (an identity-like
+    block table, requests one after another, the poison block last).  Every
+    byte the attention reads is the same; only where the pages sit changes
+    ("Attention Backends", Try it: the identity table gives the same result
+    as a shuffled one)."""
+    nb, bs = b.cache.shape[0], b.block_size
+    need = (b.seq_lens.astype(np.int64) + bs - 1) // bs
+    perm = np.full(nb, -1, dtype=np.int64)      # new id of old block b
+    nxt = 0
+    for r, n in enumerate(need):
+        for old in b.block_table[r, :n]:
+            perm[int(old)] = nxt
+            nxt += 1
+    rest = np.flatnonzero(perm < 0)
+    perm[rest] = np.arange(nxt, nxt + len(rest))
+    cache = np.empty_like(b.cache)
+    cache[perm] = b.cache
+    table = perm[b.block_table].astype(np.int32)
+    slots = perm[b.slot_mapping // bs] * bs + b.slot_mapping % bs
+    return GqaBatch(name=name or b.name, dtype=b.dtype, q=b.q, k_new=b.k_new, v_new=b.v_new,
+                    cache=cache, block_table=table, slot_mapping=slots,
+                    query_start_loc=b.query_start_loc, seq_lens=b.seq_lens, scale=b.scale,
+                    block_size=bs, poison_block=int(perm[b.poison_block]), meta=dict(b.meta))
+
+
 FP8_DECODE = "llama3_8b_gqa_decode_fp8kv"
 FP8_MLA = "mla_latent_decode_fp8kv"
 FP8_PREFILL = "chunked_prefill_varlen_fp8kv"
