@@ -175,8 +175,9 @@ def prefill_case(b, name):
     info = {"num_seqs": b.num_seqs, "num_tokens": b.num_tokens, "num_q_heads": b.num_q_heads,
             "num_kv_heads": b.num_kv_heads, "head_dim": b.head_dim, "block_size": b.block_size,
             "max_query_len": b.max_query_len, "max_seq_len": b.max_seq_len, "causal": True,
-            "grid": "ceil(max_q/128) x num_seqs x Hq work-groups of 256"}
-    c = Case(name, step, kernel, by["total"], fl, kb, fl, "mfma", "prefill_kernel<false, false>",
+            "grid": "ceil(max_q/256) x num_seqs x Hq work-groups of 512 (two 4-wave groups "
+                    "alternating MFMA and softmax half-periods)"}
+    c = Case(name, step, kernel, by["total"], fl, kb, fl, "mfma", "prefill_pp_kernel<2>",
              "prefill.hip", info)
     c.batch = b
     return c
