@@ -143,3 +143,18 @@ def test_prefill_scale_zero_is_uniform_attention():
     _, oref, lref = _oracle(b)
     check_close(out, oref, "scale 0 out")
     check_lse(lse, lref, "scale 0 lse")
+
+
+@pytest.mark.parametrize("ql,ctx", [(64, 65472), (64, 65808)], ids=["at_table_limit", "past_table"])
+def test_prefill_long_context_table_limit(ql, ctx):
+    """A request whose keys fill the bf16 prefill's 16-key-group address
+    table exactly (65536 keys: the ping-pong kernel), and one past it
+    (65872 keys: the launcher takes the 4-wave kernel instead); every row
+    against the oracle."""
+    say(f"prefill long context {ql} rows over {ctx + ql} keys")
+    b = W.make_gqa(290, [ql], np.array([ql + ctx]), 4, 1, 128, 16, W.BF16,
+                   scale=1.0 / math.sqrt(128))
+    cache_t, out, lse = _run(b)
+    _, oref, lref = _oracle(b)
+    check_close(out, oref, f"long context {ctx + ql} out")
+    check_lse(lse, lref, f"long context {ctx + ql} lse")
