@@ -91,9 +91,9 @@ __global__ __launch_bounds__(64 * kHeads, 1) void decode_balanced_kernel(DecodeB
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) qf[kk] = load16(qp + 32 * kk);
   };
-  // K (plane 0) or V (plane kv_bytes) pieces of chunk p.  Tokens past the
-  // request's end re-read its last token (finite data, masked below); the
-  // loads are unconditional so the waits stay exact.
+  // Pieces of chunk p.  Tokens past the request's end re-read its last
+  // token (finite data, masked below); the loads are unconditional so the
+  // waits stay exact.
   // The scalar address math stays small (the scalar unit is shared by the
   // compute unit's four SIMDs): page of a token by a shift when the block
   // size is a power of two, byte offsets within a page in 32 bits.
@@ -102,10 +102,12 @@ __global__ __launch_bounds__(64 * kHeads, 1) void decode_balanced_kernel(DecodeB
   const uint64_t page_bytes = 2 * uint64_t(bs) * uint64_t(tok_bytes);
   const uint32_t tok32 = uint32_t(tok_bytes);
   const uint32_t nblk = uint32_t(min(a.num_blocks, int64_t(INT32_MAX)));
-  auto load_half = [&](const ChunkPos& p, int64_t plane, u32x4_t (&dst)[kLoads]) {
+  // K and V pieces of chunk p: one address per piece for both planes (the V
+  // piece is kv_bytes on), so the page lookups and the scalar address math
+  // are done once.
+  auto load_kv = [&](const ChunkPos& p, u32x4_t (&kdst)[kLoads], u32x4_t (&vdst)[kLoads]) {
     const int32_t* table = a.block_table + int64_t(p.r) * a.max_blocks;
     const int len = max(p.len, 1);   // positions always hold keys; keeps every index >= 0
-    const char* base_p = cache_b + plane;
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) {
       const int I = wave + waves * i;
@@ -120,7 +122,9 @@ __global__ __launch_bounds__(64 * kHeads, 1) void decode_balanced_kernel(DecodeB
       // non-temporal: every cache byte is read once, so it need not displace
       // anything in L2 or the MALL (81% against 72% of HBM peak on the
       // headline batch)
-      dst[i] = load16_stream(base_p + blk * page_bytes + (uint32_t(tok - page * bs) * tok32 + uint32_t(byte)));
+      const char* src = cache_b + blk * page_bytes + (uint32_t(tok - page * bs) * tok32 + uint32_t(byte));
+      kdst[i] = load16_stream(src);
+      vdst[i] = load16_stream(src + kv_bytes);
     }
   };
   // LDS position of this lane's piece i (head tile, token row, byte of the
@@ -137,8 +141,7 @@ __global__ __launch_bounds__(64 * kHeads, 1) void decode_balanced_kernel(DecodeB
   u32x4_t qf[4];
   load_q(cur.r, qf);
   u32x4_t kr[kLoads], vr[kLoads];
-  load_half(cur, 0, kr);
-  load_half(cur, kv_bytes, vr);
+  load_kv(cur, kr, vr);
 
   f32x4_t acc[8];   // O^T: d = 16 dt + 4 kq + i, head column li
 #pragma unroll
@@ -167,8 +170,7 @@ __global__ __launch_bounds__(64 * kHeads, 1) void decode_balanced_kernel(DecodeB
     __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's LDS stores are done
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    load_half(nxt, 0, kr);
-    load_half(nxt, kv_bytes, vr);
+    load_kv(nxt, kr, vr);
     f32x4_t sc[2];
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
