@@ -333,6 +333,15 @@ pa_status_t pa_cache_write(pa_layout_t layout, pa_dtype_t dtype,
 }
 
 // ---------------------------------------------------------------------------
+static pa_status_t decode_balanced_impl(const void* q, const void* kv_cache, int64_t num_blocks,
+                                        int block_size, const int32_t* block_table,
+                                        int max_blocks_per_seq, const int32_t* seq_lens,
+                                        int num_seqs, int num_q_heads, int num_kv_heads,
+                                        int head_dim, float scale, int num_ranges, void* workspace,
+                                        size_t workspace_bytes, void* out, float* lse,
+                                        const void* k_new, const void* v_new,
+                                        const int64_t* slots, hipStream_t stream);
+
 pa_status_t pa_decode(pa_dtype_t dtype,
                       const void* q, const void* k, const void* v,
                       void* kv_cache, int64_t num_blocks, int block_size,
@@ -382,7 +391,9 @@ pa_status_t pa_decode(pa_dtype_t dtype,
                workspace_bytes);
   }
 
-  if (k) {
+  // the balanced (bf16) decode writes the new tokens itself; the others
+  // after a write kernel
+  if (k && !balanced) {
     pa::CacheWriteKV w{k, int64_t(num_kv_heads) * head_dim, v, int64_t(num_kv_heads) * head_dim,
                        kv_cache, num_blocks, block_size, num_kv_heads, head_dim, slot_mapping,
                        num_seqs, dtype == PA_BF16 ? 2 : 4};
@@ -390,9 +401,10 @@ pa_status_t pa_decode(pa_dtype_t dtype,
     if (e != hipSuccess) return hip_fail(e, "cache_write_kv launch");
   }
   if (balanced) {
-    st = pa_decode_balanced(q, kv_cache, num_blocks, block_size, block_table, max_blocks_per_seq,
-                            seq_lens, num_seqs, num_q_heads, num_kv_heads, head_dim, scale, nr,
-                            workspace, workspace_bytes, out, lse, stream);
+    st = decode_balanced_impl(q, kv_cache, num_blocks, block_size, block_table,
+                              max_blocks_per_seq, seq_lens, num_seqs, num_q_heads, num_kv_heads,
+                              head_dim, scale, nr, workspace, workspace_bytes, out, lse, k, v,
+                              slot_mapping, stream);
     if (st != PA_OK) return st;
     return pa_decode_balanced_merge(workspace, workspace_bytes, num_seqs, num_q_heads, head_dim,
                                     nr, out, lse, stream);
@@ -438,12 +450,16 @@ size_t pa_decode_balanced_workspace_bytes(int num_seqs, int num_heads, int head_
   return balanced_bytes(num_seqs, num_heads, head_dim_v, num_ranges);
 }
 
-pa_status_t pa_decode_balanced(const void* q, const void* kv_cache, int64_t num_blocks,
-                               int block_size, const int32_t* block_table,
-                               int max_blocks_per_seq, const int32_t* seq_lens, int num_seqs,
-                               int num_q_heads, int num_kv_heads, int head_dim, float scale,
-                               int num_ranges, void* workspace, size_t workspace_bytes,
-                               void* out, float* lse, hipStream_t stream) {
+// The balanced decode; with k_new (bf16 [num_seqs, Hkv, 128], v_new alike)
+// the kernel also writes the step's new tokens to their slots first.
+static pa_status_t decode_balanced_impl(const void* q, const void* kv_cache, int64_t num_blocks,
+                                        int block_size, const int32_t* block_table,
+                                        int max_blocks_per_seq, const int32_t* seq_lens,
+                                        int num_seqs, int num_q_heads, int num_kv_heads,
+                                        int head_dim, float scale, int num_ranges, void* workspace,
+                                        size_t workspace_bytes, void* out, float* lse,
+                                        const void* k_new, const void* v_new,
+                                        const int64_t* slots, hipStream_t stream) {
   PA_REQUIRE(scale_ok(scale), PA_ERR_INVALID, "scale must be finite and >= 0");
   PA_REQUIRE(num_seqs >= 0, PA_ERR_INVALID, "num_seqs must be >= 0 (got %d)", num_seqs);
   pa_status_t st = check_common_cache(num_blocks, block_size, block_table, max_blocks_per_seq,
@@ -470,9 +486,24 @@ pa_status_t pa_decode_balanced(const void* q, const void* kv_cache, int64_t num_
                        seq_lens, num_seqs, int(cap > INT_MAX ? INT_MAX : cap), num_q_heads,
                        num_kv_heads, scale, num_ranges, balanced_cu(workspace),
                        balanced_part(workspace, num_seqs), out, lse};
+  d.k_new = k_new;
+  d.v_new = v_new;
+  d.slots = slots;
   hipError_t e = pa::launch_decode_balanced(d, stream);
   if (e != hipSuccess) return hip_fail(e, "balanced decode launch");
   return ok();
+}
+
+pa_status_t pa_decode_balanced(const void* q, const void* kv_cache, int64_t num_blocks,
+                               int block_size, const int32_t* block_table,
+                               int max_blocks_per_seq, const int32_t* seq_lens, int num_seqs,
+                               int num_q_heads, int num_kv_heads, int head_dim, float scale,
+                               int num_ranges, void* workspace, size_t workspace_bytes,
+                               void* out, float* lse, hipStream_t stream) {
+  return decode_balanced_impl(q, kv_cache, num_blocks, block_size, block_table,
+                              max_blocks_per_seq, seq_lens, num_seqs, num_q_heads, num_kv_heads,
+                              head_dim, scale, num_ranges, workspace, workspace_bytes, out, lse,
+                              nullptr, nullptr, nullptr, stream);
 }
 
 pa_status_t pa_decode_balanced_merge(void* workspace, size_t workspace_bytes, int num_seqs,

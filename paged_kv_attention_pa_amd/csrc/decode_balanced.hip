@@ -52,12 +52,50 @@ __global__ __launch_bounds__(64 * kHeads, 1) void decode_balanced_kernel(DecodeB
   const int hg = blockIdx.x % n_hg;
   const int j = blockIdx.x / n_hg;
 
+  const int h = hg * kHeads + wave;   // < Hkv: the launch gives every head group whole waves
+
+  // The step's new tokens, when the decode writes them itself (bf16 cache):
+  // the range that holds a request's last chunk writes its row (each wave its
+  // KV head: lanes 0-15 the K row, 16-31 the V row) before any load, range 0
+  // also those of requests with no keys (no range holds them); after the
+  // stores have completed and a barrier, every load of the range sees them
+  // (no other range reads a request's last token).
+  const bool write_new = !kFp8 && a.k_new != nullptr;
+  const int64_t new_tok_bytes = int64_t(a.num_kv_heads) * kD * 2;
+  auto write_token = [&](int r) {
+    const int64_t slot = uniform_load(a.slots + r);
+    if (slot < 0 || slot >= a.num_blocks * a.block_size || lane >= 32) return;
+    const int plane = lane >> 4, c = lane & 15;
+    const int64_t blk = slot / a.block_size, off = slot - blk * a.block_size;
+    const char* src = static_cast<const char*>(plane ? a.v_new : a.k_new) +
+                      (int64_t(r) * a.num_kv_heads + h) * (kD * 2) + 16 * c;
+    char* dst = static_cast<char*>(const_cast<void*>(a.cache)) +
+                ((blk * 2 + plane) * a.block_size + off) * new_tok_bytes + h * (kD * 2) + 16 * c;
+    *reinterpret_cast<u32x4_t*>(dst) = load16(src);
+  };
+  if (write_new && j == 0) {
+    for (int r = 0; r < B; ++r)
+      if (clamp_len(uniform_load(a.seq_lens + r), cap) == 0) write_token(r);
+  }
+
   int c0, c1;
   ChunkPos cur;
   if (!balanced_range(a.seq_lens, B, cap, a.num_ranges, j, j == 0 && hg == 0, a.cu, s_wave_sum,
                       s_start, c0, c1, cur))
     return;
-  const int h = hg * kHeads + wave;   // < Hkv: the launch gives every head group whole waves
+  if (write_new) {
+    ChunkPos p = cur;   // holds chunk c0
+    for (;;) {
+      const int n = chunks_of(p.len);
+      const int last = p.base + n - 1;   // the request's last chunk
+      if (last >= c1) break;             // held by a later range
+      write_token(p.r);
+      if (last + 1 >= c1) break;
+      p = next_chunk(ChunkPos{p.r, n - 1, p.len, p.base}, a.seq_lens, cap, B);
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the stores have completed
+    __syncthreads();
+  }
 
   const int li = lane & 15;   // MFMA row/column index; 16-byte chunk of a loaded row
   const int kq = lane >> 4;   // 16-lane group; token within a 4-token load

@@ -84,6 +84,9 @@ struct DecodeBalanced {
   void* out; float* lse;
   // FP8 (E4M3) cache: keys are code * k_scale, values code * v_scale
   int fp8; float k_scale; float v_scale;
+  // bf16 only: the step's new tokens, k_new / v_new [num_seqs, Hkv, 128],
+  // written by the kernel itself to slots[r] (NULL: no write)
+  const void* k_new; const void* v_new; const int64_t* slots;
 };
 hipError_t launch_decode_balanced(const DecodeBalanced& a, hipStream_t s);
 

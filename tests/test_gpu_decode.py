@@ -6,6 +6,7 @@ requests of the full-size workloads.  Cache writes and integer work are
 bit-exact; outputs are within |gpu - oracle| <= 1e-2 + 1e-2 |oracle|; LSE
 within 1e-3.
 """
+import dataclasses
 import math
 
 import numpy as np
@@ -113,6 +114,26 @@ def test_decode_small(ci, splits):
     assert np.array_equal(bits(cache_t).view(np.uint8), cache_ref.view(np.uint8))
     check_close(out, oref, f"{name} out")
     check_lse(lse, lref, f"{name} lse")
+
+
+@pytest.mark.parametrize("hkv", [8, 16])
+def test_decode_writes_every_new_token(hkv):
+    """The automatic (balanced) bf16 decode writes the step's new tokens
+    itself: every request's row lands in its slot, also for a request whose
+    seq_len is 0 (no key to attend, but a slot), and a negative slot is
+    skipped; the cache after the call is the oracle's write bit for bit."""
+    say(f"decode fused write hkv={hkv}")
+    b = _small(119 + hkv, [300, 1, 900, 1, 17, 64], 4 * hkv, hkv, W.BF16)
+    seq = b.seq_lens.copy()
+    seq[[1, 3]] = 0
+    b = dataclasses.replace(b, seq_lens=seq)
+    b.slot_mapping[3] = -1   # a request with no key and no slot: nothing written
+    cache_t, out, lse = _run_decode(b, num_splits=0)
+    cache_ref, oref, lref = _oracle_decode(b)
+    assert np.array_equal(bits(cache_t).view(np.uint8), cache_ref.view(np.uint8))
+    assert np.all(out[[1, 3]] == 0) and np.all(np.isneginf(lse[[1, 3]]))
+    check_close(out, oref, "fused write out")
+    check_lse(lse, lref, "fused write lse")
 
 
 def test_decode_tiny_workload():
