@@ -9,7 +9,7 @@
 //
 // gfx950 mapping.  One work-group of 4 waves (one per SIMD) walks a run of
 // 32-key tiles for all H <= 128 query heads; wave w owns heads 32w..32w+31
-// (heads past H are zero queries whose results are dropped).  Every head
+// (heads past H compute head 0's scores; their results are dropped).  Every head
 // reads the same latent row, so both products are dense contractions on
 // v_mfma_f32_32x32x16_bf16, computed transposed so that each lane owns one
 // head:
@@ -20,11 +20,16 @@
 // twice the MFMA work of a 16-head split, and the 256-register O^T
 // accumulator lives in the AGPRs of a wave that has its SIMD to itself.
 // Each latent row is fetched from HBM once per work-group into an LDS tile
-// (global_load_lds_dwordx4, four buffers: three tiles in flight) and feeds
-// both products.  The LDS operand reads are issued as inline assembly and
-// waited for explicitly, three MFMAs ahead: the compiler cannot tell the
-// DMA-filled buffers apart and would otherwise wait for every load in
-// flight before reading any of them.
+// (global_load_lds_dwordx4, four buffers) and feeds both products.  The
+// tiles are software-pipelined: while tile t's scores are computed, tile t - 1
+// waits for its value product, which runs with tile t's softmax in its MFMA
+// shadow, and tiles t + 1, t + 2 are loading.  The LDS operand reads are
+// issued as inline assembly and waited for explicitly, three MFMAs ahead: the
+// compiler cannot tell the DMA-filled buffers apart and would otherwise wait
+// for every load in flight before reading any of them.  Per tile and
+// work-group the four waves read 144 KB of K and 128 KB of V^T from LDS (each
+// wave the whole tile), which with the tile's 36 KB of DMA writes makes LDS
+// bandwidth, not the MFMAs, this kernel's limit.
 #include "balanced.hpp"
 #include "launch.hpp"
 #include "pa_device.hpp"
@@ -48,6 +53,7 @@ struct MlaDims {
   static constexpr int kRank = R;
   static constexpr int kRow = R + kRope;                   // elements per latent row
   static constexpr int kChunks = kRow * 2 / 16;            // 16-byte chunks per row
+  static constexpr int kCG = kChunks / 8;                  // 8-chunk groups per row
   static constexpr int kRowBytes = kRow * 2;               // unpadded (swizzled)
   static constexpr int kTileBytes = kBN * kRowBytes;
   static constexpr int kTileLoads = kBN * kChunks / 64;    // wave-wide 16-byte loads per tile
@@ -57,6 +63,8 @@ struct MlaDims {
   static_assert(kTileLoads % kWaves == 0 && kKSteps % 4 == 0 && kDTiles % 2 == 0, "tiling");
   static_assert(kStages * kTileBytes <= 160 * 1024 - 64, "LDS budget");
   static_assert(2 * kLoadsPerWave < 64, "vmcnt range");
+  static_assert(kChunks % 8 == 0 && kLoadsPerWave == kCG && kBN == 8 * kWaves,
+                "one row-block of the tile per wave");
 };
 
 // s_waitcnt immediate for "at most n vector-memory operations outstanding"
@@ -64,19 +72,28 @@ struct MlaDims {
 template <int N>
 constexpr int vmcnt_imm() { return (N & 15) | ((N >> 4) << 14) | 0x0F70; }
 
-// 16-byte chunk c of latent row r sits in LDS slot c ^ sx(r) of the row (the
-// XOR stays inside c's aligned group of eight), with sx(r) holding bits 1, 2
-// and 3 of r in reverse order.  Rows are 1152 B = 72 slots, so the bank
-// offset of a row alternates with r % 2; sx then makes
+// LDS tile layout.  A tile is cut into 1 KiB blocks of 8 rows x 8 chunks
+// (16-byte chunks, 128 bytes of a row): block (m, k) holds rows 8m .. 8m+7,
+// chunks 8k .. 8k+7, and sits at 1024 (kCG m + k), kCG = chunk groups per
+// row (9 for the 576-element row, 5 for the 320-element one).  Inside a
+// block, row r takes 128 bytes at 128 (r % 8), and chunk c of it sits in slot
+// (c % 8) ^ sx(r), with sx(r) holding bits 1, 2 and 3 of r in reverse order.
+// Modulo the 256 bytes of one pass over the banks an address is then
+// 128 (r % 2) + 16 ((c % 8) ^ sx(r)), so
 // * a 16-lane phase of a K-fragment read (16 consecutive rows, one chunk)
-//   hit 16 distinct 16-byte bank groups, and
+//   hits 16 distinct 16-byte bank groups, and
 // * a 32-lane phase of a V^T transposing read (4 consecutive rows 4q..4q+3,
-//   4 consecutive chunks 4m..4m+3, both 8-byte halves) do the same,
-// so neither read has bank conflicts.
+//   4 consecutive chunks 4m..4m+3, both 8-byte halves) does the same,
+// so neither read has bank conflicts.  A block is one wave-wide 16-byte DMA
+// load whose lanes fetch from 8 rows of the cache: wave w fetches row-block
+// w, one per-lane address per tile plus 128 k for block k.
 __device__ __forceinline__ int sx(int r) {
   return (((r >> 1) & 1) << 2) | (((r >> 2) & 1) << 1) | ((r >> 3) & 1);
 }
-__device__ __forceinline__ int slot_of(int r, int c) { return (c & ~7) | ((c & 7) ^ sx(r)); }
+template <int kCG>
+__device__ __forceinline__ int lds_off(int r, int c) {
+  return 1024 * (kCG * (r >> 3) + (c >> 3)) + 128 * (r & 7) + 16 * ((c & 7) ^ sx(r));
+}
 
 // The two products are issued as inline assembly so that each keeps its own
 // register file: the 256-register O^T accumulator in AGPRs, the score
@@ -216,26 +233,15 @@ __global__ __launch_bounds__(64 * kWaves, 1) void mla_kernel(MlaDecode a) {
     for (int kk = 0; kk < kRope / 16; ++kk) qf[kRank / 16 + kk] = load16(qp + 16 * kk);
   };
 
-  // ---- gather of a tile straight into LDS: 36 wave-wide loads of 64 x 16 B
-  // (global_load_lds_dwordx4; lane i lands at byte 16 i of the load's 1 KiB),
-  // wave w issuing loads w, w + 4, ...  Position p = 64 j + i of load j is
-  // row p / 72, slot p % 72, which holds chunk slot_of(row, slot) (the XOR
-  // is an involution).  The lane's byte offset within a tile of contiguous
-  // rows is fixed (goff); rows whose key lies on the next page, or at or
-  // past kend (re-read as key kend - 1: finite, masked out below), take a
-  // per-tile correction.
-  const uint16_t* cache = static_cast<const uint16_t*>(a.cache);
-  // (sized for the largest row: with a size that depends on the template
-  // arguments, the array captured by the gather lambda cost the kernel its
-  // host-side launch stub)
-  uint32_t goff[MlaDims<512>::kLoadsPerWave];
-#pragma unroll
-  for (int jj = 0; jj < kLoadsPerWave; ++jj) {
-    const int pos = 64 * (wave + kWaves * jj) + lane;
-    const int row = pos / kChunks;
-    const int slot = pos - row * kChunks;
-    goff[jj] = uint32_t(row * kRowBytes + 16 * slot_of(row, slot));
-  }
+  // ---- gather of a tile straight into LDS (global_load_lds_dwordx4; lane i
+  // lands at byte 16 i of the load's 1 KiB): wave w fetches row-block w, lane
+  // i row 8 w + i / 8, slot i % 8 of each of the row's kCG blocks.  The lane's
+  // source is one address per tile: its row on page b0 or b1, the chunk of
+  // its slot; block k adds 128 k.  Rows at or past kend re-read key kend - 1
+  // (finite, masked out below).
+  const char* cache = static_cast<const char*>(a.cache);
+  const int my_row = 8 * wave + (lane >> 3);
+  const int lane_sw = 16 * ((lane & 7) ^ sx(my_row));
   // Page ids of a tile's first and last key (scalar loads).  They are read a
   // step before the gather that uses them, at the end of the previous tile's
   // compute: a scalar load waited for right before its use would stall the
@@ -248,38 +254,28 @@ __global__ __launch_bounds__(64 * kWaves, 1) void mla_kernel(MlaDecode a) {
     const int kl0 = min(key0, kend - 1), kl1 = min(key0 + kBN - 1, kend - 1);
     return Pages{uniform_load(table + kl0 / bs), uniform_load(table + kl1 / bs)};
   };
-  auto gload = [&](const ChunkPos& p, int stage, const Pages& pg) {
+  auto gsrc = [&](const ChunkPos& p, const Pages& pg) __attribute__((always_inline)) {
     const int key0 = kb + p.lc * kBN;
-    const int kend = p.len;
     int64_t b0 = pg.b0, b1 = pg.b1;
     b0 = (b0 < 0 || b0 >= a.num_blocks) ? 0 : b0;
     b1 = (b1 < 0 || b1 >= a.num_blocks) ? 0 : b1;
-    const int in0 = key0 - (key0 / bs) * bs;      // key0's row within page b0
-    // row 0 of the tile as a byte address; the rows run on contiguously
-    // while they stay on page b0 and below kend
-    const char* base0 = reinterpret_cast<const char*>(cache) + (b0 * bs + in0) * int64_t(kRowBytes);
-    const bool simple = in0 + kBN <= bs && key0 + kBN <= kend;   // wave-uniform
-    typedef __attribute__((address_space(3))) void* lds_ptr;
-    char* dst = smem + stage * kTileBytes;
-    // cache policy 2 = non-temporal: every latent row is read once
-    if (simple) {
+    const int in0 = key0 - (key0 / bs) * bs;        // key0's row within page b0
+    const int ip = in0 + min(my_row, p.len - 1 - key0);   // row within page b0, may run past it
+    const int64_t row = ip < bs ? b0 * bs + ip : b1 * bs + (ip - bs);
+    return cache + row * kRowBytes + lane_sw;
+  };
+  typedef __attribute__((address_space(3))) void* lds_ptr;
+  // block k of the tile in buffer `stage`; cache policy 2 = non-temporal:
+  // every latent row is read once
+  auto gissue = [&](const char* src, int stage, int k) __attribute__((always_inline)) {
+    __builtin_amdgcn_global_load_lds(src + 128 * k,
+                                     (lds_ptr)(smem + stage * kTileBytes + 1024 * (Dm::kCG * wave + k)),
+                                     16, 0, 2);
+  };
+  auto gload = [&](const ChunkPos& p, int stage, const Pages& pg) __attribute__((always_inline)) {
+    const char* src = gsrc(p, pg);
 #pragma unroll
-      for (int jj = 0; jj < kLoadsPerWave; ++jj)
-        __builtin_amdgcn_global_load_lds(base0 + goff[jj],
-                                         (lds_ptr)(dst + 1024 * (wave + kWaves * jj)), 16, 0, 2);
-    } else {
-      const int last = kend - 1 - key0;             // tile row of key kend - 1
-      const char* base1 = reinterpret_cast<const char*>(cache) +
-                          (b1 * bs - (bs - in0)) * int64_t(kRowBytes);   // row bs - in0 -> page b1 row 0
-#pragma unroll
-      for (int jj = 0; jj < kLoadsPerWave; ++jj) {
-        const int row = int(goff[jj] / uint32_t(kRowBytes));
-        const int rr = min(row, last);
-        const int64_t off = int64_t(goff[jj]) + int64_t(rr - row) * kRowBytes;
-        const char* src = (in0 + rr < bs ? base0 : base1) + off;
-        __builtin_amdgcn_global_load_lds(src, (lds_ptr)(dst + 1024 * (wave + kWaves * jj)), 16, 0, 2);
-      }
-    }
+    for (int k = 0; k < kLoadsPerWave; ++k) gissue(src, stage, k);
   };
   auto gwait = [&]() { __builtin_amdgcn_s_waitcnt(0x0F70); };   // vmcnt(0)
 
@@ -351,7 +347,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void mla_kernel(MlaDecode a) {
       const int ch = pos - row * kChunks;
       const u32x4_t w = u32x4_t{fp8x2_to_bf16x2<false>(c[i].x), fp8x2_to_bf16x2<true>(c[i].x),
                                 fp8x2_to_bf16x2<false>(c[i].y), fp8x2_to_bf16x2<true>(c[i].y)};
-      const uint32_t addr = dst + uint32_t(row * kRowBytes + 16 * slot_of(row, ch));
+      const uint32_t addr = dst + uint32_t(lds_off<Dm::kCG>(row, ch));
       lds_write16_at(addr, w);
     }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
@@ -364,7 +360,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void mla_kernel(MlaDecode a) {
   uint32_t kaddr[4];
 #pragma unroll
   for (int kq = 0; kq < 4; ++kq)
-    kaddr[kq] = lds0 + c32 * kRowBytes + 16 * slot_of(c32, 2 * kq + g);
+    kaddr[kq] = lds0 + lds_off<Dm::kCG>(c32, 2 * kq + g);
   // V^T fragment of d-tile m = 2 mh + ml and key step st, read e (0, 1):
   // within each 16-lane group, lane 4 q + i reads key row 16 st + 8 e + 4 g
   // + q, dims 32 m + 16 (lane / 16 % 2) + 4 i .. + 4 (chunk 4 m + c0, half
@@ -381,7 +377,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void mla_kernel(MlaDecode a) {
       const int row = 8 * e + 4 * g + q4;
 #pragma unroll
       for (int ml = 0; ml < 2; ++ml)
-        vaddr[e][ml] = lds0 + row * kRowBytes + 16 * slot_of(row, 4 * ml + cg) + 8 * (i4 & 1);
+        vaddr[e][ml] = lds0 + lds_off<Dm::kCG>(row, 4 * ml + cg) + 8 * (i4 & 1);
     }
   }
 
@@ -391,7 +387,6 @@ __global__ __launch_bounds__(64 * kWaves, 1) void mla_kernel(MlaDecode a) {
   const float scale2 = fmaxf((kFp8 ? a.scale * a.kv_scale : a.scale) * kLog2e, 0x1p-126f);
   float m_run = kNoMax;
   float l_run = 0.0f;          // this lane's share of head `head`'s sum
-  bool fresh = true;           // acc holds nothing yet (no rescale needed)
   f32x16_t acc[kDTiles];       // O^T: d = 32 m + 8 (r / 4) + 4 g + r % 4
 #pragma unroll
   for (int m = 0; m < kDTiles; ++m)
@@ -457,9 +452,10 @@ __global__ __launch_bounds__(64 * kWaves, 1) void mla_kernel(MlaDecode a) {
     (void)pstride;
   };
 
-  // Tile pipeline: kStages - 1 tiles are loading while one is computed.  Each
-  // wave issues 9 of a tile's 36 loads, so "tile t has landed" is "at most
-  // 9 x (tiles issued after t) loads outstanding".
+  // Tile pipeline (bf16): while tile t's scores and tile t - 1's values are
+  // computed, kStages - 2 tiles are loading.  Each wave issues 9 of a tile's
+  // 36 loads, so "tile t has landed" is "at most 9 x (tiles issued after t)
+  // loads outstanding".
   auto wait_tiles = [&](int k) {   // k = tiles issued after the one waited for
     if (k <= 0) __builtin_amdgcn_s_waitcnt(0x0F70);                               // vmcnt(0)
     else if (k == 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm<Dm::kLoadsPerWave>());
@@ -478,13 +474,47 @@ __global__ __launch_bounds__(64 * kWaves, 1) void mla_kernel(MlaDecode a) {
   zero_pad_q();
   ChunkPos ld = cur;   // next tile to load
   int n_loaded = 0;
-  constexpr int kDepth = kFp8 ? kF8Stages : kStages;   // staging buffers
-  for (; n_loaded < kDepth - 1 && n_loaded < n_tiles; ++n_loaded) {
+  constexpr int kAhead = kFp8 ? kF8Stages - 1 : kStages - 2;   // tiles loaded ahead
+  for (; n_loaded < kAhead && n_loaded < n_tiles; ++n_loaded) {
     if constexpr (kFp8) gload8(ld, n_loaded, pages(ld));
     else gload(ld, n_loaded, pages(ld));
     if (n_loaded + 1 < n_tiles) ld = advance(ld);
   }
   Pages pg_next = pages(ld);   // ld stays inside the run, so this read is in bounds
+
+  // O^T += V^T P^T over the tile at LDS offset `off`: step n = 16 st + m
+  // (d-tile m, key step st), two transposing reads per step, issued kVDepth
+  // steps ahead; between(n) runs right after step n's MFMA
+  auto pv = [&](const u32x4_t (&pfx)[2], uint32_t off, auto&& between) __attribute__((always_inline)) {
+    uint32_t vb[2][2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e)
+#pragma unroll
+      for (int ml = 0; ml < 2; ++ml) vb[e][ml] = vaddr[e][ml] + off;
+    constexpr int kD = kVDepth;
+    u32x2_t vr[kD + 1][2];
+    auto vissue = [&](auto nc) __attribute__((always_inline)) {
+      constexpr int n = decltype(nc)::value, st = n / kDTiles, m = n % kDTiles;
+      constexpr int o = 2048 * Dm::kCG * st + 1024 * (m / 2);   // row-blocks 2 st.., block m / 2
+      vr[n % (kD + 1)][0] = lds_read_tr_at<o>(vb[0][m % 2]);
+      vr[n % (kD + 1)][1] = lds_read_tr_at<o>(vb[1][m % 2]);
+    };
+    static_for<kD>([&](auto nc) __attribute__((always_inline)) { vissue(nc); });
+    static_for<2 * kDTiles>([&](auto nc) __attribute__((always_inline)) {
+      constexpr int n = decltype(nc)::value, st = n / kDTiles, m = n % kDTiles;
+      constexpr int kN = 2 * kDTiles;
+      constexpr int kLeft = 2 * (n + kD < kN ? kD : kN - 1 - n);
+      if constexpr (n + kD < kN) vissue(std::integral_constant<int, n + kD>{});
+      lds_wait<kLeft>(vr[n % (kD + 1)][0], vr[n % (kD + 1)][1]);
+      const u32x4_t vf = u32x4_t{vr[n % (kD + 1)][0].x, vr[n % (kD + 1)][0].y,
+                                 vr[n % (kD + 1)][1].x, vr[n % (kD + 1)][1].y};
+      mfma_o(acc[m], vf, pfx[st]);
+      between(nc);
+    });
+  };
+  bool pend = false;           // the previous tile's value product is still to do,
+  u32x4_t pf_prev[2] = {};     // with this P^T
+  uint32_t prev_off = 0;       // over this LDS buffer
 
   // Segments: the tiles of one request within this work-group's run.  The
   // segment boundary work (write the segment, reset, load the next q) sits
@@ -499,9 +529,22 @@ __global__ __launch_bounds__(64 * kWaves, 1) void mla_kernel(MlaDecode a) {
     // waited for).  A bare barrier: __syncthreads() would also wait for the
     // loads of the tiles still in flight.
     __builtin_amdgcn_s_barrier();
-    if (n_loaded < n_tiles) {       // refill the buffer of tile t - 1
-      if constexpr (kFp8) gload8(ld, n_loaded % kF8Stages, pg_next);
-      else gload(ld, n_loaded % kStages, pg_next);
+    // Refill the buffer of tile t - 1.  The bf16 tile's loads are spread
+    // through the score MFMAs below (one every four k-steps): issued back to
+    // back they would hold the wave for the ~16 cycles per load that the CU's
+    // address unit takes.
+    bool refill = false;
+    const char* rsrc = cache;
+    int rstage = 0;
+    if (n_loaded < n_tiles) {
+      if constexpr (kFp8) {
+        gload8(ld, n_loaded % kF8Stages, pg_next);
+      } else {
+        rsrc = gsrc(ld, pg_next);
+        rstage = n_loaded % kStages;
+        refill = true;
+        if (!active) gload(ld, rstage, pg_next);   // no MFMAs to spread them over
+      }
       if (++n_loaded < n_tiles) ld = advance(ld);
     }
     if constexpr (kFp8) {
@@ -524,12 +567,12 @@ __global__ __launch_bounds__(64 * kWaves, 1) void mla_kernel(MlaDecode a) {
         for (int kq = 0; kq < 4; ++kq) kb4[kq] = kaddr[kq] + st_off;
         constexpr int kD = kKDepth;
         u32x4_t kr[kD + 1];
-        auto issue = [&](auto kc) {
+        auto issue = [&](auto kc) __attribute__((always_inline)) {
           constexpr int kk = decltype(kc)::value;
-          kr[kk % (kD + 1)] = lds_read16_at<128 * (kk / 4)>(kb4[kk % 4]);
+          kr[kk % (kD + 1)] = lds_read16_at<1024 * (kk / 4)>(kb4[kk % 4]);   // block kk / 4
         };
-        static_for<kD>([&](auto kc) { issue(kc); });
-        static_for<kKSteps>([&](auto kc) {
+        static_for<kD>([&](auto kc) __attribute__((always_inline)) { issue(kc); });
+        static_for<kKSteps>([&](auto kc) __attribute__((always_inline)) {
           constexpr int kk = decltype(kc)::value;
           // reads of k-steps kk + 1 .. kk + kD may stay in flight
           constexpr int kLeft = kk + kD < kKSteps ? kD : kKSteps - 1 - kk;
@@ -537,87 +580,104 @@ __global__ __launch_bounds__(64 * kWaves, 1) void mla_kernel(MlaDecode a) {
           lds_wait1<kLeft>(kr[kk % (kD + 1)]);
           if constexpr (kk == 0) mfma_s0(sc, kr[0], qf[0]);
           else mfma_s(sc, kr[kk % (kD + 1)], qf[kk]);
+          if constexpr (!kFp8 && kk % 4 == 2 && kk / 4 < kLoadsPerWave) {
+            if (refill) gissue(rsrc, rstage, kk / 4);
+          }
         });
         // the VALU reads the scores: 16 wait states after the last MFMA
         asm volatile("s_nop 15" : "+v"(sc));
       }
-      if (key0 + kBN > kend) {   // tail tile: keys at or past kend weigh 0
+
+      // Online softmax of tile t in pieces, piece n placed after MFMA n of
+      // the previous tile's value product (when there is one), so that it
+      // runs in the MFMAs' shadow; the empty asm statements hold each piece
+      // between its neighbours.  Lazy rescale: the reference max only moves
+      // when a head's max grows by more than kSlack (log2 units), so
+      // p <= 2^kSlack in between; the accumulator itself is rescaled after
+      // that product.
+      float tmax = -INFINITY, m_new = m_run, alpha = 1.0f, psum = 0.0f;
+      bool need = false;
+      float pr[16];
+      u32x4_t pf[2];
+      auto sm = [&](auto nc) __attribute__((always_inline)) {
+        constexpr int n = decltype(nc)::value;
+        if constexpr (n == 0) {
+          if (key0 + kBN > kend) {   // tail tile: keys at or past kend weigh 0
 #pragma unroll
-        for (int i = 0; i < 16; ++i)
-          if (key0 + 8 * (i >> 2) + 4 * g + (i & 3) >= kend) sc[i] = -INFINITY;
-      }
-      float tmax = -INFINITY;
+            for (int i = 0; i < 16; ++i)
+              if (key0 + 8 * (i >> 2) + 4 * g + (i & 3) >= kend) sc[i] = -INFINITY;
+          }
 #pragma unroll
-      for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, sc[i]);
-      tmax = xor32_max(tmax);
-      const float tm = tmax == -INFINITY ? -INFINITY : tmax * scale2;
-      // lazy rescale: the reference max only moves when a head's max grows by
-      // more than kSlack (log2 units); p <= 2^kSlack in between
-      if (__any(tm > m_run + kSlack)) {
-        const float m_new = fmaxf(m_run, tm);
-        const float alpha = fast_exp2(m_run - m_new);
-        m_run = m_new;
-        l_run *= alpha;
-        if (!fresh) {   // one accumulator tile at a time through the VGPRs
+          for (int i = 0; i < 8; ++i) tmax = fmaxf(tmax, sc[i]);
+          asm volatile("" : "+v"(tmax));
+        } else if constexpr (n == 1) {
+#pragma unroll
+          for (int i = 8; i < 16; ++i) tmax = fmaxf(tmax, sc[i]);
+          tmax = xor32_max(tmax);
+          const float tm = tmax == -INFINITY ? -INFINITY : tmax * scale2;
+          need = __any(tm > m_run + kSlack);
+          m_new = need ? fmaxf(m_run, tm) : m_run;
+          asm volatile("" : "+v"(m_new));
+        } else if constexpr (n == 2) {
+          alpha = fast_exp2(m_run - m_new);
+          asm volatile("" : "+v"(alpha));
+        } else if constexpr (n >= 3 && n < 19) {
+          constexpr int i = n - 3;
+          float x = sc[i];
+          asm volatile("" : "+v"(x));
+          pr[i] = fast_exp2(fmaf(x, scale2, -m_new));
+          psum += pr[i];
+          asm volatile("" : "+v"(pr[i]), "+v"(psum));
+        } else if constexpr (n >= 19 && n < 23) {
+          constexpr int w = 2 * (n - 19);   // words w, w + 1 of the 8 of P^T
+          uint32_t lo = pack_bf16x2(pr[2 * w], pr[2 * w + 1]);
+          uint32_t hi = pack_bf16x2(pr[2 * w + 2], pr[2 * w + 3]);
+          asm volatile("" : "+v"(lo), "+v"(hi));
+          pf[w / 4][w % 4] = lo;
+          pf[w / 4][w % 4 + 1] = hi;
+        } else if constexpr (n == 23) {
+          l_run = l_run * alpha + psum;
+          m_run = m_new;
+          asm volatile("" : "+v"(l_run), "+v"(m_run));
+        }
+      };
+      constexpr int kSmPieces = 24;
+      if (pend) {
+        // O^T += V^T P^T of tile t - 1, softmax of tile t in its shadow:
+        // pieces [n P / N, (n + 1) P / N) after MFMA n of N
+        pv(pf_prev, prev_off, [&](auto nc) __attribute__((always_inline)) {
+          constexpr int kN = 2 * kDTiles, n = decltype(nc)::value;
+          constexpr int lo = n * kSmPieces / kN, hi = (n + 1) * kSmPieces / kN;
+          static_for<hi - lo>([&](auto jc) __attribute__((always_inline)) {
+            sm(std::integral_constant<int, lo + decltype(jc)::value>{});
+          });
+        });
+        if (need) {   // rescale the accumulator, one tile at a time through the VGPRs
+          acc_fence<15>(acc);   // the value product's last results are in
 #pragma unroll
           for (int m = 0; m < kDTiles; ++m) {
             asm volatile("" : "+a"(acc[m]));
             acc[m] *= alpha;
             asm volatile("" : "+a"(acc[m]));
           }
+          acc_fence<4>(acc);   // written by the VALU, read by the next MFMAs
         }
+      } else {
+        static_for<kSmPieces>([&](auto nc) __attribute__((always_inline)) { sm(nc); });
       }
-      fresh = false;
-      u32x4_t pf[2];
-      float psum = 0.0f;
-#pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        float p[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          p[i] = fast_exp2(fmaf(sc[8 * st + i], scale2, -m_run));
-          psum += p[i];
-        }
-        pf[st] = u32x4_t{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
-                         pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])};
-      }
-      l_run += psum;
-      // P (and a rescaled accumulator) written by the VALU, read by the MFMA
-      asm volatile("s_nop 4" : "+v"(pf[0]), "+v"(pf[1]));
-      acc_fence<4>(acc);
-
-      // O^T += V^T P^T: step n = 16 st + m (d-tile m, key step st), two
-      // transposing reads per step, issued kVDepth steps ahead
-      {
-        uint32_t vb[2][2];
-#pragma unroll
-        for (int e = 0; e < 2; ++e)
-#pragma unroll
-          for (int ml = 0; ml < 2; ++ml) vb[e][ml] = vaddr[e][ml] + st_off;
-        constexpr int kD = kVDepth;
-        u32x2_t vr[kD + 1][2];
-        auto vissue = [&](auto nc) {
-          constexpr int n = decltype(nc)::value, st = n / kDTiles, m = n % kDTiles;
-          constexpr int off = 16 * st * kRowBytes + 128 * (m / 2);
-          vr[n % (kD + 1)][0] = lds_read_tr_at<off>(vb[0][m % 2]);
-          vr[n % (kD + 1)][1] = lds_read_tr_at<off>(vb[1][m % 2]);
-        };
-        static_for<kD>([&](auto nc) { vissue(nc); });
-        static_for<2 * kDTiles>([&](auto nc) {
-          constexpr int n = decltype(nc)::value, st = n / kDTiles, m = n % kDTiles;
-          constexpr int kN = 2 * kDTiles;
-          constexpr int kLeft = 2 * (n + kD < kN ? kD : kN - 1 - n);
-          if constexpr (n + kD < kN) vissue(std::integral_constant<int, n + kD>{});
-          lds_wait<kLeft>(vr[n % (kD + 1)][0], vr[n % (kD + 1)][1]);
-          const u32x4_t vf = u32x4_t{vr[n % (kD + 1)][0].x, vr[n % (kD + 1)][0].y,
-                                     vr[n % (kD + 1)][1].x, vr[n % (kD + 1)][1].y};
-          mfma_o(acc[m], vf, pf[st]);
-        });
-      }
+      pf_prev[0] = pf[0];
+      pf_prev[1] = pf[1];
+      prev_off = st_off;
+      pend = true;
     }  // active
     if (n_loaded < n_tiles) pg_next = pages(ld);   // lands over the loop tail and the barrier
 
     if (t + 1 < seg_end) ++cur.lc;
+  }
+  if (pend) {   // the segment's last value product
+    asm volatile("s_nop 4" : "+v"(pf_prev[0]), "+v"(pf_prev[1]));   // P^T written by the VALU
+    pv(pf_prev, prev_off, [](auto) {});
+    pend = false;
   }
   if (t >= n_tiles) break;
   // end of this request's keys in the run (balanced schedule only: a split
@@ -629,7 +689,6 @@ __global__ __launch_bounds__(64 * kWaves, 1) void mla_kernel(MlaDecode a) {
     for (int i = 0; i < 16; ++i) acc[m][i] = 0.0f;
   m_run = kNoMax;
   l_run = 0.0f;
-  fresh = true;
   cur = advance(cur);
   load_q(cur.r);
   gwait();   // q (and every tile load so far) has landed
