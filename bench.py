@@ -89,7 +89,7 @@ def gqa_decode_case(b, num_splits, name, split_sweep=False):
     bt, sl = _dev(b.block_table), _dev(b.seq_lens)
     kn, vn, sm = _dev(b.k_new), _dev(b.v_new), _dev(b.slot_mapping)
     cus = pa.device_num_cus()
-    n = num_splits or pa.num_kv_splits(b.max_seq_len, cus)
+    n = num_splits or pa.decode_num_kv_splits(b.num_seqs, b.num_kv_heads, b.max_seq_len, cus)
     g = b.num_q_heads // b.num_kv_heads
     # the automatic schedule (num_splits = 0) of bf16 decode over more than one
     # split's worth of keys is the token-balanced one

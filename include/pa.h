@@ -82,6 +82,18 @@ typedef enum {
  * this library's reading).  num_cus <= 0 is treated as 1. */
 int pa_num_kv_splits(int max_seq_len, int num_cus);
 
+/* Split count pa_decode (and pa_plan_mixed's decode group) uses when called
+ * with num_splits = 0.  It starts from pa_num_kv_splits(max_seq_len,
+ * num_cus); when that rule splits at all (n > 1) and the batch has fewer
+ * than 2 * num_cus (request, KV head) pairs, it is raised until
+ * num_seqs * num_kv_heads * n reaches 2 * num_cus, with no split shorter
+ * than 64 keys (n <= ceil(max_seq_len / 64)) and n <= 2 * num_cus.  The
+ * pages' rule sizes splits from the sequence length only, which leaves most
+ * compute units idle for a batch of a few requests; a larger batch keeps the
+ * rule's count.  Non-positive num_seqs, num_kv_heads or num_cus count as 1.
+ * Size the workspace with it (or call pa_decode_workspace_size). */
+int pa_decode_num_kv_splits(int num_seqs, int num_kv_heads, int max_seq_len, int num_cus);
+
 /* Bytes of fp32 workspace pa_decode / pa_mla_decode need for num_splits
  * splits: num_seqs * num_q_heads * num_splits * (head_dim_v + 1) * 4 (the
  * "+1" holds each split's lse, "Triton 與 MLA", 資料流).  Returns 0 if any
@@ -160,10 +172,11 @@ pa_status_t pa_cache_write(pa_layout_t layout, pa_dtype_t dtype,
  *              is the request's last position.
  * max_seq_len: host copy of max(seq_lens) (sets the split partition).
  * scale:       multiplies Q K^T before the softmax (1/sqrt(head_dim) usually).
- * num_splits:  0 = automatic: with n = pa_num_kv_splits(max_seq_len,
- *              pa_device_num_cus()), n == 1 runs one unsplit pass; n > 1 with
- *              PA_BF16, out != NULL and num_kv_heads 1, 2, 4 or a multiple
- *              of 8 runs the token-balanced schedule (pa_decode_balanced +
+ * num_splits:  0 = automatic: with n = pa_decode_num_kv_splits(num_seqs,
+ *              num_kv_heads, max_seq_len, pa_device_num_cus()), n == 1
+ *              runs one unsplit pass; n > 1 with PA_BF16, out != NULL and
+ *              num_kv_heads 1, 2, 4 or a multiple of 8 runs the
+ *              token-balanced schedule (pa_decode_balanced +
  *              pa_decode_balanced_merge), whose reduction order depends on
  *              the whole batch's lengths; otherwise n splits.
  *              1 = no split (each request reduced by one work unit, in an

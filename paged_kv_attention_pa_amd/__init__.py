@@ -13,14 +13,14 @@ Functions mirror the C entry points: ``cache_write``, ``decode``,
 ``cache_write_fp8`` + ``decode_fp8`` + ``prefill_varlen_fp8`` + ``mla_decode_fp8`` (an FP8 E4M3 cache with
 per-tensor scales), ``mla_prefill`` (MLA prefill in the multi-head form),
 ``mla_decode_balanced``, ``decode_balanced_merge``, plus the host helpers ``num_kv_splits``,
-``mla_num_kv_splits``, ``decode_workspace_bytes``,
+``decode_num_kv_splits``, ``mla_num_kv_splits``, ``decode_workspace_bytes``,
 ``decode_balanced_num_ranges``, ``decode_balanced_workspace_bytes``,
 ``device_num_cus``.
 """
 
 from ._binding import (  # noqa: F401
     PA_BF16, PA_F32, PA_LAYOUT_KV, PA_LAYOUT_MLA, PaError, EXPORTED_SYMBOLS,
-    cache_write, decode, decode_balanced, decode_balanced_merge,
+    cache_write, decode, decode_balanced, decode_balanced_merge, decode_num_kv_splits,
     decode_balanced_num_ranges, decode_balanced_workspace_bytes,
     decode_workspace_bytes, decode_workspace_size, mla_decode_workspace_size, decode_noalloc,
     NOALLOC_SCRATCH_BYTES, device_num_cus, last_error, MixedPlan, mixed_attention, plan_mixed,

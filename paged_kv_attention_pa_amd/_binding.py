@@ -23,6 +23,7 @@ _STATUS = {0: "PA_OK", 1: "PA_ERR_INVALID", 2: "PA_ERR_UNSUPPORTED",
 _vp, _i32, _i64, _f32, _sz = C.c_void_p, C.c_int, C.c_int64, C.c_float, C.c_size_t
 _SIGNATURES = {
     "pa_num_kv_splits": (_i32, [_i32, _i32]),
+    "pa_decode_num_kv_splits": (_i32, [_i32, _i32, _i32, _i32]),
     "pa_decode_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32]),
     "pa_mla_num_kv_splits": (_i32, [_i32, _i32, _i32]),
     "pa_device_num_cus": (_i32, []),
@@ -122,6 +123,11 @@ def _check(status: int):
 # ------------------------------------------------------------------ helpers
 def num_kv_splits(max_seq_len: int, num_cus: int) -> int:
     return library().pa_num_kv_splits(int(max_seq_len), int(num_cus))
+
+
+def decode_num_kv_splits(num_seqs: int, num_kv_heads: int, max_seq_len: int, num_cus: int) -> int:
+    return library().pa_decode_num_kv_splits(int(num_seqs), int(num_kv_heads), int(max_seq_len),
+                                             int(num_cus))
 
 
 def mla_num_kv_splits(num_seqs: int, max_seq_len: int, num_cus: int) -> int:

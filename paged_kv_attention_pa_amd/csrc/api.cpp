@@ -143,7 +143,7 @@ pa_status_t gqa_decode_schedule(pa_dtype_t dtype, int num_seqs, int max_seq_len,
   if (s->n == 0) {
     pa_status_t st = device_cus(&cus);
     if (st != PA_OK) return st;
-    s->n = pa_num_kv_splits(max_seq_len, cus);
+    s->n = pa_decode_num_kv_splits(num_seqs, num_kv_heads, max_seq_len, cus);
   }
   s->P = split_tokens_for(max_seq_len, s->n, block_size);
   s->stage1 = stage1;
@@ -214,6 +214,20 @@ int pa_num_kv_splits(int max_seq_len, int num_cus) {
   if (n < 1) n = 1;
   const int64_t cap = 2 * int64_t(num_cus);
   return int(n > cap ? cap : n);
+}
+
+int pa_decode_num_kv_splits(int num_seqs, int num_kv_heads, int max_seq_len, int num_cus) {
+  if (num_cus < 1) num_cus = 1;
+  const int rule = pa_num_kv_splits(max_seq_len, num_cus);
+  if (rule <= 1) return rule;
+  // a batch with fewer (request, KV head) pairs than twice the compute units
+  // gets more, shorter splits, each at least 64 keys long
+  const int64_t pairs = int64_t(num_seqs < 1 ? 1 : num_seqs) * (num_kv_heads < 1 ? 1 : num_kv_heads);
+  int64_t want = (2 * int64_t(num_cus) + pairs - 1) / pairs;
+  const int64_t by_len = (int64_t(max_seq_len) + 63) / 64;
+  if (want > by_len) want = by_len;
+  if (want > 2 * int64_t(num_cus)) want = 2 * int64_t(num_cus);
+  return int(want > rule ? want : rule);
 }
 
 size_t pa_decode_workspace_bytes(int num_seqs, int num_q_heads, int head_dim_v, int num_splits) {
@@ -783,7 +797,7 @@ pa_status_t pa_plan_mixed(const int32_t* qsl, const int32_t* seq_lens, int num_s
   // the decode group's schedule: pa_decode's automatic choice (bf16)
   p.decode_splits = 1;
   if (nd > 0) {
-    const int n = pa_num_kv_splits(p.max_decode_seq_len, cus);
+    const int n = pa_decode_num_kv_splits(nd, num_kv_heads, p.max_decode_seq_len, cus);
     const int P = split_tokens_for(p.max_decode_seq_len, n, block_size);
     if (used_splits(p.max_decode_seq_len, P) > 1) {
       p.decode_splits = n;

@@ -91,6 +91,23 @@ def test_decode_workspace_size_queries(lib):
     assert lib.pa_mla_decode_workspace_size(2, 10, 8, 16, 512, 2, 0, C.byref(sz)) == INVALID
 
 
+@pytest.mark.parametrize("B,hkv,L,cus,want", [
+    (64, 8, 8192, 256, 16),       # 512 pairs already fill 256 CUs twice: the pages' count
+    (3, 2, 4096, 256, 64),        # 6 pairs: raised to 64 splits of 64 keys
+    (1, 8, 4096, 256, 64),        # 8 pairs: ceil(512 / 8) = 64, also the 64-key floor
+    (4, 8, 131072, 256, 256),     # the pages' count is already 256
+    (2, 1, 100000, 256, 256),     # 2 pairs want 256 splits, below the 2 x CUs cap
+    (1, 1, 100000, 256, 512),     # one pair: capped at 2 x CUs
+    (3, 2, 512, 256, 1),          # the pages' rule does not split: one pass stays
+    (3, 2, 600, 256, 10),         # 2 by the rule, raised to ceil(600 / 64) = 10
+    (0, 0, 4096, 0, 2),           # non-positive counts read as 1: capped at 2 x 1 CU
+])
+def test_decode_split_helper(lib, B, hkv, L, cus, want):
+    n = pa.decode_num_kv_splits(B, hkv, L, cus)
+    assert n == want
+    assert n >= O.num_kv_splits(L, max(cus, 1))
+
+
 def test_mla_split_helper(lib):
     for B, L, cus in [(128, 8192, 256), (1, 8192, 256), (4, 100, 256), (300, 1000, 256)]:
         n = pa.mla_num_kv_splits(B, L, cus)

@@ -31,14 +31,25 @@ def _qsl(q_lens):
     return [0] + list(np.cumsum(q_lens).astype(int))
 
 
+def _auto_splits(nd, hkv, max_len, cus):
+    """pa_decode_num_kv_splits as the header states it: the pages' count (the
+    oracle's copy of the rule), raised when it splits at all until
+    nd * hkv * n reaches 2 * cus, with splits of at least 64 keys."""
+    n = O.num_kv_splits(max_len, cus)
+    if n <= 1:
+        return n
+    want = min(math.ceil(2 * cus / (nd * hkv)), math.ceil(max_len / 64), 2 * cus)
+    return max(n, want)
+
+
 def _expected_decode_schedule(nd, max_len, hq, hkv, bs, cus):
     """The decode group's schedule as the header states it: n =
-    pa_num_kv_splits (the oracle's copy of the rule); one pass if the
-    block-aligned split of max_len keys needs one split, else token-balanced
-    ranges (1, 2, 4 or a multiple of 8 KV heads) or n splits."""
+    pa_decode_num_kv_splits; one pass if the block-aligned split of max_len
+    keys needs one split, else token-balanced ranges (1, 2, 4 or a multiple
+    of 8 KV heads) or n splits."""
     if nd == 0:
         return 1, 0, 0
-    n = O.num_kv_splits(max_len, cus)
+    n = _auto_splits(nd, hkv, max_len, cus)
     P = math.ceil(math.ceil(max_len / n) / bs) * bs
     if math.ceil(max_len / P) <= 1:
         return 1, 0, 0
