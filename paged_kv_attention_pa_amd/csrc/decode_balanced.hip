@@ -17,7 +17,11 @@
 // x 16 query-head columns, G of them used); the P^T registers feed O^T =
 // V^T P^T directly.  The registers of chunk c+1 are refilled as soon as
 // chunk c's pieces are in LDS, so one chunk of loads is in flight while the
-// previous one is computed; two barriers per chunk guard the shared tiles.
+// previous one is computed; two barriers per chunk guard the shared tiles
+// (bf16), or one barrier and two sets of tiles (FP8, whose tiles are half
+// the size).
+#include <type_traits>
+
 #include "balanced.hpp"
 #include "launch.hpp"
 #include "pa_device.hpp"
@@ -29,17 +33,32 @@ constexpr int kD = 128;
 constexpr int kChunk = kChunkTokens;    // tokens per chunk (one MFMA k-extent)
 constexpr int kRow = kD * 2 + 16;       // LDS row of a token: 256 B + 16 B pad
 constexpr int kTile = kChunk * kRow;    // per-wave tile (K, then V)
+// FP8 tiles hold the codes themselves: 128 B + 16 B pad per token row, and
+// the last 16 rows start 16 B further on, so that the transposed reads of
+// rows r and r + 16 (one MFMA operand) fall on different LDS banks.  Tiles
+// are 128 B past a multiple of 256 B apart: the 16-byte stores of one row of
+// two neighbouring heads then use disjoint banks.
+constexpr int kRow8 = kD + 16;
+constexpr int kTile8 = kChunk * kRow8 + 128;
 constexpr int kHeads = 8;               // KV heads (waves) per work-group
 
-// kFp8: the cache holds E4M3 codes (one byte per element); the loads fetch
-// half the bytes, each 16-byte piece is widened to bf16 on its way into LDS
-// (exact), and the scales fold into the score scale (k_scale) and the final
-// normalisation (v_scale), so the tiles and everything after them are the
-// bf16 kernel's.
+// kFp8: the cache holds E4M3 codes (one byte per element).  The loads fetch
+// half the bytes and the codes go to LDS as they are (half the LDS traffic
+// of widened tiles); each MFMA operand is widened to
+// bf16 (exact) as it is read back: 8 codes of a K row (ds_read_b64), or 8
+// keys of one V column (ds_read_b64_tr_b8).  The scales fold into the score
+// scale (k_scale) and the final normalisation (v_scale), so the products and
+// the softmax are the bf16 kernel's.
 template <int G, bool kFp8>
 __global__ __launch_bounds__(64 * kHeads, 1) void decode_balanced_kernel(DecodeBalanced a) {
   static_assert(G >= 1 && G <= 16, "group must fit the 16 MFMA columns");
-  __shared__ __align__(16) char smem[2 * kHeads * kTile];   // K tiles of every head, then V tiles
+  constexpr int kTT = kFp8 ? kTile8 : kTile;   // bytes of one head's K (or V) tile
+  // FP8: two sets of tiles, chunk c in set (c - c0) mod 2, so one barrier per
+  // chunk suffices (a wave stores chunk c + 1 only after every wave has
+  // passed chunk c's barrier, i.e. has finished reading chunk c - 1)
+  constexpr int kSets = kFp8 ? 2 : 1;
+  constexpr int kSet = 2 * kHeads * kTT;       // K tiles of every head, then V tiles
+  __shared__ __align__(16) char smem[kSets * kSet];
   __shared__ int s_wave_sum[kHeads];
   __shared__ int s_start[2];
   const int tid = threadIdx.x;
@@ -112,6 +131,15 @@ __global__ __launch_bounds__(64 * kHeads, 1) void decode_balanced_kernel(DecodeB
   const int waves = blockDim.x >> 6;
   const char* const a_base = smem + wave * kTile + li * kRow + 16 * kq;             // K: row 16 sub + li
   const char* const tr_base = smem + (kHeads + wave) * kTile + (4 * kq + (li >> 2)) * kRow + 8 * (li & 3);
+  // FP8 tiles.  K operand of S^T: row 16 sub + li, codes 32 kk + 8 kq .. +7.
+  // V^T operand: ds_read_b64_tr_b8 hands lane li of a 16-lane group byte li
+  // of each of 8 rows, row k being the 8-byte chunks of lanes 2k and 2k + 1;
+  // lane pair k points at key 4 kq + (k mod 4) + 16 (k / 4), dims 16 dt ..
+  // 16 dt + 15, so lane li gets dim 16 dt + li of the keys in P^T's order
+  // (4 kq + i, then 16 + 4 kq + i).
+  const char* const k8_base = smem + wave * kTile8 + li * kRow8 + 8 * kq;
+  const int vk = 4 * kq + ((li >> 1) & 3) + 16 * (li >> 3);
+  const char* const v8_base = smem + (kHeads + wave) * kTile8 + vk * kRow8 + 16 * (vk >> 4) + 8 * (li & 1);
   // Loads are contiguous 1 KiB pieces of the work-group's slice of a token
   // row (waves x 256 B): instruction i of wave w is piece I = w + waves i,
   // lane l its bytes 16 l .. 16 l + 15.  Piece I covers tokens (1024 I) /
@@ -143,7 +171,11 @@ __global__ __launch_bounds__(64 * kHeads, 1) void decode_balanced_kernel(DecodeB
   // K and V pieces of chunk p: one address per piece for both planes (the V
   // piece is kv_bytes on), so the page lookups and the scalar address math
   // are done once.
-  auto load_kv = [&](const ChunkPos& p, u32x4_t (&kdst)[kLoads], u32x4_t (&vdst)[kLoads]) {
+  // A load past the range's last chunk (dummy) keeps the wait counts exact
+  // but reads the first token row of block 0, the same bytes for every
+  // work-group, which stay in L2 instead of costing HBM bytes.
+  auto load_kv = [&](const ChunkPos& p, bool dummy, u32x4_t (&kdst)[kLoads],
+                     u32x4_t (&vdst)[kLoads]) {
     const int32_t* table = a.block_table + int64_t(p.r) * a.max_blocks;
     const int len = max(p.len, 1);   // positions always hold keys; keeps every index >= 0
 #pragma unroll
@@ -160,9 +192,13 @@ __global__ __launch_bounds__(64 * kHeads, 1) void decode_balanced_kernel(DecodeB
       // non-temporal: every cache byte is read once, so it need not displace
       // anything in L2 or the MALL (81% against 72% of HBM peak on the
       // headline batch)
-      const char* src = cache_b + blk * page_bytes + (uint32_t(tok - page * bs) * tok32 + uint32_t(byte));
-      kdst[i] = load16_stream(src);
-      vdst[i] = load16_stream(src + kv_bytes);
+      blk = dummy ? 0u : blk;
+      const uint32_t off = (dummy ? 0u : uint32_t(tok - page * bs) * tok32) + uint32_t(byte);
+      // page bases are scalars; the lane offset is one 32-bit register
+      const char* kpage = cache_b + blk * page_bytes;
+      const char* vpage = kpage + kv_bytes;
+      kdst[i] = load16_stream(kpage + off);
+      vdst[i] = load16_stream(vpage + off);
     }
   };
   // LDS position of this lane's piece i (head tile, token row, byte of the
@@ -170,8 +206,11 @@ __global__ __launch_bounds__(64 * kHeads, 1) void decode_balanced_kernel(DecodeB
   auto lds_off = [&](int i) {
     const int lin = (wave + waves * i) * 1024 + 16 * lane;
     const int byte = lin & ((1 << sh) - 1);
-    return (byte >> kRowShift) * kTile + (lin >> sh) * kRow +
-           (byte & ((1 << kRowShift) - 1)) * (2 / kElem);
+    const int t = lin >> sh;
+    if constexpr (kFp8)
+      return (byte >> kRowShift) * kTile8 + t * kRow8 + 16 * (t >> 4) + (byte & ((1 << kRowShift) - 1));
+    else
+      return (byte >> kRowShift) * kTile + t * kRow + (byte & ((1 << kRowShift) - 1));
   };
 
   ChunkPos nxt = c0 + 1 < c1 ? next_chunk(cur, a.seq_lens, cap, B) : cur;
@@ -179,43 +218,42 @@ __global__ __launch_bounds__(64 * kHeads, 1) void decode_balanced_kernel(DecodeB
   u32x4_t qf[4];
   load_q(cur.r, qf);
   u32x4_t kr[kLoads], vr[kLoads];
-  load_kv(cur, kr, vr);
+  load_kv(cur, false, kr, vr);
 
   f32x4_t acc[8];   // O^T: d = 16 dt + 4 kq + i, head column li
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) acc[dt] = f32x4_t{0, 0, 0, 0};
   float m_run = kNoMax, l_run = 0.0f;
 
-  for (int c = c0; c < c1; ++c) {
+  // One chunk; set (a compile-time constant) names its tiles.
+  auto step = [&](const int c, auto set) {
+    constexpr int ST = decltype(set)::value * kSet;
     // this chunk's pieces into every head's K and V tiles; once all waves'
     // are there, the registers are refilled with the next chunk
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) {
-      const int o = lds_off(i);
-      if constexpr (kFp8) {
-        u32x4_t lo, hi;
-        fp8x16_to_bf16(kr[i], lo, hi);
-        *reinterpret_cast<u32x4_t*>(smem + o) = lo;
-        *reinterpret_cast<u32x4_t*>(smem + o + 16) = hi;
-        fp8x16_to_bf16(vr[i], lo, hi);
-        *reinterpret_cast<u32x4_t*>(smem + kHeads * kTile + o) = lo;
-        *reinterpret_cast<u32x4_t*>(smem + kHeads * kTile + o + 16) = hi;
-      } else {
-        *reinterpret_cast<u32x4_t*>(smem + o) = kr[i];
-        *reinterpret_cast<u32x4_t*>(smem + kHeads * kTile + o) = vr[i];
-      }
+      const int o = ST + lds_off(i);
+      *reinterpret_cast<u32x4_t*>(smem + o) = kr[i];
+      *reinterpret_cast<u32x4_t*>(smem + kHeads * kTT + o) = vr[i];
     }
     __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's LDS stores are done
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    load_kv(nxt, kr, vr);
+    load_kv(nxt, c + 1 >= c1, kr, vr);
     f32x4_t sc[2];
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
       sc[sub] = f32x4_t{0, 0, 0, 0};
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
-        const u32x4_t kf = *reinterpret_cast<const u32x4_t*>(a_base + 16 * sub * kRow + 64 * kk);
+        u32x4_t kf;
+        if constexpr (kFp8) {
+          const u32x2_t c8 = *reinterpret_cast<const u32x2_t*>(k8_base + ST + sub * (16 * kRow8 + 16) + 32 * kk);
+          kf = u32x4_t{fp8x2_to_bf16x2<false>(c8[0]), fp8x2_to_bf16x2<true>(c8[0]),
+                       fp8x2_to_bf16x2<false>(c8[1]), fp8x2_to_bf16x2<true>(c8[1])};
+        } else {
+          kf = *reinterpret_cast<const u32x4_t*>(a_base + 16 * sub * kRow + 64 * kk);
+        }
         sc[sub] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kf), as_bf16x8(qf[kk]), sc[sub], 0, 0, 0);
       }
     }
@@ -255,11 +293,18 @@ __global__ __launch_bounds__(64 * kHeads, 1) void decode_balanced_kernel(DecodeB
     // 4 kq + li / 4 (and +16) at dims 16 dt + 4 (li % 4).
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
-      const uint2 v1 = lds_read_tr(tr_base + 32 * dt);
-      const uint2 v2 = lds_read_tr(tr_base + 16 * kRow + 32 * dt);
+      u32x4_t vf;
+      if constexpr (kFp8) {
+        const u32x2_t c8 = lds_read_tr8(v8_base + ST + 16 * dt);
+        vf = u32x4_t{fp8x2_to_bf16x2<false>(c8[0]), fp8x2_to_bf16x2<true>(c8[0]),
+                     fp8x2_to_bf16x2<false>(c8[1]), fp8x2_to_bf16x2<true>(c8[1])};
+      } else {
+        const uint2 v1 = lds_read_tr(tr_base + 32 * dt);
+        const uint2 v2 = lds_read_tr(tr_base + 16 * kRow + 32 * dt);
+        vf = u32x4_t{v1.x, v1.y, v2.x, v2.y};
+      }
       acc[dt] *= alpha;
-      acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-          as_bf16x8(u32x4_t{v1.x, v1.y, v2.x, v2.y}), as_bf16x8(pf), acc[dt], 0, 0, 0);
+      acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(vf), as_bf16x8(pf), acc[dt], 0, 0, 0);
     }
 
     // end of this request's keys within the range: emit its segment
@@ -297,7 +342,20 @@ __global__ __launch_bounds__(64 * kHeads, 1) void decode_balanced_kernel(DecodeB
     }
     cur = nxt;
     if (c + 2 < c1) nxt = next_chunk(nxt, a.seq_lens, cap, B);
-    __builtin_amdgcn_s_barrier();   // every wave is done reading the tiles
+    if constexpr (kSets == 1) __builtin_amdgcn_s_barrier();   // every wave is done reading the tiles
+  };
+  using Set0 = std::integral_constant<int, 0>;
+  using Set1 = std::integral_constant<int, kSets - 1>;
+  if constexpr (kSets == 1) {
+    for (int c = c0; c < c1; ++c) step(c, Set0{});
+  } else {
+    const int pairs = (c1 - c0) >> 1;
+    int c = c0;
+    for (int t = 0; t < pairs; ++t, c += 2) {
+      step(c, Set0{});
+      step(c + 1, Set1{});
+    }
+    if (c < c1) step(c, Set0{});
   }
 }
 

@@ -115,12 +115,22 @@ __device__ __forceinline__ uint2 lds_read_tr(const char* p) {
   return __builtin_bit_cast(uint2, v);
 }
 
+// Eight bytes from LDS, transposed within each 16-lane group: the group's
+// 16 chunks of 8 bytes form 8 rows of 16 bytes (row k = the chunks of lanes
+// 2k and 2k + 1), and lane i receives byte i of every row, row k in byte k.
+// ds_read_b64_tr_b8.
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2_t;
+__device__ __forceinline__ u32x2_t lds_read_tr8(const char* p) {
+  typedef __attribute__((ext_vector_type(2))) int s32x2_t;
+  typedef __attribute__((address_space(3))) s32x2_t lds_s2;
+  return __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_s2*)(p)));
+}
+
 // Transposed LDS read issued as inline assembly, for tiles that are filled by
 // global_load_lds: the compiler cannot tell that the read does not alias the
 // tile still being filled and would wait for every outstanding load before the
 // intrinsic form.  The result is NOT ready when this returns: it must pass
 // through lds_wait() (which ties the registers to an s_waitcnt) before use.
-typedef __attribute__((ext_vector_type(2))) uint32_t u32x2_t;
 template <int kOffset>
 __device__ __forceinline__ u32x2_t lds_read_tr_issue(const char* p) {
   u32x2_t v;
@@ -207,6 +217,16 @@ __device__ __forceinline__ void lds_wait(u32x4_t& a, u32x4_t& b, u32x4_t& c, u32
 __device__ __forceinline__ float xor32_max(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+// The same with lane l ^ 16 (v_permlane16_swap: rows 1 and 3 of one copy
+// trade places with rows 0 and 2 of the other).
+__device__ __forceinline__ float xor16_max(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor16_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 __device__ __forceinline__ float xor32_sum(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
