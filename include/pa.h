@@ -279,8 +279,9 @@ pa_status_t pa_decode_noalloc(pa_dtype_t dtype,
  * block_size / 32) < 2^31.
  * pa_decode_balanced_merge completes out / lse (a request with no keys gets
  * out = 0, lse = -inf) after pa_decode_balanced (head_dim_v 128) or
- * pa_mla_decode_balanced (head_dim_v = kv_lora_rank, 512 or 256); its num_seqs, num_heads,
- * num_ranges and workspace must be those of the preceding call.
+ * pa_mla_decode_balanced (head_dim_v = kv_lora_rank, 512 or 256; head_dim_v
+ * also tells it which of the two partitions cut the ranges); its num_seqs,
+ * num_heads, num_ranges and workspace must be those of the preceding call.
  * ------------------------------------------------------------------------- */
 int pa_decode_balanced_num_ranges(int num_kv_heads, int num_cus);
 
@@ -379,8 +380,14 @@ pa_status_t pa_mla_decode(const void* q_nope, int64_t qn_stride_b, int64_t qn_st
                           void* out, float* lse, hipStream_t stream);
 
 /* pa_mla_decode_balanced -- pa_mla_decode's reduction cut into token-balanced
- * ranges (see pa_decode_balanced: 32-key chunks of the whole batch, range j =
- * chunks [floor(j T / nr), floor((j+1) T / nr)), one work-group each).
+ * ranges, one work-group each.  As in pa_decode_balanced the batch's 32-key
+ * chunks form one list, but each request with keys is entered as 5 units of
+ * overhead followed by its chunks (a request without keys adds nothing): a
+ * request that starts inside a range costs that range about as much as five
+ * chunks (its partial is written and the next query loaded).  With T units
+ * and nr = min(num_ranges, T), range j holds the chunks whose units lie in
+ * [floor(j T / nr), floor((j+1) T / nr)); a range of overhead units only does
+ * nothing.  The workspace's prefix sums are of units.
  * Arguments as in pa_mla_decode (no latent write: call pa_cache_write
  * first), with num_ranges in [1, 2^24] and a 16-byte aligned workspace of
  * pa_decode_balanced_workspace_bytes(num_seqs, num_heads, 512, num_ranges)

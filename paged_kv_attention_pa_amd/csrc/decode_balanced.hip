@@ -97,10 +97,10 @@ __global__ __launch_bounds__(64 * kHeads, 1) void decode_balanced_kernel(DecodeB
       if (clamp_len(uniform_load(a.seq_lens + r), cap) == 0) write_token(r);
   }
 
-  int c0, c1;
+  int c0, c1, n_chunks;   // no overhead units: chunks c0 .. c1 - 1
   ChunkPos cur;
   if (!balanced_range(a.seq_lens, B, cap, a.num_ranges, j, j == 0 && hg == 0, a.cu, s_wave_sum,
-                      s_start, c0, c1, cur))
+                      s_start, c0, c1, n_chunks, cur))
     return;
   if (write_new) {
     ChunkPos p = cur;   // holds chunk c0
@@ -387,8 +387,9 @@ __global__ __launch_bounds__(256) void balanced_merge_kernel(BalancedMerge a) {
     return;
   }
   const int nr = min(a.num_ranges, total);
-  const int j0 = range_of_chunk(cb, nr, total);
-  const int j1 = range_of_chunk(ce - 1, nr, total);
+  constexpr int kW = DV == 128 ? 0 : kMlaRangeOverhead;   // GQA or MLA (rank 256) ranges
+  const int j0 = range_of_unit(cb + kW, nr, total);
+  const int j1 = range_of_unit(ce - 1, nr, total);
   if (j0 == j1) return;   // written by its range
   const int64_t step = int64_t(Hq) * kRowF;
   const float* p0 = a.part + (int64_t(j0 + r) * Hq + hq) * kRowF;
@@ -453,8 +454,8 @@ __global__ __launch_bounds__(256) void balanced_merge512_kernel(BalancedMerge a)
     return;
   }
   const int nr = min(a.num_ranges, total);
-  const int j0 = range_of_chunk(cb, nr, total);
-  const int j1 = range_of_chunk(ce - 1, nr, total);
+  const int j0 = range_of_unit(cb + kMlaRangeOverhead, nr, total);   // MLA ranges
+  const int j1 = range_of_unit(ce - 1, nr, total);
   if (j0 == j1) return;   // written by its range
   const int64_t step = int64_t(Hq) * kRowF;
   const float* p0 = a.part + (int64_t(j0 + r) * Hq + hq) * kRowF;

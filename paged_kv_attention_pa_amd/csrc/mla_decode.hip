@@ -161,7 +161,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void mla_kernel(MlaDecode a) {
   constexpr int kKSteps = Dm::kKSteps, kDTiles = Dm::kDTiles;
   (void)kTileLoads;
   __shared__ __align__(1024) char smem[kStages * kTileBytes];
-  __shared__ int s_wave_sum[kWaves];
+  __shared__ int s_wave_sum[2 * kWaves];
   __shared__ int s_start[2];
   const int lane = threadIdx.x & 63;
   const int wave = wave_id();
@@ -176,10 +176,9 @@ __global__ __launch_bounds__(64 * kWaves, 1) void mla_kernel(MlaDecode a) {
   ChunkPos cur;   // r, lc (tile index), kend, base (list index of the request's first chunk)
   if constexpr (kBalanced) {
     j = blockIdx.x;
-    if (!balanced_range(a.seq_lens, B, cap, a.num_ranges, j, j == 0, a.cu, s_wave_sum, s_start,
-                        c0, c1, cur))
+    if (!balanced_range<kMlaRangeOverhead>(a.seq_lens, B, cap, a.num_ranges, j, j == 0, a.cu,
+                                           s_wave_sum, s_start, c0, c1, n_tiles, cur))
       return;
-    n_tiles = c1 - c0;
   } else {
     const int S_spl = a.num_splits;
     s = blockIdx.x % S_spl;
@@ -206,7 +205,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void mla_kernel(MlaDecode a) {
   }
   auto advance = [&](const ChunkPos& p) {
     if constexpr (kBalanced) {
-      return next_chunk(p, a.seq_lens, cap, B);
+      return next_chunk<kMlaRangeOverhead>(p, a.seq_lens, cap, B);
     } else {
       return ChunkPos{p.r, p.lc + 1, p.len, p.base};
     }

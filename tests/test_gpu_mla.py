@@ -13,6 +13,10 @@ from gpu_util import bits, check_close, check_lse, say, to_dev, to_f64
 
 pytestmark = pytest.mark.gpu
 
+# Units of work a request start counts for when the MLA decode cuts its
+# token-balanced ranges (documented with pa_mla_decode_balanced).
+MLA_RANGE_OVERHEAD = 5
+
 
 def _run(b: W.MlaBatch, num_splits=0, write=True, fused_q=False):
     cache_t = to_dev(b.cache)
@@ -144,8 +148,12 @@ def test_mla_balanced_segments_against_oracle(num_ranges):
     b = W.make_mla(14, seq, 32, 512, 64, 64)
     B, H = b.num_seqs, b.num_heads
     cache, out, lse, ws, nr_arg = _run_balanced(b, num_ranges, merge=False)
+    # the MLA ranges count each request start as MLA_RANGE_OVERHEAD units of
+    # work: request r is units [cu[r], cu[r + 1]), its chunks the last n_r
     n = [-(-s // 32) for s in seq]
-    cu = np.concatenate([[0], np.cumsum(n)]).astype(np.int64)
+    units = [k + MLA_RANGE_OVERHEAD if k else 0 for k in n]
+    cu = np.concatenate([[0], np.cumsum(units)]).astype(np.int64)
+    first = cu[:-1] + MLA_RANGE_OVERHEAD   # unit of each request's first chunk
     T = int(cu[-1])
     nr = min(num_ranges, T)
     ranges = [(j * T // nr, (j + 1) * T // nr) for j in range(nr)]
@@ -157,7 +165,7 @@ def test_mla_balanced_segments_against_oracle(num_ranges):
     oref, lref = O.mla_decode(b.q_nope, b.q_pe, cache, b.block_table, b.seq_lens, b.scale)
     n_split = 0
     for r in range(B):
-        js = [j for j, (c0, c1) in enumerate(ranges) if c0 < cu[r + 1] and c1 > cu[r]]
+        js = [j for j, (c0, c1) in enumerate(ranges) if c0 < cu[r + 1] and c1 > first[r]]
         if len(js) == 1:
             check_close(o1[r], oref[r], f"direct request {r}")
             check_lse(l1[r], lref[r], f"direct request {r}")
@@ -167,8 +175,8 @@ def test_mla_balanced_segments_against_oracle(num_ranges):
         q = np.concatenate([O.to_f64(b.q_nope[r]), O.to_f64(b.q_pe[r])], axis=-1)[None]
         for j in js:
             c0, c1 = ranges[j]
-            lo = (max(c0, cu[r]) - cu[r]) * 32
-            hi = min((min(c1, cu[r + 1]) - cu[r]) * 32, seq[r])
+            lo = (max(c0, first[r]) - first[r]) * 32
+            hi = min((min(c1, cu[r + 1]) - first[r]) * 32, seq[r])
             po, pl = O.partial_attention(q, rows[:, None, :], rows[:, None, :512], b.scale, lo, hi,
                                          None)
             check_close(part[j + r, :, :512].astype(np.float64), po[0],
