@@ -583,7 +583,8 @@ pa_status_t pa_cache_write_fp8(pa_layout_t layout,
 /* pa_mla_decode_fp8: MLA decode (as pa_mla_decode) over an FP8 latent cache
  * [num_blocks, block_size, kv_lora_rank + rope_dim] uint8 with one scale for
  * the row (kv_scale: keys and values alike), on the token-balanced schedule
- * (num_ranges = 0: one range per compute unit of the current device),
+ * of pa_mla_decode_balanced (the same ranges, 5 overhead units per request;
+ * num_ranges = 0: one range per compute unit of the current device),
  * workspace of pa_decode_balanced_workspace_bytes(num_seqs, num_heads,
  * kv_lora_rank, num_ranges) bytes.  Enqueues the write of kv_c / k_pe (if
  * given, quantised with kv_scale), the decode kernel and the segment merge.
