@@ -267,7 +267,7 @@ def mixed_case(b, name):
         pf_flops += 2 * (L * (S - L) + L * (L + 1) // 2) * b.num_q_heads * 2 * b.head_dim
     by = W.gqa_bytes(b)
     case = Case(name, step, kernel, by["total"], W.gqa_flops(b), by["total"] - by["write"],
-                W.gqa_flops(b), "hbm+mfma", "decode_balanced_kernel + merge + prefill_kernel",
+                W.gqa_flops(b), "hbm+mfma", "decode_balanced_kernel + merge + prefill_pp_kernel",
                 "api.cpp",
                 {"num_seqs": b.num_seqs, "num_decode": nd, "prefill_tokens": plan.prefill_tokens,
                  "num_q_heads": b.num_q_heads, "num_kv_heads": b.num_kv_heads,
