@@ -387,7 +387,9 @@ pa_status_t pa_mla_decode(const void* q_nope, int64_t qn_stride_b, int64_t qn_st
  * chunks (its partial is written and the next query loaded).  With T units
  * and nr = min(num_ranges, T), range j holds the chunks whose units lie in
  * [floor(j T / nr), floor((j+1) T / nr)); a range of overhead units only does
- * nothing.  The workspace's prefix sums are of units.
+ * nothing.  The workspace's prefix sums are of units.  Sizes: num_seqs *
+ * (ceil(max_blocks_per_seq * block_size / 32) + 5) < 2^31
+ * (PA_ERR_UNSUPPORTED otherwise).
  * Arguments as in pa_mla_decode (no latent write: call pa_cache_write
  * first), with num_ranges in [1, 2^24] and a 16-byte aligned workspace of
  * pa_decode_balanced_workspace_bytes(num_seqs, num_heads, 512, num_ranges)

@@ -102,10 +102,13 @@ pa_status_t check_balanced(int num_seqs, int num_heads, int head_dim_v, int max_
                            size_t workspace_bytes) {
   PA_REQUIRE(num_ranges >= 1 && num_ranges <= (1 << 24), PA_ERR_INVALID,
              "num_ranges must be in [1, 2^24] (got %d)", num_ranges);
-  // chunk counts are summed in int32 on the device
+  // unit counts (chunks, plus the MLA list's overhead units per request; the
+  // merge's row width tells the two lists apart) are summed in int32 on the device
   const int64_t len_cap = int64_t(max_blocks_per_seq) * block_size;
-  PA_REQUIRE(int64_t(num_seqs) * ((len_cap + 31) / 32) <= INT_MAX, PA_ERR_UNSUPPORTED,
-             "num_seqs * max_blocks_per_seq * block_size / 32 exceeds 2^31 chunks");
+  const int64_t w = head_dim_v == 128 ? 0 : pa::kMlaRangeOverhead;
+  PA_REQUIRE(int64_t(num_seqs) * ((len_cap + 31) / 32 + w) <= INT_MAX, PA_ERR_UNSUPPORTED,
+             "num_seqs * (max_blocks_per_seq * block_size / 32 + %d) exceeds 2^31 units",
+             int(w));
   const size_t need = balanced_bytes(num_seqs, num_heads, head_dim_v, num_ranges);
   PA_REQUIRE(need > 0 && workspace != nullptr && workspace_bytes >= need, PA_ERR_WORKSPACE,
              "workspace of %zu bytes needed for %d ranges (got %zu)", need, num_ranges,

@@ -27,12 +27,13 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "launch.hpp"
 #include "pa_device.hpp"
 
 namespace pa {
 
 constexpr int kChunkTokens = 32;
-constexpr int kMlaRangeOverhead = 5;   // W of the MLA decode's ranges (see above)
+// kMlaRangeOverhead (launch.hpp): W of the MLA decode's ranges (see above)
 
 __device__ __forceinline__ int clamp_len(int s, int cap) { return s < 0 ? 0 : (s > cap ? cap : s); }
 __device__ __forceinline__ int chunks_of(int len) { return (len + kChunkTokens - 1) / kChunkTokens; }

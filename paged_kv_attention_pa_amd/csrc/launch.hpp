@@ -98,6 +98,9 @@ struct BalancedMerge {
 hipError_t launch_balanced_merge(const BalancedMerge& a, hipStream_t s);
 
 int balanced_num_ranges(int num_kv_heads, int num_cus);   // ranges for 8 waves per CU
+// Overhead units per request in the MLA decode's balanced list (a request
+// switch costs about five 32-key tiles); the GQA decode's list has none.
+constexpr int kMlaRangeOverhead = 5;
 size_t balanced_cu_bytes(int num_seqs);                    // cu[] size, 256-B aligned
 
 // ------------------------------------------------------------------- MLA
