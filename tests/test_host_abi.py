@@ -292,6 +292,18 @@ def test_mla_balanced_validation(lib):
     assert call(20, None) == INVALID                  # no output
     assert call(18, (1 << 20) + 8) == INVALID         # misaligned workspace
 
+    def sized(num_seqs, max_blocks):
+        a = list(base)
+        a[12], a[10] = num_seqs, max_blocks
+        return f(*a)
+
+    # the unit list (2 max_blocks chunks + 5 overhead units per request at
+    # block 64) must stay below 2^31: 2^20 (2046 + 5) units exceed it, though
+    # 2^20 * 2046 chunks alone would not; 2^20 (2040 + 5) fit, and only the
+    # workspace is then too small
+    assert sized(1 << 20, 1023) == UNSUPPORTED
+    assert sized(1 << 20, 1020) == WORKSPACE
+
 
 def test_fp8_write_validation(lib):
     f = lib.pa_cache_write_fp8
